@@ -1,0 +1,238 @@
+#!/usr/bin/env python3
+"""Throughput of the KV-vector codec hot path on one MI355X.
+
+One step = one pass of the whole path over one batch: the fused rotor
+quantize -> dequantize roundtrip of 65,536 fp16 keys (d = 128, 2-bit Lloyd-Max
+codes + 1-bit QJL signs = 3 bits, fp16 norms, S = 128 x 128 Gaussian) writing
+the record and the fp16 reconstruction, then q.k estimates of 64 fp32 queries
+against all 65,536 compressed keys.  Inputs are seeded synthetic data
+resident in HBM; the timed steps rotate over enough buffer sets (>= 1 GiB)
+that every step reads cold data from HBM rather than from the 256 MB
+last-level cache.
+
+Prints one JSON line.  `value` is quant+dequant vectors per second of whole
+steps; per-kernel times come from HIP events on the launch stream.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--sweep]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+N_VEC = 65536
+N_Q = 64
+BITS = 3
+HBM_PEAK_GBS = 8000.0
+FP16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def algorithmic_bytes(lay, in_bytes=256, out_bytes=256):
+    """Bytes one roundtrip moves per vector: input, record, output."""
+    return in_bytes + lay["record_bytes"] + out_bytes
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--sweep", action="store_true", help="also time the MSE-only roundtrip over an N sweep")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    return ap.parse_args()
+
+
+def kernel_sources_digest():
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "kv_cache_vector_norm_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, digest):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(kernel)
+    if not e or e.get("sources") != digest:
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline(x_host, q_host):
+    """The float64 oracle on a bounded sample, single thread."""
+    from threadpoolctl import threadpool_limits
+    from oracle import codec as OC
+    from oracle import params as OP
+    n = 2048
+    p = OP.Params(128, BITS, 0, OP.QJL)
+    xs = x_host[:n].astype("float64")
+    qs = q_host.astype("float64")
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            rec, _ = OC.quantize(p, xs)
+            OC.dequantize(p, rec)
+            OC.score(p, qs, rec)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el > 8.0 or reps >= 20:
+                break
+    return {"value": n * reps / el, "unit": "vectors/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} of the {N_VEC} keys (roundtrip + {N_Q} queries scored against them), "
+                      f"{reps} passes, float64 numpy, 1 thread",
+            "scores_per_s": n * N_Q * reps / el}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU: this build runs on a single MI355X and has no multi-GPU path "
+              f"(asked for --gpus {a.gpus})", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import kv_cache_vector_norm_amd as K
+    from kv_cache_vector_norm_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    codec = K.Codec(bits=BITS, seed=0, mode=K.RQ_QJL)
+    lay = codec.layout
+    x_host = W.keys_c1()
+    q_host = W.queries_c1()
+    x0 = torch.from_numpy(x_host).to(dev)
+    q = torch.from_numpy(q_host).to(dev)
+
+    set_bytes = N_VEC * (256 + 256 + lay["record_bytes"] + 4 * N_Q)
+    nsets = max(2, int(np.ceil((1 << 30) / set_bytes)))
+    xs, ys, recs, scs = [], [], [], []
+    for i in range(nsets):
+        xs.append(x0.clone())
+        ys.append(torch.empty((N_VEC, 128), dtype=torch.float16, device=dev))
+        recs.append(codec.alloc_record(N_VEC, dev))
+        scs.append(torch.empty((N_Q, N_VEC), dtype=torch.float32, device=dev))
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        k = i % nsets
+        if ev is not None:
+            ev[0].record(stream)
+        codec.roundtrip(xs[k], rec=recs[k], out=ys[k])
+        if ev is not None:
+            ev[1].record(stream)
+        codec.score(q, recs[k], N_Q, N_VEC, out=scs[k])
+        if ev is not None:
+            ev[2].record(stream)
+
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    rt_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    sc_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    ms_per_step = elapsed * 1e3 / a.steps
+
+    bytes_vec = algorithmic_bytes(lay)
+    rt_gbs = N_VEC * bytes_vec / (rt_ms * 1e-3) / 1e9
+    digest = kernel_sources_digest()
+    traffic = measured_traffic("rq_roundtrip_qjl3_f16", digest)
+    roof = {"bound": "hbm", "achieved": round(rt_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(rt_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "kernel": "rq_roundtrip (2-bit codes + QJL, fp16 in/out)",
+            "algorithmic_bytes_per_vector": bytes_vec, "vectors_per_launch": N_VEC,
+            "avg_launch_us": round(rt_ms * 1e3, 2)}
+    score_bytes = N_VEC * lay["record_bytes"] + 4 * N_Q * N_VEC
+    extras = {
+        "scores_per_s": round(N_Q * N_VEC * a.steps / elapsed, 1),
+        "roundtrip_vectors_per_s": round(N_VEC / (rt_ms * 1e-3), 1),
+        "score_us": round(sc_ms * 1e3, 2),
+        "score_scores_per_s": round(N_Q * N_VEC / (sc_ms * 1e-3), 1),
+        "score_gbs": round(score_bytes / (sc_ms * 1e-3) / 1e9, 1),
+        "buffer_sets": nsets,
+    }
+
+    # MSE-only 3-bit roundtrip (the HBM-bandwidth codec) on the same keys
+    mse = K.Codec(bits=3, seed=0, mode=K.RQ_MSE)
+    mrec = [mse.alloc_record(N_VEC, dev) for _ in range(nsets)]
+    for i in range(a.warmup):
+        mse.roundtrip(xs[i % nsets], rec=mrec[i % nsets], out=ys[i % nsets])
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(a.steps):
+        mse.roundtrip(xs[i % nsets], rec=mrec[i % nsets], out=ys[i % nsets])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    mse_us = e0.elapsed_time(e1) * 1e3 / a.steps
+    mb = algorithmic_bytes(mse.layout)
+    extras["mse3_roundtrip_us"] = round(mse_us, 2)
+    extras["mse3_roundtrip_gbs"] = round(N_VEC * mb / (mse_us * 1e-6) / 1e9, 1)
+    extras["mse3_roundtrip_vectors_per_s"] = round(N_VEC / (mse_us * 1e-6), 1)
+
+    if a.sweep:
+        sweep = {}
+        for n in (65536, 262144, 1048576, 4194304, 16777216):
+            xb = torch.randn((n, 128), device=dev).to(torch.float16)
+            yb = torch.empty_like(xb)
+            rb = mse.alloc_record(n, dev)
+            for _ in range(3):
+                mse.roundtrip(xb, rec=rb, out=yb)
+            reps = max(3, min(50, int(4e8 // (n * 566))))
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(reps):
+                mse.roundtrip(xb, rec=rb, out=yb)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            sweep[str(n)] = {"us": round(us, 2), "gbs": round(n * mb / (us * 1e-6) / 1e9, 1)}
+            del xb, yb, rb
+        extras["mse3_sweep"] = sweep
+
+    out = {
+        "metric": "quant+dequant vectors/s (d=128, 3-bit) + % HBM roofline; q·k scores/s",
+        "value": round(N_VEC * a.steps / elapsed, 1),
+        "unit": "vectors/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "65,536 fp16 N(0,1) keys d=128, RotorQuant 2-bit MSE + 1-bit QJL (3 bits), "
+                               "fused roundtrip + q.k estimates of 64 fp32 queries",
+                   "vectors": N_VEC, "queries": N_Q, "bits": BITS, "mode": "rotor+qjl", "seed": 0},
+        "roofline": roof,
+        "kernel_sources": digest,
+        **extras,
+    }
+    if not a.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(x_host, q_host)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,215 @@
+/*
+ * rq.h -- C ABI of the MI355X (gfx950) KV-vector codec: RotorQuant's per-group
+ * Cl(3,0) rotor codec and TurboQuant's dense-rotation codec, each optionally
+ * with the 1-bit QJL residual stage, plus the q.k estimator over compressed
+ * keys.
+ *
+ * The ABI follows the quantization map Q : R^d -> {0,1}^B and its inverse
+ * Q^-1 : {0,1}^B -> R^d (hyper.ai summary of arXiv 2504.19874, section "方法").
+ * A session (rq_ctx) fixes d, the bit width, the seed of the random
+ * parameters and the mode; quantize / dequantize / roundtrip / score then run
+ * asynchronously on a caller's HIP stream over caller-owned device buffers.
+ *
+ * Conventions that hold for every call below:
+ *  - Pointers named x, y, q, codes, norms, signs, rnorms, scores are DEVICE
+ *    pointers owned by the caller.  The library never frees or retains them.
+ *    rq_host_params and rq_get_params take HOST buffers.
+ *  - `stream` is a hipStream_t passed as void*; NULL is the null stream.  The
+ *    hot calls only enqueue work; they never synchronise and never allocate.
+ *  - Arguments are checked on the host before anything is enqueued.  A failed
+ *    check returns a status and writes nothing; rq_last_error() then holds a
+ *    message (thread-local, valid until the next failing call on the thread).
+ *  - Status: RQ_OK, or RQ_EINVAL (bad argument), RQ_EUNSUPPORTED (a valid but
+ *    unimplemented setting, e.g. d != 128), RQ_ENOMEM (allocation failed in
+ *    rq_init), RQ_EHIP (a HIP runtime or launch error).  Nothing aborts and no
+ *    C++ exception crosses the ABI.
+ *  - A ctx may be used by one host thread at a time.  Calls with one ctx on
+ *    different streams may run concurrently EXCEPT rq_score / tq-ctx scoring,
+ *    which stage rotated queries in a ctx-owned workspace: serialise scoring
+ *    calls that share a ctx.
+ *  - Identical inputs give identical output bytes.
+ *
+ * Record layout (structure of arrays, one row per vector; all little endian):
+ *    codes [n][code_words] uint32  -- MSE codes as ONE bit stream: the code of
+ *                                     coordinate i occupies bits
+ *                                     [b*i, b*i + b) of the row's words, b the
+ *                                     MSE bits; unused tail bits are 0.
+ *    norms [n] uint16              -- ||x||_2 as an IEEE half (round to
+ *                                     nearest even).
+ *    signs [n][4] uint32           -- QJL only: bit j (word j/32, bit j%32)
+ *                                     is 1 iff (S r)_j >= 0.
+ *    rnorms [n] uint16             -- QJL only: ||r||_2 of the unit-domain
+ *                                     residual, as an IEEE half.
+ * Rotor sessions code 129 coordinates (43 groups of 3: the 128 inputs and a
+ * zero pad; the pad's code is kept because group 42 needs it to invert);
+ * dense sessions code 128.
+ */
+#ifndef RQ_H
+#define RQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RQ_ABI_VERSION 1
+
+/* status codes */
+#define RQ_OK 0
+#define RQ_EINVAL 1
+#define RQ_EUNSUPPORTED 2
+#define RQ_ENOMEM 3
+#define RQ_EHIP 4
+
+/* mode flags (OR-able) */
+#define RQ_MSE 0   /* MSE codes only, b bits per coordinate                   */
+#define RQ_QJL 1   /* b-1 MSE bits + 1-bit QJL signs of the residual + ||r||  */
+#define RQ_DENSE 2 /* TurboQuant: dense 128x128 rotation Pi instead of rotors */
+
+/* element types of vector inputs / outputs */
+#define RQ_F32 0
+#define RQ_F16 1
+
+/* Largest number of query rows one rq_score launch stages; larger hq is
+ * processed in chunks of this many rows by the same call. */
+#define RQ_SCORE_CHUNK 4096
+
+typedef struct rq_ctx rq_ctx;
+
+/* Sizes of one session's record (see "Record layout" above). */
+typedef struct {
+    int32_t d;            /* vector dimension (128)                          */
+    int32_t bits;         /* total bits per coordinate                       */
+    int32_t mse_bits;     /* bits of the MSE codes: bits, or bits-1 with QJL */
+    int32_t mode;         /* RQ_* flags                                      */
+    int32_t n_coords;     /* coded coordinates: 129 rotor, 128 dense         */
+    int32_t n_groups;     /* rotor groups (43) or 0                          */
+    int32_t levels;       /* 2^mse_bits                                      */
+    int32_t code_words;   /* ceil(n_coords * mse_bits / 32)                  */
+    int32_t sign_words;   /* 4 with QJL, else 0                              */
+    int32_t record_bytes; /* 4*code_words + 2 (+ 16 + 2 with QJL)            */
+} rq_layout_t;
+
+/* Host copies of a session's parameter tables.  Any member may be NULL (that
+ * table is skipped).  Sizes: rotors [n_groups*4] (s, b12, b13, b23 per group:
+ * the rotor [s,0,0,0,b12,b13,b23,0] of README "How RotorQuant Works");
+ * rotmats [n_groups*9] row-major 3x3 M_g with grade-1((R v) R~) = M_g v;
+ * centroids [levels]; boundaries [levels-1] (t_k = (c_k + c_{k+1})/2);
+ * pi [d*d] row-major, y = Pi x (dense only); s [d*d] half bits row-major,
+ * z = S r (QJL only). */
+typedef struct {
+    float* rotors;
+    float* rotmats;
+    float* centroids;
+    float* boundaries;
+    float* pi;
+    uint16_t* s;
+} rq_params_host_t;
+
+/* Fills *out with the record sizes of (d, bits, mode).  CPU only.
+ * RQ_EINVAL for bits outside 1..4 (MSE) / 2..5 (QJL) or unknown mode bits;
+ * RQ_EUNSUPPORTED for d != 128. */
+int rq_layout(int d, int bits, int mode, rq_layout_t* out);
+
+/* Computes the parameter tables of (d, bits, seed, mode) on the host, with
+ * no GPU involved, into the non-NULL buffers of *out.  These are bit-for-bit
+ * the tables rq_init uploads.  Generation (float64, each table rounded once):
+ *   - SplitMix64 streams per (seed, tag): rotors tag 1, Pi tag 2, S tag 3;
+ *     Box-Muller normals.
+ *   - rotors: exp of an N(0,1) bivector per group, normalised ("normalized
+ *     random bivector exponentials"; README "How RotorQuant Works").
+ *   - codebook: Lloyd-Max for the coordinate law of a uniform unit vector in
+ *     R^d (blog "Beta 分布", "MSE 标量量化"; README "Codebook Calibration Fix":
+ *     d_eff = d).
+ *   - Pi: orthogonal factor of a QR of a Gaussian matrix with diag(R) > 0
+ *     (README "How TurboQuant Works", Stage 1).
+ *   - S: Gaussian, each entry rounded to IEEE half (README Stage 2).
+ * Same status rules as rq_layout. */
+int rq_host_params(int d, int bits, uint64_t seed, int mode, rq_params_host_t* out);
+
+/* Opens a session on the current HIP device: computes the tables as
+ * rq_host_params does, uploads them once (synchronously) and returns the
+ * ctx in *out.  On any failure *out is set to NULL and nothing is leaked. */
+int rq_init(int d, int bits, uint64_t seed, int mode, rq_ctx** out);
+
+/* Frees a session's device tables.  NULL is a no-op.  The caller must make
+ * sure no enqueued work still uses the ctx. */
+void rq_free(rq_ctx* ctx);
+
+int rq_get_layout(const rq_ctx* ctx, rq_layout_t* out);
+int rq_get_params(const rq_ctx* ctx, rq_params_host_t* out);
+
+/* Q(x) for a rotor session (README "RotorQuant Fused Kernels": normalize ->
+ * embed -> rotor sandwich -> quantize; with RQ_QJL also README Stage 2 and
+ * hyper.ai Algorithm 2: residual r = x_u - Q_mse^-1(Q_mse(x_u)), signs of
+ * S r, ||r||).
+ *   x      [n][ldx] elements of x_dtype (RQ_F16 or RQ_F32), 16-byte aligned,
+ *          ldx >= 128 and ldx * element size a multiple of 16 bytes.
+ *   n      vectors (n == 0 is a no-op returning RQ_OK).
+ *   codes  [n][code_words], norms [n]; signs [n][4] and rnorms [n] must be
+ *          non-NULL exactly when the session has RQ_QJL.
+ * RQ_EINVAL on a dense session (use tq_quantize). */
+int rq_quantize(rq_ctx* ctx, const void* x, int x_dtype, int64_t n, int64_t ldx,
+                uint32_t* codes, uint16_t* norms, uint32_t* signs, uint16_t* rnorms,
+                void* stream);
+
+/* Q^-1 for a rotor session (README: inverse_sandwich -> extract -> rescale;
+ * with RQ_QJL the QJL term sqrt(pi/2)/m * ||r|| * S^T sign(S r) is added
+ * before rescaling, blog QJL section item 5).  Writes y [n][ldy] of y_dtype;
+ * the record arrays are read.  Alignment rules as for x. */
+int rq_dequantize(rq_ctx* ctx, const uint32_t* codes, const uint16_t* norms,
+                  const uint32_t* signs, const uint16_t* rnorms, int64_t n,
+                  void* y, int y_dtype, int64_t ldy, void* stream);
+
+/* One launch doing rq_quantize and rq_dequantize: writes the record AND the
+ * reconstruction (the README's full fused quantize -> dequantize pipeline,
+ * section "Triton Kernels" / "Usage", which returns x_hat).  The
+ * reconstruction is exactly what rq_dequantize returns for the written
+ * record.  x and y must not overlap. */
+int rq_roundtrip(rq_ctx* ctx, const void* x, int x_dtype, int64_t n, int64_t ldx,
+                 uint32_t* codes, uint16_t* norms, uint32_t* signs, uint16_t* rnorms,
+                 void* y, int y_dtype, int64_t ldy, void* stream);
+
+/* q.k estimates from compressed keys (README estimator:
+ *   <q,k> ~ <q,k_mse> + ||r|| sqrt(pi/2)/m <S q, sign(S r)>),
+ * for grouped-query attention: query row h reads KV head h / group.
+ *   q       [hq][128] fp32 queries, 16-byte aligned.
+ *   group   query rows per KV head (>= 1); hq must be a multiple of group.
+ *   codes.. records of hq/group KV heads; head j's t keys start at record
+ *           row j * kv_stride (kv_stride >= t, or any value if hq == group).
+ *   scores  [hq][ld_scores] fp32, ld_scores >= t; row h gets
+ *           n^_t (<q_h, x~_mse,u(t)> + gamma^_t sqrt(pi/2)/m <S q_h, sigma_t>),
+ *           raw: no 1/sqrt(d), no softmax.
+ * Works for rotor and dense sessions.  Uses the ctx's query workspace (see
+ * conventions). */
+int rq_score(rq_ctx* ctx, const float* q, int hq, int group,
+             const uint32_t* codes, const uint16_t* norms, const uint32_t* signs,
+             const uint16_t* rnorms, int64_t t, int64_t kv_stride,
+             float* scores, int64_t ld_scores, void* stream);
+
+/* TurboQuant comparison path (hyper.ai Algorithms 1 and 2; README "How
+ * TurboQuant Works"): y = Pi x_u, per-coordinate Lloyd-Max codes on 128
+ * coordinates, x~ = Pi^T y^ (+ the QJL stage with RQ_QJL).  Same arguments
+ * and rules as the rq_ functions; the ctx must have RQ_DENSE. */
+int tq_quantize(rq_ctx* ctx, const void* x, int x_dtype, int64_t n, int64_t ldx,
+                uint32_t* codes, uint16_t* norms, uint32_t* signs, uint16_t* rnorms,
+                void* stream);
+int tq_dequantize(rq_ctx* ctx, const uint32_t* codes, const uint16_t* norms,
+                  const uint32_t* signs, const uint16_t* rnorms, int64_t n,
+                  void* y, int y_dtype, int64_t ldy, void* stream);
+int tq_roundtrip(rq_ctx* ctx, const void* x, int x_dtype, int64_t n, int64_t ldx,
+                 uint32_t* codes, uint16_t* norms, uint32_t* signs, uint16_t* rnorms,
+                 void* y, int y_dtype, int64_t ldy, void* stream);
+
+/* Message of the calling thread's last failure ("" if none). */
+const char* rq_last_error(void);
+
+/* Library version string. */
+const char* rq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RQ_H */

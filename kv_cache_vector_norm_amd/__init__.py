@@ -1,0 +1,331 @@
+"""Python binding of librq.so, the MI355X (gfx950) KV-vector codec.
+
+The functions below have the names and argument lists of include/rq.h and
+only marshal arguments: device pointers may be given as torch tensors or
+integers; every step of the codec runs in the HIP library.  The `Codec`
+class adds record allocation with torch (device memory and streams only).
+
+There is no fallback: if librq.so is missing it is built in-tree; if that
+fails, importing the binding raises.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import workloads  # noqa: F401  (seeded synthetic inputs)
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "librq.so")
+
+RQ_OK, RQ_EINVAL, RQ_EUNSUPPORTED, RQ_ENOMEM, RQ_EHIP = 0, 1, 2, 3, 4
+RQ_MSE, RQ_QJL, RQ_DENSE = 0, 1, 2
+RQ_F32, RQ_F16 = 0, 1
+RQ_SCORE_CHUNK = 4096
+
+STATUS_NAMES = {0: "RQ_OK", 1: "RQ_EINVAL", 2: "RQ_EUNSUPPORTED", 3: "RQ_ENOMEM", 4: "RQ_EHIP"}
+
+EXPORTS = ("rq_layout", "rq_host_params", "rq_init", "rq_free", "rq_get_layout", "rq_get_params",
+           "rq_quantize", "rq_dequantize", "rq_roundtrip", "rq_score", "tq_quantize", "tq_dequantize",
+           "tq_roundtrip", "rq_last_error", "rq_version")
+
+
+class RQError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("d", "bits", "mse_bits", "mode", "n_coords", "n_groups", "levels",
+                                                "code_words", "sign_words", "record_bytes")]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+class ParamsHost(ctypes.Structure):
+    _fields_ = [("rotors", ctypes.c_void_p), ("rotmats", ctypes.c_void_p), ("centroids", ctypes.c_void_p),
+                ("boundaries", ctypes.c_void_p), ("pi", ctypes.c_void_p), ("s", ctypes.c_void_p)]
+
+
+def _load():
+    from .build import build, hip_runtime_dir
+    if not os.path.exists(LIB_PATH):
+        build()
+    # One HIP runtime per process: load the libamdhip64 that torch uses before
+    # librq.so, so that librq.so's dependency resolves to that same runtime
+    # (torch owns the device memory and streams handed to the library).
+    hip = os.path.join(hip_runtime_dir(), "libamdhip64.so")
+    if os.path.exists(hip):
+        ctypes.CDLL(hip, mode=ctypes.RTLD_GLOBAL)
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, I64, U64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_uint64
+    sig = {
+        "rq_layout": ([I, I, I, ctypes.POINTER(Layout)], I),
+        "rq_host_params": ([I, I, U64, I, ctypes.POINTER(ParamsHost)], I),
+        "rq_init": ([I, I, U64, I, ctypes.POINTER(P)], I),
+        "rq_free": ([P], None),
+        "rq_get_layout": ([P, ctypes.POINTER(Layout)], I),
+        "rq_get_params": ([P, ctypes.POINTER(ParamsHost)], I),
+        "rq_quantize": ([P, P, I, I64, I64, P, P, P, P, P], I),
+        "rq_dequantize": ([P, P, P, P, P, I64, P, I, I64, P], I),
+        "rq_roundtrip": ([P, P, I, I64, I64, P, P, P, P, P, I, I64, P], I),
+        "rq_score": ([P, P, I, I, P, P, P, P, I64, I64, P, I64, P], I),
+        "tq_quantize": ([P, P, I, I64, I64, P, P, P, P, P], I),
+        "tq_dequantize": ([P, P, P, P, P, I64, P, I, I64, P], I),
+        "tq_roundtrip": ([P, P, I, I64, I64, P, P, P, P, P, I, I64, P], I),
+        "rq_last_error": ([], ctypes.c_char_p),
+        "rq_version": ([], ctypes.c_char_p),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = res
+    return lib
+
+
+_lib = _load()
+
+
+def lib():
+    return _lib
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr()
+    if isinstance(x, np.ndarray):
+        return x.ctypes.data
+    raise TypeError(f"cannot pass {type(x)} as a pointer")
+
+
+def _stream(stream):
+    if stream is None:
+        try:
+            import torch
+            if torch.cuda.is_available():
+                return torch.cuda.current_stream().cuda_stream
+        except ImportError:
+            pass
+        return None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(rc):
+    if rc != RQ_OK:
+        raise RQError(rc, rq_last_error())
+    return rc
+
+
+# ----------------------------------------------------------------- C ABI --
+def rq_last_error():
+    return _lib.rq_last_error().decode()
+
+
+def rq_version():
+    return _lib.rq_version().decode()
+
+
+def rq_layout(d, bits, mode):
+    out = Layout()
+    _check(_lib.rq_layout(d, bits, mode, ctypes.byref(out)))
+    return out.as_dict()
+
+
+def rq_host_params(d, bits, seed, mode):
+    """Host parameter tables as numpy arrays (no GPU involved)."""
+    lay = rq_layout(d, bits, mode)
+    arrays = _param_arrays(lay, mode)
+    p = ParamsHost(*[arrays[k].ctypes.data if k in arrays else None for k in
+                     ("rotors", "rotmats", "centroids", "boundaries", "pi", "s")])
+    _check(_lib.rq_host_params(d, bits, seed, mode, ctypes.byref(p)))
+    return arrays
+
+
+def _param_arrays(lay, mode):
+    d, g, levels = lay["d"], lay["n_groups"], lay["levels"]
+    a = {"centroids": np.zeros(levels, np.float32), "boundaries": np.zeros(levels - 1, np.float32)}
+    if not mode & RQ_DENSE:
+        a["rotors"] = np.zeros((g, 4), np.float32)
+        a["rotmats"] = np.zeros((g, 3, 3), np.float32)
+    else:
+        a["pi"] = np.zeros((d, d), np.float32)
+    if mode & RQ_QJL:
+        a["s"] = np.zeros((d, d), np.uint16)
+    return a
+
+
+def rq_init(d, bits, seed, mode):
+    h = ctypes.c_void_p()
+    _check(_lib.rq_init(d, bits, seed, mode, ctypes.byref(h)))
+    return h.value
+
+
+def rq_free(ctx):
+    _lib.rq_free(ctx)
+
+
+def rq_get_layout(ctx):
+    out = Layout()
+    _check(_lib.rq_get_layout(ctx, ctypes.byref(out)))
+    return out.as_dict()
+
+
+def rq_get_params(ctx):
+    lay = rq_get_layout(ctx)
+    arrays = _param_arrays(lay, lay["mode"])
+    p = ParamsHost(*[arrays[k].ctypes.data if k in arrays else None for k in
+                     ("rotors", "rotmats", "centroids", "boundaries", "pi", "s")])
+    _check(_lib.rq_get_params(ctx, ctypes.byref(p)))
+    return arrays
+
+
+def _quant(fn, ctx, x, x_dtype, n, ldx, codes, norms, signs, rnorms, stream):
+    return _check(fn(ctx, _ptr(x), x_dtype, n, ldx, _ptr(codes), _ptr(norms), _ptr(signs), _ptr(rnorms),
+                     _stream(stream)))
+
+
+def _dequant(fn, ctx, codes, norms, signs, rnorms, n, y, y_dtype, ldy, stream):
+    return _check(fn(ctx, _ptr(codes), _ptr(norms), _ptr(signs), _ptr(rnorms), n, _ptr(y), y_dtype, ldy,
+                     _stream(stream)))
+
+
+def _round(fn, ctx, x, x_dtype, n, ldx, codes, norms, signs, rnorms, y, y_dtype, ldy, stream):
+    return _check(fn(ctx, _ptr(x), x_dtype, n, ldx, _ptr(codes), _ptr(norms), _ptr(signs), _ptr(rnorms), _ptr(y),
+                     y_dtype, ldy, _stream(stream)))
+
+
+def rq_quantize(ctx, x, x_dtype, n, ldx, codes, norms, signs=None, rnorms=None, stream=None):
+    return _quant(_lib.rq_quantize, ctx, x, x_dtype, n, ldx, codes, norms, signs, rnorms, stream)
+
+
+def tq_quantize(ctx, x, x_dtype, n, ldx, codes, norms, signs=None, rnorms=None, stream=None):
+    return _quant(_lib.tq_quantize, ctx, x, x_dtype, n, ldx, codes, norms, signs, rnorms, stream)
+
+
+def rq_dequantize(ctx, codes, norms, signs, rnorms, n, y, y_dtype, ldy, stream=None):
+    return _dequant(_lib.rq_dequantize, ctx, codes, norms, signs, rnorms, n, y, y_dtype, ldy, stream)
+
+
+def tq_dequantize(ctx, codes, norms, signs, rnorms, n, y, y_dtype, ldy, stream=None):
+    return _dequant(_lib.tq_dequantize, ctx, codes, norms, signs, rnorms, n, y, y_dtype, ldy, stream)
+
+
+def rq_roundtrip(ctx, x, x_dtype, n, ldx, codes, norms, signs, rnorms, y, y_dtype, ldy, stream=None):
+    return _round(_lib.rq_roundtrip, ctx, x, x_dtype, n, ldx, codes, norms, signs, rnorms, y, y_dtype, ldy, stream)
+
+
+def tq_roundtrip(ctx, x, x_dtype, n, ldx, codes, norms, signs, rnorms, y, y_dtype, ldy, stream=None):
+    return _round(_lib.tq_roundtrip, ctx, x, x_dtype, n, ldx, codes, norms, signs, rnorms, y, y_dtype, ldy, stream)
+
+
+def rq_score(ctx, q, hq, group, codes, norms, signs, rnorms, t, kv_stride, scores, ld_scores, stream=None):
+    return _check(_lib.rq_score(ctx, _ptr(q), hq, group, _ptr(codes), _ptr(norms), _ptr(signs), _ptr(rnorms), t,
+                                kv_stride, _ptr(scores), ld_scores, _stream(stream)))
+
+
+# ----------------------------------------------------------- convenience --
+class Record:
+    """Device record arrays of n vectors (torch tensors)."""
+
+    def __init__(self, codes, norms, signs=None, rnorms=None):
+        self.codes, self.norms, self.signs, self.rnorms = codes, norms, signs, rnorms
+
+    @property
+    def n(self):
+        return self.codes.shape[0]
+
+    def host(self):
+        """(codes uint32, norms uint16, signs uint32 | None, rnorms uint16 | None) as numpy."""
+        def u(t, dt):
+            return None if t is None else t.cpu().numpy().view(dt)
+        return u(self.codes, np.uint32), u(self.norms, np.uint16), u(self.signs, np.uint32), u(self.rnorms, np.uint16)
+
+
+class Codec:
+    """A session plus torch-allocated outputs.  `dense` selects TurboQuant."""
+
+    def __init__(self, bits=3, seed=0, mode=RQ_MSE, d=128):
+        import torch
+        self.torch = torch
+        self.mode = mode
+        self.dense = bool(mode & RQ_DENSE)
+        self.ctx = rq_init(d, bits, seed, mode)
+        self.layout = rq_get_layout(self.ctx)
+
+    def close(self):
+        if self.ctx:
+            rq_free(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def params(self):
+        return rq_get_params(self.ctx)
+
+    def alloc_record(self, n, device="cuda"):
+        t = self.torch
+        lay = self.layout
+        codes = t.zeros((n, lay["code_words"]), dtype=t.int32, device=device)
+        norms = t.zeros((n,), dtype=t.int16, device=device)
+        signs = rnorms = None
+        if lay["sign_words"]:
+            signs = t.zeros((n, lay["sign_words"]), dtype=t.int32, device=device)
+            rnorms = t.zeros((n,), dtype=t.int16, device=device)
+        return Record(codes, norms, signs, rnorms)
+
+    def _dt(self, tensor):
+        t = self.torch
+        if tensor.dtype == t.float16:
+            return RQ_F16
+        if tensor.dtype == t.float32:
+            return RQ_F32
+        raise TypeError("vectors must be float16 or float32")
+
+    def quantize(self, x, rec=None, stream=None):
+        n = x.shape[0]
+        rec = rec or self.alloc_record(n, x.device)
+        fn = tq_quantize if self.dense else rq_quantize
+        fn(self.ctx, x, self._dt(x), n, x.stride(0), rec.codes, rec.norms, rec.signs, rec.rnorms, stream)
+        return rec
+
+    def dequantize(self, rec, dtype=None, out=None, stream=None):
+        t = self.torch
+        n = rec.n
+        if out is None:
+            out = t.empty((n, self.layout["d"]), dtype=dtype or t.float32, device=rec.codes.device)
+        fn = tq_dequantize if self.dense else rq_dequantize
+        fn(self.ctx, rec.codes, rec.norms, rec.signs, rec.rnorms, n, out, self._dt(out), out.stride(0), stream)
+        return out
+
+    def roundtrip(self, x, dtype=None, rec=None, out=None, stream=None):
+        t = self.torch
+        n = x.shape[0]
+        rec = rec or self.alloc_record(n, x.device)
+        if out is None:
+            out = t.empty((n, self.layout["d"]), dtype=dtype or x.dtype, device=x.device)
+        fn = tq_roundtrip if self.dense else rq_roundtrip
+        fn(self.ctx, x, self._dt(x), n, x.stride(0), rec.codes, rec.norms, rec.signs, rec.rnorms, out,
+           self._dt(out), out.stride(0), stream)
+        return rec, out
+
+    def score(self, q, rec, group, t, kv_stride=None, out=None, stream=None):
+        th = self.torch
+        hq = q.shape[0]
+        kv_stride = t if kv_stride is None else kv_stride
+        if out is None:
+            out = th.empty((hq, t), dtype=th.float32, device=q.device)
+        rq_score(self.ctx, q, hq, group, rec.codes, rec.norms, rec.signs, rec.rnorms, t, kv_stride, out,
+                 out.stride(0), stream)
+        return out

@@ -1,0 +1,428 @@
+// C ABI of the codec (declared in include/rq.h): argument checks, session
+// set-up, and dispatch to the HIP launchers.  No call here allocates after
+// rq_init, and nothing is enqueued when an argument check fails.
+#include "../../include/rq.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "rq_host.h"
+#include "rq_kernels.h"
+
+static_assert(RQ_SCORE_CHUNK == rqk::kScoreChunkRows, "score chunk size");
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+    g_last_error = msg;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(RQ_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// Test hook: RQ_TEST_FAIL_ALLOC=k makes the k-th device allocation of an
+// rq_init call fail (k >= 1), to exercise the clean-up path.
+int g_alloc_countdown_init() {
+    const char* v = std::getenv("RQ_TEST_FAIL_ALLOC");
+    return v ? std::atoi(v) : 0;
+}
+
+struct DevAlloc {
+    int countdown;
+    std::vector<void*> owned;
+    explicit DevAlloc(int k) : countdown(k) {}
+    hipError_t alloc(void** p, size_t bytes) {
+        if (countdown > 0 && --countdown == 0) return hipErrorOutOfMemory;
+        const hipError_t e = hipMalloc(p, bytes);
+        if (e == hipSuccess) owned.push_back(*p);
+        return e;
+    }
+    void release() {
+        for (void* p : owned) (void)hipFree(p);
+        owned.clear();
+    }
+};
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t elem_size(int dtype) { return dtype == RQ_F16 ? 2 : 4; }
+
+}  // namespace
+
+struct rq_ctx {
+    rqh::Tables host;
+    int device = -1;
+    uint64_t seed = 0;
+    std::vector<void*> dev;   // every device allocation of this session
+    // rotor tables
+    float* rotmat = nullptr;
+    float* thr = nullptr;
+    float* cent = nullptr;
+    // QJL
+    uint16_t* s_rows = nullptr;
+    uint16_t* s_cols = nullptr;
+    // dense (TurboQuant): Pi split into exact half pairs, both layouts
+    uint16_t* pi_hi = nullptr;
+    uint16_t* pi_lo = nullptr;
+    uint16_t* pit_hi = nullptr;
+    uint16_t* pit_lo = nullptr;
+    // scoring workspace
+    void* qws = nullptr;
+    size_t qws_bytes = 0;
+};
+
+extern "C" {
+
+const char* rq_last_error(void) { return g_last_error.c_str(); }
+
+const char* rq_version(void) { return "rq-mi355x 1.0 (gfx950)"; }
+
+static void to_abi(const rqh::Layout& l, rq_layout_t* out) {
+    out->d = l.d;
+    out->bits = l.bits;
+    out->mse_bits = l.mse_bits;
+    out->mode = l.mode;
+    out->n_coords = l.n_coords;
+    out->n_groups = l.n_groups;
+    out->levels = l.levels;
+    out->code_words = l.code_words;
+    out->sign_words = l.sign_words;
+    out->record_bytes = l.record_bytes;
+}
+
+int rq_layout(int d, int bits, int mode, rq_layout_t* out) {
+    if (!out) return fail(RQ_EINVAL, "rq_layout: out is NULL");
+    rqh::Layout l;
+    std::string err;
+    const int rc = rqh::make_layout(d, bits, mode, &l, &err);
+    if (rc) return fail(rc == 2 ? RQ_EUNSUPPORTED : RQ_EINVAL, "rq_layout: " + err);
+    to_abi(l, out);
+    return RQ_OK;
+}
+
+static void copy_params(const rqh::Tables& t, rq_params_host_t* out) {
+    auto cp = [](void* dst, const void* src, size_t bytes) {
+        if (dst && bytes) std::memcpy(dst, src, bytes);
+    };
+    cp(out->rotors, t.rotors.data(), t.rotors.size() * sizeof(float));
+    cp(out->rotmats, t.rotmats.data(), t.rotmats.size() * sizeof(float));
+    cp(out->centroids, t.centroids.data(), t.centroids.size() * sizeof(float));
+    cp(out->boundaries, t.boundaries.data(), t.boundaries.size() * sizeof(float));
+    cp(out->pi, t.pi.data(), t.pi.size() * sizeof(float));
+    cp(out->s, t.s.data(), t.s.size() * sizeof(uint16_t));
+}
+
+int rq_host_params(int d, int bits, uint64_t seed, int mode, rq_params_host_t* out) {
+    if (!out) return fail(RQ_EINVAL, "rq_host_params: out is NULL");
+    rqh::Tables t;
+    std::string err;
+    const int rc = rqh::make_tables(d, bits, seed, mode, &t, &err);
+    if (rc) return fail(rc == 2 ? RQ_EUNSUPPORTED : RQ_EINVAL, "rq_host_params: " + err);
+    copy_params(t, out);
+    return RQ_OK;
+}
+
+int rq_get_layout(const rq_ctx* ctx, rq_layout_t* out) {
+    if (!ctx || !out) return fail(RQ_EINVAL, "rq_get_layout: NULL argument");
+    to_abi(ctx->host.lay, out);
+    return RQ_OK;
+}
+
+int rq_get_params(const rq_ctx* ctx, rq_params_host_t* out) {
+    if (!ctx || !out) return fail(RQ_EINVAL, "rq_get_params: NULL argument");
+    copy_params(ctx->host, out);
+    return RQ_OK;
+}
+
+void rq_free(rq_ctx* ctx) {
+    if (!ctx) return;
+    int cur = -1;
+    const bool switch_dev = hipGetDevice(&cur) == hipSuccess && cur != ctx->device && ctx->device >= 0;
+    if (switch_dev) (void)hipSetDevice(ctx->device);
+    for (void* p : ctx->dev) (void)hipFree(p);
+    if (switch_dev) (void)hipSetDevice(cur);
+    delete ctx;
+}
+
+int rq_init(int d, int bits, uint64_t seed, int mode, rq_ctx** out) {
+    if (!out) return fail(RQ_EINVAL, "rq_init: out is NULL");
+    *out = nullptr;
+    rq_ctx* ctx = new (std::nothrow) rq_ctx;
+    if (!ctx) return fail(RQ_ENOMEM, "rq_init: host allocation failed");
+    std::string err;
+    const int rc = rqh::make_tables(d, bits, seed, mode, &ctx->host, &err);
+    if (rc) {
+        delete ctx;
+        return fail(rc == 2 ? RQ_EUNSUPPORTED : RQ_EINVAL, "rq_init: " + err);
+    }
+    ctx->seed = seed;
+    hipError_t e = hipGetDevice(&ctx->device);
+    if (e != hipSuccess) {
+        delete ctx;
+        return hip_fail(e, "rq_init: hipGetDevice");
+    }
+    const rqh::Tables& t = ctx->host;
+    const int n = t.lay.d;
+    DevAlloc da(g_alloc_countdown_init());
+    auto upload = [&](void** dst, const void* src, size_t bytes) -> hipError_t {
+        hipError_t r = da.alloc(dst, bytes);
+        if (r != hipSuccess) return r;
+        return hipMemcpy(*dst, src, bytes, hipMemcpyHostToDevice);
+    };
+    // derived half tables
+    std::vector<uint16_t> s_cols, pi_hi, pi_lo, pit_hi, pit_lo;
+    if (mode & RQ_QJL) {
+        s_cols.resize(t.s.size());
+        for (int j = 0; j < n; ++j)
+            for (int i = 0; i < n; ++i) s_cols[i * n + j] = t.s[j * n + i];
+    }
+    if (mode & RQ_DENSE) {
+        // Pi = hi + lo exactly enough: hi = half(Pi * 2^4), lo = half((Pi * 2^4 - hi) * 2^11);
+        // the kernels undo the 2^4 and 2^11 scales in fp32.
+        pi_hi.resize(t.pi.size());
+        pi_lo.resize(t.pi.size());
+        pit_hi.resize(t.pi.size());
+        pit_lo.resize(t.pi.size());
+        for (int r = 0; r < n; ++r)
+            for (int c = 0; c < n; ++c) {
+                const double v = static_cast<double>(t.pi[r * n + c]) * 16.0;
+                const uint16_t h = rqh::double_to_half_rne(v);
+                // value of h
+                const int ex = (h >> 10) & 0x1F, mant = h & 0x3FF;
+                double hv = ex == 0 ? std::ldexp(static_cast<double>(mant), -24)
+                                    : std::ldexp(1.0 + mant / 1024.0, ex - 15);
+                if (h & 0x8000) hv = -hv;
+                const uint16_t lo = rqh::double_to_half_rne((v - hv) * 2048.0);
+                pi_hi[r * n + c] = h;
+                pi_lo[r * n + c] = lo;
+                pit_hi[c * n + r] = h;
+                pit_lo[c * n + r] = lo;
+            }
+    }
+    do {
+        if (!(mode & RQ_DENSE)) {
+            if ((e = upload(reinterpret_cast<void**>(&ctx->rotmat), t.rotmats.data(), t.rotmats.size() * 4)) != hipSuccess) break;
+        }
+        if ((e = upload(reinterpret_cast<void**>(&ctx->thr), t.boundaries.data(), t.boundaries.size() * 4)) != hipSuccess) break;
+        if ((e = upload(reinterpret_cast<void**>(&ctx->cent), t.centroids.data(), t.centroids.size() * 4)) != hipSuccess) break;
+        if (mode & RQ_QJL) {
+            if ((e = upload(reinterpret_cast<void**>(&ctx->s_rows), t.s.data(), t.s.size() * 2)) != hipSuccess) break;
+            if ((e = upload(reinterpret_cast<void**>(&ctx->s_cols), s_cols.data(), s_cols.size() * 2)) != hipSuccess) break;
+        }
+        if (mode & RQ_DENSE) {
+            if ((e = upload(reinterpret_cast<void**>(&ctx->pi_hi), pi_hi.data(), pi_hi.size() * 2)) != hipSuccess) break;
+            if ((e = upload(reinterpret_cast<void**>(&ctx->pi_lo), pi_lo.data(), pi_lo.size() * 2)) != hipSuccess) break;
+            if ((e = upload(reinterpret_cast<void**>(&ctx->pit_hi), pit_hi.data(), pit_hi.size() * 2)) != hipSuccess) break;
+            if ((e = upload(reinterpret_cast<void**>(&ctx->pit_lo), pit_lo.data(), pit_lo.size() * 2)) != hipSuccess) break;
+        }
+        ctx->qws_bytes = static_cast<size_t>(RQ_SCORE_CHUNK) * rqk::kScoreQueryBytes;
+        if ((e = da.alloc(&ctx->qws, ctx->qws_bytes)) != hipSuccess) break;
+    } while (false);
+    if (e != hipSuccess) {
+        da.release();
+        delete ctx;
+        if (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation)
+            return fail(RQ_ENOMEM, std::string("rq_init: device allocation failed: ") + hipGetErrorString(e));
+        return hip_fail(e, "rq_init");
+    }
+    ctx->dev = da.owned;
+    *out = ctx;
+    return RQ_OK;
+}
+
+// ------------------------------------------------------------ checks --
+static int check_ctx(const rq_ctx* ctx, bool dense, const char* fn) {
+    if (!ctx) return fail(RQ_EINVAL, std::string(fn) + ": ctx is NULL");
+    const bool is_dense = ctx->host.lay.mode & RQ_DENSE;
+    if (dense != is_dense)
+        return fail(RQ_EINVAL, std::string(fn) + (dense ? ": needs an RQ_DENSE session" : ": needs a rotor session (use tq_*)"));
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess || cur != ctx->device)
+        return fail(RQ_EINVAL, std::string(fn) + ": current HIP device is not the session's device");
+    return RQ_OK;
+}
+
+static int check_vectors(const void* p, int dtype, int64_t ld, const char* what, const char* fn) {
+    if (dtype != RQ_F16 && dtype != RQ_F32) return fail(RQ_EINVAL, std::string(fn) + ": bad dtype for " + what);
+    if (!p) return fail(RQ_EINVAL, std::string(fn) + ": " + what + " is NULL");
+    if (!aligned(p, 16)) return fail(RQ_EINVAL, std::string(fn) + ": " + what + " must be 16-byte aligned");
+    if (ld < rqh::kDim) return fail(RQ_EINVAL, std::string(fn) + ": leading dimension of " + what + " < 128");
+    if ((ld * static_cast<int64_t>(elem_size(dtype))) % 16 != 0)
+        return fail(RQ_EINVAL, std::string(fn) + ": row pitch of " + what + " must be a multiple of 16 bytes");
+    return RQ_OK;
+}
+
+static int check_record(const rq_ctx* ctx, const void* codes, const void* norms, const void* signs,
+                        const void* rnorms, const char* fn) {
+    if (!codes || !norms) return fail(RQ_EINVAL, std::string(fn) + ": codes and norms are required");
+    if (!aligned(codes, 4) || !aligned(norms, 2)) return fail(RQ_EINVAL, std::string(fn) + ": misaligned record array");
+    const bool qjl = ctx->host.lay.mode & RQ_QJL;
+    if (qjl != (signs != nullptr) || qjl != (rnorms != nullptr))
+        return fail(RQ_EINVAL, std::string(fn) + ": signs/rnorms must be given exactly for RQ_QJL sessions");
+    if (qjl && (!aligned(signs, 4) || !aligned(rnorms, 2)))
+        return fail(RQ_EINVAL, std::string(fn) + ": misaligned record array");
+    return RQ_OK;
+}
+
+static rqk::RotorTables rotor_tables(const rq_ctx* c) {
+    rqk::RotorTables t;
+    t.rotmat = c->rotmat;
+    t.thr = c->thr;
+    t.cent = c->cent;
+    t.s_rows = c->s_rows;
+    t.s_cols = c->s_cols;
+    t.qjl_scale = static_cast<float>(std::sqrt(M_PI / 2.0) / rqh::kQjlRows);
+    t.mse_bits = c->host.lay.mse_bits;
+    t.qjl = c->host.lay.mode & RQ_QJL;
+    return t;
+}
+
+static rqk::DenseTables dense_tables(const rq_ctx* c) {
+    rqk::DenseTables t;
+    t.pi_hi = c->pi_hi;
+    t.pi_lo = c->pi_lo;
+    t.pit_hi = c->pit_hi;
+    t.pit_lo = c->pit_lo;
+    t.thr = c->thr;
+    t.cent = c->cent;
+    t.s_rows = c->s_rows;
+    t.s_cols = c->s_cols;
+    t.qjl_scale = static_cast<float>(std::sqrt(M_PI / 2.0) / rqh::kQjlRows);
+    t.mse_bits = c->host.lay.mse_bits;
+    t.qjl = c->host.lay.mode & RQ_QJL;
+    return t;
+}
+
+static int finish(hipError_t e, const char* fn) { return e == hipSuccess ? RQ_OK : hip_fail(e, fn); }
+
+static int quantize_impl(rq_ctx* ctx, bool dense, const void* x, int x_dtype, int64_t n, int64_t ldx, uint32_t* codes,
+                         uint16_t* norms, uint32_t* signs, uint16_t* rnorms, void* y, int y_dtype, int64_t ldy,
+                         bool roundtrip, void* stream, const char* fn) {
+    int rc;
+    if ((rc = check_ctx(ctx, dense, fn))) return rc;
+    if (n < 0) return fail(RQ_EINVAL, std::string(fn) + ": n < 0");
+    if ((rc = check_vectors(x, x_dtype, ldx, "x", fn))) return rc;
+    if ((rc = check_record(ctx, codes, norms, signs, rnorms, fn))) return rc;
+    if (roundtrip) {
+        if ((rc = check_vectors(y, y_dtype, ldy, "y", fn))) return rc;
+        const char* xb = static_cast<const char*>(x);
+        const char* yb = static_cast<const char*>(y);
+        const int64_t xs = (n > 0 ? (n - 1) * ldx + rqh::kDim : 0) * static_cast<int64_t>(elem_size(x_dtype));
+        const int64_t ys = (n > 0 ? (n - 1) * ldy + rqh::kDim : 0) * static_cast<int64_t>(elem_size(y_dtype));
+        if (n > 0 && xb < yb + ys && yb < xb + xs) return fail(RQ_EINVAL, std::string(fn) + ": x and y overlap");
+    }
+    if (n == 0) return RQ_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t ldx_b = ldx * static_cast<int64_t>(elem_size(x_dtype));
+    const int64_t ldy_b = roundtrip ? ldy * static_cast<int64_t>(elem_size(y_dtype)) : 0;
+    hipError_t e;
+    if (!dense)
+        e = rqk::rotor_quantize(rotor_tables(ctx), x, x_dtype == RQ_F16, ldx_b, n, codes, norms, signs, rnorms, y,
+                                y_dtype == RQ_F16, ldy_b, roundtrip, s);
+    else
+        e = rqk::dense_quantize(dense_tables(ctx), x, x_dtype == RQ_F16, ldx_b, n, codes, norms, signs, rnorms, y,
+                                y_dtype == RQ_F16, ldy_b, roundtrip, s);
+    return finish(e, fn);
+}
+
+static int dequantize_impl(rq_ctx* ctx, bool dense, const uint32_t* codes, const uint16_t* norms,
+                           const uint32_t* signs, const uint16_t* rnorms, int64_t n, void* y, int y_dtype,
+                           int64_t ldy, void* stream, const char* fn) {
+    int rc;
+    if ((rc = check_ctx(ctx, dense, fn))) return rc;
+    if (n < 0) return fail(RQ_EINVAL, std::string(fn) + ": n < 0");
+    if ((rc = check_record(ctx, codes, norms, signs, rnorms, fn))) return rc;
+    if ((rc = check_vectors(y, y_dtype, ldy, "y", fn))) return rc;
+    if (n == 0) return RQ_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t ldy_b = ldy * static_cast<int64_t>(elem_size(y_dtype));
+    hipError_t e;
+    if (!dense)
+        e = rqk::rotor_dequantize(rotor_tables(ctx), codes, norms, signs, rnorms, n, y, y_dtype == RQ_F16, ldy_b, s);
+    else
+        e = rqk::dense_dequantize(dense_tables(ctx), codes, norms, signs, rnorms, n, y, y_dtype == RQ_F16, ldy_b, s);
+    return finish(e, fn);
+}
+
+int rq_quantize(rq_ctx* ctx, const void* x, int x_dtype, int64_t n, int64_t ldx, uint32_t* codes, uint16_t* norms,
+                uint32_t* signs, uint16_t* rnorms, void* stream) {
+    return quantize_impl(ctx, false, x, x_dtype, n, ldx, codes, norms, signs, rnorms, nullptr, RQ_F16, 0, false,
+                         stream, "rq_quantize");
+}
+
+int rq_dequantize(rq_ctx* ctx, const uint32_t* codes, const uint16_t* norms, const uint32_t* signs,
+                  const uint16_t* rnorms, int64_t n, void* y, int y_dtype, int64_t ldy, void* stream) {
+    return dequantize_impl(ctx, false, codes, norms, signs, rnorms, n, y, y_dtype, ldy, stream, "rq_dequantize");
+}
+
+int rq_roundtrip(rq_ctx* ctx, const void* x, int x_dtype, int64_t n, int64_t ldx, uint32_t* codes, uint16_t* norms,
+                 uint32_t* signs, uint16_t* rnorms, void* y, int y_dtype, int64_t ldy, void* stream) {
+    return quantize_impl(ctx, false, x, x_dtype, n, ldx, codes, norms, signs, rnorms, y, y_dtype, ldy, true, stream,
+                         "rq_roundtrip");
+}
+
+int tq_quantize(rq_ctx* ctx, const void* x, int x_dtype, int64_t n, int64_t ldx, uint32_t* codes, uint16_t* norms,
+                uint32_t* signs, uint16_t* rnorms, void* stream) {
+    return quantize_impl(ctx, true, x, x_dtype, n, ldx, codes, norms, signs, rnorms, nullptr, RQ_F16, 0, false,
+                         stream, "tq_quantize");
+}
+
+int tq_dequantize(rq_ctx* ctx, const uint32_t* codes, const uint16_t* norms, const uint32_t* signs,
+                  const uint16_t* rnorms, int64_t n, void* y, int y_dtype, int64_t ldy, void* stream) {
+    return dequantize_impl(ctx, true, codes, norms, signs, rnorms, n, y, y_dtype, ldy, stream, "tq_dequantize");
+}
+
+int tq_roundtrip(rq_ctx* ctx, const void* x, int x_dtype, int64_t n, int64_t ldx, uint32_t* codes, uint16_t* norms,
+                 uint32_t* signs, uint16_t* rnorms, void* y, int y_dtype, int64_t ldy, void* stream) {
+    return quantize_impl(ctx, true, x, x_dtype, n, ldx, codes, norms, signs, rnorms, y, y_dtype, ldy, true, stream,
+                         "tq_roundtrip");
+}
+
+int rq_score(rq_ctx* ctx, const float* q, int hq, int group, const uint32_t* codes, const uint16_t* norms,
+             const uint32_t* signs, const uint16_t* rnorms, int64_t t, int64_t kv_stride, float* scores,
+             int64_t ld_scores, void* stream) {
+    const char* fn = "rq_score";
+    if (!ctx) return fail(RQ_EINVAL, "rq_score: ctx is NULL");
+    int rc;
+    if ((rc = check_ctx(ctx, ctx->host.lay.mode & RQ_DENSE, fn))) return rc;
+    if (!q || !aligned(q, 16)) return fail(RQ_EINVAL, "rq_score: q must be a 16-byte aligned device pointer");
+    if (hq < 1 || group < 1 || hq % group) return fail(RQ_EINVAL, "rq_score: need hq >= 1, group >= 1, hq % group == 0");
+    if (t < 0) return fail(RQ_EINVAL, "rq_score: t < 0");
+    if ((rc = check_record(ctx, codes, norms, signs, rnorms, fn))) return rc;
+    const int kv_heads = hq / group;
+    if (kv_heads > 1 && kv_stride < t) return fail(RQ_EINVAL, "rq_score: kv_stride < t");
+    if (!scores || !aligned(scores, 4)) return fail(RQ_EINVAL, "rq_score: scores must be a 4-byte aligned device pointer");
+    if (ld_scores < t) return fail(RQ_EINVAL, "rq_score: ld_scores < t");
+    if (t == 0) return RQ_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool dense = ctx->host.lay.mode & RQ_DENSE;
+    rqk::ScoreTables st;
+    st.dense = dense;
+    st.rot = dense ? rqk::RotorTables{} : rotor_tables(ctx);
+    st.den = dense ? dense_tables(ctx) : rqk::DenseTables{};
+    st.mse_bits = ctx->host.lay.mse_bits;
+    st.qjl = ctx->host.lay.mode & RQ_QJL;
+    st.qjl_scale = static_cast<float>(std::sqrt(M_PI / 2.0) / rqh::kQjlRows);
+    // query rows in chunks that keep whole KV heads together
+    const int heads_per_chunk = std::max(1, RQ_SCORE_CHUNK / group);
+    for (int h0 = 0; h0 < kv_heads; h0 += heads_per_chunk) {
+        const int nh = std::min(heads_per_chunk, kv_heads - h0);
+        const hipError_t e = rqk::score(st, q + static_cast<int64_t>(h0) * group * rqh::kDim, nh * group, group,
+                                        codes, norms, signs, rnorms, t, kv_stride, h0, ctx->qws,
+                                        scores + static_cast<int64_t>(h0) * group * ld_scores, ld_scores, s);
+        if (e != hipSuccess) return hip_fail(e, fn);
+    }
+    return RQ_OK;
+}
+
+}  // extern "C"

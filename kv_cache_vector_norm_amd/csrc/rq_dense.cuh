@@ -1,0 +1,461 @@
+// TurboQuant comparison path for gfx950: y = Pi x_u with a dense 128 x 128
+// random orthogonal Pi, per-coordinate Lloyd-Max codes on 128 coordinates,
+// x~ = Pi^T y^, optionally with the QJL residual stage (hyper.ai summary,
+// Algorithms 1 and 2; README "How TurboQuant Works").
+//
+// Both rotations are 32x32x16 MFMA contractions over a tile of 64 vectors
+// (one vector per lane, as in the rotor kernels).  Pi is held as an exact
+// pair of halves, 16 Pi = P_hi + 2^-11 P_lo, and so is the other operand,
+// 16 v = v_hi + 2^-11 v_lo; the three products that matter are folded into
+// one fp32 accumulator by scaling v_hi by 2^11:
+//   P_hi (2^11 v_hi) + P_hi v_lo + P_lo v_hi = 2^11 * 256 * (Pi v) + O(2^-22).
+// The residual projection S r reuses the rotor path's exact scheme (S is
+// exactly half; r enters as hi + lo).  Pi and S feed the quantize side from
+// LDS; Pi^T and S^T feed the dequantize side from global memory (L2
+// resident), which keeps LDS within one workgroup's budget.
+#pragma once
+
+#include "rq_common.cuh"
+#include "rq_kernels.h"
+
+namespace rqk {
+
+struct DenseDev {
+    const uint16_t* __restrict__ pi_hi;
+    const uint16_t* __restrict__ pi_lo;
+    const uint16_t* __restrict__ pit_hi;
+    const uint16_t* __restrict__ pit_lo;
+    const float* __restrict__ thr;
+    const float* __restrict__ cent;
+    const uint16_t* __restrict__ s_rows;
+    const uint16_t* __restrict__ s_cols;
+    float qjl_scale;
+};
+
+constexpr float kRotScale = 1.0f / (2048.0f * 256.0f);   // undoes 2^11 * 16 * 16
+constexpr float kDenseResidualScale = 4096.0f;
+
+// fragment of a row-major 128 x 128 half matrix in global memory
+__device__ __forceinline__ u32x4 gmat_frag(const uint16_t* __restrict__ m, int row, int chunk) {
+    return *reinterpret_cast<const u32x4*>(m + row * 128 + chunk * 8);
+}
+
+// 16 v as halves: hi = half(16 v), lo = half((16 v - hi) 2^11), and 2^11 hi
+// (the difference 16 v - hi is exact in fp32; scaling by 2^11 is exact).
+__device__ __forceinline__ void split16(float v, uint32_t* h11, uint32_t* h, uint32_t* l) {
+    const uint32_t hi = f2h(v * 16.0f);
+    const float hf = h2f(hi);
+    *h = hi;
+    *l = f2h((v * 16.0f - hf) * 2048.0f);
+    *h11 = f2h(hf * 2048.0f);
+}
+
+// acc[nt] += rotation of this lane's own 128-vector held as split pairs,
+// for the 32 output rows of M tile MT; A fragments from `fa_hi`, `fa_lo`.
+template <int MT, class FragHi, class FragLo>
+__device__ __forceinline__ void rot_mfma(const uint32_t (&vh11)[64], const uint32_t (&vh)[64],
+                                         const uint32_t (&vl)[64], FragHi fa_hi, FragLo fa_lo, int l,
+                                         float (&own0)[16], float (&own1)[16]) {
+    f32x16 a0 = {}, a1 = {};
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+        const int row = 32 * MT + (l & 31), chunk = 2 * kb + (l >> 5);
+        const u32x4 ph = fa_hi(row, chunk);
+        const u32x4 pl = fa_lo(row, chunk);
+        u32x4 b11_0, b11_1, bh_0, bh_1, bl_0, bl_1;
+        to_operands(u32x4{vh11[8 * kb], vh11[8 * kb + 1], vh11[8 * kb + 2], vh11[8 * kb + 3]},
+                    u32x4{vh11[8 * kb + 4], vh11[8 * kb + 5], vh11[8 * kb + 6], vh11[8 * kb + 7]}, &b11_0, &b11_1);
+        to_operands(u32x4{vh[8 * kb], vh[8 * kb + 1], vh[8 * kb + 2], vh[8 * kb + 3]},
+                    u32x4{vh[8 * kb + 4], vh[8 * kb + 5], vh[8 * kb + 6], vh[8 * kb + 7]}, &bh_0, &bh_1);
+        to_operands(u32x4{vl[8 * kb], vl[8 * kb + 1], vl[8 * kb + 2], vl[8 * kb + 3]},
+                    u32x4{vl[8 * kb + 4], vl[8 * kb + 5], vl[8 * kb + 6], vl[8 * kb + 7]}, &bl_0, &bl_1);
+        a0 = mfma(ph, b11_0, a0);
+        a0 = mfma(ph, bl_0, a0);
+        a0 = mfma(pl, bh_0, a0);
+        a1 = mfma(ph, b11_1, a1);
+        a1 = mfma(ph, bl_1, a1);
+        a1 = mfma(pl, bh_1, a1);
+    }
+    from_accumulators(a0, a1, own0, own1);
+}
+
+__device__ __forceinline__ void put_pair(uint32_t (&arr)[64], int i, uint32_t h) {
+    if (i & 1) arr[i >> 1] |= h << 16; else arr[i >> 1] = h;
+}
+
+// coordinate index of own register (h, r) in M tile MT
+__device__ __forceinline__ constexpr int own_coord(int mt, int h, int r) { return 32 * mt + own_row(h, r); }
+
+template <int B, bool QJL, class Out, class SColFrag>
+__device__ __forceinline__ void dense_dequant_vec(const DenseDev& P, const uint32_t* __restrict__ ctab,
+                                                  const uint32_t (&cw)[(128 * B + 31) / 32], float nhat, float ghat,
+                                                  const uint32_t (&sw)[4], SColFrag scol, Out& out, int l) {
+    constexpr int W = (128 * B + 31) / 32;
+    // y^ = c[code] as split pairs (ctab: lo 16 bits = hi half, hi 16 bits = 2^11 hi; ctab[L + k] = lo)
+    uint32_t yh11[64], yh[64], yl[64];
+#pragma unroll
+    for (int i = 0; i < 128; ++i) {
+        const uint32_t code = get_code<B, W>(cw, i);
+        const uint32_t e = ctab[code];
+        put_pair(yh, i, e & 0xFFFFu);
+        put_pair(yh11, i, e >> 16);
+        put_pair(yl, i, ctab[(1 << B) + code]);
+    }
+    const float k = P.qjl_scale * ghat;
+    auto tile = [&](auto mt_c) {
+        constexpr int MT = decltype(mt_c)::value;
+        float x0[16], x1[16];
+        rot_mfma<MT>(
+            yh11, yh, yl, [&](int row, int chunk) { return gmat_frag(P.pit_hi, row, chunk); },
+            [&](int row, int chunk) { return gmat_frag(P.pit_lo, row, chunk); }, l, x0, x1);
+        float q0[16], q1[16];
+        if constexpr (QJL) {
+            f32x16 a0 = {}, a1 = {};
+#pragma unroll
+            for (int kb = 0; kb < 8; ++kb) {
+                const uint32_t word = sw[kb >> 1] >> (16 * (kb & 1));
+                u32x4 op0, op1;
+                u32x4 s0, s1;
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const uint32_t b = word >> (2 * p);
+                    s0[p] = 0xBC00BC00u ^ ((b & 1u) << 15) ^ (((b >> 1) & 1u) << 31);
+                    const uint32_t c = word >> (8 + 2 * p);
+                    s1[p] = 0xBC00BC00u ^ ((c & 1u) << 15) ^ (((c >> 1) & 1u) << 31);
+                }
+                to_operands(s0, s1, &op0, &op1);
+                const u32x4 a = scol(32 * MT + (l & 31), 2 * kb + (l >> 5));
+                a0 = mfma(a, op0, a0);
+                a1 = mfma(a, op1, a1);
+            }
+            from_accumulators(a0, a1, q0, q1);
+        }
+        // coordinates of this tile in increasing order
+#pragma unroll
+        for (int il = 0; il < 32; ++il) {
+            const int b8 = il >> 3, w = il & 7;
+            const float xv = (w < 4 ? x0[4 * b8 + w] : x1[4 * b8 + w - 4]) * kRotScale;
+            float v = xv;
+            if constexpr (QJL) v = __builtin_fmaf(k, w < 4 ? q0[4 * b8 + w] : q1[4 * b8 + w - 4], xv);
+            out.set(32 * MT + il, nhat * v);
+        }
+    };
+    tile(std::integral_constant<int, 0>{});
+    tile(std::integral_constant<int, 1>{});
+    tile(std::integral_constant<int, 2>{});
+    tile(std::integral_constant<int, 3>{});
+}
+
+// ------------------------------------------------------------ kernels --
+template <int WAVES, bool QJL>
+struct DenseLds {
+    u32x4 tiles[WAVES][kTileBytes / 16];
+    u32x4 pih[128 * 16];
+    u32x4 pil[128 * 16];
+    u32x4 s_rows[QJL ? 128 * 16 : 1];
+    uint32_t ctab[32];
+    float thr[16];
+};
+
+template <int B>
+__device__ __forceinline__ void dense_tables_to_lds(const DenseDev& P, uint32_t* ctab, float* thr) {
+    constexpr int L = 1 << B;
+    if (threadIdx.x < L) {
+        uint32_t h11, h, l;
+        split16(P.cent[threadIdx.x], &h11, &h, &l);
+        ctab[threadIdx.x] = h | (h11 << 16);
+        ctab[L + threadIdx.x] = l;
+    }
+    if (threadIdx.x < L - 1) thr[threadIdx.x] = P.thr[threadIdx.x];
+}
+
+template <int B, bool QJL, bool IN_F16, bool OUT_F16, bool ROUNDTRIP, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void tq_quant_kernel(DenseDev P, const char* __restrict__ x,
+                                                              int64_t ldx_bytes, int64_t n,
+                                                              uint32_t* __restrict__ codes,
+                                                              uint16_t* __restrict__ norms,
+                                                              uint32_t* __restrict__ signs,
+                                                              uint16_t* __restrict__ rnorms, char* __restrict__ y,
+                                                              int64_t ldy_bytes) {
+    constexpr int W = (128 * B + 31) / 32;
+    constexpr int L = 1 << B;
+    __shared__ DenseLds<WAVES, QJL> sm;
+    dense_tables_to_lds<B>(P, sm.ctab, sm.thr);
+    mat_to_lds(P.pi_hi, sm.pih);
+    mat_to_lds(P.pi_lo, sm.pil);
+    if constexpr (QJL) mat_to_lds(P.s_rows, sm.s_rows);
+    __syncthreads();
+
+    const int wave = threadIdx.x >> 6;
+    u32x4* tile = sm.tiles[wave];
+    uint32_t* stage = reinterpret_cast<uint32_t*>(tile);
+    const int64_t ntiles = (n + 63) / 64;
+    for (int64_t t = blockIdx.x * (int64_t)WAVES + wave; t < ntiles; t += gridDim.x * (int64_t)WAVES) {
+        const int64_t base = t * 64;
+        const int z = opaque_zero();
+        const int l = lane_id() + z;
+        float thr[L - 1];
+#pragma unroll
+        for (int k = 0; k < L - 1; ++k) thr[k] = uniform(sm.thr[k + z]);
+
+        // load, norm (same arithmetic as the rotor path)
+        uint32_t xin[64];
+        {
+            if constexpr (IN_F16) {
+                tile_load(x, ldx_bytes, base, n, 0, tile, l);
+                wave_lds_sync();
+#pragma unroll
+                for (int c = 0; c < 16; ++c) {
+                    const u32x4 q = tile[swz(l, c)];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) xin[4 * c + e] = q[e];
+                }
+            } else {
+                // fp32: keep the values as floats in a 128-entry view
+            }
+        }
+        float xf32[IN_F16 ? 1 : 128];
+        if constexpr (!IN_F16) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                tile_load(x, ldx_bytes, base, n, 256 * h, tile, l);
+                wave_lds_sync();
+#pragma unroll
+                for (int c = 0; c < 16; ++c) {
+                    const u32x4 q = tile[swz(l, c)];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t qe = q[e];
+                        xf32[64 * h + 4 * c + e] = __builtin_bit_cast(float, qe);
+                    }
+                }
+            }
+        }
+        auto xget = [&](int i) -> float {
+            if constexpr (IN_F16) {
+                const uint32_t w = xin[i >> 1];
+                return h2f((i & 1) ? (w >> 16) : (w & 0xFFFFu));
+            } else {
+                return xf32[i];
+            }
+        };
+        float ss = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kD; ++i) {
+            const float v = xget(i);
+            ss = __builtin_fmaf(v, v, ss);
+        }
+        if constexpr (IN_F16) {
+#pragma unroll
+            for (int k = 0; k < 64; ++k) pin(xin[k]);
+        }
+        const float nrm = __builtin_sqrtf(ss);
+        const float inv = nrm > 0.0f ? 1.0f / nrm : 0.0f;
+        const uint32_t nh = f2h(nrm);
+        const float nhat = h2f(nh);
+
+        // y = Pi x_u
+        uint32_t cw[W];
+#pragma unroll
+        for (int k = 0; k < W; ++k) cw[k] = 0u;
+        {
+            uint32_t vh11[64], vh[64], vl[64];
+#pragma unroll
+            for (int i = 0; i < kD; ++i) {
+                uint32_t a, b, c;
+                split16(xget(i) * inv, &a, &b, &c);
+                put_pair(vh11, i, a);
+                put_pair(vh, i, b);
+                put_pair(vl, i, c);
+            }
+            auto tile_q = [&](auto mt_c) {
+                constexpr int MT = decltype(mt_c)::value;
+                float y0[16], y1[16];
+                rot_mfma<MT>(
+                    vh11, vh, vl, [&](int row, int chunk) { return mat_frag(sm.pih, row, chunk); },
+                    [&](int row, int chunk) { return mat_frag(sm.pil, row, chunk); }, l, y0, y1);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    put_code<B, W>(cw, own_coord(MT, 0, r), quant_code<B>(y0[r] * kRotScale, thr));
+                    put_code<B, W>(cw, own_coord(MT, 1, r), quant_code<B>(y1[r] * kRotScale, thr));
+                }
+            };
+            tile_q(std::integral_constant<int, 0>{});
+            tile_q(std::integral_constant<int, 1>{});
+            tile_q(std::integral_constant<int, 2>{});
+            tile_q(std::integral_constant<int, 3>{});
+        }
+
+        uint32_t sw[4] = {0u, 0u, 0u, 0u};
+        uint32_t gh = 0u;
+        float ghat = 0.0f;
+        if constexpr (QJL) {
+            // x~_u = Pi^T y^, r = x_u - x~_u (original domain), signs of S r
+            uint32_t rh[64], rl[64];
+            float gam2 = 0.0f;
+            {
+                uint32_t yh11[64], yh[64], yl[64];
+#pragma unroll
+                for (int i = 0; i < 128; ++i) {
+                    const uint32_t code = get_code<B, W>(cw, i);
+                    const uint32_t e = sm.ctab[code];
+                    put_pair(yh, i, e & 0xFFFFu);
+                    put_pair(yh11, i, e >> 16);
+                    put_pair(yl, i, sm.ctab[L + code]);
+                }
+                auto tile_r = [&](auto mt_c) {
+                    constexpr int MT = decltype(mt_c)::value;
+                    float x0[16], x1[16];
+                    rot_mfma<MT>(
+                        yh11, yh, yl, [&](int row, int chunk) { return gmat_frag(P.pit_hi, row, chunk); },
+                        [&](int row, int chunk) { return gmat_frag(P.pit_lo, row, chunk); }, l, x0, x1);
+#pragma unroll
+                    for (int il = 0; il < 32; ++il) {
+                        const int b8 = il >> 3, w = il & 7, i = 32 * MT + il;
+                        const float xt = (w < 4 ? x0[4 * b8 + w] : x1[4 * b8 + w - 4]) * kRotScale;
+                        const float r = xget(i) * inv - xt;
+                        gam2 = __builtin_fmaf(r, r, gam2);
+                        uint32_t hi, lo;
+                        split_h(r * kDenseResidualScale, &hi, &lo);
+                        put_pair(rh, i, hi);
+                        put_pair(rl, i, lo);
+                    }
+                };
+                tile_r(std::integral_constant<int, 0>{});
+                tile_r(std::integral_constant<int, 1>{});
+                tile_r(std::integral_constant<int, 2>{});
+                tile_r(std::integral_constant<int, 3>{});
+            }
+            const float gam = __builtin_sqrtf(gam2);
+            gh = f2h(gam);
+            ghat = h2f(gh);
+            auto zt = [&](auto mt_c) {
+                constexpr int MT = decltype(mt_c)::value;
+                f32x16 a0 = {}, a1 = {};
+#pragma unroll
+                for (int kb = 0; kb < 8; ++kb) {
+                    const u32x4 a = mat_frag(sm.s_rows, 32 * MT + (l & 31), 2 * kb + (l >> 5));
+                    u32x4 h0, h1, l0, l1;
+                    to_operands(u32x4{rh[8 * kb], rh[8 * kb + 1], rh[8 * kb + 2], rh[8 * kb + 3]},
+                                u32x4{rh[8 * kb + 4], rh[8 * kb + 5], rh[8 * kb + 6], rh[8 * kb + 7]}, &h0, &h1);
+                    to_operands(u32x4{rl[8 * kb], rl[8 * kb + 1], rl[8 * kb + 2], rl[8 * kb + 3]},
+                                u32x4{rl[8 * kb + 4], rl[8 * kb + 5], rl[8 * kb + 6], rl[8 * kb + 7]}, &l0, &l1);
+                    a0 = mfma(a, h0, a0);
+                    a0 = mfma(a, l0, a0);
+                    a1 = mfma(a, h1, a1);
+                    a1 = mfma(a, l1, a1);
+                }
+                float z0[16], z1[16];
+                from_accumulators(a0, a1, z0, z1);
+                uint32_t word = 0u;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    word |= (z0[r] >= 0.0f ? 1u : 0u) << own_row(0, r);
+                    word |= (z1[r] >= 0.0f ? 1u : 0u) << own_row(1, r);
+                }
+                sw[MT] = word;
+            };
+            zt(std::integral_constant<int, 0>{});
+            zt(std::integral_constant<int, 1>{});
+            zt(std::integral_constant<int, 2>{});
+            zt(std::integral_constant<int, 3>{});
+        }
+
+        if (base + l < n) norms[base + l] = static_cast<uint16_t>(nh);
+        words_store<W>(codes, base, n, cw, stage, l);
+        if constexpr (QJL) {
+            if (base + l < n) rnorms[base + l] = static_cast<uint16_t>(gh);
+            words_store<4>(signs, base, n, sw, stage, l);
+        }
+        if constexpr (ROUNDTRIP) {
+            VecOutT<OUT_F16> out;
+            if constexpr (!OUT_F16) out.bind(y, ldy_bytes, base, n);
+            out.begin(tile, l);
+            dense_dequant_vec<B, QJL>(P, sm.ctab, cw, nhat, ghat, sw,
+                                      [&](int row, int chunk) { return gmat_frag(P.s_cols, row, chunk); }, out, l);
+            out.store(y, ldy_bytes, base, n);
+        }
+    }
+}
+
+template <int B, bool QJL, bool OUT_F16>
+__global__ __launch_bounds__(256) void tq_dequant_kernel(DenseDev P, const uint32_t* __restrict__ codes,
+                                                         const uint16_t* __restrict__ norms,
+                                                         const uint32_t* __restrict__ signs,
+                                                         const uint16_t* __restrict__ rnorms, int64_t n,
+                                                         char* __restrict__ y, int64_t ldy_bytes) {
+    constexpr int W = (128 * B + 31) / 32;
+    __shared__ u32x4 tiles[4][kTileBytes / 16];
+    __shared__ uint32_t ctab[32];
+    __shared__ float thr_unused[16];
+    dense_tables_to_lds<B>(P, ctab, thr_unused);
+    __syncthreads();
+    const int wave = threadIdx.x >> 6;
+    u32x4* tile = tiles[wave];
+    uint32_t* stage = reinterpret_cast<uint32_t*>(tile);
+    const int64_t ntiles = (n + 63) / 64;
+    for (int64_t t = blockIdx.x * 4LL + wave; t < ntiles; t += gridDim.x * 4LL) {
+        const int64_t base = t * 64;
+        const int z = opaque_zero();
+        const int l = lane_id() + z;
+        uint32_t cw[W];
+        words_load<W>(codes, base, n, cw, stage, l);
+        const bool live = base + l < n;
+        const float nhat = live ? h2f(norms[base + l]) : 0.0f;
+        uint32_t sw[4] = {0u, 0u, 0u, 0u};
+        float ghat = 0.0f;
+        if constexpr (QJL) {
+            words_load<4>(signs, base, n, sw, stage, l);
+            ghat = live ? h2f(rnorms[base + l]) : 0.0f;
+        }
+        VecOutT<OUT_F16> out;
+        if constexpr (!OUT_F16) out.bind(y, ldy_bytes, base, n);
+        out.begin(tile, l);
+        dense_dequant_vec<B, QJL>(P, ctab, cw, nhat, ghat, sw,
+                                  [&](int row, int chunk) { return gmat_frag(P.s_cols, row, chunk); }, out, l);
+        out.store(y, ldy_bytes, base, n);
+    }
+}
+
+template <int B, bool QJL>
+hipError_t launch_tq_quant(const DenseDev& P, const void* x, bool in_f16, int64_t ldx_bytes, int64_t n,
+                           uint32_t* codes, uint16_t* norms, uint32_t* signs, uint16_t* rnorms, void* y, bool out_f16,
+                           int64_t ldy_bytes, bool roundtrip, hipStream_t s) {
+    constexpr int WAVES = QJL ? 2 : 4;
+    const int64_t ntiles = (n + 63) / 64;
+    const int64_t blocks = (ntiles + WAVES - 1) / WAVES;
+    const int grid = static_cast<int>(blocks < 256 * 4 ? (blocks > 0 ? blocks : 1) : 256 * 4);
+    const char* xc = static_cast<const char*>(x);
+    char* yc = static_cast<char*>(y);
+#define TQ_LAUNCH(IF, OF, RT)                                                                                  \
+    hipLaunchKernelGGL((tq_quant_kernel<B, QJL, IF, OF, RT, WAVES>), dim3(grid), dim3(WAVES * 64), 0, s, P, xc, \
+                       ldx_bytes, n, codes, norms, signs, rnorms, yc, ldy_bytes)
+    if (!roundtrip) {
+        if (in_f16) TQ_LAUNCH(true, true, false); else TQ_LAUNCH(false, true, false);
+    } else if (in_f16) {
+        if (out_f16) TQ_LAUNCH(true, true, true); else TQ_LAUNCH(true, false, true);
+    } else {
+        if (out_f16) TQ_LAUNCH(false, true, true); else TQ_LAUNCH(false, false, true);
+    }
+#undef TQ_LAUNCH
+    return hipGetLastError();
+}
+
+template <int B, bool QJL>
+hipError_t launch_tq_dequant(const DenseDev& P, const uint32_t* codes, const uint16_t* norms, const uint32_t* signs,
+                             const uint16_t* rnorms, int64_t n, void* y, bool out_f16, int64_t ldy_bytes,
+                             hipStream_t s) {
+    const int64_t ntiles = (n + 63) / 64;
+    const int64_t blocks = (ntiles + 3) / 4;
+    const int grid = static_cast<int>(blocks < 256 * 8 ? (blocks > 0 ? blocks : 1) : 256 * 8);
+    char* yc = static_cast<char*>(y);
+    if (out_f16)
+        hipLaunchKernelGGL((tq_dequant_kernel<B, QJL, true>), dim3(grid), dim3(256), 0, s, P, codes, norms, signs,
+                           rnorms, n, yc, ldy_bytes);
+    else
+        hipLaunchKernelGGL((tq_dequant_kernel<B, QJL, false>), dim3(grid), dim3(256), 0, s, P, codes, norms, signs,
+                           rnorms, n, yc, ldy_bytes);
+    return hipGetLastError();
+}
+
+}  // namespace rqk

@@ -1,0 +1,363 @@
+// Host core: parameter tables of a codec session and record layout.
+//
+// Everything here is float64 and is rounded once to the stored precision.
+// Build without -ffast-math and with -ffp-contract=off: the normals must be
+// the exact libm values of the published Box-Muller formula.
+#include "rq_host.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
+
+namespace rqh {
+
+namespace {
+
+constexpr uint64_t kGoldenGamma = 0x9E3779B97F4A7C15ull;
+constexpr uint64_t kStreamMul = 0xD1B54A32D192ED03ull;
+constexpr uint64_t kTagRotors = 1, kTagPi = 2, kTagS = 3;
+constexpr double kPi = 3.141592653589793;
+constexpr double kTwoPi = 2.0 * kPi;
+
+float to_f32(double x) { return static_cast<float>(x); }
+
+}  // namespace
+
+// ----------------------------------------------------------------- layout --
+int make_layout(int d, int bits, int mode, Layout* out, std::string* err) {
+    if (mode & ~(kModeQjl | kModeDense)) {
+        if (err) *err = "unknown mode bits";
+        return 1;
+    }
+    const bool qjl = mode & kModeQjl;
+    const int mse_bits = qjl ? bits - 1 : bits;
+    if (mse_bits < 1 || mse_bits > kMaxMseBits) {
+        if (err) *err = qjl ? "bits must be 2..5 with RQ_QJL" : "bits must be 1..4";
+        return 1;
+    }
+    if (d <= 0) {
+        if (err) *err = "d must be positive";
+        return 1;
+    }
+    if (d != kDim) {
+        if (err) *err = "only d = 128 is implemented";
+        return 2;
+    }
+    Layout l;
+    l.d = d;
+    l.bits = bits;
+    l.mse_bits = mse_bits;
+    l.mode = mode;
+    l.n_groups = (mode & kModeDense) ? 0 : (d + 2) / 3;
+    l.n_coords = (mode & kModeDense) ? d : 3 * l.n_groups;
+    l.levels = 1 << mse_bits;
+    l.code_words = (l.n_coords * mse_bits + 31) / 32;
+    l.sign_words = qjl ? kQjlRows / 32 : 0;
+    l.record_bytes = 4 * l.code_words + 2 + (qjl ? 4 * l.sign_words + 2 : 0);
+    *out = l;
+    return 0;
+}
+
+// ------------------------------------------------------------ SplitMix64 --
+// Steele, Lea and Flood (2014): advance by the golden gamma, then mix.
+uint64_t splitmix64_next(uint64_t* state) {
+    *state += kGoldenGamma;
+    uint64_t z = *state;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+static double next_uniform(uint64_t* state) {
+    const uint64_t w = splitmix64_next(state);
+    return (static_cast<double>(w >> 11) + 0.5) * 0x1p-53;
+}
+
+// Box-Muller: two uniforms give sqrt(-2 ln u1) cos(2 pi u2), then the sine.
+std::vector<double> normals(uint64_t seed, uint64_t tag, size_t count) {
+    uint64_t state = seed ^ (tag * kStreamMul);
+    std::vector<double> out;
+    out.reserve(count + 1);
+    while (out.size() < count) {
+        const double u1 = next_uniform(&state);
+        const double u2 = next_uniform(&state);
+        const double rad = std::sqrt(-2.0 * std::log(u1));
+        const double ang = kTwoPi * u2;
+        out.push_back(rad * std::cos(ang));
+        out.push_back(rad * std::sin(ang));
+    }
+    out.resize(count);
+    return out;
+}
+
+// ------------------------------------------------------------------ rotors --
+// Rotor R = s + b12 e12 + b13 e13 + b23 e23 acting on v = v1 e1 + v2 e2 + v3 e3.
+// The left product R v has grade-1 part t and trivector part t123; the right
+// product with R~ = s - b12 e12 - b13 e13 - b23 e23 keeps grade 1.  These are
+// the sparse products written out from e_i e_i = 1, e_i e_j = -e_j e_i.
+static void sandwich3(const double r[4], const double v[3], double y[3]) {
+    const double s = r[0], b12 = r[1], b13 = r[2], b23 = r[3];
+    const double t1 = s * v[0] + b12 * v[1] + b13 * v[2];
+    const double t2 = s * v[1] - b12 * v[0] + b23 * v[2];
+    const double t3 = s * v[2] - b13 * v[0] - b23 * v[1];
+    const double t123 = b12 * v[2] - b13 * v[1] + b23 * v[0];
+    y[0] = s * t1 + b12 * t2 + b13 * t3 + b23 * t123;
+    y[1] = -b12 * t1 + s * t2 + b23 * t3 - b13 * t123;
+    y[2] = -b13 * t1 - b23 * t2 + s * t3 + b12 * t123;
+}
+
+float rotor_matrix_entry_check(const float rf[4], double m[9]) {
+    const double r[4] = {rf[0], rf[1], rf[2], rf[3]};
+    for (int j = 0; j < 3; ++j) {
+        double e[3] = {0.0, 0.0, 0.0}, y[3];
+        e[j] = 1.0;
+        sandwich3(r, e, y);
+        for (int i = 0; i < 3; ++i) m[3 * i + j] = y[i];
+    }
+    return static_cast<float>(m[0] * (m[4] * m[8] - m[5] * m[7]) - m[1] * (m[3] * m[8] - m[5] * m[6]) +
+                              m[2] * (m[3] * m[7] - m[4] * m[6]));
+}
+
+static void make_rotors(int d, uint64_t seed, std::vector<float>* rotors, std::vector<float>* mats) {
+    const int g = (d + 2) / 3;
+    const std::vector<double> z = normals(seed, kTagRotors, 3 * static_cast<size_t>(g));
+    rotors->assign(4 * g, 0.0f);
+    mats->assign(9 * g, 0.0f);
+    for (int i = 0; i < g; ++i) {
+        const double b12 = z[3 * i], b13 = z[3 * i + 1], b23 = z[3 * i + 2];
+        // exp(B) = cos|b| + sin|b|/|b| B, then divide by sqrt(<R R~>_0)
+        const double th = std::sqrt(b12 * b12 + b13 * b13 + b23 * b23);
+        const double k = th > 0.0 ? std::sin(th) / th : 1.0;
+        double r[4] = {std::cos(th), k * b12, k * b13, k * b23};
+        const double n2 = r[0] * r[0] + r[1] * r[1] + r[2] * r[2] + r[3] * r[3];
+        const double inv = std::sqrt(n2);
+        float rf[4];
+        for (int c = 0; c < 4; ++c) {
+            rf[c] = to_f32(r[c] / inv);
+            (*rotors)[4 * i + c] = rf[c];
+        }
+        double m[9];
+        rotor_matrix_entry_check(rf, m);
+        for (int c = 0; c < 9; ++c) (*mats)[9 * i + c] = to_f32(m[c]);
+    }
+}
+
+// ----------------------------------------------------------------- Lloyd-Max --
+// Coordinate law of a uniform unit vector in R^d:
+//   f(x) = C (1 - x^2)^k on [-1, 1],  k = (d - 3)/2,
+//   C = Gamma(d/2) / (sqrt(pi) Gamma((d - 1)/2)).
+// Cell mass by composite Gauss-Legendre; first moment in closed form:
+//   int_a^b x (1-x^2)^k dx = ((1-a^2)^(k+1) - (1-b^2)^(k+1)) / (2 (k+1)).
+namespace {
+
+struct GaussLegendre {
+    std::vector<double> x, w;
+    explicit GaussLegendre(int n) : x(n), w(n) {
+        // Newton iteration on P_n from the Chebyshev-like first guess; the
+        // weight is 2 / ((1 - z^2) P_n'(z)^2) at the converged node.
+        auto legendre = [n](double z, double* dp) {
+            double p0 = 1.0, p1 = z;
+            for (int k = 2; k <= n; ++k) {
+                const double p2 = ((2.0 * k - 1.0) * z * p1 - (k - 1.0) * p0) / k;
+                p0 = p1;
+                p1 = p2;
+            }
+            *dp = n * (z * p1 - p0) / (z * z - 1.0);
+            return p1;
+        };
+        for (int i = 0; i < n; ++i) {
+            double z = std::cos(kPi * (i + 0.75) / (n + 0.5));
+            for (int it = 0; it < 100; ++it) {
+                double dp;
+                const double dz = legendre(z, &dp) / dp;
+                z -= dz;
+                if (std::fabs(dz) <= 1e-15) break;
+            }
+            double dp;
+            legendre(z, &dp);
+            x[i] = z;
+            w[i] = 2.0 / ((1.0 - z * z) * dp * dp);
+        }
+    }
+};
+
+struct SphereLaw {
+    int d;
+    double k, logc;
+    GaussLegendre gl{24};
+    explicit SphereLaw(int dim) : d(dim), k((dim - 3) / 2.0) {
+        logc = std::lgamma(dim / 2.0) - 0.5 * std::log(kPi) - std::lgamma((dim - 1) / 2.0);
+    }
+    double mass(double a, double b) const {
+        if (b <= a) return 0.0;
+        const int panels = std::max(1, static_cast<int>(std::ceil((b - a) / 0.005)));
+        const double h = (b - a) / panels;
+        double sum = 0.0;
+        for (int p = 0; p < panels; ++p) {
+            const double mid = a + (p + 0.5) * h;
+            double ps = 0.0;
+            for (size_t i = 0; i < gl.x.size(); ++i) {
+                const double x = mid + 0.5 * h * gl.x[i];
+                const double u = 1.0 - x * x;
+                ps += gl.w[i] * (u > 0.0 ? std::pow(u, k) : 0.0);
+            }
+            sum += 0.5 * h * ps;
+        }
+        return std::exp(logc) * sum;
+    }
+    double first_moment(double a, double b) const {
+        const double kp1 = k + 1.0;
+        const double ua = std::max(0.0, 1.0 - a * a), ub = std::max(0.0, 1.0 - b * b);
+        return std::exp(logc) * (std::pow(ua, kp1) - std::pow(ub, kp1)) / (2.0 * kp1);
+    }
+};
+
+}  // namespace
+
+void lloyd_max_unit_sphere(int d, int bits, std::vector<double>* centroids, std::vector<double>* boundaries) {
+    static std::mutex mu;
+    static std::map<std::pair<int, int>, std::pair<std::vector<double>, std::vector<double>>> cache;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        auto it = cache.find({d, bits});
+        if (it != cache.end()) {
+            *centroids = it->second.first;
+            *boundaries = it->second.second;
+            return;
+        }
+    }
+    const int levels = 1 << bits;
+    const SphereLaw law(d);
+    const double sigma = 1.0 / std::sqrt(static_cast<double>(d));
+    std::vector<double> c(levels), t(levels - 1), nc(levels);
+    for (int i = 0; i < levels; ++i) c[i] = sigma * (-2.0 + 4.0 * (i + 0.5) / levels);
+    for (int iter = 0; iter < 200000; ++iter) {
+        for (int i = 0; i + 1 < levels; ++i) t[i] = 0.5 * (c[i] + c[i + 1]);
+        for (int i = 0; i < levels; ++i) {
+            const double lo = i == 0 ? -1.0 : t[i - 1];
+            const double hi = i == levels - 1 ? 1.0 : t[i];
+            nc[i] = law.first_moment(lo, hi) / law.mass(lo, hi);
+        }
+        // the density is symmetric: keep the iterate exactly antisymmetric
+        double delta = 0.0;
+        std::vector<double> sym(levels);
+        for (int i = 0; i < levels; ++i) {
+            sym[i] = 0.5 * (nc[i] - nc[levels - 1 - i]);
+            delta = std::max(delta, std::fabs(sym[i] - c[i]));
+        }
+        c.swap(sym);
+        if (delta < 1e-15) break;
+    }
+    for (int i = 0; i + 1 < levels; ++i) t[i] = 0.5 * (c[i] + c[i + 1]);
+    *centroids = c;
+    *boundaries = t;
+    std::lock_guard<std::mutex> lock(mu);
+    cache[{d, bits}] = {c, t};
+}
+
+// ------------------------------------------------------------ Householder --
+// G (n x n, row-major) = Q R with Householder reflections; then column j of
+// Q is negated where R_jj < 0, so that diag(R) > 0 and Q is unique.
+void householder_q(const std::vector<double>& g, int n, std::vector<double>* qout) {
+    std::vector<double> a(g);
+    std::vector<std::vector<double>> vs(n);
+    std::vector<double> rdiag(n);
+    for (int j = 0; j < n; ++j) {
+        double norm2 = 0.0;
+        for (int i = j; i < n; ++i) norm2 += a[i * n + j] * a[i * n + j];
+        const double norm = std::sqrt(norm2);
+        const double x0 = a[j * n + j];
+        const double alpha = x0 >= 0.0 ? -norm : norm;
+        std::vector<double> v(n - j);
+        for (int i = j; i < n; ++i) v[i - j] = a[i * n + j];
+        v[0] -= alpha;
+        double vn2 = 0.0;
+        for (double e : v) vn2 += e * e;
+        if (vn2 > 0.0) {
+            const double vinv = 1.0 / std::sqrt(vn2);
+            for (double& e : v) e *= vinv;
+            for (int c = j; c < n; ++c) {
+                double dot = 0.0;
+                for (int i = j; i < n; ++i) dot += v[i - j] * a[i * n + c];
+                for (int i = j; i < n; ++i) a[i * n + c] -= 2.0 * v[i - j] * dot;
+            }
+        }
+        rdiag[j] = a[j * n + j];
+        vs[j] = std::move(v);
+    }
+    // Q = H_0 H_1 ... H_{n-1}: apply to the identity from the last reflector.
+    std::vector<double> q(static_cast<size_t>(n) * n, 0.0);
+    for (int i = 0; i < n; ++i) q[i * n + i] = 1.0;
+    for (int j = n - 1; j >= 0; --j) {
+        const std::vector<double>& v = vs[j];
+        for (int c = 0; c < n; ++c) {
+            double dot = 0.0;
+            for (int i = j; i < n; ++i) dot += v[i - j] * q[i * n + c];
+            for (int i = j; i < n; ++i) q[i * n + c] -= 2.0 * v[i - j] * dot;
+        }
+    }
+    for (int j = 0; j < n; ++j)
+        if (rdiag[j] < 0.0)
+            for (int i = 0; i < n; ++i) q[i * n + j] = -q[i * n + j];
+    *qout = std::move(q);
+}
+
+// --------------------------------------------------------------- half RNE --
+uint16_t double_to_half_rne(double x) {
+    uint64_t bits;
+    std::memcpy(&bits, &x, sizeof bits);
+    const uint16_t sign = static_cast<uint16_t>((bits >> 63) << 15);
+    const double a = std::fabs(x);
+    if (std::isnan(x)) return sign | 0x7E00;
+    if (a >= 65520.0) return sign | 0x7C00;                 // rounds to infinity
+    if (a < 0x1p-14) {                                      // subnormal range
+        const double q = std::nearbyint(a * 0x1p24);        // exact scaling, RNE
+        return sign | static_cast<uint16_t>(q);             // q == 1024 is the smallest normal
+    }
+    int e2;
+    std::frexp(a, &e2);                                     // a = f 2^e2, f in [0.5, 1)
+    int e = e2 - 1;                                         // a in [2^e, 2^(e+1))
+    double m = std::nearbyint(std::ldexp(a, 10 - e));       // [1024, 2048]
+    if (m >= 2048.0) {
+        m = 1024.0;
+        ++e;
+    }
+    if (e > 15) return sign | 0x7C00;
+    return sign | static_cast<uint16_t>(((e + 15) << 10) | (static_cast<int>(m) - 1024));
+}
+
+// ----------------------------------------------------------------- tables --
+int make_tables(int d, int bits, uint64_t seed, int mode, Tables* out, std::string* err) {
+    Layout lay;
+    const int rc = make_layout(d, bits, mode, &lay, err);
+    if (rc) return rc;
+    Tables t;
+    t.lay = lay;
+    std::vector<double> c, b;
+    lloyd_max_unit_sphere(d, lay.mse_bits, &c, &b);
+    t.centroids.resize(c.size());
+    t.boundaries.resize(b.size());
+    for (size_t i = 0; i < c.size(); ++i) t.centroids[i] = to_f32(c[i]);
+    for (size_t i = 0; i < b.size(); ++i) t.boundaries[i] = to_f32(b[i]);
+    if (mode & kModeDense) {
+        const std::vector<double> g = normals(seed, kTagPi, static_cast<size_t>(d) * d);
+        std::vector<double> q;
+        householder_q(g, d, &q);
+        t.pi.resize(q.size());
+        for (size_t i = 0; i < q.size(); ++i) t.pi[i] = to_f32(q[i]);
+    } else {
+        make_rotors(d, seed, &t.rotors, &t.rotmats);
+    }
+    if (mode & kModeQjl) {
+        const std::vector<double> z = normals(seed, kTagS, static_cast<size_t>(kQjlRows) * d);
+        t.s.resize(z.size());
+        for (size_t i = 0; i < z.size(); ++i) t.s[i] = double_to_half_rne(z[i]);
+    }
+    *out = std::move(t);
+    return 0;
+}
+
+}  // namespace rqh

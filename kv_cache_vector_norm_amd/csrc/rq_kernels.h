@@ -1,0 +1,75 @@
+// Launchers of the device kernels (called by the C ABI layer).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rqk {
+
+// Device-resident tables of a rotor session.
+struct RotorTables {
+    const float* rotmat;     // [43][9]
+    const float* thr;        // [L-1]
+    const float* cent;       // [L]
+    const uint16_t* s_rows;  // [128][128] halves (QJL)
+    const uint16_t* s_cols;  // [128][128] halves, S^T (QJL)
+    float qjl_scale;
+    int mse_bits;
+    bool qjl;
+};
+
+// Device-resident tables of a dense (TurboQuant) session.  Pi is stored as
+// two half matrices, Pi = (hi + lo * 2^-11) / 16, in both layouts.
+struct DenseTables {
+    const uint16_t* pi_hi;   // [128][128] row-major
+    const uint16_t* pi_lo;
+    const uint16_t* pit_hi;  // transposed
+    const uint16_t* pit_lo;
+    const float* thr;
+    const float* cent;
+    const uint16_t* s_rows;
+    const uint16_t* s_cols;
+    float qjl_scale;
+    int mse_bits;
+    bool qjl;
+};
+
+struct ScoreTables {
+    bool dense;
+    RotorTables rot;
+    DenseTables den;
+    int mse_bits;
+    bool qjl;
+    float qjl_scale;
+};
+
+// Bytes of staged query data per query row (rotated query and S q as exact
+// half pairs plus two scales), see rq_score.hip, and the number of query rows
+// one scoring launch stages (RQ_SCORE_CHUNK of rq.h).
+constexpr size_t kScoreQueryBytes = 1408;
+constexpr int kScoreChunkRows = 4096;
+
+hipError_t rotor_quantize(const RotorTables& t, const void* x, bool in_f16, int64_t ldx_bytes, int64_t n,
+                          uint32_t* codes, uint16_t* norms, uint32_t* signs, uint16_t* rnorms, void* y, bool out_f16,
+                          int64_t ldy_bytes, bool roundtrip, hipStream_t s);
+
+hipError_t rotor_dequantize(const RotorTables& t, const uint32_t* codes, const uint16_t* norms, const uint32_t* signs,
+                            const uint16_t* rnorms, int64_t n, void* y, bool out_f16, int64_t ldy_bytes,
+                            hipStream_t s);
+
+hipError_t dense_quantize(const DenseTables& t, const void* x, bool in_f16, int64_t ldx_bytes, int64_t n,
+                          uint32_t* codes, uint16_t* norms, uint32_t* signs, uint16_t* rnorms, void* y, bool out_f16,
+                          int64_t ldy_bytes, bool roundtrip, hipStream_t s);
+
+hipError_t dense_dequantize(const DenseTables& t, const uint32_t* codes, const uint16_t* norms, const uint32_t* signs,
+                            const uint16_t* rnorms, int64_t n, void* y, bool out_f16, int64_t ldy_bytes,
+                            hipStream_t s);
+
+// Scores hq query rows (group rows per KV head) against t keys per KV head;
+// KV head j (0-based within this call) reads record rows
+// (kv_head0 + j) * kv_stride + [0, t).  ws is the session's query workspace.
+hipError_t score(const ScoreTables& t, const float* q, int hq, int group, const uint32_t* codes,
+                 const uint16_t* norms, const uint32_t* signs, const uint16_t* rnorms, int64_t tkeys,
+                 int64_t kv_stride, int kv_head0, void* ws, float* scores, int64_t ld_scores, hipStream_t s);
+
+}  // namespace rqk

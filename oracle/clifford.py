@@ -10,6 +10,8 @@ Everything here is float64 and uses the full 8x8 product; nothing exploits
 sparsity.  The sparse, matrix or quaternion forms are checked against this
 module by the tests, never the other way round.
 """
+import math
+
 import numpy as np
 
 # Basis order of the pages, as bitmasks over (e1, e2, e3).
@@ -87,13 +89,15 @@ def rotor_from_bivector(b12, b13, b23):
     B squares to -|b|^2, so exp(B) = cos|b| + (sin|b| / |b|) B.  The result
     is then divided by sqrt(<R R~>_0) so that R R~ = 1 holds to rounding.
     This is the reading of "normalized random bivector exponentials" used
-    for the rotor tables.
+    for the rotor tables.  Scalar libm functions are used (``math``), so the
+    float64 values are those of the C library.
     """
-    th = np.sqrt(b12 * b12 + b13 * b13 + b23 * b23)
-    k = np.sin(th) / th if th > 0.0 else 1.0
-    r = rotor(np.cos(th), k * b12, k * b13, k * b23)
+    b12, b13, b23 = float(b12), float(b13), float(b23)
+    th = math.sqrt(b12 * b12 + b13 * b13 + b23 * b23)
+    k = math.sin(th) / th if th > 0.0 else 1.0
+    r = rotor(math.cos(th), k * b12, k * b13, k * b23)
     n2 = gp(r, reverse(r))[0]
-    return r / np.sqrt(n2)
+    return r / math.sqrt(n2)
 
 
 def sandwich(r, v):

@@ -56,7 +56,7 @@ def _gauss_cell_moments(lo, hi, sigma):
     return mass, first
 
 
-def lloyd_max(levels, moments, support, init, tol=1e-14, max_iter=200000):
+def lloyd_max(levels, moments, support, init, tol=1e-15, max_iter=200000):
     """Lloyd iteration for a symmetric density.
 
     `moments(lo, hi)` returns arrays (mass, first moment) per cell.  Starting
@@ -82,7 +82,7 @@ def lloyd_max(levels, moments, support, init, tol=1e-14, max_iter=200000):
     return c, t, it + 1
 
 
-def beta_codebook(bits, d=128, tol=1e-14, init_scale=1.0):
+def beta_codebook(bits, d=128, tol=1e-15, init_scale=1.0):
     """Float64 Lloyd-Max centroids and midpoint boundaries, 2^bits levels.
 
     The start is the Gaussian N(0, 1/d) quantiles at (k + 1/2) / L, scaled by
@@ -95,7 +95,7 @@ def beta_codebook(bits, d=128, tol=1e-14, init_scale=1.0):
     return c, t
 
 
-def gaussian_codebook(bits, d_eff, tol=1e-14):
+def gaussian_codebook(bits, d_eff, tol=1e-15):
     """Lloyd-Max for N(0, 1/d_eff) (the pre-fix reading of the README)."""
     levels = 1 << bits
     sigma = 1.0 / math.sqrt(d_eff)

@@ -1,0 +1,87 @@
+"""GPU parity of the TurboQuant dense path (tq_quantize / tq_dequantize /
+tq_roundtrip, and scoring with a dense session) against the oracle."""
+import numpy as np
+import pytest
+
+import parity as PR
+from oracle import codec as OC
+from oracle import params as OP
+from kv_cache_vector_norm_amd import workloads as W
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+D = 128
+MODES = [(b, OP.DENSE) for b in (1, 2, 3, 4)] + [(b, OP.DENSE | OP.QJL) for b in (2, 3, 4, 5)]
+
+
+@pytest.fixture(scope="module")
+def K():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import kv_cache_vector_norm_amd as K
+    return K
+
+
+@pytest.mark.parametrize("bits,mode", MODES)
+@pytest.mark.parametrize("n", [1, 65, 1000])
+def test_tq_quantize_parity(K, bits, mode, n):
+    x = W.gaussian(n, seed=40 + n + bits, dtype=np.float16)
+    c = K.Codec(bits=bits, seed=0, mode=mode)
+    rec = c.quantize(torch.from_numpy(x).cuda())
+    torch.cuda.synchronize()
+    codes, norms, signs, rnorms = rec.host()
+    p = OP.Params(D, bits, 0, mode)
+    orec, diag = OC.quantize(p, x.astype(np.float64))
+    excl, _ = PR.compare_codes(p, codes, diag)
+    PR.compare_halves(norms, diag.n, "norms")
+    if mode & OP.QJL:
+        PR.compare_signs(p, signs, diag, excl)
+        PR.compare_halves(rnorms[~excl], diag.gamma[~excl], "rnorms")
+
+
+@pytest.mark.parametrize("bits,mode", [(3, OP.DENSE), (1, OP.DENSE), (3, OP.DENSE | OP.QJL), (5, OP.DENSE | OP.QJL)])
+@pytest.mark.parametrize("in_dtype", [np.float16, np.float32])
+def test_tq_dequant_and_roundtrip(K, bits, mode, in_dtype):
+    n = 333
+    x = W.gaussian(n, seed=41, dtype=in_dtype)
+    c = K.Codec(bits=bits, seed=0, mode=mode)
+    xt = torch.from_numpy(x).cuda()
+    rec, y32 = c.roundtrip(xt, dtype=torch.float32)
+    y16 = c.roundtrip(xt, dtype=torch.float16)[1]
+    d32 = c.dequantize(rec, dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(y32, d32)
+    assert torch.equal(y16, d32.to(torch.float16))
+    p = OP.Params(D, bits, 0, mode)
+    hrec = PR.record_from_host(*rec.host())
+    PR.compare_recon(d32.cpu().numpy(), OC.dequantize(p, hrec), OC.half_value(hrec.norms), "tq dequantize")
+
+
+def test_tq_mse_matches_rq(K):
+    """README 'MSE Quality': TurboQuant and RotorQuant reach the same MSE."""
+    x = W.unit_vectors_c0()
+    out = {}
+    for mode in (OP.MSE, OP.DENSE):
+        c = K.Codec(bits=3, seed=0, mode=mode)
+        _, y = c.roundtrip(torch.from_numpy(x).cuda(), dtype=torch.float32)
+        torch.cuda.synchronize()
+        out[mode] = ((x.astype(np.float64) - y.cpu().numpy()) ** 2).sum(1).mean()
+    assert abs(out[OP.MSE] - 0.034) < 1.5e-3 and abs(out[OP.DENSE] - 0.034) < 1.5e-3
+
+
+@pytest.mark.parametrize("mode", [OP.DENSE, OP.DENSE | OP.QJL])
+def test_tq_score(K, mode):
+    t, hq, group = 700, 16, 8
+    keys = W.gaussian(2 * t, seed=43, dtype=np.float16)
+    q = W.queries(hq, seed=44)
+    c = K.Codec(bits=3, seed=0, mode=mode)
+    rec = c.quantize(torch.from_numpy(keys).cuda())
+    s = c.score(torch.from_numpy(q).cuda(), rec, group, t, t)
+    torch.cuda.synchronize()
+    p = OP.Params(D, 3, 0, mode)
+    hrec = PR.record_from_host(*rec.host())
+    ref = OC.score_gqa(p, q.astype(np.float64), hrec, group, t, t)
+    qn = np.linalg.norm(q.astype(np.float64), axis=1)
+    nh = np.stack([OC.half_value(hrec.norms[(h // group) * t:(h // group) * t + t]) for h in range(hq)])
+    assert np.all(np.abs(s.cpu().numpy() - ref) <= PR.SCORE_TOL * qn[:, None] * nh)

@@ -1,0 +1,129 @@
+"""CPU checks of the C ABI library: it loads, exports every declared symbol,
+reports layouts, builds the same parameter tables as the oracle, and rejects
+bad arguments without touching a GPU."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import params as OP
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def K():
+    import kv_cache_vector_norm_amd as K
+    return K
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "rq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b((?:rq|tq)_[a-z_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported(K):
+    names = declared_functions()
+    assert len(names) >= 15
+    lib = ctypes.CDLL(K.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(K.EXPORTS)
+
+
+def test_layouts(K):
+    widths = {(b, m): K.rq_layout(128, b, m) for b in (1, 2, 3, 4) for m in (K.RQ_MSE, K.RQ_DENSE)}
+    assert [widths[(b, K.RQ_MSE)]["code_words"] for b in (1, 2, 3, 4)] == [5, 9, 13, 17]
+    assert [widths[(b, K.RQ_DENSE)]["code_words"] for b in (1, 2, 3, 4)] == [4, 8, 12, 16]
+    q = K.rq_layout(128, 3, K.RQ_QJL)
+    assert q["mse_bits"] == 2 and q["sign_words"] == 4 and q["record_bytes"] == 9 * 4 + 2 + 16 + 2
+    assert K.rq_layout(128, 3, K.RQ_MSE)["record_bytes"] == 54
+    assert K.rq_layout(128, 3, K.RQ_MSE)["n_groups"] == 43
+
+
+@pytest.mark.parametrize("bits,mode", [(b, OP.MSE) for b in (1, 2, 3, 4)] + [(b, OP.QJL) for b in (2, 3, 4, 5)]
+                         + [(b, OP.DENSE) for b in (2, 3, 4)] + [(3, OP.DENSE | OP.QJL)])
+def test_host_params_match_oracle(K, bits, mode):
+    p = K.rq_host_params(128, bits, 0, mode)
+    o = OP.Params(128, bits, 0, mode)
+
+    def ulps(a, b):
+        a = np.asarray(a, np.float32)
+        b = np.asarray(b, np.float32)
+        return np.abs(a.view(np.int32).astype(np.int64) - b.view(np.int32).astype(np.int64)).max()
+
+    assert ulps(p["centroids"], o.centroids) <= 1
+    assert ulps(p["boundaries"], o.boundaries) <= 1
+    if mode & OP.DENSE:
+        assert ulps(p["pi"], o.pi) <= 1
+        pf = p["pi"].astype(np.float64)
+        assert np.abs(pf @ pf.T - np.eye(128)).max() < 1e-6
+    else:
+        assert ulps(p["rotors"], o.rotors) <= 1
+        assert np.abs(p["rotmats"].astype(np.float64) - OP.rotor_matrices(o.rotors)).max() < 2e-7
+    if mode & OP.QJL:
+        assert np.array_equal(p["s"], o.s.astype(np.float16).view(np.uint16))
+
+
+def test_different_seeds_give_different_tables(K):
+    a = K.rq_host_params(128, 3, 0, K.RQ_QJL)
+    b = K.rq_host_params(128, 3, 1, K.RQ_QJL)
+    assert not np.array_equal(a["rotors"], b["rotors"]) and not np.array_equal(a["s"], b["s"])
+    assert np.array_equal(a["centroids"], b["centroids"])
+
+
+@pytest.mark.parametrize("d,bits,mode,status", [
+    (128, 0, 0, 1), (128, 5, 0, 1), (128, 1, 1, 1), (128, 6, 1, 1), (128, 3, 8, 1), (-1, 3, 0, 1),
+    (64, 3, 0, 2), (256, 3, 1, 2)])
+def test_bad_settings(K, d, bits, mode, status):
+    with pytest.raises(K.RQError) as e:
+        K.rq_layout(d, bits, mode)
+    assert e.value.status == status
+    with pytest.raises(K.RQError) as e:
+        K.rq_host_params(d, bits, 0, mode)
+    assert e.value.status == status
+    assert K.rq_last_error() != ""
+
+
+def test_null_arguments_rejected_before_any_device_work(K):
+    lib = K.lib()
+    assert lib.rq_quantize(None, None, 1, 10, 128, None, None, None, None, None) == K.RQ_EINVAL
+    assert "ctx" in K.rq_last_error()
+    assert lib.rq_dequantize(None, None, None, None, None, 10, None, 1, 128, None) == K.RQ_EINVAL
+    assert lib.rq_roundtrip(None, None, 1, 10, 128, None, None, None, None, None, 1, 128, None) == K.RQ_EINVAL
+    assert lib.rq_score(None, None, 1, 1, None, None, None, None, 10, 10, None, 10, None) == K.RQ_EINVAL
+    assert lib.tq_quantize(None, None, 1, 10, 128, None, None, None, None, None) == K.RQ_EINVAL
+    assert lib.rq_get_layout(None, None) == K.RQ_EINVAL
+    assert lib.rq_layout(128, 3, 0, None) == K.RQ_EINVAL
+    lib.rq_free(None)
+
+
+def test_init_without_device_fails_cleanly(K):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    h = ctypes.c_void_p(12345)
+    rc = K.lib().rq_init(128, 3, 0, 0, ctypes.byref(h))
+    assert rc in (K.RQ_EHIP, K.RQ_ENOMEM) and h.value is None
+    rc = K.lib().rq_init(64, 3, 0, 0, ctypes.byref(h))
+    assert rc == K.RQ_EUNSUPPORTED and h.value is None
+
+
+def test_version(K):
+    assert "gfx950" in K.rq_version()
+
+
+def test_single_hip_runtime_in_process():
+    """librq.so and torch must share one HIP runtime (torch owns the memory
+    and streams the library is handed)."""
+    import subprocess
+    import sys
+    code = ("import kv_cache_vector_norm_amd, torch, re; "
+            "m = open('/proc/self/maps').read(); "
+            "print(len(set(re.findall(r'/\\S*libamdhip64\\S*', m))))")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip() == "1"
