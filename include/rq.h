@@ -145,7 +145,8 @@ int rq_get_params(const rq_ctx* ctx, rq_params_host_t* out);
  * hyper.ai Algorithm 2: residual r = x_u - Q_mse^-1(Q_mse(x_u)), signs of
  * S r, ||r||).
  *   x      [n][ldx] elements of x_dtype (RQ_F16 or RQ_F32), 16-byte aligned,
- *          ldx >= 128 and ldx * element size a multiple of 16 bytes.
+ *          ldx >= 128 and ldx * element size a multiple of 16 bytes and at
+ *          most 2^26 bytes.
  *   n      vectors (n == 0 is a no-op returning RQ_OK).
  *   codes  [n][code_words], norms [n]; signs [n][4] and rnorms [n] must be
  *          non-NULL exactly when the session has RQ_QJL.

@@ -68,9 +68,12 @@ struct rq_ctx {
     float* rotmat = nullptr;
     float* thr = nullptr;
     float* cent = nullptr;
+    rqk::u32x4_t* bins = nullptr;
     // QJL
     uint16_t* s_rows = nullptr;
     uint16_t* s_cols = nullptr;
+    uint16_t* s_fwd = nullptr;
+    uint16_t* s_back = nullptr;
     // dense (TurboQuant): Pi split into exact half pairs, both layouts
     uint16_t* pi_hi = nullptr;
     uint16_t* pi_lo = nullptr;
@@ -180,11 +183,23 @@ int rq_init(int d, int bits, uint64_t seed, int mode, rq_ctx** out) {
         return hipMemcpy(*dst, src, bytes, hipMemcpyHostToDevice);
     };
     // derived half tables
-    std::vector<uint16_t> s_cols, pi_hi, pi_lo, pit_hi, pit_lo;
+    std::vector<uint16_t> s_cols, s_fwd, s_back, pi_hi, pi_lo, pit_hi, pit_lo;
     if (mode & RQ_QJL) {
         s_cols.resize(t.s.size());
         for (int j = 0; j < n; ++j)
             for (int i = 0; i < n; ++i) s_cols[i * n + j] = t.s[j * n + i];
+        // MFMA layouts of the rotor kernels: accumulator row p of a 32-row M
+        // tile (lane half h = bit 2 of p) holds sign index / coordinate
+        // perm_row(p); K slot k of a 32-wide K pair feeds sign index perm_k(k).
+        auto perm_row = [](int p) { return (p & ~31) | (((p >> 2) & 1) << 4) | (((p >> 3) & 3) << 2) | (p & 3); };
+        auto perm_k = [](int k) { return (k & ~31) | (((k >> 3) & 1) << 4) | (((k >> 4) & 1) << 3) | (k & 7); };
+        s_fwd.resize(t.s.size());
+        s_back.resize(t.s.size());
+        for (int p = 0; p < n; ++p)
+            for (int k = 0; k < n; ++k) {
+                s_fwd[p * n + k] = t.s[perm_row(p) * n + k];
+                s_back[p * n + k] = t.s[perm_k(k) * n + perm_row(p)];
+            }
     }
     if (mode & RQ_DENSE) {
         // Pi = hi + lo exactly enough: hi = half(Pi * 2^4), lo = half((Pi * 2^4 - hi) * 2^11);
@@ -215,9 +230,13 @@ int rq_init(int d, int bits, uint64_t seed, int mode, rq_ctx** out) {
         }
         if ((e = upload(reinterpret_cast<void**>(&ctx->thr), t.boundaries.data(), t.boundaries.size() * 4)) != hipSuccess) break;
         if ((e = upload(reinterpret_cast<void**>(&ctx->cent), t.centroids.data(), t.centroids.size() * 4)) != hipSuccess) break;
+        static_assert(sizeof(rqh::BinEntry) == sizeof(rqk::u32x4_t) && rqh::kBins == rqk::kBinSlots, "slot table");
+        if ((e = upload(reinterpret_cast<void**>(&ctx->bins), t.bins.data(), t.bins.size() * sizeof(rqh::BinEntry))) != hipSuccess) break;
         if (mode & RQ_QJL) {
             if ((e = upload(reinterpret_cast<void**>(&ctx->s_rows), t.s.data(), t.s.size() * 2)) != hipSuccess) break;
             if ((e = upload(reinterpret_cast<void**>(&ctx->s_cols), s_cols.data(), s_cols.size() * 2)) != hipSuccess) break;
+            if ((e = upload(reinterpret_cast<void**>(&ctx->s_fwd), s_fwd.data(), s_fwd.size() * 2)) != hipSuccess) break;
+            if ((e = upload(reinterpret_cast<void**>(&ctx->s_back), s_back.data(), s_back.size() * 2)) != hipSuccess) break;
         }
         if (mode & RQ_DENSE) {
             if ((e = upload(reinterpret_cast<void**>(&ctx->pi_hi), pi_hi.data(), pi_hi.size() * 2)) != hipSuccess) break;
@@ -259,6 +278,8 @@ static int check_vectors(const void* p, int dtype, int64_t ld, const char* what,
     if (ld < rqh::kDim) return fail(RQ_EINVAL, std::string(fn) + ": leading dimension of " + what + " < 128");
     if ((ld * static_cast<int64_t>(elem_size(dtype))) % 16 != 0)
         return fail(RQ_EINVAL, std::string(fn) + ": row pitch of " + what + " must be a multiple of 16 bytes");
+    if (ld * static_cast<int64_t>(elem_size(dtype)) > (int64_t(1) << 26))
+        return fail(RQ_EINVAL, std::string(fn) + ": row pitch of " + what + " exceeds 2^26 bytes");
     return RQ_OK;
 }
 
@@ -279,8 +300,13 @@ static rqk::RotorTables rotor_tables(const rq_ctx* c) {
     t.rotmat = c->rotmat;
     t.thr = c->thr;
     t.cent = c->cent;
+    t.bins = c->bins;
+    t.bin_a = rqh::kBinA;
+    t.bin_b = c->host.bin_b;
     t.s_rows = c->s_rows;
     t.s_cols = c->s_cols;
+    t.s_fwd = c->s_fwd;
+    t.s_back = c->s_back;
     t.qjl_scale = static_cast<float>(std::sqrt(M_PI / 2.0) / rqh::kQjlRows);
     t.mse_bits = c->host.lay.mse_bits;
     t.qjl = c->host.lay.mode & RQ_QJL;

@@ -20,12 +20,25 @@ typedef _Float16 f16;
 typedef f16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef f16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kD = 128;        // vector dimension
 constexpr int kGroups = 43;    // ceil(128 / 3) rotor groups
 constexpr int kRotCoords = 129;
 constexpr int kWave = 64;
 constexpr int kTileBytes = 64 * 256;   // one wave's LDS transpose tile
+
+// Compile-time loop: f(integral_constant<int, I>) for I in [I0, N).  The
+// per-group loops use it instead of #pragma unroll, whose size limit a long
+// body exceeds, so that every register-array index is a constant.
+template <int I, int N, class F>
+__device__ __attribute__((always_inline)) inline void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
 
 // ------------------------------------------------------------------ LDS --
 // 64 rows x 16 chunks of 16 B.  Chunk c of row r lives in slot
@@ -81,6 +94,19 @@ __device__ __forceinline__ uint32_t f2h(float x) {   // round to nearest even
 }
 __device__ __forceinline__ uint32_t pack2h(float a, float b) { return f2h(a) | (f2h(b) << 16); }
 
+// Two floats -> two halves (round to nearest even) in one v_cvt_pk_f16_f32.
+__device__ __forceinline__ uint32_t cvt_pk(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), f16x2));
+}
+
+// Exact split of a float pair: (a, b) ~= hi + lo, hi = half(a, b) and lo the
+// halves of the fp32 residuals a - hi (exact) rounded to nearest even.
+__device__ __forceinline__ void split_pair(float a, float b, uint32_t* hi, uint32_t* lo) {
+    const uint32_t h = cvt_pk(a, b);
+    *hi = h;
+    *lo = cvt_pk(a - h2f(h & 0xFFFFu), b - h2f(h >> 16));
+}
+
 // Exact split of a float into two halves: x ~= hi + lo with the residual of
 // hi's rounding kept in lo (both round to nearest even).
 __device__ __forceinline__ void split_h(float x, uint32_t* hi, uint32_t* lo) {
@@ -100,31 +126,52 @@ __device__ __forceinline__ void split_h11(float x, uint32_t* hi, uint32_t* lo11)
 }
 
 // -------------------------------------------------------------- tiles --
-// Reads 64 rows of `row_bytes` (a multiple of 256) starting at byte offset
-// `col_off` of each row into the wave's LDS tile (256 bytes per row); rows at
-// or beyond n are zero.
+// Global traffic goes through raw buffer instructions: a per-tile descriptor
+// (base address in SGPRs, byte range = the rows that exist), a per-lane
+// 32-bit offset fixed for the kernel and a uniform per-instruction offset.
+// Accesses beyond the range read 0 and drop stores, which handles the
+// ragged last tile without per-row branches.  Row pitches are at most 2^26
+// bytes, so every offset of a 64-row tile fits in 32 bits.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;   // gfx9 buffer descriptor dword 3
+constexpr int kNonTemporal = 2;          // aux bits: nt
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), static_cast<short>(0), static_cast<int>(bytes),
+                                             kRsrcWord3);
+}
+// Byte range of `rows_left` rows of `row_bytes` (all of 32-bit space for a full tile).
+__device__ __forceinline__ uint32_t tile_range(int64_t rows_left, int64_t row_bytes) {
+    return rows_left >= 64 ? 0xFFFFFFFFu : static_cast<uint32_t>(rows_left * row_bytes);
+}
+
+// Reads 64 rows of 256 bytes (starting at byte offset `col_off` of each row)
+// into the wave's LDS tile; rows at or beyond n are zero.  Lane l moves
+// chunk l % 16 of rows 4 it + l / 16.
 __device__ __forceinline__ void tile_load(const char* __restrict__ src, int64_t ld_bytes, int64_t base,
                                           int64_t n, int col_off, u32x4* __restrict__ tile, int l) {
     wave_lds_sync();
+    const int rr = l >> 4, c = l & 15;
+    const uint32_t voff = static_cast<uint32_t>(rr) * static_cast<uint32_t>(ld_bytes) + static_cast<uint32_t>(c * 16);
+    const rsrc_t rs = make_rsrc(src + base * ld_bytes + col_off, tile_range(n - base, ld_bytes));
+    const int step = static_cast<int>(4 * ld_bytes);
 #pragma unroll
     for (int it = 0; it < 16; ++it) {
-        const int q = it * 64 + l, r = q >> 4, c = q & 15;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (base + r < n)
-            v = __builtin_nontemporal_load(
-                reinterpret_cast<const u32x4*>(src + (base + r) * ld_bytes + col_off + c * 16));
-        tile[swz(r, c)] = v;
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, it * step, kNonTemporal);
+        tile[swz(4 * it + rr, c)] = v;
     }
 }
 
 __device__ __forceinline__ void tile_store(char* __restrict__ dst, int64_t ld_bytes, int64_t base, int64_t n,
                                            int col_off, const u32x4* __restrict__ tile, int l) {
+    const int rr = l >> 4, c = l & 15;
+    const uint32_t voff = static_cast<uint32_t>(rr) * static_cast<uint32_t>(ld_bytes) + static_cast<uint32_t>(c * 16);
+    const rsrc_t rs = make_rsrc(dst + base * ld_bytes + col_off, tile_range(n - base, ld_bytes));
+    const int step = static_cast<int>(4 * ld_bytes);
 #pragma unroll
     for (int it = 0; it < 16; ++it) {
-        const int q = it * 64 + l, r = q >> 4, c = q & 15;
-        const u32x4 v = tile[swz(r, c)];
-        if (base + r < n)
-            __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst + (base + r) * ld_bytes + col_off + c * 16));
+        const u32x4 v = tile[swz(4 * it + rr, c)];
+        __builtin_amdgcn_raw_buffer_store_b128(v, rs, voff, it * step, kNonTemporal);
     }
 }
 
@@ -138,11 +185,11 @@ __device__ __forceinline__ void words_store(uint32_t* __restrict__ dst, int64_t 
 #pragma unroll
     for (int k = 0; k < WORDS; ++k) stage[l * WORDS + k] = w[k];
     wave_lds_sync();
-    const int64_t limit = (n - base) * WORDS;
+    const rsrc_t rs = make_rsrc(dst + base * WORDS, tile_range(n - base, 4 * WORDS));
 #pragma unroll
     for (int it = 0; it < WORDS; ++it) {
-        const int q = it * 64 + l;
-        if (q < limit) dst[base * WORDS + q] = stage[q];
+        const uint32_t v = stage[it * 64 + l];
+        __builtin_amdgcn_raw_buffer_store_b32(v, rs, static_cast<uint32_t>(4 * l), 256 * it, kNonTemporal);
     }
     wave_lds_sync();
 }
@@ -150,17 +197,25 @@ __device__ __forceinline__ void words_store(uint32_t* __restrict__ dst, int64_t 
 template <int WORDS>
 __device__ __forceinline__ void words_load(const uint32_t* __restrict__ src, int64_t base, int64_t n,
                                            uint32_t (&w)[WORDS], uint32_t* __restrict__ stage, int l) {
-    const int64_t limit = (n - base) * WORDS;
+    const rsrc_t rs = make_rsrc(src + base * WORDS, tile_range(n - base, 4 * WORDS));
     wave_lds_sync();
 #pragma unroll
-    for (int it = 0; it < WORDS; ++it) {
-        const int q = it * 64 + l;
-        stage[q] = q < limit ? src[base * WORDS + q] : 0u;
-    }
+    for (int it = 0; it < WORDS; ++it)
+        stage[it * 64 + l] = __builtin_amdgcn_raw_buffer_load_b32(rs, static_cast<uint32_t>(4 * l), 256 * it, kNonTemporal);
     wave_lds_sync();
 #pragma unroll
     for (int k = 0; k < WORDS; ++k) w[k] = stage[l * WORDS + k];
     wave_lds_sync();
+}
+
+// One 16-bit value per lane (norms): lanes beyond n are dropped / read 0.
+__device__ __forceinline__ void half_store(uint16_t* __restrict__ dst, int64_t base, int64_t n, uint32_t v, int l) {
+    const rsrc_t rs = make_rsrc(dst + base, tile_range(n - base, 2));
+    __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(v), rs, static_cast<uint32_t>(2 * l), 0, kNonTemporal);
+}
+__device__ __forceinline__ uint32_t half_load(const uint16_t* __restrict__ src, int64_t base, int64_t n, int l) {
+    const rsrc_t rs = make_rsrc(src + base, tile_range(n - base, 2));
+    return __builtin_amdgcn_raw_buffer_load_b16(rs, static_cast<uint32_t>(2 * l), 0, kNonTemporal);
 }
 
 // ------------------------------------------------------------- codes --
@@ -278,6 +333,13 @@ struct VecOutT<true> {
             t[swz(l, i >> 3)] = cur;
         }
     }
+    // coordinates i (even) and i + 1
+    __device__ void set2(int i, float v0, float v1) {
+        pin(v0);
+        pin(v1);
+        cur[(i & 7) >> 1] = cvt_pk(v0, v1);
+        if ((i & 7) == 6) t[swz(l, i >> 3)] = cur;
+    }
     __device__ void store(char* y, int64_t ld_bytes, int64_t base, int64_t n) {
         wave_lds_sync();
         tile_store(y, ld_bytes, base, n, 0, t, l);
@@ -310,6 +372,10 @@ struct VecOutT<false> {
             tile_store(y, ld_bytes, base, n, 0, t, l);
             wave_lds_sync();
         }
+    }
+    __device__ void set2(int i, float v0, float v1) {
+        set(i, v0);
+        set(i + 1, v1);
     }
     __device__ void store(char* yy, int64_t ldb, int64_t b, int64_t nn) {
         wave_lds_sync();

@@ -186,7 +186,7 @@ __global__ __launch_bounds__(WAVES * 64) void tq_quant_kernel(DenseDev P, const 
     if constexpr (QJL) mat_to_lds(P.s_rows, sm.s_rows);
     __syncthreads();
 
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     u32x4* tile = sm.tiles[wave];
     uint32_t* stage = reinterpret_cast<uint32_t*>(tile);
     const int64_t ntiles = (n + 63) / 64;
@@ -390,7 +390,7 @@ __global__ __launch_bounds__(256) void tq_dequant_kernel(DenseDev P, const uint3
     __shared__ float thr_unused[16];
     dense_tables_to_lds<B>(P, ctab, thr_unused);
     __syncthreads();
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     u32x4* tile = tiles[wave];
     uint32_t* stage = reinterpret_cast<uint32_t*>(tile);
     const int64_t ntiles = (n + 63) / 64;

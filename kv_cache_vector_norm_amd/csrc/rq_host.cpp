@@ -8,6 +8,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <limits>
 #include <map>
 #include <mutex>
 #include <utility>
@@ -329,6 +330,58 @@ uint16_t double_to_half_rne(double x) {
     return sign | static_cast<uint16_t>(((e + 15) << 10) | (static_cast<int>(m) - 1024));
 }
 
+// ------------------------------------------------------------------- bins --
+int bin_slot(float y, float bin_b) {
+    const float t = std::fmaf(y, kBinA, bin_b);
+    uint32_t u;
+    std::memcpy(&u, &t, 4);
+    return static_cast<int>((u & 0xFF0u) >> 4);
+}
+
+bool make_bins(Tables* t) {
+    const std::vector<float>& c = t->centroids;
+    const std::vector<float>& b = t->boundaries;
+    const int nb = static_cast<int>(b.size());
+    const float magic = 12582912.0f;   // 1.5 * 2^23: fp32 sums in [2^23, 2^24) are integers
+    // bias 16 * o with o = 128 + k / 16: slot(y) ~ floor(127 y + o)
+    for (int k : {0, 1, -1, 2, -2, 3, -3, 4, -4, 5, -5, 6, -6, 7, -7}) {
+        const float bias = magic + 16.0f * 128.0f + static_cast<float>(k);
+        // no wrap-around for |y| <= 1.001: the integer part stays in [0, 4096)
+        const float lo_t = std::fmaf(-1.001f, kBinA, bias) - magic;
+        const float hi_t = std::fmaf(1.001f, kBinA, bias) - magic;
+        if (lo_t < 0.0f || hi_t > 4095.0f) continue;
+        std::vector<int> owner(kBins, -1);
+        bool ok = true;
+        int prev = -1;
+        for (int i = 0; i < nb && ok; ++i) {
+            const int s = bin_slot(b[i], bias);
+            if (s <= prev || owner[s] >= 0) ok = false;
+            else owner[s] = i;
+            prev = s;
+        }
+        if (!ok) continue;
+        t->bin_b = bias;
+        t->bins.assign(kBins, BinEntry{});
+        uint32_t base = 0;
+        for (int s = 0; s < kBins; ++s) {
+            BinEntry e;
+            e.base = base;
+            e.c_lo = c[base];
+            if (owner[s] >= 0) {
+                e.thr = b[owner[s]];
+                e.c_hi = c[base + 1];
+                ++base;
+            } else {
+                e.thr = std::numeric_limits<float>::infinity();
+                e.c_hi = c[base];
+            }
+            t->bins[s] = e;
+        }
+        return true;
+    }
+    return false;
+}
+
 // ----------------------------------------------------------------- tables --
 int make_tables(int d, int bits, uint64_t seed, int mode, Tables* out, std::string* err) {
     Layout lay;
@@ -342,6 +395,10 @@ int make_tables(int d, int bits, uint64_t seed, int mode, Tables* out, std::stri
     t.boundaries.resize(b.size());
     for (size_t i = 0; i < c.size(); ++i) t.centroids[i] = to_f32(c[i]);
     for (size_t i = 0; i < b.size(); ++i) t.boundaries[i] = to_f32(b[i]);
+    if (!make_bins(&t)) {
+        if (err) *err = "no bin grid separates the codebook boundaries";
+        return 2;
+    }
     if (mode & kModeDense) {
         const std::vector<double> g = normals(seed, kTagPi, static_cast<size_t>(d) * d);
         std::vector<double> q;

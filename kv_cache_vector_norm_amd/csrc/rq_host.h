@@ -23,8 +23,29 @@ struct Layout {
 // Returns 0, 1 (invalid) or 2 (unsupported); fills *out on success.
 int make_layout(int d, int bits, int mode, Layout* out, std::string* err);
 
+// Exact nearest-centroid lookup through a 256-entry table.  The device maps a
+// unit-domain coordinate y to a table slot with one fp32 fused multiply-add
+// whose result, biased by 1.5 * 2^23, is an integer held in the low mantissa
+// bits:  t = fma(y, kBinA, bin_b),  slot = (bits(t) & 0xFF0) / 16.
+// The map is monotone in y, so with every Lloyd-Max boundary assigned (by the
+// same fp32 fma, evaluated here) to its own slot,
+//   #{k : y > t_k} = base[slot] + (y > thr[slot]),
+// exactly for every y; value = y > thr[slot] ? c_hi : c_lo is c[code].
+// Slots are 1/127 wide in y; make_bins picks the bias so no two boundaries
+// share a slot and |y| <= 1.001 never wraps.
+constexpr int kBins = 256;
+constexpr float kBinA = 2032.0f;   // 16 * 127
+struct BinEntry {
+    uint32_t base;
+    float thr, c_lo, c_hi;
+};
+// Slot of y under bias bin_b (the device computation, bit for bit).
+int bin_slot(float y, float bin_b);
+
 struct Tables {
     Layout lay;
+    std::vector<BinEntry> bins;     // [kBins]
+    float bin_b = 0.0f;
     std::vector<float> rotors;      // [G][4] s, b12, b13, b23
     std::vector<float> rotmats;     // [G][9] row-major M, y = M v
     std::vector<float> centroids;   // [L]
@@ -35,6 +56,10 @@ struct Tables {
 
 // Builds every table of (d, bits, seed, mode); returns 0/1/2 as make_layout.
 int make_tables(int d, int bits, uint64_t seed, int mode, Tables* out, std::string* err);
+
+// Fills t->bins and t->bin_b from t->centroids / t->boundaries; returns
+// false if no bias separates the boundaries (not the case for d = 128).
+bool make_bins(Tables* t);
 
 // --- pieces exposed for host tests --------------------------------------
 uint64_t splitmix64_next(uint64_t* state);

@@ -6,13 +6,27 @@
 
 namespace rqk {
 
+// 16-byte table entry as seen by host code
+struct u32x4_t {
+    uint32_t v[4];
+};
+
+// Slots of the quantiser lookup table: entry = {base code, boundary inside
+// the slot (+inf if none), c[base], c[base + 1]}; a unit-domain coordinate y
+// falls in slot (bits(fma(y, bin_a, bin_b)) & 0xFF0) / 16.
+constexpr int kBinSlots = 256;
+
 // Device-resident tables of a rotor session.
 struct RotorTables {
     const float* rotmat;     // [43][9]
     const float* thr;        // [L-1]
     const float* cent;       // [L]
+    const u32x4_t* bins;     // [kBinSlots]
+    float bin_a, bin_b;
     const uint16_t* s_rows;  // [128][128] halves (QJL)
     const uint16_t* s_cols;  // [128][128] halves, S^T (QJL)
+    const uint16_t* s_fwd;   // S with rows permuted for the quantiser's MFMA layout
+    const uint16_t* s_back;  // S^T with rows and columns permuted for the dequantiser
     float qjl_scale;
     int mse_bits;
     bool qjl;

@@ -12,10 +12,16 @@
 // QJL (README Stage 2; blog QJL section; hyper.ai Algorithm 2):
 //   r = x_u - x~_u, gamma = ||r||, sign bits of S r; dequant adds
 //   sqrt(pi/2)/m * gamma * S^T sigma.
-// The rotor matrices and codebook are wave-uniform (scalar loads); S and S^T
-// are half matrices in LDS feeding 32x32x16 MFMAs; the residual enters the
-// MFMA as an exact hi + lo pair of halves (scaled by 2^12), S being exactly
-// representable in half.
+//
+// Mapping: one lane per vector, 64 vectors per wave.  The code of a
+// coordinate and its centroid come from one 16-byte lookup (slot from one
+// fma, then one compare against the boundary inside the slot).  S r runs on
+// 32x32x16 MFMAs issued while the group loop goes on: each 16-coordinate K
+// block of the residual (an exact hi + lo half pair) is multiplied as soon as
+// it is complete.  The rows of S are permuted on the host so that each lane's
+// accumulator holds 16 consecutive sign indices of one vector; sign words are
+// then a chain of v_alignbit on the accumulator sign bits, and the +-1
+// operands of S^T sigma come straight from the accumulators.
 #pragma once
 
 #include "rq_common.cuh"
@@ -23,62 +29,90 @@
 
 namespace rqk {
 
-
-// The 43 rotor matrices (387 wave-uniform floats, more than the SGPR file
-// holds) are staged in LDS once per workgroup and read per group with
-// broadcast DS reads; their address is offset by an opaque zero made inside
-// each loop iteration, so they are not all hoisted into registers.
-constexpr float kResidualScale = 4096.0f;   // 2^12: keeps the residual's lo half normal
+// Working domain of the QJL kernels: every unit-domain quantity (normalised
+// input, rotated coordinates, boundaries, centroids, reconstruction,
+// residual) is carried times 2^12.  The scaling is exact, leaves every
+// comparison and rounding unchanged, and keeps the residual's low half a
+// normal half for the MFMA.  The MSE-only kernels work at scale 1.
+constexpr float kQjlDomain = 4096.0f;
 
 template <int B>
 constexpr int code_words(int coords) { return (coords * B + 31) / 32; }
 
-// 8 sign bits -> eight halves +-1 (bit 1 -> +1), packed in pairs.
-__device__ __forceinline__ u32x4 sigma8(uint32_t byte) {
-    u32x4 r;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const uint32_t b0 = (byte >> (2 * p)) & 1u, b1 = (byte >> (2 * p + 1)) & 1u;
-        r[p] = 0xBC00BC00u ^ (b0 << 15) ^ (b1 << 31);
+// Group in which coordinate 16 kb + 15 (the end of K block kb) is produced,
+// and the K block whose MFMAs are issued during group g (one 32-row M tile
+// per group, in the four groups after the block completes).
+__host__ __device__ constexpr int kb_done(int kb) { return (16 * kb + 15) / 3; }
+__host__ __device__ constexpr int pending_kb(int g) {
+    for (int kb = 0; kb < 7; ++kb)
+        if (g > kb_done(kb) && g <= kb_done(kb) + 4) return kb;
+    return -1;
+}
+static_assert(kb_done(7) == kGroups - 1, "last K block ends in the last group");
+static_assert(kb_done(1) - kb_done(0) > 4 && kb_done(4) - kb_done(3) > 4, "pending K blocks overlap");
+
+// -------------------------------------------------------------- set-up --
+template <bool QJL>
+__device__ __forceinline__ void stage_bins(const u32x4_t* __restrict__ g, u32x4* __restrict__ s) {
+    constexpr float D = QJL ? kQjlDomain : 1.0f;
+    const u32x4* src = reinterpret_cast<const u32x4*>(g);
+    for (int i = threadIdx.x; i < kBinSlots; i += blockDim.x) {
+        const u32x4 e = src[i];
+        const uint32_t e0 = e[0], e1 = e[1], e2 = e[2], e3 = e[3];
+        s[i] = u32x4{e0, __builtin_bit_cast(uint32_t, __builtin_bit_cast(float, e1) * D),
+                     __builtin_bit_cast(uint32_t, __builtin_bit_cast(float, e2) * D),
+                     __builtin_bit_cast(uint32_t, __builtin_bit_cast(float, e3) * D)};
     }
-    return r;
 }
 
-// -------------------------------------------------------------- inputs --
-// The vector's coordinates are read once from the LDS tile into registers
-// (fp16: 16 chunks of 8 halves; fp32: 128 floats in two 256-byte passes).
-template <bool IN_F16>
-struct VecIn;
+// Centroid pairs indexed by two adjacent codes of the bit stream.
+template <int B, bool QJL>
+__device__ __forceinline__ void stage_pairs(const float* __restrict__ cent, f32x2* __restrict__ pairs) {
+    constexpr int L = 1 << B;
+    constexpr float D = QJL ? kQjlDomain : 1.0f;
+    for (int p = threadIdx.x; p < L * L; p += blockDim.x) pairs[p] = f32x2{cent[p & (L - 1)] * D, cent[p >> B] * D};
+}
 
-template <>
-struct VecIn<true> {
-    u32x4 ch[16];
-    __device__ float get(int i) const {
-        const uint32_t w = ch[i >> 3][(i & 7) >> 1];
-        return h2f((i & 1) ? (w >> 16) : (w & 0xFFFFu));
-    }
-    __device__ void load(const char* x, int64_t ld_bytes, int64_t base, int64_t n, u32x4* t, int l) {
+// ------------------------------------------------------------ per lane --
+// Code of y and its centroid (both in the working domain).
+__device__ __forceinline__ uint32_t lut_quant(float y, float ba, float bb, const u32x4* __restrict__ bins,
+                                              float* val) {
+    const uint32_t off = __builtin_bit_cast(uint32_t, __builtin_fmaf(y, ba, bb)) & 0xFF0u;
+    const u32x4 e = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(bins) + off);
+    const uint32_t base = e[0], thr = e[1], lo = e[2], hi = e[3];
+    const bool gt = y > __builtin_bit_cast(float, thr);
+    *val = __builtin_bit_cast(float, gt ? hi : lo);
+    return base + (gt ? 1u : 0u);
+}
+
+// Centroids of codes 2p and 2p + 1.
+template <int B, int W>
+__device__ __forceinline__ f32x2 pair_vals(const uint32_t (&cw)[W], int p, const f32x2* __restrict__ pairs) {
+    constexpr uint32_t mask = (1u << (2 * B)) - 1u;
+    const int bit = 2 * B * p, wi = bit >> 5, off = bit & 31;
+    uint32_t f;
+    if (off + 2 * B <= 32 || wi + 1 >= W) f = cw[wi] >> off;
+    else f = __builtin_amdgcn_alignbit(cw[wi + 1], cw[wi], off);
+    return pairs[f & mask];
+}
+
+template <bool IN_F16>
+__device__ __forceinline__ void load_vec(const char* __restrict__ x, int64_t ld_bytes, int64_t base, int64_t n,
+                                         u32x4* __restrict__ t, int l, float (&v)[kD]) {
+    if constexpr (IN_F16) {
         tile_load(x, ld_bytes, base, n, 0, t, l);
         wave_lds_sync();
 #pragma unroll
-        for (int c = 0; c < 16; ++c) ch[c] = t[swz(l, c)];
-    }
-    // Separates two passes over the coordinates: the second pass converts
-    // again instead of keeping all 128 converted floats of the first alive.
-    __device__ void fence() {
+        for (int c = 0; c < 16; ++c) {
+            const u32x4 q = t[swz(l, c)];
 #pragma unroll
-        for (int c = 0; c < 16; ++c)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) pin_lane(ch[c], e);
-    }
-};
-
-template <>
-struct VecIn<false> {
-    float v[kD];
-    __device__ float get(int i) const { return v[i]; }
-    __device__ void fence() {}
-    __device__ void load(const char* x, int64_t ld_bytes, int64_t base, int64_t n, u32x4* t, int l) {
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t w = q[e];
+                v[8 * c + 2 * e] = h2f(w & 0xFFFFu);
+                v[8 * c + 2 * e + 1] = h2f(w >> 16);
+            }
+        }
+    } else {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             tile_load(x, ld_bytes, base, n, 256 * h, t, l);
@@ -88,15 +122,14 @@ struct VecIn<false> {
                 const u32x4 q = t[swz(l, c)];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const uint32_t qe = q[e];
-                    v[64 * h + 4 * c + e] = __builtin_bit_cast(float, qe);
+                    const uint32_t w = q[e];
+                    v[64 * h + 4 * c + e] = __builtin_bit_cast(float, w);
                 }
             }
         }
     }
-};
+}
 
-// ----------------------------------------------------- shared stages --
 // y_g = M_g v (forward sandwich as a matrix), x~_g = M_g^T yh (inverse).
 __device__ __forceinline__ void rot_fwd(const float* __restrict__ m, const float v[3], float y[3]) {
 #pragma unroll
@@ -107,80 +140,166 @@ __device__ __forceinline__ void rot_inv(const float* __restrict__ m, const float
     for (int j = 0; j < 3; ++j) x[j] = __builtin_fmaf(m[6 + j], yh[2], __builtin_fmaf(m[3 + j], yh[1], m[j] * yh[0]));
 }
 
-// QJL term of dequantisation for one 32-coordinate M tile: q0/q1 receive
-// (S^T sigma)_i of this lane's own vector for i = 32 mt + own_row(h, r).
-template <int MT>
-__device__ __forceinline__ void qjl_back_tile(const u32x4* __restrict__ st, const uint32_t (&sw)[4], float (&q0)[16],
-                                              float (&q1)[16], int l) {
-    f32x16 a0 = {}, a1 = {};
+// ---------------------------------------------------------------- QJL --
+// Four MFMAs of K block kb against 32-row M tile mt of the permuted S, for
+// the tile's two 32-vector halves; hi then lo of the residual.
+__device__ __forceinline__ void issue_fwd(const u32x4* __restrict__ sf, f32x16 (&acc)[2], int kb, int mt,
+                                          const u32x4& h0, const u32x4& h1, const u32x4& l0, const u32x4& l1,
+                                          int l) {
+    const u32x4 a = mat_frag(sf, 32 * mt + (l & 31), 2 * kb + (l >> 5));
+    acc[0] = mfma(a, h0, acc[0]);
+    acc[0] = mfma(a, l0, acc[0]);
+    acc[1] = mfma(a, h1, acc[1]);
+    acc[1] = mfma(a, l1, acc[1]);
+}
+
+// +-1 halves (sign of z_a, sign of z_b): +1 for z >= 0.  An accumulator that
+// starts at +0 never ends at -0, so the sign bit is exactly [z < 0].
+__device__ __forceinline__ uint32_t sigma_pair(float za, float zb) {
+    const uint32_t t = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, zb), __builtin_bit_cast(uint32_t, za),
+                                             0x070C030Cu);
+    return (t & 0x80008000u) | 0x3C003C00u;
+}
+
+// 16 sign bits (bit e = [z_e >= 0]) -> eight dwords of +-1 half pairs,
+// dword q = (sigma_2q, sigma_2q+1): the same values sigma_pair gives.
+__device__ __forceinline__ void sigma16(uint32_t bits16, u32x4& d0, u32x4& d1) {
+    const uint32_t nb = ~bits16;
+    const uint32_t u = (nb & 0x5555u) | ((nb & 0xAAAAu) << 15);
 #pragma unroll
-    for (int kb = 0; kb < 8; ++kb) {
-        const uint32_t word = sw[kb >> 1] >> (16 * (kb & 1));
-        u32x4 op0, op1;
-        to_operands(sigma8(word & 0xFFu), sigma8((word >> 8) & 0xFFu), &op0, &op1);
-        const u32x4 a = mat_frag(st, 32 * MT + (l & 31), 2 * kb + (l >> 5));
-        a0 = mfma(a, op0, a0);
-        a1 = mfma(a, op1, a1);
+    for (int q = 0; q < 4; ++q) {
+        d0[q] = ((u << (15 - 2 * q)) & 0x80008000u) | 0x3C003C00u;
+        d1[q] = ((u << (7 - 2 * q)) & 0x80008000u) | 0x3C003C00u;
     }
-    from_accumulators(a0, a1, q0, q1);
 }
 
-__device__ __forceinline__ float own_pick(const float (&q0)[16], const float (&q1)[16], int il) {
-    // il in [0, 32): row 8b + w; w < 4 -> q0[4b + w], else q1[4b + w - 4]
-    const int b = il >> 3, w = il & 7;
-    return w < 4 ? q0[4 * b + w] : q1[4 * b + w - 4];
-}
-
-// Dequantise one vector from its record into `out` (unit-domain MSE part,
-// plus the QJL term, times the stored norm).
-template <int B, bool QJL, int W, class Out>
-__device__ __forceinline__ void dequant_vec(const RotorDev& P, const float* __restrict__ lut,
-                                            const u32x4* __restrict__ st, const uint32_t (&cw)[W], float nhat,
-                                            float ghat, const uint32_t (&sw)[4], Out& out, int l) {
-    if constexpr (!QJL) {
+// sigma operands (B side of S^T sigma) of the tile's two vector halves, from
+// the record's sign words of vectors l % 32 and 32 + l % 32.
+__device__ __forceinline__ void sigma_from_words(const u32x4 (&wv)[2], u32x4 (&sig)[2][8], int l) {
+    const int sh = 16 * (l >> 5);
 #pragma unroll
-        for (int g = 0; g < kGroups; ++g) {
-            __builtin_amdgcn_sched_barrier(0);
-            float yh[3], xt[3];
+    for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-            for (int r = 0; r < 3; ++r) yh[r] = lut[get_code<B, W>(cw, 3 * g + r)];
-            rot_inv(P.rotmat + 9 * g, yh, xt);
-#pragma unroll
-            for (int j = 0; j < 3; ++j)
-                if (3 * g + j < kD) out.set(3 * g + j, nhat * xt[j]);
+        for (int mt = 0; mt < 4; ++mt) {
+            const uint32_t w = wv[nt][mt];
+            sigma16((w >> sh) & 0xFFFFu, sig[nt][2 * mt], sig[nt][2 * mt + 1]);
         }
-    } else {
-        const float k = P.qjl_scale * ghat;
-        auto tile = [&](auto mt_c) {
-            constexpr int MT = decltype(mt_c)::value;
-            float q0[16], q1[16];
-            qjl_back_tile<MT>(st, sw, q0, q1, l);
+}
+
+// Reconstruction with the QJL term: out_j = n^ (x~_j + k (S^T sigma)_j),
+// evaluated as (n^ / D) * fma(k D, u_j, D x~_j).  xt holds D x~ (own vector).
+template <class Out>
+__device__ __forceinline__ void back_out(const u32x4* __restrict__ sb, const u32x4 (&sig)[2][8], float kq, float ns,
+                                         const float (&xt)[kD], Out& out, int l) {
 #pragma unroll
-            for (int g = 0; g < kGroups; ++g) {
-                if (3 * g + 2 < 32 * MT || 3 * g >= 32 * MT + 32) continue;
-                __builtin_amdgcn_sched_barrier(0);
-                float yh[3], xt[3];
+    for (int mt = 0; mt < 4; ++mt) {
+        f32x16 a0 = {}, a1 = {};
 #pragma unroll
-                for (int r = 0; r < 3; ++r) yh[r] = lut[get_code<B, W>(cw, 3 * g + r)];
-                rot_inv(P.rotmat + 9 * g, yh, xt);
+        for (int kb = 0; kb < 8; ++kb) {
+            const u32x4 a = mat_frag(sb, 32 * mt + (l & 31), 2 * kb + (l >> 5));
+            a0 = mfma(a, sig[0][kb], a0);
+            a1 = mfma(a, sig[1][kb], a1);
+        }
+        float u0[16], u1[16];
+        from_accumulators(a0, a1, u0, u1);
 #pragma unroll
-                for (int j = 0; j < 3; ++j) {
-                    const int i = 3 * g + j;
-                    if (i < kD && i >= 32 * MT && i < 32 * MT + 32)
-                        out.set(i, nhat * __builtin_fmaf(k, own_pick(q0, q1, i - 32 * MT), xt[j]));
-                }
-            }
-        };
-        tile(std::integral_constant<int, 0>{});
-        tile(std::integral_constant<int, 1>{});
-        tile(std::integral_constant<int, 2>{});
-        tile(std::integral_constant<int, 3>{});
+        for (int r = 0; r < 16; r += 2) {
+            const int j = 32 * mt + r;
+            out.set2(j, ns * __builtin_fmaf(kq, u0[r], xt[j]), ns * __builtin_fmaf(kq, u0[r + 1], xt[j + 1]));
+        }
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+            const int j = 32 * mt + 16 + r;
+            out.set2(j, ns * __builtin_fmaf(kq, u1[r], xt[j]), ns * __builtin_fmaf(kq, u1[r + 1], xt[j + 1]));
+        }
     }
+}
+
+// S^T sigma of the own vector into u (coordinate order).
+__device__ __forceinline__ void back_proj(const u32x4* __restrict__ sb, const u32x4 (&sig)[2][8], float (&u)[kD],
+                                          int l) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        f32x16 a0 = {}, a1 = {};
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) {
+            const u32x4 a = mat_frag(sb, 32 * mt + (l & 31), 2 * kb + (l >> 5));
+            a0 = mfma(a, sig[0][kb], a0);
+            a1 = mfma(a, sig[1][kb], a1);
+        }
+        float u0[16], u1[16];
+        from_accumulators(a0, a1, u0, u1);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            u[32 * mt + r] = u0[r];
+            u[32 * mt + 16 + r] = u1[r];
+        }
+    }
+}
+
+// Record sign words of vectors l % 32 and 32 + l % 32 (through LDS).
+__device__ __forceinline__ void load_sign_pairs(const uint32_t* __restrict__ src, int64_t base, int64_t n,
+                                                u32x4 (&wv)[2], uint32_t* __restrict__ stage, int l) {
+    const rsrc_t rs = make_rsrc(src + base * 4, tile_range(n - base, 16));
+    wave_lds_sync();
+#pragma unroll
+    for (int it = 0; it < 4; ++it)
+        stage[it * 64 + l] = __builtin_amdgcn_raw_buffer_load_b32(rs, static_cast<uint32_t>(4 * l), 256 * it, kNonTemporal);
+    wave_lds_sync();
+    const u32x4* s4 = reinterpret_cast<const u32x4*>(stage);
+    wv[0] = s4[l & 31];
+    wv[1] = s4[32 + (l & 31)];
+    wave_lds_sync();
 }
 
 // ------------------------------------------------------------ kernels --
-// LDS: one 16 KB transpose tile per wave, S (quantize side) and S^T
-// (dequantize side) as needed, the centroid table.
+// Input vector in registers: fp16 kept as packed pairs (converted per use),
+// fp32 as floats.
+template <bool IN_F16>
+struct VecIn;
+
+template <>
+struct VecIn<true> {
+    uint32_t h[kD / 2];
+    __device__ float get(int i) const { return h2f((i & 1) ? (h[i >> 1] >> 16) : (h[i >> 1] & 0xFFFFu)); }
+    __device__ void load(const char* x, int64_t ld_bytes, int64_t base, int64_t n, u32x4* t, int l) {
+        tile_load(x, ld_bytes, base, n, 0, t, l);
+        wave_lds_sync();
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            const u32x4 q = t[swz(l, c)];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t w = q[e];
+                h[4 * c + e] = w;
+            }
+        }
+    }
+};
+
+template <>
+struct VecIn<false> {
+    float v[kD];
+    __device__ float get(int i) const { return v[i]; }
+    __device__ void load(const char* x, int64_t ld_bytes, int64_t base, int64_t n, u32x4* t, int l) {
+        load_vec<false>(x, ld_bytes, base, n, t, l, v);
+    }
+};
+
+// Rotor matrices are read with scalar loads (constant address space) two
+// groups ahead of use.
+typedef __attribute__((address_space(4))) const float* cfloat_ptr;
+__device__ __forceinline__ void load_mat(cfloat_ptr p, float (&m)[9]) {
+#pragma unroll
+    for (int k = 0; k < 9; ++k) m[k] = p[k];
+}
+
+// LDS: the slot table first (LDS address 0, so a slot's byte offset is its
+// address), one 16 KB transpose tile per wave, and (QJL) the permuted S and
+// S^T.  The group loop is software-pipelined: in group g's region the
+// forward rotation and slot lookups of group g + 1 are issued before the
+// compare / inverse / residual work of group g, so LDS latency hides behind
+// a group of arithmetic; the rotor matrix of g + 2 is fetched there too.
 template <int B, bool QJL, bool IN_F16, bool OUT_F16, bool ROUNDTRIP>
 __global__ __launch_bounds__(256) void rq_quant_kernel(RotorDev P, const char* __restrict__ x, int64_t ldx_bytes,
                                                        int64_t n, uint32_t* __restrict__ codes,
@@ -188,166 +307,237 @@ __global__ __launch_bounds__(256) void rq_quant_kernel(RotorDev P, const char* _
                                                        uint16_t* __restrict__ rnorms, char* __restrict__ y,
                                                        int64_t ldy_bytes) {
     constexpr int W = code_words<B>(kRotCoords);
-    constexpr int L = 1 << B;
-    __shared__ u32x4 tiles[4][kTileBytes / 16];
-    __shared__ u32x4 s_rows[QJL ? 128 * 16 : 1];
-    __shared__ u32x4 s_cols[(QJL && ROUNDTRIP) ? 128 * 16 : 1];
-    __shared__ float lut[L];
-    __shared__ float thr_lds[L];
-    __shared__ float rot_lds[kGroups * 9];
+    constexpr float D = QJL ? kQjlDomain : 1.0f;
+    constexpr bool BACK = QJL && ROUNDTRIP;
+    struct Lds {
+        u32x4 bins[kBinSlots];
+        u32x4 tiles[4][kTileBytes / 16];
+        u32x4 s_fwd[QJL ? 128 * 16 : 1];
+        u32x4 s_back[BACK ? 128 * 16 : 1];
+    };
+    __shared__ Lds lds;
+    u32x4* bins = lds.bins;
+    u32x4(*tiles)[kTileBytes / 16] = lds.tiles;
+    u32x4* s_fwd = lds.s_fwd;
+    u32x4* s_back = lds.s_back;
 
-    if (threadIdx.x < L) lut[threadIdx.x] = P.cent[threadIdx.x];
-    if (threadIdx.x < L - 1) thr_lds[threadIdx.x] = P.thr[threadIdx.x];
-    for (int i = threadIdx.x; i < kGroups * 9; i += blockDim.x) rot_lds[i] = P.rotmat[i];
-    if constexpr (QJL) {
-        mat_to_lds(P.s_rows, s_rows);
-        if constexpr (ROUNDTRIP) mat_to_lds(P.s_cols, s_cols);
-    }
+    stage_bins<QJL>(P.bins, bins);
+    if constexpr (QJL) mat_to_lds(P.s_fwd, s_fwd);
+    if constexpr (BACK) mat_to_lds(P.s_back, s_back);
     __syncthreads();
 
-    const int wave = threadIdx.x >> 6;
+    const float ba = P.bin_a * (1.0f / D), bb = P.bin_b;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     u32x4* tile = tiles[wave];
     uint32_t* stage = reinterpret_cast<uint32_t*>(tile);
     const int64_t ntiles = (n + 63) / 64;
+    const char* binc = reinterpret_cast<const char*>(bins);
 
     for (int64_t t = blockIdx.x * 4LL + wave; t < ntiles; t += gridDim.x * 4LL) {
         const int64_t base = t * 64;
         const int z = opaque_zero();
         const int l = lane_id() + z;
-        RotorDev Q = P;
-        Q.rotmat = rot_lds + z;
-        float thr[L - 1];
-#pragma unroll
-        for (int k = 0; k < L - 1; ++k) thr[k] = uniform(thr_lds[k + z]);
+        const cfloat_ptr rot = reinterpret_cast<cfloat_ptr>(reinterpret_cast<uintptr_t>(P.rotmat)) + z;
         VecIn<IN_F16> in;
         in.load(x, ldx_bytes, base, n, tile, l);
-
         float ss = 0.0f;
 #pragma unroll
         for (int i = 0; i < kD; ++i) {
             const float v = in.get(i);
             ss = __builtin_fmaf(v, v, ss);
         }
-        in.fence();
         const float nrm = __builtin_sqrtf(ss);
         const float inv = nrm > 0.0f ? 1.0f / nrm : 0.0f;
         const uint32_t nh = f2h(nrm);
         const float nhat = h2f(nh);
+        const float sc = inv * D;
 
         uint32_t cw[W];
 #pragma unroll
         for (int k = 0; k < W; ++k) cw[k] = 0u;
-        uint32_t rh[QJL ? kD / 2 : 1], rl[QJL ? kD / 2 : 1];
-        float gam2 = 0.0f;
+        VecOutT<OUT_F16> out;
+        if constexpr (ROUNDTRIP && !QJL) {
+            if constexpr (!OUT_F16) out.bind(y, ldy_bytes, base, n);
+            out.begin(tile, l);
+        }
+        f32x16 za[QJL ? 4 : 1][2];
+#pragma unroll
+        for (int m = 0; m < (QJL ? 4 : 1); ++m) za[m][0] = za[m][1] = f32x16{};
+        float xt[BACK ? kD : 1];
+        float g2 = 0.0f, pend = 0.0f;
+        uint32_t rh[8], rl[8];
+        u32x4 oh0{}, oh1{}, ol0{}, ol1{}, frag{};
 
-#pragma unroll
-        for (int g = 0; g < kGroups; ++g) {
-            __builtin_amdgcn_sched_barrier(0);
-            const float* m = Q.rotmat + 9 * g;
-            float v[3], yv[3];
-#pragma unroll
-            for (int j = 0; j < 3; ++j) v[j] = (3 * g + j < kD) ? in.get(3 * g + j) * inv : 0.0f;
-            rot_fwd(m, v, yv);
-            uint32_t code[3];
+        // pipeline state: matrices of groups g, g+1, g+2 (ring of 3); the
+        // inputs, rotated coordinates and table entries of groups g, g+1
+        float mx[3][9];
+        float va[2][3], ya[2][3];
+        u32x4 ea[2][3];
+        auto stage_a = [&](auto gc) __attribute__((always_inline)) {
+            constexpr int g = decltype(gc)::value;
+            constexpr int s = g & 1;
+            static_for<0, 3>([&](auto jc) __attribute__((always_inline)) {
+                constexpr int i = 3 * g + decltype(jc)::value;
+                if constexpr (i < kD) va[s][i - 3 * g] = in.get(i) * sc;
+                else va[s][i - 3 * g] = 0.0f;
+            });
+            rot_fwd(mx[g % 3], va[s], ya[s]);
 #pragma unroll
             for (int r = 0; r < 3; ++r) {
-                code[r] = quant_code<B>(yv[r], thr);
-                put_code<B, W>(cw, 3 * g + r, code[r]);
+                const uint32_t off = __builtin_bit_cast(uint32_t, __builtin_fmaf(ya[s][r], ba, bb)) & 0xFF0u;
+                ea[s][r] = *reinterpret_cast<const u32x4*>(binc + off);
+            }
+        };
+        load_mat(rot, mx[0]);
+        load_mat(rot + 9, mx[1]);
+        stage_a(std::integral_constant<int, 0>{});
+
+        static_for<0, kGroups>([&](auto gc) __attribute__((always_inline)) {
+            constexpr int g = decltype(gc)::value;
+            constexpr int s = g & 1;
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (QJL) {
+                constexpr int kb = pending_kb(g);
+                if constexpr (kb >= 0) {
+                    constexpr int mt = g - kb_done(kb) - 1;
+                    za[mt][0] = mfma(frag, oh0, za[mt][0]);
+                    za[mt][0] = mfma(frag, ol0, za[mt][0]);
+                    za[mt][1] = mfma(frag, oh1, za[mt][1]);
+                    za[mt][1] = mfma(frag, ol1, za[mt][1]);
+                }
+            }
+            if constexpr (g + 1 < kGroups) stage_a(std::integral_constant<int, g + 1>{});
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (QJL) {
+                constexpr int kb = pending_kb(g + 1);
+                if constexpr (kb >= 0) {
+                    constexpr int mt = g + 1 - kb_done(kb) - 1;
+                    frag = mat_frag(s_fwd, 32 * mt + (l & 31), 2 * kb + (l >> 5));
+                }
+            }
+            if constexpr (g + 2 < kGroups) load_mat(rot + 9 * (g + 2), mx[(g + 2) % 3]);
+            __builtin_amdgcn_sched_barrier(0);
+
+            // stage B of group g
+            float yh[3];
+#pragma unroll
+            for (int r = 0; r < 3; ++r) {
+                const u32x4 e = ea[s][r];
+                const uint32_t ebase = e[0], ethr = e[1], elo = e[2], ehi = e[3];
+                const bool gt = ya[s][r] > __builtin_bit_cast(float, ethr);
+                yh[r] = __builtin_bit_cast(float, gt ? ehi : elo);
+                put_code<B, W>(cw, 3 * g + r, ebase + (gt ? 1u : 0u));
             }
             {
-                const int w0 = (B * 3 * g) >> 5, w1 = (B * (3 * g + 2) + B - 1) >> 5;
+                constexpr int w0 = (B * 3 * g) >> 5, w1 = (B * (3 * g + 2) + B - 1) >> 5;
 #pragma unroll
-                for (int k = 0; k < W; ++k)
-                    if (k >= w0 && k <= w1) pin(cw[k]);
+                for (int k = w0; k <= w1 && k < W; ++k) pin(cw[k]);
             }
-            if constexpr (QJL) {
-                float yh[3], xt[3];
-#pragma unroll
-                for (int r = 0; r < 3; ++r) yh[r] = lut[code[r]];
-                rot_inv(m, yh, xt);
-#pragma unroll
-                for (int j = 0; j < 3; ++j) {
-                    const int i = 3 * g + j;
-                    if (i >= kD) continue;
-                    {
-                        const float r = v[j] - xt[j];
-                        gam2 = __builtin_fmaf(r, r, gam2);
-                        uint32_t hi, lo;
-                        split_h(r * kResidualScale, &hi, &lo);
-                        if (i & 1) {
-                            rh[i >> 1] |= hi << 16;
-                            rl[i >> 1] |= lo << 16;
-                            pin(rh[i >> 1]);
-                            pin(rl[i >> 1]);
-                            pin(gam2);
+            if constexpr (ROUNDTRIP || QJL) {
+                float xo[3];
+                rot_inv(mx[g % 3], yh, xo);
+                static_for<0, 3>([&](auto jc) __attribute__((always_inline)) {
+                    constexpr int j = decltype(jc)::value;
+                    constexpr int i = 3 * g + j;
+                    if constexpr (i < kD) {
+                        if constexpr (!QJL) {
+                            const float o = nhat * xo[j];
+                            if constexpr (i & 1) out.set2(i - 1, pend, o);
+                            else pend = o;
                         } else {
-                            rh[i >> 1] = hi;
-                            rl[i >> 1] = lo;
+                            if constexpr (BACK) xt[i] = xo[j];
+                            const float r = va[s][j] - xo[j];
+                            g2 = __builtin_fmaf(r, r, g2);
+                            if constexpr ((i & 1) == 0) {
+                                pend = r;
+                            } else {
+                                constexpr int d = (i & 15) >> 1;
+                                split_pair(pend, r, &rh[d], &rl[d]);
+                                pin(rh[d]);
+                                pin(rl[d]);
+                                pin(g2);
+                                if constexpr ((i & 15) == 15) {
+                                    to_operands(u32x4{rh[0], rh[1], rh[2], rh[3]}, u32x4{rh[4], rh[5], rh[6], rh[7]},
+                                                &oh0, &oh1);
+                                    to_operands(u32x4{rl[0], rl[1], rl[2], rl[3]}, u32x4{rl[4], rl[5], rl[6], rl[7]},
+                                                &ol0, &ol1);
+                                }
+                            }
                         }
                     }
-                }
+                });
             }
-        }
+        });
+
+        if constexpr (ROUNDTRIP && !QJL) out.store(y, ldy_bytes, base, n);   // frees the tile for the record
 
         uint32_t sw[4] = {0u, 0u, 0u, 0u};
-        float ghat = 0.0f;
         uint32_t gh = 0u;
+        float ghat = 0.0f;
+        u32x4 sig[BACK ? 2 : 1][8];
         if constexpr (QJL) {
-            const float gam = __builtin_sqrtf(gam2);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) issue_fwd(s_fwd, za[mt], 7, mt, oh0, oh1, ol0, ol1, l);
+            const float gam = __builtin_sqrtf(g2) * (1.0f / D);
             gh = f2h(gam);
             ghat = h2f(gh);
-            auto zt = [&](auto mt_c) {
-                constexpr int MT = decltype(mt_c)::value;
-                f32x16 a0 = {}, a1 = {};
+            const uint32_t sel = (l >> 5) ? 0x07060302u : 0x05040100u;
 #pragma unroll
-                for (int kb = 0; kb < 8; ++kb) {
-                    const u32x4 a = mat_frag(s_rows, 32 * MT + (l & 31), 2 * kb + (l >> 5));
-                    u32x4 h0, h1, l0, l1;
-                    to_operands(u32x4{rh[8 * kb], rh[8 * kb + 1], rh[8 * kb + 2], rh[8 * kb + 3]},
-                                u32x4{rh[8 * kb + 4], rh[8 * kb + 5], rh[8 * kb + 6], rh[8 * kb + 7]}, &h0, &h1);
-                    to_operands(u32x4{rl[8 * kb], rl[8 * kb + 1], rl[8 * kb + 2], rl[8 * kb + 3]},
-                                u32x4{rl[8 * kb + 4], rl[8 * kb + 5], rl[8 * kb + 6], rl[8 * kb + 7]}, &l0, &l1);
-                    a0 = mfma(a, h0, a0);
-                    a0 = mfma(a, l0, a0);
-                    a1 = mfma(a, h1, a1);
-                    a1 = mfma(a, l1, a1);
-                }
+            for (int mt = 0; mt < 4; ++mt) {
                 float z0[16], z1[16];
-                from_accumulators(a0, a1, z0, z1);
-                uint32_t word = 0u;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    word |= (z0[r] >= 0.0f ? 1u : 0u) << own_row(0, r);
-                    word |= (z1[r] >= 0.0f ? 1u : 0u) << own_row(1, r);
+                    const float e0 = za[mt][0][r];
+                    const float e1 = za[mt][1][r];
+                    z0[r] = e0;
+                    z1[r] = e1;
                 }
-                sw[MT] = word;
-            };
-            zt(std::integral_constant<int, 0>{});
-            zt(std::integral_constant<int, 1>{});
-            zt(std::integral_constant<int, 2>{});
-            zt(std::integral_constant<int, 3>{});
+                // sign bits: z1 of M tile rows 15..0 into bits 31..16, z0 into 15..0
+                uint32_t pb = 0u;
+#pragma unroll
+                for (int r = 15; r >= 0; --r) pb = __builtin_amdgcn_alignbit(pb, __builtin_bit_cast(uint32_t, z1[r]), 31);
+#pragma unroll
+                for (int r = 15; r >= 0; --r) pb = __builtin_amdgcn_alignbit(pb, __builtin_bit_cast(uint32_t, z0[r]), 31);
+                const auto sp = __builtin_amdgcn_permlane32_swap(pb, pb, false, false);
+                const uint32_t p0 = sp[0], p1 = sp[1];
+                sw[mt] = ~__builtin_amdgcn_perm(p1, p0, sel);
+                if constexpr (BACK) {
+#pragma unroll
+                    for (int c = 0; c < 2; ++c)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            sig[0][2 * mt + c][q] = sigma_pair(z0[8 * c + 2 * q], z0[8 * c + 2 * q + 1]);
+                            sig[1][2 * mt + c][q] = sigma_pair(z1[8 * c + 2 * q], z1[8 * c + 2 * q + 1]);
+                        }
+                }
+            }
         }
 
         // record
-        if (base + l < n) norms[base + l] = static_cast<uint16_t>(nh);
+        half_store(norms, base, n, nh, l);
         words_store<W>(codes, base, n, cw, stage, l);
         if constexpr (QJL) {
-            if (base + l < n) rnorms[base + l] = static_cast<uint16_t>(gh);
+            half_store(rnorms, base, n, gh, l);
             words_store<4>(signs, base, n, sw, stage, l);
         }
 
         // The reconstruction is exactly what rq_dequant_kernel computes from
         // the record just written.
-        if constexpr (ROUNDTRIP) {
-            VecOutT<OUT_F16> out;
-            if constexpr (!OUT_F16) out.bind(y, ldy_bytes, base, n);
-            out.begin(tile, l);
-            dequant_vec<B, QJL, W>(Q, lut, s_cols, cw, nhat, ghat, sw, out, l);
-            out.store(y, ldy_bytes, base, n);
+        if constexpr (BACK) {
+            const float kq = (P.qjl_scale * ghat) * D;
+            const float ns = nhat * (1.0f / D);
+            VecOutT<OUT_F16> o2;
+            if constexpr (!OUT_F16) o2.bind(y, ldy_bytes, base, n);
+            o2.begin(tile, l);
+            back_out(s_back, sig, kq, ns, xt, o2, l);
+            o2.store(y, ldy_bytes, base, n);
         }
     }
 }
 
+// Dequantisation: the centroid pairs of group g + 1 and its rotor matrix
+// (both from LDS) are fetched in group g's region.
 template <int B, bool QJL, bool OUT_F16>
 __global__ __launch_bounds__(256) void rq_dequant_kernel(RotorDev P, const uint32_t* __restrict__ codes,
                                                          const uint16_t* __restrict__ norms,
@@ -355,17 +545,24 @@ __global__ __launch_bounds__(256) void rq_dequant_kernel(RotorDev P, const uint3
                                                          const uint16_t* __restrict__ rnorms, int64_t n,
                                                          char* __restrict__ y, int64_t ldy_bytes) {
     constexpr int W = code_words<B>(kRotCoords);
-    constexpr int L = 1 << B;
-    __shared__ u32x4 tiles[4][kTileBytes / 16];
-    __shared__ u32x4 s_cols[QJL ? 128 * 16 : 1];
-    __shared__ float lut[L];
-    __shared__ float rot_lds[kGroups * 9];
-    if (threadIdx.x < L) lut[threadIdx.x] = P.cent[threadIdx.x];
+    constexpr float D = QJL ? kQjlDomain : 1.0f;
+    struct Lds {
+        f32x2 pairs[1 << (2 * B)];
+        float rot[kGroups * 9 + 1];
+        u32x4 tiles[4][kTileBytes / 16];
+        u32x4 s_back[QJL ? 128 * 16 : 1];
+    };
+    __shared__ Lds lds;
+    f32x2* pairs = lds.pairs;
+    float* rot_lds = lds.rot;
+    u32x4(*tiles)[kTileBytes / 16] = lds.tiles;
+    u32x4* s_back = lds.s_back;
+    stage_pairs<B, QJL>(P.cent, pairs);
     for (int i = threadIdx.x; i < kGroups * 9; i += blockDim.x) rot_lds[i] = P.rotmat[i];
-    if constexpr (QJL) mat_to_lds(P.s_cols, s_cols);
+    if constexpr (QJL) mat_to_lds(P.s_back, s_back);
     __syncthreads();
 
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     u32x4* tile = tiles[wave];
     uint32_t* stage = reinterpret_cast<uint32_t*>(tile);
     const int64_t ntiles = (n + 63) / 64;
@@ -373,22 +570,65 @@ __global__ __launch_bounds__(256) void rq_dequant_kernel(RotorDev P, const uint3
         const int64_t base = t * 64;
         const int z = opaque_zero();
         const int l = lane_id() + z;
+        const float* rot = rot_lds + z;
         uint32_t cw[W];
         words_load<W>(codes, base, n, cw, stage, l);
-        const bool live = base + l < n;
-        const float nhat = live ? h2f(norms[base + l]) : 0.0f;
-        uint32_t sw[4] = {0u, 0u, 0u, 0u};
-        float ghat = 0.0f;
+        const float nhat = h2f(half_load(norms, base, n, l));
+        float u[QJL ? kD : 1];
+        float kq = 0.0f, ns = nhat;
         if constexpr (QJL) {
-            words_load<4>(signs, base, n, sw, stage, l);
-            ghat = live ? h2f(rnorms[base + l]) : 0.0f;
+            u32x4 wv[2];
+            load_sign_pairs(signs, base, n, wv, stage, l);
+            const float ghat = h2f(half_load(rnorms, base, n, l));
+            u32x4 sig[2][8];
+            sigma_from_words(wv, sig, l);
+            back_proj(s_back, sig, u, l);
+            kq = (P.qjl_scale * ghat) * D;
+            ns = nhat * (1.0f / D);
         }
         VecOutT<OUT_F16> out;
         if constexpr (!OUT_F16) out.bind(y, ldy_bytes, base, n);
         out.begin(tile, l);
-        RotorDev Q = P;
-        Q.rotmat = rot_lds + z;
-        dequant_vec<B, QJL, W>(Q, lut, s_cols, cw, nhat, ghat, sw, out, l);
+        float pend = 0.0f;
+        f32x2 pv[4];
+        float mx[2][9];
+        // pairs whose first code lies in group g
+        auto fetch = [&](auto gc) __attribute__((always_inline)) {
+            constexpr int g = decltype(gc)::value;
+            static_for<0, 3>([&](auto rc) __attribute__((always_inline)) {
+                constexpr int i = 3 * g + decltype(rc)::value;
+                if constexpr ((i & 1) == 0) pv[(i >> 1) & 3] = pair_vals<B, W>(cw, i >> 1, pairs);
+            });
+#pragma unroll
+            for (int k = 0; k < 9; ++k) mx[g & 1][k] = rot[9 * g + k];
+        };
+        fetch(std::integral_constant<int, 0>{});
+        static_for<0, kGroups>([&](auto gc) __attribute__((always_inline)) {
+            constexpr int g = decltype(gc)::value;
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (g + 1 < kGroups) fetch(std::integral_constant<int, g + 1>{});
+            __builtin_amdgcn_sched_barrier(0);
+            float yh[3], xo[3];
+            static_for<0, 3>([&](auto rc) __attribute__((always_inline)) {
+                constexpr int r = decltype(rc)::value;
+                constexpr int i = 3 * g + r;
+                const f32x2 q = pv[(i >> 1) & 3];
+                const float a = q[0], b = q[1];
+                yh[r] = (i & 1) ? b : a;
+            });
+            rot_inv(mx[g & 1], yh, xo);
+            static_for<0, 3>([&](auto jc) __attribute__((always_inline)) {
+                constexpr int j = decltype(jc)::value;
+                constexpr int i = 3 * g + j;
+                if constexpr (i < kD) {
+                    float o;
+                    if constexpr (QJL) o = ns * __builtin_fmaf(kq, u[i], xo[j]);
+                    else o = nhat * xo[j];
+                    if constexpr (i & 1) out.set2(i - 1, pend, o);
+                    else pend = o;
+                }
+            });
+        });
         out.store(y, ldy_bytes, base, n);
     }
 }

@@ -7,10 +7,11 @@ namespace rqk {
 
 struct RotorDev {
     const float* __restrict__ rotmat;
-    const float* __restrict__ thr;
     const float* __restrict__ cent;
-    const uint16_t* __restrict__ s_rows;
-    const uint16_t* __restrict__ s_cols;
+    const u32x4_t* __restrict__ bins;
+    const uint16_t* __restrict__ s_fwd;
+    const uint16_t* __restrict__ s_back;
+    float bin_a, bin_b;
     float qjl_scale;
 };
 

@@ -6,10 +6,12 @@ namespace rqk {
 static RotorDev make_dev(const RotorTables& t) {
     RotorDev P;
     P.rotmat = t.rotmat;
-    P.thr = t.thr;
     P.cent = t.cent;
-    P.s_rows = t.s_rows;
-    P.s_cols = t.s_cols;
+    P.bins = t.bins;
+    P.bin_a = t.bin_a;
+    P.bin_b = t.bin_b;
+    P.s_fwd = t.s_fwd;
+    P.s_back = t.s_back;
     P.qjl_scale = t.qjl_scale;
     return P;
 }

@@ -204,7 +204,7 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
         inv_sc = 1.0f / pow2_scale(cmax);
     }
 
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     uint32_t* st = stage[wave];
     const int64_t ntiles = (a.t + 63) / 64;
     const int64_t rbase = static_cast<int64_t>(a.kv_head0 + kvh) * a.kv_stride;
