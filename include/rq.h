@@ -176,10 +176,11 @@ int rq_roundtrip(rq_ctx* ctx, const void* x, int x_dtype, int64_t n, int64_t ldx
  *   <q,k> ~ <q,k_mse> + ||r|| sqrt(pi/2)/m <S q, sign(S r)>),
  * for grouped-query attention: query row h reads KV head h / group.
  *   q       [hq][128] fp32 queries, 16-byte aligned.
- *   group   query rows per KV head (>= 1); hq must be a multiple of group.
+ *   group   query rows per KV head, 1 <= group <= RQ_SCORE_CHUNK; hq must be
+ *           a multiple of group.
  *   codes.. records of hq/group KV heads; head j's t keys start at record
  *           row j * kv_stride (kv_stride >= t, or any value if hq == group).
- *   scores  [hq][ld_scores] fp32, ld_scores >= t; row h gets
+ *   scores  [hq][ld_scores] fp32, t <= ld_scores <= 2^23; row h gets
  *           n^_t (<q_h, x~_mse,u(t)> + gamma^_t sqrt(pi/2)/m <S q_h, sigma_t>),
  *           raw: no 1/sqrt(d), no softmax.
  * Works for rotor and dense sessions.  Uses the ctx's query workspace (see

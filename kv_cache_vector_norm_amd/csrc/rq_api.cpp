@@ -429,6 +429,8 @@ int rq_score(rq_ctx* ctx, const float* q, int hq, int group, const uint32_t* cod
     if (kv_heads > 1 && kv_stride < t) return fail(RQ_EINVAL, "rq_score: kv_stride < t");
     if (!scores || !aligned(scores, 4)) return fail(RQ_EINVAL, "rq_score: scores must be a 4-byte aligned device pointer");
     if (ld_scores < t) return fail(RQ_EINVAL, "rq_score: ld_scores < t");
+    if (ld_scores > (int64_t(1) << 23)) return fail(RQ_EINVAL, "rq_score: ld_scores > 2^23");
+    if (group > RQ_SCORE_CHUNK) return fail(RQ_EINVAL, "rq_score: group > RQ_SCORE_CHUNK");
     if (t == 0) return RQ_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool dense = ctx->host.lay.mode & RQ_DENSE;

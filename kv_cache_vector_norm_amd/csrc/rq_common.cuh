@@ -297,11 +297,21 @@ __device__ __forceinline__ u32x4 mat_frag(const u32x4* __restrict__ m, int row, 
 }
 
 // Copies a 128 x 128 half matrix (row-major, 32 KB) into swizzled LDS.
+// Threads per block of the codec kernels (the TurboQuant QJL kernels use
+// 128).  The copy is unrolled so all of a thread's loads are in flight
+// before the first LDS store waits on one.
+constexpr int kBlock = 256;
+template <int NT = kBlock>
 __device__ __forceinline__ void mat_to_lds(const uint16_t* __restrict__ g, u32x4* __restrict__ m) {
+    static_assert(128 * 16 % NT == 0, "block size");
     const u32x4* src = reinterpret_cast<const u32x4*>(g);
-    for (int q = threadIdx.x; q < 128 * 16; q += blockDim.x) {
-        const int row = q >> 4, c = q & 15;
-        m[row * 16 + (c ^ (row & 15))] = src[q];
+    u32x4 v[128 * 16 / NT];
+#pragma unroll
+    for (int it = 0; it < 128 * 16 / NT; ++it) v[it] = src[it * NT + threadIdx.x];
+#pragma unroll
+    for (int it = 0; it < 128 * 16 / NT; ++it) {
+        const int q = it * NT + threadIdx.x, row = q >> 4, c = q & 15;
+        m[row * 16 + (c ^ (row & 15))] = v[it];
     }
 }
 

@@ -181,9 +181,9 @@ __global__ __launch_bounds__(WAVES * 64) void tq_quant_kernel(DenseDev P, const 
     constexpr int L = 1 << B;
     __shared__ DenseLds<WAVES, QJL> sm;
     dense_tables_to_lds<B>(P, sm.ctab, sm.thr);
-    mat_to_lds(P.pi_hi, sm.pih);
-    mat_to_lds(P.pi_lo, sm.pil);
-    if constexpr (QJL) mat_to_lds(P.s_rows, sm.s_rows);
+    mat_to_lds<WAVES * 64>(P.pi_hi, sm.pih);
+    mat_to_lds<WAVES * 64>(P.pi_lo, sm.pil);
+    if constexpr (QJL) mat_to_lds<WAVES * 64>(P.s_rows, sm.s_rows);
     __syncthreads();
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

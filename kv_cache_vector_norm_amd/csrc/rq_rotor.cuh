@@ -56,7 +56,7 @@ template <bool QJL>
 __device__ __forceinline__ void stage_bins(const u32x4_t* __restrict__ g, u32x4* __restrict__ s) {
     constexpr float D = QJL ? kQjlDomain : 1.0f;
     const u32x4* src = reinterpret_cast<const u32x4*>(g);
-    for (int i = threadIdx.x; i < kBinSlots; i += blockDim.x) {
+    for (int i = threadIdx.x; i < kBinSlots; i += kBlock) {
         const u32x4 e = src[i];
         const uint32_t e0 = e[0], e1 = e[1], e2 = e[2], e3 = e[3];
         s[i] = u32x4{e0, __builtin_bit_cast(uint32_t, __builtin_bit_cast(float, e1) * D),
@@ -70,7 +70,7 @@ template <int B, bool QJL>
 __device__ __forceinline__ void stage_pairs(const float* __restrict__ cent, f32x2* __restrict__ pairs) {
     constexpr int L = 1 << B;
     constexpr float D = QJL ? kQjlDomain : 1.0f;
-    for (int p = threadIdx.x; p < L * L; p += blockDim.x) pairs[p] = f32x2{cent[p & (L - 1)] * D, cent[p >> B] * D};
+    for (int p = threadIdx.x; p < L * L; p += kBlock) pairs[p] = f32x2{cent[p & (L - 1)] * D, cent[p >> B] * D};
 }
 
 // ------------------------------------------------------------ per lane --
@@ -558,7 +558,7 @@ __global__ __launch_bounds__(256) void rq_dequant_kernel(RotorDev P, const uint3
     u32x4(*tiles)[kTileBytes / 16] = lds.tiles;
     u32x4* s_back = lds.s_back;
     stage_pairs<B, QJL>(P.cent, pairs);
-    for (int i = threadIdx.x; i < kGroups * 9; i += blockDim.x) rot_lds[i] = P.rotmat[i];
+    for (int i = threadIdx.x; i < kGroups * 9; i += kBlock) rot_lds[i] = P.rotmat[i];
     if constexpr (QJL) mat_to_lds(P.s_back, s_back);
     __syncthreads();
 

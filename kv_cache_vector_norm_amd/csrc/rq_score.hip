@@ -9,10 +9,13 @@
 //   n^ * ( <q^, c[code]> + gamma^ sqrt(pi/2)/m <S q, sigma> ).
 //
 // Prologue: one block per query row writes q^ and S q as exact half pairs
-// with a power-of-two row scale.  Main kernel: each lane decodes one key's
-// record once (centroids as exact half pairs, sign bits as +-1 halves), the
-// tile's keys become the B operand of 32x32x16 MFMAs whose A operand is the
-// staged query rows of one KV head (rows are the GQA group).
+// with a power-of-two row scale.  Main kernel: the staged query rows of one
+// KV head are the A operand of 32x32x16 MFMAs; the B operand is decoded from
+// the records straight into MFMA layout: lane (n, h) of a wave serves keys n
+// and 32 + n of the 64-key tile and K slots 8h..8h+7 of each 16-wide block,
+// turning two codes into packed centroid halves with one LDS lookup and sign
+// bits into +-1 halves with shifts.  The rotor pad coordinate (slot 128) is
+// added in fp32 in the epilogue.
 #include "rq_common.cuh"
 #include "rq_kernels.h"
 
@@ -20,32 +23,32 @@ namespace rqk {
 
 // ---------------------------------------------------------- staged rows --
 // Per query row, in 16-byte chunks:
-//   Q1 [18 chunks] = 2^11 * hi(s_q q^)   Q2 = hi(s_q q^)   Q3 = lo(s_q q^)
+//   Q1 [16 chunks] = 2^11 * hi(s_q q^)   Q2 = hi(s_q q^)   Q3 = lo(s_q q^)
 //   P1 [16 chunks] = 2^11 * hi(s_p S q)  P2 = lo(s_p S q)
-// with hi(v) = half(v), lo(v) = half((v - hi) * 2^11) (split_h11); q^ has 144 slots
-// (129 or 128 used, the rest zero).  Against centroid halves
-// C_hi = half(s_c c), C_lo = half((s_c c - C_hi) 2^11):
+// with hi(v) = half(v), lo(v) = half((v - hi) * 2^11) (split_h11) over
+// slots 0..127.  Against centroid halves C_hi = half(s_c c),
+// C_lo = half((s_c c - C_hi) 2^11):
 //   Q1 C_hi + Q2 C_lo + Q3 C_hi = 2^11 s_q s_c <q^, c>  (to ~2^-22 relative),
 //   P1 sigma + P2 sigma = 2^11 s_p <S q, sigma>.
-constexpr int kQSlots = 144;
-constexpr int kQChunks = kQSlots / 8;   // 18
-constexpr int kPChunks = 16;
-constexpr int kRowChunks = 3 * kQChunks + 2 * kPChunks;   // 86
-constexpr int kRowStride = kRowChunks + 1;                 // LDS row pitch (bank spread)
-constexpr int kOffQ1 = 0, kOffQ2 = kQChunks, kOffQ3 = 2 * kQChunks, kOffP1 = 3 * kQChunks,
-              kOffP2 = 3 * kQChunks + kPChunks;
-static_assert(kRowChunks * 16 + 8 <= kScoreQueryBytes, "workspace row too small");
+// Row scalars (after the rows): 1 / (2^11 s_q), 1 / (2^11 s_p), and the
+// rotor pad slot q^_128 in fp32.
+constexpr int kQChunks = 16;
+constexpr int kRowChunks = 5 * kQChunks;     // 80
+constexpr int kRowStride = kRowChunks + 1;   // LDS row pitch (bank spread)
+constexpr int kOffQ1 = 0, kOffQ2 = kQChunks, kOffQ3 = 2 * kQChunks, kOffP1 = 3 * kQChunks, kOffP2 = 4 * kQChunks;
+constexpr int kRowScalars = 3;
+static_assert(kRowChunks * 16 + kRowScalars * 4 <= kScoreQueryBytes, "workspace row too small");
 
 struct ProArgs {
     const float* q;
     int hq;
     bool dense, qjl;
-    const float* rotmat;     // rotor: [43][9]
-    const uint16_t* pi_hi;   // dense: Pi = (hi + lo 2^-11) / 16, row-major
-    const uint16_t* pi_lo;
-    const uint16_t* s_rows;  // QJL: S, row-major halves
-    u32x4* rows;             // [hq][kRowChunks]
-    float* scales;           // [hq][2]: 1 / (2^11 s_q), 1 / (2^11 s_p)
+    const float* rotmat;      // rotor: [43][9]
+    const uint16_t* pit_hi;   // dense: Pi^T = (hi + lo 2^-11) / 16, row-major
+    const uint16_t* pit_lo;
+    const uint16_t* s_cols;   // QJL: S^T, row-major halves
+    u32x4* rows;              // [hq][kRowChunks]
+    float* scalars;           // [hq][kRowScalars]
 };
 
 __device__ __forceinline__ float block_max(float v, float* red) {
@@ -65,30 +68,30 @@ __device__ __forceinline__ float pow2_scale(float maxabs) {
     return ldexpf(1.0f, 1 - e);
 }
 
+// One block of 128 threads per query row; thread i owns slot i.  The
+// transposed tables are read so that a warp's loads are contiguous.
 __global__ __launch_bounds__(128) void score_prologue(ProArgs a) {
     __shared__ float qs[kD];
     __shared__ float red[2];
-    __shared__ uint16_t hv[5][kQSlots];
+    __shared__ __align__(16) uint16_t hv[5][kD];
     const int h = blockIdx.x, i = threadIdx.x;
     qs[i] = a.q[static_cast<int64_t>(h) * kD + i];
-    for (int k = i; k < kQSlots; k += 128)
-        for (int v = 0; v < 5; ++v) hv[v][k] = 0;
     __syncthreads();
-    // rotated query: rotor groups (129 slots) or y = Pi q (128)
-    float qh = 0.0f, qh_pad = 0.0f;
+    float qh = 0.0f, qpad = 0.0f;
     if (!a.dense) {
         const int g = i / 3, r = i % 3;
         const float* m = a.rotmat + 9 * g;
         const float v2 = (3 * g + 2 < kD) ? qs[3 * g + 2] : 0.0f;
         qh = __builtin_fmaf(m[3 * r + 2], v2, __builtin_fmaf(m[3 * r + 1], qs[3 * g + 1], m[3 * r] * qs[3 * g]));
-        if (i == 0) {   // slot 128: last row of group 42 (pad input 0)
-            const float* m42 = a.rotmat + 9 * 42;
-            qh_pad = __builtin_fmaf(m42[8], 0.0f, __builtin_fmaf(m42[7], qs[127], m42[6] * qs[126]));
-        }
+        // slot 128: last row of group 42 (pad input 0)
+        const float* m42 = a.rotmat + 9 * 42;
+        qpad = __builtin_fmaf(m42[8], 0.0f, __builtin_fmaf(m42[7], qs[127], m42[6] * qs[126]));
     } else {
         float acc = 0.0f;
+#pragma unroll 16
         for (int k = 0; k < kD; ++k) {
-            const float p = (h2f(a.pi_hi[i * kD + k]) + h2f(a.pi_lo[i * kD + k]) * (1.0f / 2048.0f)) * 0.0625f;
+            const float p =
+                (h2f(a.pit_hi[k * kD + i]) + h2f(a.pit_lo[k * kD + i]) * (1.0f / 2048.0f)) * 0.0625f;
             acc = __builtin_fmaf(p, qs[k], acc);
         }
         qh = acc;
@@ -96,44 +99,30 @@ __global__ __launch_bounds__(128) void score_prologue(ProArgs a) {
     float pj = 0.0f;
     if (a.qjl) {
         float acc = 0.0f;
-        for (int k = 0; k < kD; ++k) acc = __builtin_fmaf(h2f(a.s_rows[i * kD + k]), qs[k], acc);
+#pragma unroll 16
+        for (int k = 0; k < kD; ++k) acc = __builtin_fmaf(h2f(a.s_cols[k * kD + i]), qs[k], acc);
         pj = acc;
     }
-    const float sq = pow2_scale(block_max(fmaxf(fabsf(qh), fabsf(qh_pad)), red));
+    const float sq = pow2_scale(block_max(fabsf(qh), red));
     const float sp = pow2_scale(block_max(fabsf(pj), red));
-    auto put = [&](int slot, float v) {
+    {
         uint32_t hi, lo;
-        split_h11(v * sq, &hi, &lo);
-        hv[0][slot] = static_cast<uint16_t>(f2h(h2f(hi) * 2048.0f));
-        hv[1][slot] = static_cast<uint16_t>(hi);
-        hv[2][slot] = static_cast<uint16_t>(lo);
-    };
-    put(i, qh);
-    if (!a.dense && i == 0) put(128, qh_pad);
-    if (a.qjl) {
-        uint32_t hi, lo;
+        split_h11(qh * sq, &hi, &lo);
+        hv[0][i] = static_cast<uint16_t>(f2h(h2f(hi) * 2048.0f));
+        hv[1][i] = static_cast<uint16_t>(hi);
+        hv[2][i] = static_cast<uint16_t>(lo);
         split_h11(pj * sp, &hi, &lo);
         hv[3][i] = static_cast<uint16_t>(f2h(h2f(hi) * 2048.0f));
         hv[4][i] = static_cast<uint16_t>(lo);
     }
     __syncthreads();
     u32x4* row = a.rows + static_cast<int64_t>(h) * kRowChunks;
-    const u32x4* src;
-    for (int c = i; c < kRowChunks; c += 128) {
-        int v, k;
-        if (c < 3 * kQChunks) {
-            v = c / kQChunks;
-            k = c % kQChunks;
-        } else {
-            v = 3 + (c - 3 * kQChunks) / kPChunks;
-            k = (c - 3 * kQChunks) % kPChunks;
-        }
-        src = reinterpret_cast<const u32x4*>(&hv[v][0]);
-        row[c] = src[k];
-    }
+    for (int c = i; c < kRowChunks; c += 128) row[c] = reinterpret_cast<const u32x4*>(&hv[c / kQChunks][0])[c % kQChunks];
     if (i == 0) {
-        a.scales[2 * h] = 1.0f / (2048.0f * sq);
-        a.scales[2 * h + 1] = 1.0f / (2048.0f * sp);
+        float* s = a.scalars + static_cast<int64_t>(h) * kRowScalars;
+        s[0] = 1.0f / (2048.0f * sq);
+        s[1] = 1.0f / (2048.0f * sp);
+        s[2] = qpad;
     }
 }
 
@@ -146,82 +135,162 @@ struct MainArgs {
     int64_t t, kv_stride;
     int kv_head0, group, rows_per_block;
     const u32x4* rows;
-    const float* scales;
+    const float* scalars;
     const float* cent;
     float qjl_scale;
     float* scores;
     int64_t ld;
 };
 
-// Each 8-bit group of sign bits -> eight +-1 halves (bit 1 -> +1).
-__device__ __forceinline__ u32x4 sigma_bits(uint32_t byte) {
-    u32x4 r;
+// 8 sign bits (bit e = [z_e >= 0]) -> four dwords of +-1 half pairs.
+__device__ __forceinline__ u32x4 sigma8(uint32_t byte) {
+    const uint32_t nb = ~byte;
+    const uint32_t u = (nb & 0x55u) | ((nb & 0xAAu) << 15);
+    u32x4 d;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const uint32_t b0 = (byte >> (2 * p)) & 1u, b1 = (byte >> (2 * p + 1)) & 1u;
-        r[p] = 0xBC00BC00u ^ (b0 << 15) ^ (b1 << 31);
-    }
-    return r;
+    for (int q = 0; q < 4; ++q) d[q] = ((u << (15 - 2 * q)) & 0x80008000u) | 0x3C003C00u;
+    return d;
 }
 
-template <int B, bool QJL, int NC, int NMT>
+// One 16-bit record entry of key `idx` (relative to the tile base), 0 past n.
+__device__ __forceinline__ uint32_t half_at(const uint16_t* __restrict__ src, int64_t base, int64_t n, int idx) {
+    const rsrc_t rs = make_rsrc(src + base, tile_range(n - base, 2));
+    return __builtin_amdgcn_raw_buffer_load_b16(rs, static_cast<uint32_t>(2 * idx), 0, kNonTemporal);
+}
+
+template <int B, bool QJL, bool PAD, int NMT>
 __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
+    constexpr int NC = PAD ? kRotCoords : kD;
     constexpr int W = (NC * B + 31) / 32;
     constexpr int L = 1 << B;
-    constexpr int KB1 = (NC + 15) / 16;   // K blocks of <q^, c>
-    __shared__ u32x4 qrows[NMT * 32 * kRowStride];
-    __shared__ float rscale[NMT * 32][2];
-    __shared__ uint32_t ctab[L];          // C_hi | C_lo << 16 per code
-    __shared__ uint32_t stage[4][64 * (W > 4 ? W : 4)];
+    constexpr int SW = W > 4 ? W : 4;
+    constexpr int ROWS = NMT * 32;
+    struct Lds {
+        uint32_t pairs[L * L][2];     // codes (a, b) -> {C_hi[a] | C_hi[b] << 16, C_lo[a] | C_lo[b] << 16}
+        float rsc[ROWS][4];           // {1 / (2^11 s_q s_c), 1 / (2^11 s_p), q^_128, 0}
+        float cent[L];
+        uint32_t stage[4][64 * SW];
+        u32x4 qrows[ROWS * kRowStride];
+    };
+    __shared__ Lds lds;
 
-    const int head = blockIdx.y;             // KV head within this call (query block folded below)
+    const int head = blockIdx.y;   // KV head within this call (query block folded below)
     const int qblocks = (a.group + a.rows_per_block - 1) / a.rows_per_block;
     const int kvh = head / qblocks, qb = head % qblocks;
     const int row0 = kvh * a.group + qb * a.rows_per_block;
     const int nrows = min(a.rows_per_block, a.group - qb * a.rows_per_block);
 
-    // stage this block's query rows (rows >= nrows are zero)
-    for (int q = threadIdx.x; q < NMT * 32 * kRowChunks; q += blockDim.x) {
-        const int r = q / kRowChunks, c = q % kRowChunks;
-        qrows[r * kRowStride + c] = r < nrows ? a.rows[static_cast<int64_t>(row0 + r) * kRowChunks + c]
-                                              : u32x4{0u, 0u, 0u, 0u};
-    }
-    for (int r = threadIdx.x; r < NMT * 32; r += blockDim.x) {
-        rscale[r][0] = r < nrows ? a.scales[2 * (row0 + r)] : 0.0f;
-        rscale[r][1] = r < nrows ? a.scales[2 * (row0 + r) + 1] : 0.0f;
-    }
-    if (threadIdx.x < L) {
-        const float cmax = fabsf(a.cent[L - 1]) > fabsf(a.cent[0]) ? fabsf(a.cent[L - 1]) : fabsf(a.cent[0]);
-        const float sc = pow2_scale(cmax);
-        uint32_t hi, lo;
-        split_h11(a.cent[threadIdx.x] * sc, &hi, &lo);
-        ctab[threadIdx.x] = hi | (lo << 16);
-    }
-    __syncthreads();
     float inv_sc;
     {
         const float cmax = fabsf(a.cent[L - 1]) > fabsf(a.cent[0]) ? fabsf(a.cent[L - 1]) : fabsf(a.cent[0]);
-        inv_sc = 1.0f / pow2_scale(cmax);
+        const float sc = pow2_scale(cmax);
+        inv_sc = 1.0f / sc;
+        for (int p = threadIdx.x; p < L * L; p += kBlock) {
+            uint32_t h0, l0, h1, l1;
+            split_h11(a.cent[p & (L - 1)] * sc, &h0, &l0);
+            split_h11(a.cent[p >> B] * sc, &h1, &l1);
+            lds.pairs[p][0] = h0 | (h1 << 16);
+            lds.pairs[p][1] = l0 | (l1 << 16);
+        }
+        if (threadIdx.x < L) lds.cent[threadIdx.x] = a.cent[threadIdx.x];
     }
+    // this block's query rows (rows >= nrows are zero), all loads in flight at once
+    {
+        constexpr int PER = ROWS * kRowChunks / kBlock;
+        static_assert(ROWS * kRowChunks % kBlock == 0, "staging split");
+        u32x4 v[PER];
+#pragma unroll
+        for (int it = 0; it < PER; ++it) {
+            const int q = it * kBlock + threadIdx.x, r = q / kRowChunks, c = q % kRowChunks;
+            v[it] = r < nrows ? a.rows[static_cast<int64_t>(row0 + r) * kRowChunks + c] : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int it = 0; it < PER; ++it) {
+            const int q = it * kBlock + threadIdx.x, r = q / kRowChunks, c = q % kRowChunks;
+            lds.qrows[r * kRowStride + c] = v[it];
+        }
+    }
+    for (int r = threadIdx.x; r < ROWS; r += kBlock) {
+        float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f;
+        if (r < nrows) {
+            const float* s = a.scalars + static_cast<int64_t>(row0 + r) * kRowScalars;
+            s0 = s[0] * inv_sc;
+            s1 = s[1];
+            s2 = s[2];
+        }
+        lds.rsc[r][0] = s0;
+        lds.rsc[r][1] = s1;
+        lds.rsc[r][2] = s2;
+        lds.rsc[r][3] = 0.0f;
+    }
+    __syncthreads();
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    uint32_t* st = stage[wave];
-    const int64_t ntiles = (a.t + 63) / 64;
+    uint32_t* st = lds.stage[wave];
+    const int64_t nk = a.t;   // keys of this head
+    const int64_t ntiles = (nk + 63) / 64;
     const int64_t rbase = static_cast<int64_t>(a.kv_head0 + kvh) * a.kv_stride;
+    const char* pairc = reinterpret_cast<const char*>(lds.pairs);
 
     for (int64_t tile = blockIdx.x * 4LL + wave; tile < ntiles; tile += gridDim.x * 4LL) {
         const int z = opaque_zero();
         const int l = lane_id() + z;
+        const int n = l & 31, hh = l >> 5;
         const int64_t kbase = tile * 64;
-        const int64_t nk = a.t;   // keys of this head
-        // record of this lane's key
-        uint32_t cw[W];
-        words_load<W>(a.codes + rbase * W, kbase, nk, cw, st, l);
-        uint32_t sw[4] = {0u, 0u, 0u, 0u};
-        if constexpr (QJL) words_load<4>(a.signs + rbase * 4, kbase, nk, sw, st, l);
-        const bool live = kbase + l < nk;
-        const float nhat = live ? h2f(a.norms[rbase + kbase + l]) : 0.0f;
-        const float ghat = (QJL && live) ? h2f(a.rnorms[rbase + kbase + l]) : 0.0f;
+
+        // code words of keys n and 32 + n, shifted so this lane's K slots
+        // start at bit 0 (slot 8 hh of each block is bit 8 B hh further)
+        uint32_t cw[2][W];
+        {
+            const rsrc_t rs = make_rsrc(a.codes + (rbase + kbase) * W, tile_range(nk - kbase, 4 * W));
+            wave_lds_sync();
+#pragma unroll
+            for (int it = 0; it < W; ++it)
+                st[it * 64 + l] = __builtin_amdgcn_raw_buffer_load_b32(rs, static_cast<uint32_t>(4 * l), 256 * it,
+                                                                        kNonTemporal);
+            wave_lds_sync();
+#pragma unroll
+            for (int k = 0; k < W; ++k) {
+                cw[0][k] = st[n * W + k];
+                cw[1][k] = st[(32 + n) * W + k];
+            }
+        }
+        float cpad[2] = {0.0f, 0.0f};
+        if constexpr (PAD) {
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) cpad[nt] = lds.cent[cw[nt][4 * B] & (L - 1)];
+        }
+        uint32_t cs[2][W];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int k = 0; k < W; ++k) {
+                const uint32_t nxt = k + 1 < W ? cw[nt][k + 1] : 0u;
+                if constexpr (B == 4) cs[nt][k] = hh ? nxt : cw[nt][k];
+                else cs[nt][k] = __builtin_amdgcn_alignbit(nxt, cw[nt][k], 8 * B * hh);
+            }
+        uint32_t sg[2][4];
+        if constexpr (QJL) {
+            const rsrc_t rs = make_rsrc(a.signs + (rbase + kbase) * 4, tile_range(nk - kbase, 16));
+            wave_lds_sync();
+#pragma unroll
+            for (int it = 0; it < 4; ++it)
+                st[it * 64 + l] = __builtin_amdgcn_raw_buffer_load_b32(rs, static_cast<uint32_t>(4 * l), 256 * it,
+                                                                        kNonTemporal);
+            wave_lds_sync();
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                sg[0][k] = st[n * 4 + k] >> (8 * hh);
+                sg[1][k] = st[(32 + n) * 4 + k] >> (8 * hh);
+            }
+        }
+        wave_lds_sync();
+        float kn[2], kg[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            kn[nt] = h2f(half_at(a.norms + rbase, kbase, nk, 32 * nt + n));
+            kg[nt] = QJL ? h2f(half_at(a.rnorms + rbase, kbase, nk, 32 * nt + n)) * a.qjl_scale : 0.0f;
+        }
 
         f32x16 acc1[NMT][2], acc2[NMT][2];
 #pragma unroll
@@ -233,113 +302,108 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
             }
 
 #pragma unroll
-        for (int kb = 0; kb < KB1; ++kb) {
+        for (int kb = 0; kb < 8; ++kb) {
             __builtin_amdgcn_sched_barrier(0);
-            u32x4 h0, h1, lo0, lo1;   // own chunk 0 / 1 of C_hi and C_lo
-            uint32_t hp[8], lp[8];
+            u32x4 ch[2], cl[2];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                uint32_t hh = 0u, ll = 0u;
+            for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    const int i = 16 * kb + 2 * e + s;
-                    if (i < NC) {
-                        const uint32_t v = ctab[get_code<B, W>(cw, i)];
-                        hh |= (v & 0xFFFFu) << (16 * s);
-                        ll |= (v >> 16) << (16 * s);
-                    }
+                for (int q = 0; q < 4; ++q) {
+                    const int bit = 16 * B * kb + 2 * B * q, wi = bit >> 5, off = bit & 31;
+                    uint32_t f = cs[nt][wi] >> off;
+                    if (off + 2 * B > 32) f = __builtin_amdgcn_alignbit(cs[nt][wi + 1], cs[nt][wi], off);
+                    const uint32_t addr = (f & (L * L - 1)) * 8u;
+                    const uint32_t hi = *reinterpret_cast<const uint32_t*>(pairc + addr);
+                    const uint32_t lo = *reinterpret_cast<const uint32_t*>(pairc + addr + 4);
+                    ch[nt][q] = hi;
+                    cl[nt][q] = lo;
                 }
-                hp[e] = hh;
-                lp[e] = ll;
-            }
-            u32x4 ch0{hp[0], hp[1], hp[2], hp[3]}, ch1{hp[4], hp[5], hp[6], hp[7]};
-            u32x4 cl0{lp[0], lp[1], lp[2], lp[3]}, cl1{lp[4], lp[5], lp[6], lp[7]};
-            to_operands(ch0, ch1, &h0, &h1);
-            to_operands(cl0, cl1, &lo0, &lo1);
 #pragma unroll
             for (int m = 0; m < NMT; ++m) {
-                const int r = 32 * m + (l & 31);
-                const int kc = 2 * kb + (l >> 5);
-                const u32x4 q1 = qrows[r * kRowStride + kOffQ1 + kc];
-                const u32x4 q2 = qrows[r * kRowStride + kOffQ2 + kc];
-                const u32x4 q3 = qrows[r * kRowStride + kOffQ3 + kc];
-                acc1[m][0] = mfma(q1, h0, acc1[m][0]);
-                acc1[m][0] = mfma(q2, lo0, acc1[m][0]);
-                acc1[m][0] = mfma(q3, h0, acc1[m][0]);
-                acc1[m][1] = mfma(q1, h1, acc1[m][1]);
-                acc1[m][1] = mfma(q2, lo1, acc1[m][1]);
-                acc1[m][1] = mfma(q3, h1, acc1[m][1]);
+                const int r = (32 * m + n) * kRowStride + 2 * kb + hh;
+                const u32x4 q1 = lds.qrows[r + kOffQ1];
+                const u32x4 q2 = lds.qrows[r + kOffQ2];
+                const u32x4 q3 = lds.qrows[r + kOffQ3];
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    acc1[m][nt] = mfma(q1, ch[nt], acc1[m][nt]);
+                    acc1[m][nt] = mfma(q2, cl[nt], acc1[m][nt]);
+                    acc1[m][nt] = mfma(q3, ch[nt], acc1[m][nt]);
+                }
             }
         }
         if constexpr (QJL) {
 #pragma unroll
             for (int kb = 0; kb < 8; ++kb) {
                 __builtin_amdgcn_sched_barrier(0);
-                const uint32_t word = sw[kb >> 1] >> (16 * (kb & 1));
-                u32x4 s0, s1;
-                to_operands(sigma_bits(word & 0xFFu), sigma_bits((word >> 8) & 0xFFu), &s0, &s1);
+                u32x4 s[2];
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) s[nt] = sigma8((sg[nt][kb >> 1] >> (16 * (kb & 1))) & 0xFFu);
 #pragma unroll
                 for (int m = 0; m < NMT; ++m) {
-                    const int r = 32 * m + (l & 31);
-                    const int kc = 2 * kb + (l >> 5);
-                    const u32x4 p1 = qrows[r * kRowStride + kOffP1 + kc];
-                    const u32x4 p2 = qrows[r * kRowStride + kOffP2 + kc];
-                    acc2[m][0] = mfma(p1, s0, acc2[m][0]);
-                    acc2[m][0] = mfma(p2, s0, acc2[m][0]);
-                    acc2[m][1] = mfma(p1, s1, acc2[m][1]);
-                    acc2[m][1] = mfma(p2, s1, acc2[m][1]);
+                    const int r = (32 * m + n) * kRowStride + 2 * kb + hh;
+                    const u32x4 p1 = lds.qrows[r + kOffP1];
+                    const u32x4 p2 = lds.qrows[r + kOffP2];
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt) {
+                        acc2[m][nt] = mfma(p1, s[nt], acc2[m][nt]);
+                        acc2[m][nt] = mfma(p2, s[nt], acc2[m][nt]);
+                    }
                 }
             }
         }
-        // per-key factors for the two 32-key halves: lane l of half nt needs
-        // key nt * 32 + l % 32
-        float kn[2], kg[2];
-        {
-            const auto sn = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, nhat),
-                                                             __builtin_bit_cast(uint32_t, nhat), false, false);
-            const float gk = ghat * a.qjl_scale;
-            const auto sg = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, gk),
-                                                             __builtin_bit_cast(uint32_t, gk), false, false);
-            const uint32_t n0 = sn[0], n1 = sn[1], g0 = sg[0], g1 = sg[1];
-            kn[0] = __builtin_bit_cast(float, n0);
-            kn[1] = __builtin_bit_cast(float, n1);
-            kg[0] = __builtin_bit_cast(float, g0);
-            kg[1] = __builtin_bit_cast(float, g1);
+
+        // epilogue: rows past nrows fall outside the descriptor's range, keys
+        // past the end get an offset beyond it
+        const rsrc_t rs = make_rsrc(a.scores + static_cast<int64_t>(row0) * a.ld + kbase,
+                                    static_cast<uint32_t>(((nrows - 1) * a.ld + (nk - kbase)) * 4));
+        uint32_t voff[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            const int key = 32 * nt + n;
+            voff[nt] = kbase + key < nk ? static_cast<uint32_t>((4 * hh * a.ld + key) * 4) : 0x80000000u;
         }
 #pragma unroll
         for (int m = 0; m < NMT; ++m)
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                const int64_t key = kbase + 32 * nt + (l & 31);
+            for (int r = 0; r < 16; ++r) {
+                const int rowc = 32 * m + 8 * (r / 4) + (r % 4);   // row without the lane-half term 4 hh
+                const float* rsv = lds.rsc[rowc + 4 * hh];
+                const float s0 = rsv[0], s1 = rsv[1], s2 = rsv[2];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = 32 * m + 8 * (r / 4) + 4 * (l >> 5) + (r % 4);
-                    float v = acc1[m][nt][r] * (rscale[row][0] * inv_sc);
-                    if constexpr (QJL) v = __builtin_fmaf(kg[nt], acc2[m][nt][r] * rscale[row][1], v);
+                for (int nt = 0; nt < 2; ++nt) {
+                    const float e1 = acc1[m][nt][r];
+                    float v = e1 * s0;
+                    if constexpr (PAD) v = __builtin_fmaf(s2, cpad[nt], v);
+                    if constexpr (QJL) {
+                        const float e2 = acc2[m][nt][r];
+                        v = __builtin_fmaf(kg[nt], e2 * s1, v);
+                    }
                     v *= kn[nt];
-                    if (row < nrows && key < nk) a.scores[static_cast<int64_t>(row0 + row) * a.ld + key] = v;
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rs, voff[nt],
+                                                          static_cast<int>(rowc * a.ld * 4), kNonTemporal);
                 }
             }
     }
 }
 
-template <int B, bool QJL, int NC, int NMT>
+template <int B, bool QJL, bool PAD, int NMT>
 static void launch_main(const MainArgs& a, int kv_heads, int qblocks, hipStream_t s) {
     const int64_t ntiles = (a.t + 63) / 64;
     const int64_t want = (ntiles + 3) / 4;
     const int64_t per_head_cap = (4096 + kv_heads * qblocks - 1) / (kv_heads * qblocks);
     const int gx = static_cast<int>(want < per_head_cap ? want : (per_head_cap > 0 ? per_head_cap : 1));
-    hipLaunchKernelGGL((score_kernel<B, QJL, NC, NMT>), dim3(gx, kv_heads * qblocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((score_kernel<B, QJL, PAD, NMT>), dim3(gx, kv_heads * qblocks), dim3(kBlock), 0, s, a);
 }
 
 template <int B, bool QJL>
 static void launch_main_b(bool dense, int nmt, const MainArgs& a, int kv_heads, int qblocks, hipStream_t s) {
     if (dense) {
-        if (nmt == 1) launch_main<B, QJL, 128, 1>(a, kv_heads, qblocks, s);
-        else launch_main<B, QJL, 128, 2>(a, kv_heads, qblocks, s);
+        if (nmt == 1) launch_main<B, QJL, false, 1>(a, kv_heads, qblocks, s);
+        else launch_main<B, QJL, false, 2>(a, kv_heads, qblocks, s);
     } else {
-        if (nmt == 1) launch_main<B, QJL, 129, 1>(a, kv_heads, qblocks, s);
-        else launch_main<B, QJL, 129, 2>(a, kv_heads, qblocks, s);
+        if (nmt == 1) launch_main<B, QJL, true, 1>(a, kv_heads, qblocks, s);
+        else launch_main<B, QJL, true, 2>(a, kv_heads, qblocks, s);
     }
 }
 
@@ -352,11 +416,12 @@ hipError_t score(const ScoreTables& t, const float* q, int hq, int group, const 
     pa.dense = t.dense;
     pa.qjl = t.qjl;
     pa.rotmat = t.rot.rotmat;
-    pa.pi_hi = t.den.pi_hi;
-    pa.pi_lo = t.den.pi_lo;
-    pa.s_rows = t.dense ? t.den.s_rows : t.rot.s_rows;
+    pa.pit_hi = t.den.pit_hi;
+    pa.pit_lo = t.den.pit_lo;
+    pa.s_cols = t.dense ? t.den.s_cols : t.rot.s_cols;
     pa.rows = static_cast<u32x4*>(ws);
-    pa.scales = reinterpret_cast<float*>(static_cast<char*>(ws) + static_cast<size_t>(kScoreChunkRows) * kRowChunks * 16);
+    pa.scalars =
+        reinterpret_cast<float*>(static_cast<char*>(ws) + static_cast<size_t>(kScoreChunkRows) * kRowChunks * 16);
     hipLaunchKernelGGL(score_prologue, dim3(hq), dim3(128), 0, s, pa);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -372,7 +437,7 @@ hipError_t score(const ScoreTables& t, const float* q, int hq, int group, const 
     a.group = group;
     a.rows_per_block = group < 64 ? group : 64;
     a.rows = pa.rows;
-    a.scales = pa.scales;
+    a.scalars = pa.scalars;
     a.cent = t.dense ? t.den.cent : t.rot.cent;
     a.qjl_scale = t.qjl_scale;
     a.scores = scores;
