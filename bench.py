@@ -44,6 +44,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sweep", action="store_true", help="also time the MSE-only roundtrip over an N sweep")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="after timing, run 3 plain device copies of this many bytes (counter calibration)")
+    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this bench with "
+                         "--copy-bytes into profiles/traffic.json, then exit")
     return ap.parse_args()
 
 
@@ -69,6 +74,70 @@ def measured_traffic(kernel, digest):
     if not e or e.get("sources") != digest:
         return None
     return e.get("bytes_per_launch")
+
+
+ROUNDTRIP_KERNEL = "rq_quant_kernel<2, true, true, true, true>"
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def _counter_dispatches(path, counter):
+    """{kernel name: [counter value (KiB) per dispatch]} from a rocprofv3 CSV."""
+    import csv
+    sums, names = {}, {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            d = r["Dispatch_Id"]
+            sums[d] = sums.get(d, 0.0) + float(r["Counter_Value"])
+            names[d] = r["Kernel_Name"]
+    out = {}
+    for d, v in sums.items():
+        out.setdefault(names[d], []).append(v)
+    return out
+
+
+def ingest_counters(fetch_csv, write_csv, copy_bytes):
+    """HBM bytes per roundtrip launch, scaled by a plain copy of known size.
+
+    The calibration copy is the largest copyBuffer dispatch of the run (the
+    --copy-bytes copies); each counter is divided by what it reads for that
+    copy per byte moved."""
+    fetch = _counter_dispatches(fetch_csv, "FETCH_SIZE")
+    write = _counter_dispatches(write_csv, "WRITE_SIZE")
+
+    def values(d, name):
+        hits = [v for k, vs in d.items() if name in k for v in vs]
+        if not hits:
+            raise SystemExit(f"no dispatch of {name} in the counter CSV")
+        return hits
+
+    f_copy = max(values(fetch, COPY_KERNEL)) * 1024.0
+    w_copy = max(values(write, COPY_KERNEL)) * 1024.0
+    fr, wr = values(fetch, ROUNDTRIP_KERNEL), values(write, ROUNDTRIP_KERNEL)
+    f_rt = sum(fr) / len(fr) * 1024.0
+    w_rt = sum(wr) / len(wr) * 1024.0
+    cf, cw = f_copy / copy_bytes, w_copy / copy_bytes
+    entry = {
+        "sources": kernel_sources_digest(),
+        "kernel": ROUNDTRIP_KERNEL,
+        "dispatches": len(fr),
+        "fetch_kib_raw": round(f_rt / 1024.0, 1), "write_kib_raw": round(w_rt / 1024.0, 1),
+        "copy_bytes": copy_bytes, "copy_fetch_factor": round(cf, 4), "copy_write_factor": round(cw, 4),
+        "fetch_bytes_per_launch": round(f_rt / cf), "write_bytes_per_launch": round(w_rt / cw),
+        "bytes_per_launch": round(f_rt / cf + w_rt / cw),
+    }
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        t = {}
+    t["rq_roundtrip_qjl3_f16"] = entry
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as f:
+        json.dump(t, f, indent=1)
+    print(json.dumps(entry))
 
 
 def cpu_baseline(x_host, q_host):
@@ -99,6 +168,9 @@ def cpu_baseline(x_host, q_host):
 
 def main():
     a = parse()
+    if a.ingest_counters:
+        ingest_counters(a.ingest_counters[0], a.ingest_counters[1], a.copy_bytes or (256 << 20))
+        return
     if a.gpus != 1:
         print(f"bench.py measures one GPU: this build runs on a single MI355X and has no multi-GPU path "
               f"(asked for --gpus {a.gpus})", file=sys.stderr)
@@ -208,6 +280,14 @@ def main():
             sweep[str(n)] = {"us": round(us, 2), "gbs": round(n * mb / (us * 1e-6) / 1e9, 1)}
             del xb, yb, rb
         extras["mse3_sweep"] = sweep
+
+    if a.copy_bytes:
+        src = torch.empty(a.copy_bytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     out = {
         "metric": "quant+dequant vectors/s (d=128, 3-bit) + % HBM roofline; q·k scores/s",

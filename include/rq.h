@@ -128,6 +128,17 @@ int rq_layout(int d, int bits, int mode, rq_layout_t* out);
  * Same status rules as rq_layout. */
 int rq_host_params(int d, int bits, uint64_t seed, int mode, rq_params_host_t* out);
 
+/* The 256-slot lookup table through which the rotor kernels evaluate the
+ * nearest-centroid code #{k : y > t_k} and its centroid (Lloyd-Max codebook
+ * of rq_host_params; README "How RotorQuant Works", quantize step).  A
+ * unit-domain coordinate y falls in slot
+ *   s = (bits(fp32 fma(y, 2032, *bias)) & 0xFF0) / 16,
+ * and then code = table[s][0] + (y > thr), thr = bit pattern table[s][1]
+ * (+inf if the slot holds no boundary), centroid = y > thr ? table[s][3]
+ * : table[s][2] (fp32 bit patterns).  Host only; table is [256][4] u32.
+ * Same status rules as rq_layout. */
+int rq_host_quantizer(int d, int bits, int mode, float* bias, uint32_t* table);
+
 /* Opens a session on the current HIP device: computes the tables as
  * rq_host_params does, uploads them once (synchronously) and returns the
  * ctx in *out.  On any failure *out is set to NULL and nothing is leaked. */

@@ -25,7 +25,7 @@ RQ_SCORE_CHUNK = 4096
 
 STATUS_NAMES = {0: "RQ_OK", 1: "RQ_EINVAL", 2: "RQ_EUNSUPPORTED", 3: "RQ_ENOMEM", 4: "RQ_EHIP"}
 
-EXPORTS = ("rq_layout", "rq_host_params", "rq_init", "rq_free", "rq_get_layout", "rq_get_params",
+EXPORTS = ("rq_layout", "rq_host_params", "rq_host_quantizer", "rq_init", "rq_free", "rq_get_layout", "rq_get_params",
            "rq_quantize", "rq_dequantize", "rq_roundtrip", "rq_score", "tq_quantize", "tq_dequantize",
            "tq_roundtrip", "rq_last_error", "rq_version")
 
@@ -64,6 +64,7 @@ def _load():
     sig = {
         "rq_layout": ([I, I, I, ctypes.POINTER(Layout)], I),
         "rq_host_params": ([I, I, U64, I, ctypes.POINTER(ParamsHost)], I),
+        "rq_host_quantizer": ([I, I, I, P, P], I),
         "rq_init": ([I, I, U64, I, ctypes.POINTER(P)], I),
         "rq_free": ([P], None),
         "rq_get_layout": ([P, ctypes.POINTER(Layout)], I),
@@ -79,7 +80,11 @@ def _load():
         "rq_version": ([], ctypes.c_char_p),
     }
     for name, (args, res) in sig.items():
-        f = getattr(lib, name)
+        try:
+            f = getattr(lib, name)
+        except AttributeError:
+            raise ImportError(f"{LIB_PATH} does not export {name}: the library is older than its sources; "
+                              "rebuild it (__graft_entry__.build())") from None
         f.argtypes = args
         f.restype = res
     return lib
@@ -147,6 +152,14 @@ def rq_host_params(d, bits, seed, mode):
                      ("rotors", "rotmats", "centroids", "boundaries", "pi", "s")])
     _check(_lib.rq_host_params(d, bits, seed, mode, ctypes.byref(p)))
     return arrays
+
+
+def rq_host_quantizer(d, bits, mode):
+    """(bias, table [256, 4] uint32) of the kernels' slot lookup (host only)."""
+    bias = ctypes.c_float()
+    table = np.zeros((256, 4), np.uint32)
+    _check(_lib.rq_host_quantizer(d, bits, mode, ctypes.byref(bias), table.ctypes.data))
+    return float(bias.value), table
 
 
 def _param_arrays(lay, mode):

@@ -135,6 +135,17 @@ int rq_host_params(int d, int bits, uint64_t seed, int mode, rq_params_host_t* o
     return RQ_OK;
 }
 
+int rq_host_quantizer(int d, int bits, int mode, float* bias, uint32_t* table) {
+    if (!bias || !table) return fail(RQ_EINVAL, "rq_host_quantizer: NULL argument");
+    rqh::Tables t;
+    std::string err;
+    const int rc = rqh::make_tables(d, bits, 0, mode, &t, &err);
+    if (rc) return fail(rc == 2 ? RQ_EUNSUPPORTED : RQ_EINVAL, "rq_host_quantizer: " + err);
+    *bias = t.bin_b;
+    std::memcpy(table, t.bins.data(), t.bins.size() * sizeof(rqh::BinEntry));
+    return RQ_OK;
+}
+
 int rq_get_layout(const rq_ctx* ctx, rq_layout_t* out) {
     if (!ctx || !out) return fail(RQ_EINVAL, "rq_get_layout: NULL argument");
     to_abi(ctx->host.lay, out);

@@ -127,3 +127,57 @@ def test_single_hip_runtime_in_process():
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT)
     assert out.returncode == 0, out.stderr
     assert out.stdout.strip() == "1"
+
+
+def _slot(y, bias):
+    """The kernels' slot of fp32 y: fp32 fma(y, 2032, bias), mantissa bits
+    4..11.  y * 2032 is exact in float64 and so is the sum whenever a
+    double rounding could matter, so float64 then float32 is the single
+    fp32 rounding of the fma."""
+    t = (y.astype(np.float64) * 2032.0 + np.float64(bias)).astype(np.float32)
+    return (t.view(np.uint32) & 0xFF0) >> 4
+
+
+def _edge_and_boundary_probes(boundaries, bias, ulps):
+    """fp32 values within `ulps` ulps of every boundary and every slot edge."""
+    pts = [boundaries.astype(np.float32)]
+    for k in range(257):
+        pts.append(np.float32(((16 * k - 0.5) - (bias - 12582912.0)) / 2032.0))
+    pts = np.concatenate([np.atleast_1d(p) for p in pts]).astype(np.float32)
+    out = [pts]
+    up, dn = pts.copy(), pts.copy()
+    for _ in range(ulps):
+        up = np.nextafter(up, np.float32(2.0))
+        dn = np.nextafter(dn, np.float32(-2.0))
+        out += [up, dn]
+    v = np.concatenate(out)
+    return v[np.abs(v) <= np.float32(1.001)]
+
+
+@pytest.mark.parametrize("bits,mode", [(b, OP.MSE) for b in (1, 2, 3, 4)] + [(b, OP.QJL) for b in (2, 3, 4, 5)])
+def test_slot_table_is_exact_nearest_centroid(K, bits, mode):
+    """The kernels' 256-slot lookup gives #{k : y > t_k} and c[code] for every
+    fp32 y in [-1.001, 1.001]: random draws, both sides of every boundary and
+    every slot edge within 60 ulps, and the end points."""
+    p = K.rq_host_params(128, bits, 0, mode)
+    c, t = p["centroids"], p["boundaries"]
+    bias, table = K.rq_host_quantizer(128, bits, mode)
+    rng = np.random.default_rng(bits * 10 + mode)
+    y = np.concatenate([
+        rng.normal(0.0, 0.09, 400_000).astype(np.float32),
+        rng.uniform(-1.001, 1.001, 200_000).astype(np.float32),
+        _edge_and_boundary_probes(t, bias, 60),
+        np.array([-1.001, -1.0, -0.0, 0.0, 1.0, 1.001], np.float32),
+    ])
+    ref = (y[:, None] > t[None, :]).sum(axis=1)
+    e = table[_slot(y, bias)]
+    thr = e[:, 1].view(np.float32)
+    gt = y > thr
+    code = e[:, 0] + gt
+    val = np.where(gt, e[:, 3], e[:, 2]).view(np.float32)
+    assert np.array_equal(code, ref)
+    assert np.array_equal(val, c[ref])
+    # slots are monotone in y and no slot holds two boundaries
+    s = _slot(np.sort(y), bias)
+    assert np.all(np.diff(s.astype(np.int64)) >= 0)
+    assert len(set(_slot(t, bias).tolist())) == len(t)
