@@ -24,9 +24,8 @@
  *    rq_init), RQ_EHIP (a HIP runtime or launch error).  Nothing aborts and no
  *    C++ exception crosses the ABI.
  *  - A ctx may be used by one host thread at a time.  Calls with one ctx on
- *    different streams may run concurrently EXCEPT rq_score / tq-ctx scoring,
- *    which stage rotated queries in a ctx-owned workspace: serialise scoring
- *    calls that share a ctx.
+ *    different streams may run concurrently: the ctx holds only read-only
+ *    parameter tables.
  *  - Identical inputs give identical output bytes.
  *
  * Record layout (structure of arrays, one row per vector; all little endian):
@@ -71,7 +70,7 @@ extern "C" {
 #define RQ_F32 0
 #define RQ_F16 1
 
-/* Largest number of query rows one rq_score launch stages; larger hq is
+/* Largest number of query rows one rq_score launch processes; larger hq is
  * processed in chunks of this many rows by the same call. */
 #define RQ_SCORE_CHUNK 4096
 
@@ -194,8 +193,9 @@ int rq_roundtrip(rq_ctx* ctx, const void* x, int x_dtype, int64_t n, int64_t ldx
  *   scores  [hq][ld_scores] fp32, t <= ld_scores <= 2^23; row h gets
  *           n^_t (<q_h, x~_mse,u(t)> + gamma^_t sqrt(pi/2)/m <S q_h, sigma_t>),
  *           raw: no 1/sqrt(d), no softmax.
- * Works for rotor and dense sessions.  Uses the ctx's query workspace (see
- * conventions). */
+ * Works for rotor and dense sessions.  The rotated queries and S q are built
+ * on chip by the scoring kernel (no workspace); launches take at most
+ * RQ_SCORE_CHUNK query rows each. */
 int rq_score(rq_ctx* ctx, const float* q, int hq, int group,
              const uint32_t* codes, const uint16_t* norms, const uint32_t* signs,
              const uint16_t* rnorms, int64_t t, int64_t kv_stride,

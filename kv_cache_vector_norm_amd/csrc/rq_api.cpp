@@ -74,14 +74,13 @@ struct rq_ctx {
     uint16_t* s_cols = nullptr;
     uint16_t* s_fwd = nullptr;
     uint16_t* s_back = nullptr;
+    uint16_t* phi_hi = nullptr;
+    uint16_t* phi_lo = nullptr;
     // dense (TurboQuant): Pi split into exact half pairs, both layouts
     uint16_t* pi_hi = nullptr;
     uint16_t* pi_lo = nullptr;
     uint16_t* pit_hi = nullptr;
     uint16_t* pit_lo = nullptr;
-    // scoring workspace
-    void* qws = nullptr;
-    size_t qws_bytes = 0;
 };
 
 extern "C" {
@@ -194,7 +193,30 @@ int rq_init(int d, int bits, uint64_t seed, int mode, rq_ctx** out) {
         return hipMemcpy(*dst, src, bytes, hipMemcpyHostToDevice);
     };
     // derived half tables
-    std::vector<uint16_t> s_cols, s_fwd, s_back, pi_hi, pi_lo, pit_hi, pit_lo;
+    std::vector<uint16_t> s_cols, s_fwd, s_back, pi_hi, pi_lo, pit_hi, pit_lo, phi_hi, phi_lo;
+    // exact-enough half pair of 16 v: hi = half(16 v), lo = half((16 v - hi) * 2^11)
+    auto split16 = [](double v, uint16_t* hi, uint16_t* lo) {
+        const double x = v * 16.0;
+        const uint16_t h = rqh::double_to_half_rne(x);
+        const int ex = (h >> 10) & 0x1F, mant = h & 0x3FF;
+        double hv = ex == 0 ? std::ldexp(static_cast<double>(mant), -24) : std::ldexp(1.0 + mant / 1024.0, ex - 15);
+        if (h & 0x8000) hv = -hv;
+        *hi = h;
+        *lo = rqh::double_to_half_rne((x - hv) * 2048.0);
+    };
+    if (!(mode & RQ_DENSE)) {
+        // Phi[i][j]: slot i = 3 g + r reads coordinates 3 g .. 3 g + 2 through row r of M_g
+        phi_hi.assign(static_cast<size_t>(n) * n, 0);
+        phi_lo.assign(static_cast<size_t>(n) * n, 0);
+        for (int i = 0; i < n; ++i) {
+            const int g = i / 3, r = i % 3;
+            for (int c = 0; c < 3; ++c) {
+                const int j = 3 * g + c;
+                if (j >= n) continue;
+                split16(static_cast<double>(t.rotmats[9 * g + 3 * r + c]), &phi_hi[i * n + j], &phi_lo[i * n + j]);
+            }
+        }
+    }
     if (mode & RQ_QJL) {
         s_cols.resize(t.s.size());
         for (int j = 0; j < n; ++j)
@@ -221,14 +243,8 @@ int rq_init(int d, int bits, uint64_t seed, int mode, rq_ctx** out) {
         pit_lo.resize(t.pi.size());
         for (int r = 0; r < n; ++r)
             for (int c = 0; c < n; ++c) {
-                const double v = static_cast<double>(t.pi[r * n + c]) * 16.0;
-                const uint16_t h = rqh::double_to_half_rne(v);
-                // value of h
-                const int ex = (h >> 10) & 0x1F, mant = h & 0x3FF;
-                double hv = ex == 0 ? std::ldexp(static_cast<double>(mant), -24)
-                                    : std::ldexp(1.0 + mant / 1024.0, ex - 15);
-                if (h & 0x8000) hv = -hv;
-                const uint16_t lo = rqh::double_to_half_rne((v - hv) * 2048.0);
+                uint16_t h, lo;
+                split16(static_cast<double>(t.pi[r * n + c]), &h, &lo);
                 pi_hi[r * n + c] = h;
                 pi_lo[r * n + c] = lo;
                 pit_hi[c * n + r] = h;
@@ -238,6 +254,8 @@ int rq_init(int d, int bits, uint64_t seed, int mode, rq_ctx** out) {
     do {
         if (!(mode & RQ_DENSE)) {
             if ((e = upload(reinterpret_cast<void**>(&ctx->rotmat), t.rotmats.data(), t.rotmats.size() * 4)) != hipSuccess) break;
+            if ((e = upload(reinterpret_cast<void**>(&ctx->phi_hi), phi_hi.data(), phi_hi.size() * 2)) != hipSuccess) break;
+            if ((e = upload(reinterpret_cast<void**>(&ctx->phi_lo), phi_lo.data(), phi_lo.size() * 2)) != hipSuccess) break;
         }
         if ((e = upload(reinterpret_cast<void**>(&ctx->thr), t.boundaries.data(), t.boundaries.size() * 4)) != hipSuccess) break;
         if ((e = upload(reinterpret_cast<void**>(&ctx->cent), t.centroids.data(), t.centroids.size() * 4)) != hipSuccess) break;
@@ -255,8 +273,6 @@ int rq_init(int d, int bits, uint64_t seed, int mode, rq_ctx** out) {
             if ((e = upload(reinterpret_cast<void**>(&ctx->pit_hi), pit_hi.data(), pit_hi.size() * 2)) != hipSuccess) break;
             if ((e = upload(reinterpret_cast<void**>(&ctx->pit_lo), pit_lo.data(), pit_lo.size() * 2)) != hipSuccess) break;
         }
-        ctx->qws_bytes = static_cast<size_t>(RQ_SCORE_CHUNK) * rqk::kScoreQueryBytes;
-        if ((e = da.alloc(&ctx->qws, ctx->qws_bytes)) != hipSuccess) break;
     } while (false);
     if (e != hipSuccess) {
         da.release();
@@ -318,6 +334,8 @@ static rqk::RotorTables rotor_tables(const rq_ctx* c) {
     t.s_cols = c->s_cols;
     t.s_fwd = c->s_fwd;
     t.s_back = c->s_back;
+    t.phi_hi = c->phi_hi;
+    t.phi_lo = c->phi_lo;
     t.qjl_scale = static_cast<float>(std::sqrt(M_PI / 2.0) / rqh::kQjlRows);
     t.mse_bits = c->host.lay.mse_bits;
     t.qjl = c->host.lay.mode & RQ_QJL;
@@ -457,7 +475,7 @@ int rq_score(rq_ctx* ctx, const float* q, int hq, int group, const uint32_t* cod
     for (int h0 = 0; h0 < kv_heads; h0 += heads_per_chunk) {
         const int nh = std::min(heads_per_chunk, kv_heads - h0);
         const hipError_t e = rqk::score(st, q + static_cast<int64_t>(h0) * group * rqh::kDim, nh * group, group,
-                                        codes, norms, signs, rnorms, t, kv_stride, h0, ctx->qws,
+                                        codes, norms, signs, rnorms, t, kv_stride, h0,
                                         scores + static_cast<int64_t>(h0) * group * ld_scores, ld_scores, s);
         if (e != hipSuccess) return hip_fail(e, fn);
     }

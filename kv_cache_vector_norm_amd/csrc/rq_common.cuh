@@ -99,6 +99,12 @@ __device__ __forceinline__ uint32_t cvt_pk(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), f16x2));
 }
 
+// Two halves times 2^11 (v_pk_mul_f16; exact for |x| < 32).
+__device__ __forceinline__ uint32_t pk_scale2048(uint32_t h2) {
+    const f16x2 v = __builtin_bit_cast(f16x2, h2) * f16x2{static_cast<f16>(2048.0f), static_cast<f16>(2048.0f)};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
 // Exact split of a float pair: (a, b) ~= hi + lo, hi = half(a, b) and lo the
 // halves of the fp32 residuals a - hi (exact) rounded to nearest even.
 __device__ __forceinline__ void split_pair(float a, float b, uint32_t* hi, uint32_t* lo) {
@@ -143,6 +149,31 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
 // Byte range of `rows_left` rows of `row_bytes` (all of 32-bit space for a full tile).
 __device__ __forceinline__ uint32_t tile_range(int64_t rows_left, int64_t row_bytes) {
     return rows_left >= 64 ? 0xFFFFFFFFu : static_cast<uint32_t>(rows_left * row_bytes);
+}
+
+// A tile's 64 rows of 256 bytes (from byte `col_off` of each row) in
+// registers: lane l holds chunk l % 16 of rows 4 it + l / 16; rows at or
+// beyond n read as zero.  tile_put then writes them into the LDS tile.
+struct TileRegs {
+    u32x4 v[16];
+};
+__device__ __forceinline__ void tile_fetch(const char* __restrict__ src, int64_t ld_bytes, int64_t base, int64_t n,
+                                           int col_off, TileRegs& r, int l) {
+    const int rr = l >> 4, c = l & 15;
+    const uint32_t voff = static_cast<uint32_t>(rr) * static_cast<uint32_t>(ld_bytes) + static_cast<uint32_t>(c * 16);
+    const rsrc_t rs = make_rsrc(src + base * ld_bytes + col_off, tile_range(n - base, ld_bytes));
+    const int step = static_cast<int>(4 * ld_bytes);
+#pragma unroll
+    for (int it = 0; it < 16; ++it) r.v[it] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, it * step, kNonTemporal);
+}
+__device__ __forceinline__ void tile_put(const TileRegs& r, u32x4* __restrict__ tile, int l) {
+    const int rr = l >> 4, c = l & 15;
+    wave_lds_sync();
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+        const u32x4 v = r.v[it];
+        tile[swz(4 * it + rr, c)] = v;
+    }
 }
 
 // Reads 64 rows of 256 bytes (starting at byte offset `col_off` of each row)

@@ -27,6 +27,8 @@ struct RotorTables {
     const uint16_t* s_cols;  // [128][128] halves, S^T (QJL)
     const uint16_t* s_fwd;   // S with rows permuted for the quantiser's MFMA layout
     const uint16_t* s_back;  // S^T with rows and columns permuted for the dequantiser
+    const uint16_t* phi_hi;  // 16 Phi = hi + 2^-11 lo: the rotor transform of the first 128
+    const uint16_t* phi_lo;  //   slots as a block-diagonal 128 x 128 matrix (scoring)
     float qjl_scale;
     int mse_bits;
     bool qjl;
@@ -57,10 +59,7 @@ struct ScoreTables {
     float qjl_scale;
 };
 
-// Bytes of staged query data per query row (rotated query and S q as exact
-// half pairs plus two scales), see rq_score.hip, and the number of query rows
-// one scoring launch stages (RQ_SCORE_CHUNK of rq.h).
-constexpr size_t kScoreQueryBytes = 1408;
+// Query rows per scoring launch (RQ_SCORE_CHUNK of rq.h).
 constexpr int kScoreChunkRows = 4096;
 
 hipError_t rotor_quantize(const RotorTables& t, const void* x, bool in_f16, int64_t ldx_bytes, int64_t n,
@@ -81,9 +80,9 @@ hipError_t dense_dequantize(const DenseTables& t, const uint32_t* codes, const u
 
 // Scores hq query rows (group rows per KV head) against t keys per KV head;
 // KV head j (0-based within this call) reads record rows
-// (kv_head0 + j) * kv_stride + [0, t).  ws is the session's query workspace.
+// (kv_head0 + j) * kv_stride + [0, t).
 hipError_t score(const ScoreTables& t, const float* q, int hq, int group, const uint32_t* codes,
                  const uint16_t* norms, const uint32_t* signs, const uint16_t* rnorms, int64_t tkeys,
-                 int64_t kv_stride, int kv_head0, void* ws, float* scores, int64_t ld_scores, hipStream_t s);
+                 int64_t kv_stride, int kv_head0, float* scores, int64_t ld_scores, hipStream_t s);
 
 }  // namespace rqk

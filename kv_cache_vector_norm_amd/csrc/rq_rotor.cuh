@@ -264,6 +264,10 @@ struct VecIn<true> {
     __device__ float get(int i) const { return h2f((i & 1) ? (h[i >> 1] >> 16) : (h[i >> 1] & 0xFFFFu)); }
     __device__ void load(const char* x, int64_t ld_bytes, int64_t base, int64_t n, u32x4* t, int l) {
         tile_load(x, ld_bytes, base, n, 0, t, l);
+        own_row(t, l);
+    }
+    // own row of a tile already in LDS
+    __device__ void own_row(const u32x4* t, int l) {
         wave_lds_sync();
 #pragma unroll
         for (int c = 0; c < 16; ++c) {
@@ -287,11 +291,28 @@ struct VecIn<false> {
 };
 
 // Rotor matrices are read with scalar loads (constant address space) two
-// groups ahead of use.
+// groups ahead of use.  A scalar-cache miss costs an L2 round trip, far more
+// than the two groups of lead, so every 64-byte line of the table is touched
+// once per wave before the tile loop (the loads overlap the block's staging).
 typedef __attribute__((address_space(4))) const float* cfloat_ptr;
 __device__ __forceinline__ void load_mat(cfloat_ptr p, float (&m)[9]) {
 #pragma unroll
     for (int k = 0; k < 9; ++k) m[k] = p[k];
+}
+constexpr int kRotLines = (kGroups * 9 + 15) / 16;
+struct RotWarm {
+    uint32_t v[kRotLines];
+};
+// Issues one scalar load per line; finish() consumes them (one wait) later.
+__device__ __forceinline__ void warm_rotor_table(cfloat_ptr p, RotWarm& w) {
+#pragma unroll
+    for (int i = 0; i < kRotLines; ++i) w.v[i] = __builtin_bit_cast(uint32_t, p[16 * i]);
+}
+__device__ __forceinline__ void warm_finish(const RotWarm& w) {
+    uint32_t acc = 0u;
+#pragma unroll
+    for (int i = 0; i < kRotLines; ++i) acc ^= w.v[i];
+    asm volatile("" ::"s"(acc));
 }
 
 // LDS: the slot table first (LDS address 0, so a slot's byte offset is its
@@ -321,25 +342,44 @@ __global__ __launch_bounds__(256) void rq_quant_kernel(RotorDev P, const char* _
     u32x4* s_fwd = lds.s_fwd;
     u32x4* s_back = lds.s_back;
 
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t ntiles = (n + 63) / 64;
+    const int64_t t0 = blockIdx.x * 4LL + wave;
+    // the first tile's input is requested before the block's staging, so the
+    // two latencies overlap
+    TileRegs first;
+    if constexpr (IN_F16) {
+        if (t0 < ntiles) tile_fetch(x, ldx_bytes, t0 * 64, n, 0, first, lane_id());
+    }
+    // rotor table lines into the scalar cache, in flight with the staging
+    RotWarm warm;
+    warm_rotor_table(reinterpret_cast<cfloat_ptr>(reinterpret_cast<uintptr_t>(P.rotmat)), warm);
     stage_bins<QJL>(P.bins, bins);
     if constexpr (QJL) mat_to_lds(P.s_fwd, s_fwd);
     if constexpr (BACK) mat_to_lds(P.s_back, s_back);
     __syncthreads();
+    if constexpr (IN_F16) {
+        if (t0 < ntiles) tile_put(first, tiles[wave], lane_id());
+    }
+    warm_finish(warm);
 
     const float ba = P.bin_a * (1.0f / D), bb = P.bin_b;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     u32x4* tile = tiles[wave];
     uint32_t* stage = reinterpret_cast<uint32_t*>(tile);
-    const int64_t ntiles = (n + 63) / 64;
     const char* binc = reinterpret_cast<const char*>(bins);
 
-    for (int64_t t = blockIdx.x * 4LL + wave; t < ntiles; t += gridDim.x * 4LL) {
+    for (int64_t t = t0; t < ntiles; t += gridDim.x * 4LL) {
         const int64_t base = t * 64;
         const int z = opaque_zero();
         const int l = lane_id() + z;
         const cfloat_ptr rot = reinterpret_cast<cfloat_ptr>(reinterpret_cast<uintptr_t>(P.rotmat)) + z;
         VecIn<IN_F16> in;
-        in.load(x, ldx_bytes, base, n, tile, l);
+        if constexpr (IN_F16) {
+            if (t != t0) tile_load(x, ldx_bytes, base, n, 0, tile, l);
+            in.own_row(tile, l);
+        } else {
+            in.load(x, ldx_bytes, base, n, tile, l);
+        }
         float ss = 0.0f;
 #pragma unroll
         for (int i = 0; i < kD; ++i) {
@@ -378,7 +418,9 @@ __global__ __launch_bounds__(256) void rq_quant_kernel(RotorDev P, const char* _
             constexpr int s = g & 1;
             static_for<0, 3>([&](auto jc) __attribute__((always_inline)) {
                 constexpr int i = 3 * g + decltype(jc)::value;
-                if constexpr (i < kD) va[s][i - 3 * g] = in.get(i) * sc;
+                // fma with +0 (one v_fma_mix on the fp16 input); differs from
+                // x * sc only in the sign of a zero, which no step observes
+                if constexpr (i < kD) va[s][i - 3 * g] = __builtin_fmaf(in.get(i), sc, 0.0f);
                 else va[s][i - 3 * g] = 0.0f;
             });
             rot_fwd(mx[g % 3], va[s], ya[s]);

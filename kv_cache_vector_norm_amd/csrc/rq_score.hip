@@ -8,11 +8,13 @@
 // <q, M^T y^> = <M q, y^>).  Per key the score is
 //   n^ * ( <q^, c[code]> + gamma^ sqrt(pi/2)/m <S q, sigma> ).
 //
-// Prologue: one block per query row writes q^ and S q as exact half pairs
-// with a power-of-two row scale.  Main kernel: the staged query rows of one
-// KV head are the A operand of 32x32x16 MFMAs; the B operand is decoded from
-// the records straight into MFMA layout: lane (n, h) of a wave serves keys n
-// and 32 + n of the 64-key tile and K slots 8h..8h+7 of each 16-wide block,
+// Each block first builds, in LDS, the query side for its (KV head, <= 64
+// query rows): q^ and S q as exact fp16 half pairs with power-of-two row
+// scales (S q and, on the dense path, Pi q on 32x32x16 MFMAs from an exact
+// hi/lo split of the query; the rotor q^ in fp32 VALU).  Those rows are then
+// the A operand of the scoring MFMAs; the B operand is decoded from the
+// records straight into MFMA layout: lane (n, h) of a wave serves keys n and
+// 32 + n of the 64-key tile and K slots 8h..8h+7 of each 16-wide block,
 // turning two codes into packed centroid halves with one LDS lookup and sign
 // bits into +-1 halves with shifts.  The rotor pad coordinate (slot 128) is
 // added in fp32 in the epilogue.
@@ -30,35 +32,12 @@ namespace rqk {
 // C_lo = half((s_c c - C_hi) 2^11):
 //   Q1 C_hi + Q2 C_lo + Q3 C_hi = 2^11 s_q s_c <q^, c>  (to ~2^-22 relative),
 //   P1 sigma + P2 sigma = 2^11 s_p <S q, sigma>.
-// Row scalars (after the rows): 1 / (2^11 s_q), 1 / (2^11 s_p), and the
-// rotor pad slot q^_128 in fp32.
+// Row scalars: 1 / (2^11 s_q s_c), 1 / (2^11 s_p), and the rotor pad slot
+// q^_128 in fp32.
 constexpr int kQChunks = 16;
 constexpr int kRowChunks = 5 * kQChunks;     // 80
 constexpr int kRowStride = kRowChunks + 1;   // LDS row pitch (bank spread)
 constexpr int kOffQ1 = 0, kOffQ2 = kQChunks, kOffQ3 = 2 * kQChunks, kOffP1 = 3 * kQChunks, kOffP2 = 4 * kQChunks;
-constexpr int kRowScalars = 3;
-static_assert(kRowChunks * 16 + kRowScalars * 4 <= kScoreQueryBytes, "workspace row too small");
-
-struct ProArgs {
-    const float* q;
-    int hq;
-    bool dense, qjl;
-    const float* rotmat;      // rotor: [43][9]
-    const uint16_t* pit_hi;   // dense: Pi^T = (hi + lo 2^-11) / 16, row-major
-    const uint16_t* pit_lo;
-    const uint16_t* s_cols;   // QJL: S^T, row-major halves
-    u32x4* rows;              // [hq][kRowChunks]
-    float* scalars;           // [hq][kRowScalars]
-};
-
-__device__ __forceinline__ float block_max(float v, float* red) {
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-    __syncthreads();
-    v = fmaxf(red[0], red[1]);
-    __syncthreads();
-    return v;
-}
 
 // power-of-two scale putting the largest magnitude in [1, 2)
 __device__ __forceinline__ float pow2_scale(float maxabs) {
@@ -68,74 +47,19 @@ __device__ __forceinline__ float pow2_scale(float maxabs) {
     return ldexpf(1.0f, 1 - e);
 }
 
-// One block of 128 threads per query row; thread i owns slot i.  The
-// transposed tables are read so that a warp's loads are contiguous.
-__global__ __launch_bounds__(128) void score_prologue(ProArgs a) {
-    __shared__ float qs[kD];
-    __shared__ float red[2];
-    __shared__ __align__(16) uint16_t hv[5][kD];
-    const int h = blockIdx.x, i = threadIdx.x;
-    qs[i] = a.q[static_cast<int64_t>(h) * kD + i];
-    __syncthreads();
-    float qh = 0.0f, qpad = 0.0f;
-    if (!a.dense) {
-        const int g = i / 3, r = i % 3;
-        const float* m = a.rotmat + 9 * g;
-        const float v2 = (3 * g + 2 < kD) ? qs[3 * g + 2] : 0.0f;
-        qh = __builtin_fmaf(m[3 * r + 2], v2, __builtin_fmaf(m[3 * r + 1], qs[3 * g + 1], m[3 * r] * qs[3 * g]));
-        // slot 128: last row of group 42 (pad input 0)
-        const float* m42 = a.rotmat + 9 * 42;
-        qpad = __builtin_fmaf(m42[8], 0.0f, __builtin_fmaf(m42[7], qs[127], m42[6] * qs[126]));
-    } else {
-        float acc = 0.0f;
-#pragma unroll 16
-        for (int k = 0; k < kD; ++k) {
-            const float p =
-                (h2f(a.pit_hi[k * kD + i]) + h2f(a.pit_lo[k * kD + i]) * (1.0f / 2048.0f)) * 0.0625f;
-            acc = __builtin_fmaf(p, qs[k], acc);
-        }
-        qh = acc;
-    }
-    float pj = 0.0f;
-    if (a.qjl) {
-        float acc = 0.0f;
-#pragma unroll 16
-        for (int k = 0; k < kD; ++k) acc = __builtin_fmaf(h2f(a.s_cols[k * kD + i]), qs[k], acc);
-        pj = acc;
-    }
-    const float sq = pow2_scale(block_max(fabsf(qh), red));
-    const float sp = pow2_scale(block_max(fabsf(pj), red));
-    {
-        uint32_t hi, lo;
-        split_h11(qh * sq, &hi, &lo);
-        hv[0][i] = static_cast<uint16_t>(f2h(h2f(hi) * 2048.0f));
-        hv[1][i] = static_cast<uint16_t>(hi);
-        hv[2][i] = static_cast<uint16_t>(lo);
-        split_h11(pj * sp, &hi, &lo);
-        hv[3][i] = static_cast<uint16_t>(f2h(h2f(hi) * 2048.0f));
-        hv[4][i] = static_cast<uint16_t>(lo);
-    }
-    __syncthreads();
-    u32x4* row = a.rows + static_cast<int64_t>(h) * kRowChunks;
-    for (int c = i; c < kRowChunks; c += 128) row[c] = reinterpret_cast<const u32x4*>(&hv[c / kQChunks][0])[c % kQChunks];
-    if (i == 0) {
-        float* s = a.scalars + static_cast<int64_t>(h) * kRowScalars;
-        s[0] = 1.0f / (2048.0f * sq);
-        s[1] = 1.0f / (2048.0f * sp);
-        s[2] = qpad;
-    }
-}
-
 // -------------------------------------------------------------- main --
 struct MainArgs {
+    const float* q;            // [rows of this call][128] fp32 queries
+    const float* rotmat;       // rotor: [43][9]
+    const uint16_t* x_hi;      // 16 Pi (dense) or 16 Phi (rotor) = hi + 2^-11 lo, row-major halves
+    const uint16_t* x_lo;
+    const uint16_t* s_rows;    // QJL: S, row-major halves
     const uint32_t* codes;
     const uint16_t* norms;
     const uint32_t* signs;
     const uint16_t* rnorms;
     int64_t t, kv_stride;
     int kv_head0, group, rows_per_block;
-    const u32x4* rows;
-    const float* scalars;
     const float* cent;
     float qjl_scale;
     float* scores;
@@ -158,6 +82,258 @@ __device__ __forceinline__ uint32_t half_at(const uint16_t* __restrict__ src, in
     return __builtin_amdgcn_raw_buffer_load_b16(rs, static_cast<uint32_t>(2 * idx), 0, kNonTemporal);
 }
 
+// One tile's record in registers: lane l holds dword it * 64 + l of the
+// tile's code and sign runs, and the fp16 norm / residual norm of keys
+// l % 32 and 32 + l % 32.  Fetched one tile ahead.
+template <int W>
+struct RecRegs {
+    uint32_t c[W];
+    uint32_t s[4];
+    uint32_t kn[2], kg[2];
+};
+template <int W, bool QJL>
+__device__ __forceinline__ void rec_fetch(const MainArgs& a, int64_t rbase, int64_t kbase, RecRegs<W>& r, int l) {
+    const int64_t nk = a.t;
+    const rsrc_t rc = make_rsrc(a.codes + (rbase + kbase) * W, tile_range(nk - kbase, 4 * W));
+#pragma unroll
+    for (int it = 0; it < W; ++it)
+        r.c[it] = __builtin_amdgcn_raw_buffer_load_b32(rc, static_cast<uint32_t>(4 * l), 256 * it, kNonTemporal);
+    if constexpr (QJL) {
+        const rsrc_t rsg = make_rsrc(a.signs + (rbase + kbase) * 4, tile_range(nk - kbase, 16));
+#pragma unroll
+        for (int it = 0; it < 4; ++it)
+            r.s[it] = __builtin_amdgcn_raw_buffer_load_b32(rsg, static_cast<uint32_t>(4 * l), 256 * it, kNonTemporal);
+    }
+    const int n = l & 31;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+        r.kn[nt] = half_at(a.norms + rbase, kbase, nk, 32 * nt + n);
+        r.kg[nt] = QJL ? half_at(a.rnorms + rbase, kbase, nk, 32 * nt + n) : 0u;
+    }
+}
+
+// ------------------------------------------------------- query side --
+// Stores 4 consecutive fp16 values (packed in two dwords) at slots
+// j..j+3 (j % 4 == 0) of array `off` of a staged row.
+__device__ __forceinline__ void put4(u32x4* qrows, int row, int off, int j, uint32_t d0, uint32_t d1) {
+    char* p = reinterpret_cast<char*>(qrows) + (static_cast<size_t>(row) * kRowStride + off + (j >> 3)) * 16 +
+              (j & 7) * 2;
+    *reinterpret_cast<uint2*>(p) = make_uint2(d0, d1);
+}
+
+// The block's query products for one 32-row M tile (wave w) and all its
+// query rows: X q' with X = 16 Pi (dense) or 16 Phi (rotor: the block-diagonal
+// matrix of the 43 rotor sandwiches, pad column dropped), split as
+// X = hi + 2^-11 lo; and, with QJL, S q'.  q' = q * s0 (s0 a power of two)
+// enters as 2^11 hi, lo11 = (q' - hi) 2^11 and hi, computed once per K block
+// for both products.  Outputs (unscaled) hold rows 32 w + 8 (r / 4) +
+// 4 h + r % 4 of query row 32 nt + l % 32.
+// A-operand fragments of wave w's M tile of X (hi, lo) and S, all 8 K blocks.
+template <bool QJL>
+struct QueryFrags {
+    u32x4 xh[8], xl[8], sa[QJL ? 8 : 1];
+};
+template <bool QJL>
+__device__ __forceinline__ void query_frags(const MainArgs& a, int w, int l, QueryFrags<QJL>& f) {
+    const int n = l & 31, hh = l >> 5;
+    const u32x4* gxh = reinterpret_cast<const u32x4*>(a.x_hi);
+    const u32x4* gxl = reinterpret_cast<const u32x4*>(a.x_lo);
+    const u32x4* gs = reinterpret_cast<const u32x4*>(a.s_rows);
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+        const int i = (32 * w + n) * 16 + 2 * kb + hh;
+        f.xh[kb] = gxh[i];
+        f.xl[kb] = gxl[i];
+        if constexpr (QJL) f.sa[kb] = gs[i];
+    }
+}
+
+// Exact split of the block's query rows q' = q * s0 into the three B
+// operands 2^11 hi, lo11 = (q' - hi) 2^11 and hi, for K blocks 2w, 2w + 1
+// (wave w) of every N tile, written to LDS for all four waves.
+template <int NMT, class Lds>
+__device__ __forceinline__ void query_split(Lds& lds, u32x4* bop, int w, int l) {
+    const int n = l & 31, hh = l >> 5;
+#pragma unroll
+    for (int nt = 0; nt < NMT; ++nt) {
+        const int row = 32 * nt + n;
+        const float s0 = lds.s0[row];
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+            const int kb = 2 * w + k2;
+            const float* qv = &lds.qf[row][16 * kb + 8 * hh];
+            u32x4 h11, l11, h;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const float x0 = qv[2 * p] * s0, x1 = qv[2 * p + 1] * s0;
+                const uint32_t hp = cvt_pk(x0, x1);
+                const float f0 = h2f(hp & 0xFFFFu), f1 = h2f(hp >> 16);
+                h[p] = hp;
+                h11[p] = pk_scale2048(hp);
+                l11[p] = cvt_pk((x0 - f0) * 2048.0f, (x1 - f1) * 2048.0f);
+            }
+            u32x4* b = bop + ((nt * 8 + kb) * 3) * 64 + l;
+            b[0] = h11;
+            b[64] = l11;
+            b[128] = h;
+        }
+    }
+}
+
+template <bool QJL, int NMT>
+__device__ __forceinline__ void query_products(const QueryFrags<QJL>& fr, const u32x4* bop, const float (&s0r)[NMT],
+                                               int l, float (&ox)[NMT][16], float (&os)[NMT][16]) {
+#pragma unroll
+    for (int nt = 0; nt < NMT; ++nt) {
+        f32x16 ax = {}, as = {};
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) {
+            const u32x4* b = bop + ((nt * 8 + kb) * 3) * 64 + l;
+            const u32x4 h11 = b[0], l11 = b[64], h = b[128];
+            ax = mfma(fr.xh[kb], h11, ax);
+            ax = mfma(fr.xh[kb], l11, ax);
+            ax = mfma(fr.xl[kb], h, ax);
+            if constexpr (QJL) {
+                as = mfma(fr.sa[kb], h11, as);
+                as = mfma(fr.sa[kb], l11, as);
+            }
+        }
+        const float ux = 1.0f / (2048.0f * 16.0f) / s0r[nt], us = 1.0f / 2048.0f / s0r[nt];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float e = ax[r];
+            ox[nt][r] = e * ux;
+            const float f = as[r];
+            os[nt][r] = f * us;
+        }
+    }
+}
+
+// Row maxima of |out| over the 128 product rows: lane halves, then waves.
+template <int NMT, class Lds>
+__device__ __forceinline__ void product_row_max(const float (&out)[NMT][16], Lds& lds, int k, int w, int l) {
+#pragma unroll
+    for (int nt = 0; nt < NMT; ++nt) {
+        float m = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(out[nt][r]));
+        const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, m),
+                                                         __builtin_bit_cast(uint32_t, m), false, false);
+        const uint32_t a0 = sw[0], a1 = sw[1];
+        m = fmaxf(__builtin_bit_cast(float, a0), __builtin_bit_cast(float, a1));
+        if ((l >> 5) == 0) lds.part[k][w][32 * nt + (l & 31)] = m;
+    }
+}
+
+// Writes the split halves of out * s (s the row scale) into the staged rows:
+// arrays offA = 2^11 hi, offB = lo11, and (if offC >= 0) offC = hi; stores
+// 1 / (2^11 s) * mul in rsc[row][rsc_slot].
+template <int NMT, class Lds>
+__device__ __forceinline__ void product_store(const float (&out)[NMT][16], Lds& lds, int k, int w, int l, int offA,
+                                              int offB, int offC, int rsc_slot, float mul) {
+    const int n = l & 31, hh = l >> 5;
+#pragma unroll
+    for (int nt = 0; nt < NMT; ++nt) {
+        const int row = 32 * nt + n;
+        const float mx = fmaxf(fmaxf(lds.part[k][0][row], lds.part[k][1][row]),
+                               fmaxf(lds.part[k][2][row], lds.part[k][3][row]));
+        const float sc = pow2_scale(mx);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            uint32_t A[2], Bv[2], C[2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const float x0 = out[nt][4 * b + 2 * q] * sc, x1 = out[nt][4 * b + 2 * q + 1] * sc;
+                const uint32_t hp = cvt_pk(x0, x1);
+                C[q] = hp;
+                A[q] = pk_scale2048(hp);
+                Bv[q] = cvt_pk((x0 - h2f(hp & 0xFFFFu)) * 2048.0f, (x1 - h2f(hp >> 16)) * 2048.0f);
+            }
+            const int j = 32 * w + 8 * b + 4 * hh;
+            put4(lds.qrows, row, offA, j, A[0], A[1]);
+            put4(lds.qrows, row, offB, j, Bv[0], Bv[1]);
+            if (offC >= 0) put4(lds.qrows, row, offC, j, C[0], C[1]);
+        }
+        if (w == 0 && hh == 0) lds.rsc[row][rsc_slot] = mul / (2048.0f * sc);
+    }
+}
+
+// Builds the block's staged query rows (see "staged rows") and row scalars.
+// The block's query rows as loaded at kernel start: thread t holds float4 t
+// of each 256-float4 slice (rows >= nrows read as zero).
+template <int NMT>
+struct QueryRegs {
+    float4 v[NMT * 32 * 32 / kBlock];
+};
+template <int NMT>
+__device__ __forceinline__ void query_load(const MainArgs& a, int row0, int nrows, QueryRegs<NMT>& qr) {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int it = 0; it < NMT * 32 * 32 / kBlock; ++it) {
+        const int idx = it * kBlock + t, r = idx >> 5, c = idx & 31;
+        qr.v[it] = r < nrows ? reinterpret_cast<const float4*>(a.q + static_cast<int64_t>(row0 + r) * kD)[c]
+                             : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+}
+
+template <bool PAD, bool QJL, int NMT, class Lds>
+__device__ __forceinline__ void build_query_rows(const MainArgs& a, const QueryRegs<NMT>& qr,
+                                                 const QueryFrags<QJL>& fr, float inv_sc, Lds& lds) {
+    constexpr int ROWS = NMT * 32;
+    constexpr int TPR = kBlock / ROWS;   // threads per row
+    constexpr int CPT = kD / TPR;        // coordinates per thread
+    const int t = threadIdx.x;
+    {
+        constexpr int PER = ROWS * 32 / kBlock;
+        const float4* v = qr.v;
+#pragma unroll
+        for (int it = 0; it < PER; ++it) {
+            const int idx = it * kBlock + t, r = idx >> 5, c = idx & 31;
+            *reinterpret_cast<float4*>(&lds.qf[r][4 * c]) = v[it];
+        }
+    }
+    __syncthreads();
+    {
+        const int r = t / TPR, part = t % TPR;
+        const float* q = lds.qf[r];
+        float mq = 0.0f;
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) mq = fmaxf(mq, fabsf(q[part * CPT + k]));
+#pragma unroll
+        for (int o = 1; o < TPR; o <<= 1) mq = fmaxf(mq, __shfl_xor(mq, o));
+        if (part == 0) {
+            lds.s0[r] = pow2_scale(mq);
+            // rotor slot 128 (last row of group 42, pad input 0) in fp32
+            float qpad = 0.0f;
+            if constexpr (PAD) {
+                const float* m42 = a.rotmat + 9 * 42;
+                qpad = __builtin_fmaf(m42[8], 0.0f, __builtin_fmaf(m42[7], q[127], m42[6] * q[126]));
+            }
+            lds.rsc[r][1] = 0.0f;
+            lds.rsc[r][2] = qpad;
+            lds.rsc[r][3] = 0.0f;
+        }
+    }
+    __syncthreads();
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = lane_id();
+    // the split operands live where the staged rows go later
+    static_assert(NMT * 8 * 3 * 64 <= ROWS * kRowStride, "split operands overlay the staged rows");
+    u32x4* bop = lds.qrows;
+    query_split<NMT>(lds, bop, w, l);
+    float s0r[NMT];
+#pragma unroll
+    for (int nt = 0; nt < NMT; ++nt) s0r[nt] = lds.s0[32 * nt + (l & 31)];
+    __syncthreads();
+    float ox[NMT][16], os[NMT][16];
+    query_products<QJL, NMT>(fr, bop, s0r, l, ox, os);
+    product_row_max<NMT>(ox, lds, 0, w, l);
+    if constexpr (QJL) product_row_max<NMT>(os, lds, 1, w, l);
+    __syncthreads();
+    product_store<NMT>(ox, lds, 0, w, l, kOffQ1, kOffQ3, kOffQ2, 0, inv_sc);
+    if constexpr (QJL) product_store<NMT>(os, lds, 1, w, l, kOffP1, kOffP2, -1, 1, 1.0f);
+    __syncthreads();
+}
+
 template <int B, bool QJL, bool PAD, int NMT>
 __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
     constexpr int NC = PAD ? kRotCoords : kD;
@@ -169,7 +345,10 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
         uint32_t pairs[L * L][2];     // codes (a, b) -> {C_hi[a] | C_hi[b] << 16, C_lo[a] | C_lo[b] << 16}
         float rsc[ROWS][4];           // {1 / (2^11 s_q s_c), 1 / (2^11 s_p), q^_128, 0}
         float cent[L];
+        float s0[ROWS];               // power of two putting max |q| of a row in [1, 2)
+        float part[2][4][ROWS];       // per-wave partial maxima of the two products
         uint32_t stage[4][64 * SW];
+        float qf[ROWS][kD + 4];
         u32x4 qrows[ROWS * kRowStride];
     };
     __shared__ Lds lds;
@@ -179,6 +358,20 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
     const int kvh = head / qblocks, qb = head % qblocks;
     const int row0 = kvh * a.group + qb * a.rows_per_block;
     const int nrows = min(a.rows_per_block, a.group - qb * a.rows_per_block);
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t ntiles = (a.t + 63) / 64;
+    const int64_t rbase = static_cast<int64_t>(a.kv_head0 + kvh) * a.kv_stride;
+    const int64_t tstep = gridDim.x * 4LL;
+    // the first tile's record is requested before the block's staging
+    RecRegs<W> rec;
+    int64_t tile = blockIdx.x * 4LL + wave;
+    if (tile < ntiles) rec_fetch<W, QJL>(a, rbase, tile * 64, rec, lane_id());
+    // and so are the query rows and the X / S fragments of the query build
+    QueryRegs<NMT> qr;
+    query_load<NMT>(a, row0, nrows, qr);
+    QueryFrags<QJL> fr;
+    query_frags<QJL>(a, wave, lane_id(), fr);
 
     float inv_sc;
     {
@@ -194,45 +387,13 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
         }
         if (threadIdx.x < L) lds.cent[threadIdx.x] = a.cent[threadIdx.x];
     }
-    // this block's query rows (rows >= nrows are zero), all loads in flight at once
-    {
-        constexpr int PER = ROWS * kRowChunks / kBlock;
-        static_assert(ROWS * kRowChunks % kBlock == 0, "staging split");
-        u32x4 v[PER];
-#pragma unroll
-        for (int it = 0; it < PER; ++it) {
-            const int q = it * kBlock + threadIdx.x, r = q / kRowChunks, c = q % kRowChunks;
-            v[it] = r < nrows ? a.rows[static_cast<int64_t>(row0 + r) * kRowChunks + c] : u32x4{0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int it = 0; it < PER; ++it) {
-            const int q = it * kBlock + threadIdx.x, r = q / kRowChunks, c = q % kRowChunks;
-            lds.qrows[r * kRowStride + c] = v[it];
-        }
-    }
-    for (int r = threadIdx.x; r < ROWS; r += kBlock) {
-        float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f;
-        if (r < nrows) {
-            const float* s = a.scalars + static_cast<int64_t>(row0 + r) * kRowScalars;
-            s0 = s[0] * inv_sc;
-            s1 = s[1];
-            s2 = s[2];
-        }
-        lds.rsc[r][0] = s0;
-        lds.rsc[r][1] = s1;
-        lds.rsc[r][2] = s2;
-        lds.rsc[r][3] = 0.0f;
-    }
-    __syncthreads();
+    build_query_rows<PAD, QJL, NMT>(a, qr, fr, inv_sc, lds);
 
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     uint32_t* st = lds.stage[wave];
     const int64_t nk = a.t;   // keys of this head
-    const int64_t ntiles = (nk + 63) / 64;
-    const int64_t rbase = static_cast<int64_t>(a.kv_head0 + kvh) * a.kv_stride;
     const char* pairc = reinterpret_cast<const char*>(lds.pairs);
 
-    for (int64_t tile = blockIdx.x * 4LL + wave; tile < ntiles; tile += gridDim.x * 4LL) {
+    for (; tile < ntiles; tile += tstep) {
         const int z = opaque_zero();
         const int l = lane_id() + z;
         const int n = l & 31, hh = l >> 5;
@@ -241,19 +402,14 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
         // code words of keys n and 32 + n, shifted so this lane's K slots
         // start at bit 0 (slot 8 hh of each block is bit 8 B hh further)
         uint32_t cw[2][W];
-        {
-            const rsrc_t rs = make_rsrc(a.codes + (rbase + kbase) * W, tile_range(nk - kbase, 4 * W));
-            wave_lds_sync();
+        wave_lds_sync();
 #pragma unroll
-            for (int it = 0; it < W; ++it)
-                st[it * 64 + l] = __builtin_amdgcn_raw_buffer_load_b32(rs, static_cast<uint32_t>(4 * l), 256 * it,
-                                                                        kNonTemporal);
-            wave_lds_sync();
+        for (int it = 0; it < W; ++it) st[it * 64 + l] = rec.c[it];
+        wave_lds_sync();
 #pragma unroll
-            for (int k = 0; k < W; ++k) {
-                cw[0][k] = st[n * W + k];
-                cw[1][k] = st[(32 + n) * W + k];
-            }
+        for (int k = 0; k < W; ++k) {
+            cw[0][k] = st[n * W + k];
+            cw[1][k] = st[(32 + n) * W + k];
         }
         float cpad[2] = {0.0f, 0.0f};
         if constexpr (PAD) {
@@ -271,12 +427,9 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
             }
         uint32_t sg[2][4];
         if constexpr (QJL) {
-            const rsrc_t rs = make_rsrc(a.signs + (rbase + kbase) * 4, tile_range(nk - kbase, 16));
             wave_lds_sync();
 #pragma unroll
-            for (int it = 0; it < 4; ++it)
-                st[it * 64 + l] = __builtin_amdgcn_raw_buffer_load_b32(rs, static_cast<uint32_t>(4 * l), 256 * it,
-                                                                        kNonTemporal);
+            for (int it = 0; it < 4; ++it) st[it * 64 + l] = rec.s[it];
             wave_lds_sync();
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
@@ -288,9 +441,11 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
         float kn[2], kg[2];
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
-            kn[nt] = h2f(half_at(a.norms + rbase, kbase, nk, 32 * nt + n));
-            kg[nt] = QJL ? h2f(half_at(a.rnorms + rbase, kbase, nk, 32 * nt + n)) * a.qjl_scale : 0.0f;
+            kn[nt] = h2f(rec.kn[nt]);
+            kg[nt] = QJL ? h2f(rec.kg[nt]) * a.qjl_scale : 0.0f;
         }
+        // next tile's record, in flight during this tile's MFMAs and stores
+        if (tile + tstep < ntiles) rec_fetch<W, QJL>(a, rbase, (tile + tstep) * 64, rec, l);
 
         f32x16 acc1[NMT][2], acc2[NMT][2];
 #pragma unroll
@@ -409,24 +564,13 @@ static void launch_main_b(bool dense, int nmt, const MainArgs& a, int kv_heads, 
 
 hipError_t score(const ScoreTables& t, const float* q, int hq, int group, const uint32_t* codes,
                  const uint16_t* norms, const uint32_t* signs, const uint16_t* rnorms, int64_t tkeys,
-                 int64_t kv_stride, int kv_head0, void* ws, float* scores, int64_t ld_scores, hipStream_t s) {
-    ProArgs pa;
-    pa.q = q;
-    pa.hq = hq;
-    pa.dense = t.dense;
-    pa.qjl = t.qjl;
-    pa.rotmat = t.rot.rotmat;
-    pa.pit_hi = t.den.pit_hi;
-    pa.pit_lo = t.den.pit_lo;
-    pa.s_cols = t.dense ? t.den.s_cols : t.rot.s_cols;
-    pa.rows = static_cast<u32x4*>(ws);
-    pa.scalars =
-        reinterpret_cast<float*>(static_cast<char*>(ws) + static_cast<size_t>(kScoreChunkRows) * kRowChunks * 16);
-    hipLaunchKernelGGL(score_prologue, dim3(hq), dim3(128), 0, s, pa);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-
+                 int64_t kv_stride, int kv_head0, float* scores, int64_t ld_scores, hipStream_t s) {
     MainArgs a;
+    a.q = q;
+    a.rotmat = t.rot.rotmat;
+    a.x_hi = t.dense ? t.den.pi_hi : t.rot.phi_hi;
+    a.x_lo = t.dense ? t.den.pi_lo : t.rot.phi_lo;
+    a.s_rows = t.dense ? t.den.s_rows : t.rot.s_rows;
     a.codes = codes;
     a.norms = norms;
     a.signs = signs;
@@ -436,8 +580,6 @@ hipError_t score(const ScoreTables& t, const float* q, int hq, int group, const 
     a.kv_head0 = kv_head0;
     a.group = group;
     a.rows_per_block = group < 64 ? group : 64;
-    a.rows = pa.rows;
-    a.scalars = pa.scalars;
     a.cent = t.dense ? t.den.cent : t.rot.cent;
     a.qjl_scale = t.qjl_scale;
     a.scores = scores;
