@@ -193,6 +193,23 @@ __device__ __forceinline__ void tile_load(const char* __restrict__ src, int64_t 
     }
 }
 
+// A buffer store of more than 64 bits reads its data registers after it has
+// issued, so an instruction in the next cycles must not overwrite them (the
+// vector-memory store-data hazard; 128-bit stores whose first data register
+// was rewritten by the very next VALU instruction stored that new value when
+// two workgroups shared a CU).  The compiler does not separate them here, so
+// every 128-bit store group is closed by this fence: nothing is scheduled
+// across it and it adds two wait states.
+__device__ __forceinline__ void store_data_fence() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 1");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Writes the LDS tile to 64 rows of 256 bytes (from byte `col_off` of each
+// row).  Rows 4 it + l / 16 for it = b, b + 4, b + 8, b + 12 share one LDS
+// swizzle, so each group of four is read with one address and immediate
+// offsets, then stored with no other instruction in between.
 __device__ __forceinline__ void tile_store(char* __restrict__ dst, int64_t ld_bytes, int64_t base, int64_t n,
                                            int col_off, const u32x4* __restrict__ tile, int l) {
     const int rr = l >> 4, c = l & 15;
@@ -200,9 +217,15 @@ __device__ __forceinline__ void tile_store(char* __restrict__ dst, int64_t ld_by
     const rsrc_t rs = make_rsrc(dst + base * ld_bytes + col_off, tile_range(n - base, ld_bytes));
     const int step = static_cast<int>(4 * ld_bytes);
 #pragma unroll
-    for (int it = 0; it < 16; ++it) {
-        const u32x4 v = tile[swz(4 * it + rr, c)];
-        __builtin_amdgcn_raw_buffer_store_b128(v, rs, voff, it * step, kNonTemporal);
+    for (int b = 0; b < 4; ++b) {
+        u32x4 v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = tile[swz(4 * (b + 4 * k) + rr, c)];
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            __builtin_amdgcn_raw_buffer_store_b128(v[k], rs, voff, (b + 4 * k) * step, kNonTemporal);
+        store_data_fence();
     }
 }
 
