@@ -122,3 +122,34 @@ def needle_keys(t, d=HEAD_DIM, seed=7, cos=0.6):
     idx = int(rng.integers(t))
     keys[idx] = np.sqrt(d) * (cos * qu + np.sqrt(1.0 - cos * cos) * w)
     return keys.astype(np.float32), q.astype(np.float32), idx
+
+
+def kv_cache(spec, device="cpu", base_seed=0, torch=None):
+    """A whole synthetic cache of a model shape, filled head by head.
+
+    Returns (kv [2, layers, kv_heads, tokens, 128] fp16 with K at index 0 and
+    V at 1, q [layers, q_heads, 128] fp32).  Query heads h of a layer come
+    from the generator of KV head h // (q_heads / kv_heads), so each group of
+    query heads sits near its own keys' subspace.
+    """
+    if torch is None:
+        import torch  # noqa: F811
+    L, H, T, HQ = spec["layers"], spec["kv_heads"], spec["tokens"], spec["q_heads"]
+    group = HQ // H
+    kv = torch.empty((2, L, H, T, HEAD_DIM), dtype=torch.float16, device=device)
+    q = torch.empty((L, HQ, HEAD_DIM), dtype=torch.float32, device=device)
+    for layer in range(L):
+        for h in range(H):
+            k, v, qh = lowrank_head(T, cache_seed(base_seed, layer, h), device=device,
+                                    with_query_heads=group, torch=torch)
+            kv[0, layer, h].copy_(k)
+            kv[1, layer, h].copy_(v)
+            q[layer, h * group:(h + 1) * group].copy_(qh)
+    return kv, q
+
+
+def sample_rows(n, fraction, seed):
+    """Sorted seeded sample of round(fraction * n) distinct row indices."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    m = max(1, int(round(fraction * n)))
+    return np.sort(rng.choice(n, size=m, replace=False))

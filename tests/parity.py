@@ -95,3 +95,26 @@ def record_from_host(codes, norms, signs, rnorms):
     return K.Record(codes.astype(np.uint32), norms.astype(np.uint16),
                     None if signs is None else signs.astype(np.uint32),
                     None if rnorms is None else rnorms.astype(np.uint16))
+
+
+def check_records(p, x, codes, norms, signs, rnorms):
+    """Codes, norms, sign bits and residual norms of GPU records against the
+    oracle's quantisation of the same input rows.  Returns (oracle record,
+    diagnostics, band mask per vector, code report)."""
+    orec, diag = K.quantize(p, np.asarray(x, dtype=np.float64))
+    excl, rep = compare_codes(p, codes, diag)
+    compare_halves(norms, diag.n, "norms")
+    if p.qjl:
+        compare_signs(p, signs, diag, excl)
+        compare_halves(rnorms[~excl], diag.gamma[~excl], "rnorms")
+    return orec, diag, excl, rep
+
+
+def compare_scores(got, ref, qnorm, nhat, what="scores"):
+    """|gpu - oracle| <= SCORE_TOL * ||q|| * n^ elementwise (broadcasting)."""
+    got = np.asarray(got, dtype=np.float64)
+    lim = SCORE_TOL * qnorm * nhat + 1e-30
+    err = np.abs(got - ref)
+    bad = err > lim
+    assert not bad.any(), f"{what}: {bad.sum()} over tolerance, worst {np.max(err / lim):.3g}x"
+    return float(np.max(err / lim)) if err.size else 0.0

@@ -1,0 +1,269 @@
+"""GPU parity at the shapes of the pages' workloads, through the C ABI.
+
+* 262,144 fp16 N(0,1) keys: the TurboQuant dense path at 2/3/4 bits with and
+  without QJL (hyper.ai Algorithms 1 and 2), and the rotor path on the same
+  keys (README "MSE Quality");
+* a Qwen2.5-3B-shaped K/V cache (36 layers x 2 KV heads x 32,768 tokens,
+  16 query heads, GQA 8:1; README "Background", "Real Model Validation") and
+  a Llama-3.1-8B-shaped one (32 layers x 8 KV heads x 131,072 tokens, 32
+  query heads, GQA 4:1; PolarQuant article on the KV-cache problem), both
+  from the low-rank + outlier generator, quantised in bulk with 3 bits
+  (2-bit codes + QJL) and scored for one decode step.
+
+At these sizes the float64 oracle checks seeded samples of rows (every
+output of a sampled row is compared); every output is also checked at full
+size against properties that hold at any size: the roundtrip output equals
+the dequantisation of its own record bit for bit, each score equals the
+inner product of its query with the dequantised key (the estimator is that
+inner product by construction), the bulk call equals per-layer calls, and
+the MSE-only distortion of N(0,1) keys sits at the Lloyd-Max values.
+"""
+import numpy as np
+import pytest
+
+import parity as PR
+from oracle import codec as OC
+from oracle import params as OP
+from kv_cache_vector_norm_amd import workloads as W
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+D = 128
+DEV = "cuda"
+
+
+def _sync():
+    if DEV == "cuda":
+        torch.cuda.synchronize()
+
+
+@pytest.fixture(scope="module")
+def K():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import kv_cache_vector_norm_amd as K
+    return K
+
+
+def _gather(rec, idx):
+    """Host copies of the record rows at the given indices."""
+    it = torch.from_numpy(np.asarray(idx, dtype=np.int64)).to(DEV)
+
+    def g(t, dt):
+        return None if t is None else t.index_select(0, it).cpu().numpy().view(dt)
+    return g(rec.codes, np.uint32), g(rec.norms, np.uint16), g(rec.signs, np.uint32), g(rec.rnorms, np.uint16)
+
+
+def _nhat_dev(norms):
+    return norms.view(torch.float16).to(torch.float64)
+
+
+def _check_score_property(codec, q, rec, scores, group, t):
+    """scores[h, i] == <q_h, dequant(k_i)> within SCORE_TOL * ||q_h|| * n^_i,
+    for hq query heads over hq / group KV heads of t keys each (contiguous)."""
+    xt = codec.dequantize(rec, dtype=torch.float32).to(torch.float64)
+    nh = _nhat_dev(rec.norms)
+    hq = q.shape[0]
+    qd = q.to(torch.float64)
+    qn = torch.linalg.norm(qd, dim=1)
+    worst = 0.0
+    for j in range(hq // group):
+        sl = slice(j * t, (j + 1) * t)
+        ref = qd[j * group:(j + 1) * group] @ xt[sl].T
+        lim = PR.SCORE_TOL * qn[j * group:(j + 1) * group, None] * nh[None, sl] + 1e-30
+        ratio = (scores[j * group:(j + 1) * group].to(torch.float64) - ref).abs() / lim
+        worst = max(worst, float(ratio.max()))
+    assert worst <= 1.0, f"score vs dequantised key: worst {worst:.3g} x tolerance"
+    return worst
+
+
+def _check_sampled_scores(p, q_host, scores, rec, rows, kv_heads, t, group):
+    """Oracle scores of sampled keys against all query heads of their group.
+
+    `rows` index the K records laid out [layer][kv_head][token];
+    `scores` is [layers, q_heads, t] on the GPU."""
+    layer = rows // (kv_heads * t)
+    head = (rows // t) % kv_heads
+    tok = rows % t
+    codes, norms, signs, rnorms = _gather(rec, rows)
+    li = torch.from_numpy(layer).to(DEV)[:, None]
+    hi = torch.from_numpy(head * group).to(DEV)[:, None] + torch.arange(group, device=DEV)[None, :]
+    ti = torch.from_numpy(tok).to(DEV)[:, None]
+    got = scores[li, hi, ti].cpu().numpy().astype(np.float64)          # [m, group]
+    worst = 0.0
+    keys = layer * kv_heads + head
+    for key in np.unique(keys):
+        sel = keys == key
+        l, j = divmod(int(key), kv_heads)
+        sub = OC.Record(codes[sel], norms[sel], signs[sel] if signs is not None else None,
+                        rnorms[sel] if rnorms is not None else None)
+        qh = q_host[l, j * group:(j + 1) * group].astype(np.float64)
+        ref = OC.score(p, qh, sub)                                      # [group, m_sel]
+        qn = np.linalg.norm(qh, axis=1)[:, None]
+        worst = max(worst, PR.compare_scores(got[sel].T, ref, qn, OC.half_value(norms[sel])[None, :],
+                                             f"layer {l} kv head {j}"))
+    return worst
+
+
+# ------------------------------------------- 262,144 keys, dense sweep ----
+C2_N = 262144
+C2_MODES = ([(b, OP.DENSE) for b in (2, 3, 4)] + [(b, OP.DENSE | OP.QJL) for b in (2, 3, 4, 5)]
+            + [(b, OP.MSE) for b in (2, 3, 4)] + [(3, OP.QJL)])
+# Unit-vector distortion of the Lloyd-Max codebooks (README "MSE Quality";
+# hyper.ai Theorem 1 table) at 2/3/4 bits.
+LLOYD_MAX_MSE = {2: 0.1160, 3: 0.0340, 4: 0.0093}
+
+
+@pytest.fixture(scope="module")
+def c2_keys(K):
+    x = W.keys_c2()
+    return x, torch.from_numpy(x).to(DEV)
+
+
+@pytest.mark.parametrize("bits,mode", C2_MODES)
+def test_c2_sweep(K, c2_keys, bits, mode):
+    x, xd = c2_keys
+    print(f"c2 sweep bits={bits} mode={mode}", flush=True)
+    c = K.Codec(bits=bits, seed=0, mode=mode)
+    rec, y = c.roundtrip(xd, dtype=torch.float32)
+    d = c.dequantize(rec, dtype=torch.float32)
+    _sync()
+    assert torch.equal(y, d)
+    if not mode & OP.QJL:
+        xs = xd.to(torch.float64)
+        rel = (((xs - y.to(torch.float64)) ** 2).sum(1) / (xs ** 2).sum(1)).mean().item()
+        assert abs(rel - LLOYD_MAX_MSE[bits]) < 0.01 * LLOYD_MAX_MSE[bits] + 2e-4, rel
+    idx = W.sample_rows(C2_N, 1 / 16, seed=100 + 10 * bits + mode)
+    codes, norms, signs, rnorms = _gather(rec, idx)
+    p = OP.Params(D, bits, 0, mode)
+    PR.check_records(p, x[idx], codes, norms, signs, rnorms)
+    hrec = PR.record_from_host(codes, norms, signs, rnorms)
+    PR.compare_recon(y[torch.from_numpy(idx).to(DEV)].cpu().numpy(), OC.dequantize(p, hrec),
+                     OC.half_value(norms), "dequantize")
+
+
+# ------------------------------------------------- model-shaped caches ----
+def _bulk(K, spec, seed):
+    """Generate the cache on the GPU, quantise K and V of every layer in one
+    call, then score one decode step per layer.  Records are laid out
+    [K|V][layer][kv_head][token]."""
+    L, H, T, HQ = spec["layers"], spec["kv_heads"], spec["tokens"], spec["q_heads"]
+    group = HQ // H
+    print(f"{spec['name']}: generating {2 * L * H * T} vectors", flush=True)
+    kv, q = W.kv_cache(spec, device=DEV, base_seed=seed, torch=torch)
+    flat = kv.view(-1, D)
+    assert flat.shape[0] == 2 * L * H * T and q.shape == (L, HQ, D)
+    c = K.Codec(bits=3, seed=0, mode=OP.QJL)
+    rec = c.quantize(flat)
+    scores = torch.empty((L, HQ, T), dtype=torch.float32, device=DEV)
+    per_layer = H * T
+    for layer in range(L):
+        sl = slice(layer * per_layer, (layer + 1) * per_layer)
+        sub = K.Record(rec.codes[sl], rec.norms[sl], rec.signs[sl], rec.rnorms[sl])
+        c.score(q[layer], sub, group, T, T, out=scores[layer])
+    _sync()
+    print(f"{spec['name']}: quantised and scored", flush=True)
+    return dict(spec=spec, codec=c, flat=flat, q=q, q_host=q.cpu().numpy(), rec=rec, scores=scores,
+                group=group, p=OP.Params(D, 3, 0, OP.QJL))
+
+
+def _layer_record(K, st, which, layer):
+    spec = st["spec"]
+    per_layer = spec["kv_heads"] * spec["tokens"]
+    base = (which * spec["layers"] + layer) * per_layer
+    sl = slice(base, base + per_layer)
+    r = st["rec"]
+    return K.Record(r.codes[sl], r.norms[sl], r.signs[sl], r.rnorms[sl]), sl
+
+
+def _check_sample(st, rows, dequant=False):
+    p = st["p"]
+    codes, norms, signs, rnorms = _gather(st["rec"], rows)
+    it = torch.from_numpy(rows).to(DEV)
+    x = st["flat"].index_select(0, it).cpu().numpy()
+    _, _, excl, rep = PR.check_records(p, x, codes, norms, signs, rnorms)
+    if dequant:
+        sub = st["codec"].dequantize(type(st["rec"])(*(None if a is None else a.index_select(0, it) for a in
+                                                        (st["rec"].codes, st["rec"].norms, st["rec"].signs,
+                                                         st["rec"].rnorms))), dtype=torch.float32)
+        PR.compare_recon(sub.cpu().numpy(), OC.dequantize(p, PR.record_from_host(codes, norms, signs, rnorms)),
+                         OC.half_value(norms), "dequantize")
+    spec = st["spec"]
+    n_k = spec["layers"] * spec["kv_heads"] * spec["tokens"]
+    k_rows = rows[rows < n_k]
+    worst = _check_sampled_scores(p, st["q_host"], st["scores"], st["rec"], k_rows, spec["kv_heads"],
+                                  spec["tokens"], st["group"])
+    return rep, worst
+
+
+# Qwen2.5-3B shape: 36 x 2 x 32,768 x 128, K and V (4,718,592 vectors).
+@pytest.fixture(scope="module")
+def qwen(K):
+    st = _bulk(K, W.QWEN25_3B, seed=3)
+    yield st
+    st.clear()
+    if DEV == "cuda":
+        torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("part", range(4))
+def test_qwen_cache_sample(K, qwen, part):
+    """A seeded 2% of all K and V rows (a quarter per case) against the oracle:
+    codes, norms, signs, residual norms, dequantisation, and the 8 query heads'
+    scores of every sampled key."""
+    n = qwen["flat"].shape[0]
+    rows = np.array_split(W.sample_rows(n, 0.02, seed=5), 4)[part]
+    print(f"qwen sample part {part}: {rows.size} rows", flush=True)
+    _check_sample(qwen, rows, dequant=(part == 0))
+
+
+def test_qwen_scores_full(K, qwen):
+    """All 18,874,368 scores of the decode step against q . dequant(k)."""
+    spec = qwen["spec"]
+    for layer in range(spec["layers"]):
+        rec, _ = _layer_record(K, qwen, 0, layer)
+        _check_score_property(qwen["codec"], qwen["q"][layer], rec, qwen["scores"][layer], qwen["group"],
+                              spec["tokens"])
+
+
+def test_qwen_bulk_equals_per_layer(K, qwen):
+    """One call over the whole cache writes the same bytes as a call per layer."""
+    c = qwen["codec"]
+    for which, layer in ((0, 0), (0, 17), (1, 35)):
+        bulk, sl = _layer_record(K, qwen, which, layer)
+        own = c.quantize(qwen["flat"][sl])
+        _sync()
+        for a, b in zip((bulk.codes, bulk.norms, bulk.signs, bulk.rnorms),
+                        (own.codes, own.norms, own.signs, own.rnorms)):
+            assert torch.equal(a, b)
+
+
+# Llama-3.1-8B shape: 32 x 8 x 131,072 x 128, K and V (67,108,864 vectors,
+# 17.2 GB of fp16), quantised in one call.
+@pytest.fixture(scope="module")
+def llama(K):
+    st = _bulk(K, W.LLAMA31_8B, seed=4)
+    yield st
+    st.clear()
+    if DEV == "cuda":
+        torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("part", range(6))
+def test_llama_cache_sample(K, llama, part):
+    """A seeded 1% of all K and V rows (671,089; a sixth per case) against the
+    oracle, with the 4 query heads' scores of every sampled key."""
+    n = llama["flat"].shape[0]
+    rows = np.array_split(W.sample_rows(n, 0.01, seed=6), 6)[part]
+    print(f"llama sample part {part}: {rows.size} rows", flush=True)
+    _check_sample(llama, rows, dequant=(part == 0))
+
+
+def test_llama_scores_full(K, llama):
+    """All 134,217,728 decode scores (32 layers) against q . dequant(k)."""
+    spec = llama["spec"]
+    for layer in range(spec["layers"]):
+        rec, _ = _layer_record(K, llama, 0, layer)
+        _check_score_property(llama["codec"], llama["q"][layer], rec, llama["scores"][layer], llama["group"],
+                              spec["tokens"])
