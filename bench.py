@@ -52,18 +52,30 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_sources_digest():
-    h = hashlib.sha256()
-    d = os.path.join(ROOT, "kv_cache_vector_norm_amd", "csrc")
-    for f in sorted(os.listdir(d)):
-        with open(os.path.join(d, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
-    return h.hexdigest()[:16]
+def kernel_code_digest():
+    """First 16 hex digits of the sha256 of librq.so's offload section (the
+    gfx950 code objects): it changes exactly when some kernel's machine code
+    does, and not for edits that leave the code alone."""
+    import struct
+    with open(os.path.join(ROOT, "kv_cache_vector_norm_amd", "librq.so"), "rb") as f:
+        data = f.read()
+    shoff = struct.unpack_from("<Q", data, 0x28)[0]
+    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", data, 0x3A)
+
+    def section(i):
+        return struct.unpack_from("<IIQQQQIIQQ", data, shoff + i * shentsize)
+    names = section(shstrndx)[4]
+    for i in range(shnum):
+        sh = section(i)
+        name = data[names + sh[0]:data.index(b"\0", names + sh[0])]
+        if name == b".hip_fatbin":
+            return hashlib.sha256(data[sh[4]:sh[4] + sh[5]]).hexdigest()[:16]
+    raise RuntimeError("librq.so has no .hip_fatbin section")
 
 
 def measured_traffic(kernel, digest):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they
-    were taken on the current kernel sources; else None."""
+    were taken on the current kernel code; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
@@ -71,7 +83,7 @@ def measured_traffic(kernel, digest):
     except (OSError, ValueError):
         return None
     e = t.get(kernel)
-    if not e or e.get("sources") != digest:
+    if not e or e.get("code") != digest:
         return None
     return e.get("bytes_per_launch")
 
@@ -119,7 +131,7 @@ def ingest_counters(fetch_csv, write_csv, copy_bytes):
     w_rt = sum(wr) / len(wr) * 1024.0
     cf, cw = f_copy / copy_bytes, w_copy / copy_bytes
     entry = {
-        "sources": kernel_sources_digest(),
+        "code": kernel_code_digest(),
         "kernel": ROUNDTRIP_KERNEL,
         "dispatches": len(fr),
         "fetch_kib_raw": round(f_rt / 1024.0, 1), "write_kib_raw": round(w_rt / 1024.0, 1),
@@ -226,7 +238,7 @@ def main():
 
     bytes_vec = algorithmic_bytes(lay)
     rt_gbs = N_VEC * bytes_vec / (rt_ms * 1e-3) / 1e9
-    digest = kernel_sources_digest()
+    digest = kernel_code_digest()
     traffic = measured_traffic("rq_roundtrip_qjl3_f16", digest)
     roof = {"bound": "hbm", "achieved": round(rt_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(rt_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
@@ -306,7 +318,7 @@ def main():
                                "fused roundtrip + q.k estimates of 64 fp32 queries",
                    "vectors": N_VEC, "queries": N_Q, "bits": BITS, "mode": "rotor+qjl", "seed": 0},
         "roofline": roof,
-        "kernel_sources": digest,
+        "kernel_code": digest,
         **extras,
     }
     if not a.no_cpu:

@@ -10,8 +10,10 @@
 //
 // Each block first builds, in LDS, the query side for its (KV head, <= 64
 // query rows): q^ and S q as exact fp16 half pairs with power-of-two row
-// scales (S q and, on the dense path, Pi q on 32x32x16 MFMAs from an exact
-// hi/lo split of the query; the rotor q^ in fp32 VALU).  Those rows are then
+// scales, all on 32x32x16 MFMAs from an exact hi/lo split of the query
+// (q^ = Pi q on the dense path; on the rotor path q^ = Phi q with Phi the
+// 128 x 128 block-diagonal matrix of the rotor sandwiches, the pad slot
+// q^_128 from the last rotor in fp32).  Those rows are then
 // the A operand of the scoring MFMAs; the B operand is decoded from the
 // records straight into MFMA layout: lane (n, h) of a wave serves keys n and
 // 32 + n of the 64-key tile and K slots 8h..8h+7 of each 16-wide block,
