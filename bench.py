@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sweep", action="store_true", help="also time the MSE-only roundtrip over an N sweep")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the 262,144-key dense sweep and the model-shaped cache measurements")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after timing, run 3 plain device copies of this many bytes (counter calibration)")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -178,6 +180,93 @@ def cpu_baseline(x_host, q_host):
             "scores_per_s": n * N_Q * reps / el}
 
 
+def _timed(stream, fn, reps):
+    """Average microseconds per call of fn(i) over reps back-to-back calls,
+    from HIP events on the launch stream (after one untimed call)."""
+    import torch
+    fn(0)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(reps):
+        fn(i + 1)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def workload_extras(K, W, dev, stream):
+    """Throughput at the other workload shapes (inputs resident in HBM):
+    the TurboQuant dense path and the rotor path over 262,144 fp16 N(0,1)
+    keys (rotating over 8 such batches, 0.5 GB of input, so launches read
+    cold data), and the Qwen2.5-3B- and Llama-3.1-8B-shaped caches quantised
+    in one call each plus one decode step of per-layer scoring."""
+    import torch
+    out = {}
+    n = 262144
+    sets = 8
+    xs = torch.randn((sets * n, 128), device=dev).to(torch.float16)
+    ys = torch.empty_like(xs)
+    sweep = {}
+    for name, mode, bits_list in (("dense", K.RQ_DENSE, (2, 3, 4)), ("dense+qjl", K.RQ_DENSE | K.RQ_QJL, (2, 3, 4, 5)),
+                                  ("rotor", K.RQ_MSE, (2, 3, 4)), ("rotor+qjl", K.RQ_QJL, (2, 3, 4, 5))):
+        for b in bits_list:
+            c = K.Codec(bits=b, seed=0, mode=mode)
+            recs = [c.alloc_record(n, dev) for _ in range(sets)]
+
+            def rt(i, c=c, recs=recs):
+                k = i % sets
+                c.roundtrip(xs[k * n:(k + 1) * n], rec=recs[k], out=ys[k * n:(k + 1) * n])
+            us = _timed(stream, rt, 24)
+            alg = 256 + c.layout["record_bytes"] + 256
+            e = {"us": round(us, 2), "vectors_per_s": round(n / (us * 1e-6), 1),
+                 "gbs": round(n * alg / (us * 1e-6) / 1e9, 1)}
+            if mode & K.RQ_DENSE:
+                # useful MFMA work: Pi x and Pi^T y (and S r, S^T sigma with QJL), 2 flop per MAC
+                flops = 2 * 128 * 128 * (4 if mode & K.RQ_QJL else 2)
+                e["mfma_tflops"] = round(n * flops / (us * 1e-6) / 1e12, 2)
+            sweep[f"{name}{b}"] = e
+            del recs, c
+    out["keys262144_roundtrip"] = sweep
+    del xs, ys
+
+    for spec in (W.QWEN25_3B, W.LLAMA31_8B):
+        L, H, T, HQ = spec["layers"], spec["kv_heads"], spec["tokens"], spec["q_heads"]
+        g = HQ // H
+        kv, q = W.kv_cache(spec, device=dev, base_seed=1, torch=torch)
+        flat = kv.view(-1, 128)
+        c = K.Codec(bits=3, seed=0, mode=K.RQ_QJL)
+        rec = c.alloc_record(flat.shape[0], dev)
+        qus = _timed(stream, lambda i: c.quantize(flat, rec=rec), 3 if flat.shape[0] > 10_000_000 else 10)
+        scores = torch.empty((L, HQ, T), dtype=torch.float32, device=dev)
+        per = H * T
+        subs = [K.Record(rec.codes[l * per:(l + 1) * per], rec.norms[l * per:(l + 1) * per],
+                         rec.signs[l * per:(l + 1) * per], rec.rnorms[l * per:(l + 1) * per]) for l in range(L)]
+
+        def decode_layers(i):
+            for l in range(L):
+                c.score(q[l], subs[l], g, T, T, out=scores[l])
+
+        def decode(i):
+            # all layers in one call: query row l * HQ + h reads KV head
+            # (l * HQ + h) / g = l * H + h / g, i.e. record rows of layer l
+            c.score(q.view(L * HQ, 128), rec, g, T, T, out=scores.view(L * HQ, T))
+        lus = _timed(stream, decode_layers, 3)
+        dus = _timed(stream, decode, 5)
+        nv = flat.shape[0]
+        ns = L * HQ * T
+        out[spec["name"]] = {
+            "vectors": nv, "bulk_quantize_us": round(qus, 1),
+            "quantize_vectors_per_s": round(nv / (qus * 1e-6), 1),
+            "quantize_gbs": round(nv * (256 + c.layout["record_bytes"]) / (qus * 1e-6) / 1e9, 1),
+            "decode_step_us": round(dus, 1), "decode_scores": ns,
+            "decode_scores_per_s": round(ns / (dus * 1e-6), 1),
+            "decode_step_per_layer_calls_us": round(lus, 1)}
+        del kv, q, flat, rec, scores, subs, c
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     a = parse()
     if a.ingest_counters:
@@ -292,6 +381,16 @@ def main():
             sweep[str(n)] = {"us": round(us, 2), "gbs": round(n * mb / (us * 1e-6) / 1e9, 1)}
             del xb, yb, rb
         extras["mse3_sweep"] = sweep
+
+    # achievable-HBM reference: a plain device copy of 1 GiB (read + write)
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    cus = _timed(stream, lambda i: dst.copy_(src), 5)
+    extras["copy_1gib_gbs"] = round(2 * (1 << 30) / (cus * 1e-6) / 1e9, 1)
+    del src, dst
+
+    if not a.no_workloads:
+        extras["workloads"] = workload_extras(K, W, dev, stream)
 
     if a.copy_bytes:
         src = torch.empty(a.copy_bytes, dtype=torch.uint8, device=dev)

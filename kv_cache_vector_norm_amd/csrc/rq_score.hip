@@ -544,13 +544,22 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
     }
 }
 
+// Grid: (key slices, KV heads x query-row blocks).  Every block pays for
+// building its query rows once, so the slices per (head, row block) are only
+// as many as fill the workgroup slots of the chip in one round (two per CU
+// for the 32-row variant, one for the 64-row variant, whose LDS is larger);
+// each wave then walks many 64-key tiles.  At least one tile per wave.
 template <int B, bool QJL, bool PAD, int NMT>
 static void launch_main(const MainArgs& a, int kv_heads, int qblocks, hipStream_t s) {
     const int64_t ntiles = (a.t + 63) / 64;
     const int64_t want = (ntiles + 3) / 4;
-    const int64_t per_head_cap = (4096 + kv_heads * qblocks - 1) / (kv_heads * qblocks);
-    const int gx = static_cast<int>(want < per_head_cap ? want : (per_head_cap > 0 ? per_head_cap : 1));
-    hipLaunchKernelGGL((score_kernel<B, QJL, PAD, NMT>), dim3(gx, kv_heads * qblocks), dim3(kBlock), 0, s, a);
+    const int64_t slots = 256LL * (NMT == 1 ? 2 : 1);
+    const int64_t units = static_cast<int64_t>(kv_heads) * qblocks;
+    int64_t gx = slots / units;
+    if (gx > want) gx = want;
+    if (gx < 1) gx = 1;
+    hipLaunchKernelGGL((score_kernel<B, QJL, PAD, NMT>), dim3(static_cast<unsigned>(gx), kv_heads * qblocks),
+                       dim3(kBlock), 0, s, a);
 }
 
 template <int B, bool QJL>

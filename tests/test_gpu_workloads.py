@@ -267,3 +267,20 @@ def test_llama_scores_full(K, llama):
         rec, _ = _layer_record(K, llama, 0, layer)
         _check_score_property(llama["codec"], llama["q"][layer], rec, llama["scores"][layer], llama["group"],
                               spec["tokens"])
+
+
+@pytest.mark.parametrize("which", ["qwen", "llama"])
+def test_decode_step_in_one_call(K, which, request):
+    """The whole decode step as one rq_score call: query row l * HQ + h reads
+    KV head l * H + h / group, i.e. layer l's records, so the scores equal the
+    per-layer calls bit for bit."""
+    st = request.getfixturevalue(which)
+    spec = st["spec"]
+    L, HQ, T = spec["layers"], spec["q_heads"], spec["tokens"]
+    n_k = L * spec["kv_heads"] * T
+    r = st["rec"]
+    krec = K.Record(r.codes[:n_k], r.norms[:n_k], r.signs[:n_k], r.rnorms[:n_k])
+    out = torch.empty((L * HQ, T), dtype=torch.float32, device=DEV)
+    st["codec"].score(st["q"].view(L * HQ, D), krec, st["group"], T, T, out=out)
+    _sync()
+    assert torch.equal(out.view(L, HQ, T), st["scores"])
