@@ -232,10 +232,39 @@ def score_gqa(p: Params, q, rec: Record, group, t, kv_stride=None):
     for h in range(q.shape[0]):
         j = h // group
         sl = slice(j * kv_stride, j * kv_stride + t)
-        sub = Record(rec.codes[sl], rec.norms[sl],
-                     None if rec.signs is None else rec.signs[sl],
-                     None if rec.rnorms is None else rec.rnorms[sl])
-        out[h] = score(p, q[h : h + 1], sub)[0]
+        out[h] = score(p, q[h : h + 1], _rows(rec, sl))[0]
+    return out
+
+
+def _rows(rec: Record, sl):
+    return Record(rec.codes[sl], rec.norms[sl],
+                  None if rec.signs is None else rec.signs[sl],
+                  None if rec.rnorms is None else rec.rnorms[sl])
+
+
+def attend(pk: Params, pv: Params, q, krec: Record, vrec: Record, group, t, scale, kv_stride=None):
+    """Decode attention read straight from a compressed cache.
+
+    Attention is softmax(q K^T / sqrt(d)) V, a softmax-weighted sum of the
+    values (PolarQuant article, "Проблема KV-кэша в трансформерах"); the
+    README's note under "Triton Kernels" asks for the q.k scores to be taken
+    from the compressed keys.  For query head h, reading KV head j = h // group
+    (keys and values of head j start at vector j * kv_stride):
+      s_t = scale * score(q_h, k_t)        the estimator above, over t keys
+      p   = softmax(s)                     (max subtracted first; same value)
+      out_h = sum_t p_t * dequantize(v_t)  values decoded with their own session
+    Returns [H, d].
+    """
+    kv_stride = t if kv_stride is None else kv_stride
+    q = np.asarray(q, dtype=np.float64)
+    s = scale * score_gqa(pk, q, krec, group, t, kv_stride)
+    out = np.zeros((q.shape[0], pv.d))
+    for h in range(q.shape[0]):
+        j = h // group
+        e = np.exp(s[h] - s[h].max())
+        pr = e / e.sum()
+        xv = dequantize(pv, _rows(vrec, slice(j * kv_stride, j * kv_stride + t)))
+        out[h] = pr @ xv
     return out
 
 
