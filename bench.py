@@ -253,6 +253,14 @@ def workload_extras(K, W, dev, stream):
             c.score(q.view(L * HQ, 128), rec, g, T, T, out=scores.view(L * HQ, T))
         lus = _timed(stream, decode_layers, 3)
         dus = _timed(stream, decode, 5)
+        # decode attention over the compressed keys and values in one call
+        n_k = L * H * T
+        krec = K.Record(rec.codes[:n_k], rec.norms[:n_k], rec.signs[:n_k], rec.rnorms[:n_k])
+        vrec = K.Record(rec.codes[n_k:], rec.norms[n_k:], rec.signs[n_k:], rec.rnorms[n_k:])
+        ws = torch.empty(K.rq_attend_workspace(L * HQ, g, T) + 256, dtype=torch.uint8, device=dev)
+        att = torch.empty((L * HQ, 128), dtype=torch.float32, device=dev)
+        aus = _timed(stream, lambda i: K.attend(c, c, q.view(L * HQ, 128), krec, vrec, g, T, T, out=att,
+                                                workspace=ws), 5)
         nv = flat.shape[0]
         ns = L * HQ * T
         out[spec["name"]] = {
@@ -261,8 +269,10 @@ def workload_extras(K, W, dev, stream):
             "quantize_gbs": round(nv * (256 + c.layout["record_bytes"]) / (qus * 1e-6) / 1e9, 1),
             "decode_step_us": round(dus, 1), "decode_scores": ns,
             "decode_scores_per_s": round(ns / (dus * 1e-6), 1),
-            "decode_step_per_layer_calls_us": round(lus, 1)}
-        del kv, q, flat, rec, scores, subs, c
+            "decode_step_per_layer_calls_us": round(lus, 1),
+            "decode_attention_us": round(aus, 1),
+            "decode_attention_keys_per_s": round(n_k / (aus * 1e-6), 1)}
+        del kv, q, flat, rec, scores, subs, c, krec, vrec, ws, att
         torch.cuda.empty_cache()
     return out
 

@@ -74,6 +74,10 @@ extern "C" {
  * processed in chunks of this many rows by the same call. */
 #define RQ_SCORE_CHUNK 4096
 
+/* Limits of rq_attend: keys per KV head and query rows per call. */
+#define RQ_ATTEND_MAX_KEYS (1 << 23)
+#define RQ_ATTEND_MAX_ROWS 65535
+
 typedef struct rq_ctx rq_ctx;
 
 /* Sizes of one session's record (see "Record layout" above). */
@@ -200,6 +204,38 @@ int rq_score(rq_ctx* ctx, const float* q, int hq, int group,
              const uint32_t* codes, const uint16_t* norms, const uint32_t* signs,
              const uint16_t* rnorms, int64_t t, int64_t kv_stride,
              float* scores, int64_t ld_scores, void* stream);
+
+/* Decode attention read from a compressed cache (PolarQuant article,
+ * KV-cache section: attention is softmax(Q K^T / sqrt(d)) V; README, note
+ * under "Triton Kernels": the q.k scores come straight from the compressed
+ * keys).  For query row h, reading KV head j = h / group:
+ *   out[h] = sum_t softmax_t(scale * s_ht) * v~_t
+ * with s_ht the rq_score estimate of key t and v~_t what rq_dequantize
+ * returns for value t; values are not decoded to vectors (the weighted sums
+ * run over centroids and signs, the inverse rotation once per row).
+ *   kctx, vctx   sessions of the key and value records (rotor or dense, any
+ *                bits and modes; both on the current device).
+ *   q            [hq][128] fp32 queries, 16-byte aligned; hq <= RQ_ATTEND_MAX_ROWS.
+ *   group        query rows per KV head, 1 <= group <= RQ_SCORE_CHUNK, hq % group == 0.
+ *   k..., v...   records of hq/group KV heads; head j's t keys and values
+ *                start at record row j * kv_stride (kv_stride >= t unless
+ *                hq == group); 1 <= t <= RQ_ATTEND_MAX_KEYS.
+ *   scale        multiplies every estimate before the softmax (1/sqrt(128)
+ *                for standard attention); must be finite.
+ *   workspace    device memory of at least rq_attend_workspace(hq, group, t)
+ *                bytes, 256-byte aligned, owned by the caller; its contents
+ *                are scratch (estimates, row statistics, partial sums).
+ *   out          [hq][ld_out] fp32, ld_out >= 128.
+ * Asynchronous on `stream` (four launches); nothing is allocated.  Errors:
+ * RQ_EINVAL for any argument outside these rules (nothing is written),
+ * RQ_EHIP for a launch failure.  Deterministic: fixed reduction orders. */
+int64_t rq_attend_workspace(int hq, int group, int64_t t);   /* -1 if the sizes are invalid */
+int rq_attend(const rq_ctx* kctx, const rq_ctx* vctx, const float* q, int hq, int group,
+              const uint32_t* kcodes, const uint16_t* knorms, const uint32_t* ksigns,
+              const uint16_t* krnorms, const uint32_t* vcodes, const uint16_t* vnorms,
+              const uint32_t* vsigns, const uint16_t* vrnorms, int64_t t, int64_t kv_stride,
+              float scale, void* workspace, int64_t workspace_bytes, float* out,
+              int64_t ld_out, void* stream);
 
 /* TurboQuant comparison path (hyper.ai Algorithms 1 and 2; README "How
  * TurboQuant Works"): y = Pi x_u, per-coordinate Lloyd-Max codes on 128

@@ -9,6 +9,7 @@ There is no fallback: if librq.so is missing it is built in-tree; if that
 fails, importing the binding raises.
 """
 import ctypes
+import math
 import os
 
 import numpy as np
@@ -26,8 +27,8 @@ RQ_SCORE_CHUNK = 4096
 STATUS_NAMES = {0: "RQ_OK", 1: "RQ_EINVAL", 2: "RQ_EUNSUPPORTED", 3: "RQ_ENOMEM", 4: "RQ_EHIP"}
 
 EXPORTS = ("rq_layout", "rq_host_params", "rq_host_quantizer", "rq_init", "rq_free", "rq_get_layout", "rq_get_params",
-           "rq_quantize", "rq_dequantize", "rq_roundtrip", "rq_score", "tq_quantize", "tq_dequantize",
-           "tq_roundtrip", "rq_last_error", "rq_version")
+           "rq_quantize", "rq_dequantize", "rq_roundtrip", "rq_score", "rq_attend_workspace", "rq_attend",
+           "tq_quantize", "tq_dequantize", "tq_roundtrip", "rq_last_error", "rq_version")
 
 
 class RQError(RuntimeError):
@@ -73,6 +74,8 @@ def _load():
         "rq_dequantize": ([P, P, P, P, P, I64, P, I, I64, P], I),
         "rq_roundtrip": ([P, P, I, I64, I64, P, P, P, P, P, I, I64, P], I),
         "rq_score": ([P, P, I, I, P, P, P, P, I64, I64, P, I64, P], I),
+        "rq_attend_workspace": ([I, I, I64], I64),
+        "rq_attend": ([P, P, P, I, I, P, P, P, P, P, P, P, P, I64, I64, ctypes.c_float, P, I64, P, I64, P], I),
         "tq_quantize": ([P, P, I, I64, I64, P, P, P, P, P], I),
         "tq_dequantize": ([P, P, P, P, P, I64, P, I, I64, P], I),
         "tq_roundtrip": ([P, P, I, I64, I64, P, P, P, P, P, I, I64, P], I),
@@ -244,6 +247,17 @@ def rq_score(ctx, q, hq, group, codes, norms, signs, rnorms, t, kv_stride, score
                                 kv_stride, _ptr(scores), ld_scores, _stream(stream)))
 
 
+def rq_attend_workspace(hq, group, t):
+    return _lib.rq_attend_workspace(hq, group, t)
+
+
+def rq_attend(kctx, vctx, q, hq, group, kcodes, knorms, ksigns, krnorms, vcodes, vnorms, vsigns, vrnorms, t,
+              kv_stride, scale, workspace, workspace_bytes, out, ld_out, stream=None):
+    return _check(_lib.rq_attend(kctx, vctx, _ptr(q), hq, group, _ptr(kcodes), _ptr(knorms), _ptr(ksigns),
+                                 _ptr(krnorms), _ptr(vcodes), _ptr(vnorms), _ptr(vsigns), _ptr(vrnorms), t, kv_stride,
+                                 float(scale), _ptr(workspace), workspace_bytes, _ptr(out), ld_out, _stream(stream)))
+
+
 # ----------------------------------------------------------- convenience --
 class Record:
     """Device record arrays of n vectors (torch tensors)."""
@@ -342,3 +356,28 @@ class Codec:
         rq_score(self.ctx, q, hq, group, rec.codes, rec.norms, rec.signs, rec.rnorms, t, kv_stride, out,
                  out.stride(0), stream)
         return out
+
+
+def attend(kcodec, vcodec, q, krec, vrec, group, t, kv_stride=None, scale=None, out=None, workspace=None,
+           stream=None):
+    """softmax(scale * q.k) . V over compressed keys (kcodec's records) and
+    values (vcodec's records); scale defaults to 1/sqrt(128).  Returns
+    [hq, 128] fp32.  The workspace (torch uint8 tensor) is allocated when not
+    given; pass one of rq_attend_workspace(hq, group, t) bytes to avoid that."""
+    import torch
+    hq = q.shape[0]
+    kv_stride = t if kv_stride is None else kv_stride
+    scale = 1.0 / math.sqrt(kcodec.layout["d"]) if scale is None else scale
+    need = rq_attend_workspace(hq, group, t)
+    if need < 0:
+        raise RQError(RQ_EINVAL, "rq_attend_workspace: invalid sizes")
+    if workspace is None:
+        workspace = torch.empty(need + 256, dtype=torch.uint8, device=q.device)
+    base = workspace.data_ptr()
+    ws = base + ((-base) % 256)
+    avail = workspace.numel() - (ws - base)
+    if out is None:
+        out = torch.empty((hq, kcodec.layout["d"]), dtype=torch.float32, device=q.device)
+    rq_attend(kcodec.ctx, vcodec.ctx, q, hq, group, krec.codes, krec.norms, krec.signs, krec.rnorms, vrec.codes,
+              vrec.norms, vrec.signs, vrec.rnorms, t, kv_stride, scale, ws, avail, out, out.stride(0), stream)
+    return out

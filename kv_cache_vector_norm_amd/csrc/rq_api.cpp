@@ -358,6 +358,18 @@ static rqk::DenseTables dense_tables(const rq_ctx* c) {
     return t;
 }
 
+static rqk::ScoreTables score_tables(const rq_ctx* ctx) {
+    const bool dense = ctx->host.lay.mode & RQ_DENSE;
+    rqk::ScoreTables st;
+    st.dense = dense;
+    st.rot = dense ? rqk::RotorTables{} : rotor_tables(ctx);
+    st.den = dense ? dense_tables(ctx) : rqk::DenseTables{};
+    st.mse_bits = ctx->host.lay.mse_bits;
+    st.qjl = ctx->host.lay.mode & RQ_QJL;
+    st.qjl_scale = static_cast<float>(std::sqrt(M_PI / 2.0) / rqh::kQjlRows);
+    return st;
+}
+
 static int finish(hipError_t e, const char* fn) { return e == hipSuccess ? RQ_OK : hip_fail(e, fn); }
 
 static int quantize_impl(rq_ctx* ctx, bool dense, const void* x, int x_dtype, int64_t n, int64_t ldx, uint32_t* codes,
@@ -462,14 +474,7 @@ int rq_score(rq_ctx* ctx, const float* q, int hq, int group, const uint32_t* cod
     if (group > RQ_SCORE_CHUNK) return fail(RQ_EINVAL, "rq_score: group > RQ_SCORE_CHUNK");
     if (t == 0) return RQ_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const bool dense = ctx->host.lay.mode & RQ_DENSE;
-    rqk::ScoreTables st;
-    st.dense = dense;
-    st.rot = dense ? rqk::RotorTables{} : rotor_tables(ctx);
-    st.den = dense ? dense_tables(ctx) : rqk::DenseTables{};
-    st.mse_bits = ctx->host.lay.mse_bits;
-    st.qjl = ctx->host.lay.mode & RQ_QJL;
-    st.qjl_scale = static_cast<float>(std::sqrt(M_PI / 2.0) / rqh::kQjlRows);
+    const rqk::ScoreTables st = score_tables(ctx);
     // query rows in chunks that keep whole KV heads together
     const int heads_per_chunk = std::max(1, RQ_SCORE_CHUNK / group);
     for (int h0 = 0; h0 < kv_heads; h0 += heads_per_chunk) {
@@ -482,4 +487,40 @@ int rq_score(rq_ctx* ctx, const float* q, int hq, int group, const uint32_t* cod
     return RQ_OK;
 }
 
+int64_t rq_attend_workspace(int hq, int group, int64_t t) {
+    if (hq < 1 || group < 1 || hq % group || t < 1 || t > RQ_ATTEND_MAX_KEYS) return -1;
+    return rqk::attend_plan(hq, group, t).bytes;
+}
+
+int rq_attend(const rq_ctx* kctx, const rq_ctx* vctx, const float* q, int hq, int group, const uint32_t* kcodes,
+              const uint16_t* knorms, const uint32_t* ksigns, const uint16_t* krnorms, const uint32_t* vcodes,
+              const uint16_t* vnorms, const uint32_t* vsigns, const uint16_t* vrnorms, int64_t t, int64_t kv_stride,
+              float scale, void* workspace, int64_t workspace_bytes, float* out, int64_t ld_out, void* stream) {
+    const char* fn = "rq_attend";
+    if (!kctx || !vctx) return fail(RQ_EINVAL, "rq_attend: key and value sessions are required");
+    int rc;
+    if ((rc = check_ctx(kctx, kctx->host.lay.mode & RQ_DENSE, fn))) return rc;
+    if ((rc = check_ctx(vctx, vctx->host.lay.mode & RQ_DENSE, fn))) return rc;
+    if (!q || !aligned(q, 16)) return fail(RQ_EINVAL, "rq_attend: q must be a 16-byte aligned device pointer");
+    if (hq < 1 || group < 1 || hq % group) return fail(RQ_EINVAL, "rq_attend: need hq >= 1, group >= 1, hq % group == 0");
+    if (hq > RQ_ATTEND_MAX_ROWS) return fail(RQ_EINVAL, "rq_attend: hq > RQ_ATTEND_MAX_ROWS");
+    if (group > RQ_SCORE_CHUNK) return fail(RQ_EINVAL, "rq_attend: group > RQ_SCORE_CHUNK");
+    if (t < 1) return fail(RQ_EINVAL, "rq_attend: softmax over no keys (t < 1)");
+    if (t > RQ_ATTEND_MAX_KEYS) return fail(RQ_EINVAL, "rq_attend: t > RQ_ATTEND_MAX_KEYS");
+    if (hq / group > 1 && kv_stride < t) return fail(RQ_EINVAL, "rq_attend: kv_stride < t");
+    if ((rc = check_record(kctx, kcodes, knorms, ksigns, krnorms, fn))) return rc;
+    if ((rc = check_record(vctx, vcodes, vnorms, vsigns, vrnorms, fn))) return rc;
+    if (!(scale == scale) || scale > 3.0e38f || scale < -3.0e38f) return fail(RQ_EINVAL, "rq_attend: scale is not finite");
+    const rqk::AttendPlan plan = rqk::attend_plan(hq, group, t);
+    if (!workspace || !aligned(workspace, 256)) return fail(RQ_EINVAL, "rq_attend: workspace must be a 256-byte aligned device pointer");
+    if (workspace_bytes < plan.bytes) return fail(RQ_EINVAL, "rq_attend: workspace smaller than rq_attend_workspace()");
+    if (!out || !aligned(out, 4)) return fail(RQ_EINVAL, "rq_attend: out must be a 4-byte aligned device pointer");
+    if (ld_out < rqh::kDim) return fail(RQ_EINVAL, "rq_attend: ld_out < 128");
+    const rqk::ScoreTables kt = score_tables(kctx), vt = score_tables(vctx);
+    return finish(rqk::attend(kt, vt, q, hq, group, kcodes, knorms, ksigns, krnorms, vcodes, vnorms, vsigns, vrnorms, t,
+                              kv_stride, scale, workspace, out, ld_out, static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
 }  // extern "C"
+

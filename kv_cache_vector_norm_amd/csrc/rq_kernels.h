@@ -85,4 +85,21 @@ hipError_t score(const ScoreTables& t, const float* q, int hq, int group, const 
                  const uint16_t* norms, const uint32_t* signs, const uint16_t* rnorms, int64_t tkeys,
                  int64_t kv_stride, int kv_head0, float* scores, int64_t ld_scores, hipStream_t s);
 
+
+// Decode attention over compressed keys and values (rq_attend): workspace
+// layout for hq query rows over t keys, and the launcher.
+struct AttendPlan {
+    int64_t ld;                      // row pitch of the estimates (floats)
+    int gx;                          // key slices per (KV head, 32-row block)
+    int64_t producers;               // partial rows per query row (gx * 4 waves)
+    int64_t off_scores, off_stats, off_part, bytes;
+};
+AttendPlan attend_plan(int hq, int group, int64_t t);
+
+hipError_t attend(const ScoreTables& kt, const ScoreTables& vt, const float* q, int hq, int group,
+                  const uint32_t* kcodes, const uint16_t* knorms, const uint32_t* ksigns, const uint16_t* krnorms,
+                  const uint32_t* vcodes, const uint16_t* vnorms, const uint32_t* vsigns, const uint16_t* vrnorms,
+                  int64_t t, int64_t kv_stride, float scale, void* workspace, float* out, int64_t ld_out,
+                  hipStream_t s);
+
 }  // namespace rqk

@@ -284,3 +284,44 @@ def test_decode_step_in_one_call(K, which, request):
     st["codec"].score(st["q"].view(L * HQ, D), krec, st["group"], T, T, out=out)
     _sync()
     assert torch.equal(out.view(L, HQ, T), st["scores"])
+
+
+@pytest.mark.parametrize("which,nrows", [("qwen", 4), ("llama", 3)])
+def test_attention_decode_step(K, which, nrows, request):
+    """Decode attention of the whole cache in one rq_attend call (keys and
+    values of every layer, GQA), sampled query rows against the oracle:
+    end to end within the bound the score tolerance implies, and with the
+    GPU's own estimates within 1e-5 of the largest value coordinate."""
+    st = request.getfixturevalue(which)
+    spec = st["spec"]
+    L, H, HQ, T = spec["layers"], spec["kv_heads"], spec["q_heads"], spec["tokens"]
+    g = st["group"]
+    n_k = L * H * T
+    r = st["rec"]
+    krec = K.Record(r.codes[:n_k], r.norms[:n_k], r.signs[:n_k], r.rnorms[:n_k])
+    vrec = K.Record(r.codes[n_k:], r.norms[n_k:], r.signs[n_k:], r.rnorms[n_k:])
+    q = st["q"].view(L * HQ, D)
+    scale = 1 / np.sqrt(D)
+    out = K.attend(st["codec"], st["codec"], q, krec, vrec, g, T, T, scale)
+    _sync()
+    p = st["p"]
+    rows = np.sort(np.random.Generator(np.random.PCG64(7)).choice(L * HQ, size=nrows, replace=False))
+    got = out[torch.from_numpy(rows).to(DEV)].cpu().numpy().astype(np.float64)
+    for i, row in enumerate(rows):
+        j = row // g                                    # KV head over all layers: layer * H + head
+        sl = slice(j * T, (j + 1) * T)
+        kr = OC.Record(*_gather(krec, np.arange(sl.start, sl.stop)))
+        vr = OC.Record(*_gather(vrec, np.arange(sl.start, sl.stop)))
+        qh = st["q_host"].reshape(L * HQ, D)[row:row + 1].astype(np.float64)
+        s = OC.score(p, qh, kr)[0]
+        xv = OC.dequantize(p, vr)
+        vmax = np.abs(xv).max()
+        z = scale * s
+        w = np.exp(z - z.max())
+        ref = (w / w.sum()) @ xv
+        lim = (2e-4 * scale * np.linalg.norm(qh) * OC.half_value(kr.norms).max() + 1e-5) * vmax
+        assert np.abs(got[i] - ref).max() <= lim, (row, np.abs(got[i] - ref).max() / lim)
+        sg = st["scores"].view(L * HQ, T)[row].cpu().numpy().astype(np.float64)
+        zg = scale * sg
+        wg = np.exp(zg - zg.max())
+        assert np.abs(got[i] - (wg / wg.sum()) @ xv).max() <= 1e-5 * vmax, row
