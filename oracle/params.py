@@ -114,9 +114,15 @@ class Params:
         self.dense = bool(mode & DENSE)
         self.qjl = bool(mode & QJL)
         self.b_m = mse_bits(bits, mode)
-        if not 1 <= self.b_m <= 4:
-            raise ValueError("MSE bits must be 1..4")
-        self.centroids, self.boundaries = codebook(self.b_m, d)
+        if self.b_m == 0 and self.qjl:
+            # QJL only (one bit in total): no MSE stage, the residual is the
+            # whole unit vector (blog's QJL demo with zero MSE bits: r = x,
+            # gamma = 1).  One level of value 0 and no boundaries say that.
+            self.centroids, self.boundaries = np.zeros(1), np.zeros(0)
+        elif not 1 <= self.b_m <= 4:
+            raise ValueError("MSE bits must be 1..4 (0 only with QJL)")
+        else:
+            self.centroids, self.boundaries = codebook(self.b_m, d)
         if self.dense:
             self.pi = pi_matrix(d, seed)
             self.rotors = None

@@ -307,3 +307,49 @@ def test_sparse_product_structure_counts():
     v_support = [1, 2, 3]
     outs = {int(np.nonzero(C.CAYLEY[i, j])[0][0]) for i in r_support for j in v_support}
     assert sorted(outs) == [1, 2, 3, 7]
+
+
+# ------------------------------------------------ QJL only (one bit) ---
+def test_qjl_only_record_is_the_sign_sketch_of_the_unit_vector():
+    """With zero MSE bits the residual is the whole unit vector: no codes,
+    gamma = 1 (the blog's QJL demo sets exactly this), and the record is
+    the norm plus sign(S x_u)."""
+    p = P.Params(D, 1, 0, P.QJL)
+    assert p.b_m == 0 and K.code_words(p.n_coords, p.b_m) == 0
+    x = W.gaussian(50, seed=30).astype(np.float64)
+    x[7] = 0.0
+    rec, diag = K.quantize(p, x)
+    assert rec.codes.shape == (50, 0)
+    g = K.half_value(rec.rnorms)
+    assert np.all(np.delete(g, 7) == 1.0) and g[7] == 0.0
+    nhat, xmse, ghat, sigma = K.decode(p, rec)
+    assert np.all(xmse == 0.0)
+    # the sign of every projection agrees with S applied to the unit vector
+    xu = x / np.where(np.linalg.norm(x, axis=1) > 0, np.linalg.norm(x, axis=1), 1.0)[:, None]
+    z = xu @ p.s.T
+    ok = np.abs(z) > 1e-12
+    assert np.array_equal((sigma > 0)[ok], (z >= 0)[ok])
+
+
+def test_qjl_only_estimator_and_reconstruction_are_unbiased():
+    """E_S of the one-bit inner-product estimate is <q, x> (Lemma 4 with
+    r = x_u), its variance is the closed form of Lemma 4, and E_S of the
+    dequantised vector is x itself (sqrt(pi/2)/m undoes E|s^T x_u| shrinkage)."""
+    p = P.Params(D, 1, 0, P.QJL)
+    rng = np.random.default_rng(31)
+    x = rng.normal(size=(1, D))
+    q = rng.normal(size=D)
+    xu = x[0] / np.linalg.norm(x[0])
+    est, rec_sum = [], np.zeros(D)
+    for _ in range(3000):
+        _with_s(p, rng.normal(size=(D, D)))
+        rec, _ = K.quantize(p, x)
+        nhat = K.half_value(rec.norms)[0]
+        est.append(K.score(p, q[None], rec)[0, 0] / nhat)
+        rec_sum += K.dequantize(p, rec)[0] / nhat
+    est = np.array(est)
+    assert abs(est.mean() - q @ xu) < 4 * est.std() / math.sqrt(len(est))
+    assert abs(est.var() / T.qjl_variance_exact(D, xu, q) - 1) < 0.1
+    mean_rec = rec_sum / 3000
+    # per coordinate, kappa S^T sigma has variance about pi / (2 m)
+    assert np.abs(mean_rec - xu).max() < 5 * math.sqrt(math.pi / (2 * D) / 3000)
