@@ -54,25 +54,63 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_code_digest():
-    """First 16 hex digits of the sha256 of librq.so's offload section (the
-    gfx950 code objects): it changes exactly when some kernel's machine code
-    does, and not for edits that leave the code alone."""
+MAGIC_BUNDLE = b"__CLANG_OFFLOAD_BUNDLE__"
+
+
+def _elf_sections(data):
+    """{name: (offset, size, link, entsize)} of a little-endian ELF64 image."""
+    import struct
+    shoff = struct.unpack_from("<Q", data, 0x28)[0]
+    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", data, 0x3A)
+    hdrs = [struct.unpack_from("<IIQQQQIIQQ", data, shoff + i * shentsize) for i in range(shnum)]
+    names = hdrs[shstrndx][4]
+    out = {}
+    for h in hdrs:
+        name = data[names + h[0]:data.index(b"\0", names + h[0])].decode()
+        out[name] = (h[4], h[5], h[6], h[9], h[3])
+    return out, hdrs
+
+
+def kernel_code_digest(kernel_symbol=None):
+    """First 16 hex digits of a sha256 over built gfx950 machine code in
+    librq.so: of one kernel's instructions when `kernel_symbol` (its mangled
+    name) is given, else of the whole offload section.  It changes exactly
+    when that code does, not for edits that leave it alone."""
     import struct
     with open(os.path.join(ROOT, "kv_cache_vector_norm_amd", "librq.so"), "rb") as f:
         data = f.read()
-    shoff = struct.unpack_from("<Q", data, 0x28)[0]
-    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", data, 0x3A)
-
-    def section(i):
-        return struct.unpack_from("<IIQQQQIIQQ", data, shoff + i * shentsize)
-    names = section(shstrndx)[4]
-    for i in range(shnum):
-        sh = section(i)
-        name = data[names + sh[0]:data.index(b"\0", names + sh[0])]
-        if name == b".hip_fatbin":
-            return hashlib.sha256(data[sh[4]:sh[4] + sh[5]]).hexdigest()[:16]
-    raise RuntimeError("librq.so has no .hip_fatbin section")
+    secs, _ = _elf_sections(data)
+    off, size = secs[".hip_fatbin"][0], secs[".hip_fatbin"][1]
+    fatbin = data[off:off + size]
+    if kernel_symbol is None:
+        return hashlib.sha256(fatbin).hexdigest()[:16]
+    start = fatbin.find(MAGIC_BUNDLE)
+    while start >= 0:
+        n = struct.unpack_from("<Q", fatbin, start + len(MAGIC_BUNDLE))[0]
+        pos = start + len(MAGIC_BUNDLE) + 8
+        for _ in range(n):
+            o, sz, tl = struct.unpack_from("<QQQ", fatbin, pos)
+            pos += 24
+            triple = fatbin[pos:pos + tl].decode()
+            pos += tl
+            if "gfx950" not in triple or not sz:
+                continue
+            co = fatbin[start + o:start + o + sz]
+            csecs, hdrs = _elf_sections(co)
+            if ".symtab" not in csecs:
+                continue
+            so, ss, link, ent, _ = csecs[".symtab"]
+            stro = hdrs[link][4]
+            for k in range(ss // ent):
+                st_name, st_info, st_other, st_shndx, st_value, st_size = struct.unpack_from(
+                    "<IBBHQQ", co, so + k * ent)
+                name = co[stro + st_name:co.index(b"\0", stro + st_name)].decode()
+                if name == kernel_symbol and st_size:
+                    sh = hdrs[st_shndx]
+                    foff = sh[4] + (st_value - sh[3])
+                    return hashlib.sha256(co[foff:foff + st_size]).hexdigest()[:16]
+        start = fatbin.find(MAGIC_BUNDLE, start + 1)
+    raise RuntimeError(f"kernel {kernel_symbol} not found in librq.so")
 
 
 def measured_traffic(kernel, digest):
@@ -91,6 +129,7 @@ def measured_traffic(kernel, digest):
 
 
 ROUNDTRIP_KERNEL = "rq_quant_kernel<2, true, true, true, true>"
+ROUNDTRIP_SYMBOL = "_ZN3rqk15rq_quant_kernelILi2ELb1ELb1ELb1ELb1EEEvNS_8RotorDevEPKcllPjPtS4_S5_Pcl"
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
@@ -133,7 +172,7 @@ def ingest_counters(fetch_csv, write_csv, copy_bytes):
     w_rt = sum(wr) / len(wr) * 1024.0
     cf, cw = f_copy / copy_bytes, w_copy / copy_bytes
     entry = {
-        "code": kernel_code_digest(),
+        "code": kernel_code_digest(ROUNDTRIP_SYMBOL),
         "kernel": ROUNDTRIP_KERNEL,
         "dispatches": len(fr),
         "fetch_kib_raw": round(f_rt / 1024.0, 1), "write_kib_raw": round(w_rt / 1024.0, 1),
@@ -337,7 +376,7 @@ def main():
 
     bytes_vec = algorithmic_bytes(lay)
     rt_gbs = N_VEC * bytes_vec / (rt_ms * 1e-3) / 1e9
-    digest = kernel_code_digest()
+    digest = kernel_code_digest(ROUNDTRIP_SYMBOL)
     traffic = measured_traffic("rq_roundtrip_qjl3_f16", digest)
     roof = {"bound": "hbm", "achieved": round(rt_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(rt_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
@@ -371,6 +410,16 @@ def main():
     extras["mse3_roundtrip_us"] = round(mse_us, 2)
     extras["mse3_roundtrip_gbs"] = round(N_VEC * mb / (mse_us * 1e-6) / 1e9, 1)
     extras["mse3_roundtrip_vectors_per_s"] = round(N_VEC / (mse_us * 1e-6), 1)
+
+    # QJL-only keys (1 bit in total) on the same keys: roundtrip and scoring
+    q1 = K.Codec(bits=1, seed=0, mode=K.RQ_QJL)
+    q1rec = [q1.alloc_record(N_VEC, dev) for _ in range(nsets)]
+    us1 = _timed(stream, lambda i: q1.roundtrip(xs[i % nsets], rec=q1rec[i % nsets], out=ys[i % nsets]), a.steps)
+    sus1 = _timed(stream, lambda i: q1.score(q, q1rec[i % nsets], N_Q, N_VEC, out=scs[i % nsets]), a.steps)
+    extras["qjl1_roundtrip_us"] = round(us1, 2)
+    extras["qjl1_roundtrip_gbs"] = round(N_VEC * algorithmic_bytes(q1.layout) / (us1 * 1e-6) / 1e9, 1)
+    extras["qjl1_score_us"] = round(sus1, 2)
+    del q1rec, q1
 
     if a.sweep:
         sweep = {}

@@ -63,7 +63,8 @@ extern "C" {
 
 /* mode flags (OR-able) */
 #define RQ_MSE 0   /* MSE codes only, b bits per coordinate                   */
-#define RQ_QJL 1   /* b-1 MSE bits + 1-bit QJL signs of the residual + ||r||  */
+#define RQ_QJL 1   /* b-1 MSE bits + 1-bit QJL signs of the residual + ||r||;
+                      with b = 1 QJL only: no codes, signs of S x_u, gamma  */
 #define RQ_DENSE 2 /* TurboQuant: dense 128x128 rotation Pi instead of rotors */
 
 /* element types of vector inputs / outputs */
@@ -111,7 +112,12 @@ typedef struct {
 } rq_params_host_t;
 
 /* Fills *out with the record sizes of (d, bits, mode).  CPU only.
- * RQ_EINVAL for bits outside 1..4 (MSE) / 2..5 (QJL) or unknown mode bits;
+ * RQ_EINVAL for bits outside 1..4 (MSE) / 1..5 (QJL) or unknown mode bits.
+ * bits = 1 with RQ_QJL is the QJL-only codec (blog's QJL demo with zero MSE
+ * bits: the residual is the whole unit vector, gamma = 1; README "CUDA
+ * Kernels" lists its 1-bit quantiser and score kernels): code_words = 0, a
+ * 20-byte record, rotor and dense sessions identical (no rotation is used);
+ * record code pointers may then be NULL;
  * RQ_EUNSUPPORTED for d != 128. */
 int rq_layout(int d, int bits, int mode, rq_layout_t* out);
 

@@ -188,6 +188,10 @@ int rq_init(int d, int bits, uint64_t seed, int mode, rq_ctx** out) {
     const int n = t.lay.d;
     DevAlloc da(g_alloc_countdown_init());
     auto upload = [&](void** dst, const void* src, size_t bytes) -> hipError_t {
+        if (bytes == 0) {
+            *dst = nullptr;
+            return hipSuccess;
+        }
         hipError_t r = da.alloc(dst, bytes);
         if (r != hipSuccess) return r;
         return hipMemcpy(*dst, src, bytes, hipMemcpyHostToDevice);
@@ -312,8 +316,10 @@ static int check_vectors(const void* p, int dtype, int64_t ld, const char* what,
 
 static int check_record(const rq_ctx* ctx, const void* codes, const void* norms, const void* signs,
                         const void* rnorms, const char* fn) {
-    if (!codes || !norms) return fail(RQ_EINVAL, std::string(fn) + ": codes and norms are required");
-    if (!aligned(codes, 4) || !aligned(norms, 2)) return fail(RQ_EINVAL, std::string(fn) + ": misaligned record array");
+    const bool has_codes = ctx->host.lay.code_words > 0;
+    if ((has_codes && !codes) || !norms) return fail(RQ_EINVAL, std::string(fn) + ": codes and norms are required");
+    if ((has_codes && !aligned(codes, 4)) || !aligned(norms, 2))
+        return fail(RQ_EINVAL, std::string(fn) + ": misaligned record array");
     const bool qjl = ctx->host.lay.mode & RQ_QJL;
     if (qjl != (signs != nullptr) || qjl != (rnorms != nullptr))
         return fail(RQ_EINVAL, std::string(fn) + ": signs/rnorms must be given exactly for RQ_QJL sessions");
@@ -358,6 +364,14 @@ static rqk::DenseTables dense_tables(const rq_ctx* c) {
     return t;
 }
 
+static rqk::Qjl1Dev qjl1_tables(const rq_ctx* c) {
+    rqk::Qjl1Dev t;
+    t.s_fwd = c->s_fwd;
+    t.s_back = c->s_back;
+    t.qjl_scale = static_cast<float>(std::sqrt(M_PI / 2.0) / rqh::kQjlRows);
+    return t;
+}
+
 static rqk::ScoreTables score_tables(const rq_ctx* ctx) {
     const bool dense = ctx->host.lay.mode & RQ_DENSE;
     rqk::ScoreTables st;
@@ -393,7 +407,10 @@ static int quantize_impl(rq_ctx* ctx, bool dense, const void* x, int x_dtype, in
     const int64_t ldx_b = ldx * static_cast<int64_t>(elem_size(x_dtype));
     const int64_t ldy_b = roundtrip ? ldy * static_cast<int64_t>(elem_size(y_dtype)) : 0;
     hipError_t e;
-    if (!dense)
+    if (ctx->host.lay.mse_bits == 0)
+        e = rqk::qjl1_quantize(qjl1_tables(ctx), x, x_dtype == RQ_F16, ldx_b, n, norms, signs, rnorms, y,
+                               y_dtype == RQ_F16, ldy_b, roundtrip, s);
+    else if (!dense)
         e = rqk::rotor_quantize(rotor_tables(ctx), x, x_dtype == RQ_F16, ldx_b, n, codes, norms, signs, rnorms, y,
                                 y_dtype == RQ_F16, ldy_b, roundtrip, s);
     else
@@ -414,7 +431,9 @@ static int dequantize_impl(rq_ctx* ctx, bool dense, const uint32_t* codes, const
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t ldy_b = ldy * static_cast<int64_t>(elem_size(y_dtype));
     hipError_t e;
-    if (!dense)
+    if (ctx->host.lay.mse_bits == 0)
+        e = rqk::qjl1_dequantize(qjl1_tables(ctx), norms, signs, rnorms, n, y, y_dtype == RQ_F16, ldy_b, s);
+    else if (!dense)
         e = rqk::rotor_dequantize(rotor_tables(ctx), codes, norms, signs, rnorms, n, y, y_dtype == RQ_F16, ldy_b, s);
     else
         e = rqk::dense_dequantize(dense_tables(ctx), codes, norms, signs, rnorms, n, y, y_dtype == RQ_F16, ldy_b, s);
@@ -516,6 +535,8 @@ int rq_attend(const rq_ctx* kctx, const rq_ctx* vctx, const float* q, int hq, in
     if (workspace_bytes < plan.bytes) return fail(RQ_EINVAL, "rq_attend: workspace smaller than rq_attend_workspace()");
     if (!out || !aligned(out, 4)) return fail(RQ_EINVAL, "rq_attend: out must be a 4-byte aligned device pointer");
     if (ld_out < rqh::kDim) return fail(RQ_EINVAL, "rq_attend: ld_out < 128");
+    if (vctx->host.lay.mse_bits == 0)
+        return fail(RQ_EUNSUPPORTED, "rq_attend: value sessions need at least one MSE bit");
     const rqk::ScoreTables kt = score_tables(kctx), vt = score_tables(vctx);
     return finish(rqk::attend(kt, vt, q, hq, group, kcodes, knorms, ksigns, krnorms, vcodes, vnorms, vsigns, vrnorms, t,
                               kv_stride, scale, workspace, out, ld_out, static_cast<hipStream_t>(stream)),

@@ -35,8 +35,8 @@ int make_layout(int d, int bits, int mode, Layout* out, std::string* err) {
     }
     const bool qjl = mode & kModeQjl;
     const int mse_bits = qjl ? bits - 1 : bits;
-    if (mse_bits < 1 || mse_bits > kMaxMseBits) {
-        if (err) *err = qjl ? "bits must be 2..5 with RQ_QJL" : "bits must be 1..4";
+    if (mse_bits < (qjl ? 0 : 1) || mse_bits > kMaxMseBits) {
+        if (err) *err = qjl ? "bits must be 1..5 with RQ_QJL" : "bits must be 1..4";
         return 1;
     }
     if (d <= 0) {
@@ -390,7 +390,11 @@ int make_tables(int d, int bits, uint64_t seed, int mode, Tables* out, std::stri
     Tables t;
     t.lay = lay;
     std::vector<double> c, b;
-    lloyd_max_unit_sphere(d, lay.mse_bits, &c, &b);
+    if (lay.mse_bits == 0) {
+        c.assign(1, 0.0);   // QJL only: one level of value 0, no boundaries
+    } else {
+        lloyd_max_unit_sphere(d, lay.mse_bits, &c, &b);
+    }
     t.centroids.resize(c.size());
     t.boundaries.resize(b.size());
     for (size_t i = 0; i < c.size(); ++i) t.centroids[i] = to_f32(c[i]);

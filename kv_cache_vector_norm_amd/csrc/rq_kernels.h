@@ -102,4 +102,17 @@ hipError_t attend(const ScoreTables& kt, const ScoreTables& vt, const float* q, 
                   int64_t t, int64_t kv_stride, float scale, void* workspace, float* out, int64_t ld_out,
                   hipStream_t s);
 
+// QJL-only sessions (one bit in total, no MSE stage; rotor or dense alike):
+// the record is norm, signs of S x_u and gamma, with no code words.
+struct Qjl1Dev {
+    const uint16_t* s_fwd;   // S with rows permuted for the quantiser's MFMA layout
+    const uint16_t* s_back;  // S^T permuted for the dequantiser
+    float qjl_scale;
+};
+hipError_t qjl1_quantize(const Qjl1Dev& P, const void* x, bool in_f16, int64_t ldx_bytes, int64_t n, uint16_t* norms,
+                         uint32_t* signs, uint16_t* rnorms, void* y, bool out_f16, int64_t ldy_bytes, bool roundtrip,
+                         hipStream_t s);
+hipError_t qjl1_dequantize(const Qjl1Dev& P, const uint16_t* norms, const uint32_t* signs, const uint16_t* rnorms,
+                           int64_t n, void* y, bool out_f16, int64_t ldy_bytes, hipStream_t s);
+
 }  // namespace rqk

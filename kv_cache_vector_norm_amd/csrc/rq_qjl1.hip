@@ -1,0 +1,164 @@
+// QJL-only codec (one bit per coordinate in total, no MSE stage): the
+// residual of the QJL stage is the whole unit vector (blog's QJL demo with
+// zero MSE bits: r = x, gamma = 1; README "CUDA Kernels" lists the 1-bit
+// QJL quantiser and score kernels).  Record: fp16 norm, 128 sign bits of
+// S x_u, fp16 gamma = ||x_u||.  Dequantisation: n^ sqrt(pi/2)/m gamma^ S^T sigma.
+//
+// Same machinery as the rotor QJL kernels (one lane per vector, S x_u on
+// 32x32x16 fp16 MFMAs from exact hi/lo halves of x_u carried times 2^12,
+// sign words from the accumulator sign bits, S^T sigma on MFMAs), without
+// the group loop: every K block of the residual is ready after the norm.
+#include "rq_rotor.cuh"
+
+namespace rqk {
+
+template <bool IN_F16, bool OUT_F16, bool ROUNDTRIP>
+__global__ __launch_bounds__(256) void qjl1_quant_kernel(Qjl1Dev P, const char* __restrict__ x, int64_t ldx_bytes,
+                                                         int64_t n, uint16_t* __restrict__ norms,
+                                                         uint32_t* __restrict__ signs, uint16_t* __restrict__ rnorms,
+                                                         char* __restrict__ y, int64_t ldy_bytes) {
+    constexpr float D = kQjlDomain;
+    struct Lds {
+        u32x4 tiles[4][kTileBytes / 16];
+        u32x4 s_fwd[128 * 16];
+        u32x4 s_back[ROUNDTRIP ? 128 * 16 : 1];
+    };
+    __shared__ Lds lds;
+    mat_to_lds(P.s_fwd, lds.s_fwd);
+    if constexpr (ROUNDTRIP) mat_to_lds(P.s_back, lds.s_back);
+    __syncthreads();
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    u32x4* tile = lds.tiles[wave];
+    uint32_t* stage = reinterpret_cast<uint32_t*>(tile);
+    const int64_t ntiles = (n + 63) / 64;
+    for (int64_t t = blockIdx.x * 4LL + wave; t < ntiles; t += gridDim.x * 4LL) {
+        const int64_t base = t * 64;
+        const int l = lane_id() + opaque_zero();
+        VecIn<IN_F16> in;
+        in.load(x, ldx_bytes, base, n, tile, l);
+        float ss = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kD; ++i) {
+            const float v = in.get(i);
+            ss = __builtin_fmaf(v, v, ss);
+        }
+        const float nrm = __builtin_sqrtf(ss);
+        const float inv = nrm > 0.0f ? 1.0f / nrm : 0.0f;
+        const uint32_t nh = f2h(nrm);
+        const float nhat = h2f(nh);
+        const float sc = inv * D;
+
+        f32x16 za[4][2];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) za[m][0] = za[m][1] = f32x16{};
+        float g2 = 0.0f;
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) {
+            uint32_t rh[8], rl[8];
+#pragma unroll
+            for (int d = 0; d < 8; ++d) {
+                const int i = 16 * kb + 2 * d;
+                const float a = __builtin_fmaf(in.get(i), sc, 0.0f);
+                const float b = __builtin_fmaf(in.get(i + 1), sc, 0.0f);
+                g2 = __builtin_fmaf(a, a, g2);
+                g2 = __builtin_fmaf(b, b, g2);
+                split_pair(a, b, &rh[d], &rl[d]);
+            }
+            u32x4 oh0, oh1, ol0, ol1;
+            to_operands(u32x4{rh[0], rh[1], rh[2], rh[3]}, u32x4{rh[4], rh[5], rh[6], rh[7]}, &oh0, &oh1);
+            to_operands(u32x4{rl[0], rl[1], rl[2], rl[3]}, u32x4{rl[4], rl[5], rl[6], rl[7]}, &ol0, &ol1);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) issue_fwd(lds.s_fwd, za[mt], kb, mt, oh0, oh1, ol0, ol1, l);
+        }
+        const float gam = __builtin_sqrtf(g2) * (1.0f / D);
+        const uint32_t gh = f2h(gam);
+        const float ghat = h2f(gh);
+        uint32_t sw[4];
+        u32x4 sig[ROUNDTRIP ? 2 : 1][8];
+        sign_chain<ROUNDTRIP>(za, sw, sig, l);
+
+        half_store(norms, base, n, nh, l);
+        half_store(rnorms, base, n, gh, l);
+        words_store<4>(signs, base, n, sw, stage, l);
+
+        if constexpr (ROUNDTRIP) {
+            const float zero[kD] = {};
+            VecOutT<OUT_F16> out;
+            if constexpr (!OUT_F16) out.bind(y, ldy_bytes, base, n);
+            out.begin(tile, l);
+            back_out(lds.s_back, sig, (P.qjl_scale * ghat) * D, nhat * (1.0f / D), zero, out, l);
+            out.store(y, ldy_bytes, base, n);
+        }
+    }
+}
+
+template <bool OUT_F16>
+__global__ __launch_bounds__(256) void qjl1_dequant_kernel(Qjl1Dev P, const uint16_t* __restrict__ norms,
+                                                           const uint32_t* __restrict__ signs,
+                                                           const uint16_t* __restrict__ rnorms, int64_t n,
+                                                           char* __restrict__ y, int64_t ldy_bytes) {
+    constexpr float D = kQjlDomain;
+    struct Lds {
+        u32x4 tiles[4][kTileBytes / 16];
+        u32x4 s_back[128 * 16];
+    };
+    __shared__ Lds lds;
+    mat_to_lds(P.s_back, lds.s_back);
+    __syncthreads();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    u32x4* tile = lds.tiles[wave];
+    uint32_t* stage = reinterpret_cast<uint32_t*>(tile);
+    const int64_t ntiles = (n + 63) / 64;
+    for (int64_t t = blockIdx.x * 4LL + wave; t < ntiles; t += gridDim.x * 4LL) {
+        const int64_t base = t * 64;
+        const int l = lane_id() + opaque_zero();
+        u32x4 wv[2];
+        load_sign_pairs(signs, base, n, wv, stage, l);
+        const float nhat = h2f(half_load(norms, base, n, l));
+        const float ghat = h2f(half_load(rnorms, base, n, l));
+        u32x4 sig[2][8];
+        sigma_from_words(wv, sig, l);
+        const float zero[kD] = {};
+        VecOutT<OUT_F16> out;
+        if constexpr (!OUT_F16) out.bind(y, ldy_bytes, base, n);
+        out.begin(tile, l);
+        back_out(lds.s_back, sig, (P.qjl_scale * ghat) * D, nhat * (1.0f / D), zero, out, l);
+        out.store(y, ldy_bytes, base, n);
+    }
+}
+
+hipError_t qjl1_quantize(const Qjl1Dev& P, const void* x, bool in_f16, int64_t ldx_bytes, int64_t n, uint16_t* norms,
+                         uint32_t* signs, uint16_t* rnorms, void* y, bool out_f16, int64_t ldy_bytes, bool roundtrip,
+                         hipStream_t s) {
+    const int grid = grid_for(n, 1);
+    const char* xc = static_cast<const char*>(x);
+    char* yc = static_cast<char*>(y);
+#define Q1_LAUNCH(IF, OF, RT)                                                                                  \
+    hipLaunchKernelGGL((qjl1_quant_kernel<IF, OF, RT>), dim3(grid), dim3(256), 0, s, P, xc, ldx_bytes, n, norms, \
+                       signs, rnorms, yc, ldy_bytes)
+    if (!roundtrip) {
+        if (in_f16) Q1_LAUNCH(true, true, false); else Q1_LAUNCH(false, true, false);
+    } else if (in_f16) {
+        if (out_f16) Q1_LAUNCH(true, true, true); else Q1_LAUNCH(true, false, true);
+    } else {
+        if (out_f16) Q1_LAUNCH(false, true, true); else Q1_LAUNCH(false, false, true);
+    }
+#undef Q1_LAUNCH
+    return hipGetLastError();
+}
+
+hipError_t qjl1_dequantize(const Qjl1Dev& P, const uint16_t* norms, const uint32_t* signs, const uint16_t* rnorms,
+                           int64_t n, void* y, bool out_f16, int64_t ldy_bytes, hipStream_t s) {
+    const int grid = grid_for(n, 1);
+    char* yc = static_cast<char*>(y);
+    if (out_f16)
+        hipLaunchKernelGGL((qjl1_dequant_kernel<true>), dim3(grid), dim3(256), 0, s, P, norms, signs, rnorms, n, yc,
+                           ldy_bytes);
+    else
+        hipLaunchKernelGGL((qjl1_dequant_kernel<false>), dim3(grid), dim3(256), 0, s, P, norms, signs, rnorms, n, yc,
+                           ldy_bytes);
+    return hipGetLastError();
+}
+
+}  // namespace rqk

@@ -161,6 +161,43 @@ __device__ __forceinline__ uint32_t sigma_pair(float za, float zb) {
     return (t & 0x80008000u) | 0x3C003C00u;
 }
 
+// Sign words of the own vector from the S r accumulators (bit j = [z_j >= 0]),
+// and with BACK the +-1 operands of S^T sigma for both vector halves.
+template <bool BACK>
+__device__ __forceinline__ void sign_chain(const f32x16 (&za)[4][2], uint32_t (&sw)[4],
+                                           u32x4 (&sig)[BACK ? 2 : 1][8], int l) {
+    const uint32_t sel = (l >> 5) ? 0x07060302u : 0x05040100u;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        float z0[16], z1[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float e0 = za[mt][0][r];
+            const float e1 = za[mt][1][r];
+            z0[r] = e0;
+            z1[r] = e1;
+        }
+        // sign bits: z1 of M tile rows 15..0 into bits 31..16, z0 into 15..0
+        uint32_t pb = 0u;
+#pragma unroll
+        for (int r = 15; r >= 0; --r) pb = __builtin_amdgcn_alignbit(pb, __builtin_bit_cast(uint32_t, z1[r]), 31);
+#pragma unroll
+        for (int r = 15; r >= 0; --r) pb = __builtin_amdgcn_alignbit(pb, __builtin_bit_cast(uint32_t, z0[r]), 31);
+        const auto sp = __builtin_amdgcn_permlane32_swap(pb, pb, false, false);
+        const uint32_t p0 = sp[0], p1 = sp[1];
+        sw[mt] = ~__builtin_amdgcn_perm(p1, p0, sel);
+        if constexpr (BACK) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    sig[0][2 * mt + c][q] = sigma_pair(z0[8 * c + 2 * q], z0[8 * c + 2 * q + 1]);
+                    sig[1][2 * mt + c][q] = sigma_pair(z1[8 * c + 2 * q], z1[8 * c + 2 * q + 1]);
+                }
+        }
+    }
+}
+
 // 16 sign bits (bit e = [z_e >= 0]) -> eight dwords of +-1 half pairs,
 // dword q = (sigma_2q, sigma_2q+1): the same values sigma_pair gives.
 __device__ __forceinline__ void sigma16(uint32_t bits16, u32x4& d0, u32x4& d1) {
@@ -524,36 +561,7 @@ __global__ __launch_bounds__(256) void rq_quant_kernel(RotorDev P, const char* _
             const float gam = __builtin_sqrtf(g2) * (1.0f / D);
             gh = f2h(gam);
             ghat = h2f(gh);
-            const uint32_t sel = (l >> 5) ? 0x07060302u : 0x05040100u;
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                float z0[16], z1[16];
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float e0 = za[mt][0][r];
-                    const float e1 = za[mt][1][r];
-                    z0[r] = e0;
-                    z1[r] = e1;
-                }
-                // sign bits: z1 of M tile rows 15..0 into bits 31..16, z0 into 15..0
-                uint32_t pb = 0u;
-#pragma unroll
-                for (int r = 15; r >= 0; --r) pb = __builtin_amdgcn_alignbit(pb, __builtin_bit_cast(uint32_t, z1[r]), 31);
-#pragma unroll
-                for (int r = 15; r >= 0; --r) pb = __builtin_amdgcn_alignbit(pb, __builtin_bit_cast(uint32_t, z0[r]), 31);
-                const auto sp = __builtin_amdgcn_permlane32_swap(pb, pb, false, false);
-                const uint32_t p0 = sp[0], p1 = sp[1];
-                sw[mt] = ~__builtin_amdgcn_perm(p1, p0, sel);
-                if constexpr (BACK) {
-#pragma unroll
-                    for (int c = 0; c < 2; ++c)
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            sig[0][2 * mt + c][q] = sigma_pair(z0[8 * c + 2 * q], z0[8 * c + 2 * q + 1]);
-                            sig[1][2 * mt + c][q] = sigma_pair(z1[8 * c + 2 * q], z1[8 * c + 2 * q + 1]);
-                        }
-                }
-            }
+            sign_chain<BACK>(za, sw, sig, l);
         }
 
         // record

@@ -89,7 +89,7 @@ __device__ __forceinline__ uint32_t half_at(const uint16_t* __restrict__ src, in
 // l % 32 and 32 + l % 32.  Fetched one tile ahead.
 template <int W>
 struct RecRegs {
-    uint32_t c[W];
+    uint32_t c[W > 0 ? W : 1];
     uint32_t s[4];
     uint32_t kn[2], kg[2];
 };
@@ -341,6 +341,7 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
     constexpr int NC = PAD ? kRotCoords : kD;
     constexpr int W = (NC * B + 31) / 32;
     constexpr int L = 1 << B;
+    constexpr int WA = W > 0 ? W : 1;   // B = 0: QJL-only keys, no code words
     constexpr int SW = W > 4 ? W : 4;
     constexpr int ROWS = NMT * 32;
     struct Lds {
@@ -403,7 +404,7 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
 
         // code words of keys n and 32 + n, shifted so this lane's K slots
         // start at bit 0 (slot 8 hh of each block is bit 8 B hh further)
-        uint32_t cw[2][W];
+        uint32_t cw[2][WA];
         wave_lds_sync();
 #pragma unroll
         for (int it = 0; it < W; ++it) st[it * 64 + l] = rec.c[it];
@@ -414,11 +415,11 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
             cw[1][k] = st[(32 + n) * W + k];
         }
         float cpad[2] = {0.0f, 0.0f};
-        if constexpr (PAD) {
+        if constexpr (PAD && B > 0) {
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) cpad[nt] = lds.cent[cw[nt][4 * B] & (L - 1)];
         }
-        uint32_t cs[2][W];
+        uint32_t cs[2][WA];
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
@@ -458,41 +459,43 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
                 acc2[m][nt] = f32x16{};
             }
 
+        if constexpr (B > 0) {
 #pragma unroll
-        for (int kb = 0; kb < 8; ++kb) {
-            __builtin_amdgcn_sched_barrier(0);
-            u32x4 ch[2], cl[2];
+            for (int kb = 0; kb < 8; ++kb) {
+                // (no scheduling barrier: lookups of the next block may move up)
+                u32x4 ch[2], cl[2];
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
+                for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int bit = 16 * B * kb + 2 * B * q, wi = bit >> 5, off = bit & 31;
-                    uint32_t f = cs[nt][wi] >> off;
-                    if (off + 2 * B > 32) f = __builtin_amdgcn_alignbit(cs[nt][wi + 1], cs[nt][wi], off);
-                    const uint32_t addr = (f & (L * L - 1)) * 8u;
-                    const uint32_t hi = *reinterpret_cast<const uint32_t*>(pairc + addr);
-                    const uint32_t lo = *reinterpret_cast<const uint32_t*>(pairc + addr + 4);
-                    ch[nt][q] = hi;
-                    cl[nt][q] = lo;
-                }
+                    for (int q = 0; q < 4; ++q) {
+                        const int bit = 16 * B * kb + 2 * B * q, wi = bit >> 5, off = bit & 31;
+                        uint32_t f = cs[nt][wi] >> off;
+                        if (off + 2 * B > 32) f = __builtin_amdgcn_alignbit(cs[nt][wi + 1], cs[nt][wi], off);
+                        const uint32_t addr = (f & (L * L - 1)) * 8u;
+                        const uint32_t hi = *reinterpret_cast<const uint32_t*>(pairc + addr);
+                        const uint32_t lo = *reinterpret_cast<const uint32_t*>(pairc + addr + 4);
+                        ch[nt][q] = hi;
+                        cl[nt][q] = lo;
+                    }
 #pragma unroll
-            for (int m = 0; m < NMT; ++m) {
-                const int r = (32 * m + n) * kRowStride + 2 * kb + hh;
-                const u32x4 q1 = lds.qrows[r + kOffQ1];
-                const u32x4 q2 = lds.qrows[r + kOffQ2];
-                const u32x4 q3 = lds.qrows[r + kOffQ3];
+                for (int m = 0; m < NMT; ++m) {
+                    const int r = (32 * m + n) * kRowStride + 2 * kb + hh;
+                    const u32x4 q1 = lds.qrows[r + kOffQ1];
+                    const u32x4 q2 = lds.qrows[r + kOffQ2];
+                    const u32x4 q3 = lds.qrows[r + kOffQ3];
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
-                    acc1[m][nt] = mfma(q1, ch[nt], acc1[m][nt]);
-                    acc1[m][nt] = mfma(q2, cl[nt], acc1[m][nt]);
-                    acc1[m][nt] = mfma(q3, ch[nt], acc1[m][nt]);
+                    for (int nt = 0; nt < 2; ++nt) {
+                        acc1[m][nt] = mfma(q1, ch[nt], acc1[m][nt]);
+                        acc1[m][nt] = mfma(q2, cl[nt], acc1[m][nt]);
+                        acc1[m][nt] = mfma(q3, ch[nt], acc1[m][nt]);
+                    }
                 }
             }
         }
         if constexpr (QJL) {
 #pragma unroll
             for (int kb = 0; kb < 8; ++kb) {
-                __builtin_amdgcn_sched_barrier(0);
+                // (no scheduling barrier)
                 u32x4 s[2];
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) s[nt] = sigma8((sg[nt][kb >> 1] >> (16 * (kb & 1))) & 0xFFu);
@@ -599,6 +602,7 @@ hipError_t score(const ScoreTables& t, const float* q, int hq, int group, const 
     const int qblocks = (group + 63) / 64;
     const int nmt = a.rows_per_block > 32 ? 2 : 1;
     switch (t.mse_bits * 2 + (t.qjl ? 1 : 0)) {
+        case 1: launch_main_b<0, true>(t.dense, nmt, a, kv_heads, qblocks, s); break;
         case 2: launch_main_b<1, false>(t.dense, nmt, a, kv_heads, qblocks, s); break;
         case 3: launch_main_b<1, true>(t.dense, nmt, a, kv_heads, qblocks, s); break;
         case 4: launch_main_b<2, false>(t.dense, nmt, a, kv_heads, qblocks, s); break;

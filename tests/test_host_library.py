@@ -42,10 +42,14 @@ def test_layouts(K):
     assert q["mse_bits"] == 2 and q["sign_words"] == 4 and q["record_bytes"] == 9 * 4 + 2 + 16 + 2
     assert K.rq_layout(128, 3, K.RQ_MSE)["record_bytes"] == 54
     assert K.rq_layout(128, 3, K.RQ_MSE)["n_groups"] == 43
+    # QJL only: no code words, norm + 4 sign words + gamma
+    for m in (K.RQ_QJL, K.RQ_QJL | K.RQ_DENSE):
+        q1 = K.rq_layout(128, 1, m)
+        assert q1["mse_bits"] == 0 and q1["code_words"] == 0 and q1["record_bytes"] == 2 + 16 + 2
 
 
-@pytest.mark.parametrize("bits,mode", [(b, OP.MSE) for b in (1, 2, 3, 4)] + [(b, OP.QJL) for b in (2, 3, 4, 5)]
-                         + [(b, OP.DENSE) for b in (2, 3, 4)] + [(3, OP.DENSE | OP.QJL)])
+@pytest.mark.parametrize("bits,mode", [(b, OP.MSE) for b in (1, 2, 3, 4)] + [(b, OP.QJL) for b in (1, 2, 3, 4, 5)]
+                         + [(b, OP.DENSE) for b in (2, 3, 4)] + [(3, OP.DENSE | OP.QJL), (1, OP.DENSE | OP.QJL)])
 def test_host_params_match_oracle(K, bits, mode):
     p = K.rq_host_params(128, bits, 0, mode)
     o = OP.Params(128, bits, 0, mode)
@@ -53,6 +57,9 @@ def test_host_params_match_oracle(K, bits, mode):
     def ulps(a, b):
         a = np.asarray(a, np.float32)
         b = np.asarray(b, np.float32)
+        assert a.shape == b.shape
+        if a.size == 0:
+            return 0
         return np.abs(a.view(np.int32).astype(np.int64) - b.view(np.int32).astype(np.int64)).max()
 
     assert ulps(p["centroids"], o.centroids) <= 1
@@ -76,7 +83,7 @@ def test_different_seeds_give_different_tables(K):
 
 
 @pytest.mark.parametrize("d,bits,mode,status", [
-    (128, 0, 0, 1), (128, 5, 0, 1), (128, 1, 1, 1), (128, 6, 1, 1), (128, 3, 8, 1), (-1, 3, 0, 1),
+    (128, 0, 0, 1), (128, 5, 0, 1), (128, 0, 1, 1), (128, 6, 1, 1), (128, 3, 8, 1), (-1, 3, 0, 1),
     (64, 3, 0, 2), (256, 3, 1, 2)])
 def test_bad_settings(K, d, bits, mode, status):
     with pytest.raises(K.RQError) as e:
