@@ -268,6 +268,33 @@ def attend(pk: Params, pv: Params, q, krec: Record, vrec: Record, group, t, scal
     return out
 
 
+def attend_with_current(pk: Params, pv: Params, q, krec: Record, vrec: Record, group, t, scale, k_cur, v_cur,
+                        kv_stride=None):
+    """Decode attention of one step where the current token's own key and
+    value enter at full precision and the t earlier tokens come from the
+    compressed cache (README "Post-Prefill Quantization": each decode step
+    stores the new key compressed but the current token's attention uses
+    the full-precision key).  For query head h of KV head j = h // group,
+    one softmax over [scale * score(q_h, k_t) for cached t] + [scale <q_h, k_cur_j>]
+    weighs [dequantize(v_t)] + [v_cur_j].  Returns [H, d]."""
+    kv_stride = t if kv_stride is None else kv_stride
+    q = np.asarray(q, dtype=np.float64)
+    k_cur = np.asarray(k_cur, dtype=np.float64)
+    v_cur = np.asarray(v_cur, dtype=np.float64)
+    s = scale * score_gqa(pk, q, krec, group, t, kv_stride) if t > 0 else np.zeros((q.shape[0], 0))
+    out = np.zeros((q.shape[0], pv.d))
+    for h in range(q.shape[0]):
+        j = h // group
+        z = np.concatenate([s[h], [scale * (q[h] @ k_cur[j])]])
+        e = np.exp(z - z.max())
+        pr = e / e.sum()
+        vals = v_cur[j][None, :]
+        if t > 0:
+            vals = np.concatenate([dequantize(pv, _rows(vrec, slice(j * kv_stride, j * kv_stride + t))), vals])
+        out[h] = pr @ vals
+    return out
+
+
 def roundtrip(p: Params, x):
     rec, diag = quantize(p, x)
     return rec, dequantize(p, rec), diag

@@ -120,3 +120,39 @@ def test_weights_are_the_softmax_of_scaled_estimates(pk, pv):
         est = OC.score(pk, q[h:h + 1], OC._rows(krec, slice(j * t, (j + 1) * t)))[0]
         ref = softmax(scale * est) @ _head_values(pv, vrec, j, t, t)
         assert np.abs(out[h] - ref).max() < 1e-13
+
+
+# ------------------------------------------- the current token, exact ---
+def test_current_token_alone_and_uniform():
+    q = W.queries(4, seed=30)
+    kc = W.gaussian(2, seed=31).astype(np.float64)
+    vc = W.gaussian(2, seed=32).astype(np.float64)
+    krec, vrec = _cache(1, 2, 33)
+    # nothing cached: the output is the current value
+    out0 = OC.attend_with_current(PK, PV, q, krec, vrec, 2, 0, 0.1, kc, vc)
+    for h in range(4):
+        assert np.array_equal(out0[h], vc[h // 2])
+    # scale 0: the plain mean over the cached values and the current one
+    t = 20
+    krec, vrec = _cache(t, 2, 34)
+    out = OC.attend_with_current(PK, PV, q, krec, vrec, 2, t, 0.0, kc, vc)
+    for h in range(4):
+        j = h // 2
+        vals = np.concatenate([_head_values(PV, vrec, j, t, t), vc[j][None]])
+        assert np.abs(out[h] - vals.mean(0)).max() < 1e-14
+
+
+def test_current_token_dominant_or_negligible():
+    t = 16
+    krec, vrec = _cache(t, 1, 35)
+    q = W.queries(2, seed=36).astype(np.float64)
+    vc = W.gaussian(1, seed=37).astype(np.float64)
+    # the current key along q dominates: its value comes back
+    kc = 50.0 * q[:1] / np.linalg.norm(q[0])
+    out = OC.attend_with_current(PK, PV, q[:1], krec, vrec, 1, t, 1.0, kc, vc)
+    assert np.abs(out[0] - vc[0]).max() < 1e-9
+    # against q it is negligible: the cached attention comes back
+    kn = -50.0 * q[:1] / np.linalg.norm(q[0])
+    out = OC.attend_with_current(PK, PV, q[:1], krec, vrec, 1, t, 1.0, kn, vc)
+    ref = OC.attend(PK, PV, q[:1], krec, vrec, 1, t, 1.0)
+    assert np.abs(out - ref).max() < 1e-9 * np.abs(ref).max()
