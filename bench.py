@@ -269,6 +269,40 @@ def workload_extras(K, W, dev, stream):
     out["keys262144_roundtrip"] = sweep
     del xs, ys
 
+    # paged cache, Qwen2.5-3B shape, one sequence: bulk prefill of 32,768
+    # tokens per layer, then decode steps (per layer: append the new token,
+    # attend with the current token's key and value at full precision)
+    spec = W.QWEN25_3B
+    L, H, T, HQ = spec["layers"], spec["kv_heads"], spec["tokens"], spec["q_heads"]
+    kcod, vcod = K.Codec(bits=3, seed=0, mode=K.RQ_QJL), K.Codec(bits=3, seed=0, mode=K.RQ_MSE)
+    cache = K.Cache(kcod, vcod, layers=L, kv_heads=H, page_tokens=256, max_pages=L * H * (T // 256 + 8))
+    seq = cache.open(T + 1024)
+    kvl = torch.randn((2, H, T, 128), device=dev).to(torch.float16)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for layer in range(L):
+        cache.append(seq, layer, kvl[0], kvl[1])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    prefill_us = e0.elapsed_time(e1) * 1e3
+    qd = torch.randn((HQ, 128), device=dev)
+    kn = torch.randn((H, 1, 128), device=dev).to(torch.float16)
+    kcur = kn[:, 0].float().contiguous()
+    need = K.lib().rq_cache_attend_workspace(cache.h, HQ, T + 64)
+    ws = torch.empty(need + 256, dtype=torch.uint8, device=dev)
+    att = torch.empty((HQ, 128), dtype=torch.float32, device=dev)
+
+    def step(i):
+        for layer in range(L):
+            cache.attend(seq, layer, qd, k_cur=kcur, v_cur=kcur, out=att, workspace=ws)
+            cache.append(seq, layer, kn, kn)
+    dec_us = _timed(stream, step, 5)
+    out["qwen2.5-3b_paged_cache"] = {"prefill_tokens": T, "prefill_quantize_us": round(prefill_us, 1),
+                                     "decode_step_us": round(dec_us, 1), "layers": L, "page_tokens": 256}
+    cache.close(seq)
+    del cache, kvl, ws, att
+
     for spec in (W.QWEN25_3B, W.LLAMA31_8B):
         L, H, T, HQ = spec["layers"], spec["kv_heads"], spec["tokens"], spec["q_heads"]
         g = HQ // H

@@ -243,6 +243,54 @@ int rq_attend(const rq_ctx* kctx, const rq_ctx* vctx, const float* q, int hq, in
               float scale, void* workspace, int64_t workspace_bytes, float* out,
               int64_t ld_out, void* stream);
 
+/* Paged compressed KV cache (README "Post-Prefill Quantization": prefill at
+ * full precision, one bulk quantisation of the prefill cache, then each
+ * decode step stores its new key compressed while the current token's own
+ * attention uses the full-precision key; README "Project Structure" names
+ * the KV-cache classes this replaces).
+ *
+ * A cache owns a device pool of `max_pages` pages; a page holds the records
+ * of `page_tokens` consecutive tokens of one (layer, KV head), keys (kctx's
+ * layout) and values (vctx's layout) alike.  A sequence reserves
+ * ceil(max_tokens / page_tokens) pages per (layer, KV head) when opened and
+ * gives them back when closed, so its page table is fixed and uploaded once.
+ * Inputs go through a staging area of `stage_tokens` tokens per KV head.
+ * Every call below runs on the caller's stream except create/free/open/close,
+ * which synchronise the device (they are not on the decode path).  Errors:
+ * RQ_EINVAL (arguments), RQ_EUNSUPPORTED (value sessions without an MSE
+ * stage), RQ_ENOMEM (pool or device memory exhausted), RQ_EHIP. */
+typedef struct rq_cache rq_cache;
+int rq_cache_create(const rq_ctx* kctx, const rq_ctx* vctx, int layers, int kv_heads,
+                    int page_tokens /* power of two, 64..2^20 */, int64_t max_pages,
+                    int64_t stage_tokens, rq_cache** out);
+void rq_cache_free(rq_cache* cache);
+int rq_cache_open(rq_cache* cache, int64_t max_tokens, int* seq);
+int rq_cache_close(rq_cache* cache, int seq);
+/* Tokens cached for (seq, layer), or -1 for a bad argument. */
+int64_t rq_cache_length(const rq_cache* cache, int seq, int layer);
+int64_t rq_cache_free_pages(const rq_cache* cache);
+/* Quantises n new tokens of every KV head of one layer and stores them after
+ * the tokens already cached: k, v [kv_heads][n][ld] fp16 or fp32 (dtype),
+ * 16-byte aligned, ld >= 128.  n = prompt length for the bulk prefill,
+ * 1 per decode step. */
+int rq_cache_append(rq_cache* cache, int seq, int layer, const void* k, const void* v,
+                    int dtype, int64_t n, int64_t ld, void* stream);
+/* Copies the cached records of one layer back into dense record arrays
+ * [kv_heads][length] (which = 0 keys, 1 values); device pointers. */
+int rq_cache_read(const rq_cache* cache, int seq, int layer, int which, uint32_t* codes,
+                  uint16_t* norms, uint32_t* signs, uint16_t* rnorms, void* stream);
+/* Workspace rq_cache_attend needs for hq query rows over t cached tokens. */
+int64_t rq_cache_attend_workspace(const rq_cache* cache, int hq, int64_t t);
+/* rq_attend over the cached tokens of (seq, layer) through the page table
+ * (GQA: hq / kv_heads query rows per KV head), and, when k_cur and v_cur are
+ * given ([kv_heads][128] fp32, the current token's exact key and value), the
+ * current token folded into the same softmax at full precision:
+ *   out_h = sum_{t cached} p_t v~_t + p_cur v_cur, p = softmax(scale * [s_h, q_h.k_cur]).
+ * With nothing cached, k_cur/v_cur are required and out_h = v_cur. */
+int rq_cache_attend(rq_cache* cache, int seq, int layer, const float* q, int hq, float scale,
+                    const float* k_cur, const float* v_cur, void* workspace,
+                    int64_t workspace_bytes, float* out, int64_t ld_out, void* stream);
+
 /* TurboQuant comparison path (hyper.ai Algorithms 1 and 2; README "How
  * TurboQuant Works"): y = Pi x_u, per-coordinate Lloyd-Max codes on 128
  * coordinates, x~ = Pi^T y^ (+ the QJL stage with RQ_QJL).  Same arguments

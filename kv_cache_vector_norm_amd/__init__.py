@@ -28,7 +28,9 @@ STATUS_NAMES = {0: "RQ_OK", 1: "RQ_EINVAL", 2: "RQ_EUNSUPPORTED", 3: "RQ_ENOMEM"
 
 EXPORTS = ("rq_layout", "rq_host_params", "rq_host_quantizer", "rq_init", "rq_free", "rq_get_layout", "rq_get_params",
            "rq_quantize", "rq_dequantize", "rq_roundtrip", "rq_score", "rq_attend_workspace", "rq_attend",
-           "tq_quantize", "tq_dequantize", "tq_roundtrip", "rq_last_error", "rq_version")
+           "tq_quantize", "tq_dequantize", "tq_roundtrip", "rq_cache_create", "rq_cache_free", "rq_cache_open",
+           "rq_cache_close", "rq_cache_length", "rq_cache_free_pages", "rq_cache_append", "rq_cache_read",
+           "rq_cache_attend_workspace", "rq_cache_attend", "rq_last_error", "rq_version")
 
 
 class RQError(RuntimeError):
@@ -76,6 +78,16 @@ def _load():
         "rq_score": ([P, P, I, I, P, P, P, P, I64, I64, P, I64, P], I),
         "rq_attend_workspace": ([I, I, I64], I64),
         "rq_attend": ([P, P, P, I, I, P, P, P, P, P, P, P, P, I64, I64, ctypes.c_float, P, I64, P, I64, P], I),
+        "rq_cache_create": ([P, P, I, I, I, I64, I64, ctypes.POINTER(P)], I),
+        "rq_cache_free": ([P], None),
+        "rq_cache_open": ([P, I64, ctypes.POINTER(I)], I),
+        "rq_cache_close": ([P, I], I),
+        "rq_cache_length": ([P, I, I], I64),
+        "rq_cache_free_pages": ([P], I64),
+        "rq_cache_append": ([P, I, I, P, P, I, I64, I64, P], I),
+        "rq_cache_read": ([P, I, I, I, P, P, P, P, P], I),
+        "rq_cache_attend_workspace": ([P, I, I64], I64),
+        "rq_cache_attend": ([P, I, I, P, I, ctypes.c_float, P, P, P, I64, P, I64, P], I),
         "tq_quantize": ([P, P, I, I64, I64, P, P, P, P, P], I),
         "tq_dequantize": ([P, P, P, P, P, I64, P, I, I64, P], I),
         "tq_roundtrip": ([P, P, I, I64, I64, P, P, P, P, P, I, I64, P], I),
@@ -381,3 +393,73 @@ def attend(kcodec, vcodec, q, krec, vrec, group, t, kv_stride=None, scale=None, 
     rq_attend(kcodec.ctx, vcodec.ctx, q, hq, group, krec.codes, krec.norms, krec.signs, krec.rnorms, vrec.codes,
               vrec.norms, vrec.signs, vrec.rnorms, t, kv_stride, scale, ws, avail, out, out.stride(0), stream)
     return out
+
+
+class Cache:
+    """Paged compressed KV cache (rq_cache_*): keys in kcodec's format, values
+    in vcodec's, pages of `page_tokens` tokens per (layer, KV head)."""
+
+    def __init__(self, kcodec, vcodec, layers, kv_heads, page_tokens=256, max_pages=1024, stage_tokens=65536):
+        self.kc, self.vc = kcodec, vcodec
+        self.layers, self.kv_heads = layers, kv_heads
+        h = ctypes.c_void_p()
+        _check(_lib.rq_cache_create(kcodec.ctx, vcodec.ctx, layers, kv_heads, page_tokens, max_pages, stage_tokens,
+                                    ctypes.byref(h)))
+        self.h = h
+
+    def close_cache(self):
+        if self.h:
+            _lib.rq_cache_free(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close_cache()
+        except Exception:
+            pass
+
+    def open(self, max_tokens):
+        sid = ctypes.c_int()
+        _check(_lib.rq_cache_open(self.h, max_tokens, ctypes.byref(sid)))
+        return sid.value
+
+    def close(self, seq):
+        _check(_lib.rq_cache_close(self.h, seq))
+
+    def length(self, seq, layer):
+        return _lib.rq_cache_length(self.h, seq, layer)
+
+    def free_pages(self):
+        return _lib.rq_cache_free_pages(self.h)
+
+    def append(self, seq, layer, k, v, stream=None):
+        """k, v: [kv_heads, n, 128] fp16 or fp32 (rows of pitch stride(1))."""
+        dt = self.kc._dt(k)
+        _check(_lib.rq_cache_append(self.h, seq, layer, _ptr(k), _ptr(v), dt, k.shape[1], k.stride(1),
+                                    _stream(stream)))
+
+    def read(self, seq, layer, which, stream=None):
+        """Dense copy [kv_heads * length] of the cached key (0) or value (1) records."""
+        codec = self.vc if which else self.kc
+        rec = codec.alloc_record(self.kv_heads * self.length(seq, layer))
+        _check(_lib.rq_cache_read(self.h, seq, layer, which, _ptr(rec.codes), _ptr(rec.norms), _ptr(rec.signs),
+                                  _ptr(rec.rnorms), _stream(stream)))
+        return rec
+
+    def attend(self, seq, layer, q, scale=None, k_cur=None, v_cur=None, out=None, workspace=None, stream=None):
+        import torch
+        hq = q.shape[0]
+        scale = 1.0 / math.sqrt(128) if scale is None else scale
+        t = self.length(seq, layer)
+        need = _lib.rq_cache_attend_workspace(self.h, hq, t)
+        if need < 0:
+            raise RQError(RQ_EINVAL, "rq_cache_attend_workspace: invalid sizes")
+        if workspace is None:
+            workspace = torch.empty(need + 256, dtype=torch.uint8, device=q.device)
+        base = workspace.data_ptr()
+        ws = base + ((-base) % 256)
+        if out is None:
+            out = torch.empty((hq, 128), dtype=torch.float32, device=q.device)
+        _check(_lib.rq_cache_attend(self.h, seq, layer, _ptr(q), hq, float(scale), _ptr(k_cur), _ptr(v_cur), ws,
+                                    workspace.numel() - (ws - base), _ptr(out), out.stride(0), _stream(stream)))
+        return out

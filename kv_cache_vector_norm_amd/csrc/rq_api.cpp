@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -543,5 +544,288 @@ int rq_attend(const rq_ctx* kctx, const rq_ctx* vctx, const float* q, int hq, in
                   fn);
 }
 
+// ------------------------------------------------------ paged KV cache --
+// A pool of fixed-size pages of compressed K and V record rows shared by
+// sequences; a sequence reserves its pages when it is opened (so its page
+// table is fixed and uploaded once) and returns them when closed.
+struct rq_cache {
+    struct Pool {
+        uint32_t* codes = nullptr;
+        uint16_t* norms = nullptr;
+        uint32_t* signs = nullptr;
+        uint16_t* rnorms = nullptr;
+    };
+    struct Seq {
+        bool open = false;
+        int64_t cap = 0, pph = 0;          // tokens per (layer, head); pages per (layer, head)
+        std::vector<int64_t> len;          // tokens cached, per layer
+        std::vector<int32_t> pages;        // [layer][head][pph]
+        int32_t* table = nullptr;          // device copy of `pages`
+    };
+    const rq_ctx* k = nullptr;
+    const rq_ctx* v = nullptr;
+    int layers = 0, kv_heads = 0, shift = 0, device = -1;
+    int64_t page = 0, max_pages = 0, stage = 0;
+    Pool kp, vp, ks, vs;
+    std::vector<int32_t> free_pages;
+    std::vector<Seq> seqs;
+    std::vector<void*> dev;
+};
+
+static hipError_t pool_alloc(DevAlloc& da, const rq_ctx* c, int64_t rows, rq_cache::Pool* p) {
+    const rqh::Layout& l = c->host.lay;
+    hipError_t e;
+    if (l.code_words > 0 && (e = da.alloc(reinterpret_cast<void**>(&p->codes), rows * l.code_words * 4)) != hipSuccess)
+        return e;
+    if ((e = da.alloc(reinterpret_cast<void**>(&p->norms), rows * 2)) != hipSuccess) return e;
+    if (l.mode & RQ_QJL) {
+        if ((e = da.alloc(reinterpret_cast<void**>(&p->signs), rows * 16)) != hipSuccess) return e;
+        if ((e = da.alloc(reinterpret_cast<void**>(&p->rnorms), rows * 2)) != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+static rqk::PageTable page_table(const rq_cache* c, const rq_cache::Seq& q, int layer) {
+    rqk::PageTable pt;
+    pt.pages = q.table + static_cast<int64_t>(layer) * c->kv_heads * q.pph;
+    pt.shift = c->shift;
+    pt.stride = q.pph;
+    return pt;
+}
+
+static int check_seq(const rq_cache* c, int seq, int layer, const char* fn) {
+    if (!c) return fail(RQ_EINVAL, std::string(fn) + ": cache is NULL");
+    if (seq < 0 || seq >= static_cast<int>(c->seqs.size()) || !c->seqs[seq].open)
+        return fail(RQ_EINVAL, std::string(fn) + ": no such open sequence");
+    if (layer < 0 || layer >= c->layers) return fail(RQ_EINVAL, std::string(fn) + ": layer out of range");
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess || cur != c->device)
+        return fail(RQ_EINVAL, std::string(fn) + ": current HIP device is not the cache's device");
+    return RQ_OK;
+}
+
+int rq_cache_create(const rq_ctx* kctx, const rq_ctx* vctx, int layers, int kv_heads, int page_tokens,
+                    int64_t max_pages, int64_t stage_tokens, rq_cache** out) {
+    const char* fn = "rq_cache_create";
+    if (!out) return fail(RQ_EINVAL, "rq_cache_create: out is NULL");
+    *out = nullptr;
+    if (!kctx || !vctx) return fail(RQ_EINVAL, "rq_cache_create: key and value sessions are required");
+    int rc;
+    if ((rc = check_ctx(kctx, kctx->host.lay.mode & RQ_DENSE, fn))) return rc;
+    if ((rc = check_ctx(vctx, vctx->host.lay.mode & RQ_DENSE, fn))) return rc;
+    if (vctx->host.lay.mse_bits == 0) return fail(RQ_EUNSUPPORTED, "rq_cache_create: value sessions need an MSE stage");
+    if (layers < 1 || kv_heads < 1) return fail(RQ_EINVAL, "rq_cache_create: layers and kv_heads must be >= 1");
+    if (page_tokens < 64 || page_tokens > (1 << 20) || (page_tokens & (page_tokens - 1)))
+        return fail(RQ_EINVAL, "rq_cache_create: page_tokens must be a power of two in [64, 2^20]");
+    if (max_pages < 1 || max_pages > (int64_t(1) << 31) - 1) return fail(RQ_EINVAL, "rq_cache_create: max_pages out of range");
+    if (stage_tokens < 1) return fail(RQ_EINVAL, "rq_cache_create: stage_tokens must be >= 1");
+    rq_cache* c = new (std::nothrow) rq_cache;
+    if (!c) return fail(RQ_ENOMEM, "rq_cache_create: host allocation failed");
+    c->k = kctx;
+    c->v = vctx;
+    c->layers = layers;
+    c->kv_heads = kv_heads;
+    c->page = page_tokens;
+    while ((int64_t(1) << c->shift) < page_tokens) ++c->shift;
+    c->max_pages = max_pages;
+    c->stage = stage_tokens;
+    c->device = kctx->device;
+    DevAlloc da(0);
+    const int64_t rows = max_pages * page_tokens, srows = stage_tokens * kv_heads;
+    hipError_t e;
+    if ((e = pool_alloc(da, kctx, rows, &c->kp)) != hipSuccess || (e = pool_alloc(da, vctx, rows, &c->vp)) != hipSuccess ||
+        (e = pool_alloc(da, kctx, srows, &c->ks)) != hipSuccess || (e = pool_alloc(da, vctx, srows, &c->vs)) != hipSuccess) {
+        da.release();
+        delete c;
+        return fail(RQ_ENOMEM, std::string("rq_cache_create: device allocation failed: ") + hipGetErrorString(e));
+    }
+    c->dev = da.owned;
+    c->free_pages.resize(static_cast<size_t>(max_pages));
+    for (int64_t i = 0; i < max_pages; ++i) c->free_pages[static_cast<size_t>(i)] = static_cast<int32_t>(max_pages - 1 - i);
+    *out = c;
+    return RQ_OK;
+}
+
+void rq_cache_free(rq_cache* c) {
+    if (!c) return;
+    (void)hipDeviceSynchronize();
+    for (auto& q : c->seqs)
+        if (q.table) (void)hipFree(q.table);
+    for (void* p : c->dev) (void)hipFree(p);
+    delete c;
+}
+
+int rq_cache_open(rq_cache* c, int64_t max_tokens, int* seq) {
+    if (!c || !seq) return fail(RQ_EINVAL, "rq_cache_open: cache and seq are required");
+    if (max_tokens < 1) return fail(RQ_EINVAL, "rq_cache_open: max_tokens must be >= 1");
+    const int64_t pph = (max_tokens + c->page - 1) / c->page;
+    const int64_t need = pph * c->layers * c->kv_heads;
+    if (need > static_cast<int64_t>(c->free_pages.size()))
+        return fail(RQ_ENOMEM, "rq_cache_open: not enough free pages in the pool");
+    rq_cache::Seq q;
+    q.open = true;
+    q.cap = pph * c->page;
+    q.pph = pph;
+    q.len.assign(static_cast<size_t>(c->layers), 0);
+    q.pages.resize(static_cast<size_t>(need));
+    for (int64_t i = 0; i < need; ++i) {
+        q.pages[static_cast<size_t>(i)] = c->free_pages.back();
+        c->free_pages.pop_back();
+    }
+    hipError_t e = hipMalloc(reinterpret_cast<void**>(&q.table), static_cast<size_t>(need) * 4);
+    if (e == hipSuccess) e = hipMemcpy(q.table, q.pages.data(), static_cast<size_t>(need) * 4, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+        for (int32_t pg : q.pages) c->free_pages.push_back(pg);
+        if (q.table) (void)hipFree(q.table);
+        return hip_fail(e, "rq_cache_open");
+    }
+    int id = -1;
+    for (size_t i = 0; i < c->seqs.size(); ++i)
+        if (!c->seqs[i].open) {
+            id = static_cast<int>(i);
+            break;
+        }
+    if (id < 0) {
+        id = static_cast<int>(c->seqs.size());
+        c->seqs.emplace_back();
+    }
+    c->seqs[static_cast<size_t>(id)] = std::move(q);
+    *seq = id;
+    return RQ_OK;
+}
+
+int rq_cache_close(rq_cache* c, int seq) {
+    int rc;
+    if ((rc = check_seq(c, seq, 0, "rq_cache_close"))) return rc;
+    rq_cache::Seq& q = c->seqs[static_cast<size_t>(seq)];
+    (void)hipDeviceSynchronize();   // no launch may still read the pages or the table
+    for (int32_t pg : q.pages) c->free_pages.push_back(pg);
+    (void)hipFree(q.table);
+    q = rq_cache::Seq{};
+    return RQ_OK;
+}
+
+int64_t rq_cache_length(const rq_cache* c, int seq, int layer) {
+    if (!c || seq < 0 || seq >= static_cast<int>(c->seqs.size()) || !c->seqs[seq].open || layer < 0 || layer >= c->layers)
+        return -1;
+    return c->seqs[static_cast<size_t>(seq)].len[static_cast<size_t>(layer)];
+}
+
+int64_t rq_cache_free_pages(const rq_cache* c) { return c ? static_cast<int64_t>(c->free_pages.size()) : -1; }
+
+static int cache_quantize_into_pages(rq_cache* c, const rq_ctx* ctx, const rq_cache::Pool& stage,
+                                     const rq_cache::Pool& pool, const rqk::PageTable& pt, const void* x, int dtype,
+                                     int64_t n, int64_t ld, int64_t t0, hipStream_t s, const char* fn) {
+    const rqh::Layout& l = ctx->host.lay;
+    const bool dense = l.mode & RQ_DENSE;
+    const bool qjl = l.mode & RQ_QJL;
+    const char* xb = static_cast<const char*>(x);
+    const int64_t es = static_cast<int64_t>(elem_size(dtype));
+    int rc;
+    if (n <= c->stage) {
+        // every head's n rows in one launch: rows j * n + i, pitch ld
+        if ((rc = quantize_impl(const_cast<rq_ctx*>(ctx), dense, x, dtype, n * c->kv_heads, ld, stage.codes, stage.norms,
+                                stage.signs, stage.rnorms, nullptr, RQ_F32, 0, false, s, fn)))
+            return rc;
+        return finish(rqk::scatter_rows(stage.codes, stage.norms, stage.signs, stage.rnorms, pool.codes, pool.norms,
+                                        pool.signs, pool.rnorms, l.code_words, qjl, n, t0, c->kv_heads, pt, false, s),
+                      fn);
+    }
+    for (int j = 0; j < c->kv_heads; ++j) {
+        rqk::PageTable hp = pt;
+        hp.pages = pt.pages + static_cast<int64_t>(j) * pt.stride;
+        for (int64_t c0 = 0; c0 < n; c0 += c->stage) {
+            const int64_t m = std::min(c->stage, n - c0);
+            if ((rc = quantize_impl(const_cast<rq_ctx*>(ctx), dense, xb + (j * n + c0) * ld * es, dtype, m, ld, stage.codes,
+                                    stage.norms, stage.signs, stage.rnorms, nullptr, RQ_F32, 0, false, s, fn)))
+                return rc;
+            const hipError_t e = rqk::scatter_rows(stage.codes, stage.norms, stage.signs, stage.rnorms, pool.codes,
+                                                   pool.norms, pool.signs, pool.rnorms, l.code_words, qjl, m, t0 + c0, 1,
+                                                   hp, false, s);
+            if (e != hipSuccess) return hip_fail(e, fn);
+        }
+    }
+    return RQ_OK;
+}
+
+int rq_cache_append(rq_cache* c, int seq, int layer, const void* k, const void* v, int dtype, int64_t n, int64_t ld,
+                    void* stream) {
+    const char* fn = "rq_cache_append";
+    int rc;
+    if ((rc = check_seq(c, seq, layer, fn))) return rc;
+    if (n < 0) return fail(RQ_EINVAL, "rq_cache_append: n < 0");
+    if ((rc = check_vectors(k, dtype, ld, "k", fn))) return rc;
+    if ((rc = check_vectors(v, dtype, ld, "v", fn))) return rc;
+    rq_cache::Seq& q = c->seqs[static_cast<size_t>(seq)];
+    int64_t& len = q.len[static_cast<size_t>(layer)];
+    if (len + n > q.cap) return fail(RQ_EINVAL, "rq_cache_append: the sequence's reserved tokens are exhausted");
+    if (n == 0) return RQ_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const rqk::PageTable pt = page_table(c, q, layer);
+    if ((rc = cache_quantize_into_pages(c, c->k, c->ks, c->kp, pt, k, dtype, n, ld, len, s, fn))) return rc;
+    if ((rc = cache_quantize_into_pages(c, c->v, c->vs, c->vp, pt, v, dtype, n, ld, len, s, fn))) return rc;
+    len += n;
+    return RQ_OK;
+}
+
+int rq_cache_read(const rq_cache* c, int seq, int layer, int which, uint32_t* codes, uint16_t* norms, uint32_t* signs,
+                  uint16_t* rnorms, void* stream) {
+    const char* fn = "rq_cache_read";
+    int rc;
+    if ((rc = check_seq(c, seq, layer, fn))) return rc;
+    if (which != 0 && which != 1) return fail(RQ_EINVAL, "rq_cache_read: which must be 0 (keys) or 1 (values)");
+    const rq_ctx* ctx = which ? c->v : c->k;
+    if ((rc = check_record(ctx, codes, norms, signs, rnorms, fn))) return rc;
+    const rq_cache::Seq& q = c->seqs[static_cast<size_t>(seq)];
+    const int64_t n = q.len[static_cast<size_t>(layer)];
+    const rq_cache::Pool& pool = which ? c->vp : c->kp;
+    const rqh::Layout& l = ctx->host.lay;
+    return finish(rqk::scatter_rows(pool.codes, pool.norms, pool.signs, pool.rnorms, codes, norms, signs, rnorms,
+                                    l.code_words, l.mode & RQ_QJL, n, 0, c->kv_heads, page_table(c, q, layer), true,
+                                    static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
+int64_t rq_cache_attend_workspace(const rq_cache* c, int hq, int64_t t) {
+    if (!c || hq < 1 || hq % c->kv_heads || t < 0 || t > RQ_ATTEND_MAX_KEYS) return -1;
+    return t == 0 ? 0 : rqk::attend_plan(hq, hq / c->kv_heads, t).bytes;
+}
+
+int rq_cache_attend(rq_cache* c, int seq, int layer, const float* q, int hq, float scale, const float* k_cur,
+                    const float* v_cur, void* workspace, int64_t workspace_bytes, float* out, int64_t ld_out,
+                    void* stream) {
+    const char* fn = "rq_cache_attend";
+    int rc;
+    if ((rc = check_seq(c, seq, layer, fn))) return rc;
+    if (!q || !aligned(q, 16)) return fail(RQ_EINVAL, "rq_cache_attend: q must be a 16-byte aligned device pointer");
+    if (hq < 1 || hq % c->kv_heads || hq > RQ_ATTEND_MAX_ROWS)
+        return fail(RQ_EINVAL, "rq_cache_attend: hq must be a positive multiple of kv_heads, <= RQ_ATTEND_MAX_ROWS");
+    if ((k_cur == nullptr) != (v_cur == nullptr)) return fail(RQ_EINVAL, "rq_cache_attend: give both or neither of k_cur, v_cur");
+    if (k_cur && (!aligned(k_cur, 4) || !aligned(v_cur, 4))) return fail(RQ_EINVAL, "rq_cache_attend: misaligned k_cur / v_cur");
+    if (!(scale == scale) || scale > 3.0e38f || scale < -3.0e38f) return fail(RQ_EINVAL, "rq_cache_attend: scale is not finite");
+    if (!out || !aligned(out, 4) || ld_out < rqh::kDim) return fail(RQ_EINVAL, "rq_cache_attend: bad out / ld_out");
+    const rq_cache::Seq& sq = c->seqs[static_cast<size_t>(seq)];
+    const int64_t t = sq.len[static_cast<size_t>(layer)];
+    const int group = hq / c->kv_heads;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (t == 0) {
+        if (!k_cur) return fail(RQ_EINVAL, "rq_cache_attend: no cached tokens and no current token");
+        return finish(rqk::merge_current(q, hq, group, k_cur, v_cur, nullptr, scale, out, ld_out, s), fn);
+    }
+    const rqk::AttendPlan plan = rqk::attend_plan(hq, group, t);
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < plan.bytes)
+        return fail(RQ_EINVAL, "rq_cache_attend: workspace missing, misaligned or smaller than rq_cache_attend_workspace()");
+    const rqk::PageTable pt = page_table(c, sq, layer);
+    const rqk::ScoreTables kt = score_tables(c->k), vt = score_tables(c->v);
+    hipError_t e = rqk::attend(kt, vt, q, hq, group, c->kp.codes, c->kp.norms, c->kp.signs, c->kp.rnorms, c->vp.codes,
+                               c->vp.norms, c->vp.signs, c->vp.rnorms, t, 0, scale, workspace, out, ld_out, s, pt, pt);
+    if (e == hipSuccess && k_cur)
+        e = rqk::merge_current(q, hq, group, k_cur, v_cur,
+                               reinterpret_cast<const float2*>(static_cast<char*>(workspace) + plan.off_stats), scale,
+                               out, ld_out, s);
+    return finish(e, fn);
+}
+
 }  // extern "C"
+
 

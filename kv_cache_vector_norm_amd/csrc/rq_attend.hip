@@ -48,15 +48,27 @@ __global__ __launch_bounds__(256) void attend_stats_kernel(const float* __restri
     const int row = blockIdx.x;
     const float* s = scores + static_cast<int64_t>(row) * ld;
     float m = -INFINITY, l = 0.0f;
-    for (int64_t i = threadIdx.x; i < t; i += 256) {
-        const float v = s[i] * scale;
+    auto add = [&](float x) {
+        const float v = x * scale;
         if (v > m) {
             l = l * exp2_hw((m - v) * kLog2e) + 1.0f;
             m = v;
         } else {
             l += exp2_hw((v - m) * kLog2e);
         }
+    };
+    // rows are 16-byte aligned (the pitch is a multiple of 4 floats)
+    const float4* s4 = reinterpret_cast<const float4*>(s);
+    const int64_t t4 = t / 4;
+#pragma unroll 4
+    for (int64_t i = threadIdx.x; i < t4; i += 256) {
+        const float4 v = s4[i];
+        add(v.x);
+        add(v.y);
+        add(v.z);
+        add(v.w);
     }
+    for (int64_t i = 4 * t4 + threadIdx.x; i < t; i += 256) add(s[i]);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
         const float m2 = __shfl_xor(m, off);
@@ -93,6 +105,7 @@ struct AttendArgs {
     int group, rows;          // rows: query rows of the call
     const float* cent;        // value centroids
     float* part;              // [producers][rows][kPartStride]
+    PageTable pt;             // value record rows (pages == nullptr: kvh * kv_stride + key)
 };
 
 // Exact split of a pair into fp16 hi and lo11 = half((x - hi) 2^11).
@@ -115,6 +128,7 @@ __global__ __launch_bounds__(256) void attend_values_kernel(AttendArgs a) {
     struct Lds {
         u32x4 pairs[L * L];         // codes (k, k+1) -> {2^11 C_hi, C_lo, C_hi} half pairs
         Wave w[4];
+        float sum[32][kPartStride];   // the block's partial rows, waves added in order
     };
     __shared__ Lds lds;
 
@@ -173,24 +187,29 @@ __global__ __launch_bounds__(256) void attend_values_kernel(AttendArgs a) {
         // the tile's value records into LDS, key-minor
         {
             const int64_t left = a.t - kbase;
-            const rsrc_t rc = make_rsrc(a.codes + (rbase + kbase) * W, tile_range(left, 4 * W));
+            int64_t row = rbase + kbase;
+            if (a.pt.pages != nullptr) {
+                const int64_t pg = a.pt.pages[kvh * a.pt.stride + (kbase >> a.pt.shift)];
+                row = (pg << a.pt.shift) + (kbase & ((int64_t(1) << a.pt.shift) - 1));
+            }
+            const rsrc_t rc = make_rsrc(a.codes + row * W, tile_range(left, 4 * W));
             uint32_t cw[W];
 #pragma unroll
             for (int it = 0; it < W; ++it)
                 cw[it] = __builtin_amdgcn_raw_buffer_load_b32(rc, static_cast<uint32_t>(4 * l), 256 * it, kNonTemporal);
             uint32_t sw[4];
             if constexpr (QJL) {
-                const rsrc_t rs = make_rsrc(a.signs + (rbase + kbase) * 4, tile_range(left, 16));
+                const rsrc_t rs = make_rsrc(a.signs + row * 4, tile_range(left, 16));
 #pragma unroll
                 for (int it = 0; it < 4; ++it)
                     sw[it] = __builtin_amdgcn_raw_buffer_load_b32(rs, static_cast<uint32_t>(4 * l), 256 * it,
                                                                   kNonTemporal);
             }
-            const rsrc_t rn = make_rsrc(a.norms + rbase + kbase, tile_range(left, 2));
+            const rsrc_t rn = make_rsrc(a.norms + row, tile_range(left, 2));
             const uint32_t nb = __builtin_amdgcn_raw_buffer_load_b16(rn, static_cast<uint32_t>(2 * l), 0, kNonTemporal);
             uint32_t gb = 0u;
             if constexpr (QJL) {
-                const rsrc_t rg = make_rsrc(a.rnorms + rbase + kbase, tile_range(left, 2));
+                const rsrc_t rg = make_rsrc(a.rnorms + row, tile_range(left, 2));
                 gb = __builtin_amdgcn_raw_buffer_load_b16(rg, static_cast<uint32_t>(2 * l), 0, kNonTemporal);
             }
             wave_lds_sync();
@@ -312,21 +331,39 @@ __global__ __launch_bounds__(256) void attend_values_kernel(AttendArgs a) {
         }
     }
 
-    // partial rows of this wave: producer blockIdx.x * 4 + wave
-    const int64_t prod = blockIdx.x * 4LL + wave;
+    // the block's partial rows: the four waves' sums are added in wave order
+    // through LDS, then written as producer blockIdx.x
     const float uc = 1.0f / (2048.0f * sc), us = 1.0f / 2048.0f;
+    for (int w = 0; w < 4; ++w) {
+        if (wave == w) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int m = 8 * (r / 4) + (r % 4) + 4 * hh;
-        if (m < nrows) {
-            float* dst = a.part + (prod * a.rows + row0 + m) * kPartStride;
+            for (int r = 0; r < 16; ++r) {
+                const int m = 8 * (r / 4) + (r % 4) + 4 * hh;
+                if (m < nrows) {
+                    float* dst = lds.sum[m];
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                dst[32 * nt + n] = acc_c[nt][r] * uc;
-                if constexpr (QJL) dst[kPartSigma + 32 * nt + n] = acc_s[nt][r] * us;
+                    for (int nt = 0; nt < 4; ++nt) {
+                        const float c = acc_c[nt][r] * uc;
+                        dst[32 * nt + n] = w == 0 ? c : dst[32 * nt + n] + c;
+                        if constexpr (QJL) {
+                            const float g = acc_s[nt][r] * us;
+                            dst[kPartSigma + 32 * nt + n] = w == 0 ? g : dst[kPartSigma + 32 * nt + n] + g;
+                        }
+                    }
+                    if (n == 0) {
+                        const float pc = PAD ? acc_p[r] * uc : 0.0f;
+                        dst[kPartPad] = w == 0 ? pc : dst[kPartPad] + pc;
+                    }
+                }
             }
-            if (n == 0) dst[kPartPad] = PAD ? acc_p[r] * uc : 0.0f;
         }
+        __syncthreads();
+    }
+    float* out = a.part + (static_cast<int64_t>(blockIdx.x) * a.rows + row0) * kPartStride;
+    for (int i = threadIdx.x; i < nrows * kPartStride; i += kBlock) {
+        const int m = i / kPartStride, c = i % kPartStride;
+        out[static_cast<int64_t>(m) * kPartStride + c] = (c < kPartPad + 1 && (QJL || c < kPartSigma || c == kPartPad))
+                                                             ? lds.sum[m][c] : 0.0f;
     }
 }
 
@@ -346,24 +383,29 @@ struct CombineArgs {
     int64_t ld_out;
 };
 
-__global__ __launch_bounds__(256) void attend_combine_kernel(CombineArgs a) {
+__global__ __launch_bounds__(320) void attend_combine_kernel(CombineArgs a) {
     const int row = blockIdx.x;
     __shared__ float oc[kRotCoords + 3];
     __shared__ float os[kD];
     const int j = threadIdx.x;
-    if (j < kD) {
-        float c = 0.0f, s = 0.0f;
-        for (int64_t p = 0; p < a.producers; ++p) {
-            const float* src = a.part + (p * a.rows + row) * kPartStride;
-            c += src[j];
-            if (a.qjl) s += src[kPartSigma + j];
-        }
-        oc[j] = c;
-        os[j] = s;
-    } else if (j == kD) {
-        float c = 0.0f;
-        for (int64_t p = 0; p < a.producers; ++p) c += a.part[(p * a.rows + row) * kPartStride + kPartPad];
-        oc[kD] = c;
+    // producers in a fixed order: eight interleaved running sums (loads in
+    // flight together), added pairwise at the end
+    const int col = j < kD ? j : (j < 2 * kD ? kPartSigma + (j - kD) : kPartPad);
+    if (j < 2 * kD + 1 && (j < kD || j == 2 * kD || a.qjl)) {
+        float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+        const int64_t pstride = static_cast<int64_t>(a.rows) * kPartStride;
+        const float* src = a.part + static_cast<int64_t>(row) * kPartStride + col;
+        int64_t p = 0;
+        for (; p + 8 <= a.producers; p += 8)
+#pragma unroll
+            for (int u = 0; u < 8; ++u) acc[u] += src[(p + u) * pstride];
+        for (int u = 0; p < a.producers; ++p, ++u) acc[u] += src[p * pstride];
+        const float v = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+        if (j < kD) oc[j] = v;
+        else if (j == 2 * kD) oc[kD] = v;
+        else os[j - kD] = v;
+    } else if (j < 2 * kD) {
+        os[j - kD] = 0.0f;
     }
     __syncthreads();
     if (j < kD) {
@@ -398,10 +440,11 @@ AttendPlan attend_plan(int hq, int group, int64_t t) {
     const int64_t want = (ntiles + 3) / 4;
     const int64_t units = static_cast<int64_t>(kv_heads) * qblocks;
     int64_t gx = 512 / units;
+    if (gx > 64) gx = 64;           // partial rows per query row stay few
     if (gx > want) gx = want;
     if (gx < 1) gx = 1;
     p.gx = static_cast<int>(gx);
-    p.producers = gx * 4;
+    p.producers = gx;
     auto up = [](int64_t b) { return (b + 255) & ~int64_t(255); };
     p.off_scores = 0;
     p.off_stats = up(static_cast<int64_t>(hq) * p.ld * 4);
@@ -432,7 +475,7 @@ hipError_t attend(const ScoreTables& kt, const ScoreTables& vt, const float* q, 
                   const uint32_t* kcodes, const uint16_t* knorms, const uint32_t* ksigns, const uint16_t* krnorms,
                   const uint32_t* vcodes, const uint16_t* vnorms, const uint32_t* vsigns, const uint16_t* vrnorms,
                   int64_t t, int64_t kv_stride, float scale, void* workspace, float* out, int64_t ld_out,
-                  hipStream_t s) {
+                  hipStream_t s, const PageTable& kpt, const PageTable& vpt) {
     const AttendPlan p = attend_plan(hq, group, t);
     char* ws = static_cast<char*>(workspace);
     float* scores = reinterpret_cast<float*>(ws + p.off_scores);
@@ -445,7 +488,7 @@ hipError_t attend(const ScoreTables& kt, const ScoreTables& vt, const float* q, 
         const int nh = kv_heads - h0 < heads_per_chunk ? kv_heads - h0 : heads_per_chunk;
         const hipError_t e = score(kt, q + static_cast<int64_t>(h0) * group * kD, nh * group, group, kcodes, knorms,
                                    ksigns, krnorms, t, kv_stride, h0, scores + static_cast<int64_t>(h0) * group * p.ld,
-                                   p.ld, s);
+                                   p.ld, s, kpt);
         if (e != hipSuccess) return e;
     }
     // 2. row statistics
@@ -466,6 +509,7 @@ hipError_t attend(const ScoreTables& kt, const ScoreTables& vt, const float* q, 
     a.rows = hq;
     a.cent = vt.dense ? vt.den.cent : vt.rot.cent;
     a.part = part;
+    a.pt = vpt;
     hipError_t e;
     if (vt.dense)
         e = vt.qjl ? launch_values_b<true, false>(vt.mse_bits, a, p, kv_heads, s)
@@ -489,7 +533,7 @@ hipError_t attend(const ScoreTables& kt, const ScoreTables& vt, const float* q, 
     c.kappa = vt.qjl_scale;
     c.out = out;
     c.ld_out = ld_out;
-    hipLaunchKernelGGL(attend_combine_kernel, dim3(hq), dim3(kBlock), 0, s, c);
+    hipLaunchKernelGGL(attend_combine_kernel, dim3(hq), dim3(320), 0, s, c);
     return hipGetLastError();
 }
 

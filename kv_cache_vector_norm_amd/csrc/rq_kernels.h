@@ -78,12 +78,22 @@ hipError_t dense_dequantize(const DenseTables& t, const uint32_t* codes, const u
                             const uint16_t* rnorms, int64_t n, void* y, bool out_f16, int64_t ldy_bytes,
                             hipStream_t s);
 
+// Optional page table of record rows: key t of (global) KV head j lives in
+// record row pages[j * stride + (t >> shift)] * 2^shift + (t & (2^shift - 1)).
+// With pages == nullptr, KV head j's keys are rows j * kv_stride + t.
+struct PageTable {
+    const int32_t* pages = nullptr;
+    int shift = 0;          // log2 of the page size in keys, >= 6
+    int64_t stride = 0;     // table entries per KV head
+};
+
 // Scores hq query rows (group rows per KV head) against t keys per KV head;
 // KV head j (0-based within this call) reads record rows
 // (kv_head0 + j) * kv_stride + [0, t).
 hipError_t score(const ScoreTables& t, const float* q, int hq, int group, const uint32_t* codes,
                  const uint16_t* norms, const uint32_t* signs, const uint16_t* rnorms, int64_t tkeys,
-                 int64_t kv_stride, int kv_head0, float* scores, int64_t ld_scores, hipStream_t s);
+                 int64_t kv_stride, int kv_head0, float* scores, int64_t ld_scores, hipStream_t s,
+                 const PageTable& pt = PageTable{});
 
 
 // Decode attention over compressed keys and values (rq_attend): workspace
@@ -91,7 +101,7 @@ hipError_t score(const ScoreTables& t, const float* q, int hq, int group, const 
 struct AttendPlan {
     int64_t ld;                      // row pitch of the estimates (floats)
     int gx;                          // key slices per (KV head, 32-row block)
-    int64_t producers;               // partial rows per query row (gx * 4 waves)
+    int64_t producers;               // partial rows per query row (one per key-slice block)
     int64_t off_scores, off_stats, off_part, bytes;
 };
 AttendPlan attend_plan(int hq, int group, int64_t t);
@@ -100,7 +110,7 @@ hipError_t attend(const ScoreTables& kt, const ScoreTables& vt, const float* q, 
                   const uint32_t* kcodes, const uint16_t* knorms, const uint32_t* ksigns, const uint16_t* krnorms,
                   const uint32_t* vcodes, const uint16_t* vnorms, const uint32_t* vsigns, const uint16_t* vrnorms,
                   int64_t t, int64_t kv_stride, float scale, void* workspace, float* out, int64_t ld_out,
-                  hipStream_t s);
+                  hipStream_t s, const PageTable& kpt = PageTable{}, const PageTable& vpt = PageTable{});
 
 // QJL-only sessions (one bit in total, no MSE stage; rotor or dense alike):
 // the record is norm, signs of S x_u and gamma, with no code words.
@@ -114,5 +124,13 @@ hipError_t qjl1_quantize(const Qjl1Dev& P, const void* x, bool in_f16, int64_t l
                          hipStream_t s);
 hipError_t qjl1_dequantize(const Qjl1Dev& P, const uint16_t* norms, const uint32_t* signs, const uint16_t* rnorms,
                            int64_t n, void* y, bool out_f16, int64_t ldy_bytes, hipStream_t s);
+
+// Paged cache helpers (rq_cache.hip).
+hipError_t scatter_rows(const uint32_t* src_codes, const uint16_t* src_norms, const uint32_t* src_signs,
+                        const uint16_t* src_rnorms, uint32_t* dst_codes, uint16_t* dst_norms, uint32_t* dst_signs,
+                        uint16_t* dst_rnorms, int words, bool qjl, int64_t n, int64_t t0, int heads,
+                        const PageTable& pt, bool gather, hipStream_t s);
+hipError_t merge_current(const float* q, int hq, int group, const float* kcur, const float* vcur,
+                         const float2* stats, float scale, float* out, int64_t ld_out, hipStream_t s);
 
 }  // namespace rqk

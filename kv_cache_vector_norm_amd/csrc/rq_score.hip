@@ -66,7 +66,16 @@ struct MainArgs {
     float qjl_scale;
     float* scores;
     int64_t ld;
+    PageTable pt;
 };
+
+// Record row of the first key of the 64-key tile at key kbase of KV head
+// `head` (global index); pages never split a tile (page size >= 64 keys).
+__device__ __forceinline__ int64_t tile_row(const PageTable& pt, int64_t rbase, int head, int64_t kbase) {
+    if (pt.pages == nullptr) return rbase + kbase;
+    const int64_t pg = pt.pages[head * pt.stride + (kbase >> pt.shift)];
+    return (pg << pt.shift) + (kbase & ((int64_t(1) << pt.shift) - 1));
+}
 
 // 8 sign bits (bit e = [z_e >= 0]) -> four dwords of +-1 half pairs.
 __device__ __forceinline__ u32x4 sigma8(uint32_t byte) {
@@ -94,14 +103,16 @@ struct RecRegs {
     uint32_t kn[2], kg[2];
 };
 template <int W, bool QJL>
-__device__ __forceinline__ void rec_fetch(const MainArgs& a, int64_t rbase, int64_t kbase, RecRegs<W>& r, int l) {
-    const int64_t nk = a.t;
-    const rsrc_t rc = make_rsrc(a.codes + (rbase + kbase) * W, tile_range(nk - kbase, 4 * W));
+__device__ __forceinline__ void rec_fetch(const MainArgs& a, int64_t rbase, int head, int64_t kbase, RecRegs<W>& r,
+                                          int l) {
+    const int64_t left = a.t - kbase;
+    const int64_t row = tile_row(a.pt, rbase, head, kbase);
+    const rsrc_t rc = make_rsrc(a.codes + row * W, tile_range(left, 4 * W));
 #pragma unroll
     for (int it = 0; it < W; ++it)
         r.c[it] = __builtin_amdgcn_raw_buffer_load_b32(rc, static_cast<uint32_t>(4 * l), 256 * it, kNonTemporal);
     if constexpr (QJL) {
-        const rsrc_t rsg = make_rsrc(a.signs + (rbase + kbase) * 4, tile_range(nk - kbase, 16));
+        const rsrc_t rsg = make_rsrc(a.signs + row * 4, tile_range(left, 16));
 #pragma unroll
         for (int it = 0; it < 4; ++it)
             r.s[it] = __builtin_amdgcn_raw_buffer_load_b32(rsg, static_cast<uint32_t>(4 * l), 256 * it, kNonTemporal);
@@ -109,8 +120,8 @@ __device__ __forceinline__ void rec_fetch(const MainArgs& a, int64_t rbase, int6
     const int n = l & 31;
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-        r.kn[nt] = half_at(a.norms + rbase, kbase, nk, 32 * nt + n);
-        r.kg[nt] = QJL ? half_at(a.rnorms + rbase, kbase, nk, 32 * nt + n) : 0u;
+        r.kn[nt] = half_at(a.norms + row, 0, left, 32 * nt + n);
+        r.kg[nt] = QJL ? half_at(a.rnorms + row, 0, left, 32 * nt + n) : 0u;
     }
 }
 
@@ -369,7 +380,8 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
     // the first tile's record is requested before the block's staging
     RecRegs<W> rec;
     int64_t tile = blockIdx.x * 4LL + wave;
-    if (tile < ntiles) rec_fetch<W, QJL>(a, rbase, tile * 64, rec, lane_id());
+    const int ghead = a.kv_head0 + kvh;
+    if (tile < ntiles) rec_fetch<W, QJL>(a, rbase, ghead, tile * 64, rec, lane_id());
     // and so are the query rows and the X / S fragments of the query build
     QueryRegs<NMT> qr;
     query_load<NMT>(a, row0, nrows, qr);
@@ -448,7 +460,7 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
             kg[nt] = QJL ? h2f(rec.kg[nt]) * a.qjl_scale : 0.0f;
         }
         // next tile's record, in flight during this tile's MFMAs and stores
-        if (tile + tstep < ntiles) rec_fetch<W, QJL>(a, rbase, (tile + tstep) * 64, rec, l);
+        if (tile + tstep < ntiles) rec_fetch<W, QJL>(a, rbase, ghead, (tile + tstep) * 64, rec, l);
 
         f32x16 acc1[NMT][2], acc2[NMT][2];
 #pragma unroll
@@ -578,8 +590,10 @@ static void launch_main_b(bool dense, int nmt, const MainArgs& a, int kv_heads, 
 
 hipError_t score(const ScoreTables& t, const float* q, int hq, int group, const uint32_t* codes,
                  const uint16_t* norms, const uint32_t* signs, const uint16_t* rnorms, int64_t tkeys,
-                 int64_t kv_stride, int kv_head0, float* scores, int64_t ld_scores, hipStream_t s) {
+                 int64_t kv_stride, int kv_head0, float* scores, int64_t ld_scores, hipStream_t s,
+                 const PageTable& pt) {
     MainArgs a;
+    a.pt = pt;
     a.q = q;
     a.rotmat = t.rot.rotmat;
     a.x_hi = t.dense ? t.den.pi_hi : t.rot.phi_hi;
