@@ -1,0 +1,91 @@
+"""Pins for the oracle's PolarQuant (CPU only), against what the PolarQuant
+article fixes: the lemma's angle density and its normalising constant, its
+mean pi/4, the level each density belongs to (Monte Carlo over Gaussian
+vectors), the uniform level-1 codebook, the exact inverse of the polar
+transform, and the article's bit budget (496 bits per token, 4.13x)."""
+import math
+
+import numpy as np
+import pytest
+from scipy import integrate
+
+from oracle import polar as PQ
+from kv_cache_vector_norm_amd import workloads as W
+
+
+@pytest.mark.parametrize("level", [1, 2, 3])
+def test_lemma_density_is_normalised_with_mean_pi_over_4(level):
+    f = PQ.level_density(level)
+    mass = integrate.quad(f, 0, math.pi / 2, epsrel=1e-13)[0]
+    mean = integrate.quad(lambda t: t * f(t), 0, math.pi / 2, epsrel=1e-13)[0]
+    assert abs(mass - 1.0) < 1e-12
+    assert abs(mean - math.pi / 4) < 1e-12
+
+
+def test_level_one_codebook_is_uniform():
+    c, t = PQ.codebooks()[0]
+    assert np.allclose(c, (np.arange(16) + 0.5) * math.pi / 8, atol=2e-7)
+    assert np.allclose(t, np.arange(1, 16) * math.pi / 8, atol=2e-7)
+
+
+@pytest.mark.parametrize("level", [1, 2, 3])
+def test_later_codebooks_are_symmetric_about_pi_over_4(level):
+    c, t = PQ.codebooks()[level]
+    assert c.shape == (4,) and t.shape == (3,)
+    assert np.allclose(c + c[::-1], math.pi / 2, atol=4e-7)
+    assert abs(t[1] - math.pi / 4) < 2e-7
+    # tighter levels: the cells shrink toward pi/4 as k grows
+    if level > 1:
+        assert c[0] > PQ.codebooks()[level - 1][0][0]
+
+
+def test_angle_laws_per_level_monte_carlo():
+    """Angles of N(0, 1) vectors: level 1 uniform on [0, 2 pi), level l >= 2
+    the lemma's law with k = 2^(l-1) (mean pi/4, its variance)."""
+    y = np.random.Generator(np.random.PCG64(3)).standard_normal((4000, 128))
+    angles, _ = PQ.polar_transform(y)
+    a0 = angles[0].ravel()
+    assert abs(a0.mean() - math.pi) < 4 * (2 * math.pi / math.sqrt(12)) / math.sqrt(a0.size)
+    assert abs(a0.var() - (2 * math.pi) ** 2 / 12) < 0.05 * (2 * math.pi) ** 2 / 12
+    for level in (1, 2, 3):
+        f = PQ.level_density(level)
+        var = integrate.quad(lambda t: (t - math.pi / 4) ** 2 * f(t), 0, math.pi / 2)[0]
+        th = angles[level].ravel()
+        assert abs(th.mean() - math.pi / 4) < 4 * math.sqrt(var / th.size)
+        assert abs(th.var() / var - 1) < 0.06
+
+
+def test_polar_transform_inverts_exactly():
+    y = W.gaussian(20, seed=4).astype(np.float64)
+    angles, radii = PQ.polar_transform(y)
+    assert radii.shape == (20, 8)
+    assert np.abs(PQ.polar_inverse(angles, radii) - y).max() < 1e-12
+    assert np.allclose(np.linalg.norm(radii, axis=1), np.linalg.norm(y, axis=1))
+
+
+def test_bit_budget_of_the_article():
+    bits = PQ.CODE_BITS + 16 * PQ.N_RADII
+    assert PQ.CODE_BITS == 64 * 4 + 32 * 2 + 16 * 2 + 8 * 2 == 368
+    assert bits == 496
+    assert round(128 * 16 / bits, 2) == 4.13
+
+
+def test_quantise_dequantise_roundtrip():
+    p = PQ.PolarParams(128, 0)
+    x = W.gaussian(200, seed=5).astype(np.float64)
+    x[3] = 0.0
+    words, diag = PQ.quantize(p, x)
+    assert words.shape == (200, 16) and np.all(words[:, 11] >> 16 == 0)
+    codes, rb = PQ.unpack(words)
+    for l, (c, b) in enumerate(zip(codes, PQ.LEVEL_BITS)):
+        assert c.min() >= 0 and c.max() < (1 << b)
+    assert np.array_equal(PQ.pack(codes, rb), words)
+    xt = PQ.dequantize(p, words)
+    assert np.all(xt[3] == 0.0)
+    rel = np.linalg.norm(xt - x, axis=1) / np.maximum(np.linalg.norm(x, axis=1), 1e-30)
+    rel = np.delete(rel, 3)
+    # four angle levels of 4 / 2 / 2 / 2 bits: a coarse but bounded error
+    assert rel.max() < 0.8 and 0.05 < rel.mean() < 0.5
+    # more levels of the radius tree decoded exactly -> exact vector
+    ex = PQ.polar_inverse(diag.angles, PQ._half_value(rb)) @ p.pi
+    assert np.abs(ex - x).max() < 1e-2 * np.abs(x).max()
