@@ -66,6 +66,7 @@ extern "C" {
 #define RQ_QJL 1   /* b-1 MSE bits + 1-bit QJL signs of the residual + ||r||;
                       with b = 1 QJL only: no codes, signs of S x_u, gamma  */
 #define RQ_DENSE 2 /* TurboQuant: dense 128x128 rotation Pi instead of rotors */
+#define RQ_POLAR 4 /* PolarQuant (pq_* functions); alone, with bits = 4       */
 
 /* element types of vector inputs / outputs */
 #define RQ_F32 0
@@ -100,8 +101,10 @@ typedef struct {
  * the rotor [s,0,0,0,b12,b13,b23,0] of README "How RotorQuant Works");
  * rotmats [n_groups*9] row-major 3x3 M_g with grade-1((R v) R~) = M_g v;
  * centroids [levels]; boundaries [levels-1] (t_k = (c_k + c_{k+1})/2);
- * pi [d*d] row-major, y = Pi x (dense only); s [d*d] half bits row-major,
- * z = S r (QJL only). */
+ * pi [d*d] row-major, y = Pi x (dense and polar); s [d*d] half bits
+ * row-major, z = S r (QJL only).  RQ_POLAR sessions fill centroids [28] and
+ * boundaries [24]: the codebooks of its four levels (16 + 4 + 4 + 4
+ * centroids, 15 + 3 + 3 + 3 boundaries) one after another. */
 typedef struct {
     float* rotors;
     float* rotmats;
@@ -118,6 +121,9 @@ typedef struct {
  * Kernels" lists its 1-bit quantiser and score kernels): code_words = 0, a
  * 20-byte record, rotor and dense sessions identical (no rotation is used);
  * record code pointers may then be NULL;
+ * RQ_POLAR (alone, bits = 4) is PolarQuant: n_coords 128, levels 16 (its
+ * first level), code_words 16 and record_bytes 64 for the whole record (see
+ * pq_quantize), no norms, signs or residual norms;
  * RQ_EUNSUPPORTED for d != 128. */
 int rq_layout(int d, int bits, int mode, rq_layout_t* out);
 
@@ -304,6 +310,38 @@ int tq_dequantize(rq_ctx* ctx, const uint32_t* codes, const uint16_t* norms,
 int tq_roundtrip(rq_ctx* ctx, const void* x, int x_dtype, int64_t n, int64_t ldx,
                  uint32_t* codes, uint16_t* norms, uint32_t* signs, uint16_t* rnorms,
                  void* y, int y_dtype, int64_t ldy, void* stream);
+
+/* PolarQuant (PolarQuant article, sections on the polar transform, on the
+ * algorithm in practice and on the compression ratio), for RQ_POLAR
+ * sessions:
+ *   y = Pi x (the session's Pi, the same as a dense session of that seed);
+ *   level 1 pairs (y_2i, y_2i+1) -> angle in [0, 2 pi) coded with 4 bits and
+ *   radius; levels 2..4 pair the previous radii the same way, angles in
+ *   [0, pi/2] coded with 2 bits each (128 -> 64 -> 32 -> 16 -> 8 radii);
+ *   codes = #{k : angle > t_k} against each level's Lloyd codebook for the
+ *   article's angle law; the 8 final radii are stored as IEEE halves.
+ * Record: 16 u32 words per vector, 64 bytes (the article's 496 bits plus 16
+ * zero bits): words 0..11 the code bit stream, LSB first (64 level-1 codes
+ * of 4 bits, then 32, 16 and 8 codes of 2 bits; bits 368..383 zero), words
+ * 12..15 the radii, radius 2i in the low half of word 12 + i.
+ * Dequantisation walks the levels back from the radii with the centroid
+ * angles (r -> (r cos c, r sin c)) and returns x~ = Pi^T y~; pq_score
+ * returns <q_h, x~_t> for every query row and key (no 1/sqrt(d)).
+ * Argument rules as for the rq_ functions: x, y [n][ld] fp16 / fp32, words
+ * [n][16] 4-byte aligned device memory, n == 0 a no-op; pq_score: q [hq][128]
+ * fp32 16-byte aligned, hq <= 65535, query row h reads KV head h / group,
+ * whose t records start at row (h / group) * kv_stride (kv_stride >= t
+ * unless hq == group), scores [hq][ld_scores] with t <= ld_scores <= 2^23.
+ * The rotated queries Pi q are built on chip.  RQ_EINVAL on a session
+ * without RQ_POLAR; the rq_, tq_ and cache functions reject RQ_POLAR. */
+int pq_quantize(rq_ctx* ctx, const void* x, int x_dtype, int64_t n, int64_t ldx, uint32_t* words,
+                void* stream);
+int pq_dequantize(rq_ctx* ctx, const uint32_t* words, int64_t n, void* y, int y_dtype, int64_t ldy,
+                  void* stream);
+int pq_roundtrip(rq_ctx* ctx, const void* x, int x_dtype, int64_t n, int64_t ldx, uint32_t* words,
+                 void* y, int y_dtype, int64_t ldy, void* stream);
+int pq_score(rq_ctx* ctx, const float* q, int hq, int group, const uint32_t* words, int64_t t,
+             int64_t kv_stride, float* scores, int64_t ld_scores, void* stream);
 
 /* Message of the calling thread's last failure ("" if none). */
 const char* rq_last_error(void);

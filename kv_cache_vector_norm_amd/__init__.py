@@ -20,7 +20,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "librq.so")
 
 RQ_OK, RQ_EINVAL, RQ_EUNSUPPORTED, RQ_ENOMEM, RQ_EHIP = 0, 1, 2, 3, 4
-RQ_MSE, RQ_QJL, RQ_DENSE = 0, 1, 2
+RQ_MSE, RQ_QJL, RQ_DENSE, RQ_POLAR = 0, 1, 2, 4
 RQ_F32, RQ_F16 = 0, 1
 RQ_SCORE_CHUNK = 4096
 
@@ -30,7 +30,8 @@ EXPORTS = ("rq_layout", "rq_host_params", "rq_host_quantizer", "rq_init", "rq_fr
            "rq_quantize", "rq_dequantize", "rq_roundtrip", "rq_score", "rq_attend_workspace", "rq_attend",
            "tq_quantize", "tq_dequantize", "tq_roundtrip", "rq_cache_create", "rq_cache_free", "rq_cache_open",
            "rq_cache_close", "rq_cache_length", "rq_cache_free_pages", "rq_cache_append", "rq_cache_read",
-           "rq_cache_attend_workspace", "rq_cache_attend", "rq_last_error", "rq_version")
+           "rq_cache_attend_workspace", "rq_cache_attend", "pq_quantize", "pq_dequantize", "pq_roundtrip", "pq_score",
+           "rq_last_error", "rq_version")
 
 
 class RQError(RuntimeError):
@@ -91,6 +92,10 @@ def _load():
         "tq_quantize": ([P, P, I, I64, I64, P, P, P, P, P], I),
         "tq_dequantize": ([P, P, P, P, P, I64, P, I, I64, P], I),
         "tq_roundtrip": ([P, P, I, I64, I64, P, P, P, P, P, I, I64, P], I),
+        "pq_quantize": ([P, P, I, I64, I64, P, P], I),
+        "pq_dequantize": ([P, P, I64, P, I, I64, P], I),
+        "pq_roundtrip": ([P, P, I, I64, I64, P, P, I, I64, P], I),
+        "pq_score": ([P, P, I, I, P, I64, I64, P, I64, P], I),
         "rq_last_error": ([], ctypes.c_char_p),
         "rq_version": ([], ctypes.c_char_p),
     }
@@ -179,6 +184,9 @@ def rq_host_quantizer(d, bits, mode):
 
 def _param_arrays(lay, mode):
     d, g, levels = lay["d"], lay["n_groups"], lay["levels"]
+    if mode & RQ_POLAR:
+        return {"centroids": np.zeros(28, np.float32), "boundaries": np.zeros(24, np.float32),
+                "pi": np.zeros((d, d), np.float32)}
     a = {"centroids": np.zeros(levels, np.float32), "boundaries": np.zeros(levels - 1, np.float32)}
     if not mode & RQ_DENSE:
         a["rotors"] = np.zeros((g, 4), np.float32)
@@ -268,6 +276,24 @@ def rq_attend(kctx, vctx, q, hq, group, kcodes, knorms, ksigns, krnorms, vcodes,
     return _check(_lib.rq_attend(kctx, vctx, _ptr(q), hq, group, _ptr(kcodes), _ptr(knorms), _ptr(ksigns),
                                  _ptr(krnorms), _ptr(vcodes), _ptr(vnorms), _ptr(vsigns), _ptr(vrnorms), t, kv_stride,
                                  float(scale), _ptr(workspace), workspace_bytes, _ptr(out), ld_out, _stream(stream)))
+
+
+def pq_quantize(ctx, x, x_dtype, n, ldx, words, stream=None):
+    return _check(_lib.pq_quantize(ctx, _ptr(x), x_dtype, n, ldx, _ptr(words), _stream(stream)))
+
+
+def pq_dequantize(ctx, words, n, y, y_dtype, ldy, stream=None):
+    return _check(_lib.pq_dequantize(ctx, _ptr(words), n, _ptr(y), y_dtype, ldy, _stream(stream)))
+
+
+def pq_roundtrip(ctx, x, x_dtype, n, ldx, words, y, y_dtype, ldy, stream=None):
+    return _check(_lib.pq_roundtrip(ctx, _ptr(x), x_dtype, n, ldx, _ptr(words), _ptr(y), y_dtype, ldy,
+                                    _stream(stream)))
+
+
+def pq_score(ctx, q, hq, group, words, t, kv_stride, scores, ld_scores, stream=None):
+    return _check(_lib.pq_score(ctx, _ptr(q), hq, group, _ptr(words), t, kv_stride, _ptr(scores), ld_scores,
+                                _stream(stream)))
 
 
 # ----------------------------------------------------------- convenience --
@@ -367,6 +393,71 @@ class Codec:
             out = th.empty((hq, t), dtype=th.float32, device=q.device)
         rq_score(self.ctx, q, hq, group, rec.codes, rec.norms, rec.signs, rec.rnorms, t, kv_stride, out,
                  out.stride(0), stream)
+        return out
+
+
+class PolarCodec:
+    """A PolarQuant session (RQ_POLAR, bits = 4) plus torch-allocated
+    outputs.  Records are [n, 16] int32 tensors (16 u32 words per vector)."""
+
+    def __init__(self, seed=0, d=128):
+        import torch
+        self.torch = torch
+        self.ctx = rq_init(d, 4, seed, RQ_POLAR)
+        self.layout = rq_get_layout(self.ctx)
+
+    def close(self):
+        if self.ctx:
+            rq_free(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def params(self):
+        return rq_get_params(self.ctx)
+
+    def alloc_words(self, n, device="cuda"):
+        return self.torch.zeros((n, self.layout["code_words"]), dtype=self.torch.int32, device=device)
+
+    def _dt(self, tensor):
+        t = self.torch
+        if tensor.dtype == t.float16:
+            return RQ_F16
+        if tensor.dtype == t.float32:
+            return RQ_F32
+        raise TypeError("vectors must be float16 or float32")
+
+    def quantize(self, x, words=None, stream=None):
+        n = x.shape[0]
+        words = self.alloc_words(n, x.device) if words is None else words
+        pq_quantize(self.ctx, x, self._dt(x), n, x.stride(0), words, stream)
+        return words
+
+    def dequantize(self, words, dtype=None, out=None, stream=None):
+        n = words.shape[0]
+        if out is None:
+            out = self.torch.empty((n, self.layout["d"]), dtype=dtype or self.torch.float32, device=words.device)
+        pq_dequantize(self.ctx, words, n, out, self._dt(out), out.stride(0), stream)
+        return out
+
+    def roundtrip(self, x, dtype=None, words=None, out=None, stream=None):
+        n = x.shape[0]
+        words = self.alloc_words(n, x.device) if words is None else words
+        if out is None:
+            out = self.torch.empty((n, self.layout["d"]), dtype=dtype or x.dtype, device=x.device)
+        pq_roundtrip(self.ctx, x, self._dt(x), n, x.stride(0), words, out, self._dt(out), out.stride(0), stream)
+        return words, out
+
+    def score(self, q, words, group, t, kv_stride=None, out=None, stream=None):
+        hq = q.shape[0]
+        kv_stride = t if kv_stride is None else kv_stride
+        if out is None:
+            out = self.torch.empty((hq, t), dtype=self.torch.float32, device=q.device)
+        pq_score(self.ctx, q, hq, group, words, t, kv_stride, out, out.stride(0), stream)
         return out
 
 

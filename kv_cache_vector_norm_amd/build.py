@@ -38,7 +38,8 @@ HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-ffp-contract=off", "-fno-fast-math
 def _units():
     units = [("rq_host.o", [CXX] + HOST_FLAGS + ["-c", os.path.join(CSRC, "rq_host.cpp")])]
     units.append(("rq_api.o", [HIPCC] + HIP_FLAGS + ["-x", "hip", "-c", os.path.join(CSRC, "rq_api.cpp")]))
-    for f in ("rq_rotor_dispatch.hip", "rq_dense.hip", "rq_score.hip", "rq_attend.hip", "rq_qjl1.hip", "rq_cache.hip"):
+    for f in ("rq_rotor_dispatch.hip", "rq_dense.hip", "rq_score.hip", "rq_attend.hip", "rq_qjl1.hip", "rq_cache.hip",
+              "rq_polar.hip"):
         units.append((f.replace(".hip", ".o"), [HIPCC] + HIP_FLAGS + ["-c", os.path.join(CSRC, f)]))
     for kind in ("rotor", "dense"):
         for qjl in (0, 1):

@@ -82,6 +82,9 @@ struct rq_ctx {
     uint16_t* pi_lo = nullptr;
     uint16_t* pit_hi = nullptr;
     uint16_t* pit_lo = nullptr;
+    // PolarQuant: fp32 Pi and the (cos, sin) table of its angle codebooks
+    float* pi32 = nullptr;
+    float* pq_tab = nullptr;
 };
 
 extern "C" {
@@ -141,6 +144,7 @@ int rq_host_quantizer(int d, int bits, int mode, float* bias, uint32_t* table) {
     std::string err;
     const int rc = rqh::make_tables(d, bits, 0, mode, &t, &err);
     if (rc) return fail(rc == 2 ? RQ_EUNSUPPORTED : RQ_EINVAL, "rq_host_quantizer: " + err);
+    if (mode & RQ_POLAR) return fail(RQ_EINVAL, "rq_host_quantizer: RQ_POLAR sessions have no slot table");
     *bias = t.bin_b;
     std::memcpy(table, t.bins.data(), t.bins.size() * sizeof(rqh::BinEntry));
     return RQ_OK;
@@ -199,6 +203,9 @@ int rq_init(int d, int bits, uint64_t seed, int mode, rq_ctx** out) {
     };
     // derived half tables
     std::vector<uint16_t> s_cols, s_fwd, s_back, pi_hi, pi_lo, pit_hi, pit_lo, phi_hi, phi_lo;
+    std::vector<float> pq_tab;
+    const bool polar = mode & RQ_POLAR;
+    const bool rotor = !(mode & (RQ_DENSE | RQ_POLAR));
     // exact-enough half pair of 16 v: hi = half(16 v), lo = half((16 v - hi) * 2^11)
     auto split16 = [](double v, uint16_t* hi, uint16_t* lo) {
         const double x = v * 16.0;
@@ -209,7 +216,7 @@ int rq_init(int d, int bits, uint64_t seed, int mode, rq_ctx** out) {
         *hi = h;
         *lo = rqh::double_to_half_rne((x - hv) * 2048.0);
     };
-    if (!(mode & RQ_DENSE)) {
+    if (rotor) {
         // Phi[i][j]: slot i = 3 g + r reads coordinates 3 g .. 3 g + 2 through row r of M_g
         phi_hi.assign(static_cast<size_t>(n) * n, 0);
         phi_lo.assign(static_cast<size_t>(n) * n, 0);
@@ -239,7 +246,28 @@ int rq_init(int d, int bits, uint64_t seed, int mode, rq_ctx** out) {
                 s_back[p * n + k] = t.s[perm_k(k) * n + perm_row(p)];
             }
     }
-    if (mode & RQ_DENSE) {
+    if (polar) {
+        // (cos, sin) of the decision boundaries the kernels test (level 1:
+        // t_1..t_7 only, the lower half-plane is tested after a turn by pi;
+        // later levels: all three), then of every centroid, levels in order.
+        std::vector<double> bnd, cen;
+        for (int k = 0; k < 7; ++k) bnd.push_back(t.boundaries[k]);
+        for (int k = 15; k < rqh::kPolarBoundaries; ++k) bnd.push_back(t.boundaries[k]);
+        for (float c : t.centroids) cen.push_back(c);
+        for (double a : bnd) {
+            pq_tab.push_back(static_cast<float>(std::cos(a)));
+            pq_tab.push_back(static_cast<float>(std::sin(a)));
+        }
+        for (double a : cen) {
+            pq_tab.push_back(static_cast<float>(std::cos(a)));
+            pq_tab.push_back(static_cast<float>(std::sin(a)));
+        }
+        if (pq_tab.size() != static_cast<size_t>(rqk::kPolarTab)) {
+            delete ctx;
+            return fail(RQ_EINVAL, "rq_init: PolarQuant table size");
+        }
+    }
+    if (mode & (RQ_DENSE | RQ_POLAR)) {
         // Pi = hi + lo exactly enough: hi = half(Pi * 2^4), lo = half((Pi * 2^4 - hi) * 2^11);
         // the kernels undo the 2^4 and 2^11 scales in fp32.
         pi_hi.resize(t.pi.size());
@@ -257,7 +285,7 @@ int rq_init(int d, int bits, uint64_t seed, int mode, rq_ctx** out) {
             }
     }
     do {
-        if (!(mode & RQ_DENSE)) {
+        if (rotor) {
             if ((e = upload(reinterpret_cast<void**>(&ctx->rotmat), t.rotmats.data(), t.rotmats.size() * 4)) != hipSuccess) break;
             if ((e = upload(reinterpret_cast<void**>(&ctx->phi_hi), phi_hi.data(), phi_hi.size() * 2)) != hipSuccess) break;
             if ((e = upload(reinterpret_cast<void**>(&ctx->phi_lo), phi_lo.data(), phi_lo.size() * 2)) != hipSuccess) break;
@@ -272,7 +300,11 @@ int rq_init(int d, int bits, uint64_t seed, int mode, rq_ctx** out) {
             if ((e = upload(reinterpret_cast<void**>(&ctx->s_fwd), s_fwd.data(), s_fwd.size() * 2)) != hipSuccess) break;
             if ((e = upload(reinterpret_cast<void**>(&ctx->s_back), s_back.data(), s_back.size() * 2)) != hipSuccess) break;
         }
-        if (mode & RQ_DENSE) {
+        if (polar) {
+            if ((e = upload(reinterpret_cast<void**>(&ctx->pi32), t.pi.data(), t.pi.size() * 4)) != hipSuccess) break;
+            if ((e = upload(reinterpret_cast<void**>(&ctx->pq_tab), pq_tab.data(), pq_tab.size() * 4)) != hipSuccess) break;
+        }
+        if (mode & (RQ_DENSE | RQ_POLAR)) {
             if ((e = upload(reinterpret_cast<void**>(&ctx->pi_hi), pi_hi.data(), pi_hi.size() * 2)) != hipSuccess) break;
             if ((e = upload(reinterpret_cast<void**>(&ctx->pi_lo), pi_lo.data(), pi_lo.size() * 2)) != hipSuccess) break;
             if ((e = upload(reinterpret_cast<void**>(&ctx->pit_hi), pit_hi.data(), pit_hi.size() * 2)) != hipSuccess) break;
@@ -294,6 +326,8 @@ int rq_init(int d, int bits, uint64_t seed, int mode, rq_ctx** out) {
 // ------------------------------------------------------------ checks --
 static int check_ctx(const rq_ctx* ctx, bool dense, const char* fn) {
     if (!ctx) return fail(RQ_EINVAL, std::string(fn) + ": ctx is NULL");
+    if (ctx->host.lay.mode & RQ_POLAR)
+        return fail(RQ_EINVAL, std::string(fn) + ": a PolarQuant session (use pq_*)");
     const bool is_dense = ctx->host.lay.mode & RQ_DENSE;
     if (dense != is_dense)
         return fail(RQ_EINVAL, std::string(fn) + (dense ? ": needs an RQ_DENSE session" : ": needs a rotor session (use tq_*)"));
@@ -824,6 +858,92 @@ int rq_cache_attend(rq_cache* c, int seq, int layer, const float* q, int hq, flo
                                reinterpret_cast<const float2*>(static_cast<char*>(workspace) + plan.off_stats), scale,
                                out, ld_out, s);
     return finish(e, fn);
+}
+
+// ---------------------------------------------------------- PolarQuant --
+static int check_polar(const rq_ctx* ctx, const char* fn) {
+    if (!ctx) return fail(RQ_EINVAL, std::string(fn) + ": ctx is NULL");
+    if (!(ctx->host.lay.mode & RQ_POLAR)) return fail(RQ_EINVAL, std::string(fn) + ": needs an RQ_POLAR session");
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess || cur != ctx->device)
+        return fail(RQ_EINVAL, std::string(fn) + ": current HIP device is not the session's device");
+    return RQ_OK;
+}
+
+static rqk::PolarDev polar_tables(const rq_ctx* c) {
+    rqk::PolarDev p;
+    p.pi_hi = c->pi_hi;
+    p.pi_lo = c->pi_lo;
+    p.pit_hi = c->pit_hi;
+    p.pit_lo = c->pit_lo;
+    p.pi32 = c->pi32;
+    p.tab = c->pq_tab;
+    return p;
+}
+
+static int pq_quantize_impl(rq_ctx* ctx, const void* x, int x_dtype, int64_t n, int64_t ldx, uint32_t* words,
+                            void* y, int y_dtype, int64_t ldy, bool roundtrip, void* stream, const char* fn) {
+    int rc;
+    if ((rc = check_polar(ctx, fn))) return rc;
+    if (n < 0) return fail(RQ_EINVAL, std::string(fn) + ": n < 0");
+    if ((rc = check_vectors(x, x_dtype, ldx, "x", fn))) return rc;
+    if (!words || !aligned(words, 4)) return fail(RQ_EINVAL, std::string(fn) + ": words must be a 4-byte aligned device pointer");
+    if (roundtrip) {
+        if ((rc = check_vectors(y, y_dtype, ldy, "y", fn))) return rc;
+        const char* xb = static_cast<const char*>(x);
+        const char* yb = static_cast<const char*>(y);
+        const int64_t xs = (n > 0 ? (n - 1) * ldx + rqh::kDim : 0) * static_cast<int64_t>(elem_size(x_dtype));
+        const int64_t ys = (n > 0 ? (n - 1) * ldy + rqh::kDim : 0) * static_cast<int64_t>(elem_size(y_dtype));
+        if (n > 0 && xb < yb + ys && yb < xb + xs) return fail(RQ_EINVAL, std::string(fn) + ": x and y overlap");
+    }
+    if (n == 0) return RQ_OK;
+    const int64_t ldx_b = ldx * static_cast<int64_t>(elem_size(x_dtype));
+    const int64_t ldy_b = roundtrip ? ldy * static_cast<int64_t>(elem_size(y_dtype)) : 0;
+    return finish(rqk::polar_quantize(polar_tables(ctx), x, x_dtype == RQ_F16, ldx_b, n, words, y, y_dtype == RQ_F16,
+                                      ldy_b, roundtrip, static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
+int pq_quantize(rq_ctx* ctx, const void* x, int x_dtype, int64_t n, int64_t ldx, uint32_t* words, void* stream) {
+    return pq_quantize_impl(ctx, x, x_dtype, n, ldx, words, nullptr, RQ_F16, 0, false, stream, "pq_quantize");
+}
+
+int pq_roundtrip(rq_ctx* ctx, const void* x, int x_dtype, int64_t n, int64_t ldx, uint32_t* words, void* y,
+                 int y_dtype, int64_t ldy, void* stream) {
+    return pq_quantize_impl(ctx, x, x_dtype, n, ldx, words, y, y_dtype, ldy, true, stream, "pq_roundtrip");
+}
+
+int pq_dequantize(rq_ctx* ctx, const uint32_t* words, int64_t n, void* y, int y_dtype, int64_t ldy, void* stream) {
+    const char* fn = "pq_dequantize";
+    int rc;
+    if ((rc = check_polar(ctx, fn))) return rc;
+    if (n < 0) return fail(RQ_EINVAL, "pq_dequantize: n < 0");
+    if (!words || !aligned(words, 4)) return fail(RQ_EINVAL, "pq_dequantize: words must be a 4-byte aligned device pointer");
+    if ((rc = check_vectors(y, y_dtype, ldy, "y", fn))) return rc;
+    if (n == 0) return RQ_OK;
+    return finish(rqk::polar_dequantize(polar_tables(ctx), words, n, y, y_dtype == RQ_F16,
+                                        ldy * static_cast<int64_t>(elem_size(y_dtype)), static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
+int pq_score(rq_ctx* ctx, const float* q, int hq, int group, const uint32_t* words, int64_t t, int64_t kv_stride,
+             float* scores, int64_t ld_scores, void* stream) {
+    const char* fn = "pq_score";
+    int rc;
+    if ((rc = check_polar(ctx, fn))) return rc;
+    if (!q || !aligned(q, 16)) return fail(RQ_EINVAL, "pq_score: q must be a 16-byte aligned device pointer");
+    if (hq < 1 || group < 1 || hq % group) return fail(RQ_EINVAL, "pq_score: need hq >= 1, group >= 1, hq % group == 0");
+    if (hq > RQ_ATTEND_MAX_ROWS) return fail(RQ_EINVAL, "pq_score: hq > 65535");
+    if (t < 0) return fail(RQ_EINVAL, "pq_score: t < 0");
+    if (!words || !aligned(words, 4)) return fail(RQ_EINVAL, "pq_score: words must be a 4-byte aligned device pointer");
+    if (hq / group > 1 && kv_stride < t) return fail(RQ_EINVAL, "pq_score: kv_stride < t");
+    if (!scores || !aligned(scores, 4)) return fail(RQ_EINVAL, "pq_score: scores must be a 4-byte aligned device pointer");
+    if (ld_scores < t) return fail(RQ_EINVAL, "pq_score: ld_scores < t");
+    if (ld_scores > (int64_t(1) << 23)) return fail(RQ_EINVAL, "pq_score: ld_scores > 2^23");
+    if (t == 0) return RQ_OK;
+    return finish(rqk::polar_score(polar_tables(ctx), q, hq, group, words, t, hq / group > 1 ? kv_stride : 0, scores,
+                                   ld_scores, static_cast<hipStream_t>(stream)),
+                  fn);
 }
 
 }  // extern "C"

@@ -29,9 +29,40 @@ float to_f32(double x) { return static_cast<float>(x); }
 
 // ----------------------------------------------------------------- layout --
 int make_layout(int d, int bits, int mode, Layout* out, std::string* err) {
-    if (mode & ~(kModeQjl | kModeDense)) {
+    if (mode & ~(kModeQjl | kModeDense | kModePolar)) {
         if (err) *err = "unknown mode bits";
         return 1;
+    }
+    if (mode & kModePolar) {
+        if (mode != kModePolar) {
+            if (err) *err = "RQ_POLAR takes no other mode bits";
+            return 1;
+        }
+        if (bits != kPolarBits[0]) {
+            if (err) *err = "RQ_POLAR sessions have bits = 4 (4-bit first level, 2-bit later levels)";
+            return 1;
+        }
+        if (d <= 0) {
+            if (err) *err = "d must be positive";
+            return 1;
+        }
+        if (d != kDim) {
+            if (err) *err = "only d = 128 is implemented";
+            return 2;
+        }
+        Layout l;
+        l.d = d;
+        l.bits = bits;
+        l.mse_bits = bits;
+        l.mode = mode;
+        l.n_coords = d;
+        l.n_groups = 0;
+        l.levels = 1 << bits;
+        l.code_words = kPolarWords;
+        l.sign_words = 0;
+        l.record_bytes = 4 * kPolarWords;
+        *out = l;
+        return 0;
     }
     const bool qjl = mode & kModeQjl;
     const int mse_bits = qjl ? bits - 1 : bits;
@@ -259,6 +290,90 @@ void lloyd_max_unit_sphere(int d, int bits, std::vector<double>* centroids, std:
     cache[{d, bits}] = {c, t};
 }
 
+// ------------------------------------------------------- PolarQuant angles --
+// Cell masses and first moments of the angle density by composite
+// Gauss-Legendre (panels of at most 0.005 rad, 24 nodes: the integrands are
+// smooth, so every integral is exact to rounding).
+namespace {
+
+struct AngleLaw {
+    int level;
+    double lo, hi, logc;
+    int power;   // k - 1
+    GaussLegendre gl{24};
+    explicit AngleLaw(int l) : level(l) {
+        lo = 0.0;
+        hi = l == 0 ? kTwoPi : 0.5 * kPi;
+        const double k = std::ldexp(1.0, l);
+        power = static_cast<int>(k) - 1;
+        logc = l == 0 ? -std::log(kTwoPi)
+                      : std::lgamma(k) - (k - 2.0) * std::log(2.0) - 2.0 * std::lgamma(0.5 * k);
+    }
+    double density(double th) const {
+        if (level == 0) return std::exp(logc);
+        const double s = std::sin(2.0 * th);
+        return std::exp(logc) * std::pow(s, power);
+    }
+    double moment(double a, double b, int p) const {
+        if (b <= a) return 0.0;
+        const int panels = std::max(1, static_cast<int>(std::ceil((b - a) / 0.005)));
+        const double h = (b - a) / panels;
+        double sum = 0.0;
+        for (int q = 0; q < panels; ++q) {
+            const double mid = a + (q + 0.5) * h;
+            double ps = 0.0;
+            for (size_t i = 0; i < gl.x.size(); ++i) {
+                const double th = mid + 0.5 * h * gl.x[i];
+                ps += gl.w[i] * (p ? th : 1.0) * density(th);
+            }
+            sum += 0.5 * h * ps;
+        }
+        return sum;
+    }
+};
+
+}  // namespace
+
+// Lloyd's algorithm from a uniform start: boundaries at the midpoints of the
+// centroids, each centroid moved to the conditional mean of its cell, until
+// no centroid moves by 1e-14 (the iterate of that last step is kept).
+void lloyd_polar(int level, std::vector<double>* centroids, std::vector<double>* boundaries) {
+    static std::mutex mu;
+    static std::map<int, std::pair<std::vector<double>, std::vector<double>>> cache;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        auto it = cache.find(level);
+        if (it != cache.end()) {
+            *centroids = it->second.first;
+            *boundaries = it->second.second;
+            return;
+        }
+    }
+    const AngleLaw law(level);
+    const int levels = 1 << kPolarBits[level];
+    std::vector<double> c(levels), t(levels + 1), nc(levels);
+    for (int i = 0; i < levels; ++i) c[i] = law.lo + (i + 0.5) * (law.hi - law.lo) / levels;
+    for (int iter = 0; iter < 10000; ++iter) {
+        t[0] = law.lo;
+        t[levels] = law.hi;
+        for (int i = 1; i < levels; ++i) t[i] = 0.5 * (c[i - 1] + c[i]);
+        double delta = 0.0;
+        for (int i = 0; i < levels; ++i) {
+            const double mass = law.moment(t[i], t[i + 1], 0);
+            nc[i] = mass > 0.0 ? law.moment(t[i], t[i + 1], 1) / mass : 0.5 * (t[i] + t[i + 1]);
+            delta = std::max(delta, std::fabs(nc[i] - c[i]));
+        }
+        c.swap(nc);
+        if (delta < 1e-14) break;
+    }
+    std::vector<double> b(levels - 1);
+    for (int i = 0; i + 1 < levels; ++i) b[i] = 0.5 * (c[i] + c[i + 1]);
+    *centroids = c;
+    *boundaries = b;
+    std::lock_guard<std::mutex> lock(mu);
+    cache[level] = {c, b};
+}
+
 // ------------------------------------------------------------ Householder --
 // G (n x n, row-major) = Q R with Householder reflections; then column j of
 // Q is negated where R_jj < 0, so that diag(R) > 0 and Q is unique.
@@ -389,6 +504,22 @@ int make_tables(int d, int bits, uint64_t seed, int mode, Tables* out, std::stri
     if (rc) return rc;
     Tables t;
     t.lay = lay;
+    if (mode & kModePolar) {
+        // the four codebooks concatenated, then Pi as in the dense sessions
+        for (int level = 0; level < kPolarLevels; ++level) {
+            std::vector<double> c, b;
+            lloyd_polar(level, &c, &b);
+            for (double v : c) t.centroids.push_back(to_f32(v));
+            for (double v : b) t.boundaries.push_back(to_f32(v));
+        }
+        const std::vector<double> g = normals(seed, kTagPi, static_cast<size_t>(d) * d);
+        std::vector<double> q;
+        householder_q(g, d, &q);
+        t.pi.resize(q.size());
+        for (size_t i = 0; i < q.size(); ++i) t.pi[i] = to_f32(q[i]);
+        *out = std::move(t);
+        return 0;
+    }
     std::vector<double> c, b;
     if (lay.mse_bits == 0) {
         c.assign(1, 0.0);   // QJL only: one level of value 0, no boundaries

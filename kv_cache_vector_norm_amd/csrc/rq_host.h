@@ -12,7 +12,17 @@ constexpr int kDim = 128;          // the only d the device kernels support
 constexpr int kQjlRows = 128;      // m, rows of S
 constexpr int kMaxMseBits = 4;
 
-enum : int { kModeQjl = 1, kModeDense = 2 };
+enum : int { kModeQjl = 1, kModeDense = 2, kModePolar = 4 };
+
+// PolarQuant (recursive polar transform of y = Pi x): four levels of angle
+// codes, 4 bits on [0, 2 pi) for the 64 first-level pairs, 2 bits on
+// [0, pi/2] for the 32 / 16 / 8 pairs of later levels, and 8 final radii as
+// halves; a record of 16 u32 words (codes in words 0..11, radii in 12..15).
+constexpr int kPolarLevels = 4;
+constexpr int kPolarBits[kPolarLevels] = {4, 2, 2, 2};
+constexpr int kPolarWords = 16;
+constexpr int kPolarCentroids = 16 + 4 + 4 + 4;   // codebooks of the four levels, concatenated
+constexpr int kPolarBoundaries = 15 + 3 + 3 + 3;
 
 struct Layout {
     int d = 0, bits = 0, mse_bits = 0, mode = 0;
@@ -53,6 +63,11 @@ struct Tables {
     std::vector<float> pi;          // [d][d] row-major (dense)
     std::vector<uint16_t> s;        // [m][d] half bits, row-major (QJL)
 };
+
+// Lloyd's algorithm for the angle law of PolarQuant level `level` (0-based):
+// level 0 uniform on [0, 2 pi), level l >= 1 the density
+// Gamma(k) / (2^(k-2) Gamma(k/2)^2) sin^(k-1)(2 theta) on [0, pi/2], k = 2^l.
+void lloyd_polar(int level, std::vector<double>* centroids, std::vector<double>* boundaries);
 
 // Builds every table of (d, bits, seed, mode); returns 0/1/2 as make_layout.
 int make_tables(int d, int bits, uint64_t seed, int mode, Tables* out, std::string* err);

@@ -118,3 +118,84 @@ def compare_scores(got, ref, qnorm, nhat, what="scores"):
     bad = err > lim
     assert not bad.any(), f"{what}: {bad.sum()} over tolerance, worst {np.max(err / lim):.3g}x"
     return float(np.max(err / lim)) if err.size else 0.0
+
+
+# ---------------------------------------------------------------- PolarQuant --
+# Angle codes: a code that differs from the oracle's must have the oracle's
+# pair point (a, b) of that level (unit-vector domain, y = Pi x / ||x||)
+# within BAND of its nearest decision ray (perpendicular distance
+# r |sin(theta - t)|; level 1 also has the ray at angle 0); the fraction of
+# points inside the band obeys the same bound as the codec's coordinates.
+# The kernel's point carries the rotation's error (a few 1e-7 in this domain)
+# plus the fp32 rounding of its boundary constants, below BAND.
+# Radii: half bits equal unless the float64 radius lies within
+# POLAR_RADIUS_BAND (relative) of a half rounding midpoint; the kernel's
+# radius carries the rotation's error through up to 16 coordinates and the
+# fp32 norm (about 1e-6 relative at worst), hence twice the codec's 1e-6.
+POLAR_RADIUS_BAND = 2e-6
+
+
+def polar_level_points(p, x):
+    """Per level, (a, b) of every pair in the unit-vector domain, float64."""
+    from oracle import polar as PQ
+    x = np.asarray(x, dtype=np.float64)
+    nrm = np.linalg.norm(x, axis=1)
+    y = (x @ p.pi.T) / np.where(nrm > 0, nrm, 1.0)[:, None]
+    pts, r = [], y
+    for _ in range(PQ.N_LEVELS):
+        a, b = r[:, 0::2], r[:, 1::2]
+        pts.append((a, b))
+        r = np.sqrt(a * a + b * b)
+    return pts
+
+
+def polar_ray_distance(p, level, a, b):
+    """Perpendicular distance of (a, b) to the nearest decision ray of the level."""
+    t = np.asarray(p.books[level][1], dtype=np.float64)
+    if level == 0:
+        t = np.concatenate([[0.0], t])
+    th = np.arctan2(b, a)
+    r = np.sqrt(a * a + b * b)
+    d = np.abs(np.mod(th[..., None] - t + np.pi, 2.0 * np.pi) - np.pi).min(axis=-1)
+    return r * np.sin(np.minimum(d, np.pi / 2.0))
+
+
+def check_polar_words(p, x, gpu_words):
+    """GPU PolarQuant records against the oracle's quantisation of x.
+    Returns a report."""
+    from oracle import polar as PQ
+    x = np.asarray(x, dtype=np.float64)
+    owords, diag = PQ.quantize(p, x)
+    gc, grb = PQ.unpack(gpu_words)
+    oc, orb = PQ.unpack(owords)
+    pts = polar_level_points(p, x)
+    zero = np.linalg.norm(x, axis=1) == 0      # every angle 0 on both sides: exact, not banded
+    n_band = n_mism = n_all = 0
+    for level in range(PQ.N_LEVELS):
+        assert np.all(gc[level][zero] == 0) and np.all(oc[level][zero] == 0)
+        dist = polar_ray_distance(p, level, *pts[level])[~zero]
+        in_band = dist < BAND
+        mism = (gc[level] != oc[level])[~zero]
+        outside = mism & ~in_band
+        assert not outside.any(), (
+            f"level {level + 1}: {outside.sum()} angle codes differ outside the band; first at "
+            f"{np.argwhere(outside)[0]} gpu {gc[level][outside][:5]} oracle {oc[level][outside][:5]} "
+            f"distance {dist[outside][:5]}")
+        n_band += int(in_band.sum())
+        n_mism += int(mism.sum())
+        n_all += in_band.size
+    expected = BAND_FRACTION * n_all
+    allowed = expected + (3.0 * np.sqrt(expected) if n_all < 1_000_000 else 0.0)
+    assert n_band <= max(allowed, BAND_FLOOR), f"{n_band} of {n_all} angles within {BAND} of a decision ray"
+    rel = half_midpoint_distance(diag.radii)
+    bad = (grb != orb) & (rel > POLAR_RADIUS_BAND)
+    assert not bad.any(), f"{bad.sum()} radius halves differ away from a rounding midpoint"
+    return {"band_count": n_band, "code_mismatches": n_mism, "radius_mismatches": int((grb != orb).sum()),
+            "angles": n_all}
+
+
+def polar_radius_norm(words):
+    from oracle import polar as PQ
+    _, rb = PQ.unpack(words)
+    r = rb.view(np.float16).astype(np.float64)
+    return np.linalg.norm(r, axis=1)

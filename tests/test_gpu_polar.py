@@ -1,0 +1,141 @@
+"""GPU parity of PolarQuant sessions (RQ_POLAR) against the oracle, through
+the C ABI: quantise (angle codes of four levels and the eight half radii),
+dequantise, the fused roundtrip and GQA scoring.  Rules in tests/parity.py:
+angle codes equal except for points within 1e-6 of a decision ray, radius
+halves equal except near rounding midpoints, reconstructions within
+1e-5 * ||r^|| and scores within 1e-4 * ||q|| * ||r^|| (r^ the stored radii,
+whose norm is the norm of the dequantised vector)."""
+import numpy as np
+import pytest
+
+import parity as PR
+from oracle import polar as PQ
+from kv_cache_vector_norm_amd import workloads as W
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+D = 128
+
+
+@pytest.fixture(scope="module")
+def K():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import kv_cache_vector_norm_amd as K
+    return K
+
+
+@pytest.fixture(scope="module")
+def P():
+    return PQ.PolarParams(D, 0)
+
+
+def _words(t):
+    return t.cpu().numpy().view(np.uint32)
+
+
+@pytest.mark.parametrize("n", [1, 65, 1000, 4097])
+@pytest.mark.parametrize("in_dtype", [np.float16, np.float32])
+def test_polar_quantize_dequantize_roundtrip(K, P, n, in_dtype):
+    x = W.gaussian(n, seed=110 + n, dtype=in_dtype)
+    x[n // 2] = 0
+    if n > 3:
+        x[1] *= 40.0                       # norms other than ~sqrt(128)
+        x[2] *= 1e-3
+    c = K.PolarCodec(seed=0)
+    assert c.layout["record_bytes"] == 64
+    xt = torch.from_numpy(x).cuda()
+    words = c.quantize(xt)
+    w2, y32 = c.roundtrip(xt, dtype=torch.float32)
+    y16 = c.roundtrip(xt, dtype=torch.float16)[1]
+    d32 = c.dequantize(words, dtype=torch.float32)
+    d16 = c.dequantize(words, dtype=torch.float16)
+    torch.cuda.synchronize()
+    gw = _words(words)
+    rep = PR.check_polar_words(P, x, gw)
+    assert np.array_equal(gw, _words(w2))
+    assert np.all(gw[:, 11] >> 16 == 0)
+    assert torch.equal(y32, d32)
+    assert torch.equal(y16, d32.to(torch.float16)) and torch.equal(d16, y16)
+    assert np.all(gw[n // 2] == 0) and torch.all(d32[n // 2] == 0)
+    rn = PR.polar_radius_norm(gw)
+    PR.compare_recon(d32.cpu().numpy(), PQ.dequantize(P, gw), rn, "polar dequantize")
+    assert rep["angles"] == 120 * (n - 1)
+
+
+def test_polar_keys_65536(K, P):
+    """The 65,536 fp16 N(0,1) keys with their norms, fused roundtrip: 64 B
+    per key (4.13x over fp16 by the article's 496-bit count)."""
+    x = W.keys_c1()
+    c = K.PolarCodec(seed=0)
+    words, y = c.roundtrip(torch.from_numpy(x).cuda(), dtype=torch.float32)
+    torch.cuda.synchronize()
+    gw = _words(words)
+    rep = PR.check_polar_words(P, x, gw)
+    rn = PR.polar_radius_norm(gw)
+    rows = W.sample_rows(x.shape[0], 0.05, seed=111)
+    PR.compare_recon(y.cpu().numpy()[rows], PQ.dequantize(P, gw[rows]), rn[rows], "polar roundtrip")
+    # the dequantised norm is the norm of the stored radii
+    yn = np.linalg.norm(y.cpu().numpy().astype(np.float64), axis=1)
+    assert np.abs(yn - rn).max() <= 1e-5 * rn.max()
+    assert rep["band_count"] <= 1e-4 * rep["angles"] + 3 * np.sqrt(1e-4 * rep["angles"])
+
+
+@pytest.mark.parametrize("t,hq,group", [(1, 1, 1), (300, 8, 4), (2049, 32, 8), (640, 40, 40), (777, 66, 33),
+                                        (4096, 32, 4)])
+def test_polar_score(K, P, t, hq, group):
+    kvh = hq // group
+    keys = W.gaussian(kvh * t, seed=112, dtype=np.float16)
+    q = W.queries(hq, seed=113)
+    c = K.PolarCodec(seed=0)
+    words = c.quantize(torch.from_numpy(keys).cuda())
+    s = c.score(torch.from_numpy(q).cuda(), words, group, t)
+    torch.cuda.synchronize()
+    gw = _words(words)
+    got = s.cpu().numpy()
+    qn = np.linalg.norm(q.astype(np.float64), axis=1)[:, None]
+    for j in range(kvh):
+        rows = slice(j * group, (j + 1) * group)
+        kw = gw[j * t:(j + 1) * t]
+        ref = PQ.score(P, q[rows].astype(np.float64), kw)
+        PR.compare_scores(got[rows], ref, qn[rows], PR.polar_radius_norm(kw)[None, :], "polar scores")
+
+
+def test_polar_score_strided_heads(K, P):
+    """Head j's keys start at record row j * kv_stride; rows beyond t are not read."""
+    t, stride, kvh, group = 200, 256, 3, 4
+    keys = W.gaussian(kvh * stride, seed=114, dtype=np.float16)
+    q = W.queries(kvh * group, seed=115)
+    c = K.PolarCodec(seed=0)
+    words = c.quantize(torch.from_numpy(keys).cuda())
+    out = torch.full((kvh * group, 260), 7.0, device="cuda")
+    c.score(torch.from_numpy(q).cuda(), words, group, t, kv_stride=stride, out=out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.all(got[:, t:] == 7.0)
+    gw = _words(words)
+    qn = np.linalg.norm(q.astype(np.float64), axis=1)[:, None]
+    for j in range(kvh):
+        rows = slice(j * group, (j + 1) * group)
+        kw = gw[j * stride:j * stride + t]
+        ref = PQ.score(P, q[rows].astype(np.float64), kw)
+        PR.compare_scores(got[rows, :t], ref, qn[rows], PR.polar_radius_norm(kw)[None, :], "strided polar scores")
+
+
+def test_polar_sessions_are_separate(K):
+    c = K.PolarCodec(seed=0)
+    r = K.Codec(bits=3, seed=0, mode=K.RQ_QJL)
+    x = torch.from_numpy(W.gaussian(64, seed=116, dtype=np.float16)).cuda()
+    rec = r.alloc_record(64)
+    with pytest.raises(K.RQError):
+        K.rq_quantize(c.ctx, x, K.RQ_F16, 64, 128, rec.codes, rec.norms, rec.signs, rec.rnorms)
+    with pytest.raises(K.RQError):
+        K.pq_quantize(r.ctx, x, K.RQ_F16, 64, 128, c.alloc_words(64))
+    with pytest.raises(K.RQError):
+        K.Cache(c, r, layers=1, kv_heads=1)
+    # seeds give different Pi, hence different records
+    w0 = c.quantize(x)
+    w1 = K.PolarCodec(seed=1).quantize(x)
+    torch.cuda.synchronize()
+    assert not torch.equal(w0, w1)

@@ -22,7 +22,7 @@ def K():
 def declared_functions():
     src = open(os.path.join(ROOT, "include", "rq.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b((?:rq|tq)_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b((?:rq|tq|pq)_[a-z_]+)\s*\(", src)))
 
 
 def test_every_declared_symbol_is_exported(K):
@@ -75,6 +75,35 @@ def test_host_params_match_oracle(K, bits, mode):
         assert np.array_equal(p["s"], o.s.astype(np.float16).view(np.uint16))
 
 
+def test_polar_layout_and_tables_match_oracle(K):
+    """PolarQuant sessions: a 64-byte record of 16 words, the four Lloyd
+    codebooks of the article's angle laws and the dense sessions' Pi, all
+    equal to the oracle's fp32 values."""
+    from oracle import polar as PQ
+    lay = K.rq_layout(128, 4, K.RQ_POLAR)
+    assert lay["code_words"] == 16 and lay["record_bytes"] == 64 and lay["sign_words"] == 0
+    assert lay["n_coords"] == 128 and lay["n_groups"] == 0
+    p = K.rq_host_params(128, 4, 0, K.RQ_POLAR)
+    books = PQ.codebooks()
+    assert np.array_equal(p["centroids"], np.concatenate([b[0] for b in books]).astype(np.float32))
+    assert np.array_equal(p["boundaries"], np.concatenate([b[1] for b in books]).astype(np.float32))
+    assert np.array_equal(p["pi"], PQ.PolarParams(128, 0).pi.astype(np.float32))
+    assert np.array_equal(p["pi"], K.rq_host_params(128, 4, 0, K.RQ_DENSE)["pi"])
+    # the kernels test lower half-plane angles after a turn by pi against
+    # t_1..t_7: the first-level boundaries must repeat shifted by pi
+    t = p["boundaries"][:15].astype(np.float64)
+    assert np.abs(t[8:] - t[:7] - np.pi).max() < 5e-7 and abs(t[7] - np.pi) < 2e-7
+    with pytest.raises(K.RQError):
+        K.rq_host_quantizer(128, 4, K.RQ_POLAR)
+
+
+@pytest.mark.parametrize("d,bits,mode,status", [(128, 3, 4, 1), (128, 4, 5, 1), (128, 4, 6, 1), (64, 4, 4, 2)])
+def test_polar_bad_settings(K, d, bits, mode, status):
+    with pytest.raises(K.RQError) as e:
+        K.rq_layout(d, bits, mode)
+    assert e.value.status == status
+
+
 def test_different_seeds_give_different_tables(K):
     a = K.rq_host_params(128, 3, 0, K.RQ_QJL)
     b = K.rq_host_params(128, 3, 1, K.RQ_QJL)
@@ -103,6 +132,10 @@ def test_null_arguments_rejected_before_any_device_work(K):
     assert lib.rq_roundtrip(None, None, 1, 10, 128, None, None, None, None, None, 1, 128, None) == K.RQ_EINVAL
     assert lib.rq_score(None, None, 1, 1, None, None, None, None, 10, 10, None, 10, None) == K.RQ_EINVAL
     assert lib.tq_quantize(None, None, 1, 10, 128, None, None, None, None, None) == K.RQ_EINVAL
+    assert lib.pq_quantize(None, None, 1, 10, 128, None, None) == K.RQ_EINVAL
+    assert lib.pq_dequantize(None, None, 10, None, 1, 128, None) == K.RQ_EINVAL
+    assert lib.pq_roundtrip(None, None, 1, 10, 128, None, None, 1, 128, None) == K.RQ_EINVAL
+    assert lib.pq_score(None, None, 1, 1, None, 10, 10, None, 10, None) == K.RQ_EINVAL
     assert lib.rq_get_layout(None, None) == K.RQ_EINVAL
     assert lib.rq_layout(128, 3, 0, None) == K.RQ_EINVAL
     lib.rq_free(None)
