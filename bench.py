@@ -326,8 +326,14 @@ def workload_extras(K, W, dev, stream):
             c.score(q.view(L * HQ, 128), rec, g, T, T, out=scores.view(L * HQ, T))
         lus = _timed(stream, decode_layers, 3)
         dus = _timed(stream, decode, 5)
-        # decode attention over the compressed keys and values in one call
+        # PolarQuant keys of the same cache: bulk quantise, one decode step of scoring (all layers, one call)
         n_k = L * H * T
+        pc = K.PolarCodec(seed=0)
+        pw = pc.alloc_words(n_k, dev)
+        pqus = _timed(stream, lambda i: pc.quantize(flat[:n_k], words=pw), 3)
+        pdus = _timed(stream, lambda i: pc.score(q.view(L * HQ, 128), pw, g, T, T, out=scores.view(L * HQ, T)), 5)
+        del pw, pc
+        # decode attention over the compressed keys and values in one call
         krec = K.Record(rec.codes[:n_k], rec.norms[:n_k], rec.signs[:n_k], rec.rnorms[:n_k])
         vrec = K.Record(rec.codes[n_k:], rec.norms[n_k:], rec.signs[n_k:], rec.rnorms[n_k:])
         ws = torch.empty(K.rq_attend_workspace(L * HQ, g, T) + 256, dtype=torch.uint8, device=dev)
@@ -344,7 +350,11 @@ def workload_extras(K, W, dev, stream):
             "decode_scores_per_s": round(ns / (dus * 1e-6), 1),
             "decode_step_per_layer_calls_us": round(lus, 1),
             "decode_attention_us": round(aus, 1),
-            "decode_attention_keys_per_s": round(n_k / (aus * 1e-6), 1)}
+            "decode_attention_keys_per_s": round(n_k / (aus * 1e-6), 1),
+            "polar_keys_quantize_us": round(pqus, 1),
+            "polar_keys_quantize_gbs": round(n_k * (256 + 64) / (pqus * 1e-6) / 1e9, 1),
+            "polar_decode_step_us": round(pdus, 1),
+            "polar_decode_scores_per_s": round(ns / (pdus * 1e-6), 1)}
         del kv, q, flat, rec, scores, subs, c, krec, vrec, ws, att
         torch.cuda.empty_cache()
     return out
@@ -454,6 +464,19 @@ def main():
     extras["qjl1_roundtrip_gbs"] = round(N_VEC * algorithmic_bytes(q1.layout) / (us1 * 1e-6) / 1e9, 1)
     extras["qjl1_score_us"] = round(sus1, 2)
     del q1rec, q1
+
+    # PolarQuant (16-word records, 496 bits of content) on the same keys:
+    # fused roundtrip, and the 64 queries scored against all keys
+    pc = K.PolarCodec(seed=0)
+    pw = [pc.alloc_words(N_VEC, dev) for _ in range(nsets)]
+    pus = _timed(stream, lambda i: pc.roundtrip(xs[i % nsets], words=pw[i % nsets], out=ys[i % nsets]), a.steps)
+    psus = _timed(stream, lambda i: pc.score(q, pw[i % nsets], N_Q, N_VEC, out=scs[i % nsets]), a.steps)
+    extras["polar_roundtrip_us"] = round(pus, 2)
+    extras["polar_roundtrip_gbs"] = round(N_VEC * (256 + 64 + 256) / (pus * 1e-6) / 1e9, 1)
+    extras["polar_roundtrip_vectors_per_s"] = round(N_VEC / (pus * 1e-6), 1)
+    extras["polar_score_us"] = round(psus, 2)
+    extras["polar_scores_per_s"] = round(N_VEC * N_Q / (psus * 1e-6), 1)
+    del pw, pc
 
     if a.sweep:
         sweep = {}

@@ -325,3 +325,72 @@ def test_attention_decode_step(K, which, nrows, request):
         zg = scale * sg
         wg = np.exp(zg - zg.max())
         assert np.abs(got[i] - (wg / wg.sum()) @ xv).max() <= 1e-5 * vmax, row
+
+
+# ------------------------------------- PolarQuant keys at the Qwen shape ----
+@pytest.fixture(scope="module")
+def qwen_polar(K, qwen):
+    """The Qwen-shaped cache's keys (all layers, 2,359,296 vectors) as
+    PolarQuant records in one call, and one decode step of all layers'
+    scores in one pq_score call (query row l * HQ + h reads KV head
+    l * H + h / group)."""
+    from oracle import polar as PQ
+    spec = qwen["spec"]
+    L, H, T, HQ = spec["layers"], spec["kv_heads"], spec["tokens"], spec["q_heads"]
+    n_k = L * H * T
+    c = K.PolarCodec(seed=0)
+    words = c.quantize(qwen["flat"][:n_k])
+    scores = torch.empty((L * HQ, T), dtype=torch.float32, device=DEV)
+    c.score(qwen["q"].view(L * HQ, D), words, qwen["group"], T, T, out=scores)
+    _sync()
+    st = dict(codec=c, words=words, scores=scores, n_k=n_k, p=PQ.PolarParams(D, 0))
+    yield st
+    st.clear()
+
+
+def test_qwen_polar_sample(K, qwen, qwen_polar):
+    """A seeded 1% of the key rows against the oracle: angle codes, radii,
+    dequantisation, and the 8 query heads' scores of every sampled key."""
+    from oracle import polar as PQ
+    st, spec = qwen_polar, qwen["spec"]
+    H, T, HQ, g = spec["kv_heads"], spec["tokens"], spec["q_heads"], qwen["group"]
+    rows = W.sample_rows(st["n_k"], 0.01, seed=8)
+    it = torch.from_numpy(rows).to(DEV)
+    words = st["words"].index_select(0, it).cpu().numpy().view(np.uint32)
+    x = qwen["flat"].index_select(0, it).cpu().numpy()
+    rep = PR.check_polar_words(st["p"], x, words)
+    print(f"qwen polar sample: {rows.size} keys, {rep}", flush=True)
+    y = st["codec"].dequantize(st["words"].index_select(0, it), dtype=torch.float32).cpu().numpy()
+    rn = PR.polar_radius_norm(words)
+    PR.compare_recon(y, PQ.dequantize(st["p"], words), rn, "polar dequantize")
+    layer, head, tok = rows // (H * T), (rows // T) % H, rows % T
+    qrows = (layer * HQ + head * g)[:, None] + np.arange(g)[None, :]
+    got = st["scores"][torch.from_numpy(qrows).to(DEV), torch.from_numpy(tok).to(DEV)[:, None]]
+    got = got.cpu().numpy().astype(np.float64)
+    qh = qwen["q_host"].reshape(-1, D).astype(np.float64)
+    for key in np.unique(layer * H + head):
+        sel = (layer * H + head) == key
+        qk = qh[qrows[sel][0]]
+        ref = PQ.score(st["p"], qk, words[sel])
+        PR.compare_scores(got[sel].T, ref, np.linalg.norm(qk, axis=1)[:, None], rn[sel][None, :],
+                          f"polar kv head {key}")
+
+
+def test_qwen_polar_scores_full(K, qwen, qwen_polar):
+    """All 18,874,368 polar decode scores against q . dequant(k), within
+    1e-4 * ||q|| * ||r^||."""
+    st, spec = qwen_polar, qwen["spec"]
+    L, H, T, HQ, g = spec["layers"], spec["kv_heads"], spec["tokens"], spec["q_heads"], qwen["group"]
+    q = qwen["q"].view(L * HQ, D).to(torch.float64)
+    qn = torch.linalg.norm(q, dim=1)
+    worst = 0.0
+    for j in range(L * H):
+        w = st["words"][j * T:(j + 1) * T]
+        xt = st["codec"].dequantize(w, dtype=torch.float32).to(torch.float64)
+        rb = w[:, 12:16].contiguous().view(torch.float16).to(torch.float64)
+        rn = torch.linalg.norm(rb, dim=1)
+        ref = q[j * g:(j + 1) * g] @ xt.T
+        lim = PR.SCORE_TOL * qn[j * g:(j + 1) * g, None] * rn[None, :] + 1e-30
+        ratio = (st["scores"][j * g:(j + 1) * g].to(torch.float64) - ref).abs() / lim
+        worst = max(worst, float(ratio.max()))
+    assert worst <= 1.0, f"polar score vs dequantised key: worst {worst:.3g} x tolerance"

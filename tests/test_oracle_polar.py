@@ -89,3 +89,31 @@ def test_quantise_dequantise_roundtrip():
     # more levels of the radius tree decoded exactly -> exact vector
     ex = PQ.polar_inverse(diag.angles, PQ._half_value(rb)) @ p.pi
     assert np.abs(ex - x).max() < 1e-2 * np.abs(x).max()
+
+
+def test_codes_are_the_nearest_centroid():
+    """code = #{k : theta > t_k} with midpoint boundaries is the index of the
+    nearest centroid (circular distance on level 1), by brute force."""
+    p = PQ.PolarParams(128, 0)
+    x = W.gaussian(300, seed=6).astype(np.float64)
+    words, diag = PQ.quantize(p, x)
+    codes, _ = PQ.unpack(words)
+    for level in range(PQ.N_LEVELS):
+        c = p.books[level][0]
+        d = np.abs(diag.angles[level][..., None] - c)
+        if level == 0:
+            d = np.minimum(d, 2 * math.pi - d)
+        assert np.array_equal(codes[level], np.argmin(d, axis=-1))
+
+
+def test_score_reads_rotated_coordinates():
+    """With q = Pi^T e_j the score is coordinate j of the decoded polar
+    vector y~ (Pi orthogonal): a transposed Pi or a misplaced level fails."""
+    p = PQ.PolarParams(128, 0)
+    x = W.gaussian(40, seed=7).astype(np.float64)
+    words, _ = PQ.quantize(p, x)
+    codes, rb = PQ.unpack(words)
+    angles = [p.books[l][0][codes[l]] for l in range(PQ.N_LEVELS)]
+    yt = PQ.polar_inverse(angles, PQ._half_value(rb))
+    s = PQ.score(p, p.pi[[3, 77]], words)             # rows of Pi = (Pi^T e_j)^T
+    assert np.abs(s - yt[:, [3, 77]].T).max() < 1e-5 * np.abs(yt).max()
