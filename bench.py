@@ -134,7 +134,8 @@ COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
 def _counter_dispatches(path, counter):
-    """{kernel name: [counter value (KiB) per dispatch]} from a rocprofv3 CSV."""
+    """{kernel name: [counter value (KiB) per dispatch, in dispatch order]}
+    from a rocprofv3 CSV."""
     import csv
     sums, names = {}, {}
     with open(path) as f:
@@ -145,17 +146,17 @@ def _counter_dispatches(path, counter):
             sums[d] = sums.get(d, 0.0) + float(r["Counter_Value"])
             names[d] = r["Kernel_Name"]
     out = {}
-    for d, v in sums.items():
-        out.setdefault(names[d], []).append(v)
+    for d in sorted(sums, key=int):
+        out.setdefault(names[d], []).append(sums[d])
     return out
 
 
 def ingest_counters(fetch_csv, write_csv, copy_bytes):
     """HBM bytes per roundtrip launch, scaled by a plain copy of known size.
 
-    The calibration copy is the largest copyBuffer dispatch of the run (the
-    --copy-bytes copies); each counter is divided by what it reads for that
-    copy per byte moved."""
+    The calibration copy is the last copyBuffer dispatch of the run (the
+    --copy-bytes copies close the process); each counter is divided by what
+    it reads for that copy per byte moved."""
     fetch = _counter_dispatches(fetch_csv, "FETCH_SIZE")
     write = _counter_dispatches(write_csv, "WRITE_SIZE")
 
@@ -165,8 +166,8 @@ def ingest_counters(fetch_csv, write_csv, copy_bytes):
             raise SystemExit(f"no dispatch of {name} in the counter CSV")
         return hits
 
-    f_copy = max(values(fetch, COPY_KERNEL)) * 1024.0
-    w_copy = max(values(write, COPY_KERNEL)) * 1024.0
+    f_copy = values(fetch, COPY_KERNEL)[-1] * 1024.0
+    w_copy = values(write, COPY_KERNEL)[-1] * 1024.0
     fr, wr = values(fetch, ROUNDTRIP_KERNEL), values(write, ROUNDTRIP_KERNEL)
     f_rt = sum(fr) / len(fr) * 1024.0
     w_rt = sum(wr) / len(wr) * 1024.0
