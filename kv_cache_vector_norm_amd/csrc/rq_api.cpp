@@ -247,8 +247,8 @@ int rq_init(int d, int bits, uint64_t seed, int mode, rq_ctx** out) {
             }
     }
     if (polar) {
-        // (cos, sin) of the decision boundaries the kernels test (level 1:
-        // t_1..t_7 only, the lower half-plane is tested after a turn by pi;
+        // (cos, sin) of the decision boundaries (level 1: t_1..t_7, of which
+        // the kernels read t_1, folding the point into the first octant;
         // later levels: all three), then of every centroid, levels in order.
         std::vector<double> bnd, cen;
         for (int k = 0; k < 7; ++k) bnd.push_back(t.boundaries[k]);

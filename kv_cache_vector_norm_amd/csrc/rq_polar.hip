@@ -14,15 +14,17 @@
 //
 // Angle codes are taken without any arctangent: for a boundary t, the angle
 // of (a, b) exceeds t exactly when b cos t - a sin t > 0 (the angle and t
-// differ by less than pi).  First-level angles in the lower half-plane are
-// turned by pi (exact negation) and tested against t_1..t_7, since the
-// uniform first-level codebook has t_(k+8) = t_k + pi.
+// differ by less than pi).  The first level's codebook is uniform (t_k =
+// k pi / 8), so its point is folded into the first octant by exact moves —
+// a turn by pi (negation), a turn by -pi/2 (swap and negate), a reflection
+// in the diagonal (swap) — each adding its share of the code, and one cross
+// product against t_1 finishes it.
 #include "rq_dense.cuh"
 
 namespace rqk {
 
 // float2 entries of PolarDev::tab
-constexpr int kPqBnd0 = 0;    // level 1: (cos, sin) of t_1..t_7
+constexpr int kPqBnd0 = 0;    // level 1: (cos, sin) of t_1..t_7 (only t_1 is read)
 constexpr int kPqBnd = 7;     // levels 2..4: 3 each, level L at kPqBnd + 3 (L - 2)
 constexpr int kPqCen0 = 16;   // level 1: 16 centroids
 constexpr int kPqCen = 32;    // levels 2..4: 4 each, level L at kPqCen + 4 (L - 2)
@@ -33,14 +35,20 @@ __device__ __forceinline__ void pq_tab_to_lds(const float* __restrict__ g, float
     if (threadIdx.x < kPqTab2) t[threadIdx.x] = reinterpret_cast<const float2*>(g)[threadIdx.x];
 }
 
-// #{k : angle(a, b) > t_k} on [0, 2 pi) with 15 boundaries (see the header).
-__device__ __forceinline__ uint32_t pq_code_first(float a, float b, const float (&c)[7], const float (&s)[7]) {
+// #{k : angle(a, b) > t_k} on [0, 2 pi) with the 15 uniform boundaries
+// t_k = k pi / 8 (see the header): lower half-plane (+8), second quadrant of
+// what is left (+4), upper octant of that (+2, reflected), then the side of
+// the ray at pi / 8 (c1, s1 = cos, sin of t_1).
+__device__ __forceinline__ uint32_t pq_code_first(float a, float b, float c1, float s1) {
     const bool lower = b < 0.0f;
     const float u = lower ? -a : a, v = lower ? -b : b;
-    uint32_t code = lower ? 8u : 0u;
-#pragma unroll
-    for (int k = 0; k < 7; ++k) code += (__builtin_fmaf(v, c[k], -(u * s[k])) > 0.0f) ? 1u : 0u;
-    return code;
+    const bool left = u < 0.0f;   // u = 0 stays: angle pi/2 is below t_4, and (0, 0) codes 0
+    const float u1 = left ? v : u, v1 = left ? -u : v;
+    const bool diag = v1 > u1;
+    const float u2 = diag ? v1 : u1, v2 = diag ? u1 : v1;
+    const float x = __builtin_fmaf(v2, c1, -(u2 * s1));
+    const bool fine = diag ? (x < 0.0f) : (x > 0.0f);
+    return (lower ? 8u : 0u) + (left ? 4u : 0u) + (diag ? 2u : 0u) + (fine ? 1u : 0u);
 }
 
 // #{k : angle(a, b) > t_k} on [0, pi/2] (a, b >= 0) with 3 boundaries.
@@ -51,18 +59,19 @@ __device__ __forceinline__ uint32_t pq_code_later(float a, float b, const float*
     return code;
 }
 
-__device__ __forceinline__ float pq_radius(float a, float b) { return __builtin_sqrtf(__builtin_fmaf(a, a, b * b)); }
+// Radii use the hardware square root (within an ulp): they feed the next
+// level's decisions and the stored halves, far above that error.
+__device__ __forceinline__ float pq_radius(float a, float b) {
+    return __builtin_amdgcn_sqrtf(__builtin_fmaf(a, a, b * b));
+}
 
 // Boundary constants of one wave, held in SGPRs.
 struct PqBounds {
-    float c0[7], s0[7];
+    float c0, s0;
     float c[3][3], s[3][3];
     __device__ void load(const float2* __restrict__ tab, int z) {
-#pragma unroll
-        for (int k = 0; k < 7; ++k) {
-            c0[k] = uniform(tab[kPqBnd0 + k + z].x);
-            s0[k] = uniform(tab[kPqBnd0 + k + z].y);
-        }
+        c0 = uniform(tab[kPqBnd0 + z].x);
+        s0 = uniform(tab[kPqBnd0 + z].y);
 #pragma unroll
         for (int L = 0; L < 3; ++L)
 #pragma unroll
@@ -207,16 +216,24 @@ __global__ __launch_bounds__(kPqWaves * 64) void pq_quant_kernel(PolarDev P, con
                                                                  uint32_t* __restrict__ words, char* __restrict__ y,
                                                                  int64_t ldy_bytes) {
     __shared__ PqQuantLds sm;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t ntiles = (n + 63) / 64;
+    const int64_t tstep = gridDim.x * (int64_t)kPqWaves;
+    // fp16 input is fetched one tile ahead (the first one before the block's
+    // staging), so each tile's load latency hides behind the previous tile
+    TileRegs nxt;
+    const int64_t t0 = blockIdx.x * (int64_t)kPqWaves + wave;
+    if constexpr (IN_F16) {
+        if (t0 < ntiles) tile_fetch(x, ldx_bytes, t0 * 64, n, 0, nxt, lane_id());
+    }
     pq_tab_to_lds(P.tab, sm.tab);
     mat_to_lds<kPqWaves * 64>(P.pi_hi, sm.pih);
     mat_to_lds<kPqWaves * 64>(P.pi_lo, sm.pil);
     __syncthreads();
 
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     u32x4* tile = sm.tiles[wave];
     uint32_t* stage = reinterpret_cast<uint32_t*>(tile);
-    const int64_t ntiles = (n + 63) / 64;
-    for (int64_t t = blockIdx.x * (int64_t)kPqWaves + wave; t < ntiles; t += gridDim.x * (int64_t)kPqWaves) {
+    for (int64_t t = t0; t < ntiles; t += tstep) {
         const int64_t base = t * 64;
         const int z = opaque_zero();
         const int l = lane_id() + z;
@@ -227,7 +244,8 @@ __global__ __launch_bounds__(kPqWaves * 64) void pq_quant_kernel(PolarDev P, con
         uint32_t xin[IN_F16 ? 64 : 1];
         float xf32[IN_F16 ? 1 : 128];
         if constexpr (IN_F16) {
-            tile_load(x, ldx_bytes, base, n, 0, tile, l);
+            tile_put(nxt, tile, l);
+            if (t + tstep < ntiles) tile_fetch(x, ldx_bytes, (t + tstep) * 64, n, 0, nxt, l);
             wave_lds_sync();
 #pragma unroll
             for (int c = 0; c < 16; ++c) {

@@ -89,10 +89,14 @@ def test_polar_layout_and_tables_match_oracle(K):
     assert np.array_equal(p["boundaries"], np.concatenate([b[1] for b in books]).astype(np.float32))
     assert np.array_equal(p["pi"], PQ.PolarParams(128, 0).pi.astype(np.float32))
     assert np.array_equal(p["pi"], K.rq_host_params(128, 4, 0, K.RQ_DENSE)["pi"])
-    # the kernels test lower half-plane angles after a turn by pi against
-    # t_1..t_7: the first-level boundaries must repeat shifted by pi
-    t = p["boundaries"][:15].astype(np.float64)
-    assert np.abs(t[8:] - t[:7] - np.pi).max() < 5e-7 and abs(t[7] - np.pi) < 2e-7
+    # the kernels fold first-level points into the first octant (turns by pi
+    # and pi/2, a reflection in the diagonal) and test only t_1: the
+    # boundaries must repeat under those moves
+    t = np.concatenate([[0.0], p["boundaries"][:15].astype(np.float64)])
+    k = np.arange(16)
+    assert np.abs(t[1:] - k[1:] * np.pi / 8).max() < 3e-7
+    assert np.abs(t[5:] - t[1:12] - np.pi / 2).max() < 5e-7
+    assert abs(t[3] - (np.pi / 2 - t[1])) < 2e-7 and abs(t[2] - np.pi / 4) < 1e-7
     with pytest.raises(K.RQError):
         K.rq_host_quantizer(128, 4, K.RQ_POLAR)
 
