@@ -367,6 +367,9 @@ __global__ __launch_bounds__(256) void rq_quant_kernel(RotorDev P, const char* _
     constexpr int W = code_words<B>(kRotCoords);
     constexpr float D = QJL ? kQjlDomain : 1.0f;
     constexpr bool BACK = QJL && ROUNDTRIP;
+    // fp16 input of the next tile in flight during this one, where the
+    // registers allow (not in the QJL roundtrip, which holds x~ as well)
+    constexpr bool AHEAD = IN_F16 && !BACK;
     struct Lds {
         u32x4 bins[kBinSlots];
         u32x4 tiles[4][kTileBytes / 16];
@@ -411,7 +414,12 @@ __global__ __launch_bounds__(256) void rq_quant_kernel(RotorDev P, const char* _
         const int l = lane_id() + z;
         const cfloat_ptr rot = reinterpret_cast<cfloat_ptr>(reinterpret_cast<uintptr_t>(P.rotmat)) + z;
         VecIn<IN_F16> in;
-        if constexpr (IN_F16) {
+        if constexpr (AHEAD) {
+            if (t != t0) tile_put(first, tile, l);
+            in.own_row(tile, l);
+            const int64_t tn = t + gridDim.x * 4LL;
+            if (tn < ntiles) tile_fetch(x, ldx_bytes, tn * 64, n, 0, first, l);
+        } else if constexpr (IN_F16) {
             if (t != t0) tile_load(x, ldx_bytes, base, n, 0, tile, l);
             in.own_row(tile, l);
         } else {
