@@ -173,62 +173,79 @@ __global__ __launch_bounds__(256) void attend_values_kernel(AttendArgs a) {
     }
     acc_p = f32x16{};
 
-    for (int64_t tile = blockIdx.x * 4LL + wave; tile < ntiles; tile += gridDim.x * 4LL) {
-        const int64_t kbase = tile * 64;
-        // this lane's row of estimates for the tile: keys 16 kb + 8 hh .. + 7
+    // One tile's inputs in registers: this lane's row of estimates (keys
+    // 16 kb + 8 hh .. + 7 of each K block) and dword l of the tile's code,
+    // sign and norm runs.  They are fetched one tile ahead of their use, so
+    // each tile's load latency hides behind the previous tile's arithmetic.
+    struct TileIn {
         u32x4 sv[4][2];
+        uint32_t cw[W];
+        uint32_t sw[4];
+        uint32_t nb, gb;
+    };
+    auto fetch = [&](int64_t tile, TileIn& r) {
+        const int64_t kbase = tile * 64;
         const uint32_t soff = static_cast<uint32_t>((n * a.ld + kbase + 8 * hh) * 4);
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
             for (int q = 0; q < 2; ++q)
-                sv[kb][q] = live ? __builtin_amdgcn_raw_buffer_load_b128(rsc, soff, 64 * kb + 16 * q, kNonTemporal)
-                                 : u32x4{0u, 0u, 0u, 0u};
-        // the tile's value records into LDS, key-minor
-        {
-            const int64_t left = a.t - kbase;
-            int64_t row = rbase + kbase;
-            if (a.pt.pages != nullptr) {
-                const int64_t pg = a.pt.pages[kvh * a.pt.stride + (kbase >> a.pt.shift)];
-                row = (pg << a.pt.shift) + (kbase & ((int64_t(1) << a.pt.shift) - 1));
-            }
-            const rsrc_t rc = make_rsrc(a.codes + row * W, tile_range(left, 4 * W));
-            uint32_t cw[W];
-#pragma unroll
-            for (int it = 0; it < W; ++it)
-                cw[it] = __builtin_amdgcn_raw_buffer_load_b32(rc, static_cast<uint32_t>(4 * l), 256 * it, kNonTemporal);
-            uint32_t sw[4];
-            if constexpr (QJL) {
-                const rsrc_t rs = make_rsrc(a.signs + row * 4, tile_range(left, 16));
-#pragma unroll
-                for (int it = 0; it < 4; ++it)
-                    sw[it] = __builtin_amdgcn_raw_buffer_load_b32(rs, static_cast<uint32_t>(4 * l), 256 * it,
-                                                                  kNonTemporal);
-            }
-            const rsrc_t rn = make_rsrc(a.norms + row, tile_range(left, 2));
-            const uint32_t nb = __builtin_amdgcn_raw_buffer_load_b16(rn, static_cast<uint32_t>(2 * l), 0, kNonTemporal);
-            uint32_t gb = 0u;
-            if constexpr (QJL) {
-                const rsrc_t rg = make_rsrc(a.rnorms + row, tile_range(left, 2));
-                gb = __builtin_amdgcn_raw_buffer_load_b16(rg, static_cast<uint32_t>(2 * l), 0, kNonTemporal);
-            }
-            wave_lds_sync();
-#pragma unroll
-            for (int it = 0; it < W; ++it) {
-                const int d = it * 64 + l;
-                wv.code[d % W][d / W] = cw[it];
-            }
-            if constexpr (QJL) {
-#pragma unroll
-                for (int it = 0; it < 4; ++it) {
-                    const int d = it * 64 + l;
-                    wv.sign[d & 3][d >> 2] = sw[it];
-                }
-                wv.gam[l] = static_cast<uint16_t>(gb);
-            }
-            wv.nrm[l] = static_cast<uint16_t>(nb);
-            wave_lds_sync();
+                r.sv[kb][q] = live ? __builtin_amdgcn_raw_buffer_load_b128(rsc, soff, 64 * kb + 16 * q, kNonTemporal)
+                                   : u32x4{0u, 0u, 0u, 0u};
+        const int64_t left = a.t - kbase;
+        int64_t row = rbase + kbase;
+        if (a.pt.pages != nullptr) {
+            const int64_t pg = a.pt.pages[kvh * a.pt.stride + (kbase >> a.pt.shift)];
+            row = (pg << a.pt.shift) + (kbase & ((int64_t(1) << a.pt.shift) - 1));
         }
+        const rsrc_t rc = make_rsrc(a.codes + row * W, tile_range(left, 4 * W));
+#pragma unroll
+        for (int it = 0; it < W; ++it)
+            r.cw[it] = __builtin_amdgcn_raw_buffer_load_b32(rc, static_cast<uint32_t>(4 * l), 256 * it, kNonTemporal);
+        if constexpr (QJL) {
+            const rsrc_t rs = make_rsrc(a.signs + row * 4, tile_range(left, 16));
+#pragma unroll
+            for (int it = 0; it < 4; ++it)
+                r.sw[it] = __builtin_amdgcn_raw_buffer_load_b32(rs, static_cast<uint32_t>(4 * l), 256 * it, kNonTemporal);
+        }
+        const rsrc_t rn = make_rsrc(a.norms + row, tile_range(left, 2));
+        r.nb = __builtin_amdgcn_raw_buffer_load_b16(rn, static_cast<uint32_t>(2 * l), 0, kNonTemporal);
+        r.gb = 0u;
+        if constexpr (QJL) {
+            const rsrc_t rg = make_rsrc(a.rnorms + row, tile_range(left, 2));
+            r.gb = __builtin_amdgcn_raw_buffer_load_b16(rg, static_cast<uint32_t>(2 * l), 0, kNonTemporal);
+        }
+    };
+
+    const int64_t tstep = gridDim.x * 4LL;
+    TileIn nx;
+    if (blockIdx.x * 4LL + wave < ntiles) fetch(blockIdx.x * 4LL + wave, nx);
+    for (int64_t tile = blockIdx.x * 4LL + wave; tile < ntiles; tile += tstep) {
+        const int64_t kbase = tile * 64;
+        u32x4 sv[4][2];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            sv[kb][0] = nx.sv[kb][0];
+            sv[kb][1] = nx.sv[kb][1];
+        }
+        // the tile's value records into LDS, key-minor
+        wave_lds_sync();
+#pragma unroll
+        for (int it = 0; it < W; ++it) {
+            const int d = it * 64 + l;
+            wv.code[d % W][d / W] = nx.cw[it];
+        }
+        if constexpr (QJL) {
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                const int d = it * 64 + l;
+                wv.sign[d & 3][d >> 2] = nx.sw[it];
+            }
+            wv.gam[l] = static_cast<uint16_t>(nx.gb);
+        }
+        wv.nrm[l] = static_cast<uint16_t>(nx.nb);
+        wave_lds_sync();
+        if (tile + tstep < ntiles) fetch(tile + tstep, nx);
 
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {

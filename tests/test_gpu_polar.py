@@ -139,3 +139,43 @@ def test_polar_sessions_are_separate(K):
     w1 = K.PolarCodec(seed=1).quantize(x)
     torch.cuda.synchronize()
     assert not torch.equal(w0, w1)
+
+
+def test_polar_strided_rows_and_empty_calls(K, P):
+    """Row pitches above 128 elements read and write only the first 128;
+    n = 0 and t = 0 are no-ops; bad arguments are rejected before any launch."""
+    n, ld = 300, 136
+    xs = np.full((n, ld), 9.0, dtype=np.float32)
+    xs[:, :D] = W.gaussian(n, seed=117, dtype=np.float32)
+    c = K.PolarCodec(seed=0)
+    xt = torch.from_numpy(xs).cuda()
+    words = c.alloc_words(n)
+    y = torch.full((n, ld), 5.0, device="cuda")
+    K.pq_roundtrip(c.ctx, xt, K.RQ_F32, n, ld, words, y, K.RQ_F32, ld)
+    torch.cuda.synchronize()
+    gw = _words(words)
+    PR.check_polar_words(P, xs[:, :D], gw)
+    assert torch.all(y[:, D:] == 5.0)
+    ref = c.dequantize(c.quantize(torch.from_numpy(np.ascontiguousarray(xs[:, :D])).cuda()), dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(y[:, :D], ref)
+    # empty calls touch nothing
+    w0 = torch.full((1, 16), 3, dtype=torch.int32, device="cuda")
+    K.pq_quantize(c.ctx, xt, K.RQ_F32, 0, ld, w0)
+    K.pq_dequantize(c.ctx, w0, 0, y, K.RQ_F32, ld)
+    s0 = torch.full((2, 4), 1.5, device="cuda")
+    q = torch.from_numpy(W.queries(2, seed=118)).cuda()
+    K.pq_score(c.ctx, q, 2, 2, w0, 0, 0, s0, 4)
+    torch.cuda.synchronize()
+    assert torch.all(w0 == 3) and torch.all(s0 == 1.5)
+    # argument checks
+    with pytest.raises(K.RQError):
+        K.pq_quantize(c.ctx, xt, K.RQ_F32, n, 100, words)                  # ld < 128
+    with pytest.raises(K.RQError):
+        K.pq_roundtrip(c.ctx, xt, K.RQ_F32, n, ld, words, xt, K.RQ_F32, ld)   # x and y overlap
+    with pytest.raises(K.RQError):
+        K.pq_score(c.ctx, q, 2, 3, words, n, n, s0, 4)                      # hq % group != 0
+    with pytest.raises(K.RQError):
+        K.pq_score(c.ctx, q, 2, 1, words, 10, 5, torch.empty((2, 10), device="cuda"), 10)   # kv_stride < t
+    with pytest.raises(K.RQError):
+        K.pq_score(c.ctx, q, 2, 2, words, 10, 10, torch.empty((2, 10), device="cuda"), 8)   # ld < t
