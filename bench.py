@@ -369,7 +369,7 @@ def main():
         ingest_counters(a.ingest_counters[0], a.ingest_counters[1], a.copy_bytes or (256 << 20))
         return
     if a.gpus != 1:
-        print(f"bench.py measures one GPU: this build runs on a single MI355X and has no multi-GPU path "
+        print(f"bench.py measures one GPU: the codec library runs on a single MI355X and has no multi-GPU path "
               f"(asked for --gpus {a.gpus})", file=sys.stderr)
         sys.exit(2)
     import numpy as np
@@ -381,8 +381,8 @@ def main():
     torch.cuda.set_device(dev)
     codec = K.Codec(bits=BITS, seed=0, mode=K.RQ_QJL)
     lay = codec.layout
-    x_host = W.keys_c1()
-    q_host = W.queries_c1()
+    x_host = W.keys_65536()
+    q_host = W.queries_64()
     x0 = torch.from_numpy(x_host).to(dev)
     q = torch.from_numpy(q_host).to(dev)
 

@@ -43,21 +43,21 @@ def queries(h, d=HEAD_DIM, seed=1):
     return gaussian(h, d, seed, np.float32)
 
 
-def unit_vectors_c0():
+def unit_vectors_1024():
     """1,024 fp32 unit vectors (N(0,1) then normalised), seed 0."""
     return unit_gaussian(1024, seed=0, dtype=np.float32)
 
 
-def keys_c1():
+def keys_65536():
     """65,536 fp16 N(0,1) vectors (norms near sqrt(128)), seed 0."""
     return gaussian(65536, seed=0, dtype=np.float16)
 
 
-def queries_c1():
+def queries_64():
     return queries(64, seed=1)
 
 
-def keys_c2():
+def keys_262144():
     return gaussian(262144, seed=0, dtype=np.float16)
 
 

@@ -60,7 +60,7 @@ def test_tq_dequant_and_roundtrip(K, bits, mode, in_dtype):
 
 def test_tq_mse_matches_rq(K):
     """README 'MSE Quality': TurboQuant and RotorQuant reach the same MSE."""
-    x = W.unit_vectors_c0()
+    x = W.unit_vectors_1024()
     out = {}
     for mode in (OP.MSE, OP.DENSE):
         c = K.Codec(bits=3, seed=0, mode=mode)

@@ -67,7 +67,7 @@ def test_polar_quantize_dequantize_roundtrip(K, P, n, in_dtype):
 def test_polar_keys_65536(K, P):
     """The 65,536 fp16 N(0,1) keys with their norms, fused roundtrip: 64 B
     per key (4.13x over fp16 by the article's 496-bit count)."""
-    x = W.keys_c1()
+    x = W.keys_65536()
     c = K.PolarCodec(seed=0)
     words, y = c.roundtrip(torch.from_numpy(x).cuda(), dtype=torch.float32)
     torch.cuda.synchronize()

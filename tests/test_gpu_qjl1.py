@@ -59,9 +59,9 @@ def test_qjl1_quantize_dequantize_roundtrip(K, mode, n, in_dtype):
     PR.compare_recon(d32.cpu().numpy(), OC.dequantize(p, hrec), OC.half_value(hrec.norms), "qjl1 dequantize")
 
 
-def test_qjl1_c1_keys(K):
+def test_qjl1_65536_keys(K):
     """The 65,536 fp16 N(0,1) keys at one bit: 20 B per key (12.8x)."""
-    x = W.keys_c1()
+    x = W.keys_65536()
     c = K.Codec(bits=1, seed=0, mode=OP.QJL)
     rec, y = c.roundtrip(torch.from_numpy(x).cuda(), dtype=torch.float32)
     torch.cuda.synchronize()

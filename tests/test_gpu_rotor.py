@@ -151,10 +151,10 @@ def test_deterministic(K):
         assert torch.equal(u, v)
 
 
-def test_c0_unit_vectors_mse_and_cosine(K):
+def test_1024_unit_vectors_mse_and_cosine(K):
     """1,024 fp32 unit vectors, 3-bit MSE-only roundtrip (README MSE table:
     MSE 0.034, cosine 0.983)."""
-    x = W.unit_vectors_c0()
+    x = W.unit_vectors_1024()
     c = K.Codec(bits=3, seed=0, mode=OP.MSE)
     rec, y = c.roundtrip(torch.from_numpy(x).cuda(), dtype=torch.float32)
     torch.cuda.synchronize()
@@ -169,9 +169,9 @@ def test_c0_unit_vectors_mse_and_cosine(K):
     PR.compare_recon(y, OC.dequantize(p, orec), OC.half_value(orec.norms), rows=~excl)
 
 
-def test_c1_keys_full_parity(K):
+def test_65536_keys_full_parity(K):
     """65,536 fp16 N(0,1) keys, 2-bit MSE + 1-bit QJL (3 bits total)."""
-    x = W.keys_c1()
+    x = W.keys_65536()
     c = K.Codec(bits=3, seed=0, mode=OP.QJL)
     rec, y = c.roundtrip(torch.from_numpy(x).cuda(), dtype=torch.float32)
     torch.cuda.synchronize()

@@ -59,7 +59,7 @@ def test_score_gqa_shapes(K, t, hq, group, stride):
     _score_case(K, 3, OP.QJL, t, hq, group, stride)
 
 
-def test_score_c1_shape(K):
+def test_score_65536_keys_64_queries(K):
     """64 queries against 65,536 keys of one head (2-bit codes + QJL)."""
     _score_case(K, 3, OP.QJL, t=65536, hq=64, group=64, seed=1)
 

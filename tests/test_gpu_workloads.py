@@ -107,8 +107,8 @@ def _check_sampled_scores(p, q_host, scores, rec, rows, kv_heads, t, group):
 
 
 # ------------------------------------------- 262,144 keys, dense sweep ----
-C2_N = 262144
-C2_MODES = ([(b, OP.DENSE) for b in (2, 3, 4)] + [(b, OP.DENSE | OP.QJL) for b in (2, 3, 4, 5)]
+N_262144 = 262144
+MODES_262144 = ([(b, OP.DENSE) for b in (2, 3, 4)] + [(b, OP.DENSE | OP.QJL) for b in (2, 3, 4, 5)]
             + [(b, OP.MSE) for b in (2, 3, 4)] + [(3, OP.QJL)])
 # Unit-vector distortion of the Lloyd-Max codebooks (README "MSE Quality";
 # hyper.ai Theorem 1 table) at 2/3/4 bits.
@@ -116,15 +116,15 @@ LLOYD_MAX_MSE = {2: 0.1160, 3: 0.0340, 4: 0.0093}
 
 
 @pytest.fixture(scope="module")
-def c2_keys(K):
-    x = W.keys_c2()
+def keys_262144_fixture(K):
+    x = W.keys_262144()
     return x, torch.from_numpy(x).to(DEV)
 
 
-@pytest.mark.parametrize("bits,mode", C2_MODES)
-def test_c2_sweep(K, c2_keys, bits, mode):
-    x, xd = c2_keys
-    print(f"c2 sweep bits={bits} mode={mode}", flush=True)
+@pytest.mark.parametrize("bits,mode", MODES_262144)
+def test_262144_keys_sweep(K, keys_262144_fixture, bits, mode):
+    x, xd = keys_262144_fixture
+    print(f"262,144-key sweep bits={bits} mode={mode}", flush=True)
     c = K.Codec(bits=bits, seed=0, mode=mode)
     rec, y = c.roundtrip(xd, dtype=torch.float32)
     d = c.dequantize(rec, dtype=torch.float32)
@@ -134,7 +134,7 @@ def test_c2_sweep(K, c2_keys, bits, mode):
         xs = xd.to(torch.float64)
         rel = (((xs - y.to(torch.float64)) ** 2).sum(1) / (xs ** 2).sum(1)).mean().item()
         assert abs(rel - LLOYD_MAX_MSE[bits]) < 0.01 * LLOYD_MAX_MSE[bits] + 2e-4, rel
-    idx = W.sample_rows(C2_N, 1 / 16, seed=100 + 10 * bits + mode)
+    idx = W.sample_rows(N_262144, 1 / 16, seed=100 + 10 * bits + mode)
     codes, norms, signs, rnorms = _gather(rec, idx)
     p = OP.Params(D, bits, 0, mode)
     PR.check_records(p, x[idx], codes, norms, signs, rnorms)

@@ -149,8 +149,8 @@ def test_blog_norm_separation():
 
 
 # ------------------------------------------------------------ quality ---
-def test_c0_roundtrip_mse_and_cosine():
-    x = W.unit_vectors_c0().astype(np.float64)
+def test_1024_unit_vectors_mse_and_cosine():
+    x = W.unit_vectors_1024().astype(np.float64)
     g = golden("readme_mse_table.json")
     for row in g["rows"]:
         p = P.Params(D, row["bits"], 0, P.MSE)
