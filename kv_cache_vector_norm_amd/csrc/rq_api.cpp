@@ -67,6 +67,7 @@ struct rq_ctx {
     std::vector<void*> dev;   // every device allocation of this session
     // rotor tables
     float* rotmat = nullptr;
+    float* rotmat16 = nullptr;
     float* thr = nullptr;
     float* cent = nullptr;
     rqk::u32x4_t* bins = nullptr;
@@ -216,7 +217,13 @@ int rq_init(int d, int bits, uint64_t seed, int mode, rq_ctx** out) {
         *hi = h;
         *lo = rqh::double_to_half_rne((x - hv) * 2048.0);
     };
+    std::vector<float> rotmat16;
     if (rotor) {
+        // the rotor matrices padded to 16 floats (one 64-byte line) per group,
+        // for the codec kernels' scalar loads
+        rotmat16.assign(static_cast<size_t>(t.lay.n_groups) * 16, 0.0f);
+        for (int g = 0; g < t.lay.n_groups; ++g)
+            for (int k = 0; k < 9; ++k) rotmat16[16 * g + k] = t.rotmats[9 * g + k];
         // Phi[i][j]: slot i = 3 g + r reads coordinates 3 g .. 3 g + 2 through row r of M_g
         phi_hi.assign(static_cast<size_t>(n) * n, 0);
         phi_lo.assign(static_cast<size_t>(n) * n, 0);
@@ -287,6 +294,7 @@ int rq_init(int d, int bits, uint64_t seed, int mode, rq_ctx** out) {
     do {
         if (rotor) {
             if ((e = upload(reinterpret_cast<void**>(&ctx->rotmat), t.rotmats.data(), t.rotmats.size() * 4)) != hipSuccess) break;
+            if ((e = upload(reinterpret_cast<void**>(&ctx->rotmat16), rotmat16.data(), rotmat16.size() * 4)) != hipSuccess) break;
             if ((e = upload(reinterpret_cast<void**>(&ctx->phi_hi), phi_hi.data(), phi_hi.size() * 2)) != hipSuccess) break;
             if ((e = upload(reinterpret_cast<void**>(&ctx->phi_lo), phi_lo.data(), phi_lo.size() * 2)) != hipSuccess) break;
         }
@@ -366,6 +374,7 @@ static int check_record(const rq_ctx* ctx, const void* codes, const void* norms,
 static rqk::RotorTables rotor_tables(const rq_ctx* c) {
     rqk::RotorTables t;
     t.rotmat = c->rotmat;
+    t.rotmat16 = c->rotmat16;
     t.thr = c->thr;
     t.cent = c->cent;
     t.bins = c->bins;

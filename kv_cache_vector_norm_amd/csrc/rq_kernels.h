@@ -19,6 +19,7 @@ constexpr int kBinSlots = 256;
 // Device-resident tables of a rotor session.
 struct RotorTables {
     const float* rotmat;     // [43][9]
+    const float* rotmat16;   // [43][16]: the same matrices, one 64-byte line per group
     const float* thr;        // [L-1]
     const float* cent;       // [L]
     const u32x4_t* bins;     // [kBinSlots]

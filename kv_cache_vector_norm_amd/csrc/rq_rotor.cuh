@@ -328,15 +328,21 @@ struct VecIn<false> {
 };
 
 // Rotor matrices are read with scalar loads (constant address space) two
-// groups ahead of use.  A scalar-cache miss costs an L2 round trip, far more
+// groups ahead of use, from the padded table (one 64-byte line per group,
+// so each group's nine floats come in two loads).  A scalar-cache miss costs an L2 round trip, far more
 // than the two groups of lead, so every 64-byte line of the table is touched
 // once per wave before the tile loop (the loads overlap the block's staging).
 typedef __attribute__((address_space(4))) const float* cfloat_ptr;
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(4))) const f32x8* cf32x8_ptr;
+// p: a group's 64-byte line of the padded table (32-byte aligned)
 __device__ __forceinline__ void load_mat(cfloat_ptr p, float (&m)[9]) {
+    const f32x8 v = *reinterpret_cast<cf32x8_ptr>(p);
 #pragma unroll
-    for (int k = 0; k < 9; ++k) m[k] = p[k];
+    for (int k = 0; k < 8; ++k) m[k] = v[k];
+    m[8] = p[8];
 }
-constexpr int kRotLines = (kGroups * 9 + 15) / 16;
+constexpr int kRotLines = kGroups;
 struct RotWarm {
     uint32_t v[kRotLines];
 };
@@ -393,7 +399,7 @@ __global__ __launch_bounds__(256) void rq_quant_kernel(RotorDev P, const char* _
     }
     // rotor table lines into the scalar cache, in flight with the staging
     RotWarm warm;
-    warm_rotor_table(reinterpret_cast<cfloat_ptr>(reinterpret_cast<uintptr_t>(P.rotmat)), warm);
+    warm_rotor_table(reinterpret_cast<cfloat_ptr>(reinterpret_cast<uintptr_t>(P.rotmat16)), warm);
     stage_bins<QJL>(P.bins, bins);
     if constexpr (QJL) mat_to_lds(P.s_fwd, s_fwd);
     if constexpr (BACK) mat_to_lds(P.s_back, s_back);
@@ -412,7 +418,7 @@ __global__ __launch_bounds__(256) void rq_quant_kernel(RotorDev P, const char* _
         const int64_t base = t * 64;
         const int z = opaque_zero();
         const int l = lane_id() + z;
-        const cfloat_ptr rot = reinterpret_cast<cfloat_ptr>(reinterpret_cast<uintptr_t>(P.rotmat)) + z;
+        const cfloat_ptr rot = reinterpret_cast<cfloat_ptr>(reinterpret_cast<uintptr_t>(P.rotmat16)) + z;
         VecIn<IN_F16> in;
         if constexpr (AHEAD) {
             if (t != t0) tile_put(first, tile, l);
@@ -425,11 +431,21 @@ __global__ __launch_bounds__(256) void rq_quant_kernel(RotorDev P, const char* _
         } else {
             in.load(x, ldx_bytes, base, n, tile, l);
         }
+        // sum of squares: fp16 pairs through v_dot2_f32_f16 (exact products,
+        // fp32 accumulation), fp32 input by fused multiply-adds
         float ss = 0.0f;
+        if constexpr (IN_F16) {
 #pragma unroll
-        for (int i = 0; i < kD; ++i) {
-            const float v = in.get(i);
-            ss = __builtin_fmaf(v, v, ss);
+            for (int i = 0; i < kD / 2; ++i) {
+                const f16x2 h = __builtin_bit_cast(f16x2, in.h[i]);
+                ss = __builtin_amdgcn_fdot2(h, h, ss, false);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < kD; ++i) {
+                const float v = in.get(i);
+                ss = __builtin_fmaf(v, v, ss);
+            }
         }
         const float nrm = __builtin_sqrtf(ss);
         const float inv = nrm > 0.0f ? 1.0f / nrm : 0.0f;
@@ -476,7 +492,7 @@ __global__ __launch_bounds__(256) void rq_quant_kernel(RotorDev P, const char* _
             }
         };
         load_mat(rot, mx[0]);
-        load_mat(rot + 9, mx[1]);
+        load_mat(rot + 16, mx[1]);
         stage_a(std::integral_constant<int, 0>{});
 
         static_for<0, kGroups>([&](auto gc) __attribute__((always_inline)) {
@@ -502,7 +518,7 @@ __global__ __launch_bounds__(256) void rq_quant_kernel(RotorDev P, const char* _
                     frag = mat_frag(s_fwd, 32 * mt + (l & 31), 2 * kb + (l >> 5));
                 }
             }
-            if constexpr (g + 2 < kGroups) load_mat(rot + 9 * (g + 2), mx[(g + 2) % 3]);
+            if constexpr (g + 2 < kGroups) load_mat(rot + 16 * (g + 2), mx[(g + 2) % 3]);
             __builtin_amdgcn_sched_barrier(0);
 
             // stage B of group g

@@ -7,6 +7,7 @@ namespace rqk {
 
 struct RotorDev {
     const float* __restrict__ rotmat;
+    const float* __restrict__ rotmat16;
     const float* __restrict__ cent;
     const u32x4_t* __restrict__ bins;
     const uint16_t* __restrict__ s_fwd;

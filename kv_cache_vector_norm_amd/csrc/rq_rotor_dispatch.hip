@@ -6,6 +6,7 @@ namespace rqk {
 static RotorDev make_dev(const RotorTables& t) {
     RotorDev P;
     P.rotmat = t.rotmat;
+    P.rotmat16 = t.rotmat16;
     P.cent = t.cent;
     P.bins = t.bins;
     P.bin_a = t.bin_a;
