@@ -329,20 +329,23 @@ def workload_extras(K, W, dev, stream):
             c.score(q.view(L * HQ, 128), rec, g, T, T, out=scores.view(L * HQ, T))
         lus = _timed(stream, decode_layers, 3)
         dus = _timed(stream, decode, 5)
-        # PolarQuant keys of the same cache: bulk quantise, one decode step of scoring (all layers, one call)
-        n_k = L * H * T
-        pc = K.PolarCodec(seed=0)
-        pw = pc.alloc_words(n_k, dev)
-        pqus = _timed(stream, lambda i: pc.quantize(flat[:n_k], words=pw), 3)
-        pdus = _timed(stream, lambda i: pc.score(q.view(L * HQ, 128), pw, g, T, T, out=scores.view(L * HQ, T)), 5)
-        del pw, pc
         # decode attention over the compressed keys and values in one call
+        n_k = L * H * T
         krec = K.Record(rec.codes[:n_k], rec.norms[:n_k], rec.signs[:n_k], rec.rnorms[:n_k])
         vrec = K.Record(rec.codes[n_k:], rec.norms[n_k:], rec.signs[n_k:], rec.rnorms[n_k:])
         ws = torch.empty(K.rq_attend_workspace(L * HQ, g, T) + 256, dtype=torch.uint8, device=dev)
         att = torch.empty((L * HQ, 128), dtype=torch.float32, device=dev)
         aus = _timed(stream, lambda i: K.attend(c, c, q.view(L * HQ, 128), krec, vrec, g, T, T, out=att,
                                                 workspace=ws), 5)
+        # PolarQuant keys of the same cache: bulk quantise, one decode step of
+        # scoring (all layers, one call), and attention with those keys
+        pc = K.PolarCodec(seed=0)
+        pw = pc.alloc_words(n_k, dev)
+        pqus = _timed(stream, lambda i: pc.quantize(flat[:n_k], words=pw), 3)
+        pdus = _timed(stream, lambda i: pc.score(q.view(L * HQ, 128), pw, g, T, T, out=scores.view(L * HQ, T)), 5)
+        paus = _timed(stream, lambda i: K.attend(pc, c, q.view(L * HQ, 128), pw, vrec, g, T, T, out=att,
+                                                 workspace=ws), 3)
+        del pw, pc
         nv = flat.shape[0]
         ns = L * HQ * T
         out[spec["name"]] = {
@@ -357,7 +360,8 @@ def workload_extras(K, W, dev, stream):
             "polar_keys_quantize_us": round(pqus, 1),
             "polar_keys_quantize_gbs": round(n_k * (256 + 64) / (pqus * 1e-6) / 1e9, 1),
             "polar_decode_step_us": round(pdus, 1),
-            "polar_decode_scores_per_s": round(ns / (pdus * 1e-6), 1)}
+            "polar_decode_scores_per_s": round(ns / (pdus * 1e-6), 1),
+            "polar_keys_decode_attention_us": round(paus, 1)}
         del kv, q, flat, rec, scores, subs, c, krec, vrec, ws, att
         torch.cuda.empty_cache()
     return out

@@ -226,7 +226,10 @@ int rq_score(rq_ctx* ctx, const float* q, int hq, int group,
  * returns for value t; values are not decoded to vectors (the weighted sums
  * run over centroids and signs, the inverse rotation once per row).
  *   kctx, vctx   sessions of the key and value records (rotor or dense, any
- *                bits and modes; both on the current device).
+ *                bits and modes; both on the current device).  kctx may also
+ *                be an RQ_POLAR session: the keys are then its 16-word
+ *                records in kcodes (knorms, ksigns, krnorms NULL) and s_ht is
+ *                pq_score's <q_h, x~_t>.
  *   q            [hq][128] fp32 queries, 16-byte aligned; hq <= RQ_ATTEND_MAX_ROWS.
  *   group        query rows per KV head, 1 <= group <= RQ_SCORE_CHUNK, hq % group == 0.
  *   k..., v...   records of hq/group KV heads; head j's t keys and values

@@ -463,8 +463,9 @@ class PolarCodec:
 
 def attend(kcodec, vcodec, q, krec, vrec, group, t, kv_stride=None, scale=None, out=None, workspace=None,
            stream=None):
-    """softmax(scale * q.k) . V over compressed keys (kcodec's records) and
-    values (vcodec's records); scale defaults to 1/sqrt(128).  Returns
+    """softmax(scale * q.k) . V over compressed keys (kcodec's records, or a
+    PolarCodec's word tensor) and values (vcodec's records); scale defaults
+    to 1/sqrt(128).  Returns
     [hq, 128] fp32.  The workspace (torch uint8 tensor) is allocated when not
     given; pass one of rq_attend_workspace(hq, group, t) bytes to avoid that."""
     import torch
@@ -481,8 +482,12 @@ def attend(kcodec, vcodec, q, krec, vrec, group, t, kv_stride=None, scale=None, 
     avail = workspace.numel() - (ws - base)
     if out is None:
         out = torch.empty((hq, kcodec.layout["d"]), dtype=torch.float32, device=q.device)
-    rq_attend(kcodec.ctx, vcodec.ctx, q, hq, group, krec.codes, krec.norms, krec.signs, krec.rnorms, vrec.codes,
-              vrec.norms, vrec.signs, vrec.rnorms, t, kv_stride, scale, ws, avail, out, out.stride(0), stream)
+    if isinstance(kcodec, PolarCodec):          # krec: the [n, 16] word records
+        kparts = (krec, None, None, None)
+    else:
+        kparts = (krec.codes, krec.norms, krec.signs, krec.rnorms)
+    rq_attend(kcodec.ctx, vcodec.ctx, q, hq, group, *kparts, vrec.codes, vrec.norms, vrec.signs, vrec.rnorms, t,
+              kv_stride, scale, ws, avail, out, out.stride(0), stream)
     return out
 
 

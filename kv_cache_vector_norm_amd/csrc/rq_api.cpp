@@ -428,6 +428,26 @@ static rqk::ScoreTables score_tables(const rq_ctx* ctx) {
     return st;
 }
 
+static int check_polar(const rq_ctx* ctx, const char* fn) {
+    if (!ctx) return fail(RQ_EINVAL, std::string(fn) + ": ctx is NULL");
+    if (!(ctx->host.lay.mode & RQ_POLAR)) return fail(RQ_EINVAL, std::string(fn) + ": needs an RQ_POLAR session");
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess || cur != ctx->device)
+        return fail(RQ_EINVAL, std::string(fn) + ": current HIP device is not the session's device");
+    return RQ_OK;
+}
+
+static rqk::PolarDev polar_tables(const rq_ctx* c) {
+    rqk::PolarDev p;
+    p.pi_hi = c->pi_hi;
+    p.pi_lo = c->pi_lo;
+    p.pit_hi = c->pit_hi;
+    p.pit_lo = c->pit_lo;
+    p.pi32 = c->pi32;
+    p.tab = c->pq_tab;
+    return p;
+}
+
 static int finish(hipError_t e, const char* fn) { return e == hipSuccess ? RQ_OK : hip_fail(e, fn); }
 
 static int quantize_impl(rq_ctx* ctx, bool dense, const void* x, int x_dtype, int64_t n, int64_t ldx, uint32_t* codes,
@@ -562,7 +582,8 @@ int rq_attend(const rq_ctx* kctx, const rq_ctx* vctx, const float* q, int hq, in
     const char* fn = "rq_attend";
     if (!kctx || !vctx) return fail(RQ_EINVAL, "rq_attend: key and value sessions are required");
     int rc;
-    if ((rc = check_ctx(kctx, kctx->host.lay.mode & RQ_DENSE, fn))) return rc;
+    const bool kpolar = kctx->host.lay.mode & RQ_POLAR;
+    if ((rc = kpolar ? check_polar(kctx, fn) : check_ctx(kctx, kctx->host.lay.mode & RQ_DENSE, fn))) return rc;
     if ((rc = check_ctx(vctx, vctx->host.lay.mode & RQ_DENSE, fn))) return rc;
     if (!q || !aligned(q, 16)) return fail(RQ_EINVAL, "rq_attend: q must be a 16-byte aligned device pointer");
     if (hq < 1 || group < 1 || hq % group) return fail(RQ_EINVAL, "rq_attend: need hq >= 1, group >= 1, hq % group == 0");
@@ -571,7 +592,12 @@ int rq_attend(const rq_ctx* kctx, const rq_ctx* vctx, const float* q, int hq, in
     if (t < 1) return fail(RQ_EINVAL, "rq_attend: softmax over no keys (t < 1)");
     if (t > RQ_ATTEND_MAX_KEYS) return fail(RQ_EINVAL, "rq_attend: t > RQ_ATTEND_MAX_KEYS");
     if (hq / group > 1 && kv_stride < t) return fail(RQ_EINVAL, "rq_attend: kv_stride < t");
-    if ((rc = check_record(kctx, kcodes, knorms, ksigns, krnorms, fn))) return rc;
+    if (kpolar) {
+        if (!kcodes || !aligned(kcodes, 4) || knorms || ksigns || krnorms)
+            return fail(RQ_EINVAL, "rq_attend: PolarQuant keys come as 16-word records in kcodes (knorms, ksigns, krnorms NULL)");
+    } else if ((rc = check_record(kctx, kcodes, knorms, ksigns, krnorms, fn))) {
+        return rc;
+    }
     if ((rc = check_record(vctx, vcodes, vnorms, vsigns, vrnorms, fn))) return rc;
     if (!(scale == scale) || scale > 3.0e38f || scale < -3.0e38f) return fail(RQ_EINVAL, "rq_attend: scale is not finite");
     const rqk::AttendPlan plan = rqk::attend_plan(hq, group, t);
@@ -581,7 +607,18 @@ int rq_attend(const rq_ctx* kctx, const rq_ctx* vctx, const float* q, int hq, in
     if (ld_out < rqh::kDim) return fail(RQ_EINVAL, "rq_attend: ld_out < 128");
     if (vctx->host.lay.mse_bits == 0)
         return fail(RQ_EUNSUPPORTED, "rq_attend: value sessions need at least one MSE bit");
-    const rqk::ScoreTables kt = score_tables(kctx), vt = score_tables(vctx);
+    rqk::ScoreTables kt;
+    if (kpolar) {
+        kt.dense = false;
+        kt.polar = true;
+        kt.pol = polar_tables(kctx);
+        kt.mse_bits = 0;
+        kt.qjl = false;
+        kt.qjl_scale = 0.0f;
+    } else {
+        kt = score_tables(kctx);
+    }
+    const rqk::ScoreTables vt = score_tables(vctx);
     return finish(rqk::attend(kt, vt, q, hq, group, kcodes, knorms, ksigns, krnorms, vcodes, vnorms, vsigns, vrnorms, t,
                               kv_stride, scale, workspace, out, ld_out, static_cast<hipStream_t>(stream)),
                   fn);
@@ -870,26 +907,6 @@ int rq_cache_attend(rq_cache* c, int seq, int layer, const float* q, int hq, flo
 }
 
 // ---------------------------------------------------------- PolarQuant --
-static int check_polar(const rq_ctx* ctx, const char* fn) {
-    if (!ctx) return fail(RQ_EINVAL, std::string(fn) + ": ctx is NULL");
-    if (!(ctx->host.lay.mode & RQ_POLAR)) return fail(RQ_EINVAL, std::string(fn) + ": needs an RQ_POLAR session");
-    int cur = -1;
-    if (hipGetDevice(&cur) != hipSuccess || cur != ctx->device)
-        return fail(RQ_EINVAL, std::string(fn) + ": current HIP device is not the session's device");
-    return RQ_OK;
-}
-
-static rqk::PolarDev polar_tables(const rq_ctx* c) {
-    rqk::PolarDev p;
-    p.pi_hi = c->pi_hi;
-    p.pi_lo = c->pi_lo;
-    p.pit_hi = c->pit_hi;
-    p.pit_lo = c->pit_lo;
-    p.pi32 = c->pi32;
-    p.tab = c->pq_tab;
-    return p;
-}
-
 static int pq_quantize_impl(rq_ctx* ctx, const void* x, int x_dtype, int64_t n, int64_t ldx, uint32_t* words,
                             void* y, int y_dtype, int64_t ldy, bool roundtrip, void* stream, const char* fn) {
     int rc;

@@ -499,9 +499,13 @@ hipError_t attend(const ScoreTables& kt, const ScoreTables& vt, const float* q, 
     float2* stats = reinterpret_cast<float2*>(ws + p.off_stats);
     float* part = reinterpret_cast<float*>(ws + p.off_part);
     const int kv_heads = hq / group;
-    // 1. estimates, in chunks of whole KV heads
+    // 1. estimates, in chunks of whole KV heads (PolarQuant keys: one launch)
+    if (kt.polar) {
+        const hipError_t e = polar_score(kt.pol, q, hq, group, kcodes, t, kv_heads > 1 ? kv_stride : 0, scores, p.ld, s);
+        if (e != hipSuccess) return e;
+    }
     const int heads_per_chunk = group >= kScoreChunkRows ? 1 : kScoreChunkRows / group;
-    for (int h0 = 0; h0 < kv_heads; h0 += heads_per_chunk) {
+    for (int h0 = 0; h0 < (kt.polar ? 0 : kv_heads); h0 += heads_per_chunk) {
         const int nh = kv_heads - h0 < heads_per_chunk ? kv_heads - h0 : heads_per_chunk;
         const hipError_t e = score(kt, q + static_cast<int64_t>(h0) * group * kD, nh * group, group, kcodes, knorms,
                                    ksigns, krnorms, t, kv_stride, h0, scores + static_cast<int64_t>(h0) * group * p.ld,

@@ -51,10 +51,24 @@ struct DenseTables {
     bool qjl;
 };
 
+// PolarQuant sessions (rq_polar.hip): y = Pi x, four levels of polar angle
+// codes and eight half radii in a 16-word record per vector.
+constexpr int kPolarTab = 2 * (7 + 3 + 3 + 3) + 2 * (16 + 4 + 4 + 4);   // floats
+constexpr int kPolarWords = 16;       // u32 words per record
+struct PolarDev {
+    const uint16_t* pi_hi;    // 16 Pi = hi + 2^-11 lo, row-major (y = Pi x)
+    const uint16_t* pi_lo;
+    const uint16_t* pit_hi;   // the same pair transposed (x = Pi^T y)
+    const uint16_t* pit_lo;
+    const float* pi32;        // Pi in fp32, row-major
+    const float* tab;         // kPolarTab floats: (cos, sin) of boundaries, then of centroids
+};
 struct ScoreTables {
     bool dense;
     RotorTables rot;
     DenseTables den;
+    bool polar = false;      // PolarQuant keys (rq_attend only): records are 16-word rows
+    PolarDev pol{};
     int mse_bits;
     bool qjl;
     float qjl_scale;
@@ -126,18 +140,6 @@ hipError_t qjl1_quantize(const Qjl1Dev& P, const void* x, bool in_f16, int64_t l
 hipError_t qjl1_dequantize(const Qjl1Dev& P, const uint16_t* norms, const uint32_t* signs, const uint16_t* rnorms,
                            int64_t n, void* y, bool out_f16, int64_t ldy_bytes, hipStream_t s);
 
-// PolarQuant sessions (rq_polar.hip): y = Pi x, four levels of polar angle
-// codes and eight half radii in a 16-word record per vector.
-constexpr int kPolarTab = 2 * (7 + 3 + 3 + 3) + 2 * (16 + 4 + 4 + 4);   // floats
-constexpr int kPolarWords = 16;       // u32 words per record
-struct PolarDev {
-    const uint16_t* pi_hi;    // 16 Pi = hi + 2^-11 lo, row-major (y = Pi x)
-    const uint16_t* pi_lo;
-    const uint16_t* pit_hi;   // the same pair transposed (x = Pi^T y)
-    const uint16_t* pit_lo;
-    const float* pi32;        // Pi in fp32, row-major
-    const float* tab;         // kPolarTab floats: (cos, sin) of boundaries, then of centroids
-};
 constexpr int kPolarScoreRows = 32;   // query rows per scoring workgroup
 hipError_t polar_quantize(const PolarDev& P, const void* x, bool in_f16, int64_t ldx_bytes, int64_t n,
                           uint32_t* words, void* y, bool out_f16, int64_t ldy_bytes, bool roundtrip, hipStream_t s);

@@ -208,3 +208,22 @@ def boundary_distance(p: PolarParams, diag: PolarDiagnostics):
             t = np.concatenate([[0.0], t, [2.0 * math.pi]])
         out.append(np.min(np.abs(diag.angles[l][..., None] - t), axis=-1))
     return out
+
+
+def attend(p: PolarParams, pv, q, words, vrec, group, t, scale, kv_stride=None):
+    """Decode attention over PolarQuant keys: softmax(scale * <q_h, x~_t>)
+    weighs the values, decoded with their own session (the KV-cache
+    section's softmax(Q K^T / sqrt(d)) V, with the keys read from their
+    PolarQuant records).  Query head h reads KV head j = h // group, whose
+    keys and values start at row j * kv_stride.  Returns [H, d]."""
+    from . import codec as OC
+    kv_stride = t if kv_stride is None else kv_stride
+    q = np.asarray(q, dtype=np.float64)
+    out = np.zeros((q.shape[0], D))
+    for h in range(q.shape[0]):
+        j = h // group
+        rows = slice(j * kv_stride, j * kv_stride + t)
+        s = scale * score(p, q[h:h + 1], np.asarray(words)[rows])[0]
+        e = np.exp(s - s.max())
+        out[h] = (e / e.sum()) @ OC.dequantize(pv, OC._rows(vrec, rows))
+    return out

@@ -179,3 +179,45 @@ def test_polar_strided_rows_and_empty_calls(K, P):
         K.pq_score(c.ctx, q, 2, 1, words, 10, 5, torch.empty((2, 10), device="cuda"), 10)   # kv_stride < t
     with pytest.raises(K.RQError):
         K.pq_score(c.ctx, q, 2, 2, words, 10, 10, torch.empty((2, 10), device="cuda"), 8)   # ld < t
+
+
+@pytest.mark.parametrize("t,kvh,group,vspec", [(777, 2, 4, (3, "mse")), (2049, 4, 8, (3, "qjl")), (100, 1, 40, (4, "dense"))])
+def test_attention_over_polar_keys(K, P, t, kvh, group, vspec):
+    """rq_attend with PolarQuant keys: end to end against the oracle within
+    the bound the score tolerance implies (a score error e moves the
+    softmax weights by at most 2 scale e in total), and with the GPU's own
+    polar scores within 1e-5 of the largest value coordinate."""
+    from oracle import codec as OC
+    from oracle import params as OP
+    mode = {"mse": OP.MSE, "qjl": OP.QJL, "dense": OP.DENSE}[vspec[1]]
+    kc, vc = K.PolarCodec(seed=0), K.Codec(bits=vspec[0], seed=0, mode=mode)
+    keys = W.gaussian(kvh * t, seed=119, dtype=np.float16)
+    vals = W.gaussian(kvh * t, seed=120, dtype=np.float16)
+    q = W.queries(kvh * group, seed=121)
+    kw = kc.quantize(torch.from_numpy(keys).cuda())
+    vrec = vc.quantize(torch.from_numpy(vals).cuda())
+    qd = torch.from_numpy(q).cuda()
+    scale = 1 / np.sqrt(D)
+    out = K.attend(kc, vc, qd, kw, vrec, group, t, t, scale)
+    s = kc.score(qd, kw, group, t)
+    torch.cuda.synchronize()
+    pv = OP.Params(D, vspec[0], 0, mode)
+    gw = _words(kw)
+    hv = PR.record_from_host(*vrec.host())
+    ref = PQ.attend(P, pv, q.astype(np.float64), gw, hv, group, t, scale)
+    got = out.cpu().numpy().astype(np.float64)
+    sg = s.cpu().numpy().astype(np.float64)
+    for h in range(kvh * group):
+        j = h // group
+        xv = OC.dequantize(pv, OC._rows(hv, slice(j * t, (j + 1) * t)))
+        vmax = np.abs(xv).max()
+        rmax = PR.polar_radius_norm(gw[j * t:(j + 1) * t]).max()
+        lim = (2e-4 * scale * np.linalg.norm(q[h]) * rmax + 1e-5) * vmax
+        assert np.abs(got[h] - ref[h]).max() <= lim, (h, np.abs(got[h] - ref[h]).max() / lim)
+        z = scale * sg[h]
+        wgt = np.exp(z - z.max())
+        assert np.abs(got[h] - (wgt / wgt.sum()) @ xv).max() <= 1e-5 * vmax, h
+    # keys must come as word records only
+    with pytest.raises(K.RQError):
+        K.rq_attend(kc.ctx, vc.ctx, qd, kvh * group, group, kw, vrec.norms, None, None, vrec.codes, vrec.norms,
+                    vrec.signs, vrec.rnorms, t, t, scale, 0, 0, out, D)

@@ -117,3 +117,29 @@ def test_score_reads_rotated_coordinates():
     yt = PQ.polar_inverse(angles, PQ._half_value(rb))
     s = PQ.score(p, p.pi[[3, 77]], words)             # rows of Pi = (Pi^T e_j)^T
     assert np.abs(s - yt[:, [3, 77]].T).max() < 1e-5 * np.abs(yt).max()
+
+
+def test_attention_over_polar_keys():
+    """The polar-key attention is the softmax of the scaled polar scores
+    applied to the decoded values: a dominant key returns its value, scale 0
+    the mean of the values (per GQA head)."""
+    from oracle import codec as OC
+    from oracle import params as OP
+    p = PQ.PolarParams(128, 0)
+    pv = OP.Params(128, 3, 0, OP.MSE)
+    t, kvh, group = 20, 2, 3
+    k = W.gaussian(kvh * t, seed=8).astype(np.float64)
+    q = W.queries(kvh * group, seed=9).astype(np.float64)
+    k[7] = 4.0 * q[0]                                   # head 0's dominant key for query row 0
+    words, _ = PQ.quantize(p, k)
+    vrec, _ = OC.quantize(pv, W.gaussian(kvh * t, seed=10).astype(np.float64))
+    xv = OC.dequantize(pv, vrec)
+    out0 = PQ.attend(p, pv, q, words, vrec, group, t, 0.0)
+    for h in range(kvh * group):
+        j = h // group
+        assert np.abs(out0[h] - xv[j * t:(j + 1) * t].mean(0)).max() < 1e-14
+    out = PQ.attend(p, pv, q, words, vrec, group, t, 1.0)
+    s = PQ.score(p, q[:1], words[:t])[0]
+    gap = s[7] - np.max(np.delete(s, 7))
+    assert gap > 30
+    assert np.abs(out[0] - xv[7]).max() < t * np.exp(-gap) * np.abs(xv).max() + 1e-12
