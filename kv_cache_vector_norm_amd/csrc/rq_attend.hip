@@ -115,10 +115,14 @@ __device__ __forceinline__ void split_pair11(float a, float b, uint32_t* hi, uin
     *lo11 = cvt_pk((a - h2f(h & 0xFFFFu)) * 2048.0f, (b - h2f(h >> 16)) * 2048.0f);
 }
 
-template <int B, bool QJL, bool PAD>
+// CODES: the centroid sums (codes and norms are read); QJL: the sign sums
+// (signs, norms and residual norms).  A QJL value session runs two passes,
+// one of each, writing disjoint columns of the partial rows: each pass
+// holds half the accumulators, so two waves fit on a SIMD.
+template <int B, bool QJL, bool PAD, bool CODES = true>
 __global__ __launch_bounds__(256) void attend_values_kernel(AttendArgs a) {
     constexpr int L = 1 << B;
-    constexpr int W = (((PAD ? kRotCoords : kD) * B) + 31) / 32;
+    constexpr int W = CODES ? (((PAD ? kRotCoords : kD) * B) + 31) / 32 : 1;
     struct alignas(16) Wave {
         uint32_t code[W + 1][64];   // [word][key]; one spare word row for the straddle read
         uint32_t sign[4][64];
@@ -140,8 +144,8 @@ __global__ __launch_bounds__(256) void attend_values_kernel(AttendArgs a) {
     const int64_t rbase = static_cast<int64_t>(kvh) * a.kv_stride;
     const int64_t ntiles = (a.t + 63) / 64;
 
-    float sc;
-    {
+    float sc = 1.0f;
+    if constexpr (CODES) {
         const float cmax = fmaxf(fabsf(a.cent[L - 1]), fabsf(a.cent[0]));
         int e;
         frexpf(cmax, &e);
@@ -198,10 +202,13 @@ __global__ __launch_bounds__(256) void attend_values_kernel(AttendArgs a) {
             const int64_t pg = a.pt.pages[kvh * a.pt.stride + (kbase >> a.pt.shift)];
             row = (pg << a.pt.shift) + (kbase & ((int64_t(1) << a.pt.shift) - 1));
         }
-        const rsrc_t rc = make_rsrc(a.codes + row * W, tile_range(left, 4 * W));
+        if constexpr (CODES) {
+            const rsrc_t rc = make_rsrc(a.codes + row * W, tile_range(left, 4 * W));
 #pragma unroll
-        for (int it = 0; it < W; ++it)
-            r.cw[it] = __builtin_amdgcn_raw_buffer_load_b32(rc, static_cast<uint32_t>(4 * l), 256 * it, kNonTemporal);
+            for (int it = 0; it < W; ++it)
+                r.cw[it] = __builtin_amdgcn_raw_buffer_load_b32(rc, static_cast<uint32_t>(4 * l), 256 * it,
+                                                                kNonTemporal);
+        }
         if constexpr (QJL) {
             const rsrc_t rs = make_rsrc(a.signs + row * 4, tile_range(left, 16));
 #pragma unroll
@@ -230,10 +237,12 @@ __global__ __launch_bounds__(256) void attend_values_kernel(AttendArgs a) {
         }
         // the tile's value records into LDS, key-minor
         wave_lds_sync();
+        if constexpr (CODES) {
 #pragma unroll
-        for (int it = 0; it < W; ++it) {
-            const int d = it * 64 + l;
-            wv.code[d % W][d / W] = nx.cw[it];
+            for (int it = 0; it < W; ++it) {
+                const int d = it * 64 + l;
+                wv.code[d % W][d / W] = nx.cw[it];
+            }
         }
         if constexpr (QJL) {
 #pragma unroll
@@ -273,9 +282,11 @@ __global__ __launch_bounds__(256) void attend_values_kernel(AttendArgs a) {
                     }
                 }
                 uint32_t h, lo;
-                split_pair11(w2[0], w2[1], &h, &lo);
-                wh[q] = h;
-                wl[q] = lo;
+                if constexpr (CODES) {
+                    split_pair11(w2[0], w2[1], &h, &lo);
+                    wh[q] = h;
+                    wl[q] = lo;
+                }
                 if constexpr (QJL) {
                     split_pair11(g2[0], g2[1], &h, &lo);
                     gwh[q] = h;
@@ -284,7 +295,7 @@ __global__ __launch_bounds__(256) void attend_values_kernel(AttendArgs a) {
             }
             // centroid operands: coordinate 32 nt + n (nt < 4), pad slot (nt = 4)
 #pragma unroll
-            for (int nt = 0; nt < (PAD ? 5 : 4); ++nt) {
+            for (int nt = 0; nt < (CODES ? (PAD ? 5 : 4) : 0); ++nt) {
                 const int coord = nt < 4 ? 32 * nt + n : 128;
                 const int bit = B * coord, wi = bit >> 5, off = bit & 31;
                 const u32x4 w0a = *reinterpret_cast<const u32x4*>(&wv.code[wi][k0]);
@@ -360,14 +371,16 @@ __global__ __launch_bounds__(256) void attend_values_kernel(AttendArgs a) {
                     float* dst = lds.sum[m];
 #pragma unroll
                     for (int nt = 0; nt < 4; ++nt) {
-                        const float c = acc_c[nt][r] * uc;
-                        dst[32 * nt + n] = w == 0 ? c : dst[32 * nt + n] + c;
+                        if constexpr (CODES) {
+                            const float c = acc_c[nt][r] * uc;
+                            dst[32 * nt + n] = w == 0 ? c : dst[32 * nt + n] + c;
+                        }
                         if constexpr (QJL) {
                             const float g = acc_s[nt][r] * us;
                             dst[kPartSigma + 32 * nt + n] = w == 0 ? g : dst[kPartSigma + 32 * nt + n] + g;
                         }
                     }
-                    if (n == 0) {
+                    if (CODES && n == 0) {
                         const float pc = PAD ? acc_p[r] * uc : 0.0f;
                         dst[kPartPad] = w == 0 ? pc : dst[kPartPad] + pc;
                     }
@@ -377,10 +390,13 @@ __global__ __launch_bounds__(256) void attend_values_kernel(AttendArgs a) {
         __syncthreads();
     }
     float* out = a.part + (static_cast<int64_t>(blockIdx.x) * a.rows + row0) * kPartStride;
+    // columns of this pass: the sign sums (QJL), or the centroid sums, the
+    // pad slot and the spare columns (CODES)
     for (int i = threadIdx.x; i < nrows * kPartStride; i += kBlock) {
         const int m = i / kPartStride, c = i % kPartStride;
-        out[static_cast<int64_t>(m) * kPartStride + c] = (c < kPartPad + 1 && (QJL || c < kPartSigma || c == kPartPad))
-                                                             ? lds.sum[m][c] : 0.0f;
+        const bool sig = c >= kPartSigma && c < kPartSigma + kD;
+        if (sig ? QJL : CODES)
+            out[static_cast<int64_t>(m) * kPartStride + c] = (sig || c < kPartSigma || c == kPartPad) ? lds.sum[m][c] : 0.0f;
     }
 }
 
@@ -470,10 +486,13 @@ AttendPlan attend_plan(int hq, int group, int64_t t) {
     return p;
 }
 
+// Centroid sums, then (QJL) sign sums: two passes over the tiles.
 template <int B, bool QJL, bool PAD>
 static void launch_values(const AttendArgs& a, const AttendPlan& p, int kv_heads, hipStream_t s) {
     const int qblocks = (a.group + 31) / 32;
-    hipLaunchKernelGGL((attend_values_kernel<B, QJL, PAD>), dim3(p.gx, kv_heads * qblocks), dim3(kBlock), 0, s, a);
+    const dim3 grid(p.gx, kv_heads * qblocks);
+    hipLaunchKernelGGL((attend_values_kernel<B, false, PAD, true>), grid, dim3(kBlock), 0, s, a);
+    if constexpr (QJL) hipLaunchKernelGGL((attend_values_kernel<1, true, false, false>), grid, dim3(kBlock), 0, s, a);
 }
 
 template <bool QJL, bool PAD>
