@@ -540,6 +540,9 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int rowc = 32 * m + 8 * (r / 4) + (r % 4);   // row without the lane-half term 4 hh
+                if constexpr (NMT == 1) {
+                    if (rowc >= nrows) continue;   // no lane holds a live row (small GQA groups)
+                }
                 const float* rsv = lds.rsc[rowc + 4 * hh];
                 const float s0 = rsv[0], s1 = rsv[1], s2 = rsv[2];
 #pragma unroll
