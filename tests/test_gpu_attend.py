@@ -156,3 +156,38 @@ def test_attend_rejects_bad_arguments(K):
     with pytest.raises(K.RQError):
         K.attend(kc, vc, q, krec, vrec, 4, 10, workspace=small)     # workspace too small
     assert K.rq_attend_workspace(4, 3, 10) == -1
+
+
+def test_attend_at_the_key_limit(K):
+    """t = RQ_ATTEND_MAX_KEYS (2^23 keys for one KV head, 4 query rows):
+    the output equals softmax(scale * s_gpu) . dequantize(v) evaluated in
+    float64 on the device from the GPU's own estimates and dequantised
+    values (chunks of 2^20 values), within 1e-5 max |v~|; one key more is
+    rejected before any launch."""
+    t, group = 1 << 23, 4
+    assert K.rq_attend_workspace(4, 4, t) > 0
+    kc, vc = K.Codec(bits=3, seed=0, mode=OP.QJL), K.Codec(bits=3, seed=0, mode=OP.MSE)
+    g = torch.Generator(device="cuda").manual_seed(82)
+    krec = kc.quantize(torch.randn((t, D), generator=g, device="cuda").to(torch.float16))
+    vrec = vc.quantize(torch.randn((t, D), generator=g, device="cuda").to(torch.float16))
+    q = torch.from_numpy(W.queries(group, seed=83)).cuda()
+    scale = 1 / np.sqrt(D)
+    out = K.attend(kc, vc, q, krec, vrec, group, t, t, scale)
+    s = kc.score(q, krec, group, t).to(torch.float64)
+    z = scale * s
+    p = torch.exp(z - z.max(dim=1, keepdim=True).values)
+    p = p / p.sum(dim=1, keepdim=True)
+    ref = torch.zeros((group, D), dtype=torch.float64, device="cuda")
+    vmax = 0.0
+    step = 1 << 20
+    for i in range(0, t, step):
+        sub = K.Record(vrec.codes[i:i + step], vrec.norms[i:i + step])
+        xv = vc.dequantize(sub, dtype=torch.float32).to(torch.float64)
+        ref += p[:, i:i + step] @ xv
+        vmax = max(vmax, float(xv.abs().max()))
+    torch.cuda.synchronize()
+    err = float((out.to(torch.float64) - ref).abs().max())
+    assert err <= OUT_TOL * vmax, (err, vmax)
+    with pytest.raises(K.RQError):
+        K.attend(kc, vc, q, krec, vrec, group, t + 1, t + 1, scale)
+    assert K.rq_attend_workspace(4, 4, t + 1) == -1
