@@ -28,6 +28,7 @@ constexpr int kGroups = 43;    // ceil(128 / 3) rotor groups
 constexpr int kRotCoords = 129;
 constexpr int kWave = 64;
 constexpr int kTileBytes = 64 * 256;   // one wave's LDS transpose tile
+constexpr int kSimds = 256 * 4;         // MI355X: 256 compute units of 4 SIMDs
 
 // Compile-time loop: f(integral_constant<int, I>) for I in [I0, N).  The
 // per-group loops use it instead of #pragma unroll, whose size limit a long
@@ -229,6 +230,24 @@ __device__ __forceinline__ void tile_store(char* __restrict__ dst, int64_t ld_by
     }
 }
 
+// Writes chunks c0 .. c0 + 3 (64 bytes) of the LDS tile's 64 rows: lane l
+// moves chunk c0 + l % 4 of rows l / 4 + 16 k.  Lets a kernel store each
+// finished quarter of fp16 output rows while it computes the next.
+__device__ __forceinline__ void tile_store_cols(char* __restrict__ dst, int64_t ld_bytes, int64_t base, int64_t n,
+                                                const u32x4* __restrict__ tile, int l, int c0) {
+    const int rr = l >> 2, c = c0 + (l & 3);
+    const uint32_t voff = static_cast<uint32_t>(rr) * static_cast<uint32_t>(ld_bytes) + static_cast<uint32_t>(c * 16);
+    const rsrc_t rs = make_rsrc(dst + base * ld_bytes, tile_range(n - base, ld_bytes));
+    const int step = static_cast<int>(16 * ld_bytes);
+    u32x4 v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = tile[swz(rr + 16 * k, c)];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) __builtin_amdgcn_raw_buffer_store_b128(v[k], rs, voff, k * step, kNonTemporal);
+    store_data_fence();
+}
+
 // Record rows of `words` u32 per vector are contiguous, so a tile's rows form
 // one run of 64 * words dwords: stage through LDS (row-major, stride `words`,
 // odd or small strides are conflict-free for dword access) and copy the run.
@@ -407,6 +426,11 @@ struct VecOutT<true> {
     __device__ void store(char* y, int64_t ld_bytes, int64_t base, int64_t n) {
         wave_lds_sync();
         tile_store(y, ld_bytes, base, n, 0, t, l);
+    }
+    // coordinates 8 c0 .. 8 c0 + 31 of every row, once all lanes have set them
+    __device__ void store_cols(char* y, int64_t ld_bytes, int64_t base, int64_t n, int c0) {
+        wave_lds_sync();
+        tile_store_cols(y, ld_bytes, base, n, t, l, c0);
     }
 };
 

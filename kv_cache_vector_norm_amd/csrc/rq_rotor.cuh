@@ -225,9 +225,10 @@ __device__ __forceinline__ void sigma_from_words(const u32x4 (&wv)[2], u32x4 (&s
 
 // Reconstruction with the QJL term: out_j = n^ (x~_j + k (S^T sigma)_j),
 // evaluated as (n^ / D) * fma(k D, u_j, D x~_j).  xt holds D x~ (own vector).
-template <class Out>
+// done(mt) runs once the outputs of M tile mt (coordinates 32 mt ..) are set.
+template <class Out, class Done>
 __device__ __forceinline__ void back_out(const u32x4* __restrict__ sb, const u32x4 (&sig)[2][8], float kq, float ns,
-                                         const float (&xt)[kD], Out& out, int l) {
+                                         const float (&xt)[kD], Out& out, int l, Done done) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
         f32x16 a0 = {}, a1 = {};
@@ -249,7 +250,13 @@ __device__ __forceinline__ void back_out(const u32x4* __restrict__ sb, const u32
             const int j = 32 * mt + 16 + r;
             out.set2(j, ns * __builtin_fmaf(kq, u1[r], xt[j]), ns * __builtin_fmaf(kq, u1[r + 1], xt[j + 1]));
         }
+        done(mt);
     }
+}
+template <class Out>
+__device__ __forceinline__ void back_out(const u32x4* __restrict__ sb, const u32x4 (&sig)[2][8], float kq, float ns,
+                                         const float (&xt)[kD], Out& out, int l) {
+    back_out(sb, sig, kq, ns, xt, out, l, [](int) {});
 }
 
 // S^T sigma of the own vector into u (coordinate order).
@@ -391,6 +398,9 @@ __global__ __launch_bounds__(256) void rq_quant_kernel(RotorDev P, const char* _
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t ntiles = (n + 63) / 64;
     const int64_t t0 = blockIdx.x * 4LL + wave;
+    // at most one tile per SIMD in the whole launch: no other wave can
+    // overlap this one's stores, so the output leaves in quarters
+    const bool single = ntiles <= kSimds;
     // the first tile's input is requested before the block's staging, so the
     // two latencies overlap
     TileRegs first;
@@ -570,9 +580,28 @@ __global__ __launch_bounds__(256) void rq_quant_kernel(RotorDev P, const char* _
                     }
                 });
             }
+            // When the launch has at most one tile per SIMD (small batches,
+            // where nothing else overlaps the stores), fp16 output of the MSE roundtrip
+            // leaves a quarter of each row at a time: coordinates 32 m ..
+            // 32 m + 31 are complete after group (32 m + 31) / 3.  Larger
+            // batches store whole rows, which HBM writes more efficiently.
+            if constexpr (ROUNDTRIP && !QJL && OUT_F16) {
+                if (single) {
+                    if constexpr (g == 10) out.store_cols(y, ldy_bytes, base, n, 0);
+                    if constexpr (g == 21) out.store_cols(y, ldy_bytes, base, n, 4);
+                    if constexpr (g == 31) out.store_cols(y, ldy_bytes, base, n, 8);
+                }
+            }
         });
 
-        if constexpr (ROUNDTRIP && !QJL) out.store(y, ldy_bytes, base, n);   // frees the tile for the record
+        if constexpr (ROUNDTRIP && !QJL) {      // frees the tile for the record
+            if constexpr (OUT_F16) {
+                if (single) out.store_cols(y, ldy_bytes, base, n, 12);
+                else out.store(y, ldy_bytes, base, n);
+            } else {
+                out.store(y, ldy_bytes, base, n);
+            }
+        }
 
         uint32_t sw[4] = {0u, 0u, 0u, 0u};
         uint32_t gh = 0u;
@@ -604,8 +633,14 @@ __global__ __launch_bounds__(256) void rq_quant_kernel(RotorDev P, const char* _
             VecOutT<OUT_F16> o2;
             if constexpr (!OUT_F16) o2.bind(y, ldy_bytes, base, n);
             o2.begin(tile, l);
-            back_out(s_back, sig, kq, ns, xt, o2, l);
-            o2.store(y, ldy_bytes, base, n);
+            // with at most one tile per SIMD, fp16 rows leave a quarter at a
+            // time, each while the next is computed; else whole rows
+            back_out(s_back, sig, kq, ns, xt, o2, l, [&](int mt) {
+                if constexpr (OUT_F16) {
+                    if (single) o2.store_cols(y, ldy_bytes, base, n, 4 * mt);
+                }
+            });
+            if (!OUT_F16 || !single) o2.store(y, ldy_bytes, base, n);
         }
     }
 }

@@ -184,3 +184,20 @@ def test_65536_keys_full_parity(K):
     PR.compare_signs(p, signs, diag, excl)
     PR.compare_recon(y.cpu().numpy(), OC.dequantize(p, PR.record_from_host(codes, norms, signs, rnorms)),
                      OC.half_value(norms), "dequantize")
+
+
+@pytest.mark.parametrize("bits,mode,n", [(3, OP.MSE, 600_000), (3, OP.QJL, 300_000), (4, OP.DENSE, 300_000)])
+def test_roundtrip_with_several_tiles_per_wave(K, bits, mode, n):
+    """Batches large enough that each wave of the roundtrip handles more than
+    one 64-vector tile (the whole-row output path): the record equals
+    rq_quantize's and the output equals rq_dequantize of it, bit for bit."""
+    c = K.Codec(bits=bits, seed=0, mode=mode)
+    g = torch.Generator(device="cuda").manual_seed(5)
+    x = torch.randn((n, D), generator=g, device="cuda").to(torch.float16)
+    rec, y = c.roundtrip(x, dtype=torch.float16)
+    rec2 = c.quantize(x)
+    d = c.dequantize(rec, dtype=torch.float16)
+    torch.cuda.synchronize()
+    for a, b in zip((rec.codes, rec.norms, rec.signs, rec.rnorms), (rec2.codes, rec2.norms, rec2.signs, rec2.rnorms)):
+        assert (a is None and b is None) or torch.equal(a, b)
+    assert torch.equal(y, d)
