@@ -86,10 +86,11 @@ __device__ __forceinline__ void put_pair(uint32_t (&arr)[64], int i, uint32_t h)
 // coordinate index of own register (h, r) in M tile MT
 __device__ __forceinline__ constexpr int own_coord(int mt, int h, int r) { return 32 * mt + own_row(h, r); }
 
-template <int B, bool QJL, class Out, class SColFrag>
+// done(mt) runs once coordinates 32 mt .. 32 mt + 31 are set.
+template <int B, bool QJL, class Out, class SColFrag, class Done>
 __device__ __forceinline__ void dense_dequant_vec(const DenseDev& P, const uint32_t* __restrict__ ctab,
                                                   const uint32_t (&cw)[(128 * B + 31) / 32], float nhat, float ghat,
-                                                  const uint32_t (&sw)[4], SColFrag scol, Out& out, int l) {
+                                                  const uint32_t (&sw)[4], SColFrag scol, Out& out, int l, Done done) {
     constexpr int W = (128 * B + 31) / 32;
     // y^ = c[code] as split pairs (ctab: lo 16 bits = hi half, hi 16 bits = 2^11 hi; ctab[L + k] = lo)
     uint32_t yh11[64], yh[64], yl[64];
@@ -139,6 +140,7 @@ __device__ __forceinline__ void dense_dequant_vec(const DenseDev& P, const uint3
             if constexpr (QJL) v = __builtin_fmaf(k, w < 4 ? q0[4 * b8 + w] : q1[4 * b8 + w - 4], xv);
             out.set(32 * MT + il, nhat * v);
         }
+        done(MT);
     };
     tile(std::integral_constant<int, 0>{});
     tile(std::integral_constant<int, 1>{});
@@ -190,6 +192,7 @@ __global__ __launch_bounds__(WAVES * 64) void tq_quant_kernel(DenseDev P, const 
     u32x4* tile = sm.tiles[wave];
     uint32_t* stage = reinterpret_cast<uint32_t*>(tile);
     const int64_t ntiles = (n + 63) / 64;
+    const bool single = ntiles <= kSimds;   // at most one tile per SIMD: output leaves in quarters
     for (int64_t t = blockIdx.x * (int64_t)WAVES + wave; t < ntiles; t += gridDim.x * (int64_t)WAVES) {
         const int64_t base = t * 64;
         const int z = opaque_zero();
@@ -371,9 +374,14 @@ __global__ __launch_bounds__(WAVES * 64) void tq_quant_kernel(DenseDev P, const 
             VecOutT<OUT_F16> out;
             if constexpr (!OUT_F16) out.bind(y, ldy_bytes, base, n);
             out.begin(tile, l);
-            dense_dequant_vec<B, QJL>(P, sm.ctab, cw, nhat, ghat, sw,
-                                      [&](int row, int chunk) { return gmat_frag(P.s_cols, row, chunk); }, out, l);
-            out.store(y, ldy_bytes, base, n);
+            dense_dequant_vec<B, QJL>(
+                P, sm.ctab, cw, nhat, ghat, sw, [&](int row, int chunk) { return gmat_frag(P.s_cols, row, chunk); },
+                out, l, [&](int mt) {
+                    if constexpr (OUT_F16) {
+                        if (single) out.store_cols(y, ldy_bytes, base, n, 4 * mt);
+                    }
+                });
+            if (!OUT_F16 || !single) out.store(y, ldy_bytes, base, n);
         }
     }
 }
@@ -394,6 +402,7 @@ __global__ __launch_bounds__(256) void tq_dequant_kernel(DenseDev P, const uint3
     u32x4* tile = tiles[wave];
     uint32_t* stage = reinterpret_cast<uint32_t*>(tile);
     const int64_t ntiles = (n + 63) / 64;
+    const bool single = ntiles <= kSimds;
     for (int64_t t = blockIdx.x * 4LL + wave; t < ntiles; t += gridDim.x * 4LL) {
         const int64_t base = t * 64;
         const int z = opaque_zero();
@@ -411,9 +420,14 @@ __global__ __launch_bounds__(256) void tq_dequant_kernel(DenseDev P, const uint3
         VecOutT<OUT_F16> out;
         if constexpr (!OUT_F16) out.bind(y, ldy_bytes, base, n);
         out.begin(tile, l);
-        dense_dequant_vec<B, QJL>(P, ctab, cw, nhat, ghat, sw,
-                                  [&](int row, int chunk) { return gmat_frag(P.s_cols, row, chunk); }, out, l);
-        out.store(y, ldy_bytes, base, n);
+        dense_dequant_vec<B, QJL>(
+            P, ctab, cw, nhat, ghat, sw, [&](int row, int chunk) { return gmat_frag(P.s_cols, row, chunk); }, out, l,
+            [&](int mt) {
+                if constexpr (OUT_F16) {
+                    if (single) out.store_cols(y, ldy_bytes, base, n, 4 * mt);
+                }
+            });
+        if (!OUT_F16 || !single) out.store(y, ldy_bytes, base, n);
     }
 }
 

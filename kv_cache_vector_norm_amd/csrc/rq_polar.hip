@@ -175,10 +175,11 @@ __device__ __forceinline__ float pq_decode_split(const float2* __restrict__ tab,
     return rn;
 }
 
-// x~ = Pi^T y~ of one record into `out` (coordinates in increasing order).
-template <class Out>
+// x~ = Pi^T y~ of one record into `out` (coordinates in increasing order);
+// done(mt) runs once coordinates 32 mt .. 32 mt + 31 are set.
+template <class Out, class Done>
 __device__ __forceinline__ void pq_dequant_vec(const PolarDev& P, const float2* __restrict__ tab,
-                                               const uint32_t (&w)[kPolarWords], Out& out, int l) {
+                                               const uint32_t (&w)[kPolarWords], Out& out, int l, Done done) {
     uint32_t yh11[64], yh[64], yl[64];
     const float rn = pq_decode_split(tab, w, yh11, yh, yl) * kRotScale;
     auto tile = [&](auto mt_c) {
@@ -193,6 +194,7 @@ __device__ __forceinline__ void pq_dequant_vec(const PolarDev& P, const float2* 
             const float xv = k < 4 ? x0[4 * b8 + k] : x1[4 * b8 + k - 4];
             out.set(32 * MT + il, rn * xv);
         }
+        done(MT);
     };
     tile(std::integral_constant<int, 0>{});
     tile(std::integral_constant<int, 1>{});
@@ -218,6 +220,7 @@ __global__ __launch_bounds__(kPqWaves * 64) void pq_quant_kernel(PolarDev P, con
     __shared__ PqQuantLds sm;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t ntiles = (n + 63) / 64;
+    const bool single = ntiles <= kSimds;   // at most one tile per SIMD: output leaves in quarters
     const int64_t tstep = gridDim.x * (int64_t)kPqWaves;
     // fp16 input is fetched one tile ahead (the first one before the block's
     // staging), so each tile's load latency hides behind the previous tile
@@ -322,8 +325,12 @@ __global__ __launch_bounds__(kPqWaves * 64) void pq_quant_kernel(PolarDev P, con
             VecOutT<OUT_F16> out;
             if constexpr (!OUT_F16) out.bind(y, ldy_bytes, base, n);
             out.begin(tile, l);
-            pq_dequant_vec(P, sm.tab, w, out, l);
-            out.store(y, ldy_bytes, base, n);
+            pq_dequant_vec(P, sm.tab, w, out, l, [&](int mt) {
+                if constexpr (OUT_F16) {
+                    if (single) out.store_cols(y, ldy_bytes, base, n, 4 * mt);
+                }
+            });
+            if (!OUT_F16 || !single) out.store(y, ldy_bytes, base, n);
         }
     }
 }
@@ -340,6 +347,7 @@ __global__ __launch_bounds__(kPqWaves * 64) void pq_dequant_kernel(PolarDev P, c
     u32x4* tile = tiles[wave];
     uint32_t* stage = reinterpret_cast<uint32_t*>(tile);
     const int64_t ntiles = (n + 63) / 64;
+    const bool single = ntiles <= kSimds;
     for (int64_t t = blockIdx.x * (int64_t)kPqWaves + wave; t < ntiles; t += gridDim.x * (int64_t)kPqWaves) {
         const int64_t base = t * 64;
         const int z = opaque_zero();
@@ -349,8 +357,12 @@ __global__ __launch_bounds__(kPqWaves * 64) void pq_dequant_kernel(PolarDev P, c
         VecOutT<OUT_F16> out;
         if constexpr (!OUT_F16) out.bind(y, ldy_bytes, base, n);
         out.begin(tile, l);
-        pq_dequant_vec(P, tab, w, out, l);
-        out.store(y, ldy_bytes, base, n);
+        pq_dequant_vec(P, tab, w, out, l, [&](int mt) {
+            if constexpr (OUT_F16) {
+                if (single) out.store_cols(y, ldy_bytes, base, n, 4 * mt);
+            }
+        });
+        if (!OUT_F16 || !single) out.store(y, ldy_bytes, base, n);
     }
 }
 

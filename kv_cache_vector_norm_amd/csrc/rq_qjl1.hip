@@ -32,6 +32,7 @@ __global__ __launch_bounds__(256) void qjl1_quant_kernel(Qjl1Dev P, const char* 
     u32x4* tile = lds.tiles[wave];
     uint32_t* stage = reinterpret_cast<uint32_t*>(tile);
     const int64_t ntiles = (n + 63) / 64;
+    const bool single = ntiles <= kSimds;   // at most one tile per SIMD: output leaves in quarters
     for (int64_t t = blockIdx.x * 4LL + wave; t < ntiles; t += gridDim.x * 4LL) {
         const int64_t base = t * 64;
         const int l = lane_id() + opaque_zero();
@@ -87,8 +88,12 @@ __global__ __launch_bounds__(256) void qjl1_quant_kernel(Qjl1Dev P, const char* 
             VecOutT<OUT_F16> out;
             if constexpr (!OUT_F16) out.bind(y, ldy_bytes, base, n);
             out.begin(tile, l);
-            back_out(lds.s_back, sig, (P.qjl_scale * ghat) * D, nhat * (1.0f / D), zero, out, l);
-            out.store(y, ldy_bytes, base, n);
+            back_out(lds.s_back, sig, (P.qjl_scale * ghat) * D, nhat * (1.0f / D), zero, out, l, [&](int mt) {
+                if constexpr (OUT_F16) {
+                    if (single) out.store_cols(y, ldy_bytes, base, n, 4 * mt);
+                }
+            });
+            if (!OUT_F16 || !single) out.store(y, ldy_bytes, base, n);
         }
     }
 }
@@ -110,6 +115,7 @@ __global__ __launch_bounds__(256) void qjl1_dequant_kernel(Qjl1Dev P, const uint
     u32x4* tile = lds.tiles[wave];
     uint32_t* stage = reinterpret_cast<uint32_t*>(tile);
     const int64_t ntiles = (n + 63) / 64;
+    const bool single = ntiles <= kSimds;   // at most one tile per SIMD: output leaves in quarters
     for (int64_t t = blockIdx.x * 4LL + wave; t < ntiles; t += gridDim.x * 4LL) {
         const int64_t base = t * 64;
         const int l = lane_id() + opaque_zero();
@@ -123,8 +129,12 @@ __global__ __launch_bounds__(256) void qjl1_dequant_kernel(Qjl1Dev P, const uint
         VecOutT<OUT_F16> out;
         if constexpr (!OUT_F16) out.bind(y, ldy_bytes, base, n);
         out.begin(tile, l);
-        back_out(lds.s_back, sig, (P.qjl_scale * ghat) * D, nhat * (1.0f / D), zero, out, l);
-        out.store(y, ldy_bytes, base, n);
+        back_out(lds.s_back, sig, (P.qjl_scale * ghat) * D, nhat * (1.0f / D), zero, out, l, [&](int mt) {
+            if constexpr (OUT_F16) {
+                if (single) out.store_cols(y, ldy_bytes, base, n, 4 * mt);
+            }
+        });
+        if (!OUT_F16 || !single) out.store(y, ldy_bytes, base, n);
     }
 }
 
