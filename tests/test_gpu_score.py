@@ -82,3 +82,22 @@ def test_score_rejects_bad_group(K):
     q = torch.zeros((6, D), device="cuda")
     with pytest.raises(K.RQError):
         c.score(q, rec, 4, 10)
+
+
+@pytest.mark.parametrize("col0,pad", [(0, 4), (4, 8), (1, 6), (3, 1), (2, 2)])
+def test_score_into_strided_rows(K, col0, pad):
+    """Scores written into columns col0 .. col0 + t of wider rows equal the
+    dense output bit for bit, and nothing outside those columns changes
+    (rows wider than t, and rows that are not 16-byte aligned)."""
+    t, hq, group = 1000, 8, 4
+    keys = W.gaussian(2 * t, seed=31, dtype=np.float16)
+    q = torch.from_numpy(W.queries(hq, seed=32)).cuda()
+    c = K.Codec(bits=3, seed=0, mode=OP.QJL)
+    rec = c.quantize(torch.from_numpy(keys).cuda())
+    dense = c.score(q, rec, group, t)
+    big = torch.full((hq, col0 + t + pad), float("nan"), device="cuda")
+    out = big[:, col0:col0 + t]
+    c.score(q, rec, group, t, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, dense)
+    assert torch.isnan(big[:, :col0]).all() and torch.isnan(big[:, col0 + t:]).all()
