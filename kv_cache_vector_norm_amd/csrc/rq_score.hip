@@ -355,8 +355,21 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
     constexpr int WA = W > 0 ? W : 1;   // B = 0: QJL-only keys, no code words
     constexpr int SW = W > 4 ? W : 4;
     constexpr int ROWS = NMT * 32;
+    // 1- and 2-bit codes: four codes (one byte or nibble of the stream) select
+    // two dwords of C_hi halves and two of C_lo halves, which land in the MFMA
+    // operand as they are; wider codes go by pairs.  Sign bytes map to their
+    // four +-1 dwords through a table while LDS stays within two blocks per CU.
+    constexpr bool QUAD = B == 1 || B == 2;
+    constexpr int NQ = QUAD ? 1 << (4 * B) : 1;
+    // C_lo entries start 2056 bytes after the C_hi ones: no two-address LDS
+    // read can fetch a C_hi and a C_lo entry together, so each 8-byte read
+    // lands in its own half of an MFMA operand without register moves
+    constexpr int QLO = QUAD ? 257 : 1;
+    constexpr bool STAB = QJL && B <= 3;
     struct Lds {
         uint32_t pairs[L * L][2];     // codes (a, b) -> {C_hi[a] | C_hi[b] << 16, C_lo[a] | C_lo[b] << 16}
+        uint2 quad[QLO + NQ];         // codes (a, b, c, d) -> C_hi halves at [p], C_lo halves at [QLO + p]
+        u32x4 sigt[STAB ? 256 : 1];   // sign byte -> sigma8
         float rsc[ROWS][4];           // {1 / (2^11 s_q s_c), 1 / (2^11 s_p), q^_128, 0}
         float cent[L];
         float s0[ROWS];               // power of two putting max |q| of a row in [1, 2)
@@ -399,6 +412,18 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
             split_h11(a.cent[p >> B] * sc, &h1, &l1);
             lds.pairs[p][0] = h0 | (h1 << 16);
             lds.pairs[p][1] = l0 | (l1 << 16);
+        }
+        if constexpr (QUAD) {
+            for (int p = threadIdx.x; p < NQ; p += kBlock) {
+                uint32_t h[4], o[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) split_h11(a.cent[(p >> (B * i)) & (L - 1)] * sc, &h[i], &o[i]);
+                lds.quad[p] = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+                lds.quad[QLO + p] = make_uint2(o[0] | (o[1] << 16), o[2] | (o[3] << 16));
+            }
+        }
+        if constexpr (STAB) {
+            for (int p = threadIdx.x; p < 256; p += kBlock) lds.sigt[p] = sigma8(static_cast<uint32_t>(p));
         }
         if (threadIdx.x < L) lds.cent[threadIdx.x] = a.cent[threadIdx.x];
     }
@@ -476,6 +501,19 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
             for (int kb = 0; kb < 8; ++kb) {
                 // (no scheduling barrier: lookups of the next block may move up)
                 u32x4 ch[2], cl[2];
+                if constexpr (QUAD) {
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt) {
+                        // this lane's eight slots of block kb: 8 B bits (cs is pre-shifted by 8 B hh)
+                        const int bit = 16 * B * kb;
+                        const uint32_t f = cs[nt][bit >> 5] >> (bit & 31);
+                        const uint32_t i0 = f & (NQ - 1), i1 = (f >> (4 * B)) & (NQ - 1);
+                        const uint2 h0 = lds.quad[i0], h1 = lds.quad[i1];
+                        const uint2 o0 = lds.quad[QLO + i0], o1 = lds.quad[QLO + i1];
+                        ch[nt] = u32x4{h0.x, h0.y, h1.x, h1.y};
+                        cl[nt] = u32x4{o0.x, o0.y, o1.x, o1.y};
+                    }
+                } else {
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
@@ -489,6 +527,7 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
                         ch[nt][q] = hi;
                         cl[nt][q] = lo;
                     }
+                }
 #pragma unroll
                 for (int m = 0; m < NMT; ++m) {
                     const int r = (32 * m + n) * kRowStride + 2 * kb + hh;
@@ -510,7 +549,11 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
                 // (no scheduling barrier)
                 u32x4 s[2];
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt) s[nt] = sigma8((sg[nt][kb >> 1] >> (16 * (kb & 1))) & 0xFFu);
+                for (int nt = 0; nt < 2; ++nt) {
+                    const uint32_t byte = (sg[nt][kb >> 1] >> (16 * (kb & 1))) & 0xFFu;
+                    if constexpr (STAB) s[nt] = lds.sigt[byte];
+                    else s[nt] = sigma8(byte);
+                }
 #pragma unroll
                 for (int m = 0; m < NMT; ++m) {
                     const int r = (32 * m + n) * kRowStride + 2 * kb + hh;
