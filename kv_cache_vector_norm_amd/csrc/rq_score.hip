@@ -87,6 +87,12 @@ __device__ __forceinline__ u32x4 sigma8(uint32_t byte) {
     return d;
 }
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                 0, 0);
+}
+
 // One 16-bit record entry of key `idx` (relative to the tile base), 0 past n.
 __device__ __forceinline__ uint32_t half_at(const uint16_t* __restrict__ src, int64_t base, int64_t n, int idx) {
     const rsrc_t rs = make_rsrc(src + base, tile_range(n - base, 2));
@@ -95,16 +101,16 @@ __device__ __forceinline__ uint32_t half_at(const uint16_t* __restrict__ src, in
 
 // One tile's record in registers: lane l holds dword it * 64 + l of the
 // tile's code and sign runs, and the fp16 norm / residual norm of keys
-// l % 32 and 32 + l % 32.  Fetched one tile ahead.
-template <int W>
+// l % 32 + 32 j (KPL = 2) or l % 16 + 16 j (KPL = 4).  Fetched one tile ahead.
+template <int W, int KPL>
 struct RecRegs {
     uint32_t c[W > 0 ? W : 1];
     uint32_t s[4];
-    uint32_t kn[2], kg[2];
+    uint32_t kn[KPL], kg[KPL];
 };
-template <int W, bool QJL>
-__device__ __forceinline__ void rec_fetch(const MainArgs& a, int64_t rbase, int head, int64_t kbase, RecRegs<W>& r,
-                                          int l) {
+template <int W, bool QJL, int KPL>
+__device__ __forceinline__ void rec_fetch(const MainArgs& a, int64_t rbase, int head, int64_t kbase,
+                                          RecRegs<W, KPL>& r, int l) {
     const int64_t left = a.t - kbase;
     const int64_t row = tile_row(a.pt, rbase, head, kbase);
     const rsrc_t rc = make_rsrc(a.codes + row * W, tile_range(left, 4 * W));
@@ -117,11 +123,12 @@ __device__ __forceinline__ void rec_fetch(const MainArgs& a, int64_t rbase, int 
         for (int it = 0; it < 4; ++it)
             r.s[it] = __builtin_amdgcn_raw_buffer_load_b32(rsg, static_cast<uint32_t>(4 * l), 256 * it, kNonTemporal);
     }
-    const int n = l & 31;
+    constexpr int KS = 64 / KPL;   // key stride between a lane's keys
+    const int n = l & (KS - 1);
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-        r.kn[nt] = half_at(a.norms + row, 0, left, 32 * nt + n);
-        r.kg[nt] = QJL ? half_at(a.rnorms + row, 0, left, 32 * nt + n) : 0u;
+    for (int j = 0; j < KPL; ++j) {
+        r.kn[j] = half_at(a.norms + row, 0, left, KS * j + n);
+        r.kg[j] = QJL ? half_at(a.rnorms + row, 0, left, KS * j + n) : 0u;
     }
 }
 
@@ -347,14 +354,19 @@ __device__ __forceinline__ void build_query_rows(const MainArgs& a, const QueryR
     __syncthreads();
 }
 
+// NMT = 1, 2: 32-row M tiles (32x32x16 MFMAs), NMT = 0: groups of at most 16
+// query rows on 16x16x32 MFMAs (the query side is built as for one 32-row
+// tile and rows 0..15 are read).
 template <int B, bool QJL, bool PAD, int NMT>
 __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
+    constexpr int NB = NMT > 0 ? NMT : 1;   // 32-row tiles of the query build
+    constexpr int KPL = NMT > 0 ? 2 : 4;    // keys per lane in a 64-key tile
     constexpr int NC = PAD ? kRotCoords : kD;
     constexpr int W = (NC * B + 31) / 32;
     constexpr int L = 1 << B;
     constexpr int WA = W > 0 ? W : 1;   // B = 0: QJL-only keys, no code words
     constexpr int SW = W > 4 ? W : 4;
-    constexpr int ROWS = NMT * 32;
+    constexpr int ROWS = NB * 32;
     // 1- and 2-bit codes: four codes (one byte or nibble of the stream) select
     // two dwords of C_hi halves and two of C_lo halves, which land in the MFMA
     // operand as they are; wider codes go by pairs.  Sign bytes map to their
@@ -374,7 +386,7 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
         float cent[L];
         float s0[ROWS];               // power of two putting max |q| of a row in [1, 2)
         float part[2][4][ROWS];       // per-wave partial maxima of the two products
-        uint32_t stage[4][64 * SW];
+        uint32_t stage[4][64 * SW + 4];   // (+4: the 3-bit reads of the 16-row loop run one word past)
         float qf[ROWS][kD + 4];
         u32x4 qrows[ROWS * kRowStride];
     };
@@ -391,13 +403,13 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
     const int64_t rbase = static_cast<int64_t>(a.kv_head0 + kvh) * a.kv_stride;
     const int64_t tstep = gridDim.x * 4LL;
     // the first tile's record is requested before the block's staging
-    RecRegs<W> rec;
+    RecRegs<W, KPL> rec;
     int64_t tile = blockIdx.x * 4LL + wave;
     const int ghead = a.kv_head0 + kvh;
-    if (tile < ntiles) rec_fetch<W, QJL>(a, rbase, ghead, tile * 64, rec, lane_id());
+    if (tile < ntiles) rec_fetch<W, QJL, KPL>(a, rbase, ghead, tile * 64, rec, lane_id());
     // and so are the query rows and the X / S fragments of the query build
-    QueryRegs<NMT> qr;
-    query_load<NMT>(a, row0, nrows, qr);
+    QueryRegs<NB> qr;
+    query_load<NB>(a, row0, nrows, qr);
     QueryFrags<QJL> fr;
     query_frags<QJL>(a, wave, lane_id(), fr);
 
@@ -427,12 +439,147 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
         }
         if (threadIdx.x < L) lds.cent[threadIdx.x] = a.cent[threadIdx.x];
     }
-    build_query_rows<PAD, QJL, NMT>(a, qr, fr, inv_sc, lds);
+    build_query_rows<PAD, QJL, NB>(a, qr, fr, inv_sc, lds);
 
     uint32_t* st = lds.stage[wave];
     const int64_t nk = a.t;   // keys of this head
     const char* pairc = reinterpret_cast<const char*>(lds.pairs);
 
+    // C_hi / C_lo operand halves of eight codes held in the low 8 B bits of f
+    auto decode8 = [&](uint32_t f, u32x4& ch, u32x4& cl) {
+        if constexpr (QUAD) {
+            const uint32_t i0 = f & (NQ - 1), i1 = (f >> (4 * B)) & (NQ - 1);
+            const uint2 h0 = lds.quad[i0], h1 = lds.quad[i1];
+            const uint2 o0 = lds.quad[QLO + i0], o1 = lds.quad[QLO + i1];
+            ch = u32x4{h0.x, h0.y, h1.x, h1.y};
+            cl = u32x4{o0.x, o0.y, o1.x, o1.y};
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t addr = ((f >> (2 * B * q)) & (L * L - 1)) * 8u;
+                ch[q] = *reinterpret_cast<const uint32_t*>(pairc + addr);
+                cl[q] = *reinterpret_cast<const uint32_t*>(pairc + addr + 4);
+            }
+        }
+    };
+
+    if constexpr (NMT == 0) {
+        // Lane (c, g) = (l % 16, l / 16) serves keys 16 j + c (j = 0..3) of the
+        // 64-key tile and K slots 32 ks + 8 g .. + 7 of each 32-wide step; the
+        // A operand of step ks is chunk 4 ks + g of staged row c.
+        for (; tile < ntiles; tile += tstep) {
+            const int z = opaque_zero();
+            const int l = lane_id() + z;
+            const int c = l & 15, g = l >> 4;
+            const int64_t kbase = tile * 64;
+            const int gb = 8 * B * g;   // this lane's first code bit within a K step
+            uint32_t cs[4][4];          // [j][ks]: the lane's 8 B code bits, from bit 0
+            float cpad[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            if constexpr (B > 0) {
+                wave_lds_sync();
+#pragma unroll
+                for (int it = 0; it < W; ++it) st[it * 64 + l] = rec.c[it];
+                wave_lds_sync();
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t* kw = st + (16 * j + c) * W;
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) {
+                        // bit B (32 ks + 8 g) of the key's stream; only 3-bit codes straddle words
+                        const uint32_t* wp = kw + B * ks + (gb >> 5);
+                        if constexpr (B == 3) cs[j][ks] = __builtin_amdgcn_alignbit(wp[1], wp[0], gb & 31);
+                        else cs[j][ks] = wp[0] >> (gb & 31);
+                    }
+                    if constexpr (PAD) cpad[j] = lds.cent[kw[4 * B] & (L - 1)];
+                }
+            }
+            uint32_t sb[4][4];   // [j][ks]: the lane's sign byte
+            if constexpr (QJL) {
+                wave_lds_sync();
+#pragma unroll
+                for (int it = 0; it < 4; ++it) st[it * 64 + l] = rec.s[it];
+                wave_lds_sync();
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) sb[j][ks] = (st[(16 * j + c) * 4 + ks] >> (8 * g)) & 0xFFu;
+            }
+            wave_lds_sync();
+            float kn[4], kg[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                kn[j] = h2f(rec.kn[j]);
+                kg[j] = QJL ? h2f(rec.kg[j]) * a.qjl_scale : 0.0f;
+            }
+            if (tile + tstep < ntiles) rec_fetch<W, QJL, KPL>(a, rbase, ghead, (tile + tstep) * 64, rec, l);
+
+            f32x4 acc1[4], acc2[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                acc1[j] = f32x4{};
+                acc2[j] = f32x4{};
+            }
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int r = c * kRowStride + 4 * ks + g;
+                if constexpr (B > 0) {
+                    const u32x4 q1 = lds.qrows[r + kOffQ1];
+                    const u32x4 q2 = lds.qrows[r + kOffQ2];
+                    const u32x4 q3 = lds.qrows[r + kOffQ3];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        u32x4 ch, cl;
+                        decode8(cs[j][ks], ch, cl);
+                        acc1[j] = mfma16(q1, ch, acc1[j]);
+                        acc1[j] = mfma16(q2, cl, acc1[j]);
+                        acc1[j] = mfma16(q3, ch, acc1[j]);
+                    }
+                }
+                if constexpr (QJL) {
+                    const u32x4 p1 = lds.qrows[r + kOffP1];
+                    const u32x4 p2 = lds.qrows[r + kOffP2];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        u32x4 sv;
+                        if constexpr (STAB) sv = lds.sigt[sb[j][ks]];
+                        else sv = sigma8(sb[j][ks]);
+                        acc2[j] = mfma16(p1, sv, acc2[j]);
+                        acc2[j] = mfma16(p2, sv, acc2[j]);
+                    }
+                }
+            }
+
+            // epilogue: lane (c, g) holds rows 4 g .. 4 g + 3 of key 16 j + c;
+            // rows past nrows fall outside the descriptor's range, keys past
+            // the end get an offset beyond it
+            const rsrc_t rs = make_rsrc(a.scores + static_cast<int64_t>(row0) * a.ld + kbase,
+                                        static_cast<uint32_t>(((nrows - 1) * a.ld + (nk - kbase)) * 4));
+            if (4 * g < nrows) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 4 * g + i;
+                    const float* rsv = lds.rsc[row];
+                    const float s0 = rsv[0], s1 = rsv[1], s2 = rsv[2];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int key = 16 * j + c;
+                        const float e1 = acc1[j][i];
+                        float v = e1 * s0;
+                        if constexpr (PAD) v = __builtin_fmaf(s2, cpad[j], v);
+                        if constexpr (QJL) {
+                            const float e2 = acc2[j][i];
+                            v = __builtin_fmaf(kg[j], e2 * s1, v);
+                        }
+                        v *= kn[j];
+                        const uint32_t voff =
+                            kbase + key < nk ? static_cast<uint32_t>((row * a.ld + key) * 4) : 0x80000000u;
+                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rs, voff, 0,
+                                                              kNonTemporal);
+                    }
+                }
+            }
+        }
+    } else {
     for (; tile < ntiles; tile += tstep) {
         const int z = opaque_zero();
         const int l = lane_id() + z;
@@ -485,7 +632,7 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
             kg[nt] = QJL ? h2f(rec.kg[nt]) * a.qjl_scale : 0.0f;
         }
         // next tile's record, in flight during this tile's MFMAs and stores
-        if (tile + tstep < ntiles) rec_fetch<W, QJL>(a, rbase, ghead, (tile + tstep) * 64, rec, l);
+        if (tile + tstep < ntiles) rec_fetch<W, QJL, KPL>(a, rbase, ghead, (tile + tstep) * 64, rec, l);
 
         f32x16 acc1[NMT][2], acc2[NMT][2];
 #pragma unroll
@@ -603,6 +750,7 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
                 }
             }
     }
+    }
 }
 
 // Grid: (key slices, KV heads x query-row blocks).  Every block pays for
@@ -614,7 +762,7 @@ template <int B, bool QJL, bool PAD, int NMT>
 static void launch_main(const MainArgs& a, int kv_heads, int qblocks, hipStream_t s) {
     const int64_t ntiles = (a.t + 63) / 64;
     const int64_t want = (ntiles + 3) / 4;
-    const int64_t slots = 256LL * (NMT == 1 ? 2 : 1);
+    const int64_t slots = 256LL * (NMT < 2 ? 2 : 1);
     const int64_t units = static_cast<int64_t>(kv_heads) * qblocks;
     int64_t gx = slots / units;
     if (gx > want) gx = want;
@@ -626,10 +774,12 @@ static void launch_main(const MainArgs& a, int kv_heads, int qblocks, hipStream_
 template <int B, bool QJL>
 static void launch_main_b(bool dense, int nmt, const MainArgs& a, int kv_heads, int qblocks, hipStream_t s) {
     if (dense) {
-        if (nmt == 1) launch_main<B, QJL, false, 1>(a, kv_heads, qblocks, s);
+        if (nmt == 0) launch_main<B, QJL, false, 0>(a, kv_heads, qblocks, s);
+        else if (nmt == 1) launch_main<B, QJL, false, 1>(a, kv_heads, qblocks, s);
         else launch_main<B, QJL, false, 2>(a, kv_heads, qblocks, s);
     } else {
-        if (nmt == 1) launch_main<B, QJL, true, 1>(a, kv_heads, qblocks, s);
+        if (nmt == 0) launch_main<B, QJL, true, 0>(a, kv_heads, qblocks, s);
+        else if (nmt == 1) launch_main<B, QJL, true, 1>(a, kv_heads, qblocks, s);
         else launch_main<B, QJL, true, 2>(a, kv_heads, qblocks, s);
     }
 }
@@ -660,7 +810,7 @@ hipError_t score(const ScoreTables& t, const float* q, int hq, int group, const 
     a.ld = ld_scores;
     const int kv_heads = hq / group;
     const int qblocks = (group + 63) / 64;
-    const int nmt = a.rows_per_block > 32 ? 2 : 1;
+    const int nmt = a.rows_per_block > 32 ? 2 : a.rows_per_block > 16 ? 1 : 0;
     switch (t.mse_bits * 2 + (t.qjl ? 1 : 0)) {
         case 1: launch_main_b<0, true>(t.dense, nmt, a, kv_heads, qblocks, s); break;
         case 2: launch_main_b<1, false>(t.dense, nmt, a, kv_heads, qblocks, s); break;
