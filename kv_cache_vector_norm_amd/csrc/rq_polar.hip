@@ -176,6 +176,85 @@ __device__ __forceinline__ float pq_decode_split(const float2* __restrict__ tab,
 }
 
 // x~ = Pi^T y~ of one record into `out` (coordinates in increasing order);
+// The scoring form of pq_decode_split followed by rot_mfma<0>: each 32
+// coordinates are split and enter the rotation's two K blocks as soon as
+// they are decoded, so only one chunk's half pairs are live (the same
+// values and the same MFMA order as the two steps one after the other).
+template <class FragHi, class FragLo>
+__device__ __forceinline__ float pq_decode_rot(const float2* __restrict__ tab, const uint32_t (&w)[kPolarWords],
+                                               FragHi fa_hi, FragLo fa_lo, int l, float (&own0)[16],
+                                               float (&own1)[16]) {
+    float R[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) R[i] = h2f((w[12 + (i >> 1)] >> (16 * (i & 1))) & 0xFFFFu);
+    float ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss = __builtin_fmaf(R[i], R[i], ss);
+    const float rn = __builtin_sqrtf(ss);
+    const float inv16 = rn > 0.0f ? 16.0f / rn : 0.0f;
+    f32x16 a0 = {}, a1 = {};
+#pragma unroll
+    for (int MT = 0; MT < 4; ++MT) {
+        float r3[4], r2[8], r1[16];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int I = 2 * MT + i;
+            const float2 cs = tab[kPqCen + 8 + ((w[11] >> (2 * I)) & 3u)];
+            const float r = R[I] * inv16;
+            r3[2 * i] = r * cs.x;
+            r3[2 * i + 1] = r * cs.y;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int J = 4 * MT + j;
+            const float2 cs = tab[kPqCen + 4 + ((w[10] >> (2 * J)) & 3u)];
+            r2[2 * j] = r3[j] * cs.x;
+            r2[2 * j + 1] = r3[j] * cs.y;
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int K = 8 * MT + k;
+            const float2 cs = tab[kPqCen + ((w[8 + (K >> 4)] >> (2 * (K & 15))) & 3u)];
+            r1[2 * k] = r2[k] * cs.x;
+            r1[2 * k + 1] = r2[k] * cs.y;
+        }
+        uint32_t yh11[16], yh[16], yl[16];
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+            const int M = 16 * MT + m;
+            const float2 cs = tab[kPqCen0 + ((w[M >> 3] >> (4 * (M & 7))) & 15u)];
+            const float va = r1[m] * cs.x, vb = r1[m] * cs.y;
+            const uint32_t hi = cvt_pk(va, vb);
+            const float da = va - h2f(hi & 0xFFFFu), db = vb - h2f(hi >> 16);
+            yh[m] = hi;
+            yl[m] = cvt_pk(da * 2048.0f, db * 2048.0f);
+            yh11[m] = pk_scale2048(hi);
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const int kb = 2 * MT + kk, o = 8 * kk;
+            const int row = l & 31, chunk = 2 * kb + (l >> 5);
+            const u32x4 ph = fa_hi(row, chunk);
+            const u32x4 pl = fa_lo(row, chunk);
+            u32x4 b11_0, b11_1, bh_0, bh_1, bl_0, bl_1;
+            to_operands(u32x4{yh11[o], yh11[o + 1], yh11[o + 2], yh11[o + 3]},
+                        u32x4{yh11[o + 4], yh11[o + 5], yh11[o + 6], yh11[o + 7]}, &b11_0, &b11_1);
+            to_operands(u32x4{yh[o], yh[o + 1], yh[o + 2], yh[o + 3]},
+                        u32x4{yh[o + 4], yh[o + 5], yh[o + 6], yh[o + 7]}, &bh_0, &bh_1);
+            to_operands(u32x4{yl[o], yl[o + 1], yl[o + 2], yl[o + 3]},
+                        u32x4{yl[o + 4], yl[o + 5], yl[o + 6], yl[o + 7]}, &bl_0, &bl_1);
+            a0 = mfma(ph, b11_0, a0);
+            a0 = mfma(ph, bl_0, a0);
+            a0 = mfma(pl, bh_0, a0);
+            a1 = mfma(ph, b11_1, a1);
+            a1 = mfma(ph, bl_1, a1);
+            a1 = mfma(pl, bh_1, a1);
+        }
+    }
+    from_accumulators(a0, a1, own0, own1);
+    return rn;
+}
+
 // done(mt) runs once coordinates 32 mt .. 32 mt + 31 are set.
 template <class Out, class Done>
 __device__ __forceinline__ void pq_dequant_vec(const PolarDev& P, const float2* __restrict__ tab,
@@ -394,39 +473,61 @@ __global__ __launch_bounds__(kPqWaves * 64) void pq_score_kernel(PolarDev P, con
     const int l = lane_id();
     pq_tab_to_lds(P.tab, sm.tab);
     {
-        // lane l < nrows: query row row0 + l, unit-normalised, split
-        float qv[kD];
+        // lane l < nrows: query row row0 + l, unit-normalised, split; the
+        // row is read twice (its norm, then 16 coordinates per K block) so
+        // that only one block's half pairs are live
         const bool live = l < nrows;
         const float4* src = reinterpret_cast<const float4*>(q + (row0 + (live ? l : 0)) * kD);
+        float ss = 0.0f;
 #pragma unroll
         for (int c = 0; c < kD / 4; ++c) {
             const float4 v = live ? src[c] : float4{0.0f, 0.0f, 0.0f, 0.0f};
-            qv[4 * c] = v.x;
-            qv[4 * c + 1] = v.y;
-            qv[4 * c + 2] = v.z;
-            qv[4 * c + 3] = v.w;
+            ss = __builtin_fmaf(v.x, v.x, ss);
+            ss = __builtin_fmaf(v.y, v.y, ss);
+            ss = __builtin_fmaf(v.z, v.z, ss);
+            ss = __builtin_fmaf(v.w, v.w, ss);
         }
-        float ss = 0.0f;
-#pragma unroll
-        for (int i = 0; i < kD; ++i) ss = __builtin_fmaf(qv[i], qv[i], ss);
         const float nq = __builtin_sqrtf(ss);
         const float inv = nq > 0.0f ? 1.0f / nq : 0.0f;
         if (wave == 0 && l < kPolarScoreRows) sm.qn[l] = nq;
-        uint32_t vh11[64], vh[64], vl[64];
-#pragma unroll
-        for (int i = 0; i < kD; ++i) {
-            uint32_t a, b, c;
-            split16(qv[i] * inv, &a, &b, &c);
-            put_pair(vh11, i, a);
-            put_pair(vh, i, b);
-            put_pair(vl, i, c);
-        }
         auto rot = [&](auto mt_c) {
             constexpr int MT = decltype(mt_c)::value;
+            f32x16 a0 = {}, a1 = {};
+#pragma unroll
+            for (int kb = 0; kb < 8; ++kb) {
+                uint32_t vh11[8], vh[8], vl[8];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const float4 v = live ? src[4 * kb + c] : float4{0.0f, 0.0f, 0.0f, 0.0f};
+                    const float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int k = 0; k < 4; k += 2) {
+                        uint32_t a0h, b0h, c0h, a1h, b1h, c1h;
+                        split16(e[k] * inv, &a0h, &b0h, &c0h);
+                        split16(e[k + 1] * inv, &a1h, &b1h, &c1h);
+                        const int i = 2 * c + (k >> 1);
+                        vh11[i] = a0h | (a1h << 16);
+                        vh[i] = b0h | (b1h << 16);
+                        vl[i] = c0h | (c1h << 16);
+                    }
+                }
+                const int row = 32 * MT + (l & 31), chunk = 2 * kb + (l >> 5);
+                const u32x4 ph = gmat_frag(P.pi_hi, row, chunk);
+                const u32x4 pl = gmat_frag(P.pi_lo, row, chunk);
+                u32x4 b11_0, b11_1, bh_0, bh_1, bl_0, bl_1;
+                to_operands(u32x4{vh11[0], vh11[1], vh11[2], vh11[3]}, u32x4{vh11[4], vh11[5], vh11[6], vh11[7]},
+                            &b11_0, &b11_1);
+                to_operands(u32x4{vh[0], vh[1], vh[2], vh[3]}, u32x4{vh[4], vh[5], vh[6], vh[7]}, &bh_0, &bh_1);
+                to_operands(u32x4{vl[0], vl[1], vl[2], vl[3]}, u32x4{vl[4], vl[5], vl[6], vl[7]}, &bl_0, &bl_1);
+                a0 = mfma(ph, b11_0, a0);
+                a0 = mfma(ph, bl_0, a0);
+                a0 = mfma(pl, bh_0, a0);
+                a1 = mfma(ph, b11_1, a1);
+                a1 = mfma(ph, bl_1, a1);
+                a1 = mfma(pl, bh_1, a1);
+            }
             float y0[16], y1[16];
-            rot_mfma<MT>(
-                vh11, vh, vl, [&](int row, int chunk) { return gmat_frag(P.pi_hi, row, chunk); },
-                [&](int row, int chunk) { return gmat_frag(P.pi_lo, row, chunk); }, l, y0, y1);
+            from_accumulators(a0, a1, y0, y1);
             if (l < kPolarScoreRows) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
@@ -467,19 +568,25 @@ __global__ __launch_bounds__(kPqWaves * 64) void pq_score_kernel(PolarDev P, con
         const int lz = lane_id() + z;
         uint32_t w[kPolarWords];
         words_load<kPolarWords>(kw, base, t, w, stage, lz);
-        uint32_t yh11[64], yh[64], yl[64];
-        const float rn = pq_decode_split(sm.tab, w, yh11, yh, yl) * kRotScale;
         float s0[16], s1[16];
-        rot_mfma<0>(
-            yh11, yh, yl, [&](int row, int chunk) { return mat_frag(sm.ah, row, chunk); },
-            [&](int row, int chunk) { return mat_frag(sm.al, row, chunk); }, lz, s0, s1);
-        const bool live = base + lz < t;
+        const float rn = pq_decode_rot(
+                             sm.tab, w, [&](int row, int chunk) { return mat_frag(sm.ah, row, chunk); },
+                             [&](int row, int chunk) { return mat_frag(sm.al, row, chunk); }, lz, s0, s1) *
+                         kRotScale;
+        // rows past nrows are skipped (a uniform test) and fall outside the
+        // range; keys past the end get an offset beyond it
+        const rsrc_t rs = make_rsrc(out + base, static_cast<uint32_t>(((nrows - 1) * ld + (t - base)) * 4));
+        const uint32_t voff = base + lz < t ? static_cast<uint32_t>(lz * 4) : 0x80000000u;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int row = own_row(h, r);
-                if (row < nrows && live) out[row * ld + base + lz] = (h ? s1[r] : s0[r]) * rn * sm.qn[row];
+                if (row < nrows) {
+                    const float v = (h ? s1[r] : s0[r]) * rn * sm.qn[row];
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rs, voff,
+                                                          static_cast<int>(row * ld * 4), kNonTemporal);
+                }
             }
         }
     }

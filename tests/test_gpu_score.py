@@ -54,7 +54,9 @@ def test_score_single_head(K, bits, mode):
 
 @pytest.mark.parametrize("t,hq,group,stride", [
     (1, 1, 1, None), (63, 4, 4, None), (65, 8, 4, 80), (640, 16, 8, 700), (300, 64, 64, None),
-    (257, 100, 100, None), (129, 6, 1, 130), (2048, 32, 4, 2048)])
+    (257, 100, 100, None), (129, 6, 1, 130), (2048, 32, 4, 2048),
+    # around the 16-row (16x16x32) and 32-row tiles: 16 / 17 / 32 / 33 rows a group
+    (700, 32, 16, None), (333, 34, 17, None), (200, 64, 32, 256), (96, 33, 33, None)])
 def test_score_gqa_shapes(K, t, hq, group, stride):
     _score_case(K, 3, OP.QJL, t, hq, group, stride)
 
