@@ -633,7 +633,9 @@ hipError_t polar_score(const PolarDev& P, const float* q, int hq, int group, con
                        int64_t kv_stride, float* scores, int64_t ld_scores, hipStream_t s) {
     const int chunks = (group + kPolarScoreRows - 1) / kPolarScoreRows;
     const int gy = (hq / group) * chunks;
-    const int64_t want = (512 + gy - 1) / gy;
+    // about three blocks per CU in all (the kernel's occupancy), each walking
+    // its key slice tile by tile
+    const int64_t want = (768 + gy - 1) / gy;
     const int gx = pq_grid(t, want > 0 ? want : 1);
     hipLaunchKernelGGL(pq_score_kernel, dim3(gx, gy), dim3(kPqWaves * 64), 0, s, P, q, group, chunks, words, t,
                        kv_stride, scores, ld_scores);
