@@ -83,32 +83,88 @@ __device__ __forceinline__ void put_pair(uint32_t (&arr)[64], int i, uint32_t h)
     if (i & 1) arr[i >> 1] |= h << 16; else arr[i >> 1] = h;
 }
 
+// rot_mfma for all four M tiles with the K blocks outermost: split(kb, h11,
+// h, lo) forms the 16 split coordinates of block kb (as 8 half pairs each),
+// which feed every tile, so the 128 split coordinates are never live at
+// once.  Per tile the MFMA order is rot_mfma's.
+template <class Split, class FragHi, class FragLo>
+__device__ __forceinline__ void rot4_mfma(Split split, FragHi fa_hi, FragLo fa_lo, int l, f32x16 (&ax0)[4],
+                                          f32x16 (&ax1)[4]) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        ax0[mt] = f32x16{};
+        ax1[mt] = f32x16{};
+    }
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+        uint32_t h11[8], h[8], lo[8];
+        split(kb, h11, h, lo);
+        u32x4 b11_0, b11_1, bh_0, bh_1, bl_0, bl_1;
+        to_operands(u32x4{h11[0], h11[1], h11[2], h11[3]}, u32x4{h11[4], h11[5], h11[6], h11[7]}, &b11_0, &b11_1);
+        to_operands(u32x4{h[0], h[1], h[2], h[3]}, u32x4{h[4], h[5], h[6], h[7]}, &bh_0, &bh_1);
+        to_operands(u32x4{lo[0], lo[1], lo[2], lo[3]}, u32x4{lo[4], lo[5], lo[6], lo[7]}, &bl_0, &bl_1);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            const int row = 32 * mt + (l & 31), chunk = 2 * kb + (l >> 5);
+            const u32x4 ph = fa_hi(row, chunk);
+            const u32x4 pl = fa_lo(row, chunk);
+            ax0[mt] = mfma(ph, b11_0, ax0[mt]);
+            ax0[mt] = mfma(ph, bl_0, ax0[mt]);
+            ax0[mt] = mfma(pl, bh_0, ax0[mt]);
+            ax1[mt] = mfma(ph, b11_1, ax1[mt]);
+            ax1[mt] = mfma(ph, bl_1, ax1[mt]);
+            ax1[mt] = mfma(pl, bh_1, ax1[mt]);
+        }
+    }
+}
+
 // coordinate index of own register (h, r) in M tile MT
 __device__ __forceinline__ constexpr int own_coord(int mt, int h, int r) { return 32 * mt + own_row(h, r); }
 
-// done(mt) runs once coordinates 32 mt .. 32 mt + 31 are set.
-template <int B, bool QJL, class Out, class SColFrag, class Done>
-__device__ __forceinline__ void dense_dequant_vec(const DenseDev& P, const uint32_t* __restrict__ ctab,
-                                                  const uint32_t (&cw)[(128 * B + 31) / 32], float nhat, float ghat,
-                                                  const uint32_t (&sw)[4], SColFrag scol, Out& out, int l, Done done) {
+// Pi^T y^ for all four 32-row M tiles with the K blocks outermost: each
+// block's 16 centroid halves (ctab: lo 16 bits = hi half, hi 16 bits =
+// 2^11 hi; ctab[L + k] = lo) are formed once and feed every tile, so the
+// 128 split coordinates are never live at once.  Per tile the MFMA order is
+// that of rot_mfma (K blocks 0..7, the same three products each).
+template <int B>
+__device__ __forceinline__ void dense_pit_tiles(const DenseDev& P, const uint32_t* __restrict__ ctab,
+                                                const uint32_t (&cw)[(128 * B + 31) / 32], int l,
+                                                f32x16 (&ax0)[4], f32x16 (&ax1)[4]) {
     constexpr int W = (128 * B + 31) / 32;
-    // y^ = c[code] as split pairs (ctab: lo 16 bits = hi half, hi 16 bits = 2^11 hi; ctab[L + k] = lo)
-    uint32_t yh11[64], yh[64], yl[64];
+    constexpr int L = 1 << B;
+    rot4_mfma(
+        [&](int kb, uint32_t (&yh11)[8], uint32_t (&yh)[8], uint32_t (&yl)[8]) {
 #pragma unroll
-    for (int i = 0; i < 128; ++i) {
-        const uint32_t code = get_code<B, W>(cw, i);
-        const uint32_t e = ctab[code];
-        put_pair(yh, i, e & 0xFFFFu);
-        put_pair(yh11, i, e >> 16);
-        put_pair(yl, i, ctab[(1 << B) + code]);
-    }
+            for (int i = 0; i < 16; ++i) {
+                const uint32_t code = get_code<B, W>(cw, 16 * kb + i);
+                const uint32_t e = ctab[code];
+                const uint32_t eh = e & 0xFFFFu, e11 = e >> 16, el = ctab[L + code];
+                if (i & 1) {
+                    yh[i >> 1] |= eh << 16;
+                    yh11[i >> 1] |= e11 << 16;
+                    yl[i >> 1] |= el << 16;
+                } else {
+                    yh[i >> 1] = eh;
+                    yh11[i >> 1] = e11;
+                    yl[i >> 1] = el;
+                }
+            }
+        },
+        [&](int row, int chunk) { return gmat_frag(P.pit_hi, row, chunk); },
+        [&](int row, int chunk) { return gmat_frag(P.pit_lo, row, chunk); }, l, ax0, ax1);
+}
+
+// The output of one record from its Pi^T y^ accumulators (dense_pit_tiles):
+// plus the QJL term k S^T sigma per tile, times the norm.
+template <bool QJL, class Out, class SColFrag, class Done>
+__device__ __forceinline__ void dense_finish_vec(const DenseDev& P, const f32x16 (&ax0)[4], const f32x16 (&ax1)[4],
+                                                 float nhat, float ghat, const uint32_t (&sw)[4], SColFrag scol,
+                                                 Out& out, int l, Done done) {
     const float k = P.qjl_scale * ghat;
     auto tile = [&](auto mt_c) {
         constexpr int MT = decltype(mt_c)::value;
         float x0[16], x1[16];
-        rot_mfma<MT>(
-            yh11, yh, yl, [&](int row, int chunk) { return gmat_frag(P.pit_hi, row, chunk); },
-            [&](int row, int chunk) { return gmat_frag(P.pit_lo, row, chunk); }, l, x0, x1);
+        from_accumulators(ax0[MT], ax1[MT], x0, x1);
         float q0[16], q1[16];
         if constexpr (QJL) {
             f32x16 a0 = {}, a1 = {};
@@ -146,6 +202,16 @@ __device__ __forceinline__ void dense_dequant_vec(const DenseDev& P, const uint3
     tile(std::integral_constant<int, 1>{});
     tile(std::integral_constant<int, 2>{});
     tile(std::integral_constant<int, 3>{});
+}
+
+template <int B, bool QJL, class Out, class SColFrag, class Done>
+__device__ __forceinline__ void dense_dequant_vec(const DenseDev& P, const uint32_t* __restrict__ ctab,
+                                                  const uint32_t (&cw)[(128 * B + 31) / 32], float nhat, float ghat,
+                                                  const uint32_t (&sw)[4], SColFrag scol, Out& out, int l, Done done) {
+    // x~ = Pi^T y^, y^ = c[code]
+    f32x16 ax0[4], ax1[4];
+    dense_pit_tiles<B>(P, ctab, cw, l, ax0, ax1);
+    dense_finish_vec<QJL>(P, ax0, ax1, nhat, ghat, sw, scol, out, l, done);
 }
 
 // ------------------------------------------------------------ kernels --
@@ -262,59 +328,53 @@ __global__ __launch_bounds__(WAVES * 64) void tq_quant_kernel(DenseDev P, const 
 #pragma unroll
         for (int k = 0; k < W; ++k) cw[k] = 0u;
         {
-            uint32_t vh11[64], vh[64], vl[64];
+            f32x16 ay0[4], ay1[4];
+            rot4_mfma(
+                [&](int kb, uint32_t (&vh11)[8], uint32_t (&vh)[8], uint32_t (&vl)[8]) {
 #pragma unroll
-            for (int i = 0; i < kD; ++i) {
-                uint32_t a, b, c;
-                split16(xget(i) * inv, &a, &b, &c);
-                put_pair(vh11, i, a);
-                put_pair(vh, i, b);
-                put_pair(vl, i, c);
-            }
-            auto tile_q = [&](auto mt_c) {
-                constexpr int MT = decltype(mt_c)::value;
+                    for (int i = 0; i < 16; i += 2) {
+                        uint32_t a0, b0, c0, a1, b1, c1;
+                        split16(xget(16 * kb + i) * inv, &a0, &b0, &c0);
+                        split16(xget(16 * kb + i + 1) * inv, &a1, &b1, &c1);
+                        vh11[i >> 1] = a0 | (a1 << 16);
+                        vh[i >> 1] = b0 | (b1 << 16);
+                        vl[i >> 1] = c0 | (c1 << 16);
+                    }
+                },
+                [&](int row, int chunk) { return mat_frag(sm.pih, row, chunk); },
+                [&](int row, int chunk) { return mat_frag(sm.pil, row, chunk); }, l, ay0, ay1);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
                 float y0[16], y1[16];
-                rot_mfma<MT>(
-                    vh11, vh, vl, [&](int row, int chunk) { return mat_frag(sm.pih, row, chunk); },
-                    [&](int row, int chunk) { return mat_frag(sm.pil, row, chunk); }, l, y0, y1);
+                from_accumulators(ay0[mt], ay1[mt], y0, y1);
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    put_code<B, W>(cw, own_coord(MT, 0, r), quant_code<B>(y0[r] * kRotScale, thr));
-                    put_code<B, W>(cw, own_coord(MT, 1, r), quant_code<B>(y1[r] * kRotScale, thr));
+                    put_code<B, W>(cw, 32 * mt + own_row(0, r), quant_code<B>(y0[r] * kRotScale, thr));
+                    put_code<B, W>(cw, 32 * mt + own_row(1, r), quant_code<B>(y1[r] * kRotScale, thr));
                 }
-            };
-            tile_q(std::integral_constant<int, 0>{});
-            tile_q(std::integral_constant<int, 1>{});
-            tile_q(std::integral_constant<int, 2>{});
-            tile_q(std::integral_constant<int, 3>{});
+            }
         }
 
         uint32_t sw[4] = {0u, 0u, 0u, 0u};
         uint32_t gh = 0u;
         float ghat = 0.0f;
+        // with QJL, Pi^T y^ of the residual step is kept for the roundtrip's
+        // output (the values rq_dequantize forms from the record)
+        f32x16 ax0[QJL ? 4 : 1], ax1[QJL ? 4 : 1];
         if constexpr (QJL) {
             // x~_u = Pi^T y^, r = x_u - x~_u (original domain), signs of S r
             uint32_t rh[64], rl[64];
             float gam2 = 0.0f;
             {
-                uint32_t yh11[64], yh[64], yl[64];
+                // x~_u = Pi^T y^ (all four M tiles), then the residual tile by tile
+                dense_pit_tiles<B>(P, sm.ctab, cw, l, ax0, ax1);
 #pragma unroll
-                for (int i = 0; i < 128; ++i) {
-                    const uint32_t code = get_code<B, W>(cw, i);
-                    const uint32_t e = sm.ctab[code];
-                    put_pair(yh, i, e & 0xFFFFu);
-                    put_pair(yh11, i, e >> 16);
-                    put_pair(yl, i, sm.ctab[L + code]);
-                }
-                auto tile_r = [&](auto mt_c) {
-                    constexpr int MT = decltype(mt_c)::value;
+                for (int mt = 0; mt < 4; ++mt) {
                     float x0[16], x1[16];
-                    rot_mfma<MT>(
-                        yh11, yh, yl, [&](int row, int chunk) { return gmat_frag(P.pit_hi, row, chunk); },
-                        [&](int row, int chunk) { return gmat_frag(P.pit_lo, row, chunk); }, l, x0, x1);
+                    from_accumulators(ax0[mt], ax1[mt], x0, x1);
 #pragma unroll
                     for (int il = 0; il < 32; ++il) {
-                        const int b8 = il >> 3, w = il & 7, i = 32 * MT + il;
+                        const int b8 = il >> 3, w = il & 7, i = 32 * mt + il;
                         const float xt = (w < 4 ? x0[4 * b8 + w] : x1[4 * b8 + w - 4]) * kRotScale;
                         const float r = xget(i) * inv - xt;
                         gam2 = __builtin_fmaf(r, r, gam2);
@@ -323,11 +383,7 @@ __global__ __launch_bounds__(WAVES * 64) void tq_quant_kernel(DenseDev P, const 
                         put_pair(rh, i, hi);
                         put_pair(rl, i, lo);
                     }
-                };
-                tile_r(std::integral_constant<int, 0>{});
-                tile_r(std::integral_constant<int, 1>{});
-                tile_r(std::integral_constant<int, 2>{});
-                tile_r(std::integral_constant<int, 3>{});
+                }
             }
             const float gam = __builtin_sqrtf(gam2);
             gh = f2h(gam);
@@ -374,13 +430,14 @@ __global__ __launch_bounds__(WAVES * 64) void tq_quant_kernel(DenseDev P, const 
             VecOutT<OUT_F16> out;
             if constexpr (!OUT_F16) out.bind(y, ldy_bytes, base, n);
             out.begin(tile, l);
-            dense_dequant_vec<B, QJL>(
-                P, sm.ctab, cw, nhat, ghat, sw, [&](int row, int chunk) { return gmat_frag(P.s_cols, row, chunk); },
-                out, l, [&](int mt) {
-                    if constexpr (OUT_F16) {
-                        if (single) out.store_cols(y, ldy_bytes, base, n, 4 * mt);
-                    }
-                });
+            auto scol = [&](int row, int chunk) { return gmat_frag(P.s_cols, row, chunk); };
+            auto done = [&](int mt) {
+                if constexpr (OUT_F16) {
+                    if (single) out.store_cols(y, ldy_bytes, base, n, 4 * mt);
+                }
+            };
+            if constexpr (QJL) dense_finish_vec<QJL>(P, ax0, ax1, nhat, ghat, sw, scol, out, l, done);
+            else dense_dequant_vec<B, QJL>(P, sm.ctab, cw, nhat, ghat, sw, scol, out, l, done);
             if (!OUT_F16 || !single) out.store(y, ldy_bytes, base, n);
         }
     }
