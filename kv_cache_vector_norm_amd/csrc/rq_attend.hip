@@ -119,8 +119,11 @@ __device__ __forceinline__ void split_pair11(float a, float b, uint32_t* hi, uin
 // (signs, norms and residual norms).  A QJL value session runs two passes,
 // one of each, writing disjoint columns of the partial rows: each pass
 // holds half the accumulators, so two waves fit on a SIMD.
+// Register budget: two waves per SIMD for the centroid pass (3- and 4-bit
+// values included), three for the sign pass.
 template <int B, bool QJL, bool PAD, bool CODES = true>
-__global__ __launch_bounds__(256) void attend_values_kernel(AttendArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CODES ? 2 : 3))) void attend_values_kernel(
+    AttendArgs a) {
     constexpr int L = 1 << B;
     constexpr int W = CODES ? (((PAD ? kRotCoords : kD) * B) + 31) / 32 : 1;
     struct alignas(16) Wave {
@@ -130,7 +133,11 @@ __global__ __launch_bounds__(256) void attend_values_kernel(AttendArgs a) {
         alignas(16) uint16_t gam[64];
     };
     struct Lds {
-        u32x4 pairs[L * L];         // codes (k, k+1) -> {2^11 C_hi, C_lo, C_hi} half pairs
+        // codes (k, k+1) -> 2^11 C_hi, C_lo and C_hi half pairs at [p], [257 + p],
+        // [514 + p]: 1,028 bytes apart, so no two-address LDS read fetches two of
+        // them together and each lands in its own MFMA operand without moves
+        uint32_t ptab[CODES ? 3 * 257 : 1];
+        u32x4 sig[QJL ? 256 : 1][2];   // eight sign bits -> {+-1, +-2^11} half pairs (bit 2q + e: dword q, half e)
         Wave w[4];
         float sum[32][kPartStride];   // the block's partial rows, waves added in order
     };
@@ -155,9 +162,26 @@ __global__ __launch_bounds__(256) void attend_values_kernel(AttendArgs a) {
             split_h11(a.cent[p & (L - 1)] * sc, &h0, &l0);
             split_h11(a.cent[p >> B] * sc, &h1, &l1);
             const uint32_t hp = h0 | (h1 << 16);
-            lds.pairs[p] = u32x4{pk_scale2048(hp), l0 | (l1 << 16), hp, 0u};
+            lds.ptab[p] = pk_scale2048(hp);
+            lds.ptab[257 + p] = l0 | (l1 << 16);
+            lds.ptab[514 + p] = hp;
         }
         for (int i = threadIdx.x; i < 4 * 64; i += kBlock) lds.w[i >> 6].code[W][i & 63] = 0u;
+    }
+    if constexpr (QJL) {
+        // sigma = 2 bit - 1 as half pairs; the sign bit is set where the stored bit is 0
+        for (int p = threadIdx.x; p < 256; p += kBlock) {
+            u32x4 s1, s11;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t b0 = (p >> (2 * q)) & 1u, b1 = (p >> (2 * q + 1)) & 1u;
+                const uint32_t sgn = ((b0 ^ 1u) << 15) | ((b1 ^ 1u) << 31);
+                s1[q] = 0x3C003C00u | sgn;     // +-1
+                s11[q] = 0x68006800u | sgn;    // +-2^11
+            }
+            lds.sig[p][0] = s1;
+            lds.sig[p][1] = s11;
+        }
     }
     __syncthreads();
 
@@ -190,12 +214,12 @@ __global__ __launch_bounds__(256) void attend_values_kernel(AttendArgs a) {
     auto fetch = [&](int64_t tile, TileIn& r) {
         const int64_t kbase = tile * 64;
         const uint32_t soff = static_cast<uint32_t>((n * a.ld + kbase + 8 * hh) * 4);
+        // (rows past nrows lie outside rsc's range and read as zero)
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
             for (int q = 0; q < 2; ++q)
-                r.sv[kb][q] = live ? __builtin_amdgcn_raw_buffer_load_b128(rsc, soff, 64 * kb + 16 * q, kNonTemporal)
-                                   : u32x4{0u, 0u, 0u, 0u};
+                r.sv[kb][q] = __builtin_amdgcn_raw_buffer_load_b128(rsc, soff, 64 * kb + 16 * q, kNonTemporal);
         const int64_t left = a.t - kbase;
         int64_t row = rbase + kbase;
         if (a.pt.pages != nullptr) {
@@ -229,6 +253,7 @@ __global__ __launch_bounds__(256) void attend_values_kernel(AttendArgs a) {
     if (blockIdx.x * 4LL + wave < ntiles) fetch(blockIdx.x * 4LL + wave, nx);
     for (int64_t tile = blockIdx.x * 4LL + wave; tile < ntiles; tile += tstep) {
         const int64_t kbase = tile * 64;
+        const int kleft = static_cast<int>(a.t - kbase < 64 ? a.t - kbase : 64);   // live keys of the tile
         u32x4 sv[4][2];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
@@ -272,7 +297,7 @@ __global__ __launch_bounds__(256) void attend_values_kernel(AttendArgs a) {
                     const int k = 2 * q + e;
                     const uint32_t sbits = sv[kb][k >> 2][k & 3];
                     const float s = __builtin_bit_cast(float, sbits);
-                    const bool in = live && kbase + k0 + k < a.t;
+                    const bool in = live && k0 + k < kleft;
                     const float ex = in ? exp2_hw((s * a.scale - mrow) * kLog2e) : 0.0f;
                     const uint32_t nn = e ? (nh[q] >> 16) : (nh[q] & 0xFFFFu);
                     w2[e] = ex * h2f(nn);
@@ -320,11 +345,11 @@ __global__ __launch_bounds__(256) void attend_values_kernel(AttendArgs a) {
                             f[e] = (x0 >> off) & (L - 1);
                         }
                     }
-                    const u32x4 pe = lds.pairs[f[0] | (f[1] << B)];
+                    const uint32_t ix = f[0] | (f[1] << B);
                     const bool keep = nt < 4 || n == 0;
-                    b11[q] = keep ? pe[0] : 0u;
-                    blo[q] = keep ? pe[1] : 0u;
-                    bhi[q] = keep ? pe[2] : 0u;
+                    b11[q] = keep ? lds.ptab[ix] : 0u;
+                    blo[q] = keep ? lds.ptab[257 + ix] : 0u;
+                    bhi[q] = keep ? lds.ptab[514 + ix] : 0u;
                 }
                 f32x16& acc = nt < 4 ? acc_c[nt] : acc_p;
                 acc = mfma(wh, b11, acc);
@@ -343,15 +368,7 @@ __global__ __launch_bounds__(256) void attend_values_kernel(AttendArgs a) {
                         const uint32_t x = k < 4 ? sa[k] : sb[k - 4];
                         byte |= ((x >> n) & 1u) << k;
                     }
-                    // sigma = 2 bit - 1 as half pairs; sign bit from the stored bit
-                    u32x4 s1, s11;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const uint32_t b0 = (byte >> (2 * q)) & 1u, b1 = (byte >> (2 * q + 1)) & 1u;
-                        const uint32_t sgn = ((b0 ^ 1u) << 15) | ((b1 ^ 1u) << 31);
-                        s1[q] = 0x3C003C00u | sgn;     // +-1
-                        s11[q] = 0x68006800u | sgn;    // +-2^11
-                    }
+                    const u32x4 s1 = lds.sig[byte][0], s11 = lds.sig[byte][1];
                     acc_s[nt] = mfma(gwh, s11, acc_s[nt]);
                     acc_s[nt] = mfma(gwl, s1, acc_s[nt]);
                 }
