@@ -327,7 +327,9 @@ __global__ __launch_bounds__(WAVES * 64) void tq_quant_kernel(DenseDev P, const 
         uint32_t cw[W];
 #pragma unroll
         for (int k = 0; k < W; ++k) cw[k] = 0u;
-        {
+        if constexpr (QJL) {
+            // the K blocks outermost (the residual step that follows needs the
+            // registers)
             f32x16 ay0[4], ay1[4];
             rot4_mfma(
                 [&](int kb, uint32_t (&vh11)[8], uint32_t (&vh)[8], uint32_t (&vl)[8]) {
@@ -353,6 +355,34 @@ __global__ __launch_bounds__(WAVES * 64) void tq_quant_kernel(DenseDev P, const 
                     put_code<B, W>(cw, 32 * mt + own_row(1, r), quant_code<B>(y1[r] * kRotScale, thr));
                 }
             }
+        } else {
+            // all 128 split coordinates, then one M tile at a time (each tile's
+            // codes are formed while the next tile's MFMAs run)
+            uint32_t vh11[64], vh[64], vl[64];
+#pragma unroll
+            for (int i = 0; i < kD; ++i) {
+                uint32_t a, b, c;
+                split16(xget(i) * inv, &a, &b, &c);
+                put_pair(vh11, i, a);
+                put_pair(vh, i, b);
+                put_pair(vl, i, c);
+            }
+            auto tile_q = [&](auto mt_c) {
+                constexpr int MT = decltype(mt_c)::value;
+                float y0[16], y1[16];
+                rot_mfma<MT>(
+                    vh11, vh, vl, [&](int row, int chunk) { return mat_frag(sm.pih, row, chunk); },
+                    [&](int row, int chunk) { return mat_frag(sm.pil, row, chunk); }, l, y0, y1);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    put_code<B, W>(cw, own_coord(MT, 0, r), quant_code<B>(y0[r] * kRotScale, thr));
+                    put_code<B, W>(cw, own_coord(MT, 1, r), quant_code<B>(y1[r] * kRotScale, thr));
+                }
+            };
+            tile_q(std::integral_constant<int, 0>{});
+            tile_q(std::integral_constant<int, 1>{});
+            tile_q(std::integral_constant<int, 2>{});
+            tile_q(std::integral_constant<int, 3>{});
         }
 
         uint32_t sw[4] = {0u, 0u, 0u, 0u};
