@@ -16,10 +16,12 @@
 // q^_128 from the last rotor in fp32).  Those rows are then
 // the A operand of the scoring MFMAs; the B operand is decoded from the
 // records straight into MFMA layout: lane (n, h) of a wave serves keys n and
-// 32 + n of the 64-key tile and K slots 8h..8h+7 of each 16-wide block,
-// turning two codes into packed centroid halves with one LDS lookup and sign
-// bits into +-1 halves with shifts.  The rotor pad coordinate (slot 128) is
-// added in fp32 in the epilogue.
+// 32 + n of the 64-key tile and K slots 8h..8h+7 of each 16-wide block
+// (groups of at most 16 rows: 16x16x32 MFMAs, lane (c, g) serving keys
+// 16 j + c and K slots 8g..8g+7 of each 32-wide step), turning four 1- or
+// 2-bit codes (or two wider ones) into packed centroid halves with LDS
+// table lookups and eight sign bits into +-1 halves with a table or shifts.
+// The rotor pad coordinate (slot 128) is added in fp32 in the epilogue.
 #include "rq_common.cuh"
 #include "rq_kernels.h"
 
