@@ -229,7 +229,11 @@ int rq_score(rq_ctx* ctx, const float* q, int hq, int group,
  *                bits and modes; both on the current device).  kctx may also
  *                be an RQ_POLAR session: the keys are then its 16-word
  *                records in kcodes (knorms, ksigns, krnorms NULL) and s_ht is
- *                pq_score's <q_h, x~_t>.
+ *                pq_score's <q_h, x~_t>.  vctx may be an RQ_POLAR session:
+ *                the values are then its 16-word records in vcodes (vnorms,
+ *                vsigns, vrnorms NULL) and v~_t is pq_dequantize's x~_t
+ *                (the weighted sums run over the decoded y~_t, Pi^T once
+ *                per row).
  *   q            [hq][128] fp32 queries, 16-byte aligned; hq <= RQ_ATTEND_MAX_ROWS.
  *   group        query rows per KV head, 1 <= group <= RQ_SCORE_CHUNK, hq % group == 0.
  *   k..., v...   records of hq/group KV heads; head j's t keys and values

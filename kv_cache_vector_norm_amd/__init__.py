@@ -464,7 +464,8 @@ class PolarCodec:
 def attend(kcodec, vcodec, q, krec, vrec, group, t, kv_stride=None, scale=None, out=None, workspace=None,
            stream=None):
     """softmax(scale * q.k) . V over compressed keys (kcodec's records, or a
-    PolarCodec's word tensor) and values (vcodec's records); scale defaults
+    PolarCodec's word tensor) and values (vcodec's records, or a PolarCodec's
+    word tensor); scale defaults
     to 1/sqrt(128).  Returns
     [hq, 128] fp32.  The workspace (torch uint8 tensor) is allocated when not
     given; pass one of rq_attend_workspace(hq, group, t) bytes to avoid that."""
@@ -486,8 +487,12 @@ def attend(kcodec, vcodec, q, krec, vrec, group, t, kv_stride=None, scale=None, 
         kparts = (krec, None, None, None)
     else:
         kparts = (krec.codes, krec.norms, krec.signs, krec.rnorms)
-    rq_attend(kcodec.ctx, vcodec.ctx, q, hq, group, *kparts, vrec.codes, vrec.norms, vrec.signs, vrec.rnorms, t,
-              kv_stride, scale, ws, avail, out, out.stride(0), stream)
+    if isinstance(vcodec, PolarCodec):          # vrec: the [n, 16] word records
+        vparts = (vrec, None, None, None)
+    else:
+        vparts = (vrec.codes, vrec.norms, vrec.signs, vrec.rnorms)
+    rq_attend(kcodec.ctx, vcodec.ctx, q, hq, group, *kparts, *vparts, t, kv_stride, scale, ws, avail, out,
+              out.stride(0), stream)
     return out
 
 

@@ -583,8 +583,9 @@ int rq_attend(const rq_ctx* kctx, const rq_ctx* vctx, const float* q, int hq, in
     if (!kctx || !vctx) return fail(RQ_EINVAL, "rq_attend: key and value sessions are required");
     int rc;
     const bool kpolar = kctx->host.lay.mode & RQ_POLAR;
+    const bool vpolar = vctx->host.lay.mode & RQ_POLAR;
     if ((rc = kpolar ? check_polar(kctx, fn) : check_ctx(kctx, kctx->host.lay.mode & RQ_DENSE, fn))) return rc;
-    if ((rc = check_ctx(vctx, vctx->host.lay.mode & RQ_DENSE, fn))) return rc;
+    if ((rc = vpolar ? check_polar(vctx, fn) : check_ctx(vctx, vctx->host.lay.mode & RQ_DENSE, fn))) return rc;
     if (!q || !aligned(q, 16)) return fail(RQ_EINVAL, "rq_attend: q must be a 16-byte aligned device pointer");
     if (hq < 1 || group < 1 || hq % group) return fail(RQ_EINVAL, "rq_attend: need hq >= 1, group >= 1, hq % group == 0");
     if (hq > RQ_ATTEND_MAX_ROWS) return fail(RQ_EINVAL, "rq_attend: hq > RQ_ATTEND_MAX_ROWS");
@@ -598,14 +599,19 @@ int rq_attend(const rq_ctx* kctx, const rq_ctx* vctx, const float* q, int hq, in
     } else if ((rc = check_record(kctx, kcodes, knorms, ksigns, krnorms, fn))) {
         return rc;
     }
-    if ((rc = check_record(vctx, vcodes, vnorms, vsigns, vrnorms, fn))) return rc;
+    if (vpolar) {
+        if (!vcodes || !aligned(vcodes, 4) || vnorms || vsigns || vrnorms)
+            return fail(RQ_EINVAL, "rq_attend: PolarQuant values come as 16-word records in vcodes (vnorms, vsigns, vrnorms NULL)");
+    } else if ((rc = check_record(vctx, vcodes, vnorms, vsigns, vrnorms, fn))) {
+        return rc;
+    }
     if (!(scale == scale) || scale > 3.0e38f || scale < -3.0e38f) return fail(RQ_EINVAL, "rq_attend: scale is not finite");
     const rqk::AttendPlan plan = rqk::attend_plan(hq, group, t);
     if (!workspace || !aligned(workspace, 256)) return fail(RQ_EINVAL, "rq_attend: workspace must be a 256-byte aligned device pointer");
     if (workspace_bytes < plan.bytes) return fail(RQ_EINVAL, "rq_attend: workspace smaller than rq_attend_workspace()");
     if (!out || !aligned(out, 4)) return fail(RQ_EINVAL, "rq_attend: out must be a 4-byte aligned device pointer");
     if (ld_out < rqh::kDim) return fail(RQ_EINVAL, "rq_attend: ld_out < 128");
-    if (vctx->host.lay.mse_bits == 0)
+    if (!vpolar && vctx->host.lay.mse_bits == 0)
         return fail(RQ_EUNSUPPORTED, "rq_attend: value sessions need at least one MSE bit");
     rqk::ScoreTables kt;
     if (kpolar) {
@@ -618,7 +624,17 @@ int rq_attend(const rq_ctx* kctx, const rq_ctx* vctx, const float* q, int hq, in
     } else {
         kt = score_tables(kctx);
     }
-    const rqk::ScoreTables vt = score_tables(vctx);
+    rqk::ScoreTables vt;
+    if (vpolar) {
+        vt.dense = false;
+        vt.polar = true;
+        vt.pol = polar_tables(vctx);
+        vt.mse_bits = 0;
+        vt.qjl = false;
+        vt.qjl_scale = 0.0f;
+    } else {
+        vt = score_tables(vctx);
+    }
     return finish(rqk::attend(kt, vt, q, hq, group, kcodes, knorms, ksigns, krnorms, vcodes, vnorms, vsigns, vrnorms, t,
                               kv_stride, scale, workspace, out, ld_out, static_cast<hipStream_t>(stream)),
                   fn);

@@ -86,11 +86,6 @@ __global__ __launch_bounds__(256) void attend_stats_kernel(const float* __restri
 }
 
 // ------------------------------------------------ pass 3: weighted sums --
-// A partial row: centroid sums for coordinates 0..127, sign sums 0..127,
-// the rotor pad coordinate, padding.
-constexpr int kPartStride = 260;
-constexpr int kPartSigma = 128;
-constexpr int kPartPad = 256;
 
 struct AttendArgs {
     const float* scores;      // [rows][ld] raw estimates of this call's rows
@@ -550,7 +545,22 @@ hipError_t attend(const ScoreTables& kt, const ScoreTables& vt, const float* q, 
     }
     // 2. row statistics
     hipLaunchKernelGGL(attend_stats_kernel, dim3(hq), dim3(kBlock), 0, s, scores, p.ld, t, scale, stats);
-    // 3. weighted sums in the rotated domain
+    // 3. weighted sums in the rotated domain (PolarQuant values: of y~)
+    if (vt.polar) {
+        PolarValueArgs pa;
+        pa.scores = scores;
+        pa.ld = p.ld;
+        pa.stats = stats;
+        pa.scale = scale;
+        pa.words = vcodes;
+        pa.t = t;
+        pa.kv_stride = kv_stride;
+        pa.group = group;
+        pa.rows = hq;
+        pa.part = part;
+        const hipError_t e = polar_attend_values(vt.pol, pa, static_cast<int>(p.producers), kv_heads, s);
+        if (e != hipSuccess) return e;
+    }
     AttendArgs a;
     a.scores = scores;
     a.ld = p.ld;
@@ -567,8 +577,10 @@ hipError_t attend(const ScoreTables& kt, const ScoreTables& vt, const float* q, 
     a.cent = vt.dense ? vt.den.cent : vt.rot.cent;
     a.part = part;
     a.pt = vpt;
-    hipError_t e;
-    if (vt.dense)
+    hipError_t e = hipSuccess;
+    if (vt.polar) {
+        // (done above)
+    } else if (vt.dense)
         e = vt.qjl ? launch_values_b<true, false>(vt.mse_bits, a, p, kv_heads, s)
                    : launch_values_b<false, false>(vt.mse_bits, a, p, kv_heads, s);
     else
@@ -581,11 +593,11 @@ hipError_t attend(const ScoreTables& kt, const ScoreTables& vt, const float* q, 
     c.producers = p.producers;
     c.rows = hq;
     c.stats = stats;
-    c.rotor = !vt.dense;
+    c.rotor = !vt.dense && !vt.polar;
     c.qjl = vt.qjl;
     c.rotmat = vt.rot.rotmat;
-    c.pi_hi = vt.den.pi_hi;
-    c.pi_lo = vt.den.pi_lo;
+    c.pi_hi = vt.polar ? vt.pol.pi_hi : vt.den.pi_hi;   // x~ = Pi^T (sums)
+    c.pi_lo = vt.polar ? vt.pol.pi_lo : vt.den.pi_lo;
     c.s_rows = vt.dense ? vt.den.s_rows : vt.rot.s_rows;
     c.kappa = vt.qjl_scale;
     c.out = out;

@@ -111,6 +111,29 @@ hipError_t score(const ScoreTables& t, const float* q, int hq, int group, const 
                  const PageTable& pt = PageTable{});
 
 
+// A partial row of the attention value pass: centroid sums for coordinates
+// 0..127 (PolarQuant values: the sums of y~), sign sums 0..127, the rotor
+// pad coordinate, padding.
+constexpr int kPartStride = 260;
+constexpr int kPartSigma = 128;
+constexpr int kPartPad = 256;
+
+// The PolarQuant value pass of rq_attend: partial rows [producers][rows]
+// [kPartStride] of sum_t p_t y~_t for the estimates `scores` (row stride ld)
+// and the row statistics `stats` (max, sum of exp) of scale * estimate.
+struct PolarValueArgs {
+    const float* scores;
+    int64_t ld;
+    const float2* stats;
+    float scale;
+    const uint32_t* words;    // value records, 16 words per key; KV head j at row j * kv_stride
+    int64_t t, kv_stride;
+    int group, rows;
+    float* part;
+};
+hipError_t polar_attend_values(const PolarDev& P, const PolarValueArgs& a, int producers, int kv_heads,
+                               hipStream_t s);
+
 // Decode attention over compressed keys and values (rq_attend): workspace
 // layout for hq query rows over t keys, and the launcher.
 struct AttendPlan {

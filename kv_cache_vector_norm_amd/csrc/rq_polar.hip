@@ -592,6 +592,184 @@ __global__ __launch_bounds__(kPqWaves * 64) void pq_score_kernel(PolarDev P, con
     }
 }
 
+// ------------------------------------------------- attention values --
+// Decode attention with PolarQuant values (the weighted-sum pass of
+// rq_attend).  Each wave walks 64-key tiles of its KV head.  Lane l decodes
+// the record of key l into y~ / ||r|| (the levels walked back from the
+// radii, as in the dequantiser; the radii norm ||r|| joins the key's
+// weight), 32 coordinates at a time, into a [coordinate][key] block in LDS;
+// lane (n, h) then takes coordinate 32 nt + n of keys 8h..8h+7 of each
+// 16-key block as split halves (2^11 hi, lo11, hi) against the weights
+// p ||r|| of query row n (hi, lo11) on 32x32x16 MFMAs.  The partial rows
+// hold sum_t p_t y~_t in columns 0..127; the combine applies Pi^T (the
+// dequantiser's x~ = Pi^T y~ is linear) and divides by the sum of weights.
+constexpr int kPvPitch = 68;   // floats per coordinate row of the block (bank spread)
+struct PqValueLds {
+    float2 tab[kPqTab2];
+    float yb[kPqWaves][32][kPvPitch];   // per wave; its first 4 KB also stage the records
+    float rn[kPqWaves][64];
+    float sum[32][kPartStride];
+};
+static_assert(32 * kPvPitch * 4 >= 64 * kPolarWords * 4, "record staging fits in the block");
+
+__global__ __launch_bounds__(kPqWaves * 64) void pq_attend_values_kernel(PolarDev P, PolarValueArgs a) {
+    __shared__ PqValueLds sm;
+    const int qblocks = (a.group + 31) / 32;
+    const int kvh = blockIdx.y / qblocks, qb = blockIdx.y % qblocks;
+    const int row0 = kvh * a.group + qb * 32;
+    const int nrows = min(32, a.group - qb * 32);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t rbase = static_cast<int64_t>(kvh) * a.kv_stride;
+    const int64_t ntiles = (a.t + 63) / 64;
+    pq_tab_to_lds(P.tab, sm.tab);
+    __syncthreads();
+
+    const int l = lane_id();
+    const int n = l & 31, hh = l >> 5;
+    const bool live = n < nrows;
+    const float mrow = live ? a.stats[row0 + n].x : 0.0f;
+    // estimates of this call's rows; rows past nrows lie outside the range and read as zero
+    const rsrc_t rsc = make_rsrc(a.scores + static_cast<int64_t>(row0) * a.ld,
+                                 static_cast<uint32_t>(nrows * a.ld * 4));
+    const float2* tab = sm.tab;
+    float(*yb)[kPvPitch] = sm.yb[wave];
+    uint32_t* stage = reinterpret_cast<uint32_t*>(&sm.yb[wave][0][0]);
+    float* rnw = sm.rn[wave];
+    f32x16 acc[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x16{};
+
+    for (int64_t tile = blockIdx.x * (int64_t)kPqWaves + wave; tile < ntiles; tile += gridDim.x * (int64_t)kPqWaves) {
+        const int64_t kbase = tile * 64;
+        const int kleft = static_cast<int>(a.t - kbase < 64 ? a.t - kbase : 64);   // live keys of the tile
+        const int z = opaque_zero();
+        const int lz = l + z;
+        // estimates of row n for keys 16 kb + 8 hh .. + 7
+        u32x4 sv[4][2];
+        const uint32_t soff = static_cast<uint32_t>((n * a.ld + kbase + 8 * hh) * 4);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                sv[kb][q] = __builtin_amdgcn_raw_buffer_load_b128(rsc, soff, 64 * kb + 16 * q, kNonTemporal);
+        // key lz's record (zero past the end) and its radii norm
+        uint32_t w[kPolarWords];
+        words_load<kPolarWords>(a.words + rbase * kPolarWords, kbase, a.t, w, stage, lz);
+        float R[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) R[i] = h2f((w[12 + (i >> 1)] >> (16 * (i & 1))) & 0xFFFFu);
+        float ss = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ss = __builtin_fmaf(R[i], R[i], ss);
+        const float rn = __builtin_sqrtf(ss);
+        const float inv = rn > 0.0f ? 1.0f / rn : 0.0f;
+        rnw[lz] = rn;
+        wave_lds_sync();
+        // weights p ||r|| of keys 16 kb + 8 hh + k for row n, split
+        u32x4 wh[4], wl[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const int k0 = 16 * kb + 8 * hh;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float w2[2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int k = 2 * q + e;
+                    const uint32_t sbits = sv[kb][k >> 2][k & 3];
+                    const float sc = __builtin_bit_cast(float, sbits);
+                    const bool in = live && k0 + k < kleft;
+                    const float ex = in ? __builtin_amdgcn_exp2f((sc * a.scale - mrow) * 1.44269504088896341f) : 0.0f;
+                    w2[e] = ex * rnw[k0 + k];
+                }
+                const uint32_t h = cvt_pk(w2[0], w2[1]);
+                wh[kb][q] = h;
+                wl[kb][q] = cvt_pk((w2[0] - h2f(h & 0xFFFFu)) * 2048.0f, (w2[1] - h2f(h >> 16)) * 2048.0f);
+            }
+        }
+        // y~ / ||r||, 32 coordinates (M tile MT of the dequantiser) at a time
+#pragma unroll
+        for (int MT = 0; MT < 4; ++MT) {
+            float r3[4], r2[8], r1[16];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int I = 2 * MT + i;
+                const float2 cs = tab[kPqCen + 8 + ((w[11] >> (2 * I)) & 3u)];
+                const float r = R[I] * inv;
+                r3[2 * i] = r * cs.x;
+                r3[2 * i + 1] = r * cs.y;
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int J = 4 * MT + j;
+                const float2 cs = tab[kPqCen + 4 + ((w[10] >> (2 * J)) & 3u)];
+                r2[2 * j] = r3[j] * cs.x;
+                r2[2 * j + 1] = r3[j] * cs.y;
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int K = 8 * MT + k;
+                const float2 cs = tab[kPqCen + ((w[8 + (K >> 4)] >> (2 * (K & 15))) & 3u)];
+                r1[2 * k] = r2[k] * cs.x;
+                r1[2 * k + 1] = r2[k] * cs.y;
+            }
+            wave_lds_sync();   // the previous block's reads (or the record staging) are done
+#pragma unroll
+            for (int m = 0; m < 16; ++m) {
+                const int M = 16 * MT + m;
+                const float2 cs = tab[kPqCen0 + ((w[M >> 3] >> (4 * (M & 7))) & 15u)];
+                yb[2 * m][lz] = r1[m] * cs.x;
+                yb[2 * m + 1][lz] = r1[m] * cs.y;
+            }
+            wave_lds_sync();
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const float4 y0 = *reinterpret_cast<const float4*>(&yb[n][16 * kb + 8 * hh]);
+                const float4 y1 = *reinterpret_cast<const float4*>(&yb[n][16 * kb + 8 * hh + 4]);
+                const float y[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+                u32x4 b11, blo, bhi;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t h = cvt_pk(y[2 * q], y[2 * q + 1]);
+                    bhi[q] = h;
+                    b11[q] = pk_scale2048(h);
+                    blo[q] = cvt_pk((y[2 * q] - h2f(h & 0xFFFFu)) * 2048.0f, (y[2 * q + 1] - h2f(h >> 16)) * 2048.0f);
+                }
+                acc[MT] = mfma(wh[kb], b11, acc[MT]);
+                acc[MT] = mfma(wh[kb], blo, acc[MT]);
+                acc[MT] = mfma(wl[kb], bhi, acc[MT]);
+            }
+        }
+        wave_lds_sync();   // this tile's block reads are done before the next staging
+    }
+
+    // the block's partial rows: the four waves' sums added in wave order
+    // through LDS, then written as producer blockIdx.x
+    const float uc = 1.0f / 2048.0f;
+    for (int wv = 0; wv < kPqWaves; ++wv) {
+        if (wave == wv) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = own_row(hh, r);
+                if (m < nrows) {
+                    float* dst = sm.sum[m];
+#pragma unroll
+                    for (int nt = 0; nt < 4; ++nt) {
+                        const float c = acc[nt][r] * uc;
+                        dst[32 * nt + n] = wv == 0 ? c : dst[32 * nt + n] + c;
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+    float* out = a.part + (static_cast<int64_t>(blockIdx.x) * a.rows + row0) * kPartStride;
+    for (int i = threadIdx.x; i < nrows * kPartStride; i += kPqWaves * 64) {
+        const int m = i / kPartStride, c = i % kPartStride;
+        out[static_cast<int64_t>(m) * kPartStride + c] = c < kD ? sm.sum[m][c] : 0.0f;
+    }
+}
+
 // ------------------------------------------------------------ launchers --
 static int pq_grid(int64_t n, int64_t cap) {
     const int64_t ntiles = (n + 63) / 64;
@@ -639,6 +817,13 @@ hipError_t polar_score(const PolarDev& P, const float* q, int hq, int group, con
     const int gx = pq_grid(t, want > 0 ? want : 1);
     hipLaunchKernelGGL(pq_score_kernel, dim3(gx, gy), dim3(kPqWaves * 64), 0, s, P, q, group, chunks, words, t,
                        kv_stride, scores, ld_scores);
+    return hipGetLastError();
+}
+
+hipError_t polar_attend_values(const PolarDev& P, const PolarValueArgs& a, int producers, int kv_heads,
+                               hipStream_t s) {
+    const int qblocks = (a.group + 31) / 32;
+    hipLaunchKernelGGL(pq_attend_values_kernel, dim3(producers, kv_heads * qblocks), dim3(kPqWaves * 64), 0, s, P, a);
     return hipGetLastError();
 }
 
