@@ -227,3 +227,29 @@ def attend(p: PolarParams, pv, q, words, vrec, group, t, scale, kv_stride=None):
         e = np.exp(s - s.max())
         out[h] = (e / e.sum()) @ OC.dequantize(pv, OC._rows(vrec, rows))
     return out
+
+
+def attend_values(pk, pv, q, keys, vwords, group, t, scale, kv_stride=None):
+    """Decode attention with PolarQuant values: softmax(scale * <q_h, k~_t>)
+    weighs the values decoded from their PolarQuant records (pv, the value
+    session), the KV-cache section's softmax(Q K^T / sqrt(d)) V with V read
+    from its PolarQuant records.  Keys are scored by their own session: pk a
+    PolarParams (keys: 16-word records) or a codec Params (keys: a codec
+    Record, scored by the codec's estimator).  Query head h reads KV head
+    j = h // group, whose keys and values start at row j * kv_stride.
+    Returns [H, d]."""
+    from . import codec as OC
+    kv_stride = t if kv_stride is None else kv_stride
+    q = np.asarray(q, dtype=np.float64)
+    out = np.zeros((q.shape[0], D))
+    for h in range(q.shape[0]):
+        j = h // group
+        rows = slice(j * kv_stride, j * kv_stride + t)
+        if isinstance(pk, PolarParams):
+            s = score(pk, q[h:h + 1], np.asarray(keys)[rows])[0]
+        else:
+            s = OC.score(pk, q[h:h + 1], OC._rows(keys, rows))[0]
+        s = scale * s
+        e = np.exp(s - s.max())
+        out[h] = (e / e.sum()) @ dequantize(pv, np.asarray(vwords)[rows])
+    return out

@@ -221,3 +221,70 @@ def test_attention_over_polar_keys(K, P, t, kvh, group, vspec):
     with pytest.raises(K.RQError):
         K.rq_attend(kc.ctx, vc.ctx, qd, kvh * group, group, kw, vrec.norms, None, None, vrec.codes, vrec.norms,
                     vrec.signs, vrec.rnorms, t, t, scale, 0, 0, out, D)
+
+
+@pytest.mark.parametrize("t,kvh,group", [(1000, 2, 4), (63, 3, 1), (4097, 1, 8), (200, 2, 32), (130, 1, 40)])
+@pytest.mark.parametrize("kspec", ["polar", "rotor+qjl3", "dense2"])
+def test_attention_over_polar_values(K, P, t, kvh, group, kspec):
+    """rq_attend with PolarQuant values (keys: PolarQuant, rotor with QJL,
+    TurboQuant dense): end to end against the oracle within the bound the
+    score tolerance implies, and with the GPU's own estimates within 1e-5
+    of the largest value coordinate of the decoded values."""
+    from oracle import codec as OC
+    from oracle import params as OP
+    pv = PQ.PolarParams(D, 3)
+    vc = K.PolarCodec(seed=3)
+    keys = W.gaussian(kvh * t, seed=131, dtype=np.float16)
+    vals = W.gaussian(kvh * t, seed=132, dtype=np.float16)
+    q = W.queries(kvh * group, seed=133)
+    if kspec == "polar":
+        kc, pk = K.PolarCodec(seed=0), P
+    else:
+        bits, mode = (3, OP.QJL) if kspec == "rotor+qjl3" else (2, OP.DENSE)
+        kc, pk = K.Codec(bits=bits, seed=0, mode=mode), OP.Params(D, bits, 0, mode)
+    kd = kc.quantize(torch.from_numpy(keys).cuda())
+    vw = vc.quantize(torch.from_numpy(vals).cuda())
+    qd = torch.from_numpy(q).cuda()
+    scale = 1 / np.sqrt(D)
+    out = K.attend(kc, vc, qd, kd, vw, group, t, t, scale)
+    s = kc.score(qd, kd, group, t)
+    torch.cuda.synchronize()
+    if kspec == "polar":
+        hk = _words(kd)
+        knorm = PR.polar_radius_norm(hk)
+    else:
+        hk = PR.record_from_host(*kd.host())
+        knorm = OC.half_value(hk.norms)
+    hv = _words(vw)
+    ref = PQ.attend_values(pk, pv, q.astype(np.float64), hk, hv, group, t, scale)
+    got = out.cpu().numpy().astype(np.float64)
+    sg = s.cpu().numpy().astype(np.float64)
+    for h in range(kvh * group):
+        j = h // group
+        xv = PQ.dequantize(pv, hv[j * t:(j + 1) * t])
+        vmax = np.abs(xv).max()
+        kmax = knorm[j * t:(j + 1) * t].max()
+        lim = (2e-4 * scale * np.linalg.norm(q[h]) * kmax + 1e-5) * vmax
+        assert np.abs(got[h] - ref[h]).max() <= lim, (h, np.abs(got[h] - ref[h]).max() / lim)
+        z = scale * sg[h]
+        wgt = np.exp(z - z.max())
+        assert np.abs(got[h] - (wgt / wgt.sum()) @ xv).max() <= 1e-5 * vmax, h
+
+
+def test_attention_polar_values_argument_checks(K):
+    """PolarQuant values come as word records only."""
+    kc, vc = K.Codec(bits=3, seed=0, mode=K.RQ_QJL), K.PolarCodec(seed=3)
+    t = 64
+    kd = kc.quantize(torch.zeros((t, D), dtype=torch.float16, device="cuda"))
+    vw = vc.quantize(torch.zeros((t, D), dtype=torch.float16, device="cuda"))
+    qd = torch.zeros((2, D), device="cuda")
+    out = torch.empty((2, D), device="cuda")
+    ws = torch.empty(K.rq_attend_workspace(2, 2, t) + 256, dtype=torch.uint8, device="cuda")
+    base = ws.data_ptr() + ((-ws.data_ptr()) % 256)
+    with pytest.raises(K.RQError):
+        K.rq_attend(kc.ctx, vc.ctx, qd, 2, 2, kd.codes, kd.norms, kd.signs, kd.rnorms, vw, kd.norms, None, None,
+                    t, t, 1.0, base, ws.numel() - 256, out, D)
+    K.rq_attend(kc.ctx, vc.ctx, qd, 2, 2, kd.codes, kd.norms, kd.signs, kd.rnorms, vw, None, None, None,
+                t, t, 1.0, base, ws.numel() - 256, out, D)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()

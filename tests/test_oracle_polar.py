@@ -143,3 +143,37 @@ def test_attention_over_polar_keys():
     gap = s[7] - np.max(np.delete(s, 7))
     assert gap > 30
     assert np.abs(out[0] - xv[7]).max() < t * np.exp(-gap) * np.abs(xv).max() + 1e-12
+
+
+def test_attention_over_polar_values():
+    """PolarQuant values: scale 0 gives the mean of the decoded values, a
+    single key its decoded value, and a dominant key its value (per GQA
+    head; rotor-scored and polar-scored keys)."""
+    from oracle import codec as OC
+    from oracle import params as OP
+    pv = PQ.PolarParams(128, 3)
+    t, kvh, group = 20, 2, 3
+    vw, _ = PQ.quantize(pv, W.gaussian(kvh * t, seed=11).astype(np.float64))
+    xv = PQ.dequantize(pv, vw)
+    q = W.queries(kvh * group, seed=12).astype(np.float64)
+    k = W.gaussian(kvh * t, seed=13).astype(np.float64)
+    k[5] = 4.0 * q[0]                                    # head 0's dominant key for query row 0
+    pk_rotor = OP.Params(128, 3, 0, OP.QJL)
+    krec, _ = OC.quantize(pk_rotor, k)
+    pk_polar = PQ.PolarParams(128, 0)
+    kw, _ = PQ.quantize(pk_polar, k)
+    for pk, keys in ((pk_rotor, krec), (pk_polar, kw)):
+        out0 = PQ.attend_values(pk, pv, q, keys, vw, group, t, 0.0)
+        for h in range(kvh * group):
+            j = h // group
+            assert np.abs(out0[h] - xv[j * t:(j + 1) * t].mean(0)).max() < 1e-14
+        one = PQ.attend_values(pk, pv, q[:group], keys, vw, group, 1, 1.0)
+        assert np.abs(one - xv[:1]).max() < 1e-14
+        out = PQ.attend_values(pk, pv, q, keys, vw, group, t, 1.0)
+        if isinstance(pk, PQ.PolarParams):
+            s = PQ.score(pk, q[:1], kw[:t])[0]
+        else:
+            s = OC.score(pk, q[:1], OC._rows(krec, slice(0, t)))[0]
+        gap = s[5] - np.max(np.delete(s, 5))
+        assert gap > 30
+        assert np.abs(out[0] - xv[5]).max() < t * np.exp(-gap) * np.abs(xv).max() + 1e-12
