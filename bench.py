@@ -345,7 +345,16 @@ def workload_extras(K, W, dev, stream):
         pdus = _timed(stream, lambda i: pc.score(q.view(L * HQ, 128), pw, g, T, T, out=scores.view(L * HQ, T)), 5)
         paus = _timed(stream, lambda i: K.attend(pc, c, q.view(L * HQ, 128), pw, vrec, g, T, T, out=att,
                                                  workspace=ws), 3)
-        del pw, pc
+        # PolarQuant values of the same cache: attention with the rotor keys,
+        # and with PolarQuant keys and values
+        pv = K.PolarCodec(seed=3)
+        pvw = pv.alloc_words(n_k, dev)
+        pv.quantize(flat[n_k:], words=pvw)
+        pvus = _timed(stream, lambda i: K.attend(c, pv, q.view(L * HQ, 128), krec, pvw, g, T, T, out=att,
+                                                 workspace=ws), 3)
+        ppus = _timed(stream, lambda i: K.attend(pc, pv, q.view(L * HQ, 128), pw, pvw, g, T, T, out=att,
+                                                 workspace=ws), 3)
+        del pw, pc, pvw, pv
         nv = flat.shape[0]
         ns = L * HQ * T
         out[spec["name"]] = {
@@ -361,7 +370,9 @@ def workload_extras(K, W, dev, stream):
             "polar_keys_quantize_gbs": round(n_k * (256 + 64) / (pqus * 1e-6) / 1e9, 1),
             "polar_decode_step_us": round(pdus, 1),
             "polar_decode_scores_per_s": round(ns / (pdus * 1e-6), 1),
-            "polar_keys_decode_attention_us": round(paus, 1)}
+            "polar_keys_decode_attention_us": round(paus, 1),
+            "polar_values_decode_attention_us": round(pvus, 1),
+            "polar_keys_and_values_decode_attention_us": round(ppus, 1)}
         del kv, q, flat, rec, scores, subs, c, krec, vrec, ws, att
         torch.cuda.empty_cache()
     return out
