@@ -288,3 +288,29 @@ def test_attention_polar_values_argument_checks(K):
                 t, t, 1.0, base, ws.numel() - 256, out, D)
     torch.cuda.synchronize()
     assert torch.isfinite(out).all()
+
+
+def test_attention_polar_values_strided_heads(K, P):
+    """PolarQuant keys and values of three KV heads 130 rows apart, 100 keys
+    each (the rows between heads hold other data)."""
+    t, stride, kvh, group = 100, 130, 3, 2
+    pv = PQ.PolarParams(D, 3)
+    kc, vc = K.PolarCodec(seed=0), K.PolarCodec(seed=3)
+    keys = W.gaussian(kvh * stride, seed=141, dtype=np.float16)
+    vals = W.gaussian(kvh * stride, seed=142, dtype=np.float16)
+    q = W.queries(kvh * group, seed=143)
+    kw = kc.quantize(torch.from_numpy(keys).cuda())
+    vw = vc.quantize(torch.from_numpy(vals).cuda())
+    scale = 1 / np.sqrt(D)
+    out = K.attend(kc, vc, torch.from_numpy(q).cuda(), kw, vw, group, t, stride, scale)
+    torch.cuda.synchronize()
+    hk, hv = _words(kw), _words(vw)
+    ref = PQ.attend_values(P, pv, q.astype(np.float64), hk, hv, group, t, scale, stride)
+    got = out.cpu().numpy().astype(np.float64)
+    for h in range(kvh * group):
+        j = h // group
+        xv = PQ.dequantize(pv, hv[j * stride:j * stride + t])
+        vmax = np.abs(xv).max()
+        kmax = PR.polar_radius_norm(hk[j * stride:j * stride + t]).max()
+        lim = (2e-4 * scale * np.linalg.norm(q[h]) * kmax + 1e-5) * vmax
+        assert np.abs(got[h] - ref[h]).max() <= lim, h
