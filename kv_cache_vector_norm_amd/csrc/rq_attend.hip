@@ -13,7 +13,10 @@
 //   sum_t p_t v~_t = X^T (sum_t p_t n^_t c_t) + kappa S^T (sum_t p_t n^_t gamma^_t sigma_t).
 // The two sums are products of a weight matrix [rows x keys] with the
 // centroid / sign matrices [keys x coordinates] and run on 32x32x16 fp16
-// MFMAs; X^T and S^T are applied once per query row at the end.
+// MFMAs; X^T and S^T are applied once per query row at the end.  PolarQuant
+// values are the one kind decoded (to y~ = Pi x~, in rq_polar.hip's value
+// pass): sum_t p_t v~_t = Pi^T (sum_t p_t y~_t), Pi^T once per row.  PolarQuant
+// keys are scored by pq_score in pass 1.
 //
 // Passes (all on the caller's stream, workspace from the caller):
 //   1. the estimates s (rq_score's kernel) into the workspace;
