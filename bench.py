@@ -44,7 +44,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--sweep", action="store_true", help="also time the MSE-only roundtrip over an N sweep")
+    ap.add_argument("--sweep", action="store_true",
+                    help="also time the MSE-only and the 2-bit + QJL roundtrips over an N sweep")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-workloads", action="store_true",
                     help="skip the 262,144-key dense sweep and the model-shaped cache measurements")
@@ -502,24 +503,27 @@ def main():
     del pw, pc
 
     if a.sweep:
-        sweep = {}
-        for n in (65536, 262144, 1048576, 4194304, 16777216):
-            xb = torch.randn((n, 128), device=dev).to(torch.float16)
-            yb = torch.empty_like(xb)
-            rb = mse.alloc_record(n, dev)
-            for _ in range(3):
-                mse.roundtrip(xb, rec=rb, out=yb)
-            reps = max(3, min(50, int(4e8 // (n * 566))))
-            torch.cuda.synchronize()
-            e0.record(stream)
-            for _ in range(reps):
-                mse.roundtrip(xb, rec=rb, out=yb)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) * 1e3 / reps
-            sweep[str(n)] = {"us": round(us, 2), "gbs": round(n * mb / (us * 1e-6) / 1e9, 1)}
-            del xb, yb, rb
-        extras["mse3_sweep"] = sweep
+        # the MSE-only 3-bit roundtrip and the headline 2-bit + QJL one over N
+        sweeps = {"mse3_sweep": (mse, mb), "qjl3_sweep": (codec, algorithmic_bytes(lay))}
+        for key, (cdc, nb) in sweeps.items():
+            sweep = {}
+            for n in (65536, 262144, 1048576, 4194304, 16777216):
+                xb = torch.randn((n, 128), device=dev).to(torch.float16)
+                yb = torch.empty_like(xb)
+                rb = cdc.alloc_record(n, dev)
+                for _ in range(3):
+                    cdc.roundtrip(xb, rec=rb, out=yb)
+                reps = max(3, min(50, int(4e8 // (n * 566))))
+                torch.cuda.synchronize()
+                e0.record(stream)
+                for _ in range(reps):
+                    cdc.roundtrip(xb, rec=rb, out=yb)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) * 1e3 / reps
+                sweep[str(n)] = {"us": round(us, 2), "gbs": round(n * nb / (us * 1e-6) / 1e9, 1)}
+                del xb, yb, rb
+            extras[key] = sweep
 
     # achievable-HBM reference: a plain device copy of 1 GiB (read + write)
     src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
