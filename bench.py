@@ -11,15 +11,24 @@ that every step reads cold data from HBM rather than from the 256 MB
 last-level cache.
 
 Prints one JSON line.  `value` is quant+dequant vectors per second of whole
-steps; per-kernel times come from HIP events on the launch stream around
-the launches of every eighth timed step.
+steps (host clock around the K steps).  Kernel times come from HIP events on
+the launch stream around back-to-back launches over the rotating buffer sets
+(median of several trials), so they hold only the kernels and the gaps
+between them.  The line also carries the reference copy of the same bytes
+(the practical HBM ceiling), the 1,024-vector fp32 quality row, the
+roundtrips over an N sweep, the other codecs and workload shapes, and the
+float64 CPU oracle timed on one core and on all host cores.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--sweep]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep]
+                    [--no-workloads] [--no-cpu]
+    python bench.py --profile-set        # the kernels the profiles/ summaries cover
+    python bench.py --summarize DIR      # rocprofv3 CSVs of --profile-set -> profiles/
 """
 import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -28,10 +37,11 @@ sys.path.insert(0, ROOT)
 
 N_VEC = 65536
 N_Q = 64
-EVENT_EVERY = 8
 BITS = 3
 HBM_PEAK_GBS = 8000.0
 FP16_MFMA_PEAK_TFLOPS = 2500.0
+CPU_SHARE = 16          # host threads one GPU's share of the box may use
+ORACLE_SECONDS = 8.0    # wall time of each CPU oracle leg
 
 
 def algorithmic_bytes(lay, in_bytes=256, out_bytes=256):
@@ -44,19 +54,19 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--sweep", action="store_true",
-                    help="also time the MSE-only and the 2-bit + QJL roundtrips over an N sweep")
+    ap.add_argument("--trials", type=int, default=10, help="trials of back-to-back launches per kernel time")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the roundtrips over the N sweep")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-workloads", action="store_true",
                     help="skip the 262,144-key dense sweep and the model-shaped cache measurements")
-    ap.add_argument("--copy-bytes", type=int, default=0,
-                    help="after timing, run 3 plain device copies of this many bytes (counter calibration)")
-    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this bench with "
-                         "--copy-bytes into profiles/traffic.json, then exit")
+    ap.add_argument("--profile-set", action="store_true",
+                    help="run each profiled kernel a few times (for rocprofv3) and exit")
+    ap.add_argument("--summarize", metavar="DIR",
+                    help="turn rocprofv3 runs of --profile-set under DIR into profiles/ summaries, then exit")
     return ap.parse_args()
 
 
+# ------------------------------------------------- machine-code digests --
 MAGIC_BUNDLE = b"__CLANG_OFFLOAD_BUNDLE__"
 
 
@@ -74,19 +84,17 @@ def _elf_sections(data):
     return out, hdrs
 
 
-def kernel_code_digest(kernel_symbol=None):
-    """First 16 hex digits of a sha256 over built gfx950 machine code in
-    librq.so: of one kernel's instructions when `kernel_symbol` (its mangled
-    name) is given, else of the whole offload section.  It changes exactly
-    when that code does, not for edits that leave it alone."""
+def kernel_digests():
+    """{mangled kernel symbol: first 16 hex digits of a sha256 over its
+    gfx950 machine code} for every kernel in librq.so (built here from this
+    repository's sources).  A digest changes exactly when that code does."""
     import struct
     with open(os.path.join(ROOT, "kv_cache_vector_norm_amd", "librq.so"), "rb") as f:
         data = f.read()
     secs, _ = _elf_sections(data)
     off, size = secs[".hip_fatbin"][0], secs[".hip_fatbin"][1]
     fatbin = data[off:off + size]
-    if kernel_symbol is None:
-        return hashlib.sha256(fatbin).hexdigest()[:16]
+    out = {"": hashlib.sha256(fatbin).hexdigest()[:16]}
     start = fatbin.find(MAGIC_BUNDLE)
     while start >= 0:
         n = struct.unpack_from("<Q", fatbin, start + len(MAGIC_BUNDLE))[0]
@@ -108,134 +116,481 @@ def kernel_code_digest(kernel_symbol=None):
                 st_name, st_info, st_other, st_shndx, st_value, st_size = struct.unpack_from(
                     "<IBBHQQ", co, so + k * ent)
                 name = co[stro + st_name:co.index(b"\0", stro + st_name)].decode()
-                if name == kernel_symbol and st_size:
+                if st_size and (st_info & 0xF) == 2 and not name.endswith(".kd"):
                     sh = hdrs[st_shndx]
                     foff = sh[4] + (st_value - sh[3])
-                    return hashlib.sha256(co[foff:foff + st_size]).hexdigest()[:16]
+                    out[name] = hashlib.sha256(co[foff:foff + st_size]).hexdigest()[:16]
         start = fatbin.find(MAGIC_BUNDLE, start + 1)
-    raise RuntimeError(f"kernel {kernel_symbol} not found in librq.so")
+    return out
 
 
-def measured_traffic(kernel, digest):
+def kernel_code_digest(kernel_symbol=None, _cache={}):
+    """Digest of one kernel's machine code (its mangled name), or of the
+    whole offload section when kernel_symbol is None."""
+    if "d" not in _cache:
+        _cache["d"] = kernel_digests()
+    d = _cache["d"]
+    key = kernel_symbol or ""
+    if key not in d:
+        raise RuntimeError(f"kernel {kernel_symbol} not found in librq.so")
+    return d[key]
+
+
+def digest_of(mangled_part):
+    """Digest of the one kernel whose mangled name contains `mangled_part`."""
+    hits = [s for s in kernel_digests() if s and mangled_part in s]
+    if len(hits) != 1:
+        raise RuntimeError(f"{len(hits)} kernels match {mangled_part}")
+    return kernel_code_digest(hits[0])
+
+
+ROUNDTRIP_KERNEL = "rq_quant_kernel<2, true, true, true, true>"
+ROUNDTRIP_SYMBOL = "_ZN3rqk15rq_quant_kernelILi2ELb1ELb1ELb1ELb1EEEvNS_8RotorDevEPKcllPjPtS4_S5_Pcl"
+
+
+# -------------------------------------------------- profiled kernel set --
+# Each case of --profile-set: (label, kernel name prefix in rocprofv3 output,
+# mangled-name part for the code digest, launches (one warm-up + timed),
+# algorithmic bytes per launch, useful MFMA flops per launch, what it is).
+def profile_cases():
+    n1, nm, nd = N_VEC, 1 << 20, 262144
+    fl = 2 * 128 * 128      # flops of one 128 x 128 matrix-vector product
+    return [
+        ("copy_65536_same_bytes", "rqk::copy_kernel", "11copy_kernel", 4, n1 * 568, 0,
+         "reference copy of 65,536 x 568 B (read 284 B, write 284 B per vector)"),
+        ("rq_roundtrip_qjl3_65536", "rqk::rq_quant_kernel<2, true, true, true, true>",
+         "15rq_quant_kernelILi2ELb1ELb1ELb1ELb1EE", 4, n1 * 568, 0,
+         "rotor roundtrip, 2-bit codes + QJL, fp16 in/out, 65,536 keys (the step's codec kernel)"),
+        ("rq_score_64x65536", "rqk::score_kernel<2, true, true, 2>", "12score_kernelILi2ELb1ELb1ELi2EE", 4,
+         n1 * 56 + 4 * N_Q * n1, 0, "q.k estimates of 64 queries against 65,536 compressed keys"),
+        ("rq_roundtrip_mse3_65536", "rqk::rq_quant_kernel<3, false, true, true, true>",
+         "15rq_quant_kernelILi3ELb0ELb1ELb1ELb1EE", 4, n1 * 566, 0,
+         "rotor roundtrip, 3-bit MSE only, fp16 in/out, 65,536 keys"),
+        ("rq_roundtrip_mse3_1048576", "rqk::rq_quant_kernel<3, false, true, true, true>",
+         "15rq_quant_kernelILi3ELb0ELb1ELb1ELb1EE", 4, nm * 566, 0,
+         "rotor roundtrip, 3-bit MSE only, fp16 in/out, 1,048,576 keys"),
+        ("copy_1048576_same_bytes", "rqk::copy_kernel", "11copy_kernel", 4, nm * 566, 0,
+         "reference copy of 1,048,576 x 566 B"),
+        ("tq_roundtrip_dense3_262144", "rqk::tq_quant_kernel<3, false, true, true, true,",
+         "15tq_quant_kernelILi3ELb0ELb1ELb1ELb1ELi", 4, nd * (256 + 50 + 256), nd * 2 * fl * 3,
+         "TurboQuant roundtrip, 3-bit MSE, fp16 in/out, 262,144 keys (flops: Pi x, Pi^T y, 3 fp16 MFMAs each)"),
+        ("tq_roundtrip_dense_qjl3_262144", "rqk::tq_quant_kernel<2, true, true, true, true,",
+         "15tq_quant_kernelILi2ELb1ELb1ELb1ELb1ELi", 4, nd * (256 + 52 + 256), nd * fl * (3 + 3 + 2 + 2 + 1),
+         "TurboQuant roundtrip, 2-bit + QJL, fp16 in/out, 262,144 keys"),
+        ("rq_attend_values_qwen", "rqk::attend_values_kernel<2, false, true, true>",
+         "20attend_values_kernelILi2ELb0ELb1ELb1EE", 4, 0, 0,
+         "decode attention value pass (centroid sums), Qwen2.5-3B-shaped cache, all layers"),
+        ("rq_attend_signs_qwen", "rqk::attend_values_kernel<1, true, false, false>",
+         "20attend_values_kernelILi1ELb1ELb0ELb0EE", 4, 0, 0,
+         "decode attention value pass (sign sums), Qwen2.5-3B-shaped cache, all layers"),
+        ("copy_calibration_256mib", "rqk::copy_kernel", "11copy_kernel", 1, 2 * (256 << 20), 0,
+         "counter calibration: reference copy of 256 MiB"),
+    ]
+
+
+def profile_set(K, W, dev):
+    """Launch every case of profile_cases() in order: one warm-up and three
+    timed launches each (one launch for the calibration copy), nothing else
+    from this library in between."""
+    import torch
+    stream = torch.cuda.current_stream()
+
+    def note(label):
+        torch.cuda.synchronize()
+        print(f"profile-set: {label}", flush=True)
+
+    x = torch.from_numpy(W.keys_65536()).to(dev)
+    q = torch.from_numpy(W.queries_64()).to(dev)
+    big = torch.empty((1 << 20, 128), dtype=torch.float16, device=dev)
+    big.normal_()
+    ybig = torch.empty_like(big)
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.random_(0, 255)
+
+    def copy(nbytes, times):
+        for _ in range(times):
+            K.rq_bench_copy(src, dst, nbytes, stream)
+
+    note("copy_65536_same_bytes")
+    copy(N_VEC * 284, 4)
+    c = K.Codec(bits=3, seed=0, mode=K.RQ_QJL)
+    rec = c.alloc_record(N_VEC, dev)
+    y = torch.empty_like(x)
+    note("rq_roundtrip_qjl3_65536")
+    for _ in range(4):
+        c.roundtrip(x, rec=rec, out=y)
+    sc = torch.empty((N_Q, N_VEC), dtype=torch.float32, device=dev)
+    note("rq_score_64x65536")
+    for _ in range(4):
+        c.score(q, rec, N_Q, N_VEC, out=sc)
+    m = K.Codec(bits=3, seed=0, mode=K.RQ_MSE)
+    mrec = m.alloc_record(1 << 20, dev)
+    note("rq_roundtrip_mse3_65536")
+    for _ in range(4):
+        m.roundtrip(x, rec=mrec, out=y)
+    note("rq_roundtrip_mse3_1048576")
+    for _ in range(4):
+        m.roundtrip(big, rec=mrec, out=ybig)
+    note("copy_1048576_same_bytes")
+    copy((1 << 20) * 283, 4)
+    xd = big[:262144]
+    yd = ybig[:262144]
+    for label, bits, mode in (("tq_roundtrip_dense3_262144", 3, K.RQ_DENSE),
+                              ("tq_roundtrip_dense_qjl3_262144", 3, K.RQ_DENSE | K.RQ_QJL)):
+        dc = K.Codec(bits=bits, seed=0, mode=mode)
+        drec = dc.alloc_record(262144, dev)
+        note(label)
+        for _ in range(4):
+            dc.roundtrip(xd, rec=drec, out=yd)
+        del dc, drec
+    del big, ybig, mrec
+    spec = W.QWEN25_3B
+    L, H, T, HQ = spec["layers"], spec["kv_heads"], spec["tokens"], spec["q_heads"]
+    kv, qq = W.kv_cache(spec, device=dev, base_seed=1, torch=torch)
+    flat = kv.view(-1, 128)
+    crec = c.alloc_record(flat.shape[0], dev)
+    c.quantize(flat, rec=crec)
+    n_k = L * H * T
+    krec = K.Record(crec.codes[:n_k], crec.norms[:n_k], crec.signs[:n_k], crec.rnorms[:n_k])
+    vrec = K.Record(crec.codes[n_k:], crec.norms[n_k:], crec.signs[n_k:], crec.rnorms[n_k:])
+    g = HQ // H
+    ws = torch.empty(K.rq_attend_workspace(L * HQ, g, T) + 256, dtype=torch.uint8, device=dev)
+    att = torch.empty((L * HQ, 128), dtype=torch.float32, device=dev)
+    note("rq_attend_qwen (rq_attend_values_qwen, rq_attend_signs_qwen)")
+    for _ in range(4):
+        K.attend(c, c, qq.view(L * HQ, 128), krec, vrec, g, T, T, out=att, workspace=ws)
+    del kv, crec, ws
+    note("copy_calibration_256mib")
+    copy(256 << 20, 1)
+    torch.cuda.synchronize()
+    print("profile-set: done", flush=True)
+
+
+# --------------------------------------------- rocprofv3 CSV summaries --
+PMC_PASSES = {
+    "fetch": ["FETCH_SIZE"],
+    "write": ["WRITE_SIZE"],
+    "busy": ["VALUBusy", "MfmaUtil", "OccupancyPercent", "LDSBankConflict"],
+    "insts": ["SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS"],
+    "insts2": ["SQ_INSTS_SALU", "SQ_INSTS_SMEM", "SQ_INSTS_VMEM_RD", "SQ_INSTS_VMEM_WR"],
+}
+
+
+def _read_csv(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _find(dirpath, suffix):
+    for base, _, files in os.walk(dirpath):
+        for fn in files:
+            if fn.endswith(suffix):
+                return os.path.join(base, fn)
+    return None
+
+
+def _col(row, *names):
+    for n in names:
+        if n in row and row[n] != "":
+            return row[n]
+    return None
+
+
+def _assign(names_in_order, cases):
+    """Dispatch indices (in order) of each case: the k-th group of `launches`
+    dispatches whose kernel name starts with the case's prefix."""
+    taken = {}
+    out = {}
+    for label, prefix, _, launches, *_ in cases:
+        idx = [i for i, nm in enumerate(names_in_order) if nm.startswith(prefix)]
+        start = taken.get(prefix, 0)
+        out[label] = idx[start:start + launches]
+        taken[prefix] = start + launches
+    return out
+
+
+def summarize(d):
+    """profiles/ summaries from rocprofv3 runs of `bench.py --profile-set`
+    kept under d: kt/ (kernel trace) and one directory per PMC pass."""
+    cases = profile_cases()
+    trace = _read_csv(_find(os.path.join(d, "kt"), "kernel_trace.csv"))
+    trace.sort(key=lambda r: int(r["Start_Timestamp"]))
+    names = [r["Kernel_Name"] for r in trace]
+    where = _assign(names, cases)
+    res = {}
+    for label, prefix, mpart, launches, alg, flops, what in cases:
+        rows = [trace[i] for i in where[label]]
+        timed = rows[1:] if len(rows) > 1 else rows
+        durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in timed]
+        r0 = rows[0] if rows else {}
+        res[label] = {
+            "what": what, "kernel": prefix, "code": digest_of(mpart), "launches": len(rows),
+            "avg_us": round(sum(durs) / len(durs), 2) if durs else None,
+            "vgpr": _col(r0, "Arch_VGPR_Count", "VGPR_Count", "arch_vgpr_count"),
+            "agpr": _col(r0, "Accum_VGPR_Count", "accum_vgpr_count"),
+            "sgpr": _col(r0, "SGPR_Count", "sgpr_count"),
+            "lds_bytes": _col(r0, "LDS_Block_Size", "Group_Segment_Size", "lds_block_size"),
+            "scratch_bytes": _col(r0, "Scratch_Size", "Private_Segment_Size", "scratch_size"),
+            "grid": _col(r0, "Grid_Size", "Grid_Size_X", "grid_size"),
+            "workgroup": _col(r0, "Workgroup_Size", "Workgroup_Size_X", "workgroup_size"),
+            "alg_bytes": alg, "flops": flops,
+        }
+        if durs and alg:
+            res[label]["alg_gbs"] = round(alg / (res[label]["avg_us"] * 1e-6) / 1e9, 1)
+            res[label]["frac_hbm"] = round(res[label]["alg_gbs"] / HBM_PEAK_GBS, 4)
+        if durs and flops:
+            res[label]["mfma_tflops"] = round(flops / (res[label]["avg_us"] * 1e-6) / 1e12, 2)
+    # counter passes: per dispatch, in dispatch order
+    counters = {}
+    for pas in PMC_PASSES:
+        path = _find(os.path.join(d, pas), "counter_collection.csv")
+        if not path:
+            continue
+        rows = _read_csv(path)
+        per = {}
+        for r in rows:
+            did = int(r["Dispatch_Id"])
+            e = per.setdefault(did, {"name": r["Kernel_Name"], "vals": {}})
+            cn = r["Counter_Name"]
+            e["vals"][cn] = e["vals"].get(cn, 0.0) + float(r["Counter_Value"])
+        order = sorted(per)
+        nm = [per[i]["name"] for i in order]
+        w = _assign(nm, cases)
+        for label in w:
+            ds = [per[order[i]]["vals"] for i in w[label]]
+            ds = ds[1:] if len(ds) > 1 else ds
+            if not ds:
+                continue
+            for cn in ds[0]:
+                counters.setdefault(label, {})[cn] = sum(v.get(cn, 0.0) for v in ds) / len(ds)
+    # HBM bytes: counters scaled by what they read for the calibration copy
+    cal = counters.get("copy_calibration_256mib", {})
+    cal_bytes = 256 << 20
+    cf = cal.get("FETCH_SIZE", 0.0) * 1024.0 / cal_bytes
+    cw = cal.get("WRITE_SIZE", 0.0) * 1024.0 / cal_bytes
+    traffic = {}
+    for label, c in counters.items():
+        e = res[label]
+        e["counters"] = {k: round(v, 3) for k, v in sorted(c.items())}
+        if cf > 0 and cw > 0 and "FETCH_SIZE" in c and "WRITE_SIZE" in c:
+            fb = c["FETCH_SIZE"] * 1024.0 / cf
+            wb = c["WRITE_SIZE"] * 1024.0 / cw
+            e["hbm_read_bytes"], e["hbm_write_bytes"] = round(fb), round(wb)
+            if e["alg_bytes"]:
+                e["traffic_over_alg"] = round((fb + wb) / e["alg_bytes"], 3)
+            traffic[label] = {"code": e["code"], "kernel": e["kernel"], "fetch_bytes_per_launch": round(fb),
+                              "write_bytes_per_launch": round(wb), "bytes_per_launch": round(fb + wb),
+                              "copy_fetch_factor": round(cf, 4), "copy_write_factor": round(cw, 4)}
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump(traffic, f, indent=1)
+    with open(os.path.join(ROOT, "profiles", "kernels.json"), "w") as f:
+        json.dump(res, f, indent=1)
+    print(json.dumps(res, indent=1))
+
+
+def measured_traffic(label, digest):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they
     were taken on the current kernel code; else None."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
-        with open(path) as f:
+        with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    e = t.get(kernel)
+    e = t.get(label)
     if not e or e.get("code") != digest:
         return None
     return e.get("bytes_per_launch")
 
 
-ROUNDTRIP_KERNEL = "rq_quant_kernel<2, true, true, true, true>"
-ROUNDTRIP_SYMBOL = "_ZN3rqk15rq_quant_kernelILi2ELb1ELb1ELb1ELb1EEEvNS_8RotorDevEPKcllPjPtS4_S5_Pcl"
-COPY_KERNEL = "__amd_rocclr_copyBuffer"
-
-
-def _counter_dispatches(path, counter):
-    """{kernel name: [counter value (KiB) per dispatch, in dispatch order]}
-    from a rocprofv3 CSV."""
-    import csv
-    sums, names = {}, {}
-    with open(path) as f:
-        for r in csv.DictReader(f):
-            if r["Counter_Name"] != counter:
-                continue
-            d = r["Dispatch_Id"]
-            sums[d] = sums.get(d, 0.0) + float(r["Counter_Value"])
-            names[d] = r["Kernel_Name"]
-    out = {}
-    for d in sorted(sums, key=int):
-        out.setdefault(names[d], []).append(sums[d])
-    return out
-
-
-def ingest_counters(fetch_csv, write_csv, copy_bytes):
-    """HBM bytes per roundtrip launch, scaled by a plain copy of known size.
-
-    The calibration copy is the last copyBuffer dispatch of the run (the
-    --copy-bytes copies close the process); each counter is divided by what
-    it reads for that copy per byte moved."""
-    fetch = _counter_dispatches(fetch_csv, "FETCH_SIZE")
-    write = _counter_dispatches(write_csv, "WRITE_SIZE")
-
-    def values(d, name):
-        hits = [v for k, vs in d.items() if name in k for v in vs]
-        if not hits:
-            raise SystemExit(f"no dispatch of {name} in the counter CSV")
-        return hits
-
-    f_copy = values(fetch, COPY_KERNEL)[-1] * 1024.0
-    w_copy = values(write, COPY_KERNEL)[-1] * 1024.0
-    fr, wr = values(fetch, ROUNDTRIP_KERNEL), values(write, ROUNDTRIP_KERNEL)
-    f_rt = sum(fr) / len(fr) * 1024.0
-    w_rt = sum(wr) / len(wr) * 1024.0
-    cf, cw = f_copy / copy_bytes, w_copy / copy_bytes
-    entry = {
-        "code": kernel_code_digest(ROUNDTRIP_SYMBOL),
-        "kernel": ROUNDTRIP_KERNEL,
-        "dispatches": len(fr),
-        "fetch_kib_raw": round(f_rt / 1024.0, 1), "write_kib_raw": round(w_rt / 1024.0, 1),
-        "copy_bytes": copy_bytes, "copy_fetch_factor": round(cf, 4), "copy_write_factor": round(cw, 4),
-        "fetch_bytes_per_launch": round(f_rt / cf), "write_bytes_per_launch": round(w_rt / cw),
-        "bytes_per_launch": round(f_rt / cf + w_rt / cw),
-    }
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    try:
-        with open(path) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
-        t = {}
-    t["rq_roundtrip_qjl3_f16"] = entry
-    os.makedirs(os.path.dirname(path), exist_ok=True)
-    with open(path, "w") as f:
-        json.dump(t, f, indent=1)
-    print(json.dumps(entry))
-
-
-def cpu_baseline(x_host, q_host):
-    """The float64 oracle on a bounded sample, single thread."""
+# ---------------------------------------------------- CPU oracle baseline --
+def _oracle_leg(args):
+    """One worker of the CPU baseline: the float64 oracle's roundtrip and
+    64-query scoring (or bulk quantisation only) of rows [lo, hi), repeated
+    for `seconds`, on one BLAS thread (pinned to `cpu` when given)."""
+    lo, hi, seconds, cpu, kind = args
+    if cpu is not None:
+        os.sched_setaffinity(0, {cpu})
+    import numpy as np
     from threadpoolctl import threadpool_limits
+    from kv_cache_vector_norm_amd import workloads as W
     from oracle import codec as OC
     from oracle import params as OP
-    n = 2048
     p = OP.Params(128, BITS, 0, OP.QJL)
-    xs = x_host[:n].astype("float64")
-    qs = q_host.astype("float64")
+    if kind == "lowrank":
+        import torch
+        k, _, _ = W.lowrank_head(hi - lo, W.cache_seed(1, 0, 0), torch=torch)
+        xs = k.numpy().astype(np.float64)
+    else:
+        xs = W.keys_65536()[lo:hi].astype(np.float64)
+    qs = W.queries_64().astype(np.float64)
+    reps = 0
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        reps = 0
         while True:
             rec, _ = OC.quantize(p, xs)
-            OC.dequantize(p, rec)
-            OC.score(p, qs, rec)
+            if kind != "lowrank":
+                OC.dequantize(p, rec)
+                OC.score(p, qs, rec)
             reps += 1
             el = time.perf_counter() - t0
-            if el > 8.0 or reps >= 20:
+            if el > seconds:
                 break
-    return {"value": n * reps / el, "unit": "vectors/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} of the {N_VEC} keys (roundtrip + {N_Q} queries scored against them), "
-                      f"{reps} passes, float64 numpy, 1 thread",
-            "scores_per_s": n * N_Q * reps / el}
+    return (hi - lo) * reps, el
 
 
-def _timed(stream, fn, reps):
-    """Average microseconds per call of fn(i) over reps back-to-back calls,
-    from HIP events on the launch stream (after one untimed call)."""
+def cpu_baseline():
+    """The float64 oracle (as it stands) on the host cores: one pinned core,
+    then all cores of this GPU's share, each worker on its own contiguous
+    2,048-key slice of the 65,536 keys, plus the bulk-quantisation rate on
+    low-rank keys of the model-shaped caches (one core), extrapolated to the
+    Qwen2.5-3B- and Llama-3.1-8B-shaped caches.  Workers are spawned before
+    anything touches the GPU."""
+    import multiprocessing as mp
+    ctx = mp.get_context("spawn")
+    cpus = sorted(os.sched_getaffinity(0))
+    ncores = min(CPU_SHARE, len(cpus))
+    slice_n = 2048
+    with ctx.Pool(1) as pool:
+        v1, e1 = pool.map(_oracle_leg, [(0, slice_n, ORACLE_SECONDS, cpus[0], "step")])[0]
+        vq, eq = pool.map(_oracle_leg, [(0, slice_n, ORACLE_SECONDS / 2, cpus[0], "lowrank")])[0]
+    with ctx.Pool(ncores) as pool:
+        legs = [(i * slice_n, (i + 1) * slice_n, ORACLE_SECONDS, cpus[i], "step") for i in range(ncores)]
+        res = pool.map(_oracle_leg, legs)
+    one = v1 / e1
+    allc = sum(v / e for v, e in res)
+    qrate = vq / eq
+    qwen = 36 * 2 * 2 * 32768
+    llama = 32 * 8 * 2 * 131072
+    return {
+        "value": round(allc, 1), "unit": "vectors/s", "cores": ncores, "kind": "oracle",
+        "sample": (f"float64 numpy oracle, one BLAS thread per process: {ncores} processes, each on its own "
+                   f"{slice_n}-key slice of the {N_VEC} keys (roundtrip + {N_Q} queries scored per key), "
+                   f"{ORACLE_SECONDS:.0f} s each"),
+        "scores_per_s": round(allc * N_Q, 1),
+        "one_core": {"value": round(one, 1), "unit": "vectors/s", "cores": 1, "scores_per_s": round(one * N_Q, 1),
+                     "sample": f"{slice_n} keys, {int(v1 // slice_n)} passes, pinned to cpu {cpus[0]}"},
+        "bulk_quantize_one_core": {
+            "vectors_per_s": round(qrate, 1),
+            "sample": f"{slice_n} low-rank + outlier keys of one (layer, KV head), quantise only",
+            "qwen2.5-3b_cache_s_extrapolated": round(qwen / qrate, 1),
+            "llama3.1-8b_cache_s_extrapolated": round(llama / qrate, 1)},
+    }
+
+
+# -------------------------------------------------------------- timing --
+def _b2b(stream, fn, reps, trials):
+    """Median and minimum over `trials` of the average microseconds per call
+    of fn(i) over `reps` back-to-back calls, from HIP events recorded on the
+    launch stream (after one untimed call)."""
     import torch
     fn(0)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    e0.record(stream)
-    for i in range(reps):
-        fn(i + 1)
-    e1.record(stream)
+    ts = []
+    i = 1
+    for _ in range(trials):
+        e0.record(stream)
+        for _ in range(reps):
+            fn(i)
+            i += 1
+        e1.record(stream)
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3 / reps)
+    return statistics.median(ts), min(ts)
+
+
+def _timed(stream, fn, reps):
+    return _b2b(stream, fn, reps, 1)[0]
+
+
+def quality_row(K, W, dev, stream):
+    """1,024 fp32 unit vectors, rotor MSE-only 3 bits, roundtrip fp32 ->
+    fp32: MSE and mean cosine of the GPU reconstruction and of the oracle's,
+    and the launch time at this size (latency-bound)."""
+    import numpy as np
+    import torch
+    from oracle import codec as OC
+    from oracle import params as OP
+    xh = W.unit_vectors_1024()
+    x = torch.from_numpy(xh).to(dev)
+    c = K.Codec(bits=3, seed=0, mode=K.RQ_MSE)
+    rec, y = c.roundtrip(x)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e3 / reps
+    yh = y.cpu().numpy().astype(np.float64)
+    xd = xh.astype(np.float64)
+
+    def mse_cos(r):
+        mse = float(np.mean(np.sum((xd - r) ** 2, axis=1)))
+        cos = float(np.mean(np.sum(xd * r, axis=1) / (np.linalg.norm(xd, axis=1) * np.linalg.norm(r, axis=1))))
+        return mse, cos
+    g_mse, g_cos = mse_cos(yh)
+    p = OP.Params(128, 3, 0, OP.MSE)
+    o_mse, o_cos = mse_cos(OC.roundtrip(p, xd))
+    us, us_min = _b2b(stream, lambda i: c.roundtrip(x, rec=rec, out=y), 50, 5)
+    # one launch after an idle device: event pair around a single call
+    lat = []
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(20):
+        torch.cuda.synchronize()
+        e0.record(stream)
+        c.roundtrip(x, rec=rec, out=y)
+        e1.record(stream)
+        e1.synchronize()
+        lat.append(e0.elapsed_time(e1) * 1e3)
+    return {"workload": "1,024 fp32 unit vectors (N(0,1) normalised, seed 0), rotor 3-bit MSE, fp32 in/out",
+            "mse": round(g_mse, 6), "cosine": round(g_cos, 6), "oracle_mse": round(o_mse, 6),
+            "oracle_cosine": round(o_cos, 6), "pages_mse_cosine": [0.034, 0.983],
+            "us_per_launch_back_to_back": round(us, 2), "single_launch_us": round(statistics.median(lat), 2)}
+
+
+def sweeps(K, dev, stream, codecs):
+    """Roundtrip rate over N (65,536 * 4^k up to 16,777,216) for each codec,
+    beside the reference copy of the same bytes at each N.  Below 1 M
+    vectors the launches rotate over enough buffer sets to read cold data."""
+    import torch
+    out = {}
+    nmax = 16777216
+    xb = torch.empty((nmax, 128), dtype=torch.float16, device=dev)
+    xb.normal_()
+    yb = torch.empty_like(xb)
+    ccap = nmax * 284
+    csrc = torch.empty(ccap, dtype=torch.uint8, device=dev)
+    cdst = torch.empty_like(csrc)
+    for key, cdc in codecs.items():
+        nb = algorithmic_bytes(cdc.layout)
+        rb = cdc.alloc_record(nmax, dev)
+        sweep = {}
+        for n in (65536, 262144, 1048576, 4194304, 16777216):
+            sets = max(1, min(nmax // n, (1 << 30) // (n * nb)))
+            half = n * nb // 2
+            if sets * half > ccap or half % 16:
+                raise RuntimeError("reference copy sizes outside its buffers")
+
+            def rt(i, n=n, sets=sets):
+                k = i % sets
+                r = K.Record(rb.codes[k * n:(k + 1) * n], rb.norms[k * n:(k + 1) * n],
+                             None if rb.signs is None else rb.signs[k * n:(k + 1) * n],
+                             None if rb.rnorms is None else rb.rnorms[k * n:(k + 1) * n])
+                cdc.roundtrip(xb[k * n:(k + 1) * n], rec=r, out=yb[k * n:(k + 1) * n])
+
+            def cp(i, n=n, sets=sets, half=half):
+                k = i % sets
+                K.rq_bench_copy(csrc[k * half:(k + 1) * half], cdst[k * half:(k + 1) * half], half, stream)
+            reps = max(3, min(64, int(4e9 // (n * nb))))
+            us, _ = _b2b(stream, rt, reps, 5)
+            cus, _ = _b2b(stream, cp, reps, 5)
+            gbs = n * nb / (us * 1e-6) / 1e9
+            cgbs = 2 * half / (cus * 1e-6) / 1e9
+            sweep[str(n)] = {"us": round(us, 2), "gbs": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                             "copy_gbs": round(cgbs, 1), "frac_copy": round(gbs / cgbs, 4)}
+        out[key] = sweep
+        del rb
+    del xb, yb, csrc, cdst
+    torch.cuda.empty_cache()
+    return out
 
 
 def workload_extras(K, W, dev, stream):
@@ -260,10 +615,10 @@ def workload_extras(K, W, dev, stream):
             def rt(i, c=c, recs=recs):
                 k = i % sets
                 c.roundtrip(xs[k * n:(k + 1) * n], rec=recs[k], out=ys[k * n:(k + 1) * n])
-            us = _timed(stream, rt, 24)
+            us, _ = _b2b(stream, rt, 8, 5)
             alg = 256 + c.layout["record_bytes"] + 256
             e = {"us": round(us, 2), "vectors_per_s": round(n / (us * 1e-6), 1),
-                 "gbs": round(n * alg / (us * 1e-6) / 1e9, 1)}
+                 "gbs": round(n * alg / (us * 1e-6) / 1e9, 1), "frac_hbm": round(n * alg / (us * 1e-6) / 8e12, 4)}
             if mode & K.RQ_DENSE:
                 # useful MFMA work: Pi x and Pi^T y (and S r, S^T sigma with QJL), 2 flop per MAC
                 flops = 2 * 128 * 128 * (4 if mode & K.RQ_QJL else 2)
@@ -367,6 +722,7 @@ def workload_extras(K, W, dev, stream):
             "decode_step_per_layer_calls_us": round(lus, 1),
             "decode_attention_us": round(aus, 1),
             "decode_attention_keys_per_s": round(n_k / (aus * 1e-6), 1),
+            "decode_attention_frac_hbm": round(2 * n_k * c.layout["record_bytes"] / (aus * 1e-6) / 8e12, 4),
             "polar_keys_quantize_us": round(pqus, 1),
             "polar_keys_quantize_gbs": round(n_k * (256 + 64) / (pqus * 1e-6) / 1e9, 1),
             "polar_decode_step_us": round(pdus, 1),
@@ -381,13 +737,16 @@ def workload_extras(K, W, dev, stream):
 
 def main():
     a = parse()
-    if a.ingest_counters:
-        ingest_counters(a.ingest_counters[0], a.ingest_counters[1], a.copy_bytes or (256 << 20))
+    if a.summarize:
+        summarize(a.summarize)
         return
     if a.gpus != 1:
         print(f"bench.py measures one GPU: the codec library runs on a single MI355X and has no multi-GPU path "
               f"(asked for --gpus {a.gpus})", file=sys.stderr)
         sys.exit(2)
+    # the CPU baseline runs first, in spawned workers, before the GPU is used
+    cpu = None if (a.no_cpu or a.profile_set) else cpu_baseline()
+
     import numpy as np
     import torch
     import kv_cache_vector_norm_amd as K
@@ -395,6 +754,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if a.profile_set:
+        profile_set(K, W, dev)
+        return
     codec = K.Codec(bits=BITS, seed=0, mode=K.RQ_QJL)
     lay = codec.layout
     x_host = W.keys_65536()
@@ -412,78 +774,79 @@ def main():
         scs.append(torch.empty((N_Q, N_VEC), dtype=torch.float32, device=dev))
     stream = torch.cuda.current_stream()
 
-    def step(i, ev=None):
+    def roundtrip(i):
         k = i % nsets
-        if ev is not None:
-            ev[0].record(stream)
         codec.roundtrip(xs[k], rec=recs[k], out=ys[k])
-        if ev is not None:
-            ev[1].record(stream)
+
+    def score(i):
+        k = i % nsets
         codec.score(q, recs[k], N_Q, N_VEC, out=scs[k])
-        if ev is not None:
-            ev[2].record(stream)
 
     for i in range(a.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    # Per-kernel durations come from HIP events around the two launches of
-    # every EVENT_EVERY-th timed step: an event record is a GPU-side marker
-    # costing a few microseconds, so bracketing every step would slow the
-    # very steps being timed.
-    sampled = list(range(0, a.steps, EVENT_EVERY))
-    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in sampled}
+        roundtrip(i)
+        score(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(a.steps):
-        step(i, evs.get(i))
+        roundtrip(i)
+        score(i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    rt_ms = float(np.mean([evs[i][0].elapsed_time(evs[i][1]) for i in sampled]))
-    sc_ms = float(np.mean([evs[i][1].elapsed_time(evs[i][2]) for i in sampled]))
     ms_per_step = elapsed * 1e3 / a.steps
 
+    # per-kernel times: back-to-back launches over the rotating sets
+    rt_us, rt_min = _b2b(stream, roundtrip, nsets, a.trials)
+    sc_us, sc_min = _b2b(stream, score, nsets, a.trials)
+    # the reference copy of the same bytes (568 B per vector: read 284, write 284)
+    cbytes = N_VEC * algorithmic_bytes(lay) // 2
+    csrc = torch.empty((nsets, cbytes), dtype=torch.uint8, device=dev)
+    cdst = torch.empty_like(csrc)
+    cp_us, _ = _b2b(stream, lambda i: K.rq_bench_copy(csrc[i % nsets], cdst[i % nsets], cbytes, stream), nsets,
+                    a.trials)
+    del csrc, cdst
+
     bytes_vec = algorithmic_bytes(lay)
-    rt_gbs = N_VEC * bytes_vec / (rt_ms * 1e-3) / 1e9
+    rt_gbs = N_VEC * bytes_vec / (rt_us * 1e-6) / 1e9
+    cp_gbs = 2 * cbytes / (cp_us * 1e-6) / 1e9
     digest = kernel_code_digest(ROUNDTRIP_SYMBOL)
-    traffic = measured_traffic("rq_roundtrip_qjl3_f16", digest)
+    traffic = measured_traffic("rq_roundtrip_qjl3_65536", digest)
     roof = {"bound": "hbm", "achieved": round(rt_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(rt_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": "rq_roundtrip (2-bit codes + QJL, fp16 in/out)",
+            "kernel": "rq_roundtrip (2-bit codes + QJL, fp16 in/out): rqk::" + ROUNDTRIP_KERNEL,
             "algorithmic_bytes_per_vector": bytes_vec, "vectors_per_launch": N_VEC,
-            "avg_launch_us": round(rt_ms * 1e3, 2), "launches_timed": len(sampled)}
+            "avg_launch_us": round(rt_us, 2), "min_trial_us": round(rt_min, 2),
+            "timing": f"median over {a.trials} trials of {nsets} back-to-back launches over {nsets} rotating "
+                      f"buffer sets, HIP events on the launch stream",
+            "copy_same_bytes_gbs": round(cp_gbs, 1), "frac_of_copy": round(rt_gbs / cp_gbs, 4)}
     score_bytes = N_VEC * lay["record_bytes"] + 4 * N_Q * N_VEC
     extras = {
         "scores_per_s": round(N_Q * N_VEC * a.steps / elapsed, 1),
-        "roundtrip_vectors_per_s": round(N_VEC / (rt_ms * 1e-3), 1),
-        "score_us": round(sc_ms * 1e3, 2),
-        "score_scores_per_s": round(N_Q * N_VEC / (sc_ms * 1e-3), 1),
-        "score_gbs": round(score_bytes / (sc_ms * 1e-3) / 1e9, 1),
+        "roundtrip_vectors_per_s": round(N_VEC / (rt_us * 1e-6), 1),
+        "score_us": round(sc_us, 2),
+        "score_scores_per_s": round(N_Q * N_VEC / (sc_us * 1e-6), 1),
+        "score_gbs": round(score_bytes / (sc_us * 1e-6) / 1e9, 1),
+        "score_frac_hbm": round(score_bytes / (sc_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "kernels_within_step": bool(rt_us + sc_us <= ms_per_step * 1e3 * 1.02),
         "buffer_sets": nsets,
     }
+    extras["c0_quality"] = quality_row(K, W, dev, stream)
 
     # MSE-only 3-bit roundtrip (the HBM-bandwidth codec) on the same keys
     mse = K.Codec(bits=3, seed=0, mode=K.RQ_MSE)
     mrec = [mse.alloc_record(N_VEC, dev) for _ in range(nsets)]
-    for i in range(a.warmup):
-        mse.roundtrip(xs[i % nsets], rec=mrec[i % nsets], out=ys[i % nsets])
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for i in range(a.steps):
-        mse.roundtrip(xs[i % nsets], rec=mrec[i % nsets], out=ys[i % nsets])
-    e1.record(stream)
-    torch.cuda.synchronize()
-    mse_us = e0.elapsed_time(e1) * 1e3 / a.steps
+    mse_us, _ = _b2b(stream, lambda i: mse.roundtrip(xs[i % nsets], rec=mrec[i % nsets], out=ys[i % nsets]), nsets,
+                     a.trials)
     mb = algorithmic_bytes(mse.layout)
     extras["mse3_roundtrip_us"] = round(mse_us, 2)
     extras["mse3_roundtrip_gbs"] = round(N_VEC * mb / (mse_us * 1e-6) / 1e9, 1)
     extras["mse3_roundtrip_vectors_per_s"] = round(N_VEC / (mse_us * 1e-6), 1)
+    del mrec
 
     # QJL-only keys (1 bit in total) on the same keys: roundtrip and scoring
     q1 = K.Codec(bits=1, seed=0, mode=K.RQ_QJL)
     q1rec = [q1.alloc_record(N_VEC, dev) for _ in range(nsets)]
-    us1 = _timed(stream, lambda i: q1.roundtrip(xs[i % nsets], rec=q1rec[i % nsets], out=ys[i % nsets]), a.steps)
-    sus1 = _timed(stream, lambda i: q1.score(q, q1rec[i % nsets], N_Q, N_VEC, out=scs[i % nsets]), a.steps)
+    us1 = _timed(stream, lambda i: q1.roundtrip(xs[i % nsets], rec=q1rec[i % nsets], out=ys[i % nsets]), 4 * nsets)
+    sus1 = _timed(stream, lambda i: q1.score(q, q1rec[i % nsets], N_Q, N_VEC, out=scs[i % nsets]), 4 * nsets)
     extras["qjl1_roundtrip_us"] = round(us1, 2)
     extras["qjl1_roundtrip_gbs"] = round(N_VEC * algorithmic_bytes(q1.layout) / (us1 * 1e-6) / 1e9, 1)
     extras["qjl1_score_us"] = round(sus1, 2)
@@ -493,55 +856,29 @@ def main():
     # fused roundtrip, and the 64 queries scored against all keys
     pc = K.PolarCodec(seed=0)
     pw = [pc.alloc_words(N_VEC, dev) for _ in range(nsets)]
-    pus = _timed(stream, lambda i: pc.roundtrip(xs[i % nsets], words=pw[i % nsets], out=ys[i % nsets]), a.steps)
-    psus = _timed(stream, lambda i: pc.score(q, pw[i % nsets], N_Q, N_VEC, out=scs[i % nsets]), a.steps)
+    pus = _timed(stream, lambda i: pc.roundtrip(xs[i % nsets], words=pw[i % nsets], out=ys[i % nsets]), 4 * nsets)
+    psus = _timed(stream, lambda i: pc.score(q, pw[i % nsets], N_Q, N_VEC, out=scs[i % nsets]), 4 * nsets)
     extras["polar_roundtrip_us"] = round(pus, 2)
     extras["polar_roundtrip_gbs"] = round(N_VEC * (256 + 64 + 256) / (pus * 1e-6) / 1e9, 1)
     extras["polar_roundtrip_vectors_per_s"] = round(N_VEC / (pus * 1e-6), 1)
     extras["polar_score_us"] = round(psus, 2)
     extras["polar_scores_per_s"] = round(N_VEC * N_Q / (psus * 1e-6), 1)
     del pw, pc
+    del xs, ys, recs, scs
+    torch.cuda.empty_cache()
 
-    if a.sweep:
-        # the MSE-only 3-bit roundtrip and the headline 2-bit + QJL one over N
-        sweeps = {"mse3_sweep": (mse, mb), "qjl3_sweep": (codec, algorithmic_bytes(lay))}
-        for key, (cdc, nb) in sweeps.items():
-            sweep = {}
-            for n in (65536, 262144, 1048576, 4194304, 16777216):
-                xb = torch.randn((n, 128), device=dev).to(torch.float16)
-                yb = torch.empty_like(xb)
-                rb = cdc.alloc_record(n, dev)
-                for _ in range(3):
-                    cdc.roundtrip(xb, rec=rb, out=yb)
-                reps = max(3, min(50, int(4e8 // (n * 566))))
-                torch.cuda.synchronize()
-                e0.record(stream)
-                for _ in range(reps):
-                    cdc.roundtrip(xb, rec=rb, out=yb)
-                e1.record(stream)
-                torch.cuda.synchronize()
-                us = e0.elapsed_time(e1) * 1e3 / reps
-                sweep[str(n)] = {"us": round(us, 2), "gbs": round(n * nb / (us * 1e-6) / 1e9, 1)}
-                del xb, yb, rb
-            extras[key] = sweep
+    if not a.no_sweep:
+        extras["sweeps"] = sweeps(K, dev, stream, {"mse3": mse, "qjl3": codec})
 
-    # achievable-HBM reference: a plain device copy of 1 GiB (read + write)
+    # the runtime's own device copy of 1 GiB, for comparison with rq_bench_copy
     src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
     cus = _timed(stream, lambda i: dst.copy_(src), 5)
-    extras["copy_1gib_gbs"] = round(2 * (1 << 30) / (cus * 1e-6) / 1e9, 1)
+    extras["runtime_copy_1gib_gbs"] = round(2 * (1 << 30) / (cus * 1e-6) / 1e9, 1)
     del src, dst
 
     if not a.no_workloads:
         extras["workloads"] = workload_extras(K, W, dev, stream)
-
-    if a.copy_bytes:
-        src = torch.empty(a.copy_bytes, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
 
     out = {
         "metric": "quant+dequant vectors/s (d=128, 3-bit) + % HBM roofline; q·k scores/s",
@@ -563,8 +900,8 @@ def main():
         "kernel_code": digest,
         **extras,
     }
-    if not a.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(x_host, q_host)
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
 
 

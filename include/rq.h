@@ -350,6 +350,15 @@ int pq_roundtrip(rq_ctx* ctx, const void* x, int x_dtype, int64_t n, int64_t ldx
 int pq_score(rq_ctx* ctx, const float* q, int hq, int group, const uint32_t* words, int64_t t,
              int64_t kv_stride, float* scores, int64_t ld_scores, void* stream);
 
+/* Measurement reference, not part of the codec: copies `bytes` from src to
+ * dst (device pointers, 16-byte aligned, bytes a multiple of 16, no overlap)
+ * with the codec kernels' own global access pattern (each wave moves 16 KB
+ * blocks as 16-byte non-temporal buffer loads, then 16-byte stores).  Its
+ * rate is the practical HBM ceiling that kernel rates are compared with.
+ * Asynchronous on `stream`; RQ_EINVAL for bad arguments (nothing is
+ * enqueued), RQ_EHIP for a launch failure. */
+int rq_bench_copy(const void* src, void* dst, int64_t bytes, void* stream);
+
 /* Message of the calling thread's last failure ("" if none). */
 const char* rq_last_error(void);
 

@@ -5,16 +5,17 @@ only marshal arguments: device pointers may be given as torch tensors or
 integers; every step of the codec runs in the HIP library.  The `Codec`
 class adds record allocation with torch (device memory and streams only).
 
-There is no fallback: if librq.so is missing it is built in-tree; if that
-fails, importing the binding raises.
+The library is loaded on first use, so importing the package (or its
+CPU-only `workloads` module) touches no HIP code.  There is no fallback: if
+librq.so is missing it is built in-tree (and the first call raises if that
+fails); if it was built from other sources than those in csrc/ and include/
+the first call raises instead of running stale code.
 """
 import ctypes
 import math
 import os
 
 import numpy as np
-
-from . import workloads  # noqa: F401  (seeded synthetic inputs)
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "librq.so")
@@ -31,7 +32,7 @@ EXPORTS = ("rq_layout", "rq_host_params", "rq_host_quantizer", "rq_init", "rq_fr
            "tq_quantize", "tq_dequantize", "tq_roundtrip", "rq_cache_create", "rq_cache_free", "rq_cache_open",
            "rq_cache_close", "rq_cache_length", "rq_cache_free_pages", "rq_cache_append", "rq_cache_read",
            "rq_cache_attend_workspace", "rq_cache_attend", "pq_quantize", "pq_dequantize", "pq_roundtrip", "pq_score",
-           "rq_last_error", "rq_version")
+           "rq_bench_copy", "rq_last_error", "rq_version")
 
 
 class RQError(RuntimeError):
@@ -54,9 +55,17 @@ class ParamsHost(ctypes.Structure):
 
 
 def _load():
-    from .build import build, hip_runtime_dir
+    from .build import build, hip_runtime_dir, source_digest, stamp_path
     if not os.path.exists(LIB_PATH):
         build()
+    try:
+        with open(stamp_path()) as f:
+            built_from = f.read().strip()
+    except OSError:
+        built_from = None
+    if built_from != source_digest():
+        raise ImportError(f"{LIB_PATH} was built from other sources than those in csrc/ and include/ "
+                          "(or carries no source stamp); rebuild it (__graft_entry__.build())")
     # One HIP runtime per process: load the libamdhip64 that torch uses before
     # librq.so, so that librq.so's dependency resolves to that same runtime
     # (torch owns the device memory and streams handed to the library).
@@ -96,6 +105,7 @@ def _load():
         "pq_dequantize": ([P, P, I64, P, I, I64, P], I),
         "pq_roundtrip": ([P, P, I, I64, I64, P, P, I, I64, P], I),
         "pq_score": ([P, P, I, I, P, I64, I64, P, I64, P], I),
+        "rq_bench_copy": ([P, P, I64, P], I),
         "rq_last_error": ([], ctypes.c_char_p),
         "rq_version": ([], ctypes.c_char_p),
     }
@@ -110,11 +120,24 @@ def _load():
     return lib
 
 
-_lib = _load()
+class _LazyLib:
+    """The ctypes handle of librq.so, loaded (and checked) on first use."""
+    _handle = None
+
+    def __getattr__(self, name):
+        if _LazyLib._handle is None:
+            _LazyLib._handle = _load()
+        return getattr(_LazyLib._handle, name)
+
+
+_lib = _LazyLib()
 
 
 def lib():
-    return _lib
+    """The loaded librq.so (ctypes.CDLL), loading it on the first call."""
+    if _LazyLib._handle is None:
+        _LazyLib._handle = _load()
+    return _LazyLib._handle
 
 
 def _ptr(x):
@@ -276,6 +299,10 @@ def rq_attend(kctx, vctx, q, hq, group, kcodes, knorms, ksigns, krnorms, vcodes,
     return _check(_lib.rq_attend(kctx, vctx, _ptr(q), hq, group, _ptr(kcodes), _ptr(knorms), _ptr(ksigns),
                                  _ptr(krnorms), _ptr(vcodes), _ptr(vnorms), _ptr(vsigns), _ptr(vrnorms), t, kv_stride,
                                  float(scale), _ptr(workspace), workspace_bytes, _ptr(out), ld_out, _stream(stream)))
+
+
+def rq_bench_copy(src, dst, nbytes, stream=None):
+    return _check(_lib.rq_bench_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)))
 
 
 def pq_quantize(ctx, x, x_dtype, n, ldx, words, stream=None):

@@ -9,6 +9,7 @@ parameter draws are the exact libm values); the kernels and the C ABI layer
 are built with hipcc for gfx950 only.
 """
 import argparse
+import hashlib
 import os
 import shutil
 import subprocess
@@ -35,11 +36,33 @@ HIP_FLAGS = [
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-ffp-contract=off", "-fno-fast-math", "-Wall"]
 
 
+def stamp_path():
+    """File next to librq.so holding the source digest it was built from."""
+    return LIB + ".srcdigest"
+
+
+def source_digest():
+    """sha256 over every file of csrc/ and include/ and this build script
+    (names and contents, sorted): what librq.so is built from."""
+    h = hashlib.sha256()
+    paths = [os.path.abspath(__file__)]
+    for d in (CSRC, os.path.join(ROOT, "include")):
+        for name in sorted(os.listdir(d)):
+            p = os.path.join(d, name)
+            if os.path.isfile(p):
+                paths.append(p)
+    for p in paths:
+        h.update(os.path.relpath(p, ROOT).encode() + b"\0")
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:32]
+
+
 def _units():
     units = [("rq_host.o", [CXX] + HOST_FLAGS + ["-c", os.path.join(CSRC, "rq_host.cpp")])]
     units.append(("rq_api.o", [HIPCC] + HIP_FLAGS + ["-x", "hip", "-c", os.path.join(CSRC, "rq_api.cpp")]))
     for f in ("rq_rotor_dispatch.hip", "rq_dense.hip", "rq_score.hip", "rq_attend.hip", "rq_qjl1.hip", "rq_cache.hip",
-              "rq_polar.hip"):
+              "rq_polar.hip", "rq_copy.hip"):
         units.append((f.replace(".hip", ".o"), [HIPCC] + HIP_FLAGS + ["-c", os.path.join(CSRC, f)]))
     for kind in ("rotor", "dense"):
         for qjl in (0, 1):
@@ -81,7 +104,10 @@ def build(jobs=None, verbose=False):
     hip_dir = hip_runtime_dir()
     _run(["g++", "-shared", "-fPIC", "-o", tmp] + objs +
          [f"-L{hip_dir}", "-l:libamdhip64.so", f"-Wl,-rpath,{hip_dir}", "-Wl,--no-undefined"], verbose)
+    digest = source_digest()
     os.replace(tmp, LIB)
+    with open(stamp_path(), "w") as f:
+        f.write(digest + "\n")
     return LIB
 
 

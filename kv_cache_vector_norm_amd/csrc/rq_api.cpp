@@ -94,6 +94,19 @@ const char* rq_last_error(void) { return g_last_error.c_str(); }
 
 const char* rq_version(void) { return "rq-mi355x 1.0 (gfx950)"; }
 
+int rq_bench_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+    const char* fn = "rq_bench_copy";
+    if (bytes < 0 || bytes % 16) return fail(RQ_EINVAL, std::string(fn) + ": bytes must be a non-negative multiple of 16");
+    if (bytes == 0) return RQ_OK;
+    if (!src || !dst) return fail(RQ_EINVAL, std::string(fn) + ": NULL pointer");
+    if (!aligned(src, 16) || !aligned(dst, 16)) return fail(RQ_EINVAL, std::string(fn) + ": pointers must be 16-byte aligned");
+    const char* s8 = static_cast<const char*>(src);
+    const char* d8 = static_cast<const char*>(dst);
+    if (s8 < d8 + bytes && d8 < s8 + bytes) return fail(RQ_EINVAL, std::string(fn) + ": src and dst overlap");
+    const hipError_t e = rqk::copy_bytes(src, dst, bytes, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? RQ_OK : hip_fail(e, fn);
+}
+
 static void to_abi(const rqh::Layout& l, rq_layout_t* out) {
     out->d = l.d;
     out->bits = l.bits;

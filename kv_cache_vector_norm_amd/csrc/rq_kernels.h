@@ -171,6 +171,10 @@ hipError_t polar_dequantize(const PolarDev& P, const uint32_t* words, int64_t n,
 hipError_t polar_score(const PolarDev& P, const float* q, int hq, int group, const uint32_t* words, int64_t t,
                        int64_t kv_stride, float* scores, int64_t ld_scores, hipStream_t s);
 
+// Reference copy of `bytes` (a multiple of 16, 16-byte aligned) with the
+// codec kernels' 16-byte buffer load/store pattern (rq_copy.hip).
+hipError_t copy_bytes(const void* src, void* dst, int64_t bytes, hipStream_t s);
+
 // Paged cache helpers (rq_cache.hip).
 hipError_t scatter_rows(const uint32_t* src_codes, const uint16_t* src_norms, const uint32_t* src_signs,
                         const uint16_t* src_rnorms, uint32_t* dst_codes, uint16_t* dst_norms, uint32_t* dst_signs,

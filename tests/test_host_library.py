@@ -225,3 +225,27 @@ def test_slot_table_is_exact_nearest_centroid(K, bits, mode):
     s = _slot(np.sort(y), bias)
     assert np.all(np.diff(s.astype(np.int64)) >= 0)
     assert len(set(_slot(t, bias).tolist())) == len(t)
+
+
+def test_workloads_and_package_import_touch_no_hip():
+    """The input generators (shared by the oracle's tests) and the package
+    itself import without loading librq.so or the HIP runtime; the library
+    is loaded on the first call."""
+    import subprocess
+    import sys
+    code = ("import kv_cache_vector_norm_amd as K, kv_cache_vector_norm_amd.workloads as W; "
+            "W.gaussian(4, seed=0); "
+            "m = open('/proc/self/maps').read(); "
+            "print(int('librq' in m), int('libamdhip64' in m))")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.split() == ["0", "0"]
+
+
+def test_library_stamp_matches_sources(K):
+    """librq.so carries the digest of the sources it was built from, and the
+    loader accepts it only when that equals the digest of csrc/ and include/."""
+    from kv_cache_vector_norm_amd import build as B
+    with open(B.stamp_path()) as f:
+        assert f.read().strip() == B.source_digest()
+    K.lib()
