@@ -256,6 +256,24 @@ int rq_attend(const rq_ctx* kctx, const rq_ctx* vctx, const float* q, int hq, in
               float scale, void* workspace, int64_t workspace_bytes, float* out,
               int64_t ld_out, void* stream);
 
+/* rq_attend for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same computation, arguments and rules as rq_attend, with the workspace
+ * replaced by a fixed device array of RQ_ATTEND_NOALLOC_BYTES that the
+ * library holds on each GPU it runs on until the process ends.  Nothing is
+ * allocated and no allocating routine is called.  RQ_EINVAL (nothing is
+ * enqueued) when rq_attend_workspace(hq, group, t) exceeds
+ * RQ_ATTEND_NOALLOC_BYTES, besides rq_attend's own argument errors.  Every
+ * call on one GPU uses that GPU's one array: calls on one stream are ordered
+ * and safe, but calls that overlap in time on one GPU (other streams, other
+ * host threads) race on it and give wrong results. */
+#define RQ_ATTEND_NOALLOC_BYTES (64 << 20)
+int rq_attend_noalloc(const rq_ctx* kctx, const rq_ctx* vctx, const float* q, int hq, int group,
+                      const uint32_t* kcodes, const uint16_t* knorms, const uint32_t* ksigns,
+                      const uint16_t* krnorms, const uint32_t* vcodes, const uint16_t* vnorms,
+                      const uint32_t* vsigns, const uint16_t* vrnorms, int64_t t, int64_t kv_stride,
+                      float scale, float* out, int64_t ld_out, void* stream);
+
 /* Paged compressed KV cache (README "Post-Prefill Quantization": prefill at
  * full precision, one bulk quantisation of the prefill cache, then each
  * decode step stores its new key compressed while the current token's own

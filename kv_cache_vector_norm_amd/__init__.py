@@ -29,6 +29,7 @@ STATUS_NAMES = {0: "RQ_OK", 1: "RQ_EINVAL", 2: "RQ_EUNSUPPORTED", 3: "RQ_ENOMEM"
 
 EXPORTS = ("rq_layout", "rq_host_params", "rq_host_quantizer", "rq_init", "rq_free", "rq_get_layout", "rq_get_params",
            "rq_quantize", "rq_dequantize", "rq_roundtrip", "rq_score", "rq_attend_workspace", "rq_attend",
+           "rq_attend_noalloc",
            "tq_quantize", "tq_dequantize", "tq_roundtrip", "rq_cache_create", "rq_cache_free", "rq_cache_open",
            "rq_cache_close", "rq_cache_length", "rq_cache_free_pages", "rq_cache_append", "rq_cache_read",
            "rq_cache_attend_workspace", "rq_cache_attend", "pq_quantize", "pq_dequantize", "pq_roundtrip", "pq_score",
@@ -88,6 +89,7 @@ def _load():
         "rq_score": ([P, P, I, I, P, P, P, P, I64, I64, P, I64, P], I),
         "rq_attend_workspace": ([I, I, I64], I64),
         "rq_attend": ([P, P, P, I, I, P, P, P, P, P, P, P, P, I64, I64, ctypes.c_float, P, I64, P, I64, P], I),
+        "rq_attend_noalloc": ([P, P, P, I, I, P, P, P, P, P, P, P, P, I64, I64, ctypes.c_float, P, I64, P], I),
         "rq_cache_create": ([P, P, I, I, I, I64, I64, ctypes.POINTER(P)], I),
         "rq_cache_free": ([P], None),
         "rq_cache_open": ([P, I64, ctypes.POINTER(I)], I),
@@ -303,6 +305,16 @@ def rq_attend(kctx, vctx, q, hq, group, kcodes, knorms, ksigns, krnorms, vcodes,
 
 def rq_bench_copy(src, dst, nbytes, stream=None):
     return _check(_lib.rq_bench_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)))
+
+
+RQ_ATTEND_NOALLOC_BYTES = 64 << 20
+
+
+def rq_attend_noalloc(kctx, vctx, q, hq, group, kcodes, knorms, ksigns, krnorms, vcodes, vnorms, vsigns, vrnorms, t,
+                      kv_stride, scale, out, ld_out, stream=None):
+    return _check(_lib.rq_attend_noalloc(kctx, vctx, _ptr(q), hq, group, _ptr(kcodes), _ptr(knorms), _ptr(ksigns),
+                                         _ptr(krnorms), _ptr(vcodes), _ptr(vnorms), _ptr(vsigns), _ptr(vrnorms), t,
+                                         kv_stride, float(scale), _ptr(out), ld_out, _stream(stream)))
 
 
 def pq_quantize(ctx, x, x_dtype, n, ldx, words, stream=None):

@@ -17,6 +17,7 @@
 #include "rq_kernels.h"
 
 static_assert(RQ_SCORE_CHUNK == rqk::kScoreChunkRows, "score chunk size");
+static_assert(RQ_ATTEND_NOALLOC_BYTES == rqk::kNoAllocScratchBytes, "fixed attention scratch size");
 
 namespace {
 
@@ -588,44 +589,52 @@ int64_t rq_attend_workspace(int hq, int group, int64_t t) {
     return rqk::attend_plan(hq, group, t).bytes;
 }
 
-int rq_attend(const rq_ctx* kctx, const rq_ctx* vctx, const float* q, int hq, int group, const uint32_t* kcodes,
-              const uint16_t* knorms, const uint32_t* ksigns, const uint16_t* krnorms, const uint32_t* vcodes,
-              const uint16_t* vnorms, const uint32_t* vsigns, const uint16_t* vrnorms, int64_t t, int64_t kv_stride,
-              float scale, void* workspace, int64_t workspace_bytes, float* out, int64_t ld_out, void* stream) {
-    const char* fn = "rq_attend";
-    if (!kctx || !vctx) return fail(RQ_EINVAL, "rq_attend: key and value sessions are required");
+static int attend_impl(const rq_ctx* kctx, const rq_ctx* vctx, const float* q, int hq, int group,
+                       const uint32_t* kcodes, const uint16_t* knorms, const uint32_t* ksigns, const uint16_t* krnorms,
+                       const uint32_t* vcodes, const uint16_t* vnorms, const uint32_t* vsigns,
+                       const uint16_t* vrnorms, int64_t t, int64_t kv_stride, float scale, void* workspace,
+                       int64_t workspace_bytes, float* out, int64_t ld_out, void* stream, bool noalloc) {
+    const char* fn = noalloc ? "rq_attend_noalloc" : "rq_attend";
+    if (!kctx || !vctx) return fail(RQ_EINVAL, std::string(fn) + ": key and value sessions are required");
     int rc;
     const bool kpolar = kctx->host.lay.mode & RQ_POLAR;
     const bool vpolar = vctx->host.lay.mode & RQ_POLAR;
     if ((rc = kpolar ? check_polar(kctx, fn) : check_ctx(kctx, kctx->host.lay.mode & RQ_DENSE, fn))) return rc;
     if ((rc = vpolar ? check_polar(vctx, fn) : check_ctx(vctx, vctx->host.lay.mode & RQ_DENSE, fn))) return rc;
-    if (!q || !aligned(q, 16)) return fail(RQ_EINVAL, "rq_attend: q must be a 16-byte aligned device pointer");
-    if (hq < 1 || group < 1 || hq % group) return fail(RQ_EINVAL, "rq_attend: need hq >= 1, group >= 1, hq % group == 0");
-    if (hq > RQ_ATTEND_MAX_ROWS) return fail(RQ_EINVAL, "rq_attend: hq > RQ_ATTEND_MAX_ROWS");
-    if (group > RQ_SCORE_CHUNK) return fail(RQ_EINVAL, "rq_attend: group > RQ_SCORE_CHUNK");
-    if (t < 1) return fail(RQ_EINVAL, "rq_attend: softmax over no keys (t < 1)");
-    if (t > RQ_ATTEND_MAX_KEYS) return fail(RQ_EINVAL, "rq_attend: t > RQ_ATTEND_MAX_KEYS");
-    if (hq / group > 1 && kv_stride < t) return fail(RQ_EINVAL, "rq_attend: kv_stride < t");
+    if (!q || !aligned(q, 16)) return fail(RQ_EINVAL, std::string(fn) + ": q must be a 16-byte aligned device pointer");
+    if (hq < 1 || group < 1 || hq % group) return fail(RQ_EINVAL, std::string(fn) + ": need hq >= 1, group >= 1, hq % group == 0");
+    if (hq > RQ_ATTEND_MAX_ROWS) return fail(RQ_EINVAL, std::string(fn) + ": hq > RQ_ATTEND_MAX_ROWS");
+    if (group > RQ_SCORE_CHUNK) return fail(RQ_EINVAL, std::string(fn) + ": group > RQ_SCORE_CHUNK");
+    if (t < 1) return fail(RQ_EINVAL, std::string(fn) + ": softmax over no keys (t < 1)");
+    if (t > RQ_ATTEND_MAX_KEYS) return fail(RQ_EINVAL, std::string(fn) + ": t > RQ_ATTEND_MAX_KEYS");
+    if (hq / group > 1 && kv_stride < t) return fail(RQ_EINVAL, std::string(fn) + ": kv_stride < t");
     if (kpolar) {
         if (!kcodes || !aligned(kcodes, 4) || knorms || ksigns || krnorms)
-            return fail(RQ_EINVAL, "rq_attend: PolarQuant keys come as 16-word records in kcodes (knorms, ksigns, krnorms NULL)");
+            return fail(RQ_EINVAL, std::string(fn) + ": PolarQuant keys come as 16-word records in kcodes (knorms, ksigns, krnorms NULL)");
     } else if ((rc = check_record(kctx, kcodes, knorms, ksigns, krnorms, fn))) {
         return rc;
     }
     if (vpolar) {
         if (!vcodes || !aligned(vcodes, 4) || vnorms || vsigns || vrnorms)
-            return fail(RQ_EINVAL, "rq_attend: PolarQuant values come as 16-word records in vcodes (vnorms, vsigns, vrnorms NULL)");
+            return fail(RQ_EINVAL, std::string(fn) + ": PolarQuant values come as 16-word records in vcodes (vnorms, vsigns, vrnorms NULL)");
     } else if ((rc = check_record(vctx, vcodes, vnorms, vsigns, vrnorms, fn))) {
         return rc;
     }
-    if (!(scale == scale) || scale > 3.0e38f || scale < -3.0e38f) return fail(RQ_EINVAL, "rq_attend: scale is not finite");
+    if (!(scale == scale) || scale > 3.0e38f || scale < -3.0e38f) return fail(RQ_EINVAL, std::string(fn) + ": scale is not finite");
     const rqk::AttendPlan plan = rqk::attend_plan(hq, group, t);
-    if (!workspace || !aligned(workspace, 256)) return fail(RQ_EINVAL, "rq_attend: workspace must be a 256-byte aligned device pointer");
-    if (workspace_bytes < plan.bytes) return fail(RQ_EINVAL, "rq_attend: workspace smaller than rq_attend_workspace()");
-    if (!out || !aligned(out, 4)) return fail(RQ_EINVAL, "rq_attend: out must be a 4-byte aligned device pointer");
-    if (ld_out < rqh::kDim) return fail(RQ_EINVAL, "rq_attend: ld_out < 128");
+    if (noalloc) {
+        if (plan.bytes > rqk::kNoAllocScratchBytes)
+            return fail(RQ_EINVAL, "rq_attend_noalloc: rq_attend_workspace(hq, group, t) = " + std::to_string(plan.bytes) +
+                                       " bytes exceeds the fixed scratch of RQ_ATTEND_NOALLOC_BYTES = " +
+                                       std::to_string(rqk::kNoAllocScratchBytes));
+    } else {
+        if (!workspace || !aligned(workspace, 256)) return fail(RQ_EINVAL, std::string(fn) + ": workspace must be a 256-byte aligned device pointer");
+        if (workspace_bytes < plan.bytes) return fail(RQ_EINVAL, std::string(fn) + ": workspace smaller than rq_attend_workspace()");
+    }
+    if (!out || !aligned(out, 4)) return fail(RQ_EINVAL, std::string(fn) + ": out must be a 4-byte aligned device pointer");
+    if (ld_out < rqh::kDim) return fail(RQ_EINVAL, std::string(fn) + ": ld_out < 128");
     if (!vpolar && vctx->host.lay.mse_bits == 0)
-        return fail(RQ_EUNSUPPORTED, "rq_attend: value sessions need at least one MSE bit");
+        return fail(RQ_EUNSUPPORTED, std::string(fn) + ": value sessions need at least one MSE bit");
     rqk::ScoreTables kt;
     if (kpolar) {
         kt.dense = false;
@@ -648,9 +657,29 @@ int rq_attend(const rq_ctx* kctx, const rq_ctx* vctx, const float* q, int hq, in
     } else {
         vt = score_tables(vctx);
     }
+    if (noalloc) {
+        const hipError_t e = rqk::noalloc_scratch(&workspace);
+        if (e != hipSuccess) return hip_fail(e, "rq_attend_noalloc: address of the fixed scratch");
+    }
     return finish(rqk::attend(kt, vt, q, hq, group, kcodes, knorms, ksigns, krnorms, vcodes, vnorms, vsigns, vrnorms, t,
                               kv_stride, scale, workspace, out, ld_out, static_cast<hipStream_t>(stream)),
                   fn);
+}
+
+int rq_attend(const rq_ctx* kctx, const rq_ctx* vctx, const float* q, int hq, int group, const uint32_t* kcodes,
+              const uint16_t* knorms, const uint32_t* ksigns, const uint16_t* krnorms, const uint32_t* vcodes,
+              const uint16_t* vnorms, const uint32_t* vsigns, const uint16_t* vrnorms, int64_t t, int64_t kv_stride,
+              float scale, void* workspace, int64_t workspace_bytes, float* out, int64_t ld_out, void* stream) {
+    return attend_impl(kctx, vctx, q, hq, group, kcodes, knorms, ksigns, krnorms, vcodes, vnorms, vsigns, vrnorms, t,
+                       kv_stride, scale, workspace, workspace_bytes, out, ld_out, stream, false);
+}
+
+int rq_attend_noalloc(const rq_ctx* kctx, const rq_ctx* vctx, const float* q, int hq, int group,
+                      const uint32_t* kcodes, const uint16_t* knorms, const uint32_t* ksigns, const uint16_t* krnorms,
+                      const uint32_t* vcodes, const uint16_t* vnorms, const uint32_t* vsigns, const uint16_t* vrnorms,
+                      int64_t t, int64_t kv_stride, float scale, float* out, int64_t ld_out, void* stream) {
+    return attend_impl(kctx, vctx, q, hq, group, kcodes, knorms, ksigns, krnorms, vcodes, vnorms, vsigns, vrnorms, t,
+                       kv_stride, scale, nullptr, 0, out, ld_out, stream, true);
 }
 
 // ------------------------------------------------------ paged KV cache --

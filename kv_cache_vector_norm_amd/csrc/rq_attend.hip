@@ -29,6 +29,8 @@
 #include "rq_common.cuh"
 #include "rq_kernels.h"
 
+#include <mutex>
+
 namespace rqk {
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -607,6 +609,38 @@ hipError_t attend(const ScoreTables& kt, const ScoreTables& vt, const float* q, 
     c.ld_out = ld_out;
     hipLaunchKernelGGL(attend_combine_kernel, dim3(hq), dim3(320), 0, s, c);
     return hipGetLastError();
+}
+
+// ------------------------------------------------ fixed scratch buffer --
+// The workspace of rq_attend_noalloc: one array per GPU, part of the code
+// object, so it exists on every device the library runs on until the
+// process ends.  Host code never uses this name as an address (on the host
+// it is only a stand-in); it uses the device address hipGetSymbolAddress
+// returns for the current device.
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+    *ptr = nullptr;
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 }  // namespace rqk

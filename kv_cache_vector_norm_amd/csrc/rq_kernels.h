@@ -150,6 +150,12 @@ hipError_t attend(const ScoreTables& kt, const ScoreTables& vt, const float* q, 
                   int64_t t, int64_t kv_stride, float scale, void* workspace, float* out, int64_t ld_out,
                   hipStream_t s, const PageTable& kpt = PageTable{}, const PageTable& vpt = PageTable{});
 
+// rq_attend_noalloc: a fixed device array per GPU (rq_attend.hip) serves as
+// the workspace.  noalloc_scratch resolves its address on the current device
+// (once per device, then cached); it allocates nothing.
+constexpr int64_t kNoAllocScratchBytes = int64_t(64) << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 // QJL-only sessions (one bit in total, no MSE stage; rotor or dense alike):
 // the record is norm, signs of S x_u and gamma, with no code words.
 struct Qjl1Dev {
