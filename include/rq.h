@@ -274,6 +274,48 @@ int rq_attend_noalloc(const rq_ctx* kctx, const rq_ctx* vctx, const float* q, in
                       const uint32_t* vsigns, const uint16_t* vrnorms, int64_t t, int64_t kv_stride,
                       float scale, float* out, int64_t ld_out, void* stream);
 
+/* Outlier-channel separation for QJL-only keys (sessions with bits = 1 and
+ * RQ_QJL, rotor or dense alike).  The README's list of QJL kernels ("CUDA
+ * Kernels", "QJL Kernels") gives the one-bit quantiser "outlier separation"
+ * and grouped-query score kernels; the blog's random-rotation section
+ * (Lemma 1) and the podcast page say LLM vectors carry very large outliers.
+ * The pages fix no rule; these calls implement this one:
+ *  - a head's outlier channels are the k channels of largest mean |x_j| over
+ *    its keys (a tie goes to the lower channel), in increasing order, chosen
+ *    once (bulk quantisation) and then fixed;
+ *  - a key's values on them are stored as IEEE halves (exact for fp16
+ *    input) in `outliers` [n][k];
+ *  - the QJL record (norm, signs of S x_u, gamma) is that of the key with
+ *    those channels set to 0;
+ *  - dequantisation returns the QJL reconstruction with the outlier channels
+ *    replaced by the stored values; the score is <q, x~>, i.e.
+ *    n^ sqrt(pi/2)/m gamma^ <S q_in, sigma> + sum_i q_{c_i} o^_i with q_in
+ *    = q with the outlier channels set to 0.
+ * Layout: record row r belongs to head r / head_rows; chans [heads][k]
+ * uint8 device array (every entry < 128, increasing within a head); k is
+ * 0..RQ_MAX_OUTLIERS (k = 0 is the plain QJL-only codec: chans and outliers
+ * may then be NULL).  outliers must be 2-byte aligned.  Other rules as for
+ * rq_quantize / rq_dequantize / rq_score; RQ_EINVAL on a session that is not
+ * QJL-only. */
+#define RQ_MAX_OUTLIERS 16
+/* chans[h][0..k) for each of `heads` heads of head_rows consecutive rows of
+ * x (x rules as for rq_quantize). */
+int rq_outlier_channels(const void* x, int x_dtype, int64_t heads, int64_t head_rows, int64_t ldx, int k,
+                        uint8_t* chans, void* stream);
+int rq_quantize_outliers(rq_ctx* ctx, const void* x, int x_dtype, int64_t n, int64_t ldx, int64_t head_rows,
+                         int k, const uint8_t* chans, uint16_t* norms, uint32_t* signs, uint16_t* rnorms,
+                         uint16_t* outliers, void* stream);
+int rq_dequantize_outliers(rq_ctx* ctx, const uint16_t* norms, const uint32_t* signs, const uint16_t* rnorms,
+                           const uint16_t* outliers, int64_t n, int64_t head_rows, int k, const uint8_t* chans,
+                           void* y, int y_dtype, int64_t ldy, void* stream);
+/* Scores as rq_score (query row h reads KV head h / group, whose t keys
+ * start at record row (h / group) * kv_stride and whose channel set is
+ * chans[h / group]). */
+int rq_score_outliers(rq_ctx* ctx, const float* q, int hq, int group, const uint16_t* norms,
+                      const uint32_t* signs, const uint16_t* rnorms, const uint16_t* outliers, int k,
+                      const uint8_t* chans, int64_t t, int64_t kv_stride, float* scores, int64_t ld_scores,
+                      void* stream);
+
 /* Paged compressed KV cache (README "Post-Prefill Quantization": prefill at
  * full precision, one bulk quantisation of the prefill cache, then each
  * decode step stores its new key compressed while the current token's own

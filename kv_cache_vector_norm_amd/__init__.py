@@ -33,6 +33,7 @@ EXPORTS = ("rq_layout", "rq_host_params", "rq_host_quantizer", "rq_init", "rq_fr
            "tq_quantize", "tq_dequantize", "tq_roundtrip", "rq_cache_create", "rq_cache_free", "rq_cache_open",
            "rq_cache_close", "rq_cache_length", "rq_cache_free_pages", "rq_cache_append", "rq_cache_read",
            "rq_cache_attend_workspace", "rq_cache_attend", "pq_quantize", "pq_dequantize", "pq_roundtrip", "pq_score",
+           "rq_outlier_channels", "rq_quantize_outliers", "rq_dequantize_outliers", "rq_score_outliers",
            "rq_bench_copy", "rq_last_error", "rq_version")
 
 
@@ -107,6 +108,10 @@ def _load():
         "pq_dequantize": ([P, P, I64, P, I, I64, P], I),
         "pq_roundtrip": ([P, P, I, I64, I64, P, P, I, I64, P], I),
         "pq_score": ([P, P, I, I, P, I64, I64, P, I64, P], I),
+        "rq_outlier_channels": ([P, I, I64, I64, I64, I, P, P], I),
+        "rq_quantize_outliers": ([P, P, I, I64, I64, I64, I, P, P, P, P, P, P], I),
+        "rq_dequantize_outliers": ([P, P, P, P, P, I64, I64, I, P, P, I, I64, P], I),
+        "rq_score_outliers": ([P, P, I, I, P, P, P, P, I, P, I64, I64, P, I64, P], I),
         "rq_bench_copy": ([P, P, I64, P], I),
         "rq_last_error": ([], ctypes.c_char_p),
         "rq_version": ([], ctypes.c_char_p),
@@ -301,6 +306,30 @@ def rq_attend(kctx, vctx, q, hq, group, kcodes, knorms, ksigns, krnorms, vcodes,
     return _check(_lib.rq_attend(kctx, vctx, _ptr(q), hq, group, _ptr(kcodes), _ptr(knorms), _ptr(ksigns),
                                  _ptr(krnorms), _ptr(vcodes), _ptr(vnorms), _ptr(vsigns), _ptr(vrnorms), t, kv_stride,
                                  float(scale), _ptr(workspace), workspace_bytes, _ptr(out), ld_out, _stream(stream)))
+
+
+RQ_MAX_OUTLIERS = 16
+
+
+def rq_outlier_channels(x, x_dtype, heads, head_rows, ldx, k, chans, stream=None):
+    return _check(_lib.rq_outlier_channels(_ptr(x), x_dtype, heads, head_rows, ldx, k, _ptr(chans), _stream(stream)))
+
+
+def rq_quantize_outliers(ctx, x, x_dtype, n, ldx, head_rows, k, chans, norms, signs, rnorms, outliers, stream=None):
+    return _check(_lib.rq_quantize_outliers(ctx, _ptr(x), x_dtype, n, ldx, head_rows, k, _ptr(chans), _ptr(norms),
+                                            _ptr(signs), _ptr(rnorms), _ptr(outliers), _stream(stream)))
+
+
+def rq_dequantize_outliers(ctx, norms, signs, rnorms, outliers, n, head_rows, k, chans, y, y_dtype, ldy, stream=None):
+    return _check(_lib.rq_dequantize_outliers(ctx, _ptr(norms), _ptr(signs), _ptr(rnorms), _ptr(outliers), n,
+                                              head_rows, k, _ptr(chans), _ptr(y), y_dtype, ldy, _stream(stream)))
+
+
+def rq_score_outliers(ctx, q, hq, group, norms, signs, rnorms, outliers, k, chans, t, kv_stride, scores, ld_scores,
+                      stream=None):
+    return _check(_lib.rq_score_outliers(ctx, _ptr(q), hq, group, _ptr(norms), _ptr(signs), _ptr(rnorms),
+                                         _ptr(outliers), k, _ptr(chans), t, kv_stride, _ptr(scores), ld_scores,
+                                         _stream(stream)))
 
 
 def rq_bench_copy(src, dst, nbytes, stream=None):

@@ -62,7 +62,7 @@ def _units():
     units = [("rq_host.o", [CXX] + HOST_FLAGS + ["-c", os.path.join(CSRC, "rq_host.cpp")])]
     units.append(("rq_api.o", [HIPCC] + HIP_FLAGS + ["-x", "hip", "-c", os.path.join(CSRC, "rq_api.cpp")]))
     for f in ("rq_rotor_dispatch.hip", "rq_dense.hip", "rq_score.hip", "rq_attend.hip", "rq_qjl1.hip", "rq_cache.hip",
-              "rq_polar.hip", "rq_copy.hip"):
+              "rq_polar.hip", "rq_copy.hip", "rq_outlier.hip"):
         units.append((f.replace(".hip", ".o"), [HIPCC] + HIP_FLAGS + ["-c", os.path.join(CSRC, f)]))
     for kind in ("rotor", "dense"):
         for qjl in (0, 1):

@@ -17,6 +17,7 @@
 #include "rq_kernels.h"
 
 static_assert(RQ_SCORE_CHUNK == rqk::kScoreChunkRows, "score chunk size");
+static_assert(RQ_MAX_OUTLIERS == rqk::kMaxOutliers, "outlier channels per head");
 static_assert(RQ_ATTEND_NOALLOC_BYTES == rqk::kNoAllocScratchBytes, "fixed attention scratch size");
 
 namespace {
@@ -680,6 +681,125 @@ int rq_attend_noalloc(const rq_ctx* kctx, const rq_ctx* vctx, const float* q, in
                       int64_t t, int64_t kv_stride, float scale, float* out, int64_t ld_out, void* stream) {
     return attend_impl(kctx, vctx, q, hq, group, kcodes, knorms, ksigns, krnorms, vcodes, vnorms, vsigns, vrnorms, t,
                        kv_stride, scale, nullptr, 0, out, ld_out, stream, true);
+}
+
+// ---------------------------------------------- outlier-channel separation --
+static int check_outlier_ctx(const rq_ctx* ctx, const char* fn) {
+    if (!ctx) return fail(RQ_EINVAL, std::string(fn) + ": ctx is NULL");
+    int rc;
+    if ((rc = check_ctx(ctx, ctx->host.lay.mode & RQ_DENSE, fn))) return rc;
+    if (!(ctx->host.lay.mode & RQ_QJL) || ctx->host.lay.mse_bits != 0)
+        return fail(RQ_EINVAL, std::string(fn) + ": needs a QJL-only session (bits = 1 with RQ_QJL)");
+    return RQ_OK;
+}
+
+static int check_outlier_arrays(int k, const uint8_t* chans, const uint16_t* outliers, const char* fn) {
+    if (k < 0 || k > RQ_MAX_OUTLIERS) return fail(RQ_EINVAL, std::string(fn) + ": k outside 0..RQ_MAX_OUTLIERS");
+    if (k > 0 && (!chans || !outliers)) return fail(RQ_EINVAL, std::string(fn) + ": chans and outliers are required for k > 0");
+    if (outliers && !aligned(outliers, 2)) return fail(RQ_EINVAL, std::string(fn) + ": outliers must be 2-byte aligned");
+    return RQ_OK;
+}
+
+int rq_outlier_channels(const void* x, int x_dtype, int64_t heads, int64_t head_rows, int64_t ldx, int k,
+                        uint8_t* chans, void* stream) {
+    const char* fn = "rq_outlier_channels";
+    int rc;
+    if (heads < 0 || head_rows < 1) return fail(RQ_EINVAL, "rq_outlier_channels: need heads >= 0, head_rows >= 1");
+    if (heads > 65535) return fail(RQ_EINVAL, "rq_outlier_channels: heads > 65535");
+    if (k < 0 || k > RQ_MAX_OUTLIERS) return fail(RQ_EINVAL, "rq_outlier_channels: k outside 0..RQ_MAX_OUTLIERS");
+    if (heads == 0 || k == 0) return RQ_OK;
+    if ((rc = check_vectors(x, x_dtype, ldx, "x", fn))) return rc;
+    if (!chans) return fail(RQ_EINVAL, "rq_outlier_channels: chans is NULL");
+    const hipError_t e = rqk::outlier_select(x, x_dtype == RQ_F16, heads, head_rows,
+                                             ldx * static_cast<int64_t>(elem_size(x_dtype)), k, chans,
+                                             static_cast<hipStream_t>(stream));
+    return finish(e, fn);
+}
+
+static rqk::OutlierArgs outlier_args(int64_t n, int64_t head_rows, int k, const uint8_t* chans) {
+    rqk::OutlierArgs o;
+    o.chans = chans;
+    o.heads = k > 0 ? (n + head_rows - 1) / head_rows : 0;
+    o.head_rows = head_rows;
+    o.k = k;
+    return o;
+}
+
+int rq_quantize_outliers(rq_ctx* ctx, const void* x, int x_dtype, int64_t n, int64_t ldx, int64_t head_rows, int k,
+                         const uint8_t* chans, uint16_t* norms, uint32_t* signs, uint16_t* rnorms, uint16_t* outliers,
+                         void* stream) {
+    const char* fn = "rq_quantize_outliers";
+    int rc;
+    if ((rc = check_outlier_ctx(ctx, fn))) return rc;
+    if (n < 0) return fail(RQ_EINVAL, "rq_quantize_outliers: n < 0");
+    if (head_rows < 1) return fail(RQ_EINVAL, "rq_quantize_outliers: head_rows < 1");
+    if ((rc = check_vectors(x, x_dtype, ldx, "x", fn))) return rc;
+    if ((rc = check_record(ctx, nullptr, norms, signs, rnorms, fn))) return rc;
+    if ((rc = check_outlier_arrays(k, chans, outliers, fn))) return rc;
+    if (n == 0) return RQ_OK;
+    rqk::OutlierArgs o = outlier_args(n, head_rows, k, chans);
+    o.out = outliers;
+    const hipError_t e = rqk::qjl1_quantize_outliers(qjl1_tables(ctx), x, x_dtype == RQ_F16,
+                                                     ldx * static_cast<int64_t>(elem_size(x_dtype)), n, norms, signs,
+                                                     rnorms, o, static_cast<hipStream_t>(stream));
+    return finish(e, fn);
+}
+
+int rq_dequantize_outliers(rq_ctx* ctx, const uint16_t* norms, const uint32_t* signs, const uint16_t* rnorms,
+                           const uint16_t* outliers, int64_t n, int64_t head_rows, int k, const uint8_t* chans,
+                           void* y, int y_dtype, int64_t ldy, void* stream) {
+    const char* fn = "rq_dequantize_outliers";
+    int rc;
+    if ((rc = check_outlier_ctx(ctx, fn))) return rc;
+    if (n < 0) return fail(RQ_EINVAL, "rq_dequantize_outliers: n < 0");
+    if (head_rows < 1) return fail(RQ_EINVAL, "rq_dequantize_outliers: head_rows < 1");
+    if ((rc = check_record(ctx, nullptr, norms, signs, rnorms, fn))) return rc;
+    if ((rc = check_outlier_arrays(k, chans, outliers, fn))) return rc;
+    if ((rc = check_vectors(y, y_dtype, ldy, "y", fn))) return rc;
+    if (n == 0) return RQ_OK;
+    rqk::OutlierArgs o = outlier_args(n, head_rows, k, chans);
+    o.in = outliers;
+    const hipError_t e = rqk::qjl1_dequantize_outliers(qjl1_tables(ctx), norms, signs, rnorms, n, y, y_dtype == RQ_F16,
+                                                       ldy * static_cast<int64_t>(elem_size(y_dtype)), o,
+                                                       static_cast<hipStream_t>(stream));
+    return finish(e, fn);
+}
+
+int rq_score_outliers(rq_ctx* ctx, const float* q, int hq, int group, const uint16_t* norms, const uint32_t* signs,
+                      const uint16_t* rnorms, const uint16_t* outliers, int k, const uint8_t* chans, int64_t t,
+                      int64_t kv_stride, float* scores, int64_t ld_scores, void* stream) {
+    const char* fn = "rq_score_outliers";
+    int rc;
+    if ((rc = check_outlier_ctx(ctx, fn))) return rc;
+    if ((rc = check_outlier_arrays(k, chans, outliers, fn))) return rc;
+    if (k == 0) return rq_score(ctx, q, hq, group, nullptr, norms, signs, rnorms, t, kv_stride, scores, ld_scores, stream);
+    if (!q || !aligned(q, 16)) return fail(RQ_EINVAL, "rq_score_outliers: q must be a 16-byte aligned device pointer");
+    if (hq < 1 || group < 1 || hq % group) return fail(RQ_EINVAL, "rq_score_outliers: need hq >= 1, group >= 1, hq % group == 0");
+    if (t < 0) return fail(RQ_EINVAL, "rq_score_outliers: t < 0");
+    if ((rc = check_record(ctx, nullptr, norms, signs, rnorms, fn))) return rc;
+    const int kv_heads = hq / group;
+    if (kv_heads > 1 && kv_stride < t) return fail(RQ_EINVAL, "rq_score_outliers: kv_stride < t");
+    if (!scores || !aligned(scores, 4)) return fail(RQ_EINVAL, "rq_score_outliers: scores must be a 4-byte aligned device pointer");
+    if (ld_scores < t) return fail(RQ_EINVAL, "rq_score_outliers: ld_scores < t");
+    if (ld_scores > (int64_t(1) << 23)) return fail(RQ_EINVAL, "rq_score_outliers: ld_scores > 2^23");
+    if (group > RQ_SCORE_CHUNK) return fail(RQ_EINVAL, "rq_score_outliers: group > RQ_SCORE_CHUNK");
+    if (t == 0) return RQ_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const rqk::ScoreTables st = score_tables(ctx);
+    rqk::ScoreOutliers so;
+    so.chans = chans;
+    so.values = outliers;
+    so.k = k;
+    const int heads_per_chunk = std::max(1, RQ_SCORE_CHUNK / group);
+    for (int h0 = 0; h0 < kv_heads; h0 += heads_per_chunk) {
+        const int nh = std::min(heads_per_chunk, kv_heads - h0);
+        const hipError_t e = rqk::score(st, q + static_cast<int64_t>(h0) * group * rqh::kDim, nh * group, group,
+                                        nullptr, norms, signs, rnorms, t, kv_stride, h0,
+                                        scores + static_cast<int64_t>(h0) * group * ld_scores, ld_scores, s,
+                                        rqk::PageTable{}, so);
+        if (e != hipSuccess) return hip_fail(e, fn);
+    }
+    return RQ_OK;
 }
 
 // ------------------------------------------------------ paged KV cache --

@@ -93,6 +93,26 @@ hipError_t dense_dequantize(const DenseTables& t, const uint32_t* codes, const u
                             const uint16_t* rnorms, int64_t n, void* y, bool out_f16, int64_t ldy_bytes,
                             hipStream_t s);
 
+// Outlier channels of QJL-only keys: record row r belongs to head
+// r / head_rows, whose k channels are chans[head * k .. + k) (increasing,
+// < 128); the record's outlier array holds k halves per row.
+constexpr int kMaxOutliers = 16;
+struct OutlierArgs {
+    const uint8_t* chans = nullptr;
+    int64_t heads = 0;            // rows of chans
+    int64_t head_rows = 1;
+    int k = 0;
+    uint16_t* out = nullptr;      // quantise: written [n][k]
+    const uint16_t* in = nullptr; // dequantise: read [n][k]
+};
+// Scoring QJL-only keys with separated outliers: channel sets per KV head
+// (global head index) and the keys' outlier halves, record-row major.
+struct ScoreOutliers {
+    const uint8_t* chans = nullptr;
+    const uint16_t* values = nullptr;
+    int k = 0;
+};
+
 // Optional page table of record rows: key t of (global) KV head j lives in
 // record row pages[j * stride + (t >> shift)] * 2^shift + (t & (2^shift - 1)).
 // With pages == nullptr, KV head j's keys are rows j * kv_stride + t.
@@ -108,7 +128,7 @@ struct PageTable {
 hipError_t score(const ScoreTables& t, const float* q, int hq, int group, const uint32_t* codes,
                  const uint16_t* norms, const uint32_t* signs, const uint16_t* rnorms, int64_t tkeys,
                  int64_t kv_stride, int kv_head0, float* scores, int64_t ld_scores, hipStream_t s,
-                 const PageTable& pt = PageTable{});
+                 const PageTable& pt = PageTable{}, const ScoreOutliers& so = ScoreOutliers{});
 
 
 // A partial row of the attention value pass: centroid sums for coordinates
@@ -168,6 +188,16 @@ hipError_t qjl1_quantize(const Qjl1Dev& P, const void* x, bool in_f16, int64_t l
                          hipStream_t s);
 hipError_t qjl1_dequantize(const Qjl1Dev& P, const uint16_t* norms, const uint32_t* signs, const uint16_t* rnorms,
                            int64_t n, void* y, bool out_f16, int64_t ldy_bytes, hipStream_t s);
+hipError_t qjl1_quantize_outliers(const Qjl1Dev& P, const void* x, bool in_f16, int64_t ldx_bytes, int64_t n,
+                                  uint16_t* norms, uint32_t* signs, uint16_t* rnorms, const OutlierArgs& o,
+                                  hipStream_t s);
+hipError_t qjl1_dequantize_outliers(const Qjl1Dev& P, const uint16_t* norms, const uint32_t* signs,
+                                    const uint16_t* rnorms, int64_t n, void* y, bool out_f16, int64_t ldy_bytes,
+                                    const OutlierArgs& o, hipStream_t s);
+// Per head of head_rows consecutive rows: the k channels of largest mean |x|
+// (rq_outlier.hip).
+hipError_t outlier_select(const void* x, bool in_f16, int64_t heads, int64_t head_rows, int64_t ldx_bytes, int k,
+                          uint8_t* chans, hipStream_t s);
 
 constexpr int kPolarScoreRows = 32;   // query rows per scoring workgroup
 hipError_t polar_quantize(const PolarDev& P, const void* x, bool in_f16, int64_t ldx_bytes, int64_t n,

@@ -8,15 +8,83 @@
 // 32x32x16 fp16 MFMAs from exact hi/lo halves of x_u carried times 2^12,
 // sign words from the accumulator sign bits, S^T sigma on MFMAs), without
 // the group loop: every K block of the residual is ready after the norm.
+//
+// Outlier-channel separation (README "CUDA Kernels": the 1-bit QJL quantiser
+// separates outliers): with OUTL, the k channels listed for a vector's head
+// are read out of the LDS tile as exact halves, stored in the record's
+// outlier array and cleared before the norm, so the sign sketch sees only
+// the inlier part; dequantisation writes the stored values back over those
+// channels after the reconstruction has left.
 #include "rq_rotor.cuh"
 
 namespace rqk {
 
-template <bool IN_F16, bool OUT_F16, bool ROUNDTRIP>
+// Lane l's vector (row base + l) belongs to head (base + l) / head_rows;
+// channel i of that head is chans[head * k + i] (masked to 0..127).
+__device__ __forceinline__ uint32_t outlier_channel(const OutlierArgs& o, int64_t head, int i) {
+    const rsrc_t rc = make_rsrc(o.chans, static_cast<uint32_t>(o.heads * o.k));
+    return __builtin_amdgcn_raw_buffer_load_b8(rc, static_cast<uint32_t>(head * o.k + i), 0, 0) & 127u;
+}
+
+// fp16 tile in LDS: store this lane's outlier halves, then clear them.
+__device__ __forceinline__ void outliers_take_f16(const OutlierArgs& o, int64_t base, int64_t n, u32x4* tile, int l) {
+    const int64_t head = (base + l) / o.head_rows;
+    const rsrc_t ro = make_rsrc(o.out + base * o.k, tile_range(n - base, 2 * o.k));
+    char* t8 = reinterpret_cast<char*>(tile);
+    for (int i = 0; i < o.k; ++i) {
+        const uint32_t c = outlier_channel(o, head, i);
+        uint16_t* p = reinterpret_cast<uint16_t*>(t8 + swz(l, static_cast<int>(c >> 3)) * 16 + (c & 7) * 2);
+        const uint16_t v = *p;
+        __builtin_amdgcn_raw_buffer_store_b16(v, ro, static_cast<uint32_t>(2 * (l * o.k + i)), 0, kNonTemporal);
+        *p = 0;
+    }
+}
+
+// fp32 input: half h of the row (coordinates 64 h .. 64 h + 63) is in LDS;
+// its outlier values are stored as halves (round to nearest even), then cleared.
+__device__ __forceinline__ void outliers_take_f32(const OutlierArgs& o, int64_t base, int64_t n, u32x4* tile, int l,
+                                                  int h) {
+    const int64_t head = (base + l) / o.head_rows;
+    const rsrc_t ro = make_rsrc(o.out + base * o.k, tile_range(n - base, 2 * o.k));
+    char* t8 = reinterpret_cast<char*>(tile);
+    for (int i = 0; i < o.k; ++i) {
+        const int c = static_cast<int>(outlier_channel(o, head, i)) - 64 * h;
+        if (c < 0 || c >= 64) continue;
+        float* p = reinterpret_cast<float*>(t8 + swz(l, c >> 2) * 16 + (c & 3) * 4);
+        const float v = *p;
+        __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(f2h(v)), ro, static_cast<uint32_t>(2 * (l * o.k + i)),
+                                              0, kNonTemporal);
+        *p = 0.0f;
+    }
+}
+
+// After this wave's output rows have been stored: the stored outlier values
+// over their channels (the wait orders them after the earlier stores).
+template <bool OUT_F16>
+__device__ __forceinline__ void outliers_put(const OutlierArgs& o, int64_t base, int64_t n, char* y, int64_t ldy_bytes,
+                                             int l) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const int64_t head = (base + l) / o.head_rows;
+    const rsrc_t ri = make_rsrc(o.in + base * o.k, tile_range(n - base, 2 * o.k));
+    const rsrc_t ry = make_rsrc(y + base * ldy_bytes, tile_range(n - base, ldy_bytes));
+    for (int i = 0; i < o.k; ++i) {
+        const uint32_t c = outlier_channel(o, head, i);
+        const uint32_t v = __builtin_amdgcn_raw_buffer_load_b16(ri, static_cast<uint32_t>(2 * (l * o.k + i)), 0, 0);
+        const uint32_t off = static_cast<uint32_t>(l * ldy_bytes);
+        if constexpr (OUT_F16)
+            __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(v), ry, off + 2 * c, 0, kNonTemporal);
+        else
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, h2f(v)), ry, off + 4 * c, 0,
+                                                  kNonTemporal);
+    }
+}
+
+template <bool IN_F16, bool OUT_F16, bool ROUNDTRIP, bool OUTL = false>
 __global__ __launch_bounds__(256) void qjl1_quant_kernel(Qjl1Dev P, const char* __restrict__ x, int64_t ldx_bytes,
                                                          int64_t n, uint16_t* __restrict__ norms,
                                                          uint32_t* __restrict__ signs, uint16_t* __restrict__ rnorms,
-                                                         char* __restrict__ y, int64_t ldy_bytes) {
+                                                         char* __restrict__ y, int64_t ldy_bytes, OutlierArgs o) {
+    static_assert(!(OUTL && ROUNDTRIP), "outlier sessions have no fused roundtrip");
     constexpr float D = kQjlDomain;
     struct Lds {
         u32x4 tiles[4][kTileBytes / 16];
@@ -37,7 +105,31 @@ __global__ __launch_bounds__(256) void qjl1_quant_kernel(Qjl1Dev P, const char* 
         const int64_t base = t * 64;
         const int l = lane_id() + opaque_zero();
         VecIn<IN_F16> in;
-        in.load(x, ldx_bytes, base, n, tile, l);
+        if constexpr (!OUTL) {
+            in.load(x, ldx_bytes, base, n, tile, l);
+        } else if constexpr (IN_F16) {
+            tile_load(x, ldx_bytes, base, n, 0, tile, l);
+            wave_lds_sync();
+            outliers_take_f16(o, base, n, tile, l);
+            in.own_row(tile, l);
+        } else {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                tile_load(x, ldx_bytes, base, n, 256 * h, tile, l);
+                wave_lds_sync();
+                outliers_take_f32(o, base, n, tile, l, h);
+                wave_lds_sync();
+#pragma unroll
+                for (int c = 0; c < 16; ++c) {
+                    const u32x4 q = tile[swz(l, c)];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t w = q[e];
+                        in.v[64 * h + 4 * c + e] = __builtin_bit_cast(float, w);
+                    }
+                }
+            }
+        }
         float ss = 0.0f;
 #pragma unroll
         for (int i = 0; i < kD; ++i) {
@@ -98,11 +190,11 @@ __global__ __launch_bounds__(256) void qjl1_quant_kernel(Qjl1Dev P, const char* 
     }
 }
 
-template <bool OUT_F16>
+template <bool OUT_F16, bool OUTL = false>
 __global__ __launch_bounds__(256) void qjl1_dequant_kernel(Qjl1Dev P, const uint16_t* __restrict__ norms,
                                                            const uint32_t* __restrict__ signs,
                                                            const uint16_t* __restrict__ rnorms, int64_t n,
-                                                           char* __restrict__ y, int64_t ldy_bytes) {
+                                                           char* __restrict__ y, int64_t ldy_bytes, OutlierArgs o) {
     constexpr float D = kQjlDomain;
     struct Lds {
         u32x4 tiles[4][kTileBytes / 16];
@@ -135,6 +227,7 @@ __global__ __launch_bounds__(256) void qjl1_dequant_kernel(Qjl1Dev P, const uint
             }
         });
         if (!OUT_F16 || !single) out.store(y, ldy_bytes, base, n);
+        if constexpr (OUTL) outliers_put<OUT_F16>(o, base, n, y, ldy_bytes, l);
     }
 }
 
@@ -146,7 +239,7 @@ hipError_t qjl1_quantize(const Qjl1Dev& P, const void* x, bool in_f16, int64_t l
     char* yc = static_cast<char*>(y);
 #define Q1_LAUNCH(IF, OF, RT)                                                                                  \
     hipLaunchKernelGGL((qjl1_quant_kernel<IF, OF, RT>), dim3(grid), dim3(256), 0, s, P, xc, ldx_bytes, n, norms, \
-                       signs, rnorms, yc, ldy_bytes)
+                       signs, rnorms, yc, ldy_bytes, OutlierArgs{})
     if (!roundtrip) {
         if (in_f16) Q1_LAUNCH(true, true, false); else Q1_LAUNCH(false, true, false);
     } else if (in_f16) {
@@ -164,10 +257,38 @@ hipError_t qjl1_dequantize(const Qjl1Dev& P, const uint16_t* norms, const uint32
     char* yc = static_cast<char*>(y);
     if (out_f16)
         hipLaunchKernelGGL((qjl1_dequant_kernel<true>), dim3(grid), dim3(256), 0, s, P, norms, signs, rnorms, n, yc,
-                           ldy_bytes);
+                           ldy_bytes, OutlierArgs{});
     else
         hipLaunchKernelGGL((qjl1_dequant_kernel<false>), dim3(grid), dim3(256), 0, s, P, norms, signs, rnorms, n, yc,
-                           ldy_bytes);
+                           ldy_bytes, OutlierArgs{});
+    return hipGetLastError();
+}
+
+hipError_t qjl1_quantize_outliers(const Qjl1Dev& P, const void* x, bool in_f16, int64_t ldx_bytes, int64_t n,
+                                  uint16_t* norms, uint32_t* signs, uint16_t* rnorms, const OutlierArgs& o,
+                                  hipStream_t s) {
+    const int grid = grid_for(n, 1);
+    const char* xc = static_cast<const char*>(x);
+    if (in_f16)
+        hipLaunchKernelGGL((qjl1_quant_kernel<true, true, false, true>), dim3(grid), dim3(256), 0, s, P, xc, ldx_bytes,
+                           n, norms, signs, rnorms, nullptr, 0, o);
+    else
+        hipLaunchKernelGGL((qjl1_quant_kernel<false, true, false, true>), dim3(grid), dim3(256), 0, s, P, xc,
+                           ldx_bytes, n, norms, signs, rnorms, nullptr, 0, o);
+    return hipGetLastError();
+}
+
+hipError_t qjl1_dequantize_outliers(const Qjl1Dev& P, const uint16_t* norms, const uint32_t* signs,
+                                    const uint16_t* rnorms, int64_t n, void* y, bool out_f16, int64_t ldy_bytes,
+                                    const OutlierArgs& o, hipStream_t s) {
+    const int grid = grid_for(n, 1);
+    char* yc = static_cast<char*>(y);
+    if (out_f16)
+        hipLaunchKernelGGL((qjl1_dequant_kernel<true, true>), dim3(grid), dim3(256), 0, s, P, norms, signs, rnorms, n,
+                           yc, ldy_bytes, o);
+    else
+        hipLaunchKernelGGL((qjl1_dequant_kernel<false, true>), dim3(grid), dim3(256), 0, s, P, norms, signs, rnorms,
+                           n, yc, ldy_bytes, o);
     return hipGetLastError();
 }
 

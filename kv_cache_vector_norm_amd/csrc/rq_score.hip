@@ -22,6 +22,13 @@
 // 2-bit codes (or two wider ones) into packed centroid halves with LDS
 // table lookups and eight sign bits into +-1 halves with a table or shifts.
 // The rotor pad coordinate (slot 128) is added in fp32 in the epilogue.
+//
+// QJL-only keys with separated outlier channels (OUTL; README "CUDA
+// Kernels": the 1-bit quantiser separates outliers): the block's query rows
+// are split into their values on the KV head's outlier channels (kept in
+// fp32) and the rest q_in (those channels cleared) before S q_in is built;
+// per key the score is n^ gamma^ sqrt(pi/2)/m <S q_in, sigma> +
+// sum_i q_{c_i} o^_i over the key's stored outlier halves o^.
 #include "rq_common.cuh"
 #include "rq_kernels.h"
 
@@ -69,6 +76,9 @@ struct MainArgs {
     float* scores;
     int64_t ld;
     PageTable pt;
+    const uint8_t* ochans = nullptr;   // OUTL: outlier channels, [KV heads][ok]
+    const uint16_t* outl = nullptr;    // OUTL: outlier halves of the keys, [record rows][ok]
+    int ok = 0;                        // outlier channels per head (<= 16)
 };
 
 // Record row of the first key of the 64-key tile at key kbase of KV head
@@ -104,15 +114,16 @@ __device__ __forceinline__ uint32_t half_at(const uint16_t* __restrict__ src, in
 // One tile's record in registers: lane l holds dword it * 64 + l of the
 // tile's code and sign runs, and the fp16 norm / residual norm of keys
 // l % 32 + 32 j (KPL = 2) or l % 16 + 16 j (KPL = 4).  Fetched one tile ahead.
-template <int W, int KPL>
+template <int W, int KPL, bool OUTL = false>
 struct RecRegs {
     uint32_t c[W > 0 ? W : 1];
     uint32_t s[4];
     uint32_t kn[KPL], kg[KPL];
+    uint32_t o[OUTL ? 16 : 1];  // half it * 64 + l of the tile's outlier halves
 };
-template <int W, bool QJL, int KPL>
+template <int W, bool QJL, int KPL, bool OUTL = false>
 __device__ __forceinline__ void rec_fetch(const MainArgs& a, int64_t rbase, int head, int64_t kbase,
-                                          RecRegs<W, KPL>& r, int l) {
+                                          RecRegs<W, KPL, OUTL>& r, int l) {
     const int64_t left = a.t - kbase;
     const int64_t row = tile_row(a.pt, rbase, head, kbase);
     const rsrc_t rc = make_rsrc(a.codes + row * W, tile_range(left, 4 * W));
@@ -131,6 +142,29 @@ __device__ __forceinline__ void rec_fetch(const MainArgs& a, int64_t rbase, int 
     for (int j = 0; j < KPL; ++j) {
         r.kn[j] = half_at(a.norms + row, 0, left, KS * j + n);
         r.kg[j] = QJL ? half_at(a.rnorms + row, 0, left, KS * j + n) : 0u;
+    }
+    if constexpr (OUTL) {
+        // the tile's keys hold 64 ok halves in one run (16-bit loads: the run
+        // starts on any half boundary)
+        const rsrc_t ro = make_rsrc(a.outl + row * a.ok, tile_range(left, 2 * a.ok));
+#pragma unroll
+        for (int it = 0; it < 16; ++it)
+            r.o[it] = it < a.ok ? __builtin_amdgcn_raw_buffer_load_b16(ro, static_cast<uint32_t>(2 * l), 128 * it,
+                                                                       kNonTemporal)
+                                : 0u;
+    }
+}
+
+// OUTL: the tile's outlier halves into the wave's LDS stage (key-major,
+// ok halves per key).
+template <int W, int KPL, bool OUTL>
+__device__ __forceinline__ void stage_outliers(const MainArgs& a, const RecRegs<W, KPL, OUTL>& r,
+                                               uint32_t* __restrict__ ost, int l) {
+    if constexpr (OUTL) {
+        uint16_t* o16 = reinterpret_cast<uint16_t*>(ost);
+#pragma unroll
+        for (int it = 0; it < 16; ++it)
+            if (it < a.ok) o16[it * 64 + l] = static_cast<uint16_t>(r.o[it]);
     }
 }
 
@@ -298,9 +332,9 @@ __device__ __forceinline__ void query_load(const MainArgs& a, int row0, int nrow
     }
 }
 
-template <bool PAD, bool QJL, int NMT, class Lds>
+template <bool PAD, bool QJL, int NMT, bool OUTL = false, class Lds>
 __device__ __forceinline__ void build_query_rows(const MainArgs& a, const QueryRegs<NMT>& qr,
-                                                 const QueryFrags<QJL>& fr, float inv_sc, Lds& lds) {
+                                                 const QueryFrags<QJL>& fr, float inv_sc, Lds& lds, int ghead = 0) {
     constexpr int ROWS = NMT * 32;
     constexpr int TPR = kBlock / ROWS;   // threads per row
     constexpr int CPT = kD / TPR;        // coordinates per thread
@@ -315,6 +349,20 @@ __device__ __forceinline__ void build_query_rows(const MainArgs& a, const QueryR
         }
     }
     __syncthreads();
+    if constexpr (OUTL) {
+        // the KV head's outlier channels: the query values there are kept for
+        // the separate term, then cleared so that S q sees q_in only
+        for (int idx = t; idx < ROWS * a.ok; idx += kBlock) {
+            const int r = idx / a.ok, i = idx % a.ok;
+            lds.qo[r][i] = lds.qf[r][a.ochans[static_cast<int64_t>(ghead) * a.ok + i] & 127];
+        }
+        __syncthreads();
+        for (int idx = t; idx < ROWS * a.ok; idx += kBlock) {
+            const int r = idx / a.ok, i = idx % a.ok;
+            lds.qf[r][a.ochans[static_cast<int64_t>(ghead) * a.ok + i] & 127] = 0.0f;
+        }
+        __syncthreads();
+    }
     {
         const int r = t / TPR, part = t % TPR;
         const float* q = lds.qf[r];
@@ -359,8 +407,9 @@ __device__ __forceinline__ void build_query_rows(const MainArgs& a, const QueryR
 // NMT = 1, 2: 32-row M tiles (32x32x16 MFMAs), NMT = 0: groups of at most 16
 // query rows on 16x16x32 MFMAs (the query side is built as for one 32-row
 // tile and rows 0..15 are read).
-template <int B, bool QJL, bool PAD, int NMT>
+template <int B, bool QJL, bool PAD, int NMT, bool OUTL = false>
 __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
+    static_assert(!OUTL || (B == 0 && QJL && !PAD), "outlier channels are separated for QJL-only keys");
     constexpr int NB = NMT > 0 ? NMT : 1;   // 32-row tiles of the query build
     constexpr int KPL = NMT > 0 ? 2 : 4;    // keys per lane in a 64-key tile
     constexpr int NC = PAD ? kRotCoords : kD;
@@ -391,6 +440,8 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
         uint32_t stage[4][64 * SW + 4];   // (+4: the 3-bit reads of the 16-row loop run one word past)
         float qf[ROWS][kD + 4];
         u32x4 qrows[ROWS * kRowStride];
+        float qo[OUTL ? ROWS : 1][16];                 // query values on the outlier channels
+        uint32_t ostage[OUTL ? 4 : 1][OUTL ? 512 : 1];  // per wave: the tile's outlier halves
     };
     __shared__ Lds lds;
 
@@ -405,10 +456,10 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
     const int64_t rbase = static_cast<int64_t>(a.kv_head0 + kvh) * a.kv_stride;
     const int64_t tstep = gridDim.x * 4LL;
     // the first tile's record is requested before the block's staging
-    RecRegs<W, KPL> rec;
+    RecRegs<W, KPL, OUTL> rec;
     int64_t tile = blockIdx.x * 4LL + wave;
     const int ghead = a.kv_head0 + kvh;
-    if (tile < ntiles) rec_fetch<W, QJL, KPL>(a, rbase, ghead, tile * 64, rec, lane_id());
+    if (tile < ntiles) rec_fetch<W, QJL, KPL, OUTL>(a, rbase, ghead, tile * 64, rec, lane_id());
     // and so are the query rows and the X / S fragments of the query build
     QueryRegs<NB> qr;
     query_load<NB>(a, row0, nrows, qr);
@@ -441,7 +492,9 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
         }
         if (threadIdx.x < L) lds.cent[threadIdx.x] = a.cent[threadIdx.x];
     }
-    build_query_rows<PAD, QJL, NB>(a, qr, fr, inv_sc, lds);
+    build_query_rows<PAD, QJL, NB, OUTL>(a, qr, fr, inv_sc, lds, ghead);
+    uint32_t* ost = lds.ostage[wave];
+    const uint16_t* oh = reinterpret_cast<const uint16_t*>(ost);
 
     uint32_t* st = lds.stage[wave];
     const int64_t nk = a.t;   // keys of this head
@@ -513,7 +566,8 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
                 kn[j] = h2f(rec.kn[j]);
                 kg[j] = QJL ? h2f(rec.kg[j]) * a.qjl_scale : 0.0f;
             }
-            if (tile + tstep < ntiles) rec_fetch<W, QJL, KPL>(a, rbase, ghead, (tile + tstep) * 64, rec, l);
+            stage_outliers(a, rec, ost, l);
+            if (tile + tstep < ntiles) rec_fetch<W, QJL, KPL, OUTL>(a, rbase, ghead, (tile + tstep) * 64, rec, l);
 
             f32x4 acc1[4], acc2[4];
 #pragma unroll
@@ -556,6 +610,22 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
             // the end get an offset beyond it
             const rsrc_t rs = make_rsrc(a.scores + static_cast<int64_t>(row0) * a.ld + kbase,
                                         static_cast<uint32_t>(((nrows - 1) * a.ld + (nk - kbase)) * 4));
+            // OUTL: sum_i q_{c_i} o^_i for rows 4 g + i of keys 16 j + c
+            float ot[4][4] = {};
+            if constexpr (OUTL) {
+                wave_lds_sync();
+                for (int i = 0; i < a.ok; ++i) {
+                    float ov[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) ov[j] = h2f(oh[(16 * j + c) * a.ok + i]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float qv = lds.qo[4 * g + r][i];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) ot[r][j] = __builtin_fmaf(qv, ov[j], ot[r][j]);
+                    }
+                }
+            }
             if (4 * g < nrows) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -573,6 +643,7 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
                             v = __builtin_fmaf(kg[j], e2 * s1, v);
                         }
                         v *= kn[j];
+                        if constexpr (OUTL) v += ot[i][j];
                         const uint32_t voff =
                             kbase + key < nk ? static_cast<uint32_t>((row * a.ld + key) * 4) : 0x80000000u;
                         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rs, voff, 0,
@@ -634,7 +705,8 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
             kg[nt] = QJL ? h2f(rec.kg[nt]) * a.qjl_scale : 0.0f;
         }
         // next tile's record, in flight during this tile's MFMAs and stores
-        if (tile + tstep < ntiles) rec_fetch<W, QJL, KPL>(a, rbase, ghead, (tile + tstep) * 64, rec, l);
+        stage_outliers(a, rec, ost, l);
+        if (tile + tstep < ntiles) rec_fetch<W, QJL, KPL, OUTL>(a, rbase, ghead, (tile + tstep) * 64, rec, l);
 
         f32x16 acc1[NMT][2], acc2[NMT][2];
 #pragma unroll
@@ -727,6 +799,22 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
             const int key = 32 * nt + n;
             voff[nt] = kbase + key < nk ? static_cast<uint32_t>((4 * hh * a.ld + key) * 4) : 0x80000000u;
         }
+        // OUTL: sum_i q_{c_i} o^_i for the lane's rows of keys n and 32 + n
+        float ot[OUTL ? NMT : 1][OUTL ? 16 : 1][2] = {};
+        if constexpr (OUTL) {
+            wave_lds_sync();
+            for (int i = 0; i < a.ok; ++i) {
+                const float ov0 = h2f(oh[n * a.ok + i]), ov1 = h2f(oh[(32 + n) * a.ok + i]);
+#pragma unroll
+                for (int m = 0; m < NMT; ++m)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float qv = lds.qo[32 * m + 8 * (r / 4) + (r % 4) + 4 * hh][i];
+                        ot[m][r][0] = __builtin_fmaf(qv, ov0, ot[m][r][0]);
+                        ot[m][r][1] = __builtin_fmaf(qv, ov1, ot[m][r][1]);
+                    }
+            }
+        }
 #pragma unroll
         for (int m = 0; m < NMT; ++m)
 #pragma unroll
@@ -747,6 +835,7 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
                         v = __builtin_fmaf(kg[nt], e2 * s1, v);
                     }
                     v *= kn[nt];
+                    if constexpr (OUTL) v += ot[m][r][nt];
                     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rs, voff[nt],
                                                           static_cast<int>(rowc * a.ld * 4), kNonTemporal);
                 }
@@ -760,7 +849,7 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
 // as many as fill the workgroup slots of the chip in one round (two per CU
 // for the 32-row variant, one for the 64-row variant, whose LDS is larger);
 // each wave then walks many 64-key tiles.  At least one tile per wave.
-template <int B, bool QJL, bool PAD, int NMT>
+template <int B, bool QJL, bool PAD, int NMT, bool OUTL = false>
 static void launch_main(const MainArgs& a, int kv_heads, int qblocks, hipStream_t s) {
     const int64_t ntiles = (a.t + 63) / 64;
     const int64_t want = (ntiles + 3) / 4;
@@ -769,7 +858,7 @@ static void launch_main(const MainArgs& a, int kv_heads, int qblocks, hipStream_
     int64_t gx = slots / units;
     if (gx > want) gx = want;
     if (gx < 1) gx = 1;
-    hipLaunchKernelGGL((score_kernel<B, QJL, PAD, NMT>), dim3(static_cast<unsigned>(gx), kv_heads * qblocks),
+    hipLaunchKernelGGL((score_kernel<B, QJL, PAD, NMT, OUTL>), dim3(static_cast<unsigned>(gx), kv_heads * qblocks),
                        dim3(kBlock), 0, s, a);
 }
 
@@ -789,7 +878,7 @@ static void launch_main_b(bool dense, int nmt, const MainArgs& a, int kv_heads, 
 hipError_t score(const ScoreTables& t, const float* q, int hq, int group, const uint32_t* codes,
                  const uint16_t* norms, const uint32_t* signs, const uint16_t* rnorms, int64_t tkeys,
                  int64_t kv_stride, int kv_head0, float* scores, int64_t ld_scores, hipStream_t s,
-                 const PageTable& pt) {
+                 const PageTable& pt, const ScoreOutliers& so) {
     MainArgs a;
     a.pt = pt;
     a.q = q;
@@ -813,6 +902,16 @@ hipError_t score(const ScoreTables& t, const float* q, int hq, int group, const 
     const int kv_heads = hq / group;
     const int qblocks = (group + 63) / 64;
     const int nmt = a.rows_per_block > 32 ? 2 : a.rows_per_block > 16 ? 1 : 0;
+    if (so.chans) {
+        if (t.mse_bits != 0 || !t.qjl) return hipErrorInvalidValue;
+        a.ochans = so.chans;
+        a.outl = so.values;
+        a.ok = so.k;
+        if (nmt == 0) launch_main<0, true, false, 0, true>(a, kv_heads, qblocks, s);
+        else if (nmt == 1) launch_main<0, true, false, 1, true>(a, kv_heads, qblocks, s);
+        else launch_main<0, true, false, 2, true>(a, kv_heads, qblocks, s);
+        return hipGetLastError();
+    }
     switch (t.mse_bits * 2 + (t.qjl ? 1 : 0)) {
         case 1: launch_main_b<0, true>(t.dense, nmt, a, kv_heads, qblocks, s); break;
         case 2: launch_main_b<1, false>(t.dense, nmt, a, kv_heads, qblocks, s); break;
