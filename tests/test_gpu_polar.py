@@ -314,3 +314,36 @@ def test_attention_polar_values_strided_heads(K, P):
         kmax = PR.polar_radius_norm(hk[j * stride:j * stride + t]).max()
         lim = (2e-4 * scale * np.linalg.norm(q[h]) * kmax + 1e-5) * vmax
         assert np.abs(got[h] - ref[h]).max() <= lim, h
+
+
+@pytest.mark.parametrize("t,kvh,group", [(40000, 1, 4), (40000, 2, 4)])
+def test_attention_polar_values_several_tiles_per_wave(K, P, t, kvh, group):
+    """PolarQuant values over 40,000 keys per KV head: with at most 64 key
+    slices per (KV head, row block), each wave of the value pass carries its
+    sums across two or three 64-key tiles (the loop that reuses the staging
+    LDS and the row weights).  Against softmax of the GPU's own estimates
+    times the oracle's dequantised values, in float64."""
+    pv = PQ.PolarParams(D, 3)
+    kc, vc = K.Codec(bits=3, seed=0, mode=K.RQ_QJL), K.PolarCodec(seed=3)
+    plan_slices = min(64, 512 // kvh)
+    assert -(-t // 64) > 4 * plan_slices          # more tiles than waves: several per wave
+    keys = W.gaussian(kvh * t, seed=151, dtype=np.float16)
+    vals = W.gaussian(kvh * t, seed=152, dtype=np.float16)
+    q = W.queries(kvh * group, seed=153)
+    kd = kc.quantize(torch.from_numpy(keys).cuda())
+    vw = vc.quantize(torch.from_numpy(vals).cuda())
+    qd = torch.from_numpy(q).cuda()
+    scale = 1 / np.sqrt(D)
+    out = K.attend(kc, vc, qd, kd, vw, group, t, t, scale)
+    s = kc.score(qd, kd, group, t)
+    torch.cuda.synchronize()
+    hv = _words(vw)
+    got = out.cpu().numpy().astype(np.float64)
+    sg = s.cpu().numpy().astype(np.float64)
+    for j in range(kvh):
+        xv = PQ.dequantize(pv, hv[j * t:(j + 1) * t])
+        vmax = np.abs(xv).max()
+        for h in range(j * group, (j + 1) * group):
+            z = scale * sg[h]
+            wgt = np.exp(z - z.max())
+            assert np.abs(got[h] - (wgt / wgt.sum()) @ xv).max() <= 1e-5 * vmax, h

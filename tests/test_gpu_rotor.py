@@ -201,3 +201,17 @@ def test_roundtrip_with_several_tiles_per_wave(K, bits, mode, n):
     for a, b in zip((rec.codes, rec.norms, rec.signs, rec.rnorms), (rec2.codes, rec2.norms, rec2.signs, rec2.rnorms)):
         assert (a is None and b is None) or torch.equal(a, b)
     assert torch.equal(y, d)
+    # oracle sample: rows of the last 65,536 (for the MSE-only launch these are
+    # all second tiles of their waves, fetched during the first) and of the first
+    rows = np.concatenate([W.sample_rows(65536, 1 / 32, seed=n), n - 65536 + W.sample_rows(65536, 1 / 32, seed=n + 1)])
+    idx = torch.from_numpy(rows).cuda()
+    xs = x[idx].float().cpu().numpy()
+    codes, norms, signs, rnorms = (None if a is None else a[idx].cpu().numpy()
+                                   for a in (rec.codes, rec.norms, rec.signs, rec.rnorms))
+    codes, norms = codes.view(np.uint32), norms.view(np.uint16)
+    signs = None if signs is None else signs.view(np.uint32)
+    rnorms = None if rnorms is None else rnorms.view(np.uint16)
+    p = _oracle_params(bits, mode)
+    PR.check_records(p, xs, codes, norms, signs, rnorms)
+    PR.compare_recon(y[idx].float().cpu().numpy(), OC.dequantize(p, PR.record_from_host(codes, norms, signs, rnorms)),
+                     OC.half_value(norms), "roundtrip sample", tol=PR.RECON_TOL + 2.0 ** -11)

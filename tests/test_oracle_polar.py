@@ -177,3 +177,29 @@ def test_attention_over_polar_values():
         gap = s[5] - np.max(np.delete(s, 5))
         assert gap > 30
         assert np.abs(out[0] - xv[5]).max() < t * np.exp(-gap) * np.abs(xv).max() + 1e-12
+
+
+@pytest.mark.parametrize("level", [1, 2, 3])
+def test_later_codebooks_are_cell_means_by_gauss_legendre(level):
+    """The centroid condition of Lloyd's algorithm checked by a quadrature
+    other than the one the oracle iterates with: on every cell
+    [t_(i-1), t_i] of levels 2..4 the centroid is the mean angle of the
+    article's law sin^(k-1)(2 theta), k = 2^(l-1) (normalising constants
+    cancel), from 200-point Gauss-Legendre rules on 16 sub-intervals; the
+    boundaries are the centroids' midpoints.  Stored values are fp32, hence
+    the tolerance."""
+    c, t = PQ.codebooks()[level]
+    k = 2 ** level
+    lo = np.r_[0.0, t]
+    hi = np.r_[t, math.pi / 2.0]
+    xg, wg = np.polynomial.legendre.leggauss(200)
+    for i in range(len(c)):
+        edges = np.linspace(lo[i], hi[i], 17)
+        m0 = m1 = 0.0
+        for a, b in zip(edges[:-1], edges[1:]):
+            th = 0.5 * (b - a) * xg + 0.5 * (b + a)
+            w = 0.5 * (b - a) * wg * np.sin(2.0 * th) ** (k - 1)
+            m0 += w.sum()
+            m1 += (w * th).sum()
+        assert abs(m1 / m0 - c[i]) <= 2e-7 * abs(c[i])
+    assert np.allclose(t, 0.5 * (c[:-1] + c[1:]), rtol=2e-7, atol=0)
