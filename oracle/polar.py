@@ -100,29 +100,45 @@ class PolarParams:
         self.books = codebooks()
 
 
+def polar_pairs(y):
+    """The pairs each level's angles are taken of, and the final radii.
+
+    A level turns a vector of n coordinates into n/2 (angle, radius) pairs:
+    coordinate 2i is paired with coordinate 2i + 1 (the PolarQuant article's
+    polar transform takes consecutive coordinates two at a time), and the
+    next level does the same to the n/2 radii.  Returns ([pairs of level
+    1..4, each [N, n_l, 2]], radii [N, 8])."""
+    v = np.asarray(y, dtype=np.float64)
+    pairs = []
+    for _ in range(N_LEVELS):
+        pr = v.reshape(v.shape[0], v.shape[1] // 2, 2)
+        pairs.append(pr)
+        v = np.hypot(pr[..., 0], pr[..., 1])
+    return pairs, v
+
+
 def polar_transform(y):
-    """(angles per level, final radii) of rows of y, float64."""
-    r = np.asarray(y, dtype=np.float64)
+    """(angles per level, final radii) of rows of y, float64.  The angle of a
+    pair (first, second) is the polar angle of the point with those Cartesian
+    coordinates; level-1 angles are taken in [0, 2 pi), later levels pair
+    non-negative radii, so their angles lie in [0, pi/2]."""
+    pairs, radii = polar_pairs(y)
     angles = []
-    for level in range(N_LEVELS):
-        a, b = r[:, 0::2], r[:, 1::2]
-        th = np.arctan2(b, a)
+    for level, pr in enumerate(pairs):
+        th = np.arctan2(pr[..., 1], pr[..., 0])
         if level == 0:
-            th = np.mod(th, 2.0 * math.pi)
+            th = np.where(th < 0.0, th + 2.0 * math.pi, th)
         angles.append(th)
-        r = np.sqrt(a * a + b * b)
-    return angles, r
+    return angles, radii
 
 
 def polar_inverse(angles, radii):
-    """Walks the levels back: each radius r with angle th gives (r cos th, r sin th)."""
+    """Walks the levels back: each radius r with angle th is the pair
+    (r cos th, r sin th) of the level below."""
     r = np.asarray(radii, dtype=np.float64)
     for level in reversed(range(N_LEVELS)):
         th = angles[level]
-        out = np.empty((r.shape[0], 2 * r.shape[1]))
-        out[:, 0::2] = r * np.cos(th)
-        out[:, 1::2] = r * np.sin(th)
-        r = out
+        r = np.stack([r * np.cos(th), r * np.sin(th)], axis=-1).reshape(r.shape[0], 2 * r.shape[1])
     return r
 
 

@@ -141,12 +141,8 @@ def polar_level_points(p, x):
     x = np.asarray(x, dtype=np.float64)
     nrm = np.linalg.norm(x, axis=1)
     y = (x @ p.pi.T) / np.where(nrm > 0, nrm, 1.0)[:, None]
-    pts, r = [], y
-    for _ in range(PQ.N_LEVELS):
-        a, b = r[:, 0::2], r[:, 1::2]
-        pts.append((a, b))
-        r = np.sqrt(a * a + b * b)
-    return pts
+    pairs, _ = PQ.polar_pairs(y)
+    return [(pr[..., 0], pr[..., 1]) for pr in pairs]
 
 
 def polar_ray_distance(p, level, a, b):
