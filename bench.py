@@ -63,6 +63,8 @@ def parse():
                     help="run each profiled kernel a few times (for rocprofv3) and exit")
     ap.add_argument("--summarize", metavar="DIR",
                     help="turn rocprofv3 runs of --profile-set under DIR into profiles/ summaries, then exit")
+    ap.add_argument("--trace-summary", nargs=2, metavar=("TRACE_CSV", "OUT_MD"),
+                    help="group a rocprofv3 kernel trace by kernel and grid size into a markdown table, then exit")
     return ap.parse_args()
 
 
@@ -161,7 +163,7 @@ def profile_cases():
         ("rq_roundtrip_qjl3_65536", "rqk::rq_quant_kernel<2, true, true, true, true>",
          "15rq_quant_kernelILi2ELb1ELb1ELb1ELb1EE", 4, n1 * 568, 0,
          "rotor roundtrip, 2-bit codes + QJL, fp16 in/out, 65,536 keys (the step's codec kernel)"),
-        ("rq_score_64x65536", "rqk::score_kernel<2, true, true, 2>", "12score_kernelILi2ELb1ELb1ELi2EE", 4,
+        ("rq_score_64x65536", "rqk::score_kernel<2, true, true, 2, false>", "12score_kernelILi2ELb1ELb1ELi2ELb0EE", 4,
          n1 * 56 + 4 * N_Q * n1, 0, "q.k estimates of 64 queries against 65,536 compressed keys"),
         ("rq_roundtrip_mse3_65536", "rqk::rq_quant_kernel<3, false, true, true, true>",
          "15rq_quant_kernelILi3ELb0ELb1ELb1ELb1EE", 4, n1 * 566, 0,
@@ -300,7 +302,9 @@ def _col(row, *names):
 
 def _assign(names_in_order, cases):
     """Dispatch indices (in order) of each case: the k-th group of `launches`
-    dispatches whose kernel name starts with the case's prefix."""
+    dispatches whose kernel name (without a leading "void ") starts with the
+    case's prefix."""
+    names_in_order = [nm[5:] if nm.startswith("void ") else nm for nm in names_in_order]
     taken = {}
     out = {}
     for label, prefix, _, launches, *_ in cases:
@@ -388,7 +392,91 @@ def summarize(d):
         json.dump(traffic, f, indent=1)
     with open(os.path.join(ROOT, "profiles", "kernels.json"), "w") as f:
         json.dump(res, f, indent=1)
+    with open(os.path.join(ROOT, "profiles", "profile_set_counters.md"), "w") as f:
+        f.write(profile_markdown(res, cf, cw))
     print(json.dumps(res, indent=1))
+
+
+PROFILE_COMMANDS = """    cd /tmp && export TMPDIR=/tmp
+    rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/prof/kt -o kt -- python3 $R/bench.py --profile-set
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/prof/fetch -o p -- python3 $R/bench.py --profile-set
+    rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/prof/write -o p -- python3 $R/bench.py --profile-set
+    rocprofv3 --pmc VALUBusy MfmaUtil OccupancyPercent LDSBankConflict --output-format csv -d $R/gpurun_out/prof/busy -o p -- python3 $R/bench.py --profile-set
+    rocprofv3 --pmc SQ_WAVES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS --output-format csv -d $R/gpurun_out/prof/insts -o p -- python3 $R/bench.py --profile-set
+    rocprofv3 --pmc SQ_INSTS_SALU SQ_INSTS_SMEM SQ_INSTS_VMEM_RD SQ_INSTS_VMEM_WR --output-format csv -d $R/gpurun_out/prof/insts2 -o p -- python3 $R/bench.py --profile-set
+    python3 bench.py --summarize gpurun_out/prof          # (R = the repository root)
+"""
+
+
+def profile_markdown(res, cf, cw):
+    """One table per measured quantity over the profiled kernels."""
+    def g(e, k):
+        return e.get("counters", {}).get(k)
+
+    def fmt(v, nd=1):
+        if v is None:
+            return "-"
+        if isinstance(v, str):
+            return v
+        return f"{v:,.{nd}f}" if isinstance(v, float) else f"{v:,}"
+    out = ["# rocprofv3 counters of the profiled kernels (`bench.py --profile-set`)", "",
+           "Commands (MI355X; one counter set per run, each over the same launch sequence):", "",
+           PROFILE_COMMANDS, "",
+           "Each kernel runs one warm-up and three measured launches (the 256 MiB calibration copy",
+           "once); figures are means over the measured launches.  Machine-code digests tie each",
+           "row to the kernel as built (`kernel_code` / `profiles/kernels.json`).  HBM bytes are",
+           f"FETCH_SIZE and WRITE_SIZE scaled by what they read for the 256 MiB copy_kernel (fetch factor "
+           f"{cf:.4f}, write factor {cw:.4f} per byte moved).", "",
+           "| kernel (workload) | code | avg us (trace) | alg. bytes | alg. GB/s | of 8 TB/s | HBM bytes read + written "
+           "| HBM / alg. | VGPR | LDS B | scratch B/lane |",
+           "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for label, e in res.items():
+        hbm = (e["hbm_read_bytes"] + e["hbm_write_bytes"]) if "hbm_read_bytes" in e else None
+        out.append(f"| {label} | {e['code']} | {fmt(e['avg_us'], 2)} | {fmt(e['alg_bytes'] or None)} | "
+                   f"{fmt(e.get('alg_gbs'))} | {fmt(e.get('frac_hbm'), 3)} | {fmt(hbm)} | "
+                   f"{fmt(e.get('traffic_over_alg'), 3)} | {e['vgpr']} | {e['lds_bytes']} | {e['scratch_bytes']} |")
+    out += ["", "Busy and occupancy (rocprofv3 derived counters; percent of the GPU's time over the dispatch):", "",
+            "| kernel | VALUBusy % | MfmaUtil % | OccupancyPercent | LDSBankConflict % | useful MFMA TFLOP/s |",
+            "|---|---|---|---|---|---|"]
+    for label, e in res.items():
+        out.append(f"| {label} | {fmt(g(e, 'VALUBusy'))} | {fmt(g(e, 'MfmaUtil'))} | {fmt(g(e, 'OccupancyPercent'))} | "
+                   f"{fmt(g(e, 'LDSBankConflict'))} | {fmt(e.get('mfma_tflops'), 2)} |")
+    out += ["", "Instruction counts per dispatch (all waves; per wave = count / SQ_WAVES):", "",
+            "| kernel | SQ_WAVES | VALU / wave | MFMA / wave | LDS / wave | SALU / wave | SMEM / wave | VMEM rd / wave "
+            "| VMEM wr / wave |", "|---|---|---|---|---|---|---|---|---|"]
+    for label, e in res.items():
+        w = g(e, "SQ_WAVES")
+
+        def pw(k):
+            v = g(e, k)
+            return fmt(v / w) if v is not None and w else "-"
+        out.append(f"| {label} | {fmt(w, 0)} | {pw('SQ_INSTS_VALU')} | {pw('SQ_INSTS_MFMA')} | {pw('SQ_INSTS_LDS')} | "
+                   f"{pw('SQ_INSTS_SALU')} | {pw('SQ_INSTS_SMEM')} | {pw('SQ_INSTS_VMEM_RD')} | "
+                   f"{pw('SQ_INSTS_VMEM_WR')} |")
+    out += ["", "Workloads:", ""]
+    out += [f"- {label}: {e['what']}" for label, e in res.items()]
+    return "\n".join(out) + "\n"
+
+
+def trace_summary(path):
+    """Markdown table of a rocprofv3 kernel trace grouped by kernel and grid
+    size (this library's kernels): calls, average / minimum / maximum
+    duration in microseconds."""
+    rows = _read_csv(path)
+    groups = {}
+    for r in rows:
+        nm = r["Kernel_Name"]
+        nm = nm[5:] if nm.startswith("void ") else nm
+        if not nm.startswith("rqk::"):
+            continue                # the library's kernels only (not torch's set-up kernels)
+        nm = nm.split("(")[0]
+        key = (nm, int(r.get("Grid_Size_X") or r.get("Grid_Size") or 0))
+        groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = ["| kernel | grid (threads) | calls | avg us | min us | max us | total us |", "|---|---|---|---|---|---|---|"]
+    for (nm, grid), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| {nm} | {grid:,} | {len(d)} | {sum(d) / len(d):.2f} | {min(d):.2f} | {max(d):.2f} | "
+                     f"{sum(d):,.1f} |")
+    return "\n".join(lines) + "\n"
 
 
 def measured_traffic(label, digest):
@@ -528,7 +616,7 @@ def quality_row(K, W, dev, stream):
         return mse, cos
     g_mse, g_cos = mse_cos(yh)
     p = OP.Params(128, 3, 0, OP.MSE)
-    o_mse, o_cos = mse_cos(OC.roundtrip(p, xd))
+    o_mse, o_cos = mse_cos(OC.roundtrip(p, xd)[1])
     us, us_min = _b2b(stream, lambda i: c.roundtrip(x, rec=rec, out=y), 50, 5)
     # one launch after an idle device: event pair around a single call
     lat = []
@@ -739,6 +827,10 @@ def main():
     a = parse()
     if a.summarize:
         summarize(a.summarize)
+        return
+    if a.trace_summary:
+        with open(a.trace_summary[1], "w") as f:
+            f.write(trace_summary(a.trace_summary[0]))
         return
     if a.gpus != 1:
         print(f"bench.py measures one GPU: the codec library runs on a single MI355X and has no multi-GPU path "
