@@ -417,6 +417,9 @@ static rqk::DenseTables dense_tables(const rq_ctx* c) {
     t.cent = c->cent;
     t.s_rows = c->s_rows;
     t.s_cols = c->s_cols;
+    t.bins = c->bins;
+    t.bin_a = rqh::kBinA;
+    t.bin_b = c->host.bin_b;
     t.qjl_scale = static_cast<float>(std::sqrt(M_PI / 2.0) / rqh::kQjlRows);
     t.mse_bits = c->host.lay.mse_bits;
     t.qjl = c->host.lay.mode & RQ_QJL;

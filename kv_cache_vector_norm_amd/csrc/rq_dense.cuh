@@ -10,9 +10,13 @@
 // one fp32 accumulator by scaling v_hi by 2^11:
 //   P_hi (2^11 v_hi) + P_hi v_lo + P_lo v_hi = 2^11 * 256 * (Pi v) + O(2^-22).
 // The residual projection S r reuses the rotor path's exact scheme (S is
-// exactly half; r enters as hi + lo).  Pi and S feed the quantize side from
-// LDS; Pi^T and S^T feed the dequantize side from global memory (L2
-// resident), which keeps LDS within one workgroup's budget.
+// exactly half; r enters as hi + lo).  Pi feeds the quantize side from LDS;
+// Pi^T, S and S^T come from global memory (L2 resident), which keeps LDS
+// within one four-wave workgroup per CU.  Codes come from the rotor path's
+// exact 256-slot quantiser, with its thresholds scaled by 2^19 so that the
+// unscaled accumulators are compared directly.  With QJL, each 32-row tile
+// of x~_u = Pi^T y^ is turned into its two K blocks of the residual at once
+// and multiplied by S, so the split residual is never held whole.
 #pragma once
 
 #include "rq_common.cuh"
@@ -29,6 +33,8 @@ struct DenseDev {
     const float* __restrict__ cent;
     const uint16_t* __restrict__ s_rows;
     const uint16_t* __restrict__ s_cols;
+    const u32x4_t* __restrict__ bins;
+    float bin_a, bin_b;
     float qjl_scale;
 };
 
@@ -215,15 +221,38 @@ __device__ __forceinline__ void dense_dequant_vec(const DenseDev& P, const uint3
 }
 
 // ------------------------------------------------------------ kernels --
-template <int WAVES, bool QJL>
+template <int WAVES>
 struct DenseLds {
+    u32x4 bins[kBinSlots];      // slot table (LDS address 0), thresholds and centroids times 2^19
     u32x4 tiles[WAVES][kTileBytes / 16];
     u32x4 pih[128 * 16];
     u32x4 pil[128 * 16];
-    u32x4 s_rows[QJL ? 128 * 16 : 1];
     uint32_t ctab[32];
     float thr[16];
 };
+
+// The slot table with thresholds and centroids in the rotation's
+// accumulator scale (unit domain times 2^19 = 1 / kRotScale, exact).
+__device__ __forceinline__ void dense_bins_to_lds(const DenseDev& P, u32x4* __restrict__ s) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(P.bins);
+    for (int i = threadIdx.x; i < kBinSlots; i += blockDim.x) {
+        const u32x4 e = src[i];
+        const uint32_t e0 = e[0], e1 = e[1], e2 = e[2], e3 = e[3];
+        constexpr float up = 1.0f / kRotScale;
+        s[i] = u32x4{e0, __builtin_bit_cast(uint32_t, __builtin_bit_cast(float, e1) * up),
+                     __builtin_bit_cast(uint32_t, __builtin_bit_cast(float, e2) * up),
+                     __builtin_bit_cast(uint32_t, __builtin_bit_cast(float, e3) * up)};
+    }
+}
+
+// #{k : y > t_k} of y = acc * kRotScale through the slot table: the slot of
+// fma(acc, bin_a * kRotScale, bin_b) equals that of fma(y, bin_a, bin_b)
+// (power-of-two scalings are exact), and acc > 2^19 t equals y > t.
+__device__ __forceinline__ uint32_t dense_code(float acc, float ba, float bb, const char* __restrict__ bins) {
+    const uint32_t off = __builtin_bit_cast(uint32_t, __builtin_fmaf(acc, ba, bb)) & 0xFF0u;
+    const uint2 e = *reinterpret_cast<const uint2*>(bins + off);   // {base code, boundary in the slot}
+    return e.x + (acc > __builtin_bit_cast(float, e.y) ? 1u : 0u);
+}
 
 template <int B>
 __device__ __forceinline__ void dense_tables_to_lds(const DenseDev& P, uint32_t* ctab, float* thr) {
@@ -246,13 +275,14 @@ __global__ __launch_bounds__(WAVES * 64) void tq_quant_kernel(DenseDev P, const 
                                                               uint16_t* __restrict__ rnorms, char* __restrict__ y,
                                                               int64_t ldy_bytes) {
     constexpr int W = (128 * B + 31) / 32;
-    constexpr int L = 1 << B;
-    __shared__ DenseLds<WAVES, QJL> sm;
+    __shared__ DenseLds<WAVES> sm;
     dense_tables_to_lds<B>(P, sm.ctab, sm.thr);
+    dense_bins_to_lds(P, sm.bins);
     mat_to_lds<WAVES * 64>(P.pi_hi, sm.pih);
     mat_to_lds<WAVES * 64>(P.pi_lo, sm.pil);
-    if constexpr (QJL) mat_to_lds<WAVES * 64>(P.s_rows, sm.s_rows);
     __syncthreads();
+    const float ba = P.bin_a * kRotScale, bb = P.bin_b;
+    const char* binc = reinterpret_cast<const char*>(sm.bins);
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     u32x4* tile = sm.tiles[wave];
@@ -263,26 +293,19 @@ __global__ __launch_bounds__(WAVES * 64) void tq_quant_kernel(DenseDev P, const 
         const int64_t base = t * 64;
         const int z = opaque_zero();
         const int l = lane_id() + z;
-        float thr[L - 1];
-#pragma unroll
-        for (int k = 0; k < L - 1; ++k) thr[k] = uniform(sm.thr[k + z]);
 
-        // load, norm (same arithmetic as the rotor path)
-        uint32_t xin[64];
-        {
-            if constexpr (IN_F16) {
-                tile_load(x, ldx_bytes, base, n, 0, tile, l);
-                wave_lds_sync();
-#pragma unroll
-                for (int c = 0; c < 16; ++c) {
-                    const u32x4 q = tile[swz(l, c)];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) xin[4 * c + e] = q[e];
-                }
-            } else {
-                // fp32: keep the values as floats in a 128-entry view
-            }
+        // load, norm (same arithmetic as the rotor path).  fp16 input stays in
+        // the wave's LDS tile until the residual step (nothing writes the tile
+        // before the record is staged) and is read from there where it is
+        // used, so no input registers are held across the rotations.
+        if constexpr (IN_F16) {
+            tile_load(x, ldx_bytes, base, n, 0, tile, l);
+            wave_lds_sync();
         }
+        auto xword = [&](int k) -> uint32_t {
+            const u32x4 q = tile[swz(l, k >> 2)];
+            return q[k & 3];
+        };
         float xf32[IN_F16 ? 1 : 128];
         if constexpr (!IN_F16) {
 #pragma unroll
@@ -302,7 +325,7 @@ __global__ __launch_bounds__(WAVES * 64) void tq_quant_kernel(DenseDev P, const 
         }
         auto xget = [&](int i) -> float {
             if constexpr (IN_F16) {
-                const uint32_t w = xin[i >> 1];
+                const uint32_t w = xword(i >> 1);
                 return h2f((i & 1) ? (w >> 16) : (w & 0xFFFFu));
             } else {
                 return xf32[i];
@@ -314,10 +337,7 @@ __global__ __launch_bounds__(WAVES * 64) void tq_quant_kernel(DenseDev P, const 
             const float v = xget(i);
             ss = __builtin_fmaf(v, v, ss);
         }
-        if constexpr (IN_F16) {
-#pragma unroll
-            for (int k = 0; k < 64; ++k) pin(xin[k]);
-        }
+
         const float nrm = __builtin_sqrtf(ss);
         const float inv = nrm > 0.0f ? 1.0f / nrm : 0.0f;
         const uint32_t nh = f2h(nrm);
@@ -351,8 +371,8 @@ __global__ __launch_bounds__(WAVES * 64) void tq_quant_kernel(DenseDev P, const 
                 from_accumulators(ay0[mt], ay1[mt], y0, y1);
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    put_code<B, W>(cw, 32 * mt + own_row(0, r), quant_code<B>(y0[r] * kRotScale, thr));
-                    put_code<B, W>(cw, 32 * mt + own_row(1, r), quant_code<B>(y1[r] * kRotScale, thr));
+                    put_code<B, W>(cw, 32 * mt + own_row(0, r), dense_code(y0[r], ba, bb, binc));
+                    put_code<B, W>(cw, 32 * mt + own_row(1, r), dense_code(y1[r], ba, bb, binc));
                 }
             }
         } else {
@@ -375,8 +395,8 @@ __global__ __launch_bounds__(WAVES * 64) void tq_quant_kernel(DenseDev P, const 
                     [&](int row, int chunk) { return mat_frag(sm.pil, row, chunk); }, l, y0, y1);
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    put_code<B, W>(cw, own_coord(MT, 0, r), quant_code<B>(y0[r] * kRotScale, thr));
-                    put_code<B, W>(cw, own_coord(MT, 1, r), quant_code<B>(y1[r] * kRotScale, thr));
+                    put_code<B, W>(cw, own_coord(MT, 0, r), dense_code(y0[r], ba, bb, binc));
+                    put_code<B, W>(cw, own_coord(MT, 1, r), dense_code(y1[r], ba, bb, binc));
                 }
             };
             tile_q(std::integral_constant<int, 0>{});
@@ -388,66 +408,70 @@ __global__ __launch_bounds__(WAVES * 64) void tq_quant_kernel(DenseDev P, const 
         uint32_t sw[4] = {0u, 0u, 0u, 0u};
         uint32_t gh = 0u;
         float ghat = 0.0f;
-        // with QJL, Pi^T y^ of the residual step is kept for the roundtrip's
-        // output (the values rq_dequantize forms from the record)
-        f32x16 ax0[QJL ? 4 : 1], ax1[QJL ? 4 : 1];
         if constexpr (QJL) {
-            // x~_u = Pi^T y^, r = x_u - x~_u (original domain), signs of S r
-            uint32_t rh[64], rl[64];
+            // x~_u = Pi^T y^ (all four M tiles, K blocks outermost); then each
+            // tile gives the residual r = x_u - x~_u of its two K blocks
+            // (original domain), whose S r MFMAs run at once for all four
+            // output tiles (the K order of every z accumulator stays 0..7)
+            f32x16 ax0[4], ax1[4];
+            dense_pit_tiles<B>(P, sm.ctab, cw, l, ax0, ax1);
+            f32x16 za[4][2];
+#pragma unroll
+            for (int mz = 0; mz < 4; ++mz) za[mz][0] = za[mz][1] = f32x16{};
             float gam2 = 0.0f;
-            {
-                // x~_u = Pi^T y^ (all four M tiles), then the residual tile by tile
-                dense_pit_tiles<B>(P, sm.ctab, cw, l, ax0, ax1);
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
-                    float x0[16], x1[16];
-                    from_accumulators(ax0[mt], ax1[mt], x0, x1);
+            for (int mt = 0; mt < 4; ++mt) {
+                float x0[16], x1[16];
+                from_accumulators(ax0[mt], ax1[mt], x0, x1);
 #pragma unroll
-                    for (int il = 0; il < 32; ++il) {
+                for (int kk = 0; kk < 2; ++kk) {
+                    const int kb = 2 * mt + kk;
+                    uint32_t rh[8], rl[8];
+#pragma unroll
+                    for (int il = 16 * kk; il < 16 * kk + 16; ++il) {
                         const int b8 = il >> 3, w = il & 7, i = 32 * mt + il;
                         const float xt = (w < 4 ? x0[4 * b8 + w] : x1[4 * b8 + w - 4]) * kRotScale;
                         const float r = xget(i) * inv - xt;
                         gam2 = __builtin_fmaf(r, r, gam2);
                         uint32_t hi, lo;
                         split_h(r * kDenseResidualScale, &hi, &lo);
-                        put_pair(rh, i, hi);
-                        put_pair(rl, i, lo);
+                        const int d = (il & 15) >> 1;
+                        if (il & 1) {
+                            rh[d] |= hi << 16;
+                            rl[d] |= lo << 16;
+                        } else {
+                            rh[d] = hi;
+                            rl[d] = lo;
+                        }
+                    }
+                    u32x4 h0, h1, l0, l1;
+                    to_operands(u32x4{rh[0], rh[1], rh[2], rh[3]}, u32x4{rh[4], rh[5], rh[6], rh[7]}, &h0, &h1);
+                    to_operands(u32x4{rl[0], rl[1], rl[2], rl[3]}, u32x4{rl[4], rl[5], rl[6], rl[7]}, &l0, &l1);
+#pragma unroll
+                    for (int mz = 0; mz < 4; ++mz) {
+                        const u32x4 a = gmat_frag(P.s_rows, 32 * mz + (l & 31), 2 * kb + (l >> 5));
+                        za[mz][0] = mfma(a, h0, za[mz][0]);
+                        za[mz][0] = mfma(a, l0, za[mz][0]);
+                        za[mz][1] = mfma(a, h1, za[mz][1]);
+                        za[mz][1] = mfma(a, l1, za[mz][1]);
                     }
                 }
             }
             const float gam = __builtin_sqrtf(gam2);
             gh = f2h(gam);
             ghat = h2f(gh);
-            auto zt = [&](auto mt_c) {
-                constexpr int MT = decltype(mt_c)::value;
-                f32x16 a0 = {}, a1 = {};
 #pragma unroll
-                for (int kb = 0; kb < 8; ++kb) {
-                    const u32x4 a = mat_frag(sm.s_rows, 32 * MT + (l & 31), 2 * kb + (l >> 5));
-                    u32x4 h0, h1, l0, l1;
-                    to_operands(u32x4{rh[8 * kb], rh[8 * kb + 1], rh[8 * kb + 2], rh[8 * kb + 3]},
-                                u32x4{rh[8 * kb + 4], rh[8 * kb + 5], rh[8 * kb + 6], rh[8 * kb + 7]}, &h0, &h1);
-                    to_operands(u32x4{rl[8 * kb], rl[8 * kb + 1], rl[8 * kb + 2], rl[8 * kb + 3]},
-                                u32x4{rl[8 * kb + 4], rl[8 * kb + 5], rl[8 * kb + 6], rl[8 * kb + 7]}, &l0, &l1);
-                    a0 = mfma(a, h0, a0);
-                    a0 = mfma(a, l0, a0);
-                    a1 = mfma(a, h1, a1);
-                    a1 = mfma(a, l1, a1);
-                }
+            for (int mz = 0; mz < 4; ++mz) {
                 float z0[16], z1[16];
-                from_accumulators(a0, a1, z0, z1);
+                from_accumulators(za[mz][0], za[mz][1], z0, z1);
                 uint32_t word = 0u;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     word |= (z0[r] >= 0.0f ? 1u : 0u) << own_row(0, r);
                     word |= (z1[r] >= 0.0f ? 1u : 0u) << own_row(1, r);
                 }
-                sw[MT] = word;
-            };
-            zt(std::integral_constant<int, 0>{});
-            zt(std::integral_constant<int, 1>{});
-            zt(std::integral_constant<int, 2>{});
-            zt(std::integral_constant<int, 3>{});
+                sw[mz] = word;
+            }
         }
 
         if (base + l < n) norms[base + l] = static_cast<uint16_t>(nh);
@@ -466,8 +490,24 @@ __global__ __launch_bounds__(WAVES * 64) void tq_quant_kernel(DenseDev P, const 
                     if (single) out.store_cols(y, ldy_bytes, base, n, 4 * mt);
                 }
             };
-            if constexpr (QJL) dense_finish_vec<QJL>(P, ax0, ax1, nhat, ghat, sw, scol, out, l, done);
-            else dense_dequant_vec<B, QJL>(P, sm.ctab, cw, nhat, ghat, sw, scol, out, l, done);
+            // the output is what tq_dequantize forms from the record (Pi^T y^
+            // again: the residual step's accumulators are not kept).  The
+            // codes and the Pi^T pointers pass through opaque copies so that
+            // the compiler does not reuse the residual step's table addresses
+            // and fragment loads (holding them live until here); nothing is
+            // scheduled across either.
+            __builtin_amdgcn_sched_barrier(0);
+            DenseDev P2 = P;
+            const int oz = opaque_zero();
+            P2.pit_hi += oz;
+            P2.pit_lo += oz;
+            uint32_t cw2[W];
+#pragma unroll
+            for (int k = 0; k < W; ++k) {
+                cw2[k] = cw[k];
+                pin(cw2[k]);
+            }
+            dense_dequant_vec<B, QJL>(P2, sm.ctab, cw2, nhat, ghat, sw, scol, out, l, done);
             if (!OUT_F16 || !single) out.store(y, ldy_bytes, base, n);
         }
     }
@@ -522,7 +562,7 @@ template <int B, bool QJL>
 hipError_t launch_tq_quant(const DenseDev& P, const void* x, bool in_f16, int64_t ldx_bytes, int64_t n,
                            uint32_t* codes, uint16_t* norms, uint32_t* signs, uint16_t* rnorms, void* y, bool out_f16,
                            int64_t ldy_bytes, bool roundtrip, hipStream_t s) {
-    constexpr int WAVES = QJL ? 2 : 4;
+    constexpr int WAVES = 4;
     const int64_t ntiles = (n + 63) / 64;
     const int64_t blocks = (ntiles + WAVES - 1) / WAVES;
     const int grid = static_cast<int>(blocks < 256 * 4 ? (blocks > 0 ? blocks : 1) : 256 * 4);

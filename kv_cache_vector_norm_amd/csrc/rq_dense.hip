@@ -12,6 +12,8 @@ struct DenseDev {
     const float* __restrict__ cent;
     const uint16_t* __restrict__ s_rows;
     const uint16_t* __restrict__ s_cols;
+    const u32x4_t* __restrict__ bins;
+    float bin_a, bin_b;
     float qjl_scale;
 };
 
@@ -34,6 +36,9 @@ static DenseDev make_dense(const DenseTables& t) {
     P.cent = t.cent;
     P.s_rows = t.s_rows;
     P.s_cols = t.s_cols;
+    P.bins = t.bins;
+    P.bin_a = t.bin_a;
+    P.bin_b = t.bin_b;
     P.qjl_scale = t.qjl_scale;
     return P;
 }

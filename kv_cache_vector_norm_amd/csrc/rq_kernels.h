@@ -46,6 +46,8 @@ struct DenseTables {
     const float* cent;
     const uint16_t* s_rows;
     const uint16_t* s_cols;
+    const u32x4_t* bins;     // the slot table of the rotor sessions (same codebook)
+    float bin_a, bin_b;
     float qjl_scale;
     int mse_bits;
     bool qjl;

@@ -198,7 +198,8 @@ def _edge_and_boundary_probes(boundaries, bias, ulps):
     return v[np.abs(v) <= np.float32(1.001)]
 
 
-@pytest.mark.parametrize("bits,mode", [(b, OP.MSE) for b in (1, 2, 3, 4)] + [(b, OP.QJL) for b in (2, 3, 4, 5)])
+@pytest.mark.parametrize("bits,mode", [(b, OP.MSE) for b in (1, 2, 3, 4)] + [(b, OP.QJL) for b in (2, 3, 4, 5)]
+                         + [(b, OP.DENSE) for b in (1, 2, 3, 4)] + [(b, OP.DENSE | OP.QJL) for b in (2, 3, 4, 5)])
 def test_slot_table_is_exact_nearest_centroid(K, bits, mode):
     """The kernels' 256-slot lookup gives #{k : y > t_k} and c[code] for every
     fp32 y in [-1.001, 1.001]: random draws, both sides of every boundary and
