@@ -745,10 +745,24 @@ def workload_extras(K, W, dev, stream):
             cache.attend(seq, layer, qd, k_cur=kcur, v_cur=kcur, out=att, workspace=ws)
             cache.append(seq, layer, kn, kn)
     dec_us = _timed(stream, step, 5)
+    # the same step over all layers in two calls (attend, then append)
+    ql = qd.unsqueeze(0).expand(L, HQ, 128).contiguous()
+    kl = kcur.unsqueeze(0).expand(L, H, 128).contiguous()
+    knl = kn.unsqueeze(0).expand(L, H, 1, 128).contiguous()
+    needl = K.lib().rq_cache_attend_layers_workspace(cache.h, L, HQ, T + 64)
+    wsl = torch.empty(needl + 256, dtype=torch.uint8, device=dev)
+    attl = torch.empty((L * HQ, 128), dtype=torch.float32, device=dev)
+
+    def step_layers(i):
+        cache.attend_layers(seq, 0, ql, k_cur=kl, v_cur=kl, out=attl, workspace=wsl)
+        cache.append_layers(seq, 0, knl, knl)
+    decl_us = _timed(stream, step_layers, 5)
     out["qwen2.5-3b_paged_cache"] = {"prefill_tokens": T, "prefill_quantize_us": round(prefill_us, 1),
-                                     "decode_step_us": round(dec_us, 1), "layers": L, "page_tokens": 256}
+                                     "decode_step_us": round(decl_us, 1), "decode_calls": 2,
+                                     "decode_step_per_layer_calls_us": round(dec_us, 1), "layers": L,
+                                     "page_tokens": 256}
     cache.close(seq)
-    del cache, kvl, ws, att
+    del cache, kvl, ws, att, wsl, attl
 
     for spec in (W.QWEN25_3B, W.LLAMA31_8B):
         L, H, T, HQ = spec["layers"], spec["kv_heads"], spec["tokens"], spec["q_heads"]

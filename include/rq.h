@@ -364,6 +364,24 @@ int rq_cache_attend(rq_cache* cache, int seq, int layer, const float* q, int hq,
                     const float* k_cur, const float* v_cur, void* workspace,
                     int64_t workspace_bytes, float* out, int64_t ld_out, void* stream);
 
+/* A decode step over a range of layers in one call each (README "Post-Prefill
+ * Quantization": every decode step appends the new token's key and value to
+ * every layer's compressed cache and attends with the current token at full
+ * precision).  Layers layer0 .. layer0 + nlayers - 1 must hold the same
+ * number of cached tokens.  Layouts: k, v [nlayers][kv_heads][n][ld];
+ * q [nlayers][hq][128] fp32; k_cur, v_cur [nlayers][kv_heads][128] fp32;
+ * out [nlayers * hq][ld_out], row l * hq + h for query head h of layer
+ * layer0 + l.  The results equal, bit for bit, those of the per-layer calls
+ * (rq_cache_append per layer; rq_cache_attend per layer, whose key slices
+ * the layered call reproduces); nlayers * hq <= RQ_ATTEND_MAX_ROWS.
+ * Same errors as the per-layer calls. */
+int rq_cache_append_layers(rq_cache* cache, int seq, int layer0, int nlayers, const void* k, const void* v,
+                           int dtype, int64_t n, int64_t ld, void* stream);
+int64_t rq_cache_attend_layers_workspace(const rq_cache* cache, int nlayers, int hq, int64_t t);
+int rq_cache_attend_layers(rq_cache* cache, int seq, int layer0, int nlayers, const float* q, int hq, float scale,
+                           const float* k_cur, const float* v_cur, void* workspace, int64_t workspace_bytes,
+                           float* out, int64_t ld_out, void* stream);
+
 /* TurboQuant comparison path (hyper.ai Algorithms 1 and 2; README "How
  * TurboQuant Works"): y = Pi x_u, per-coordinate Lloyd-Max codes on 128
  * coordinates, x~ = Pi^T y^ (+ the QJL stage with RQ_QJL).  Same arguments

@@ -32,7 +32,8 @@ EXPORTS = ("rq_layout", "rq_host_params", "rq_host_quantizer", "rq_init", "rq_fr
            "rq_attend_noalloc",
            "tq_quantize", "tq_dequantize", "tq_roundtrip", "rq_cache_create", "rq_cache_free", "rq_cache_open",
            "rq_cache_close", "rq_cache_length", "rq_cache_free_pages", "rq_cache_append", "rq_cache_read",
-           "rq_cache_attend_workspace", "rq_cache_attend", "pq_quantize", "pq_dequantize", "pq_roundtrip", "pq_score",
+           "rq_cache_attend_workspace", "rq_cache_attend",
+           "rq_cache_append_layers", "rq_cache_attend_layers_workspace", "rq_cache_attend_layers", "pq_quantize", "pq_dequantize", "pq_roundtrip", "pq_score",
            "rq_outlier_channels", "rq_quantize_outliers", "rq_dequantize_outliers", "rq_score_outliers",
            "rq_bench_copy", "rq_last_error", "rq_version")
 
@@ -101,6 +102,9 @@ def _load():
         "rq_cache_read": ([P, I, I, I, P, P, P, P, P], I),
         "rq_cache_attend_workspace": ([P, I, I64], I64),
         "rq_cache_attend": ([P, I, I, P, I, ctypes.c_float, P, P, P, I64, P, I64, P], I),
+        "rq_cache_append_layers": ([P, I, I, I, P, P, I, I64, I64, P], I),
+        "rq_cache_attend_layers_workspace": ([P, I, I, I64], I64),
+        "rq_cache_attend_layers": ([P, I, I, I, P, I, ctypes.c_float, P, P, P, I64, P, I64, P], I),
         "tq_quantize": ([P, P, I, I64, I64, P, P, P, P, P], I),
         "tq_dequantize": ([P, P, P, P, P, I64, P, I, I64, P], I),
         "tq_roundtrip": ([P, P, I, I64, I64, P, P, P, P, P, I, I64, P], I),
@@ -614,6 +618,35 @@ class Cache:
         _check(_lib.rq_cache_read(self.h, seq, layer, which, _ptr(rec.codes), _ptr(rec.norms), _ptr(rec.signs),
                                   _ptr(rec.rnorms), _stream(stream)))
         return rec
+
+    def append_layers(self, seq, layer0, k, v, stream=None):
+        """k, v: [nlayers, kv_heads, n, 128] fp16 or fp32 (rows of pitch stride(2)) for
+        layers layer0 .. layer0 + nlayers - 1, in one call."""
+        dt = self.kc._dt(k)
+        _check(_lib.rq_cache_append_layers(self.h, seq, layer0, k.shape[0], _ptr(k), _ptr(v), dt, k.shape[2],
+                                           k.stride(2), _stream(stream)))
+
+    def attend_layers(self, seq, layer0, q, scale=None, k_cur=None, v_cur=None, out=None, workspace=None,
+                      stream=None):
+        """q: [nlayers, hq, 128] fp32; k_cur, v_cur: [nlayers, kv_heads, 128] fp32.
+        Returns [nlayers * hq, 128] fp32."""
+        import torch
+        nl, hq = q.shape[0], q.shape[1]
+        scale = 1.0 / math.sqrt(128) if scale is None else scale
+        t = self.length(seq, layer0)
+        need = _lib.rq_cache_attend_layers_workspace(self.h, nl, hq, t)
+        if need < 0:
+            raise RQError(RQ_EINVAL, "rq_cache_attend_layers_workspace: invalid sizes")
+        if workspace is None:
+            workspace = torch.empty(need + 256, dtype=torch.uint8, device=q.device)
+        base = workspace.data_ptr()
+        ws = base + ((-base) % 256)
+        if out is None:
+            out = torch.empty((nl * hq, 128), dtype=torch.float32, device=q.device)
+        _check(_lib.rq_cache_attend_layers(self.h, seq, layer0, nl, _ptr(q), hq, float(scale), _ptr(k_cur),
+                                           _ptr(v_cur), ws, workspace.numel() - (ws - base), _ptr(out),
+                                           out.stride(0), _stream(stream)))
+        return out
 
     def attend(self, seq, layer, q, scale=None, k_cur=None, v_cur=None, out=None, workspace=None, stream=None):
         import torch

@@ -974,25 +974,30 @@ int64_t rq_cache_length(const rq_cache* c, int seq, int layer) {
 
 int64_t rq_cache_free_pages(const rq_cache* c) { return c ? static_cast<int64_t>(c->free_pages.size()) : -1; }
 
+// Quantises n new rows of each of `heads` (layer, KV head) blocks of x
+// ([heads][n][ld]) and scatters them to key positions t0.. of those blocks'
+// pages; block j's page list starts at pt.pages + j * pt.stride (the page
+// tables of consecutive layers follow each other).
 static int cache_quantize_into_pages(rq_cache* c, const rq_ctx* ctx, const rq_cache::Pool& stage,
                                      const rq_cache::Pool& pool, const rqk::PageTable& pt, const void* x, int dtype,
-                                     int64_t n, int64_t ld, int64_t t0, hipStream_t s, const char* fn) {
+                                     int64_t n, int64_t ld, int64_t t0, hipStream_t s, const char* fn, int heads = 0) {
+    if (heads <= 0) heads = c->kv_heads;
     const rqh::Layout& l = ctx->host.lay;
     const bool dense = l.mode & RQ_DENSE;
     const bool qjl = l.mode & RQ_QJL;
     const char* xb = static_cast<const char*>(x);
     const int64_t es = static_cast<int64_t>(elem_size(dtype));
     int rc;
-    if (n <= c->stage) {
-        // every head's n rows in one launch: rows j * n + i, pitch ld
-        if ((rc = quantize_impl(const_cast<rq_ctx*>(ctx), dense, x, dtype, n * c->kv_heads, ld, stage.codes, stage.norms,
+    if (n * heads <= c->stage * c->kv_heads) {
+        // every block's n rows in one launch: rows j * n + i, pitch ld
+        if ((rc = quantize_impl(const_cast<rq_ctx*>(ctx), dense, x, dtype, n * heads, ld, stage.codes, stage.norms,
                                 stage.signs, stage.rnorms, nullptr, RQ_F32, 0, false, s, fn)))
             return rc;
         return finish(rqk::scatter_rows(stage.codes, stage.norms, stage.signs, stage.rnorms, pool.codes, pool.norms,
-                                        pool.signs, pool.rnorms, l.code_words, qjl, n, t0, c->kv_heads, pt, false, s),
+                                        pool.signs, pool.rnorms, l.code_words, qjl, n, t0, heads, pt, false, s),
                       fn);
     }
-    for (int j = 0; j < c->kv_heads; ++j) {
+    for (int j = 0; j < heads; ++j) {
         rqk::PageTable hp = pt;
         hp.pages = pt.pages + static_cast<int64_t>(j) * pt.stride;
         for (int64_t c0 = 0; c0 < n; c0 += c->stage) {
@@ -1082,6 +1087,87 @@ int rq_cache_attend(rq_cache* c, int seq, int layer, const float* q, int hq, flo
                                c->vp.norms, c->vp.signs, c->vp.rnorms, t, 0, scale, workspace, out, ld_out, s, pt, pt);
     if (e == hipSuccess && k_cur)
         e = rqk::merge_current(q, hq, group, k_cur, v_cur,
+                               reinterpret_cast<const float2*>(static_cast<char*>(workspace) + plan.off_stats), scale,
+                               out, ld_out, s);
+    return finish(e, fn);
+}
+
+// ------------------------------------------- all layers of a decode step --
+static int check_layers(const rq_cache* c, int seq, int layer0, int nlayers, int64_t* len, const char* fn) {
+    int rc;
+    if ((rc = check_seq(c, seq, 0, fn))) return rc;
+    if (nlayers < 1 || layer0 < 0 || layer0 + nlayers > c->layers)
+        return fail(RQ_EINVAL, std::string(fn) + ": layers [layer0, layer0 + nlayers) out of range");
+    const rq_cache::Seq& q = c->seqs[static_cast<size_t>(seq)];
+    const int64_t t = q.len[static_cast<size_t>(layer0)];
+    for (int l = layer0 + 1; l < layer0 + nlayers; ++l)
+        if (q.len[static_cast<size_t>(l)] != t)
+            return fail(RQ_EINVAL, std::string(fn) + ": the layers hold different numbers of cached tokens");
+    *len = t;
+    return RQ_OK;
+}
+
+int rq_cache_append_layers(rq_cache* c, int seq, int layer0, int nlayers, const void* k, const void* v, int dtype,
+                           int64_t n, int64_t ld, void* stream) {
+    const char* fn = "rq_cache_append_layers";
+    int rc;
+    int64_t t0 = 0;
+    if ((rc = check_layers(c, seq, layer0, nlayers, &t0, fn))) return rc;
+    if (n < 0) return fail(RQ_EINVAL, "rq_cache_append_layers: n < 0");
+    if ((rc = check_vectors(k, dtype, ld, "k", fn))) return rc;
+    if ((rc = check_vectors(v, dtype, ld, "v", fn))) return rc;
+    rq_cache::Seq& q = c->seqs[static_cast<size_t>(seq)];
+    if (t0 + n > q.cap) return fail(RQ_EINVAL, "rq_cache_append_layers: the sequence's reserved tokens are exhausted");
+    if (n == 0) return RQ_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const rqk::PageTable pt = page_table(c, q, layer0);
+    const int heads = nlayers * c->kv_heads;
+    if ((rc = cache_quantize_into_pages(c, c->k, c->ks, c->kp, pt, k, dtype, n, ld, t0, s, fn, heads))) return rc;
+    if ((rc = cache_quantize_into_pages(c, c->v, c->vs, c->vp, pt, v, dtype, n, ld, t0, s, fn, heads))) return rc;
+    for (int l = layer0; l < layer0 + nlayers; ++l) q.len[static_cast<size_t>(l)] += n;
+    return RQ_OK;
+}
+
+int64_t rq_cache_attend_layers_workspace(const rq_cache* c, int nlayers, int hq, int64_t t) {
+    if (!c || nlayers < 1 || hq < 1 || hq % c->kv_heads || t < 0 || t > RQ_ATTEND_MAX_KEYS) return -1;
+    if (static_cast<int64_t>(nlayers) * hq > RQ_ATTEND_MAX_ROWS) return -1;
+    return t == 0 ? 0 : rqk::attend_plan(nlayers * hq, hq / c->kv_heads, t, hq).bytes;
+}
+
+int rq_cache_attend_layers(rq_cache* c, int seq, int layer0, int nlayers, const float* q, int hq, float scale,
+                           const float* k_cur, const float* v_cur, void* workspace, int64_t workspace_bytes,
+                           float* out, int64_t ld_out, void* stream) {
+    const char* fn = "rq_cache_attend_layers";
+    int rc;
+    int64_t t = 0;
+    if ((rc = check_layers(c, seq, layer0, nlayers, &t, fn))) return rc;
+    if (!q || !aligned(q, 16)) return fail(RQ_EINVAL, "rq_cache_attend_layers: q must be a 16-byte aligned device pointer");
+    if (hq < 1 || hq % c->kv_heads || static_cast<int64_t>(nlayers) * hq > RQ_ATTEND_MAX_ROWS)
+        return fail(RQ_EINVAL, "rq_cache_attend_layers: hq must be a positive multiple of kv_heads and nlayers * hq <= RQ_ATTEND_MAX_ROWS");
+    if ((k_cur == nullptr) != (v_cur == nullptr)) return fail(RQ_EINVAL, "rq_cache_attend_layers: give both or neither of k_cur, v_cur");
+    if (k_cur && (!aligned(k_cur, 4) || !aligned(v_cur, 4))) return fail(RQ_EINVAL, "rq_cache_attend_layers: misaligned k_cur / v_cur");
+    if (!(scale == scale) || scale > 3.0e38f || scale < -3.0e38f) return fail(RQ_EINVAL, "rq_cache_attend_layers: scale is not finite");
+    if (!out || !aligned(out, 4) || ld_out < rqh::kDim) return fail(RQ_EINVAL, "rq_cache_attend_layers: bad out / ld_out");
+    const rq_cache::Seq& sq = c->seqs[static_cast<size_t>(seq)];
+    const int group = hq / c->kv_heads;
+    const int rows = nlayers * hq;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (t == 0) {
+        if (!k_cur) return fail(RQ_EINVAL, "rq_cache_attend_layers: no cached tokens and no current token");
+        return finish(rqk::merge_current(q, rows, group, k_cur, v_cur, nullptr, scale, out, ld_out, s), fn);
+    }
+    const rqk::AttendPlan plan = rqk::attend_plan(rows, group, t, hq);
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < plan.bytes)
+        return fail(RQ_EINVAL, "rq_cache_attend_layers: workspace missing, misaligned or smaller than rq_cache_attend_layers_workspace()");
+    // the layers' page tables follow each other: query row l * hq + h reads
+    // KV head l * kv_heads + h / group, whose pages start at that head's row
+    const rqk::PageTable pt = page_table(c, sq, layer0);
+    const rqk::ScoreTables kt = score_tables(c->k), vt = score_tables(c->v);
+    hipError_t e = rqk::attend(kt, vt, q, rows, group, c->kp.codes, c->kp.norms, c->kp.signs, c->kp.rnorms, c->vp.codes,
+                               c->vp.norms, c->vp.signs, c->vp.rnorms, t, 0, scale, workspace, out, ld_out, s, pt, pt,
+                               hq);
+    if (e == hipSuccess && k_cur)
+        e = rqk::merge_current(q, rows, group, k_cur, v_cur,
                                reinterpret_cast<const float2*>(static_cast<char*>(workspace) + plan.off_stats), scale,
                                out, ld_out, s);
     return finish(e, fn);

@@ -481,10 +481,10 @@ __global__ __launch_bounds__(320) void attend_combine_kernel(CombineArgs a) {
 }
 
 // ----------------------------------------------------------- launchers --
-AttendPlan attend_plan(int hq, int group, int64_t t) {
+AttendPlan attend_plan(int hq, int group, int64_t t, int plan_rows) {
     AttendPlan p;
     p.ld = (t + 3) & ~int64_t(3);
-    const int kv_heads = hq / group;
+    const int kv_heads = (plan_rows > 0 ? plan_rows : hq) / group;
     const int qblocks = (group + 31) / 32;
     const int64_t ntiles = (t + 63) / 64;
     const int64_t want = (ntiles + 3) / 4;
@@ -528,8 +528,8 @@ hipError_t attend(const ScoreTables& kt, const ScoreTables& vt, const float* q, 
                   const uint32_t* kcodes, const uint16_t* knorms, const uint32_t* ksigns, const uint16_t* krnorms,
                   const uint32_t* vcodes, const uint16_t* vnorms, const uint32_t* vsigns, const uint16_t* vrnorms,
                   int64_t t, int64_t kv_stride, float scale, void* workspace, float* out, int64_t ld_out,
-                  hipStream_t s, const PageTable& kpt, const PageTable& vpt) {
-    const AttendPlan p = attend_plan(hq, group, t);
+                  hipStream_t s, const PageTable& kpt, const PageTable& vpt, int plan_rows) {
+    const AttendPlan p = attend_plan(hq, group, t, plan_rows);
     char* ws = static_cast<char*>(workspace);
     float* scores = reinterpret_cast<float*>(ws + p.off_scores);
     float2* stats = reinterpret_cast<float2*>(ws + p.off_stats);

@@ -164,13 +164,18 @@ struct AttendPlan {
     int64_t producers;               // partial rows per query row (one per key-slice block)
     int64_t off_scores, off_stats, off_part, bytes;
 };
-AttendPlan attend_plan(int hq, int group, int64_t t);
+// plan_rows: the query rows whose KV heads size the key slices (default
+// hq).  A call over several layers of a paged cache passes one layer's rows,
+// so that every (KV head, row block) is cut into the same slices, and summed
+// in the same order, as in a one-layer call.
+AttendPlan attend_plan(int hq, int group, int64_t t, int plan_rows = 0);
 
 hipError_t attend(const ScoreTables& kt, const ScoreTables& vt, const float* q, int hq, int group,
                   const uint32_t* kcodes, const uint16_t* knorms, const uint32_t* ksigns, const uint16_t* krnorms,
                   const uint32_t* vcodes, const uint16_t* vnorms, const uint32_t* vsigns, const uint16_t* vrnorms,
                   int64_t t, int64_t kv_stride, float scale, void* workspace, float* out, int64_t ld_out,
-                  hipStream_t s, const PageTable& kpt = PageTable{}, const PageTable& vpt = PageTable{});
+                  hipStream_t s, const PageTable& kpt = PageTable{}, const PageTable& vpt = PageTable{},
+                  int plan_rows = 0);
 
 // rq_attend_noalloc: a fixed device array per GPU (rq_attend.hip) serves as
 // the workspace.  noalloc_scratch resolves its address on the current device

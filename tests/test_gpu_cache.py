@@ -158,3 +158,71 @@ def test_cache_rejects_bad_use(K):
     kk, vv = _kv(2, 65, 69)
     with pytest.raises(K.RQError):
         cache.append(seq, 0, kk.contiguous(), vv.contiguous())            # 65 > 64 reserved
+
+
+@pytest.mark.parametrize("layers,l0,nl,kv_heads,group,t0,steps,kspec,vspec,stage,cur", [
+    (4, 1, 3, 2, 8, 130, 3, (3, OP.QJL), (3, OP.MSE), 65536, True),
+    (36, 0, 36, 2, 8, 600, 2, (3, OP.QJL), (3, OP.MSE), 65536, True),     # Qwen2.5-3B-shaped step
+    (3, 0, 3, 4, 2, 300, 2, (1, OP.QJL), (4, OP.MSE), 65536, False),
+    (2, 0, 2, 2, 4, 200, 1, (4, OP.DENSE | OP.QJL), (3, OP.DENSE), 128, True),   # chunked staging
+])
+def test_all_layers_calls_equal_per_layer_calls(K, layers, l0, nl, kv_heads, group, t0, steps, kspec, vspec, stage,
+                                                cur):
+    """rq_cache_append_layers / rq_cache_attend_layers over layers l0 .. l0+nl-1
+    give the same records and the same attention, bit for bit, as one
+    rq_cache_append / rq_cache_attend per layer on a twin cache."""
+    kc = K.Codec(bits=kspec[0], seed=0, mode=kspec[1])
+    vc = K.Codec(bits=vspec[0], seed=0, mode=vspec[1])
+    mk = lambda: K.Cache(kc, vc, layers=layers, kv_heads=kv_heads, page_tokens=64, max_pages=4096,
+                         stage_tokens=stage)
+    a, b = mk(), mk()
+    t = t0 + steps
+    sa, sb = a.open(t + 64), b.open(t + 64)
+    kk = torch.stack([_kv(kv_heads, t, 80 + l)[0] for l in range(nl)])
+    vv = torch.stack([_kv(kv_heads, t, 80 + l)[1] for l in range(nl)])
+    hq = kv_heads * group
+    scale = 1 / np.sqrt(D)
+    chunks = [(0, t0)] + [(i, i + 1) for i in range(t0, t)]
+    for step, (i0, i1) in enumerate(chunks):
+        a.append_layers(sa, l0, kk[:, :, i0:i1].contiguous(), vv[:, :, i0:i1].contiguous())
+        for l in range(nl):
+            b.append(sb, l0 + l, kk[l, :, i0:i1].contiguous(), vv[l, :, i0:i1].contiguous())
+        q = torch.from_numpy(W.queries(nl * hq, seed=90 + step)).cuda().reshape(nl, hq, D)
+        kcur = vcur = None
+        if cur:
+            kcur = torch.from_numpy(W.gaussian(nl * kv_heads, seed=91 + step, dtype=np.float32)).cuda()
+            vcur = torch.from_numpy(W.gaussian(nl * kv_heads, seed=92 + step, dtype=np.float32)).cuda()
+            kcur, vcur = kcur.reshape(nl, kv_heads, D), vcur.reshape(nl, kv_heads, D)
+        got = a.attend_layers(sa, l0, q, scale, k_cur=kcur, v_cur=vcur)
+        ref = torch.cat([b.attend(sb, l0 + l, q[l].contiguous(), scale,
+                                  k_cur=None if kcur is None else kcur[l].contiguous(),
+                                  v_cur=None if vcur is None else vcur[l].contiguous()) for l in range(nl)])
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), step
+    for l in range(layers):
+        assert a.length(sa, l) == (t if l0 <= l < l0 + nl else 0)
+    for l in range(l0, l0 + nl):
+        for which in (0, 1):
+            _same_record(a.read(sa, l, which), b.read(sb, l, which))
+
+
+def test_all_layers_calls_reject_bad_use(K):
+    kc, vc = K.Codec(bits=3, seed=0, mode=OP.QJL), K.Codec(bits=3, seed=0, mode=OP.MSE)
+    cache = K.Cache(kc, vc, layers=3, kv_heads=2, page_tokens=64, max_pages=64)
+    seq = cache.open(128)
+    kk, vv = _kv(2, 10, 95)
+    k3, v3 = torch.stack([kk] * 3), torch.stack([vv] * 3)
+    with pytest.raises(K.RQError):
+        cache.append_layers(seq, 1, k3.contiguous(), v3.contiguous())        # layers 1..3 of 3
+    cache.append(seq, 0, kk.contiguous(), vv.contiguous())
+    q = torch.from_numpy(W.queries(3 * 8, seed=96)).cuda().reshape(3, 8, D)
+    with pytest.raises(K.RQError):
+        cache.attend_layers(seq, 0, q)                                       # layer 0 holds 10, the rest 0
+    with pytest.raises(K.RQError):
+        cache.append_layers(seq, 0, k3.contiguous(), v3.contiguous())        # unequal lengths
+    cache.append_layers(seq, 1, k3[:2].contiguous(), v3[:2].contiguous())    # now all hold 10
+    out = cache.attend_layers(seq, 0, q)
+    torch.cuda.synchronize()
+    assert out.shape == (24, D) and torch.isfinite(out).all()
+    with pytest.raises(K.RQError):
+        cache.attend_layers(seq, 0, q[:, :7].contiguous())                   # hq not a multiple of kv_heads
