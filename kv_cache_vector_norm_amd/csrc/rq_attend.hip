@@ -26,7 +26,7 @@
 //      its tiles in the rotated domain, written as partial rows;
 //   4. per row: sum the partials in a fixed order, apply X^T and kappa S^T,
 //      divide by L.
-#include "rq_common.cuh"
+#include "rq_common_dev.h"
 #include "rq_kernels.h"
 
 #include <mutex>

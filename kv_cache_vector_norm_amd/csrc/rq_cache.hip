@@ -1,7 +1,7 @@
 // Kernels of the paged compressed KV cache (rq_cache_* in rq.h): moving
 // freshly quantised record rows into their pages, and folding the current
 // token's exact key and value into an attention result over the cache.
-#include "rq_common.cuh"
+#include "rq_common_dev.h"
 #include "rq_kernels.h"
 
 namespace rqk {

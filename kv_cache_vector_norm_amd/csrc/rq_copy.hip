@@ -3,7 +3,7 @@
 // each wave reads a 16 KB block as 16 coalesced 16-byte non-temporal raw
 // buffer loads (64 lanes x 16 B each), then writes it back with 16 such
 // stores; the descriptor's range drops the ragged tail.
-#include "rq_common.cuh"
+#include "rq_common_dev.h"
 #include "rq_kernels.h"
 
 namespace rqk {

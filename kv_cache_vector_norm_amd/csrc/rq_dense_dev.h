@@ -19,7 +19,7 @@
 // and multiplied by S, so the split residual is never held whole.
 #pragma once
 
-#include "rq_common.cuh"
+#include "rq_common_dev.h"
 #include "rq_kernels.h"
 
 namespace rqk {

@@ -10,7 +10,7 @@
 // then added in a fixed order in LDS, so the sums (and the choice) are
 // deterministic.  Each channel finds its rank among the 128 sums and its
 // position among the chosen channels by counting.
-#include "rq_common.cuh"
+#include "rq_common_dev.h"
 #include "rq_kernels.h"
 
 namespace rqk {

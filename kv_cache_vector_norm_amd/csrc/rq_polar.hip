@@ -19,7 +19,7 @@
 // a turn by pi (negation), a turn by -pi/2 (swap and negate), a reflection
 // in the diagonal (swap) — each adding its share of the code, and one cross
 // product against t_1 finishes it.
-#include "rq_dense.cuh"
+#include "rq_dense_dev.h"
 
 namespace rqk {
 

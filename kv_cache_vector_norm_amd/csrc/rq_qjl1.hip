@@ -15,7 +15,7 @@
 // outlier array and cleared before the norm, so the sign sketch sees only
 // the inlier part; dequantisation writes the stored values back over those
 // channels after the reconstruction has left.
-#include "rq_rotor.cuh"
+#include "rq_rotor_dev.h"
 
 namespace rqk {
 

@@ -24,7 +24,7 @@
 // operands of S^T sigma come straight from the accumulators.
 #pragma once
 
-#include "rq_common.cuh"
+#include "rq_common_dev.h"
 #include "rq_rotor_decl.h"
 
 namespace rqk {

@@ -29,7 +29,7 @@
 // fp32) and the rest q_in (those channels cleared) before S q_in is built;
 // per key the score is n^ gamma^ sqrt(pi/2)/m <S q_in, sigma> +
 // sum_i q_{c_i} o^_i over the key's stored outlier halves o^.
-#include "rq_common.cuh"
+#include "rq_common_dev.h"
 #include "rq_kernels.h"
 
 namespace rqk {
