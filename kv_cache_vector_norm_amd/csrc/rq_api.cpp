@@ -255,18 +255,43 @@ int rq_init(int d, int bits, uint64_t seed, int mode, rq_ctx** out) {
         s_cols.resize(t.s.size());
         for (int j = 0; j < n; ++j)
             for (int i = 0; i < n; ++i) s_cols[i * n + j] = t.s[j * n + i];
-        // MFMA layouts of the rotor kernels: accumulator row p of a 32-row M
-        // tile (lane half h = bit 2 of p) holds sign index / coordinate
-        // perm_row(p); K slot k of a 32-wide K pair feeds sign index perm_k(k).
-        auto perm_row = [](int p) { return (p & ~31) | (((p >> 2) & 1) << 4) | (((p >> 3) & 3) << 2) | (p & 3); };
-        auto perm_k = [](int k) { return (k & ~31) | (((k >> 3) & 1) << 4) | (((k >> 4) & 1) << 3) | (k & 7); };
         s_fwd.resize(t.s.size());
         s_back.resize(t.s.size());
-        for (int p = 0; p < n; ++p)
-            for (int k = 0; k < n; ++k) {
-                s_fwd[p * n + k] = t.s[perm_row(p) * n + k];
-                s_back[p * n + k] = t.s[perm_k(k) * n + perm_row(p)];
-            }
+        if (t.lay.mse_bits == 0) {
+            // QJL-only kernels (one lane per vector): accumulator row p of a
+            // 32-row M tile (lane half h = bit 2 of p) holds sign index /
+            // coordinate perm_row(p); K slot k of a 32-wide K pair feeds sign
+            // index perm_k(k).
+            auto perm_row = [](int p) { return (p & ~31) | (((p >> 2) & 1) << 4) | (((p >> 3) & 3) << 2) | (p & 3); };
+            auto perm_k = [](int k) { return (k & ~31) | (((k >> 3) & 1) << 4) | (((k >> 4) & 1) << 3) | (k & 7); };
+            for (int p = 0; p < n; ++p)
+                for (int k = 0; k < n; ++k) {
+                    s_fwd[p * n + k] = t.s[perm_row(p) * n + k];
+                    s_back[p * n + k] = t.s[perm_k(k) * n + perm_row(p)];
+                }
+        } else {
+            // Rotor codec kernels (two lanes per vector): local slot j of lane
+            // half h is coordinate 66 h + j, except that half 1's slots 62 and
+            // 63 stand for coordinates 64 and 65.  Accumulator element r of
+            // half h in M tile mt (row p = 8 (r / 4) + 4 h + r % 4) holds sign
+            // index / coordinate slot 64 h + 16 mt + r / slot 16 mt + r; K
+            // column 16 kb + 8 h + e takes slot 8 kb + e of half h (forward)
+            // or sign index 64 h + 8 kb + e (back-projection).
+            auto slot_coord = [](int h, int j) { return h == 0 ? j : (j < 62 ? 66 + j : j + 2); };
+            auto row_half = [](int r) { return ((r & 31) >> 2) & 1; };
+            auto row_elem = [](int r) { return (r >> 5) * 16 + 4 * ((r & 31) >> 3) + (r & 3); };
+            auto col_half = [](int c) { return (c >> 3) & 1; };
+            auto col_slot = [](int c) { return 8 * (c >> 4) + (c & 7); };
+            for (int r = 0; r < n; ++r)
+                for (int c = 0; c < n; ++c) {
+                    const int sign_row = 64 * row_half(r) + row_elem(r);
+                    const int coord_col = slot_coord(col_half(c), col_slot(c));
+                    const int coord_row = slot_coord(row_half(r), row_elem(r));
+                    const int sign_col = 64 * col_half(c) + col_slot(c);
+                    s_fwd[r * n + c] = t.s[sign_row * n + coord_col];
+                    s_back[r * n + c] = t.s[sign_col * n + coord_row];
+                }
+        }
     }
     if (polar) {
         // (cos, sin) of the decision boundaries (level 1: t_1..t_7, of which

@@ -26,8 +26,8 @@ struct RotorTables {
     float bin_a, bin_b;
     const uint16_t* s_rows;  // [128][128] halves (QJL)
     const uint16_t* s_cols;  // [128][128] halves, S^T (QJL)
-    const uint16_t* s_fwd;   // S with rows permuted for the quantiser's MFMA layout
-    const uint16_t* s_back;  // S^T with rows and columns permuted for the dequantiser
+    const uint16_t* s_fwd;   // S, rows and columns permuted for the codec kernels' MFMA layout
+    const uint16_t* s_back;  // S^T, rows and columns permuted for the back-projection
     const uint16_t* phi_hi;  // 16 Phi = hi + 2^-11 lo: the rotor transform of the first 128
     const uint16_t* phi_lo;  //   slots as a block-diagonal 128 x 128 matrix (scoring)
     float qjl_scale;

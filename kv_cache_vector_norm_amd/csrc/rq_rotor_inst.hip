@@ -1,6 +1,6 @@
 // One (bits, QJL) variant of the rotor kernels per translation unit, so the
 // variants build in parallel.  RQ_B and RQ_QJL are set by the build.
-#include "rq_rotor_dev.h"
+#include "rq_rotor_codec_dev.h"
 
 namespace rqk {
 template hipError_t launch_quant_b<RQ_B, RQ_QJL>(const RotorDev&, const void*, bool, int64_t, int64_t, uint32_t*,
