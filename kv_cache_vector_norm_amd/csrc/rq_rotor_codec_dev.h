@@ -50,8 +50,12 @@ constexpr int kSteps = 22;                   // group steps per lane
 constexpr int kSlots = 3 * kSteps;           // local slots per lane
 constexpr int kRotStride = 12;               // floats per group in the LDS matrix table
 constexpr int kRotGroups = kGroups + 1;      // + the idle step's zero matrix
-constexpr int kStageCode = 32 * 17 + 64;     // dwords: code words of a tile (+ read slack)
-constexpr int kStageWords = kStageCode + 128;   // + sign words
+// Per-wave record stage: the code words of a tile (with the slack the
+// copies read past them), later the sign words in the same place.
+template <int B>
+constexpr int stage_words2() {
+    return (32 * code_words<B>(kRotCoords) + 1 + 63) / 64 * 64;
+}
 
 template <bool F16>
 constexpr int row_bytes2() { return F16 ? 272 : 528; }
@@ -65,7 +69,7 @@ struct CodeSplit {
     static constexpr int J = kHalf1 * B / 32;             // record word shared by both halves
     static constexpr int S = kHalf1 * B % 32;             // bit of word J where half 1's stream starts
     static_assert(S != 0 && W == 2 * J + 1 && L == J + 1, "code word split");
-    static_assert(32 * W + 1 <= kStageCode, "stage size");
+    static_assert(stage_words2<B>() >= 128, "stage holds the sign words");
 };
 
 // Group step after which K block kb (slots 8 kb .. 8 kb + 7) is complete, and
@@ -279,8 +283,9 @@ __device__ __forceinline__ void out_pair(char* rowo, int k, float a, float b) {
 
 // Rotor matrices, 12 floats per group (the ninth to eleventh unused), and a
 // zero matrix for half 1's idle step.
+template <int NT>
 __device__ __forceinline__ void stage_rot(const float* __restrict__ g, float* __restrict__ s) {
-    for (int i = threadIdx.x; i < kRotGroups * kRotStride; i += kBlock) {
+    for (int i = threadIdx.x; i < kRotGroups * kRotStride; i += NT) {
         const int grp = i / kRotStride, k = i - grp * kRotStride;
         s[i] = (grp < kGroups && k < 9) ? g[9 * grp + k] : 0.0f;
     }
@@ -370,8 +375,8 @@ __device__ __forceinline__ void qjl_out2(const f32x16 (&acc)[4], const float (&x
 // s's region the forward rotation and slot lookups of step s + 1 are issued
 // before the compare / inverse / residual work of step s, and the matrix of
 // step s + 2 is fetched there too.
-template <int B, bool QJL, bool IN_F16, bool OUT_F16, bool ROUNDTRIP>
-__global__ __launch_bounds__(256) void rq_quant_kernel(RotorDev P, const char* __restrict__ x, int64_t ldx_bytes,
+template <int B, bool QJL, bool IN_F16, bool OUT_F16, bool ROUNDTRIP, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void rq_quant_kernel(RotorDev P, const char* __restrict__ x, int64_t ldx_bytes,
                                                        int64_t n, uint32_t* __restrict__ codes,
                                                        uint16_t* __restrict__ norms, uint32_t* __restrict__ signs,
                                                        uint16_t* __restrict__ rnorms, char* __restrict__ y,
@@ -382,36 +387,36 @@ __global__ __launch_bounds__(256) void rq_quant_kernel(RotorDev P, const char* _
     constexpr bool BACK = QJL && ROUNDTRIP;
     constexpr int RBI = row_bytes2<IN_F16>(), RBO = row_bytes2<OUT_F16>();
     constexpr int TB = 32 * (RBI > RBO ? RBI : RBO);
+    constexpr int NT = 64 * WAVES;
     struct Lds {
         u32x4 bins[kBinSlots];
         float rot[kRotGroups * kRotStride];
         u32x4 s_fwd[QJL ? 128 * 16 : 1];
         u32x4 s_back[BACK ? 128 * 16 : 1];
-        u32x4 tiles[4][TB / 16];
-        uint32_t stage[4][kStageWords];
+        u32x4 tiles[WAVES][TB / 16];
+        uint32_t stage[WAVES][stage_words2<B>()];
     };
     __shared__ Lds lds;
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t ntiles = (n + 31) / 32;
-    const int64_t tstep = gridDim.x * 4LL;
-    const int64_t t0 = blockIdx.x * 4LL + wave;
+    const int64_t tstep = static_cast<int64_t>(gridDim.x) * WAVES;
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * WAVES + wave;
     // fp16 input: each tile's fetch is issued one tile ahead (the first one
     // before the block's staging, so the two latencies overlap)
     Tile2Regs<true> nx;
     if constexpr (IN_F16) {
         if (t0 < ntiles) tile2_fetch<true>(x, ldx_bytes, t0 * 32, n, nx, lane_id());
     }
-    stage_bins<QJL>(P.bins, lds.bins);
-    stage_rot(P.rotmat, lds.rot);
-    if constexpr (QJL) mat_to_lds(P.s_fwd, lds.s_fwd);
-    if constexpr (BACK) mat_to_lds(P.s_back, lds.s_back);
+    stage_bins<QJL, NT>(P.bins, lds.bins);
+    stage_rot<NT>(P.rotmat, lds.rot);
+    if constexpr (QJL) mat_to_lds<NT>(P.s_fwd, lds.s_fwd);
+    if constexpr (BACK) mat_to_lds<NT>(P.s_back, lds.s_back);
     __syncthreads();
 
     const float ba = P.bin_a * (1.0f / D), bb = P.bin_b;
     char* tile = reinterpret_cast<char*>(lds.tiles[wave]);
     uint32_t* stw = lds.stage[wave];
-    uint32_t* sts = stw + kStageCode;
     const char* binc = reinterpret_cast<const char*>(lds.bins);
 
     for (int64_t t = t0; t < ntiles; t += tstep) {
@@ -613,9 +618,10 @@ __global__ __launch_bounds__(256) void rq_quant_kernel(RotorDev P, const char* _
         words2_store<W>(codes, base, n, stw, l);
         if constexpr (QJL) {
             half_store2(rnorms, base, n, gh, vi);
-            sts[vi * 4 + 2 * h] = sw0;
-            sts[vi * 4 + 2 * h + 1] = sw1;
-            words2_store<4>(signs, base, n, sts, l);
+            wave_lds_sync();   // the code words have left the stage
+            stw[vi * 4 + 2 * h] = sw0;
+            stw[vi * 4 + 2 * h + 1] = sw1;
+            words2_store<4>(signs, base, n, stw, l);
         }
 
         // The reconstruction is exactly what rq_dequant_kernel computes from
@@ -649,18 +655,17 @@ __global__ __launch_bounds__(256) void rq_dequant_kernel(RotorDev P, const uint3
         float rot[kRotGroups * kRotStride];
         u32x4 s_back[QJL ? 128 * 16 : 1];
         u32x4 tiles[4][32 * RBO / 16];
-        uint32_t stage[4][kStageWords];
+        uint32_t stage[4][stage_words2<B>()];
     };
     __shared__ Lds lds;
     stage_pairs<B, QJL>(P.cent, lds.pairs);
-    stage_rot(P.rotmat, lds.rot);
+    stage_rot<kBlock>(P.rotmat, lds.rot);
     if constexpr (QJL) mat_to_lds(P.s_back, lds.s_back);
     __syncthreads();
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     char* tile = reinterpret_cast<char*>(lds.tiles[wave]);
     uint32_t* stw = lds.stage[wave];
-    uint32_t* sts = stw + kStageCode;
     const int64_t ntiles = (n + 31) / 32;
     for (int64_t t = blockIdx.x * 4LL + wave; t < ntiles; t += gridDim.x * 4LL) {
         const int64_t base = t * 32;
@@ -675,8 +680,8 @@ __global__ __launch_bounds__(256) void rq_dequant_kernel(RotorDev P, const uint3
         float kq = 0.0f, ns = nhat;
         f32x16 acc[QJL ? 4 : 1];
         if constexpr (QJL) {
-            words2_load<4>(signs, base, n, sts, l);
-            const uint32_t sw0 = sts[vi * 4 + 2 * h], sw1 = sts[vi * 4 + 2 * h + 1];
+            words2_load<4>(signs, base, n, stw, l);   // the code words are in registers
+            const uint32_t sw0 = stw[vi * 4 + 2 * h], sw1 = stw[vi * 4 + 2 * h + 1];
             const float ghat = h2f(half_load2(rnorms, base, n, vi));
             u32x4 sig[8];
 #pragma unroll
@@ -743,31 +748,45 @@ __global__ __launch_bounds__(256) void rq_dequant_kernel(RotorDev P, const uint3
 }
 
 // ----------------------------------------------------------- launchers --
-// Workgroups of four waves, at most per_cu per compute unit in one round:
+// Workgroups of `waves` waves, at most per_cu per compute unit in one round:
 // every wave then loops over its tiles.
-inline int grid2_for(int64_t n, int per_cu) {
+inline int grid2_for(int64_t n, int waves, int per_cu) {
     const int64_t ntiles = (n + 31) / 32;
-    const int64_t blocks = (ntiles + 3) / 4;
+    const int64_t blocks = (ntiles + waves - 1) / waves;
     const int64_t cap = 256LL * per_cu;
     return static_cast<int>(blocks < cap ? (blocks > 0 ? blocks : 1) : cap);
 }
 
+// Launch shapes: QJL kernels with fp16 input and output run eight waves per
+// workgroup sharing one copy of S and S^T (two waves per SIMD); the other
+// QJL shapes need four waves' LDS.  MSE-only kernels run four-wave groups,
+// two per compute unit in a round.
+#ifndef RQ_QJL_F16_WAVES
+#define RQ_QJL_F16_WAVES 8
+#endif
+#ifndef RQ_MSE_PER_CU
+#define RQ_MSE_PER_CU 2
+#endif
 template <int B, bool QJL>
 hipError_t launch_quant_b(const RotorDev& P, const void* x, bool in_f16, int64_t ldx_bytes, int64_t n,
                           uint32_t* codes, uint16_t* norms, uint32_t* signs, uint16_t* rnorms, void* y, bool out_f16,
                           int64_t ldy_bytes, bool roundtrip, hipStream_t s) {
-    const int grid = grid2_for(n, QJL ? 1 : 2);
     const char* xc = static_cast<const char*>(x);
     char* yc = static_cast<char*>(y);
-#define RQ_LAUNCH(IF, OF, RT)                                                                                     \
-    hipLaunchKernelGGL((rq_quant_kernel<B, QJL, IF, OF, RT>), dim3(grid), dim3(256), 0, s, P, xc, ldx_bytes, n, \
-                       codes, norms, signs, rnorms, yc, ldy_bytes)
+    constexpr int WF = QJL ? RQ_QJL_F16_WAVES : 4;   // fp16 in and out
+    constexpr int PC = QJL ? 1 : RQ_MSE_PER_CU;
+#define RQ_LAUNCH(IF, OF, RT, WV)                                                                               \
+    hipLaunchKernelGGL((rq_quant_kernel<B, QJL, IF, OF, RT, WV>), dim3(grid2_for(n, WV, PC)), dim3(64 * WV), 0, s, \
+                       P, xc, ldx_bytes, n, codes, norms, signs, rnorms, yc, ldy_bytes)
     if (!roundtrip) {
-        if (in_f16) RQ_LAUNCH(true, true, false); else RQ_LAUNCH(false, true, false);
+        if (in_f16) RQ_LAUNCH(true, true, false, WF);
+        else RQ_LAUNCH(false, true, false, 4);
     } else if (in_f16) {
-        if (out_f16) RQ_LAUNCH(true, true, true); else RQ_LAUNCH(true, false, true);
+        if (out_f16) RQ_LAUNCH(true, true, true, WF);
+        else RQ_LAUNCH(true, false, true, 4);
     } else {
-        if (out_f16) RQ_LAUNCH(false, true, true); else RQ_LAUNCH(false, false, true);
+        if (out_f16) RQ_LAUNCH(false, true, true, 4);
+        else RQ_LAUNCH(false, false, true, 4);
     }
 #undef RQ_LAUNCH
     return hipGetLastError();
@@ -777,7 +796,7 @@ template <int B, bool QJL>
 hipError_t launch_dequant_b(const RotorDev& P, const uint32_t* codes, const uint16_t* norms, const uint32_t* signs,
                             const uint16_t* rnorms, int64_t n, void* y, bool out_f16, int64_t ldy_bytes,
                             hipStream_t s) {
-    const int grid = grid2_for(n, QJL ? 1 : 2);
+    const int grid = grid2_for(n, 4, QJL ? 1 : RQ_MSE_PER_CU);
     char* yc = static_cast<char*>(y);
     if (out_f16)
         hipLaunchKernelGGL((rq_dequant_kernel<B, QJL, true>), dim3(grid), dim3(256), 0, s, P, codes, norms, signs,

@@ -33,11 +33,11 @@ constexpr int code_words(int coords) { return (coords * B + 31) / 32; }
 
 
 // -------------------------------------------------------------- set-up --
-template <bool QJL>
+template <bool QJL, int NT = kBlock>
 __device__ __forceinline__ void stage_bins(const u32x4_t* __restrict__ g, u32x4* __restrict__ s) {
     constexpr float D = QJL ? kQjlDomain : 1.0f;
     const u32x4* src = reinterpret_cast<const u32x4*>(g);
-    for (int i = threadIdx.x; i < kBinSlots; i += kBlock) {
+    for (int i = threadIdx.x; i < kBinSlots; i += NT) {
         const u32x4 e = src[i];
         const uint32_t e0 = e[0], e1 = e[1], e2 = e[2], e3 = e[3];
         s[i] = u32x4{e0, __builtin_bit_cast(uint32_t, __builtin_bit_cast(float, e1) * D),
