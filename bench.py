@@ -146,8 +146,8 @@ def digest_of(mangled_part):
     return kernel_code_digest(hits[0])
 
 
-ROUNDTRIP_KERNEL = "rq_quant_kernel<2, true, true, true, true>"
-ROUNDTRIP_SYMBOL = "_ZN3rqk15rq_quant_kernelILi2ELb1ELb1ELb1ELb1EEEvNS_8RotorDevEPKcllPjPtS4_S5_Pcl"
+ROUNDTRIP_KERNEL = "rq_quant_kernel<2, true, true, true, true, 8>"
+ROUNDTRIP_SYMBOL = "_ZN3rqk15rq_quant_kernelILi2ELb1ELb1ELb1ELb1ELi8EEEvNS_8RotorDevEPKcllPjPtS4_S5_Pcl"
 
 
 # -------------------------------------------------- profiled kernel set --
@@ -160,16 +160,16 @@ def profile_cases():
     return [
         ("copy_65536_same_bytes", "rqk::copy_kernel", "11copy_kernel", 4, n1 * 568, 0,
          "reference copy of 65,536 x 568 B (read 284 B, write 284 B per vector)"),
-        ("rq_roundtrip_qjl3_65536", "rqk::rq_quant_kernel<2, true, true, true, true>",
-         "15rq_quant_kernelILi2ELb1ELb1ELb1ELb1EE", 4, n1 * 568, 0,
+        ("rq_roundtrip_qjl3_65536", "rqk::rq_quant_kernel<2, true, true, true, true, 8>",
+         "15rq_quant_kernelILi2ELb1ELb1ELb1ELb1ELi8EE", 4, n1 * 568, 0,
          "rotor roundtrip, 2-bit codes + QJL, fp16 in/out, 65,536 keys (the step's codec kernel)"),
         ("rq_score_64x65536", "rqk::score_kernel<2, true, true, 2, false>", "12score_kernelILi2ELb1ELb1ELi2ELb0EE", 4,
          n1 * 56 + 4 * N_Q * n1, 0, "q.k estimates of 64 queries against 65,536 compressed keys"),
-        ("rq_roundtrip_mse3_65536", "rqk::rq_quant_kernel<3, false, true, true, true>",
-         "15rq_quant_kernelILi3ELb0ELb1ELb1ELb1EE", 4, n1 * 566, 0,
+        ("rq_roundtrip_mse3_65536", "rqk::rq_quant_kernel<3, false, true, true, true, 4>",
+         "15rq_quant_kernelILi3ELb0ELb1ELb1ELb1ELi4EE", 4, n1 * 566, 0,
          "rotor roundtrip, 3-bit MSE only, fp16 in/out, 65,536 keys"),
-        ("rq_roundtrip_mse3_1048576", "rqk::rq_quant_kernel<3, false, true, true, true>",
-         "15rq_quant_kernelILi3ELb0ELb1ELb1ELb1EE", 4, nm * 566, 0,
+        ("rq_roundtrip_mse3_1048576", "rqk::rq_quant_kernel<3, false, true, true, true, 4>",
+         "15rq_quant_kernelILi3ELb0ELb1ELb1ELb1ELi4EE", 4, nm * 566, 0,
          "rotor roundtrip, 3-bit MSE only, fp16 in/out, 1,048,576 keys"),
         ("copy_1048576_same_bytes", "rqk::copy_kernel", "11copy_kernel", 4, nm * 566, 0,
          "reference copy of 1,048,576 x 566 B"),

@@ -185,12 +185,12 @@ __device__ __forceinline__ void put4(u32x4* qrows, int row, int off, int j, uint
 // for both products.  Outputs (unscaled) hold rows 32 w + 8 (r / 4) +
 // 4 h + r % 4 of query row 32 nt + l % 32.
 // A-operand fragments of wave w's M tile of X (hi, lo) and S, all 8 K blocks.
-template <bool QJL>
+template <bool QJL, bool X>
 struct QueryFrags {
-    u32x4 xh[8], xl[8], sa[QJL ? 8 : 1];
+    u32x4 xh[X ? 8 : 1], xl[X ? 8 : 1], sa[QJL ? 8 : 1];
 };
-template <bool QJL>
-__device__ __forceinline__ void query_frags(const MainArgs& a, int w, int l, QueryFrags<QJL>& f) {
+template <bool QJL, bool X>
+__device__ __forceinline__ void query_frags(const MainArgs& a, int w, int l, QueryFrags<QJL, X>& f) {
     const int n = l & 31, hh = l >> 5;
     const u32x4* gxh = reinterpret_cast<const u32x4*>(a.x_hi);
     const u32x4* gxl = reinterpret_cast<const u32x4*>(a.x_lo);
@@ -198,8 +198,10 @@ __device__ __forceinline__ void query_frags(const MainArgs& a, int w, int l, Que
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) {
         const int i = (32 * w + n) * 16 + 2 * kb + hh;
-        f.xh[kb] = gxh[i];
-        f.xl[kb] = gxl[i];
+        if constexpr (X) {
+            f.xh[kb] = gxh[i];
+            f.xl[kb] = gxl[i];
+        }
         if constexpr (QJL) f.sa[kb] = gs[i];
     }
 }
@@ -236,9 +238,10 @@ __device__ __forceinline__ void query_split(Lds& lds, u32x4* bop, int w, int l) 
     }
 }
 
-template <bool QJL, int NMT>
-__device__ __forceinline__ void query_products(const QueryFrags<QJL>& fr, const u32x4* bop, const float (&s0r)[NMT],
-                                               int l, float (&ox)[NMT][16], float (&os)[NMT][16]) {
+template <bool QJL, bool X, int NMT>
+__device__ __forceinline__ void query_products(const QueryFrags<QJL, X>& fr, const u32x4* bop,
+                                               const float (&s0r)[NMT], int l, float (&ox)[NMT][16],
+                                               float (&os)[NMT][16]) {
 #pragma unroll
     for (int nt = 0; nt < NMT; ++nt) {
         f32x16 ax = {}, as = {};
@@ -246,9 +249,11 @@ __device__ __forceinline__ void query_products(const QueryFrags<QJL>& fr, const 
         for (int kb = 0; kb < 8; ++kb) {
             const u32x4* b = bop + ((nt * 8 + kb) * 3) * 64 + l;
             const u32x4 h11 = b[0], l11 = b[64], h = b[128];
-            ax = mfma(fr.xh[kb], h11, ax);
-            ax = mfma(fr.xh[kb], l11, ax);
-            ax = mfma(fr.xl[kb], h, ax);
+            if constexpr (X) {
+                ax = mfma(fr.xh[kb], h11, ax);
+                ax = mfma(fr.xh[kb], l11, ax);
+                ax = mfma(fr.xl[kb], h, ax);
+            }
             if constexpr (QJL) {
                 as = mfma(fr.sa[kb], h11, as);
                 as = mfma(fr.sa[kb], l11, as);
@@ -314,6 +319,77 @@ __device__ __forceinline__ void product_store(const float (&out)[NMT][16], Lds& 
     }
 }
 
+// Rotor path: q^ = Phi q on the VALU (each slot is one row of its group's
+// 3x3 sandwich matrix; blog section on the random rotation: rotate the
+// query once), written over the staged fp32 rows: job (row, group) reads and
+// writes that group's three entries, the pad input being 0 (slot 128 lands
+// in the row's padding).
+template <int ROWS, class Lds>
+__device__ __forceinline__ void rotor_qhat_in_place(Lds& lds) {
+    for (int job = threadIdx.x; job < ROWS * kGroups; job += kBlock) {
+        const int r = job / kGroups, g = job - r * kGroups;
+        float* q = &lds.qf[r][3 * g];
+        const u32x4 m0 = *reinterpret_cast<const u32x4*>(&lds.rot[12 * g]);
+        const u32x4 m1 = *reinterpret_cast<const u32x4*>(&lds.rot[12 * g + 4]);
+        const float m8 = lds.rot[12 * g + 8];
+        float m[9];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t a0 = m0[k];
+            const uint32_t a1 = m1[k];
+            m[k] = __builtin_bit_cast(float, a0);
+            m[4 + k] = __builtin_bit_cast(float, a1);
+        }
+        m[8] = m8;
+        const float v0 = q[0], v1 = q[1], v2 = g == kGroups - 1 ? 0.0f : q[2];
+        float y[3];
+#pragma unroll
+        for (int rr = 0; rr < 3; ++rr)
+            y[rr] = __builtin_fmaf(m[3 * rr + 2], v2, __builtin_fmaf(m[3 * rr + 1], v1, m[3 * rr] * v0));
+        q[0] = y[0];
+        q[1] = y[1];
+        q[2] = y[2];
+    }
+}
+
+// Q1 = 2^11 hi, Q2 = hi, Q3 = lo11 of sc q^ over slots 0..127 (sc a power of
+// two putting the row's largest |q^| in [1, 2)), whole 16-byte chunks per
+// thread, and the row scalar 1 / (2^11 sc) * inv_sc.
+template <int ROWS, class Lds>
+__device__ __forceinline__ void rotor_qhat_store(Lds& lds, float inv_sc) {
+    constexpr int TPR = kBlock / ROWS, CPT = kD / TPR;
+    const int t = threadIdx.x, r = t / TPR, part = t % TPR;
+    const float* q = &lds.qf[r][CPT * part];
+    float v[CPT];
+    float mx = 0.0f;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+        v[k] = q[k];
+        mx = fmaxf(mx, fabsf(v[k]));
+    }
+#pragma unroll
+    for (int o = 1; o < TPR; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    const float sc = pow2_scale(mx);
+#pragma unroll
+    for (int c = 0; c < CPT / 8; ++c) {
+        u32x4 A, Bv, C;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const float x0 = v[8 * c + 2 * d] * sc, x1 = v[8 * c + 2 * d + 1] * sc;
+            const uint32_t hp = cvt_pk(x0, x1);
+            C[d] = hp;
+            A[d] = pk_scale2048(hp);
+            Bv[d] = cvt_pk((x0 - h2f(hp & 0xFFFFu)) * 2048.0f, (x1 - h2f(hp >> 16)) * 2048.0f);
+        }
+        const int chunk = (CPT * part) / 8 + c;
+        u32x4* row = lds.qrows + r * kRowStride;
+        row[kOffQ1 + chunk] = A;
+        row[kOffQ3 + chunk] = Bv;
+        row[kOffQ2 + chunk] = C;
+    }
+    if (part == 0) lds.rsc[r][0] = inv_sc / (2048.0f * sc);
+}
+
 // Builds the block's staged query rows (see "staged rows") and row scalars.
 // The block's query rows as loaded at kernel start: thread t holds float4 t
 // of each 256-float4 slice (rows >= nrows read as zero).
@@ -334,7 +410,8 @@ __device__ __forceinline__ void query_load(const MainArgs& a, int row0, int nrow
 
 template <bool PAD, bool QJL, int NMT, bool OUTL = false, class Lds>
 __device__ __forceinline__ void build_query_rows(const MainArgs& a, const QueryRegs<NMT>& qr,
-                                                 const QueryFrags<QJL>& fr, float inv_sc, Lds& lds, int ghead = 0) {
+                                                 const QueryFrags<QJL, !PAD>& fr, float inv_sc, Lds& lds,
+                                                 int ghead = 0) {
     constexpr int ROWS = NMT * 32;
     constexpr int TPR = kBlock / ROWS;   // threads per row
     constexpr int CPT = kD / TPR;        // coordinates per thread
@@ -394,12 +471,15 @@ __device__ __forceinline__ void build_query_rows(const MainArgs& a, const QueryR
 #pragma unroll
     for (int nt = 0; nt < NMT; ++nt) s0r[nt] = lds.s0[32 * nt + (l & 31)];
     __syncthreads();
+    // rotor: q^ on the VALU over the fp32 rows (S q' reads the split operands)
+    if constexpr (PAD) rotor_qhat_in_place<ROWS>(lds);
     float ox[NMT][16], os[NMT][16];
-    query_products<QJL, NMT>(fr, bop, s0r, l, ox, os);
-    product_row_max<NMT>(ox, lds, 0, w, l);
+    query_products<QJL, !PAD, NMT>(fr, bop, s0r, l, ox, os);
+    if constexpr (!PAD) product_row_max<NMT>(ox, lds, 0, w, l);
     if constexpr (QJL) product_row_max<NMT>(os, lds, 1, w, l);
     __syncthreads();
-    product_store<NMT>(ox, lds, 0, w, l, kOffQ1, kOffQ3, kOffQ2, 0, inv_sc);
+    if constexpr (PAD) rotor_qhat_store<ROWS>(lds, inv_sc);
+    else product_store<NMT>(ox, lds, 0, w, l, kOffQ1, kOffQ3, kOffQ2, 0, inv_sc);
     if constexpr (QJL) product_store<NMT>(os, lds, 1, w, l, kOffP1, kOffP2, -1, 1, 1.0f);
     __syncthreads();
 }
@@ -440,6 +520,7 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
         uint32_t stage[4][64 * SW + 4];   // (+4: the 3-bit reads of the 16-row loop run one word past)
         float qf[ROWS][kD + 4];
         u32x4 qrows[ROWS * kRowStride];
+        float rot[PAD ? 12 * kGroups : 4];             // rotor matrices, 12 floats per group
         float qo[OUTL ? ROWS : 1][16];                 // query values on the outlier channels
         uint32_t ostage[OUTL ? 4 : 1][OUTL ? 512 : 1];  // per wave: the tile's outlier halves
     };
@@ -455,42 +536,60 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
     const int64_t ntiles = (a.t + 63) / 64;
     const int64_t rbase = static_cast<int64_t>(a.kv_head0 + kvh) * a.kv_stride;
     const int64_t tstep = gridDim.x * 4LL;
-    // the first tile's record is requested before the block's staging
+    const int t = threadIdx.x;
+    // Global loads in the order of use (loads complete in order): the
+    // codebook and (rotor) the sandwich matrices, the query rows, the S
+    // (and dense Pi) fragments of the query build, then the first tile's record.
+    const float cv = t < L ? a.cent[t] : 0.0f;
+    constexpr int RV = (12 * kGroups + kBlock - 1) / kBlock;
+    float rv[RV] = {};
+    if constexpr (PAD) {
+#pragma unroll
+        for (int k = 0; k < RV; ++k) {
+            const int i = t + kBlock * k, g = i / 12, e = i - 12 * g;
+            rv[k] = (g < kGroups && e < 9) ? a.rotmat[9 * g + e] : 0.0f;
+        }
+    }
+    QueryRegs<NB> qr;
+    query_load<NB>(a, row0, nrows, qr);
+    QueryFrags<QJL, !PAD> fr;
+    query_frags<QJL, !PAD>(a, wave, lane_id(), fr);
     RecRegs<W, KPL, OUTL> rec;
     int64_t tile = blockIdx.x * 4LL + wave;
     const int ghead = a.kv_head0 + kvh;
     if (tile < ntiles) rec_fetch<W, QJL, KPL, OUTL>(a, rbase, ghead, tile * 64, rec, lane_id());
-    // and so are the query rows and the X / S fragments of the query build
-    QueryRegs<NB> qr;
-    query_load<NB>(a, row0, nrows, qr);
-    QueryFrags<QJL> fr;
-    query_frags<QJL>(a, wave, lane_id(), fr);
 
     float inv_sc;
     {
-        const float cmax = fabsf(a.cent[L - 1]) > fabsf(a.cent[0]) ? fabsf(a.cent[L - 1]) : fabsf(a.cent[0]);
+        if (t < L) lds.cent[t] = cv;
+        if constexpr (PAD) {
+#pragma unroll
+            for (int k = 0; k < RV; ++k)
+                if (t + kBlock * k < 12 * kGroups) lds.rot[t + kBlock * k] = rv[k];
+        }
+        __syncthreads();
+        const float cmax = fabsf(lds.cent[L - 1]) > fabsf(lds.cent[0]) ? fabsf(lds.cent[L - 1]) : fabsf(lds.cent[0]);
         const float sc = pow2_scale(cmax);
         inv_sc = 1.0f / sc;
-        for (int p = threadIdx.x; p < L * L; p += kBlock) {
+        for (int p = t; p < L * L; p += kBlock) {
             uint32_t h0, l0, h1, l1;
-            split_h11(a.cent[p & (L - 1)] * sc, &h0, &l0);
-            split_h11(a.cent[p >> B] * sc, &h1, &l1);
+            split_h11(lds.cent[p & (L - 1)] * sc, &h0, &l0);
+            split_h11(lds.cent[p >> B] * sc, &h1, &l1);
             lds.pairs[p][0] = h0 | (h1 << 16);
             lds.pairs[p][1] = l0 | (l1 << 16);
         }
         if constexpr (QUAD) {
-            for (int p = threadIdx.x; p < NQ; p += kBlock) {
+            for (int p = t; p < NQ; p += kBlock) {
                 uint32_t h[4], o[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) split_h11(a.cent[(p >> (B * i)) & (L - 1)] * sc, &h[i], &o[i]);
+                for (int i = 0; i < 4; ++i) split_h11(lds.cent[(p >> (B * i)) & (L - 1)] * sc, &h[i], &o[i]);
                 lds.quad[p] = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
                 lds.quad[QLO + p] = make_uint2(o[0] | (o[1] << 16), o[2] | (o[3] << 16));
             }
         }
         if constexpr (STAB) {
-            for (int p = threadIdx.x; p < 256; p += kBlock) lds.sigt[p] = sigma8(static_cast<uint32_t>(p));
+            for (int p = t; p < 256; p += kBlock) lds.sigt[p] = sigma8(static_cast<uint32_t>(p));
         }
-        if (threadIdx.x < L) lds.cent[threadIdx.x] = a.cent[threadIdx.x];
     }
     build_query_rows<PAD, QJL, NB, OUTL>(a, qr, fr, inv_sc, lds, ghead);
     uint32_t* ost = lds.ostage[wave];
