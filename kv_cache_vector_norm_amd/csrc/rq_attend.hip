@@ -121,16 +121,28 @@ __device__ __forceinline__ void split_pair11(float a, float b, uint32_t* hi, uin
 // holds half the accumulators, so two waves fit on a SIMD.
 // Register budget: two waves per SIMD for the centroid pass (3- and 4-bit
 // values included), three for the sign pass.
+//
+// Per tile, the weights (p n^ for the centroid sums, p n^ gamma^ for the
+// sign sums) are computed only for the block's live query rows: lane l takes
+// key pair l % 32 of rows l / 32, l / 32 + 2, ..., and writes the split
+// halves to a per-wave table that the MFMA A fragments read (rows past the
+// live ones are zero operands).
 template <int B, bool QJL, bool PAD, bool CODES = true>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CODES ? 2 : 3))) void attend_values_kernel(
     AttendArgs a) {
+    static_assert(CODES != QJL, "one kind of sum per pass");
     constexpr int L = 1 << B;
     constexpr int W = CODES ? (((PAD ? kRotCoords : kD) * B) + 31) / 32 : 1;
+    constexpr int WTS = 36;   // weight-table row pitch (dwords): conflict-free 16-byte reads
     struct alignas(16) Wave {
         uint32_t code[W + 1][64];   // [word][key]; one spare word row for the straddle read
         uint32_t sign[4][64];
         alignas(16) uint16_t nrm[64];
         alignas(16) uint16_t gam[64];
+    };
+    struct WaveW {
+        uint32_t hi[32][WTS];       // [row][key pair]: fp16 hi of the weights of keys 2q, 2q+1
+        uint32_t lo[32][WTS];       // lo11 = half((w - hi) 2^11)
     };
     struct Lds {
         // codes (k, k+1) -> 2^11 C_hi, C_lo and C_hi half pairs at [p], [257 + p],
@@ -139,7 +151,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CODES ? 2 :
         uint32_t ptab[CODES ? 3 * 257 : 1];
         u32x4 sig[QJL ? 256 : 1][2];   // eight sign bits -> {+-1, +-2^11} half pairs (bit 2q + e: dword q, half e)
         Wave w[4];
-        float sum[32][kPartStride];   // the block's partial rows, waves added in order
+        union {
+            WaveW wt[4];                  // tile loop: per-wave weight tables
+            float sum[32][kPartStride];   // after it: the block's partial rows, waves added in order
+        };
     };
     __shared__ Lds lds;
 
@@ -186,12 +201,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CODES ? 2 :
     __syncthreads();
 
     Wave& wv = lds.w[wave];
+    WaveW& wt = lds.wt[wave];
     const int l = lane_id();
     const int n = l & 31, hh = l >> 5;
     const bool live = n < nrows;
-    const float mrow = live ? a.stats[row0 + n].x : 0.0f;
     const rsrc_t rsc = make_rsrc(a.scores + static_cast<int64_t>(row0) * a.ld,
                                  static_cast<uint32_t>(nrows * a.ld * 4));
+    // the weight rows of this lane: l / 32 + 2 i for i < ri, key pair l % 32
+    const int ri = (nrows - hh + 1) >> 1;
+    float mrow[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mrow[i] = i < ri ? a.stats[row0 + hh + 2 * i].x : 0.0f;
 
     f32x16 acc_c[4], acc_p, acc_s[4];
 #pragma unroll
@@ -205,21 +225,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CODES ? 2 :
     // 16 kb + 8 hh .. + 7 of each K block) and dword l of the tile's code,
     // sign and norm runs.  They are fetched one tile ahead of their use, so
     // each tile's load latency hides behind the previous tile's arithmetic.
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
     struct TileIn {
-        u32x4 sv[4][2];
+        u32x2 sp[16];
         uint32_t cw[W];
         uint32_t sw[4];
         uint32_t nb, gb;
     };
     auto fetch = [&](int64_t tile, TileIn& r) {
         const int64_t kbase = tile * 64;
-        const uint32_t soff = static_cast<uint32_t>((n * a.ld + kbase + 8 * hh) * 4);
-        // (rows past nrows lie outside rsc's range and read as zero)
+        // estimates of keys 2 n, 2 n + 1 of rows hh + 2 i (rows past nrows lie
+        // outside rsc's range and read as zero)
+        const uint32_t soff = static_cast<uint32_t>((hh * a.ld + kbase + 2 * n) * 4);
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-            for (int q = 0; q < 2; ++q)
-                r.sv[kb][q] = __builtin_amdgcn_raw_buffer_load_b128(rsc, soff, 64 * kb + 16 * q, kNonTemporal);
+        for (int i = 0; i < 16; ++i)
+            if (i < ri) r.sp[i] = __builtin_amdgcn_raw_buffer_load_b64(rsc, soff, static_cast<int>(2 * i * a.ld * 4),
+                                                                       kNonTemporal);
         const int64_t left = a.t - kbase;
         int64_t row = rbase + kbase;
         if (a.pt.pages != nullptr) {
@@ -254,12 +275,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CODES ? 2 :
     for (int64_t tile = blockIdx.x * 4LL + wave; tile < ntiles; tile += tstep) {
         const int64_t kbase = tile * 64;
         const int kleft = static_cast<int>(a.t - kbase < 64 ? a.t - kbase : 64);   // live keys of the tile
-        u32x4 sv[4][2];
+        u32x2 sp[16];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            sv[kb][0] = nx.sv[kb][0];
-            sv[kb][1] = nx.sv[kb][1];
-        }
+        for (int i = 0; i < 16; ++i) sp[i] = nx.sp[i];
         // the tile's value records into LDS, key-minor
         wave_lds_sync();
         if constexpr (CODES) {
@@ -279,45 +297,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CODES ? 2 :
         }
         wv.nrm[l] = static_cast<uint16_t>(nx.nb);
         wave_lds_sync();
+        // weights of the live rows into the table
+        {
+            const uint32_t nn = *reinterpret_cast<const uint32_t*>(&wv.nrm[2 * n]);
+            uint32_t gg = 0u;
+            if constexpr (QJL) gg = *reinterpret_cast<const uint32_t*>(&wv.gam[2 * n]);
+            const float n0 = h2f(nn & 0xFFFFu), n1 = h2f(nn >> 16);
+            const float ga = h2f(gg & 0xFFFFu), gb = h2f(gg >> 16);
+            const bool in0 = 2 * n < kleft, in1 = 2 * n + 1 < kleft;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                if (i < ri) {
+                    const uint32_t b0 = sp[i][0];
+                    const uint32_t b1 = sp[i][1];
+                    const float s0 = __builtin_bit_cast(float, b0), s1 = __builtin_bit_cast(float, b1);
+                    const float e0 = in0 ? exp2_hw((s0 * a.scale - mrow[i]) * kLog2e) : 0.0f;
+                    const float e1 = in1 ? exp2_hw((s1 * a.scale - mrow[i]) * kLog2e) : 0.0f;
+                    float w0 = e0 * n0, w1 = e1 * n1;   // p n^ (sign pass: p n^ gamma^)
+                    if constexpr (QJL) {
+                        w0 = w0 * ga;
+                        w1 = w1 * gb;
+                    }
+                    uint32_t h, lo;
+                    split_pair11(w0, w1, &h, &lo);
+                    wt.hi[hh + 2 * i][n] = h;
+                    wt.lo[hh + 2 * i][n] = lo;
+                }
+            }
+        }
+        wave_lds_sync();
         if (tile + tstep < ntiles) fetch(tile + tstep, nx);
 
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
             const int k0 = 16 * kb + 8 * hh;
-            // weights p n^ (and p n^ gamma^) of keys k0..k0+7 for row n, split
-            const u32x4 nh = *reinterpret_cast<const u32x4*>(&wv.nrm[k0]);
-            u32x4 gh{};
-            if constexpr (QJL) gh = *reinterpret_cast<const u32x4*>(&wv.gam[k0]);
-            u32x4 wh, wl, gwh, gwl;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                float w2[2], g2[2];
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    const int k = 2 * q + e;
-                    const uint32_t sbits = sv[kb][k >> 2][k & 3];
-                    const float s = __builtin_bit_cast(float, sbits);
-                    const bool in = live && k0 + k < kleft;
-                    const float ex = in ? exp2_hw((s * a.scale - mrow) * kLog2e) : 0.0f;
-                    const uint32_t nn = e ? (nh[q] >> 16) : (nh[q] & 0xFFFFu);
-                    w2[e] = ex * h2f(nn);
-                    if constexpr (QJL) {
-                        const uint32_t gg = e ? (gh[q] >> 16) : (gh[q] & 0xFFFFu);
-                        g2[e] = w2[e] * h2f(gg);
-                    }
-                }
-                uint32_t h, lo;
-                if constexpr (CODES) {
-                    split_pair11(w2[0], w2[1], &h, &lo);
-                    wh[q] = h;
-                    wl[q] = lo;
-                }
-                if constexpr (QJL) {
-                    split_pair11(g2[0], g2[1], &h, &lo);
-                    gwh[q] = h;
-                    gwl[q] = lo;
-                }
+            // A operands: row n's weights of keys k0..k0+7 (zero past the live rows)
+            u32x4 wh{}, wl{};
+            if (live) {
+                wh = *reinterpret_cast<const u32x4*>(&wt.hi[n][8 * kb + 4 * hh]);
+                wl = *reinterpret_cast<const u32x4*>(&wt.lo[n][8 * kb + 4 * hh]);
             }
+            const u32x4 gwh = wh, gwl = wl;
             // centroid operands: coordinate 32 nt + n (nt < 4), pad slot (nt = 4)
 #pragma unroll
             for (int nt = 0; nt < (CODES ? (PAD ? 5 : 4) : 0); ++nt) {
@@ -377,7 +397,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CODES ? 2 :
     }
 
     // the block's partial rows: the four waves' sums are added in wave order
-    // through LDS, then written as producer blockIdx.x
+    // through LDS (over the weight tables, once every wave has left its tiles),
+    // then written as producer blockIdx.x
+    __syncthreads();
     const float uc = 1.0f / (2048.0f * sc), us = 1.0f / 2048.0f;
     for (int w = 0; w < 4; ++w) {
         if (wave == w) {
