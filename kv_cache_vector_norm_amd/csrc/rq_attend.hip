@@ -149,6 +149,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CODES ? 2 :
         // [514 + p]: 1,028 bytes apart, so no two-address LDS read fetches two of
         // them together and each lands in its own MFMA operand without moves
         uint32_t ptab[CODES ? 3 * 257 : 1];
+        float centf[PAD ? L : 1];      // the centroids (rotor pad slot, summed on the VALU)
         u32x4 sig[QJL ? 256 : 1][2];   // eight sign bits -> {+-1, +-2^11} half pairs (bit 2q + e: dword q, half e)
         Wave w[4];
         union {
@@ -182,6 +183,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CODES ? 2 :
             lds.ptab[514 + p] = hp;
         }
         for (int i = threadIdx.x; i < 4 * 64; i += kBlock) lds.w[i >> 6].code[W][i & 63] = 0u;
+        if constexpr (PAD) {
+            if (threadIdx.x < L) lds.centf[threadIdx.x] = a.cent[threadIdx.x];
+        }
     }
     if constexpr (QJL) {
         // sigma = 2 bit - 1 as half pairs; the sign bit is set where the stored bit is 0
@@ -213,13 +217,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CODES ? 2 :
 #pragma unroll
     for (int i = 0; i < 16; ++i) mrow[i] = i < ri ? a.stats[row0 + hh + 2 * i].x : 0.0f;
 
-    f32x16 acc_c[4], acc_p, acc_s[4];
+    f32x16 acc_c[4], acc_s[4];
+    // rotor pad slot: sum of p n^ c[code of slot 128] of rows hh + 2 i over this lane's keys
+    float padacc[PAD ? 16 : 1];
+#pragma unroll
+    for (int i = 0; i < (PAD ? 16 : 1); ++i) padacc[i] = 0.0f;
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
         acc_c[nt] = f32x16{};
         acc_s[nt] = f32x16{};
     }
-    acc_p = f32x16{};
 
     // One tile's inputs in registers: this lane's row of estimates (keys
     // 16 kb + 8 hh .. + 7 of each K block) and dword l of the tile's code,
@@ -305,6 +312,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CODES ? 2 :
             const float n0 = h2f(nn & 0xFFFFu), n1 = h2f(nn >> 16);
             const float ga = h2f(gg & 0xFFFFu), gb = h2f(gg >> 16);
             const bool in0 = 2 * n < kleft, in1 = 2 * n + 1 < kleft;
+            float cp0 = 0.0f, cp1 = 0.0f;   // centroids of the pad slot of keys 2 n, 2 n + 1
+            if constexpr (PAD) {
+                cp0 = lds.centf[wv.code[4 * B][2 * n] & (L - 1)];
+                cp1 = lds.centf[wv.code[4 * B][2 * n + 1] & (L - 1)];
+            }
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 if (i < ri) {
@@ -318,6 +330,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CODES ? 2 :
                         w0 = w0 * ga;
                         w1 = w1 * gb;
                     }
+                    if constexpr (PAD) padacc[i] = __builtin_fmaf(w1, cp1, __builtin_fmaf(w0, cp0, padacc[i]));
                     uint32_t h, lo;
                     split_pair11(w0, w1, &h, &lo);
                     wt.hi[hh + 2 * i][n] = h;
@@ -338,10 +351,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CODES ? 2 :
                 wl = *reinterpret_cast<const u32x4*>(&wt.lo[n][8 * kb + 4 * hh]);
             }
             const u32x4 gwh = wh, gwl = wl;
-            // centroid operands: coordinate 32 nt + n (nt < 4), pad slot (nt = 4)
+            // centroid operands: coordinate 32 nt + n
 #pragma unroll
-            for (int nt = 0; nt < (CODES ? (PAD ? 5 : 4) : 0); ++nt) {
-                const int coord = nt < 4 ? 32 * nt + n : 128;
+            for (int nt = 0; nt < (CODES ? 4 : 0); ++nt) {
+                const int coord = 32 * nt + n;
                 const int bit = B * coord, wi = bit >> 5, off = bit & 31;
                 const u32x4 w0a = *reinterpret_cast<const u32x4*>(&wv.code[wi][k0]);
                 const u32x4 w0b = *reinterpret_cast<const u32x4*>(&wv.code[wi][k0 + 4]);
@@ -366,12 +379,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CODES ? 2 :
                         }
                     }
                     const uint32_t ix = f[0] | (f[1] << B);
-                    const bool keep = nt < 4 || n == 0;
-                    b11[q] = keep ? lds.ptab[ix] : 0u;
-                    blo[q] = keep ? lds.ptab[257 + ix] : 0u;
-                    bhi[q] = keep ? lds.ptab[514 + ix] : 0u;
+                    b11[q] = lds.ptab[ix];
+                    blo[q] = lds.ptab[257 + ix];
+                    bhi[q] = lds.ptab[514 + ix];
                 }
-                f32x16& acc = nt < 4 ? acc_c[nt] : acc_p;
+                f32x16& acc = acc_c[nt];
                 acc = mfma(wh, b11, acc);
                 acc = mfma(wh, blo, acc);
                 acc = mfma(wl, bhi, acc);
@@ -400,6 +412,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CODES ? 2 :
     // through LDS (over the weight tables, once every wave has left its tiles),
     // then written as producer blockIdx.x
     __syncthreads();
+    // pad slot: this half-wave's 32 key pairs added in a fixed butterfly order
+    if constexpr (PAD) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+#pragma unroll
+            for (int off = 16; off >= 1; off >>= 1) padacc[i] += __shfl_xor(padacc[i], off);
+    }
     const float uc = 1.0f / (2048.0f * sc), us = 1.0f / 2048.0f;
     for (int w = 0; w < 4; ++w) {
         if (wave == w) {
@@ -419,8 +438,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CODES ? 2 :
                             dst[kPartSigma + 32 * nt + n] = w == 0 ? g : dst[kPartSigma + 32 * nt + n] + g;
                         }
                     }
-                    if (CODES && n == 0) {
-                        const float pc = PAD ? acc_p[r] * uc : 0.0f;
+                }
+            }
+            if (CODES && n == 0) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    if (i < ri) {
+                        float* dst = lds.sum[hh + 2 * i];
+                        float pc = 0.0f;
+                        if constexpr (PAD) pc = padacc[i];
                         dst[kPartPad] = w == 0 ? pc : dst[kPartPad] + pc;
                     }
                 }
