@@ -135,7 +135,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CODES ? 2 :
     constexpr int W = CODES ? (((PAD ? kRotCoords : kD) * B) + 31) / 32 : 1;
     constexpr int WTS = 36;   // weight-table row pitch (dwords): conflict-free 16-byte reads
     struct alignas(16) Wave {
-        uint32_t code[W + 1][64];   // [word][key]; one spare word row for the straddle read
+        uint32_t code[W + 1][68];   // [word][key] (rows 68 apart: lanes reading different words of
+                                    // the same keys hit different banks); a spare row for straddles
         uint32_t sign[4][64];
         alignas(16) uint16_t nrm[64];
         alignas(16) uint16_t gam[64];
@@ -145,10 +146,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CODES ? 2 :
         uint32_t lo[32][WTS];       // lo11 = half((w - hi) 2^11)
     };
     struct Lds {
-        // codes (k, k+1) -> 2^11 C_hi, C_lo and C_hi half pairs at [p], [257 + p],
-        // [514 + p]: 1,028 bytes apart, so no two-address LDS read fetches two of
-        // them together and each lands in its own MFMA operand without moves
-        uint32_t ptab[CODES ? 3 * 257 : 1];
+        // codes (k, k+1) -> C_lo and C_hi half pairs at [p] and [257 + p]: 1,028
+        // bytes apart, so no two-address LDS read fetches both together and
+        // each lands in its own MFMA operand without moves (2^11 C_hi is one
+        // packed multiply of C_hi)
+        uint32_t ptab[CODES ? 2 * 257 : 1];
         float centf[PAD ? L : 1];      // the centroids (rotor pad slot, summed on the VALU)
         u32x4 sig[QJL ? 256 : 1][2];   // eight sign bits -> {+-1, +-2^11} half pairs (bit 2q + e: dword q, half e)
         Wave w[4];
@@ -177,10 +179,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CODES ? 2 :
             uint32_t h0, l0, h1, l1;
             split_h11(a.cent[p & (L - 1)] * sc, &h0, &l0);
             split_h11(a.cent[p >> B] * sc, &h1, &l1);
-            const uint32_t hp = h0 | (h1 << 16);
-            lds.ptab[p] = pk_scale2048(hp);
-            lds.ptab[257 + p] = l0 | (l1 << 16);
-            lds.ptab[514 + p] = hp;
+            lds.ptab[p] = l0 | (l1 << 16);
+            lds.ptab[257 + p] = h0 | (h1 << 16);
         }
         for (int i = threadIdx.x; i < 4 * 64; i += kBlock) lds.w[i >> 6].code[W][i & 63] = 0u;
         if constexpr (PAD) {
@@ -351,42 +351,46 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CODES ? 2 :
                 wl = *reinterpret_cast<const u32x4*>(&wt.lo[n][8 * kb + 4 * hh]);
             }
             const u32x4 gwh = wh, gwl = wl;
-            // centroid operands: coordinate 32 nt + n
-#pragma unroll
-            for (int nt = 0; nt < (CODES ? 4 : 0); ++nt) {
-                const int coord = 32 * nt + n;
-                const int bit = B * coord, wi = bit >> 5, off = bit & 31;
+            // centroid operands: column n of N tile nt is coordinate 4 n + nt, so
+            // the lane's four coordinates share one field of 4 B bits per key,
+            // read once per K block
+            if constexpr (CODES) {
+                const int bit = 4 * B * n, wi = bit >> 5, off = bit & 31;
                 const u32x4 w0a = *reinterpret_cast<const u32x4*>(&wv.code[wi][k0]);
                 const u32x4 w0b = *reinterpret_cast<const u32x4*>(&wv.code[wi][k0 + 4]);
                 u32x4 w1a{}, w1b{};
-                if constexpr (32 % B != 0) {
+                if constexpr (32 % (4 * B) != 0) {
                     w1a = *reinterpret_cast<const u32x4*>(&wv.code[wi + 1][k0]);
                     w1b = *reinterpret_cast<const u32x4*>(&wv.code[wi + 1][k0 + 4]);
                 }
-                u32x4 b11, blo, bhi;
+                uint32_t fld[8];   // keys k0..k0+7: their codes of coordinates 4 n .. 4 n + 3 from bit 0
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    uint32_t f[2];
-#pragma unroll
-                    for (int e = 0; e < 2; ++e) {
-                        const int k = 2 * q + e;
-                        const uint32_t x0 = k < 4 ? w0a[k] : w0b[k - 4];
-                        if constexpr (32 % B != 0) {
-                            const uint32_t x1 = k < 4 ? w1a[k] : w1b[k - 4];
-                            f[e] = __builtin_amdgcn_alignbit(x1, x0, off) & (L - 1);
-                        } else {
-                            f[e] = (x0 >> off) & (L - 1);
-                        }
+                for (int k = 0; k < 8; ++k) {
+                    const uint32_t x0 = k < 4 ? w0a[k] : w0b[k - 4];
+                    if constexpr (32 % (4 * B) != 0) {
+                        const uint32_t x1 = k < 4 ? w1a[k] : w1b[k - 4];
+                        fld[k] = __builtin_amdgcn_alignbit(x1, x0, off);
+                    } else {
+                        fld[k] = x0 >> off;
                     }
-                    const uint32_t ix = f[0] | (f[1] << B);
-                    b11[q] = lds.ptab[ix];
-                    blo[q] = lds.ptab[257 + ix];
-                    bhi[q] = lds.ptab[514 + ix];
                 }
-                f32x16& acc = acc_c[nt];
-                acc = mfma(wh, b11, acc);
-                acc = mfma(wh, blo, acc);
-                acc = mfma(wl, bhi, acc);
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) {
+                    u32x4 b11, blo, bhi;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const uint32_t f0 = (fld[2 * q] >> (B * nt)) & (L - 1);
+                        const uint32_t f1 = (fld[2 * q + 1] >> (B * nt)) & (L - 1);
+                        const uint32_t ix = f0 | (f1 << B);
+                        const uint32_t hp = lds.ptab[257 + ix];
+                        blo[q] = lds.ptab[ix];
+                        bhi[q] = hp;
+                        b11[q] = pk_scale2048(hp);
+                    }
+                    acc_c[nt] = mfma(wh, b11, acc_c[nt]);
+                    acc_c[nt] = mfma(wh, blo, acc_c[nt]);
+                    acc_c[nt] = mfma(wl, bhi, acc_c[nt]);
+                }
             }
             if constexpr (QJL) {
                 // sign operands: index 32 nt + n, +-2^11 (hi) and +-1 (lo11)
@@ -431,7 +435,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CODES ? 2 :
                     for (int nt = 0; nt < 4; ++nt) {
                         if constexpr (CODES) {
                             const float c = acc_c[nt][r] * uc;
-                            dst[32 * nt + n] = w == 0 ? c : dst[32 * nt + n] + c;
+                            dst[4 * n + nt] = w == 0 ? c : dst[4 * n + nt] + c;
                         }
                         if constexpr (QJL) {
                             const float g = acc_s[nt][r] * us;
