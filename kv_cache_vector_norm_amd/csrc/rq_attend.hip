@@ -137,7 +137,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CODES ? 2 :
     struct alignas(16) Wave {
         uint32_t code[W + 1][68];   // [word][key] (rows 68 apart: lanes reading different words of
                                     // the same keys hit different banks); a spare row for straddles
-        uint32_t sign[4][64];
+        uint32_t sign[4][68];       // [word][key], rows padded like the code rows
         alignas(16) uint16_t nrm[64];
         alignas(16) uint16_t gam[64];
     };
@@ -152,7 +152,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CODES ? 2 :
         // packed multiply of C_hi)
         uint32_t ptab[CODES ? 2 * 257 : 1];
         float centf[PAD ? L : 1];      // the centroids (rotor pad slot, summed on the VALU)
-        u32x4 sig[QJL ? 256 : 1][2];   // eight sign bits -> {+-1, +-2^11} half pairs (bit 2q + e: dword q, half e)
+        // two keys' four sign bits (key a: bits 0..3, key b: bits 4..7) -> for
+        // each of the four bit positions nt, the +-1 half pair (sigma_a, sigma_b)
+        u32x4 sig[QJL ? 256 : 1];
         Wave w[4];
         union {
             WaveW wt[4];                  // tile loop: per-wave weight tables
@@ -190,16 +192,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CODES ? 2 :
     if constexpr (QJL) {
         // sigma = 2 bit - 1 as half pairs; the sign bit is set where the stored bit is 0
         for (int p = threadIdx.x; p < 256; p += kBlock) {
-            u32x4 s1, s11;
+            u32x4 e;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint32_t b0 = (p >> (2 * q)) & 1u, b1 = (p >> (2 * q + 1)) & 1u;
-                const uint32_t sgn = ((b0 ^ 1u) << 15) | ((b1 ^ 1u) << 31);
-                s1[q] = 0x3C003C00u | sgn;     // +-1
-                s11[q] = 0x68006800u | sgn;    // +-2^11
+            for (int nt = 0; nt < 4; ++nt) {
+                const uint32_t ba = (p >> nt) & 1u, bb = (p >> (4 + nt)) & 1u;
+                e[nt] = 0x3C003C00u | ((ba ^ 1u) << 15) | ((bb ^ 1u) << 31);
             }
-            lds.sig[p][0] = s1;
-            lds.sig[p][1] = s11;
+            lds.sig[p] = e;
         }
     }
     __syncthreads();
@@ -393,20 +392,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CODES ? 2 :
                 }
             }
             if constexpr (QJL) {
-                // sign operands: index 32 nt + n, +-2^11 (hi) and +-1 (lo11)
+                // sign operands: column n of N tile nt is sign index 4 n + nt, so
+                // each key's four bits of the lane lie in one nibble of one word;
+                // +-2^11 (hi) is a packed multiply of +-1 (lo11)
+                const u32x4 sa = *reinterpret_cast<const u32x4*>(&wv.sign[n >> 3][k0]);
+                const u32x4 sb = *reinterpret_cast<const u32x4*>(&wv.sign[n >> 3][k0 + 4]);
+                const int sh = 4 * (n & 7);
+                u32x4 s1[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t xa = q < 2 ? sa[2 * q] : sb[2 * q - 4];
+                    const uint32_t xb = q < 2 ? sa[2 * q + 1] : sb[2 * q - 3];
+                    const uint32_t pb = ((xa >> sh) & 0xFu) | (((xb >> sh) & 0xFu) << 4);
+                    const u32x4 e = lds.sig[pb];
+#pragma unroll
+                    for (int nt = 0; nt < 4; ++nt) {
+                        const uint32_t en = e[nt];
+                        s1[nt][q] = en;
+                    }
+                }
 #pragma unroll
                 for (int nt = 0; nt < 4; ++nt) {
-                    const u32x4 sa = *reinterpret_cast<const u32x4*>(&wv.sign[nt][k0]);
-                    const u32x4 sb = *reinterpret_cast<const u32x4*>(&wv.sign[nt][k0 + 4]);
-                    uint32_t byte = 0u;
+                    u32x4 s11;
 #pragma unroll
-                    for (int k = 0; k < 8; ++k) {
-                        const uint32_t x = k < 4 ? sa[k] : sb[k - 4];
-                        byte |= ((x >> n) & 1u) << k;
+                    for (int q = 0; q < 4; ++q) {
+                        const uint32_t v = s1[nt][q];
+                        s11[q] = pk_scale2048(v);
                     }
-                    const u32x4 s1 = lds.sig[byte][0], s11 = lds.sig[byte][1];
                     acc_s[nt] = mfma(gwh, s11, acc_s[nt]);
-                    acc_s[nt] = mfma(gwl, s1, acc_s[nt]);
+                    acc_s[nt] = mfma(gwl, s1[nt], acc_s[nt]);
                 }
             }
         }
@@ -439,7 +453,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CODES ? 2 :
                         }
                         if constexpr (QJL) {
                             const float g = acc_s[nt][r] * us;
-                            dst[kPartSigma + 32 * nt + n] = w == 0 ? g : dst[kPartSigma + 32 * nt + n] + g;
+                            dst[kPartSigma + 4 * n + nt] = w == 0 ? g : dst[kPartSigma + 4 * n + nt] + g;
                         }
                     }
                 }
