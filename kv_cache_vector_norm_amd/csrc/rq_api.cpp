@@ -85,6 +85,11 @@ struct rq_ctx {
     uint16_t* pi_lo = nullptr;
     uint16_t* pit_hi = nullptr;
     uint16_t* pit_lo = nullptr;
+    // dense codec kernels (two lanes per vector): Pi and Pi^T permuted
+    uint16_t* pi2_hi = nullptr;
+    uint16_t* pi2_lo = nullptr;
+    uint16_t* pit2_hi = nullptr;
+    uint16_t* pit2_lo = nullptr;
     // PolarQuant: fp32 Pi and the (cos, sin) table of its angle codebooks
     float* pi32 = nullptr;
     float* pq_tab = nullptr;
@@ -219,6 +224,7 @@ int rq_init(int d, int bits, uint64_t seed, int mode, rq_ctx** out) {
     };
     // derived half tables
     std::vector<uint16_t> s_cols, s_fwd, s_back, pi_hi, pi_lo, pit_hi, pit_lo, phi_hi, phi_lo;
+    std::vector<uint16_t> pi2_hi, pi2_lo, pit2_hi, pit2_lo;
     std::vector<float> pq_tab;
     const bool polar = mode & RQ_POLAR;
     const bool rotor = !(mode & (RQ_DENSE | RQ_POLAR));
@@ -270,14 +276,18 @@ int rq_init(int d, int bits, uint64_t seed, int mode, rq_ctx** out) {
                     s_back[p * n + k] = t.s[perm_k(k) * n + perm_row(p)];
                 }
         } else {
-            // Rotor codec kernels (two lanes per vector): local slot j of lane
-            // half h is coordinate 66 h + j, except that half 1's slots 62 and
-            // 63 stand for coordinates 64 and 65.  Accumulator element r of
+            // Codec kernels with two lanes per vector: local slot j of lane
+            // half h is coordinate 66 h + j for rotor sessions, except that
+            // half 1's slots 62 and 63 stand for coordinates 64 and 65.  Accumulator element r of
             // half h in M tile mt (row p = 8 (r / 4) + 4 h + r % 4) holds sign
             // index / coordinate slot 64 h + 16 mt + r / slot 16 mt + r; K
             // column 16 kb + 8 h + e takes slot 8 kb + e of half h (forward)
             // or sign index 64 h + 8 kb + e (back-projection).
-            auto slot_coord = [](int h, int j) { return h == 0 ? j : (j < 62 ? 66 + j : j + 2); };
+            // (dense sessions: slot j of half h is coordinate 64 h + j)
+            const bool dense_map = mode & RQ_DENSE;
+            auto slot_coord = [dense_map](int h, int j) {
+                return dense_map ? 64 * h + j : (h == 0 ? j : (j < 62 ? 66 + j : j + 2));
+            };
             auto row_half = [](int r) { return ((r & 31) >> 2) & 1; };
             auto row_elem = [](int r) { return (r >> 5) * 16 + 4 * ((r & 31) >> 3) + (r & 3); };
             auto col_half = [](int c) { return (c >> 3) & 1; };
@@ -331,6 +341,26 @@ int rq_init(int d, int bits, uint64_t seed, int mode, rq_ctx** out) {
                 pit_lo[c * n + r] = lo;
             }
     }
+    if (mode & RQ_DENSE) {
+        // The dense codec kernels' MFMA layouts (two lanes per vector, slot j
+        // of half h = coordinate 64 h + j): accumulator row r of M tile mt
+        // (lane half h = bit 2 of r % 32, element 4 (r % 32 / 8) + r % 4) is
+        // coordinate 64 h + 16 mt + element; K column c is slot 8 (c / 16) +
+        // c % 8 of half (c / 8) % 2.  pi2 = Pi, pit2 = Pi^T in that order.
+        auto row_coord = [](int r) { return 64 * (((r & 31) >> 2) & 1) + 16 * (r >> 5) + 4 * ((r & 31) >> 3) + (r & 3); };
+        auto col_coord = [](int c) { return 64 * ((c >> 3) & 1) + 8 * (c >> 4) + (c & 7); };
+        pi2_hi.resize(t.pi.size());
+        pi2_lo.resize(t.pi.size());
+        pit2_hi.resize(t.pi.size());
+        pit2_lo.resize(t.pi.size());
+        for (int r = 0; r < n; ++r)
+            for (int c = 0; c < n; ++c) {
+                split16(static_cast<double>(t.pi[row_coord(r) * n + col_coord(c)]), &pi2_hi[r * n + c],
+                        &pi2_lo[r * n + c]);
+                split16(static_cast<double>(t.pi[col_coord(c) * n + row_coord(r)]), &pit2_hi[r * n + c],
+                        &pit2_lo[r * n + c]);
+            }
+    }
     do {
         if (rotor) {
             if ((e = upload(reinterpret_cast<void**>(&ctx->rotmat), t.rotmats.data(), t.rotmats.size() * 4)) != hipSuccess) break;
@@ -357,6 +387,12 @@ int rq_init(int d, int bits, uint64_t seed, int mode, rq_ctx** out) {
             if ((e = upload(reinterpret_cast<void**>(&ctx->pi_lo), pi_lo.data(), pi_lo.size() * 2)) != hipSuccess) break;
             if ((e = upload(reinterpret_cast<void**>(&ctx->pit_hi), pit_hi.data(), pit_hi.size() * 2)) != hipSuccess) break;
             if ((e = upload(reinterpret_cast<void**>(&ctx->pit_lo), pit_lo.data(), pit_lo.size() * 2)) != hipSuccess) break;
+        }
+        if (mode & RQ_DENSE) {
+            if ((e = upload(reinterpret_cast<void**>(&ctx->pi2_hi), pi2_hi.data(), pi2_hi.size() * 2)) != hipSuccess) break;
+            if ((e = upload(reinterpret_cast<void**>(&ctx->pi2_lo), pi2_lo.data(), pi2_lo.size() * 2)) != hipSuccess) break;
+            if ((e = upload(reinterpret_cast<void**>(&ctx->pit2_hi), pit2_hi.data(), pit2_hi.size() * 2)) != hipSuccess) break;
+            if ((e = upload(reinterpret_cast<void**>(&ctx->pit2_lo), pit2_lo.data(), pit2_lo.size() * 2)) != hipSuccess) break;
         }
     } while (false);
     if (e != hipSuccess) {
@@ -438,6 +474,12 @@ static rqk::DenseTables dense_tables(const rq_ctx* c) {
     t.pi_lo = c->pi_lo;
     t.pit_hi = c->pit_hi;
     t.pit_lo = c->pit_lo;
+    t.pi2_hi = c->pi2_hi;
+    t.pi2_lo = c->pi2_lo;
+    t.pit2_hi = c->pit2_hi;
+    t.pit2_lo = c->pit2_lo;
+    t.s_fwd = c->s_fwd;
+    t.s_back = c->s_back;
     t.thr = c->thr;
     t.cent = c->cent;
     t.s_rows = c->s_rows;

@@ -8,6 +8,12 @@ struct DenseDev {
     const uint16_t* __restrict__ pi_lo;
     const uint16_t* __restrict__ pit_hi;
     const uint16_t* __restrict__ pit_lo;
+    const uint16_t* __restrict__ pi2_hi;
+    const uint16_t* __restrict__ pi2_lo;
+    const uint16_t* __restrict__ pit2_hi;
+    const uint16_t* __restrict__ pit2_lo;
+    const uint16_t* __restrict__ s_fwd;
+    const uint16_t* __restrict__ s_back;
     const float* __restrict__ thr;
     const float* __restrict__ cent;
     const uint16_t* __restrict__ s_rows;
@@ -32,6 +38,12 @@ static DenseDev make_dense(const DenseTables& t) {
     P.pi_lo = t.pi_lo;
     P.pit_hi = t.pit_hi;
     P.pit_lo = t.pit_lo;
+    P.pi2_hi = t.pi2_hi;
+    P.pi2_lo = t.pi2_lo;
+    P.pit2_hi = t.pit2_hi;
+    P.pit2_lo = t.pit2_lo;
+    P.s_fwd = t.s_fwd;
+    P.s_back = t.s_back;
     P.thr = t.thr;
     P.cent = t.cent;
     P.s_rows = t.s_rows;

@@ -1,5 +1,5 @@
 // One (bits, QJL) variant of the dense kernels per translation unit.
-#include "rq_dense_dev.h"
+#include "rq_dense_codec_dev.h"
 
 namespace rqk {
 template hipError_t launch_tq_quant<RQ_B, RQ_QJL>(const DenseDev&, const void*, bool, int64_t, int64_t, uint32_t*,

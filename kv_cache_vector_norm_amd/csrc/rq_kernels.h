@@ -42,6 +42,12 @@ struct DenseTables {
     const uint16_t* pi_lo;
     const uint16_t* pit_hi;  // transposed
     const uint16_t* pit_lo;
+    const uint16_t* pi2_hi;  // Pi and Pi^T permuted for the codec kernels' MFMA layout
+    const uint16_t* pi2_lo;
+    const uint16_t* pit2_hi;
+    const uint16_t* pit2_lo;
+    const uint16_t* s_fwd;   // S and S^T permuted likewise (sessions with an MSE stage)
+    const uint16_t* s_back;
     const float* thr;
     const float* cent;
     const uint16_t* s_rows;
