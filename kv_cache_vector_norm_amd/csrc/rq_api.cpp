@@ -90,6 +90,8 @@ struct rq_ctx {
     uint16_t* pi2_lo = nullptr;
     uint16_t* pit2_hi = nullptr;
     uint16_t* pit2_lo = nullptr;
+    uint16_t* t2_hi = nullptr;   // T = S Pi^T (sessions with QJL)
+    uint16_t* t2_lo = nullptr;
     // PolarQuant: fp32 Pi and the (cos, sin) table of its angle codebooks
     float* pi32 = nullptr;
     float* pq_tab = nullptr;
@@ -224,19 +226,37 @@ int rq_init(int d, int bits, uint64_t seed, int mode, rq_ctx** out) {
     };
     // derived half tables
     std::vector<uint16_t> s_cols, s_fwd, s_back, pi_hi, pi_lo, pit_hi, pit_lo, phi_hi, phi_lo;
-    std::vector<uint16_t> pi2_hi, pi2_lo, pit2_hi, pit2_lo;
+    std::vector<uint16_t> pi2_hi, pi2_lo, pit2_hi, pit2_lo, t2_hi, t2_lo;
     std::vector<float> pq_tab;
     const bool polar = mode & RQ_POLAR;
     const bool rotor = !(mode & (RQ_DENSE | RQ_POLAR));
-    // exact-enough half pair of 16 v: hi = half(16 v), lo = half((16 v - hi) * 2^11)
-    auto split16 = [](double v, uint16_t* hi, uint16_t* lo) {
-        const double x = v * 16.0;
-        const uint16_t h = rqh::double_to_half_rne(x);
+    auto half_value = [](uint16_t h) {
         const int ex = (h >> 10) & 0x1F, mant = h & 0x3FF;
-        double hv = ex == 0 ? std::ldexp(static_cast<double>(mant), -24) : std::ldexp(1.0 + mant / 1024.0, ex - 15);
-        if (h & 0x8000) hv = -hv;
+        const double v = ex == 0 ? std::ldexp(static_cast<double>(mant), -24) : std::ldexp(1.0 + mant / 1024.0, ex - 15);
+        return (h & 0x8000) ? -v : v;
+    };
+    // exact-enough half pair of s v: hi = half(s v), lo = half((s v - hi) * 2^11)
+    auto split_scaled = [half_value](double v, double s, uint16_t* hi, uint16_t* lo) {
+        const double x = v * s;
+        const uint16_t h = rqh::double_to_half_rne(x);
         *hi = h;
-        *lo = rqh::double_to_half_rne((x - hv) * 2048.0);
+        *lo = rqh::double_to_half_rne((x - half_value(h)) * 2048.0);
+    };
+    auto split16 = [split_scaled](double v, uint16_t* hi, uint16_t* lo) { split_scaled(v, 16.0, hi, lo); };
+    // The dense codec kernels read the matrices they do not stage in LDS in
+    // MFMA fragment order: the 16 bytes that lane l takes as the A operand of
+    // M tile mt and K block kb (row 32 mt + l % 32, columns 16 kb + 8 (l / 32)
+    // .. + 7 of the permuted matrix) sit at ((mt * 8 + kb) * 64 + l) * 16, so
+    // one wave's fragment is one contiguous kilobyte.
+    auto frag_order = [n](const std::vector<uint16_t>& m) {
+        std::vector<uint16_t> f(m.size());
+        for (int mt = 0; mt < n / 32; ++mt)
+            for (int kb = 0; kb < n / 16; ++kb)
+                for (int l = 0; l < 64; ++l)
+                    for (int e = 0; e < 8; ++e)
+                        f[((static_cast<size_t>(mt) * (n / 16) + kb) * 64 + l) * 8 + e] =
+                            m[static_cast<size_t>(32 * mt + (l & 31)) * n + 16 * kb + 8 * (l >> 5) + e];
+        return f;
     };
     std::vector<float> rotmat16;
     if (rotor) {
@@ -301,6 +321,32 @@ int rq_init(int d, int bits, uint64_t seed, int mode, rq_ctx** out) {
                     s_fwd[r * n + c] = t.s[sign_row * n + coord_col];
                     s_back[r * n + c] = t.s[sign_col * n + coord_row];
                 }
+            if (dense_map) {
+                // The dense kernels form S r as T (y - y^) with T = S Pi^T
+                // (r = Pi^T (y - y^) for orthogonal Pi), in the same permuted
+                // order as s_fwd with y coordinates for x coordinates; T is
+                // an exact-enough half pair T = hi + 2^-11 lo.  S^T is read
+                // in fragment order; s_fwd itself is not needed.
+                std::vector<double> tm(static_cast<size_t>(n) * n, 0.0);
+                for (int i = 0; i < n; ++i)
+                    for (int j = 0; j < n; ++j) {
+                        double acc = 0.0;
+                        for (int k = 0; k < n; ++k)
+                            acc += half_value(t.s[i * n + k]) * static_cast<double>(t.pi[j * n + k]);
+                        tm[static_cast<size_t>(i) * n + j] = acc;
+                    }
+                t2_hi.resize(t.s.size());
+                t2_lo.resize(t.s.size());
+                for (int r = 0; r < n; ++r)
+                    for (int c = 0; c < n; ++c)
+                        split_scaled(tm[static_cast<size_t>(64 * row_half(r) + row_elem(r)) * n +
+                                        slot_coord(col_half(c), col_slot(c))],
+                                     1.0, &t2_hi[r * n + c], &t2_lo[r * n + c]);
+                t2_hi = frag_order(t2_hi);
+                t2_lo = frag_order(t2_lo);
+                s_back = frag_order(s_back);
+                s_fwd.clear();
+            }
         }
     }
     if (polar) {
@@ -346,7 +392,8 @@ int rq_init(int d, int bits, uint64_t seed, int mode, rq_ctx** out) {
         // of half h = coordinate 64 h + j): accumulator row r of M tile mt
         // (lane half h = bit 2 of r % 32, element 4 (r % 32 / 8) + r % 4) is
         // coordinate 64 h + 16 mt + element; K column c is slot 8 (c / 16) +
-        // c % 8 of half (c / 8) % 2.  pi2 = Pi, pit2 = Pi^T in that order.
+        // c % 8 of half (c / 8) % 2.  pi2 = Pi, pit2 = Pi^T in that order (pit2 in
+        // fragment order; pi2 is staged in LDS row by row).
         auto row_coord = [](int r) { return 64 * (((r & 31) >> 2) & 1) + 16 * (r >> 5) + 4 * ((r & 31) >> 3) + (r & 3); };
         auto col_coord = [](int c) { return 64 * ((c >> 3) & 1) + 8 * (c >> 4) + (c & 7); };
         pi2_hi.resize(t.pi.size());
@@ -360,6 +407,8 @@ int rq_init(int d, int bits, uint64_t seed, int mode, rq_ctx** out) {
                 split16(static_cast<double>(t.pi[col_coord(c) * n + row_coord(r)]), &pit2_hi[r * n + c],
                         &pit2_lo[r * n + c]);
             }
+        pit2_hi = frag_order(pit2_hi);
+        pit2_lo = frag_order(pit2_lo);
     }
     do {
         if (rotor) {
@@ -393,6 +442,8 @@ int rq_init(int d, int bits, uint64_t seed, int mode, rq_ctx** out) {
             if ((e = upload(reinterpret_cast<void**>(&ctx->pi2_lo), pi2_lo.data(), pi2_lo.size() * 2)) != hipSuccess) break;
             if ((e = upload(reinterpret_cast<void**>(&ctx->pit2_hi), pit2_hi.data(), pit2_hi.size() * 2)) != hipSuccess) break;
             if ((e = upload(reinterpret_cast<void**>(&ctx->pit2_lo), pit2_lo.data(), pit2_lo.size() * 2)) != hipSuccess) break;
+            if ((e = upload(reinterpret_cast<void**>(&ctx->t2_hi), t2_hi.data(), t2_hi.size() * 2)) != hipSuccess) break;
+            if ((e = upload(reinterpret_cast<void**>(&ctx->t2_lo), t2_lo.data(), t2_lo.size() * 2)) != hipSuccess) break;
         }
     } while (false);
     if (e != hipSuccess) {
@@ -478,7 +529,8 @@ static rqk::DenseTables dense_tables(const rq_ctx* c) {
     t.pi2_lo = c->pi2_lo;
     t.pit2_hi = c->pit2_hi;
     t.pit2_lo = c->pit2_lo;
-    t.s_fwd = c->s_fwd;
+    t.t2_hi = c->t2_hi;
+    t.t2_lo = c->t2_lo;
     t.s_back = c->s_back;
     t.thr = c->thr;
     t.cent = c->cent;

@@ -1,27 +1,7 @@
 // Dispatch of dense-session (TurboQuant) calls to the (bits, QJL) variants.
-#include "rq_kernels.h"
+#include "rq_dense_dev.h"
 
 namespace rqk {
-
-struct DenseDev {
-    const uint16_t* __restrict__ pi_hi;
-    const uint16_t* __restrict__ pi_lo;
-    const uint16_t* __restrict__ pit_hi;
-    const uint16_t* __restrict__ pit_lo;
-    const uint16_t* __restrict__ pi2_hi;
-    const uint16_t* __restrict__ pi2_lo;
-    const uint16_t* __restrict__ pit2_hi;
-    const uint16_t* __restrict__ pit2_lo;
-    const uint16_t* __restrict__ s_fwd;
-    const uint16_t* __restrict__ s_back;
-    const float* __restrict__ thr;
-    const float* __restrict__ cent;
-    const uint16_t* __restrict__ s_rows;
-    const uint16_t* __restrict__ s_cols;
-    const u32x4_t* __restrict__ bins;
-    float bin_a, bin_b;
-    float qjl_scale;
-};
 
 template <int B, bool QJL>
 hipError_t launch_tq_quant(const DenseDev& P, const void* x, bool in_f16, int64_t ldx_bytes, int64_t n,
@@ -42,7 +22,8 @@ static DenseDev make_dense(const DenseTables& t) {
     P.pi2_lo = t.pi2_lo;
     P.pit2_hi = t.pit2_hi;
     P.pit2_lo = t.pit2_lo;
-    P.s_fwd = t.s_fwd;
+    P.t2_hi = t.t2_hi;
+    P.t2_lo = t.t2_lo;
     P.s_back = t.s_back;
     P.thr = t.thr;
     P.cent = t.cent;

@@ -8,20 +8,26 @@
 // v, lane half h holding coordinates 64 h .. 64 h + 63 (its 64 slots).  Every
 // contraction is a 32x32x16 MFMA over the tile (N = the 32 vectors) whose
 // two 8-element K halves are the two lane halves: K block kb is slots
-// 8 kb .. 8 kb + 7 of both halves.  Pi, Pi^T, S and S^T are permuted on the
+// 8 kb .. 8 kb + 7 of both halves.  Pi, Pi^T, T and S^T are permuted on the
 // host so that accumulator element r of M tile mt in half h is slot
-// 16 mt + r of that half, so operands and results never leave their lane
-// (the one-lane design moved every operand and result across lanes).  The
-// record's 4 B code words split evenly too: half h packs its 64 codes into
-// record words 2 B h .. 2 B h + 2 B - 1.
+// 16 mt + r of that half, so operands and results never leave their lane.
+// The record's 4 B code words split evenly too: half h packs its 64 codes
+// into record words 2 B h .. 2 B h + 2 B - 1.
 //
-// Precision (as the one-lane design): 16 Pi = P_hi + 2^-11 P_lo and
-// 16 v = v_hi + 2^-11 v_lo as exact half pairs, three products folded into
-// one fp32 accumulator, P_hi (2^11 v_hi) + P_hi v_lo + P_lo v_hi =
-// 2^19 (Pi v) + O(2^-22); codes from the rotor path's exact slot table with
-// thresholds scaled by 2^19; the residual r enters S r as an exact hi + lo
-// pair (S is exactly half).  Pi sits in LDS (the quantize side); Pi^T, S and
-// S^T are read from L2.
+// QJL stage.  The sign sketch of the residual r = x_u - Pi^T y^ is formed in
+// the rotated domain: S r = T (y - y^) with T = S Pi^T (host, float64), and
+// gamma = |r| = |y - y^| (Pi orthogonal).  So the quantiser never forms
+// Pi^T y^; only a reconstruction (roundtrip, dequantiser) does.
+//
+// Precision: 16 Pi = P_hi + 2^-11 P_lo and 16 v = v_hi + 2^-11 v_lo as exact
+// half pairs, three products folded into one fp32 accumulator,
+// P_hi (2^11 v_hi) + P_hi v_lo + P_lo v_hi = 2^19 (Pi v) + O(2^-22); codes
+// from the rotor path's exact slot table with thresholds scaled by 2^19; T
+// and 8 (y - y^) enter T (y - y^) as pairs the same way (T unscaled).
+//
+// Operands.  Pi sits in LDS (the quantiser); Pi^T, T and S^T are read from
+// L2 in fragment order (one contiguous kilobyte per wave and fragment), the
+// fragments of K block kb + 1 requested before the products of K block kb.
 #pragma once
 
 #include "rq_dense_dev.h"
@@ -32,10 +38,11 @@ namespace rqk {
 
 constexpr int kDenseSlots = 64;
 
-template <bool F16>
-constexpr int dense_half_bytes() { return F16 ? 128 : 256; }
-
 // The lane's 64 input slots.
+// The lane's 64 input slots from the DMA-filled tile (rows of 256 / 512
+// bytes, chunk c of row v at position c ^ (v & 15); lane half h reads chunks
+// 8 h .. (fp16) or 16 h .. (fp32) of its row, 16 rows of a half-wave on 16
+// distinct bank groups).
 template <bool IN_F16>
 struct DSlots;
 
@@ -43,18 +50,16 @@ template <>
 struct DSlots<true> {
     uint32_t w[kDenseSlots / 2];
     __device__ void read(const char* tile, int vi, int h) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(tile + vi * row_bytes2<true>() + dense_half_bytes<true>() * h);
-        wave_lds_sync();
+        const char* row = tile + vi * 256;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const u32x4 q = p[c];
+        for (int k = 0; k < 8; ++k) {
+            const u32x4 q = *reinterpret_cast<const u32x4*>(row + 16 * ((8 * h + k) ^ (vi & 15)));
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const uint32_t x = q[e];
-                w[4 * c + e] = x;
+                w[4 * k + e] = x;
             }
         }
-        wave_lds_sync();
     }
     __device__ float get(int j) const { return h2f((j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xFFFFu)); }
 };
@@ -63,40 +68,149 @@ template <>
 struct DSlots<false> {
     float v[kDenseSlots];
     __device__ void read(const char* tile, int vi, int h) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(tile + vi * row_bytes2<false>() + dense_half_bytes<false>() * h);
-        wave_lds_sync();
+        const char* row = tile + vi * 512;
 #pragma unroll
-        for (int c = 0; c < 16; ++c) {
-            const u32x4 q = p[c];
+        for (int k = 0; k < 16; ++k) {
+            const u32x4 q = *reinterpret_cast<const u32x4*>(row + 16 * ((16 * h + k) ^ (vi & 15)));
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const uint32_t x = q[e];
-                v[4 * c + e] = __builtin_bit_cast(float, x);
+                v[4 * k + e] = __builtin_bit_cast(float, x);
             }
         }
-        wave_lds_sync();
     }
     __device__ float get(int j) const { return v[j]; }
 };
+
+// mat_to_lds of 2^11 times a half matrix (exact: |2^11 P_hi| < 2^14).
+template <int NT>
+__device__ __forceinline__ void mat_to_lds_x2048(const uint16_t* __restrict__ g, u32x4* __restrict__ m) {
+    static_assert(128 * 16 % NT == 0, "block size");
+    const u32x4* src = reinterpret_cast<const u32x4*>(g);
+    constexpr f16x2 k2048 = {static_cast<f16>(2048.0f), static_cast<f16>(2048.0f)};
+    u32x4 v[128 * 16 / NT];
+#pragma unroll
+    for (int it = 0; it < 128 * 16 / NT; ++it) v[it] = src[it * NT + threadIdx.x];
+#pragma unroll
+    for (int it = 0; it < 128 * 16 / NT; ++it) {
+        const int q = it * NT + threadIdx.x, row = q >> 4, c = q & 15;
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t x = v[it][e];
+            w[e] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, x) * k2048);
+        }
+        m[row * 16 + (c ^ (row & 15))] = w;
+    }
+}
 
 // Operands of K block kb from the 8 split slots (half pairs): 2^11 hi, lo, hi.
 struct Split8 {
     u32x4 h11, lo, hi;
 };
 
-// acc[mt] += the product of the permuted matrix (A fragments fa_hi, fa_lo)
-// with the three split operands of K block kb, for all four M tiles.
-template <class FragHi, class FragLo>
-__device__ __forceinline__ void dense_kblock(f32x16 (&acc)[4], const Split8& s, int kb, FragHi fa_hi, FragLo fa_lo,
-                                             int l, int h) {
+// Splits of 8 values into the three operands (split16: 16 v = hi + 2^-11 lo).
+template <class Val>
+__device__ __forceinline__ Split8 split8(Val val) {
+    Split8 s;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-        const int row = 32 * mt + (l & 31), chunk = 2 * kb + h;
-        const u32x4 ph = fa_hi(row, chunk);
-        const u32x4 pl = fa_lo(row, chunk);
-        acc[mt] = mfma(ph, s.h11, acc[mt]);
-        acc[mt] = mfma(ph, s.lo, acc[mt]);
-        acc[mt] = mfma(pl, s.hi, acc[mt]);
+    for (int q = 0; q < 4; ++q) {
+        uint32_t a0, b0, c0, a1, b1, c1;
+        split16(val(2 * q), &a0, &b0, &c0);
+        split16(val(2 * q + 1), &a1, &b1, &c1);
+        s.h11[q] = a0 | (a1 << 16);
+        s.hi[q] = b0 | (b1 << 16);
+        s.lo[q] = c0 | (c1 << 16);
+    }
+    return s;
+}
+
+// The three products of one K block for the four M tiles, M tiles innermost
+// (four independent accumulators between dependent MFMAs); per accumulator
+// the order is always 2^11 hi, lo, hi.
+__device__ __forceinline__ void kblock3(f32x16 (&acc)[4], const Split8& s, const u32x4 (&fh)[4],
+                                        const u32x4 (&fl)[4]) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) acc[mt] = mfma(fh[mt], s.h11, acc[mt]);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) acc[mt] = mfma(fh[mt], s.lo, acc[mt]);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) acc[mt] = mfma(fl[mt], s.hi, acc[mt]);
+}
+
+// A fragment-ordered 128 x 128 half matrix in global memory.
+constexpr int kFragMatBytes = 128 * 128 * 2;
+__device__ __forceinline__ u32x4 gfrag(rsrc_t rs, uint32_t voff, int mt, int kb) {
+    return __builtin_amdgcn_raw_buffer_load_b128(rs, voff, (mt * 8 + kb) * 1024, 0);
+}
+
+// The hi and lo fragments of one K block (all four M tiles) of a
+// fragment-ordered pair, and the fragments of one K block of a single
+// matrix.
+struct Frag8 {
+    u32x4 h[4], l[4];
+};
+struct Frag4 {
+    u32x4 f[4];
+};
+struct GPair {
+    rsrc_t hi, lo;
+    uint32_t vo;
+    __device__ GPair(const uint16_t* mh, const uint16_t* ml, int l)
+        : hi(make_rsrc(mh, kFragMatBytes)), lo(make_rsrc(ml, kFragMatBytes)), vo(16u * static_cast<uint32_t>(l)) {}
+    __device__ Frag8 load(int kb) const {
+        Frag8 f;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            f.h[mt] = gfrag(hi, vo, mt, kb);
+            f.l[mt] = gfrag(lo, vo, mt, kb);
+        }
+        return f;
+    }
+};
+struct GOne {
+    rsrc_t m;
+    uint32_t vo;
+    __device__ GOne(const uint16_t* p, int l) : m(make_rsrc(p, kFragMatBytes)), vo(16u * static_cast<uint32_t>(l)) {}
+    __device__ Frag4 load(int kb) const {
+        Frag4 f;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) f.f[mt] = gfrag(m, vo, mt, kb);
+        return f;
+    }
+};
+
+// acc[mt] = sum over K blocks of (hi, lo matrix pair) x make(kb); `first`
+// holds K block 0's fragments (requested by the caller as early as it can),
+// later K blocks are requested one K block ahead.
+template <class Make>
+__device__ __forceinline__ void gprod3(f32x16 (&acc)[4], const GPair& g, const Frag8& first, Make make) {
+    Frag8 f[2];
+    f[0] = first;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x16{};
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+        const int cur = kb & 1;
+        if (kb < 7) f[cur ^ 1] = g.load(kb + 1);
+        kblock3(acc, make(kb), f[cur].h, f[cur].l);
+    }
+}
+
+// acc[mt] = sum over K blocks of (exact half matrix) x make(kb), likewise.
+template <class Make>
+__device__ __forceinline__ void gprod1(f32x16 (&acc)[4], const GOne& g, const Frag4& first, Make make) {
+    Frag4 f[2];
+    f[0] = first;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x16{};
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+        const int cur = kb & 1;
+        if (kb < 7) f[cur ^ 1] = g.load(kb + 1);
+        const u32x4 b = make(kb);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) acc[mt] = mfma(f[cur].f[mt], b, acc[mt]);
     }
 }
 
@@ -104,13 +218,10 @@ __device__ __forceinline__ void dense_kblock(f32x16 (&acc)[4], const Split8& s, 
 // centroids of the lane's codes; the same sequence in the quantiser's
 // roundtrip and in the dequantiser.
 template <int B>
-__device__ __forceinline__ void dense_pit2(const DenseDev& P, const uint32_t* __restrict__ ctab,
-                                           const uint32_t (&cw)[2 * B], f32x16 (&ax)[4], int l, int h) {
+__device__ __forceinline__ void dense_pit2(const GPair& g, const Frag8& first, const uint32_t* __restrict__ ctab,
+                                           const uint32_t (&cw)[2 * B], f32x16 (&ax)[4]) {
     constexpr int L = 1 << B;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) ax[mt] = f32x16{};
-#pragma unroll
-    for (int kb = 0; kb < 8; ++kb) {
+    gprod3(ax, g, first, [&](int kb) {
         Split8 s;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -122,58 +233,70 @@ __device__ __forceinline__ void dense_pit2(const DenseDev& P, const uint32_t* __
             s.h11[q] = (e0 >> 16) | (e1 & 0xFFFF0000u);
             s.lo[q] = o0 | (o1 << 16);
         }
-        dense_kblock(
-            ax, s, kb, [&](int row, int chunk) { return gmat_frag(P.pit2_hi, row, chunk); },
-            [&](int row, int chunk) { return gmat_frag(P.pit2_lo, row, chunk); }, l, h);
-    }
+        return s;
+    });
 }
 
 // S^T sigma of the lane's slots from its two sign words (sign indices
-// 64 h .. 64 h + 63); the same sequence in the roundtrip and the dequantiser.
-__device__ __forceinline__ void dense_back2(const DenseDev& P, uint32_t sw0, uint32_t sw1, f32x16 (&acc)[4], int l,
-                                            int h) {
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x16{};
-    // K blocks in order, their +-1 operands formed two at a time
-#pragma unroll
-    for (int kp = 0; kp < 4; ++kp) {
-        u32x4 sig[2];
-        const uint32_t w = kp < 2 ? sw0 : sw1;
-        sigma16((w >> (16 * (kp & 1))) & 0xFFFFu, sig[0], sig[1]);
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-                acc[mt] = mfma(gmat_frag(P.s_back, 32 * mt + (l & 31), 2 * (2 * kp + c) + h), sig[c], acc[mt]);
-    }
+// 64 h .. 64 h + 63; K block kb takes bits 8 kb .. 8 kb + 7); the same
+// sequence in the roundtrip and the dequantiser.
+__device__ __forceinline__ void dense_back2(const GOne& g, const Frag4& first, uint32_t sw0, uint32_t sw1,
+                                            f32x16 (&acc)[4]) {
+    gprod1(acc, g, first, [&](int kb) {
+        const uint32_t w = kb < 4 ? sw0 : sw1;
+        u32x4 d0, d1;
+        sigma16((w >> (16 * ((kb >> 1) & 1))) & 0xFFFFu, d0, d1);
+        return (kb & 1) ? d1 : d0;
+    });
 }
 
-// Output slots of the lane: n^ x~ (MSE) or n^ (x~ + k (S^T sigma)) (QJL),
-// x~ = ax * kRotScale, as pairs into the lane's part of its LDS row.
+// Output slots of the lane, n^ x~ (MSE) or n^ (x~ + k (S^T sigma)) (QJL) with
+// x~ = ax * kRotScale, stored straight from registers: the lane's 64 slots
+// are coordinates 64 h .. 64 h + 63 of row vi, 128 (fp16) or 256 (fp32)
+// contiguous bytes.  Rows at or beyond n are not written.  fp16 output is
+// the rounding of the materialised fp32 value.  The stores are ordinary
+// (cached) ones: L2 merges a lane's 16-byte pieces into whole lines, where
+// non-temporal stores of partial lines cost several times more.
 template <bool QJL, bool OUT_F16>
-__device__ __forceinline__ void dense_out2(const f32x16 (&ax)[4], const f32x16 (&aq)[4], float k, float nhat,
-                                           char* rowo) {
+__device__ __forceinline__ void dense_out_store(const f32x16 (&ax)[4], const f32x16 (&aq)[4], float k, float nhat,
+                                                char* __restrict__ y, int64_t ldy_bytes, int64_t base, int64_t n,
+                                                int vi, int h) {
+    const rsrc_t rs = make_rsrc(y + base * ldy_bytes, tile2_range(n - base, ldy_bytes));
+    const uint32_t voff = static_cast<uint32_t>(vi) * static_cast<uint32_t>(ldy_bytes) +
+                          static_cast<uint32_t>((OUT_F16 ? 128 : 256) * h);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-        float xv[16], qv[16];
+        float o[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const float e = ax[mt][r];
-            xv[r] = e * kRotScale;
+            float v = e * kRotScale;
             if constexpr (QJL) {
                 const float f = aq[mt][r];
-                qv[r] = f;
+                v = __builtin_fmaf(k, f, v);
             }
+            o[r] = nhat * v;
         }
+        constexpr int NC = OUT_F16 ? 2 : 4;   // 16-byte chunks of this M tile
+        u32x4 w[NC];
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-            float v0 = xv[r], v1 = xv[r + 1];
-            if constexpr (QJL) {
-                v0 = __builtin_fmaf(k, qv[r], v0);
-                v1 = __builtin_fmaf(k, qv[r + 1], v1);
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if constexpr (OUT_F16) {
+                    float a = o[8 * c + 2 * q], b = o[8 * c + 2 * q + 1];
+                    pin(a);
+                    pin(b);
+                    w[c][q] = cvt_pk(a, b);
+                } else {
+                    w[c][q] = __builtin_bit_cast(uint32_t, o[4 * c + q]);
+                }
             }
-            out_pair<OUT_F16>(rowo, (16 * mt + r) >> 1, nhat * v0, nhat * v1);
-        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+            __builtin_amdgcn_raw_buffer_store_b128(w[c], rs, voff, 16 * (NC * mt + c), 0);
+        store_data_fence();
     }
 }
 
@@ -189,15 +312,16 @@ __global__ __launch_bounds__(64 * WAVES) void tq_quant_kernel(DenseDev P, const 
     constexpr int LW = 2 * B;   // record words of one lane half
     constexpr int W = 4 * B;    // record words per vector
     constexpr int NT = 64 * WAVES;
-    constexpr int RBI = row_bytes2<IN_F16>(), RBO = row_bytes2<OUT_F16>();
-    constexpr int TB = 32 * (RBI > RBO ? RBI : RBO);
+    constexpr int TB = 32 * (IN_F16 ? 256 : 512);   // input tile (LDS DMA)
     constexpr int SW = 32 * W > 128 ? 32 * W : 128;
+    // The input tiles come first: the copies address them below 64 KB.
+    static_assert(WAVES * TB <= 65536, "input tiles must lie in the first 64 KB of LDS");
     struct Lds {
-        u32x4 bins[kBinSlots];      // slot table (LDS address 0), thresholds and centroids times 2^19
-        u32x4 pih[128 * 16];
+        u32x4 tiles[WAVES][TB / 16];
+        u32x4 bins[kBinSlots];      // slot table, thresholds and centroids times 2^19
+        u32x4 pih[128 * 16];       // P_hi, or 2^11 P_hi for fp16 input
         u32x4 pil[128 * 16];
         uint32_t ctab[32];
-        u32x4 tiles[WAVES][TB / 16];
         uint32_t stage[WAVES][SW];
     };
     __shared__ Lds lds;
@@ -206,18 +330,16 @@ __global__ __launch_bounds__(64 * WAVES) void tq_quant_kernel(DenseDev P, const 
     const int64_t ntiles = (n + 31) / 32;
     const int64_t tstep = static_cast<int64_t>(gridDim.x) * WAVES;
     const int64_t t0 = static_cast<int64_t>(blockIdx.x) * WAVES + wave;
-    Tile2Regs<true> nx;
-    if constexpr (IN_F16) {
-        if (t0 < ntiles) tile2_fetch<true>(x, ldx_bytes, t0 * 32, n, nx, lane_id());
-    }
+    char* tile = reinterpret_cast<char*>(lds.tiles[wave]);
+    if (t0 < ntiles) tile2_dma<IN_F16>(x, ldx_bytes, t0 * 32, n, tile, lane_id());
     dense_tables_to_lds<B>(P, lds.ctab);
     dense_bins_to_lds(P, lds.bins);
-    mat_to_lds<NT>(P.pi2_hi, lds.pih);
+    if constexpr (IN_F16) mat_to_lds_x2048<NT>(P.pi2_hi, lds.pih);   // 2^11 P_hi
+    else mat_to_lds<NT>(P.pi2_hi, lds.pih);
     mat_to_lds<NT>(P.pi2_lo, lds.pil);
     __syncthreads();
     const float ba = P.bin_a * kRotScale, bb = P.bin_b;
     const char* binc = reinterpret_cast<const char*>(lds.bins);
-    char* tile = reinterpret_cast<char*>(lds.tiles[wave]);
     uint32_t* stw = lds.stage[wave];
 
     for (int64_t t = t0; t < ntiles; t += tstep) {
@@ -225,22 +347,25 @@ __global__ __launch_bounds__(64 * WAVES) void tq_quant_kernel(DenseDev P, const 
         const int z = opaque_zero();
         const int l = lane_id() + z;
         const int h = l >> 5, vi = l & 31;
+        // this tile's input, then the next tile's copy into the same buffer
         DSlots<IN_F16> in;
-        if constexpr (IN_F16) {
-            tile2_put<true>(nx, tile, l);
-            in.read(tile, vi, h);
-            if (t + tstep < ntiles) tile2_fetch<true>(x, ldx_bytes, (t + tstep) * 32, n, nx, l);
-        } else {
-            Tile2Regs<false> r;
-            tile2_fetch<false>(x, ldx_bytes, base, n, r, l);
-            tile2_put<false>(r, tile, l);
-            in.read(tile, vi, h);
-        }
+        tile2_dma_wait();
+        in.read(tile, vi, h);
+        lds_reads_done();
+        if (t + tstep < ntiles) tile2_dma<IN_F16>(x, ldx_bytes, (t + tstep) * 32, n, tile, l);
         float ss = 0.0f;
+        if constexpr (IN_F16) {
 #pragma unroll
-        for (int j = 0; j < kDenseSlots; ++j) {
-            const float v = in.get(j);
-            ss = __builtin_fmaf(v, v, ss);
+            for (int k = 0; k < kDenseSlots / 2; ++k) {
+                const f16x2 v = __builtin_bit_cast(f16x2, in.w[k]);
+                ss = __builtin_amdgcn_fdot2(v, v, ss, false);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < kDenseSlots; ++j) {
+                const float v = in.get(j);
+                ss = __builtin_fmaf(v, v, ss);
+            }
         }
         ss = ss + other_half(ss, h);
         const float nrm = __builtin_sqrtf(ss);
@@ -248,26 +373,39 @@ __global__ __launch_bounds__(64 * WAVES) void tq_quant_kernel(DenseDev P, const 
         const uint32_t nh = f2h(nrm);
         const float nhat = h2f(nh);
 
-        // y = Pi x_u, K blocks outermost
+        // y = Pi x_u, Pi from LDS.  fp16 input enters the MFMAs as it is
+        // (exact): (2^11 P_hi) x + P_lo x = 2^15 Pi x, then times 16 / |x|.
+        // fp32 input is normalised first and split: accumulator 2^19 Pi x_u.
         f32x16 ay[4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) ay[mt] = f32x16{};
 #pragma unroll
         for (int kb = 0; kb < 8; ++kb) {
-            Split8 s;
+            u32x4 fh[4], fl[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                uint32_t a0, b0, c0, a1, b1, c1;
-                split16(in.get(8 * kb + 2 * q) * inv, &a0, &b0, &c0);
-                split16(in.get(8 * kb + 2 * q + 1) * inv, &a1, &b1, &c1);
-                s.h11[q] = a0 | (a1 << 16);
-                s.hi[q] = b0 | (b1 << 16);
-                s.lo[q] = c0 | (c1 << 16);
+            for (int mt = 0; mt < 4; ++mt) {
+                const int row = 32 * mt + (l & 31), chunk = 2 * kb + h;
+                fh[mt] = mat_frag(lds.pih, row, chunk);
+                fl[mt] = mat_frag(lds.pil, row, chunk);
             }
-            dense_kblock(
-                ay, s, kb, [&](int row, int chunk) { return mat_frag(lds.pih, row, chunk); },
-                [&](int row, int chunk) { return mat_frag(lds.pil, row, chunk); }, l, h);
+            if constexpr (IN_F16) {
+                const u32x4 xb = {in.w[4 * kb], in.w[4 * kb + 1], in.w[4 * kb + 2], in.w[4 * kb + 3]};
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) ay[mt] = mfma(fh[mt], xb, ay[mt]);
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) ay[mt] = mfma(fl[mt], xb, ay[mt]);
+            } else {
+                kblock3(ay, split8([&](int e) { return in.get(8 * kb + e) * inv; }), fh, fl);
+            }
         }
+        const float ysc = IN_F16 ? 16.0f * inv : 1.0f;
+
+        // QJL: the first fragments of T (y - y^) requested now
+        const GPair tg(P.t2_hi, P.t2_lo, l);
+        Frag8 tf0;
+        if constexpr (QJL) tf0 = tg.load(0);
+
+        // codes; with QJL the accumulators become 2^19 (y - y^) in place
         uint32_t cw[LW];
 #pragma unroll
         for (int k = 0; k < LW; ++k) cw[k] = 0u;
@@ -275,53 +413,36 @@ __global__ __launch_bounds__(64 * WAVES) void tq_quant_kernel(DenseDev P, const 
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float e = ay[mt][r];
-                put_code<B, LW>(cw, 16 * mt + r, dense_code(e, ba, bb, binc));
+                const float e = IN_F16 ? ay[mt][r] * ysc : ay[mt][r];
+                if constexpr (QJL) {
+                    float cv;
+                    put_code<B, LW>(cw, 16 * mt + r, dense_code_c(e, ba, bb, binc, &cv));
+                    ay[mt][r] = e - cv;
+                } else {
+                    put_code<B, LW>(cw, 16 * mt + r, dense_code(e, ba, bb, binc));
+                }
             }
 
-        // x~ = Pi^T y^ (roundtrip or QJL), then with QJL the residual, S r
-        // and the sign words
-        f32x16 ax[4];
+        // QJL: gamma = |y - y^|, z = T (y - y^) (scale 2^14), sign words
+        // 2 h, 2 h + 1: bit r of M tile 2 w + p at 16 p + r = [z >= 0]
         uint32_t sw0 = 0u, sw1 = 0u, gh = 0u;
         float ghat = 0.0f;
-        if constexpr (ROUNDTRIP || QJL) dense_pit2<B>(P, lds.ctab, cw, ax, l, h);
         if constexpr (QJL) {
-            f32x16 za[4];
-#pragma unroll
-            for (int mz = 0; mz < 4; ++mz) za[mz] = f32x16{};
             float gam2 = 0.0f;
 #pragma unroll
-            for (int kb = 0; kb < 8; ++kb) {
-                const int mt = kb >> 1, c = kb & 1;
-                u32x4 rh, rl;
+            for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    float rr[2];
-#pragma unroll
-                    for (int e = 0; e < 2; ++e) {
-                        const int r = 8 * c + 2 * q + e;
-                        const float xe = ax[mt][r];
-                        rr[e] = in.get(16 * mt + r) * inv - xe * kRotScale;
-                        gam2 = __builtin_fmaf(rr[e], rr[e], gam2);
-                    }
-                    uint32_t h0, l0, h1, l1;
-                    split_h(rr[0] * kDenseResidualScale, &h0, &l0);
-                    split_h(rr[1] * kDenseResidualScale, &h1, &l1);
-                    rh[q] = h0 | (h1 << 16);
-                    rl[q] = l0 | (l1 << 16);
+                for (int r = 0; r < 16; ++r) {
+                    const float d = ay[mt][r] * kRotScale;
+                    gam2 = __builtin_fmaf(d, d, gam2);
                 }
-#pragma unroll
-                for (int mz = 0; mz < 4; ++mz) {
-                    const u32x4 a = gmat_frag(P.s_fwd, 32 * mz + (l & 31), 2 * kb + h);
-                    za[mz] = mfma(a, rh, za[mz]);
-                    za[mz] = mfma(a, rl, za[mz]);
-                }
-            }
             gam2 = gam2 + other_half(gam2, h);
-            const float gam = __builtin_sqrtf(gam2);
-            gh = f2h(gam);
+            gh = f2h(__builtin_sqrtf(gam2));
             ghat = h2f(gh);
-            // sign words 2 h, 2 h + 1: bit r of M tile 2 w + p at 16 p + r = [z >= 0]
+            f32x16 za[4];
+            gprod3(za, tg, tf0, [&](int kb) {
+                return split8([&](int e) { return ay[kb >> 1][8 * (kb & 1) + e] * (kRotScale * 0.5f); });
+            });
             // (an accumulator that starts at +0 never ends at -0)
 #pragma unroll
             for (int w = 0; w < 2; ++w) {
@@ -337,6 +458,12 @@ __global__ __launch_bounds__(64 * WAVES) void tq_quant_kernel(DenseDev P, const 
                 else sw1 = ~pb;
             }
         }
+
+        // the reconstruction's first Pi^T fragments requested before the
+        // record is written
+        const GPair pg(P.pit2_hi, P.pit2_lo, l);
+        Frag8 pf0;
+        if constexpr (ROUNDTRIP) pf0 = pg.load(0);
 
         // record
         half_store2(norms, base, n, nh, vi);
@@ -355,36 +482,34 @@ __global__ __launch_bounds__(64 * WAVES) void tq_quant_kernel(DenseDev P, const 
         // The reconstruction is exactly what tq_dequant_kernel forms from the
         // record just written.
         if constexpr (ROUNDTRIP) {
-            f32x16 aq[4];
-            if constexpr (QJL) dense_back2(P, sw0, sw1, aq, l, h);
-            char* rowo = tile + vi * RBO + dense_half_bytes<OUT_F16>() * h;
-            wave_lds_sync();
-            dense_out2<QJL, OUT_F16>(ax, aq, P.qjl_scale * ghat, nhat, rowo);
-            tile2_store<OUT_F16>(y, ldy_bytes, base, n, tile, l);
+            f32x16 ax[4], aq[4];
+            dense_pit2<B>(pg, pf0, lds.ctab, cw, ax);
+            if constexpr (QJL) {
+                const GOne sg(P.s_back, l);
+                dense_back2(sg, sg.load(0), sw0, sw1, aq);
+            }
+            dense_out_store<QJL, OUT_F16>(ax, aq, P.qjl_scale * ghat, nhat, y, ldy_bytes, base, n, vi, h);
         }
     }
 }
 
 template <int B, bool QJL, bool OUT_F16>
-__global__ __launch_bounds__(256) void tq_dequant_kernel(DenseDev P, const uint32_t* __restrict__ codes,
+__global__ __launch_bounds__(256, 2) void tq_dequant_kernel(DenseDev P, const uint32_t* __restrict__ codes,
                                                          const uint16_t* __restrict__ norms,
                                                          const uint32_t* __restrict__ signs,
                                                          const uint16_t* __restrict__ rnorms, int64_t n,
                                                          char* __restrict__ y, int64_t ldy_bytes) {
     constexpr int LW = 2 * B;
     constexpr int W = 4 * B;
-    constexpr int RBO = row_bytes2<OUT_F16>();
     constexpr int SW = 32 * W > 128 ? 32 * W : 128;
     struct Lds {
         uint32_t ctab[32];
-        u32x4 tiles[4][32 * RBO / 16];
         uint32_t stage[4][SW];
     };
     __shared__ Lds lds;
     dense_tables_to_lds<B>(P, lds.ctab);
     __syncthreads();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    char* tile = reinterpret_cast<char*>(lds.tiles[wave]);
     uint32_t* stw = lds.stage[wave];
     const int64_t ntiles = (n + 31) / 32;
     for (int64_t t = blockIdx.x * 4LL + wave; t < ntiles; t += gridDim.x * 4LL) {
@@ -406,18 +531,19 @@ __global__ __launch_bounds__(256) void tq_dequant_kernel(DenseDev P, const uint3
             ghat = h2f(half_load2(rnorms, base, n, vi));
         }
         f32x16 ax[4], aq[4];
-        dense_pit2<B>(P, lds.ctab, cw, ax, l, h);
-        if constexpr (QJL) dense_back2(P, sw0, sw1, aq, l, h);
-        char* rowo = tile + vi * RBO + dense_half_bytes<OUT_F16>() * h;
-        wave_lds_sync();
-        dense_out2<QJL, OUT_F16>(ax, aq, P.qjl_scale * ghat, nhat, rowo);
-        tile2_store<OUT_F16>(y, ldy_bytes, base, n, tile, l);
+        const GPair pg(P.pit2_hi, P.pit2_lo, l);
+        dense_pit2<B>(pg, pg.load(0), lds.ctab, cw, ax);
+        if constexpr (QJL) {
+            const GOne sg(P.s_back, l);
+            dense_back2(sg, sg.load(0), sw0, sw1, aq);
+        }
+        dense_out_store<QJL, OUT_F16>(ax, aq, P.qjl_scale * ghat, nhat, y, ldy_bytes, base, n, vi, h);
     }
 }
 
 // ----------------------------------------------------------- launchers --
-// fp16 input and output: eight-wave workgroups sharing one LDS copy of Pi
-// (two waves per SIMD); fp32 tiles need four waves' LDS.
+// fp16 input: eight-wave workgroups sharing one LDS copy of Pi (two waves
+// per SIMD); fp32 input tiles need four waves' LDS.
 template <int B, bool QJL>
 hipError_t launch_tq_quant(const DenseDev& P, const void* x, bool in_f16, int64_t ldx_bytes, int64_t n,
                            uint32_t* codes, uint16_t* norms, uint32_t* signs, uint16_t* rnorms, void* y, bool out_f16,
@@ -437,7 +563,7 @@ hipError_t launch_tq_quant(const DenseDev& P, const void* x, bool in_f16, int64_
         else TQ_LAUNCH(false, true, false, 4);
     } else if (in_f16) {
         if (out_f16) TQ_LAUNCH(true, true, true, 8);
-        else TQ_LAUNCH(true, false, true, 4);
+        else TQ_LAUNCH(true, false, true, 8);
     } else {
         if (out_f16) TQ_LAUNCH(false, true, true, 4);
         else TQ_LAUNCH(false, false, true, 4);

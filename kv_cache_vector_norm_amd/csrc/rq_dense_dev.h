@@ -27,7 +27,8 @@ struct DenseDev {
     const uint16_t* __restrict__ pi2_lo;
     const uint16_t* __restrict__ pit2_hi;
     const uint16_t* __restrict__ pit2_lo;
-    const uint16_t* __restrict__ s_fwd;
+    const uint16_t* __restrict__ t2_hi;
+    const uint16_t* __restrict__ t2_lo;
     const uint16_t* __restrict__ s_back;
     const float* __restrict__ thr;
     const float* __restrict__ cent;
@@ -107,10 +108,24 @@ __device__ __forceinline__ void dense_bins_to_lds(const DenseDev& P, u32x4* __re
 // #{k : y > t_k} of y = acc * kRotScale through the slot table: the slot of
 // fma(acc, bin_a * kRotScale, bin_b) equals that of fma(y, bin_a, bin_b)
 // (power-of-two scalings are exact), and acc > 2^19 t equals y > t.
+// dense_code_c also gives the centroid c[code] times 2^19 in *cv.
+__device__ __forceinline__ uint32_t dense_code_c(float acc, float ba, float bb, const char* __restrict__ bins,
+                                                 float* cv) {
+    const uint32_t off = __builtin_bit_cast(uint32_t, __builtin_fmaf(acc, ba, bb)) & 0xFF0u;
+    const u32x4 e = *reinterpret_cast<const u32x4*>(bins + off);   // {base code, boundary, c_lo, c_hi}
+    // (elements go through scalars: hipcc turns a bit cast of an ext-vector
+    // element straight into one of element 0)
+    const uint32_t base = e[0], thr = e[1], c_lo = e[2], c_hi = e[3];
+    const bool up = acc > __builtin_bit_cast(float, thr);
+    *cv = __builtin_bit_cast(float, up ? c_hi : c_lo);
+    return base + (up ? 1u : 0u);
+}
+
 __device__ __forceinline__ uint32_t dense_code(float acc, float ba, float bb, const char* __restrict__ bins) {
     const uint32_t off = __builtin_bit_cast(uint32_t, __builtin_fmaf(acc, ba, bb)) & 0xFF0u;
-    const uint2 e = *reinterpret_cast<const uint2*>(bins + off);   // {base code, boundary in the slot}
-    return e.x + (acc > __builtin_bit_cast(float, e.y) ? 1u : 0u);
+    const uint2 e = *reinterpret_cast<const uint2*>(bins + off);
+    const uint32_t base = e.x, thr = e.y;
+    return base + (acc > __builtin_bit_cast(float, thr) ? 1u : 0u);
 }
 
 // Centroid halves: ctab[k] = hi | (2^11 hi) << 16, ctab[L + k] = lo, for

@@ -42,12 +42,13 @@ struct DenseTables {
     const uint16_t* pi_lo;
     const uint16_t* pit_hi;  // transposed
     const uint16_t* pit_lo;
-    const uint16_t* pi2_hi;  // Pi and Pi^T permuted for the codec kernels' MFMA layout
+    const uint16_t* pi2_hi;  // Pi permuted for the codec kernels' MFMA layout, row-major
     const uint16_t* pi2_lo;
-    const uint16_t* pit2_hi;
+    const uint16_t* pit2_hi; // Pi^T permuted likewise, in MFMA fragment order
     const uint16_t* pit2_lo;
-    const uint16_t* s_fwd;   // S and S^T permuted likewise (sessions with an MSE stage)
-    const uint16_t* s_back;
+    const uint16_t* t2_hi;   // T = S Pi^T permuted likewise, fragment order (QJL)
+    const uint16_t* t2_lo;
+    const uint16_t* s_back;  // S^T permuted likewise, fragment order (QJL)
     const float* thr;
     const float* cent;
     const uint16_t* s_rows;

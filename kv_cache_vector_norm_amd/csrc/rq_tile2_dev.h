@@ -68,6 +68,40 @@ __device__ __forceinline__ void tile2_put(const Tile2Regs<F16>& r, char* __restr
     }
 }
 
+// A tile's 32 rows of 256 (fp16) or 512 (fp32) bytes copied into LDS by the
+// gfx950 direct-to-LDS buffer load (16 bytes per lane), without registers:
+// rows unpadded, 16-byte chunk c of row v at position c ^ (v & 15).
+// Instruction it fills the kilobyte at 1024 it (rows RPI it ..): lane l
+// writes position l % CH of row RPI it + l / CH and reads the chunk that
+// belongs there.  Rows at or beyond n read as zero.  The copy is
+// asynchronous: tile2_dma_wait() before the tile is read.
+typedef __attribute__((address_space(3))) void lds_void_t;
+template <bool F16>
+__device__ __forceinline__ void tile2_dma(const char* __restrict__ src, int64_t ld_bytes, int64_t base, int64_t n,
+                                          char* tile, int l) {
+    using T = Tile2Shape<F16>;
+    const rsrc_t rs = make_rsrc(src + base * ld_bytes, tile2_range(n - base, ld_bytes));
+    const int rr = l / T::CH, p = l % T::CH;
+#pragma unroll
+    for (int it = 0; it < T::IT; ++it) {
+        const int row = T::RPI * it + rr;
+        const uint32_t voff = static_cast<uint32_t>(row) * static_cast<uint32_t>(ld_bytes) +
+                              static_cast<uint32_t>(16 * (p ^ (row & 15)));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(tile + 1024 * it), 16, voff, 0, 0, kNonTemporal);
+    }
+}
+// Waits until this wave's LDS reads have returned (before a copy overwrites
+// what they read).
+__device__ __forceinline__ void lds_reads_done() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+}
+// Waits for this wave's outstanding vector-memory operations, the tile copy
+// among them.
+__device__ __forceinline__ void tile2_dma_wait() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    wave_lds_sync();
+}
+
 // Writes the tile's 32 rows from LDS; each group of four 16-byte reads is
 // followed by its four stores with nothing in between.
 template <bool F16>
