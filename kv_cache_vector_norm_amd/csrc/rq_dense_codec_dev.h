@@ -109,18 +109,23 @@ struct Split8 {
     u32x4 h11, lo, hi;
 };
 
-// Splits of 8 values into the three operands (split16: 16 v = hi + 2^-11 lo).
-template <class Val>
-__device__ __forceinline__ Split8 split8(Val val) {
+// Splits of 8 values v into the three operands, pairs at a time: val16(e)
+// gives a = 16 v; hi = half(a) (packed conversion), 2^11 hi by a packed half
+// multiply (exact), lo = half(2^11 a - 2^11 hi) (the fma is exact, since
+// a - hi is).  Bit for bit what split16 gives per value.
+template <class Val16>
+__device__ __forceinline__ Split8 split8(Val16 val16) {
+    constexpr f16x2 k2048 = {static_cast<f16>(2048.0f), static_cast<f16>(2048.0f)};
     Split8 s;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        uint32_t a0, b0, c0, a1, b1, c1;
-        split16(val(2 * q), &a0, &b0, &c0);
-        split16(val(2 * q + 1), &a1, &b1, &c1);
-        s.h11[q] = a0 | (a1 << 16);
-        s.hi[q] = b0 | (b1 << 16);
-        s.lo[q] = c0 | (c1 << 16);
+        const float a = val16(2 * q), b = val16(2 * q + 1);
+        const uint32_t hi = cvt_pk(a, b);
+        const f16x2 h11 = __builtin_bit_cast(f16x2, hi) * k2048;
+        const float ha = static_cast<float>(h11[0]), hb = static_cast<float>(h11[1]);
+        s.hi[q] = hi;
+        s.h11[q] = __builtin_bit_cast(uint32_t, h11);
+        s.lo[q] = cvt_pk(__builtin_fmaf(a, 2048.0f, -ha), __builtin_fmaf(b, 2048.0f, -hb));
     }
     return s;
 }
@@ -218,20 +223,19 @@ __device__ __forceinline__ void gprod1(f32x16 (&acc)[4], const GOne& g, const Fr
 // centroids of the lane's codes; the same sequence in the quantiser's
 // roundtrip and in the dequantiser.
 template <int B>
-__device__ __forceinline__ void dense_pit2(const GPair& g, const Frag8& first, const uint32_t* __restrict__ ctab,
+__device__ __forceinline__ void dense_pit2(const GPair& g, const Frag8& first, const uint2* __restrict__ ptab,
                                            const uint32_t (&cw)[2 * B], f32x16 (&ax)[4]) {
-    constexpr int L = 1 << B;
+    constexpr f16x2 k2048 = {static_cast<f16>(2048.0f), static_cast<f16>(2048.0f)};
     gprod3(ax, g, first, [&](int kb) {
         Split8 s;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const uint32_t c0 = get_code<B, 2 * B>(cw, 8 * kb + 2 * q);
-            const uint32_t c1 = get_code<B, 2 * B>(cw, 8 * kb + 2 * q + 1);
-            const uint32_t e0 = ctab[c0], e1 = ctab[c1];        // lo 16 bits: hi half, hi 16 bits: 2^11 hi
-            const uint32_t o0 = ctab[L + c0], o1 = ctab[L + c1];  // lo half
-            s.hi[q] = (e0 & 0xFFFFu) | (e1 << 16);
-            s.h11[q] = (e0 >> 16) | (e1 & 0xFFFF0000u);
-            s.lo[q] = o0 | (o1 << 16);
+            // slots 8 kb + 2 q and 8 kb + 2 q + 1: one 2B-bit code pair
+            const uint2 e = ptab[get_code<2 * B, 2 * B>(cw, 4 * kb + q)];
+            const uint32_t hi = e.x, lo = e.y;
+            s.hi[q] = hi;
+            s.lo[q] = lo;
+            s.h11[q] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, hi) * k2048);   // exact
         }
         return s;
     });
@@ -264,18 +268,20 @@ __device__ __forceinline__ void dense_out_store(const f32x16 (&ax)[4], const f32
     const rsrc_t rs = make_rsrc(y + base * ldy_bytes, tile2_range(n - base, ldy_bytes));
     const uint32_t voff = static_cast<uint32_t>(vi) * static_cast<uint32_t>(ldy_bytes) +
                           static_cast<uint32_t>((OUT_F16 ? 128 : 256) * h);
+    // n^ (ax 2^-19 + k aq) == (n^ 2^-19) (ax + (k 2^19) aq) bit for bit
+    // (power-of-two scalings commute with rounding)
+    const float k19 = k * (1.0f / kRotScale), n19 = nhat * kRotScale;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
         float o[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const float e = ax[mt][r];
-            float v = e * kRotScale;
+            float v = ax[mt][r];
             if constexpr (QJL) {
                 const float f = aq[mt][r];
-                v = __builtin_fmaf(k, f, v);
+                v = __builtin_fmaf(k19, f, v);
             }
-            o[r] = nhat * v;
+            o[r] = n19 * v;
         }
         constexpr int NC = OUT_F16 ? 2 : 4;   // 16-byte chunks of this M tile
         u32x4 w[NC];
@@ -321,7 +327,7 @@ __global__ __launch_bounds__(64 * WAVES) void tq_quant_kernel(DenseDev P, const 
         u32x4 bins[kBinSlots];      // slot table, thresholds and centroids times 2^19
         u32x4 pih[128 * 16];       // P_hi, or 2^11 P_hi for fp16 input
         u32x4 pil[128 * 16];
-        uint32_t ctab[32];
+        uint2 ptab[1 << (2 * B)];   // centroid pair table
         uint32_t stage[WAVES][SW];
     };
     __shared__ Lds lds;
@@ -332,7 +338,7 @@ __global__ __launch_bounds__(64 * WAVES) void tq_quant_kernel(DenseDev P, const 
     const int64_t t0 = static_cast<int64_t>(blockIdx.x) * WAVES + wave;
     char* tile = reinterpret_cast<char*>(lds.tiles[wave]);
     if (t0 < ntiles) tile2_dma<IN_F16>(x, ldx_bytes, t0 * 32, n, tile, lane_id());
-    dense_tables_to_lds<B>(P, lds.ctab);
+    dense_tables_to_lds<B>(P, lds.ptab);
     dense_bins_to_lds(P, lds.bins);
     if constexpr (IN_F16) mat_to_lds_x2048<NT>(P.pi2_hi, lds.pih);   // 2^11 P_hi
     else mat_to_lds<NT>(P.pi2_hi, lds.pih);
@@ -373,6 +379,8 @@ __global__ __launch_bounds__(64 * WAVES) void tq_quant_kernel(DenseDev P, const 
         const uint32_t nh = f2h(nrm);
         const float nhat = h2f(nh);
 
+        const float inv16 = 16.0f * inv;   // (v inv) 16 == v (16 inv): power-of-two scaling
+
         // y = Pi x_u, Pi from LDS.  fp16 input enters the MFMAs as it is
         // (exact): (2^11 P_hi) x + P_lo x = 2^15 Pi x, then times 16 / |x|.
         // fp32 input is normalised first and split: accumulator 2^19 Pi x_u.
@@ -395,10 +403,13 @@ __global__ __launch_bounds__(64 * WAVES) void tq_quant_kernel(DenseDev P, const 
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) ay[mt] = mfma(fl[mt], xb, ay[mt]);
             } else {
-                kblock3(ay, split8([&](int e) { return in.get(8 * kb + e) * inv; }), fh, fl);
+                kblock3(ay, split8([&](int e) { return in.get(8 * kb + e) * inv16; }), fh, fl);
             }
         }
-        const float ysc = IN_F16 ? 16.0f * inv : 1.0f;
+        const float ysc = IN_F16 ? inv16 : 1.0f;
+        // phases stay in order: interleaving the rotation with the sketch
+        // below only lengthens register lifetimes
+        __builtin_amdgcn_sched_barrier(0);
 
         // QJL: the first fragments of T (y - y^) requested now
         const GPair tg(P.t2_hi, P.t2_lo, l);
@@ -428,20 +439,22 @@ __global__ __launch_bounds__(64 * WAVES) void tq_quant_kernel(DenseDev P, const 
         uint32_t sw0 = 0u, sw1 = 0u, gh = 0u;
         float ghat = 0.0f;
         if constexpr (QJL) {
+            // (summed at the accumulator scale 2^19 and scaled once: bit for
+            // bit the sum of the unscaled squares)
             float gam2 = 0.0f;
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const float d = ay[mt][r] * kRotScale;
+                    const float d = ay[mt][r];
                     gam2 = __builtin_fmaf(d, d, gam2);
                 }
-            gam2 = gam2 + other_half(gam2, h);
+            gam2 = (gam2 + other_half(gam2, h)) * (kRotScale * kRotScale);
             gh = f2h(__builtin_sqrtf(gam2));
             ghat = h2f(gh);
             f32x16 za[4];
             gprod3(za, tg, tf0, [&](int kb) {
-                return split8([&](int e) { return ay[kb >> 1][8 * (kb & 1) + e] * (kRotScale * 0.5f); });
+                return split8([&](int e) { return ay[kb >> 1][8 * (kb & 1) + e] * (kRotScale * 8.0f); });
             });
             // (an accumulator that starts at +0 never ends at -0)
 #pragma unroll
@@ -483,7 +496,7 @@ __global__ __launch_bounds__(64 * WAVES) void tq_quant_kernel(DenseDev P, const 
         // record just written.
         if constexpr (ROUNDTRIP) {
             f32x16 ax[4], aq[4];
-            dense_pit2<B>(pg, pf0, lds.ctab, cw, ax);
+            dense_pit2<B>(pg, pf0, lds.ptab, cw, ax);
             if constexpr (QJL) {
                 const GOne sg(P.s_back, l);
                 dense_back2(sg, sg.load(0), sw0, sw1, aq);
@@ -503,11 +516,11 @@ __global__ __launch_bounds__(256, 2) void tq_dequant_kernel(DenseDev P, const ui
     constexpr int W = 4 * B;
     constexpr int SW = 32 * W > 128 ? 32 * W : 128;
     struct Lds {
-        uint32_t ctab[32];
+        uint2 ptab[1 << (2 * B)];   // centroid pair table
         uint32_t stage[4][SW];
     };
     __shared__ Lds lds;
-    dense_tables_to_lds<B>(P, lds.ctab);
+    dense_tables_to_lds<B>(P, lds.ptab);
     __syncthreads();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     uint32_t* stw = lds.stage[wave];
@@ -532,7 +545,7 @@ __global__ __launch_bounds__(256, 2) void tq_dequant_kernel(DenseDev P, const ui
         }
         f32x16 ax[4], aq[4];
         const GPair pg(P.pit2_hi, P.pit2_lo, l);
-        dense_pit2<B>(pg, pg.load(0), lds.ctab, cw, ax);
+        dense_pit2<B>(pg, pg.load(0), lds.ptab, cw, ax);
         if constexpr (QJL) {
             const GOne sg(P.s_back, l);
             dense_back2(sg, sg.load(0), sw0, sw1, aq);

@@ -128,16 +128,17 @@ __device__ __forceinline__ uint32_t dense_code(float acc, float ba, float bb, co
     return base + (acc > __builtin_bit_cast(float, thr) ? 1u : 0u);
 }
 
-// Centroid halves: ctab[k] = hi | (2^11 hi) << 16, ctab[L + k] = lo, for
-// 16 c_k = hi + 2^-11 lo.
+// Centroid pair table: for codes (a, b), ptab[a + L b] = {hi[a] | hi[b] << 16,
+// lo[a] | lo[b] << 16} with 16 c_k = hi[k] + 2^-11 lo[k]: one 8-byte read
+// gives two slots' hi and lo operand halves.
 template <int B>
-__device__ __forceinline__ void dense_tables_to_lds(const DenseDev& P, uint32_t* ctab) {
+__device__ __forceinline__ void dense_tables_to_lds(const DenseDev& P, uint2* ptab) {
     constexpr int L = 1 << B;
-    if (threadIdx.x < L) {
-        uint32_t h11, h, l;
-        split16(P.cent[threadIdx.x], &h11, &h, &l);
-        ctab[threadIdx.x] = h | (h11 << 16);
-        ctab[L + threadIdx.x] = l;
+    for (int p = threadIdx.x; p < L * L; p += blockDim.x) {
+        uint32_t h11a, ha, la, h11b, hb, lb;
+        split16(P.cent[p & (L - 1)], &h11a, &ha, &la);
+        split16(P.cent[p >> B], &h11b, &hb, &lb);
+        ptab[p] = make_uint2(ha | (hb << 16), la | (lb << 16));
     }
 }
 
