@@ -226,13 +226,22 @@ template <int B>
 __device__ __forceinline__ void dense_pit2(const GPair& g, const Frag8& first, const uint2* __restrict__ ptab,
                                            const uint32_t (&cw)[2 * B], f32x16 (&ax)[4]) {
     constexpr f16x2 k2048 = {static_cast<f16>(2048.0f), static_cast<f16>(2048.0f)};
+    // slots 8 kb + 2 q and 8 kb + 2 q + 1 are one 2B-bit code pair; the
+    // table entries of K block kb + 1 are read while K block kb is formed
+    uint2 ent[2][4];
+    auto read = [&](int kb, uint2 (&d)[4]) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) d[q] = ptab[get_code<2 * B, 2 * B>(cw, 4 * kb + q)];
+    };
+    read(0, ent[0]);
     gprod3(ax, g, first, [&](int kb) {
+        const int cur = kb & 1;
+        if (kb < 7) read(kb + 1, ent[cur ^ 1]);
+        __builtin_amdgcn_sched_barrier(0);
         Split8 s;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            // slots 8 kb + 2 q and 8 kb + 2 q + 1: one 2B-bit code pair
-            const uint2 e = ptab[get_code<2 * B, 2 * B>(cw, 4 * kb + q)];
-            const uint32_t hi = e.x, lo = e.y;
+            const uint32_t hi = ent[cur][q].x, lo = ent[cur][q].y;
             s.hi[q] = hi;
             s.lo[q] = lo;
             s.h11[q] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, hi) * k2048);   // exact
@@ -255,19 +264,17 @@ __device__ __forceinline__ void dense_back2(const GOne& g, const Frag4& first, u
 }
 
 // Output slots of the lane, n^ x~ (MSE) or n^ (x~ + k (S^T sigma)) (QJL) with
-// x~ = ax * kRotScale, stored straight from registers: the lane's 64 slots
-// are coordinates 64 h .. 64 h + 63 of row vi, 128 (fp16) or 256 (fp32)
-// contiguous bytes.  Rows at or beyond n are not written.  fp16 output is
-// the rounding of the materialised fp32 value.  The stores are ordinary
-// (cached) ones: L2 merges a lane's 16-byte pieces into whole lines, where
-// non-temporal stores of partial lines cost several times more.
+// x~ = ax * kRotScale, as the 16-byte words the lane stores: its 64 slots are
+// coordinates 64 h .. 64 h + 63 of row vi, 128 (fp16) or 256 (fp32)
+// contiguous bytes.  fp16 output is the rounding of the materialised fp32
+// value.
+template <bool OUT_F16>
+struct OutWords {
+    u32x4 w[OUT_F16 ? 8 : 16];
+};
 template <bool QJL, bool OUT_F16>
-__device__ __forceinline__ void dense_out_store(const f32x16 (&ax)[4], const f32x16 (&aq)[4], float k, float nhat,
-                                                char* __restrict__ y, int64_t ldy_bytes, int64_t base, int64_t n,
-                                                int vi, int h) {
-    const rsrc_t rs = make_rsrc(y + base * ldy_bytes, tile2_range(n - base, ldy_bytes));
-    const uint32_t voff = static_cast<uint32_t>(vi) * static_cast<uint32_t>(ldy_bytes) +
-                          static_cast<uint32_t>((OUT_F16 ? 128 : 256) * h);
+__device__ __forceinline__ void dense_out_words(const f32x16 (&ax)[4], const f32x16 (&aq)[4], float k, float nhat,
+                                                OutWords<OUT_F16>& out) {
     // n^ (ax 2^-19 + k aq) == (n^ 2^-19) (ax + (k 2^19) aq) bit for bit
     // (power-of-two scalings commute with rounding)
     const float k19 = k * (1.0f / kRotScale), n19 = nhat * kRotScale;
@@ -283,8 +290,7 @@ __device__ __forceinline__ void dense_out_store(const f32x16 (&ax)[4], const f32
             }
             o[r] = n19 * v;
         }
-        constexpr int NC = OUT_F16 ? 2 : 4;   // 16-byte chunks of this M tile
-        u32x4 w[NC];
+        constexpr int NC = OUT_F16 ? 2 : 4;   // 16-byte words of this M tile
 #pragma unroll
         for (int c = 0; c < NC; ++c)
 #pragma unroll
@@ -293,17 +299,28 @@ __device__ __forceinline__ void dense_out_store(const f32x16 (&ax)[4], const f32
                     float a = o[8 * c + 2 * q], b = o[8 * c + 2 * q + 1];
                     pin(a);
                     pin(b);
-                    w[c][q] = cvt_pk(a, b);
+                    out.w[NC * mt + c][q] = cvt_pk(a, b);
                 } else {
-                    w[c][q] = __builtin_bit_cast(uint32_t, o[4 * c + q]);
+                    out.w[NC * mt + c][q] = __builtin_bit_cast(uint32_t, o[4 * c + q]);
                 }
             }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int c = 0; c < NC; ++c)
-            __builtin_amdgcn_raw_buffer_store_b128(w[c], rs, voff, 16 * (NC * mt + c), 0);
-        store_data_fence();
     }
+}
+// Stores them for the tile at row `base`; rows at or beyond n are not
+// written.  The stores are ordinary (cached) ones: L2 merges a lane's
+// 16-byte pieces into whole lines, where non-temporal stores of partial
+// lines cost several times more.
+template <bool OUT_F16>
+__device__ __forceinline__ void dense_out_put(const OutWords<OUT_F16>& out, char* __restrict__ y, int64_t ldy_bytes,
+                                              int64_t base, int64_t n, int vi, int h) {
+    const rsrc_t rs = make_rsrc(y + base * ldy_bytes, tile2_range(n - base, ldy_bytes));
+    const uint32_t voff = static_cast<uint32_t>(vi) * static_cast<uint32_t>(ldy_bytes) +
+                          static_cast<uint32_t>((OUT_F16 ? 128 : 256) * h);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int c = 0; c < (OUT_F16 ? 8 : 16); ++c)
+        __builtin_amdgcn_raw_buffer_store_b128(out.w[c], rs, voff, 16 * c, 0);
+    store_data_fence();
 }
 
 // ------------------------------------------------------------ kernels --
@@ -348,6 +365,12 @@ __global__ __launch_bounds__(64 * WAVES) void tq_quant_kernel(DenseDev P, const 
     const char* binc = reinterpret_cast<const char*>(lds.bins);
     uint32_t* stw = lds.stage[wave];
 
+    // A roundtrip stores each tile's output after the next tile's input has
+    // arrived (the wait for the input covers every earlier memory operation,
+    // so stores issued just before it would be waited for at once).
+    OutWords<OUT_F16> pend;
+    int64_t pend_base = -1;
+
     for (int64_t t = t0; t < ntiles; t += tstep) {
         const int64_t base = t * 32;
         const int z = opaque_zero();
@@ -359,6 +382,9 @@ __global__ __launch_bounds__(64 * WAVES) void tq_quant_kernel(DenseDev P, const 
         in.read(tile, vi, h);
         lds_reads_done();
         if (t + tstep < ntiles) tile2_dma<IN_F16>(x, ldx_bytes, (t + tstep) * 32, n, tile, l);
+        if constexpr (ROUNDTRIP) {
+            if (pend_base >= 0) dense_out_put<OUT_F16>(pend, y, ldy_bytes, pend_base, n, vi, h);
+        }
         float ss = 0.0f;
         if constexpr (IN_F16) {
 #pragma unroll
@@ -384,26 +410,35 @@ __global__ __launch_bounds__(64 * WAVES) void tq_quant_kernel(DenseDev P, const 
         // y = Pi x_u, Pi from LDS.  fp16 input enters the MFMAs as it is
         // (exact): (2^11 P_hi) x + P_lo x = 2^15 Pi x, then times 16 / |x|.
         // fp32 input is normalised first and split: accumulator 2^19 Pi x_u.
+        // (K block kb + 1's fragments are read before K block kb's MFMAs
+        // issue; the scheduling barrier keeps the compiler from moving each
+        // read down next to its MFMA)
         f32x16 ay[4];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) ay[mt] = f32x16{};
-#pragma unroll
-        for (int kb = 0; kb < 8; ++kb) {
-            u32x4 fh[4], fl[4];
+        u32x4 fh[2][4], fl[2][4];
+        auto pi_frags = [&](int kb, u32x4 (&dh)[4], u32x4 (&dl)[4]) {
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
                 const int row = 32 * mt + (l & 31), chunk = 2 * kb + h;
-                fh[mt] = mat_frag(lds.pih, row, chunk);
-                fl[mt] = mat_frag(lds.pil, row, chunk);
+                dh[mt] = mat_frag(lds.pih, row, chunk);
+                dl[mt] = mat_frag(lds.pil, row, chunk);
             }
+        };
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) ay[mt] = f32x16{};
+        pi_frags(0, fh[0], fl[0]);
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) {
+            const int cur = kb & 1;
+            if (kb < 7) pi_frags(kb + 1, fh[cur ^ 1], fl[cur ^ 1]);
+            __builtin_amdgcn_sched_barrier(0);
             if constexpr (IN_F16) {
                 const u32x4 xb = {in.w[4 * kb], in.w[4 * kb + 1], in.w[4 * kb + 2], in.w[4 * kb + 3]};
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt) ay[mt] = mfma(fh[mt], xb, ay[mt]);
+                for (int mt = 0; mt < 4; ++mt) ay[mt] = mfma(fh[cur][mt], xb, ay[mt]);
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt) ay[mt] = mfma(fl[mt], xb, ay[mt]);
+                for (int mt = 0; mt < 4; ++mt) ay[mt] = mfma(fl[cur][mt], xb, ay[mt]);
             } else {
-                kblock3(ay, split8([&](int e) { return in.get(8 * kb + e) * inv16; }), fh, fl);
+                kblock3(ay, split8([&](int e) { return in.get(8 * kb + e) * inv16; }), fh[cur], fl[cur]);
             }
         }
         const float ysc = IN_F16 ? inv16 : 1.0f;
@@ -420,19 +455,33 @@ __global__ __launch_bounds__(64 * WAVES) void tq_quant_kernel(DenseDev P, const 
         uint32_t cw[LW];
 #pragma unroll
         for (int k = 0; k < LW; ++k) cw[k] = 0u;
+        // (slot-table entries read CB at a time ahead of their use)
+        constexpr int CB = QJL ? 8 : 16;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+        for (int b0 = 0; b0 < 64; b0 += CB) {
+            float e[CB];
+            u32x4 ent[CB];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float e = IN_F16 ? ay[mt][r] * ysc : ay[mt][r];
+            for (int i = 0; i < CB; ++i) {
+                const int mt = (b0 + i) >> 4, r = (b0 + i) & 15;
+                e[i] = IN_F16 ? ay[mt][r] * ysc : ay[mt][r];
+                const char* pe = binc + dense_slot(e[i], ba, bb);
                 if constexpr (QJL) {
-                    float cv;
-                    put_code<B, LW>(cw, 16 * mt + r, dense_code_c(e, ba, bb, binc, &cv));
-                    ay[mt][r] = e - cv;
+                    ent[i] = *reinterpret_cast<const u32x4*>(pe);
                 } else {
-                    put_code<B, LW>(cw, 16 * mt + r, dense_code(e, ba, bb, binc));
+                    const uint2 v = *reinterpret_cast<const uint2*>(pe);
+                    ent[i] = u32x4{v.x, v.y, 0u, 0u};
                 }
             }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < CB; ++i) {
+                const int mt = (b0 + i) >> 4, r = (b0 + i) & 15;
+                float cv;
+                put_code<B, LW>(cw, b0 + i, dense_decide(e[i], ent[i], &cv));
+                if constexpr (QJL) ay[mt][r] = e[i] - cv;
+            }
+        }
 
         // QJL: gamma = |y - y^|, z = T (y - y^) (scale 2^14), sign words
         // 2 h, 2 h + 1: bit r of M tile 2 w + p at 16 p + r = [z >= 0]
@@ -501,7 +550,14 @@ __global__ __launch_bounds__(64 * WAVES) void tq_quant_kernel(DenseDev P, const 
                 const GOne sg(P.s_back, l);
                 dense_back2(sg, sg.load(0), sw0, sw1, aq);
             }
-            dense_out_store<QJL, OUT_F16>(ax, aq, P.qjl_scale * ghat, nhat, y, ldy_bytes, base, n, vi, h);
+            dense_out_words<QJL, OUT_F16>(ax, aq, P.qjl_scale * ghat, nhat, pend);
+            pend_base = base;
+        }
+    }
+    if constexpr (ROUNDTRIP) {
+        if (pend_base >= 0) {
+            const int l = lane_id();
+            dense_out_put<OUT_F16>(pend, y, ldy_bytes, pend_base, n, l & 31, l >> 5);
         }
     }
 }
@@ -525,6 +581,9 @@ __global__ __launch_bounds__(256, 2) void tq_dequant_kernel(DenseDev P, const ui
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     uint32_t* stw = lds.stage[wave];
     const int64_t ntiles = (n + 31) / 32;
+    // each tile's output is stored after the next tile's record has arrived
+    OutWords<OUT_F16> pend;
+    int64_t pend_base = -1;
     for (int64_t t = blockIdx.x * 4LL + wave; t < ntiles; t += gridDim.x * 4LL) {
         const int64_t base = t * 32;
         const int z = opaque_zero();
@@ -543,6 +602,7 @@ __global__ __launch_bounds__(256, 2) void tq_dequant_kernel(DenseDev P, const ui
             sw1 = stw[vi * 4 + 2 * h + 1];
             ghat = h2f(half_load2(rnorms, base, n, vi));
         }
+        if (pend_base >= 0) dense_out_put<OUT_F16>(pend, y, ldy_bytes, pend_base, n, vi, h);
         f32x16 ax[4], aq[4];
         const GPair pg(P.pit2_hi, P.pit2_lo, l);
         dense_pit2<B>(pg, pg.load(0), lds.ptab, cw, ax);
@@ -550,7 +610,12 @@ __global__ __launch_bounds__(256, 2) void tq_dequant_kernel(DenseDev P, const ui
             const GOne sg(P.s_back, l);
             dense_back2(sg, sg.load(0), sw0, sw1, aq);
         }
-        dense_out_store<QJL, OUT_F16>(ax, aq, P.qjl_scale * ghat, nhat, y, ldy_bytes, base, n, vi, h);
+        dense_out_words<QJL, OUT_F16>(ax, aq, P.qjl_scale * ghat, nhat, pend);
+        pend_base = base;
+    }
+    if (pend_base >= 0) {
+        const int l = lane_id();
+        dense_out_put<OUT_F16>(pend, y, ldy_bytes, pend_base, n, l & 31, l >> 5);
     }
 }
 

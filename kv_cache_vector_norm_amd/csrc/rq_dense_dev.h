@@ -107,25 +107,20 @@ __device__ __forceinline__ void dense_bins_to_lds(const DenseDev& P, u32x4* __re
 
 // #{k : y > t_k} of y = acc * kRotScale through the slot table: the slot of
 // fma(acc, bin_a * kRotScale, bin_b) equals that of fma(y, bin_a, bin_b)
-// (power-of-two scalings are exact), and acc > 2^19 t equals y > t.
-// dense_code_c also gives the centroid c[code] times 2^19 in *cv.
-__device__ __forceinline__ uint32_t dense_code_c(float acc, float ba, float bb, const char* __restrict__ bins,
-                                                 float* cv) {
-    const uint32_t off = __builtin_bit_cast(uint32_t, __builtin_fmaf(acc, ba, bb)) & 0xFF0u;
-    const u32x4 e = *reinterpret_cast<const u32x4*>(bins + off);   // {base code, boundary, c_lo, c_hi}
-    // (elements go through scalars: hipcc turns a bit cast of an ext-vector
-    // element straight into one of element 0)
+// (power-of-two scalings are exact), and acc > 2^19 t equals y > t.  The
+// table's elements go through scalars: hipcc turns a bit cast of an
+// ext-vector element straight into one of element 0.
+// In two steps, so that table reads can be issued ahead of their use: the
+// byte offset of y's slot entry, then the code (and the centroid times
+// 2^19, when the entry's c_lo, c_hi were read) from the entry.
+__device__ __forceinline__ uint32_t dense_slot(float acc, float ba, float bb) {
+    return __builtin_bit_cast(uint32_t, __builtin_fmaf(acc, ba, bb)) & 0xFF0u;
+}
+__device__ __forceinline__ uint32_t dense_decide(float acc, const u32x4& e, float* cv) {
     const uint32_t base = e[0], thr = e[1], c_lo = e[2], c_hi = e[3];
     const bool up = acc > __builtin_bit_cast(float, thr);
     *cv = __builtin_bit_cast(float, up ? c_hi : c_lo);
     return base + (up ? 1u : 0u);
-}
-
-__device__ __forceinline__ uint32_t dense_code(float acc, float ba, float bb, const char* __restrict__ bins) {
-    const uint32_t off = __builtin_bit_cast(uint32_t, __builtin_fmaf(acc, ba, bb)) & 0xFF0u;
-    const uint2 e = *reinterpret_cast<const uint2*>(bins + off);
-    const uint32_t base = e.x, thr = e.y;
-    return base + (acc > __builtin_bit_cast(float, thr) ? 1u : 0u);
 }
 
 // Centroid pair table: for codes (a, b), ptab[a + L b] = {hi[a] | hi[b] << 16,
