@@ -245,10 +245,23 @@ __device__ __forceinline__ void query_products(const QueryFrags<QJL, X>& fr, con
 #pragma unroll
     for (int nt = 0; nt < NMT; ++nt) {
         f32x16 ax = {}, as = {};
+        // the split operands of K block kb + 1 are read before K block kb's
+        // MFMAs issue (the scheduling barrier keeps each read from moving
+        // down next to its MFMA)
+        u32x4 op[2][3];
+        auto read = [&](int kb, u32x4 (&d)[3]) {
+            const u32x4* b = bop + ((nt * 8 + kb) * 3) * 64 + l;
+            d[0] = b[0];
+            d[1] = b[64];
+            d[2] = b[128];
+        };
+        read(0, op[0]);
 #pragma unroll
         for (int kb = 0; kb < 8; ++kb) {
-            const u32x4* b = bop + ((nt * 8 + kb) * 3) * 64 + l;
-            const u32x4 h11 = b[0], l11 = b[64], h = b[128];
+            const int cur = kb & 1;
+            if (kb < 7) read(kb + 1, op[cur ^ 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            const u32x4 h11 = op[cur][0], l11 = op[cur][1], h = op[cur][2];
             if constexpr (X) {
                 ax = mfma(fr.xh[kb], h11, ax);
                 ax = mfma(fr.xh[kb], l11, ax);
@@ -326,29 +339,48 @@ __device__ __forceinline__ void product_store(const float (&out)[NMT][16], Lds& 
 // in the row's padding).
 template <int ROWS, class Lds>
 __device__ __forceinline__ void rotor_qhat_in_place(Lds& lds) {
-    for (int job = threadIdx.x; job < ROWS * kGroups; job += kBlock) {
-        const int r = job / kGroups, g = job - r * kGroups;
-        float* q = &lds.qf[r][3 * g];
-        const u32x4 m0 = *reinterpret_cast<const u32x4*>(&lds.rot[12 * g]);
-        const u32x4 m1 = *reinterpret_cast<const u32x4*>(&lds.rot[12 * g + 4]);
-        const float m8 = lds.rot[12 * g + 8];
-        float m[9];
+    // a thread's jobs in batches of four: the batch's LDS reads are all
+    // issued before its writes (the compiler cannot tell jobs apart, so
+    // one job at a time would serialise every read behind the last write)
+    constexpr int JOBS = ROWS * kGroups, PER = (JOBS + kBlock - 1) / kBlock, BATCH = 4;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const uint32_t a0 = m0[k];
-            const uint32_t a1 = m1[k];
-            m[k] = __builtin_bit_cast(float, a0);
-            m[4 + k] = __builtin_bit_cast(float, a1);
+    for (int b0 = 0; b0 < PER; b0 += BATCH) {
+        float v[BATCH][3], m[BATCH][9];
+        float* qp[BATCH];
+        bool ok[BATCH];
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i) {
+            const int job = threadIdx.x + (b0 + i) * kBlock;
+            ok[i] = b0 + i < PER && job < JOBS;
+            const int jc = ok[i] ? job : 0;
+            const int r = jc / kGroups, g = jc - r * kGroups;
+            qp[i] = &lds.qf[r][3 * g];
+            const u32x4 m0 = *reinterpret_cast<const u32x4*>(&lds.rot[12 * g]);
+            const u32x4 m1 = *reinterpret_cast<const u32x4*>(&lds.rot[12 * g + 4]);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t a0 = m0[k];
+                const uint32_t a1 = m1[k];
+                m[i][k] = __builtin_bit_cast(float, a0);
+                m[i][4 + k] = __builtin_bit_cast(float, a1);
+            }
+            m[i][8] = lds.rot[12 * g + 8];
+            v[i][0] = qp[i][0];
+            v[i][1] = qp[i][1];
+            v[i][2] = g == kGroups - 1 ? 0.0f : qp[i][2];
         }
-        m[8] = m8;
-        const float v0 = q[0], v1 = q[1], v2 = g == kGroups - 1 ? 0.0f : q[2];
-        float y[3];
 #pragma unroll
-        for (int rr = 0; rr < 3; ++rr)
-            y[rr] = __builtin_fmaf(m[3 * rr + 2], v2, __builtin_fmaf(m[3 * rr + 1], v1, m[3 * rr] * v0));
-        q[0] = y[0];
-        q[1] = y[1];
-        q[2] = y[2];
+        for (int i = 0; i < BATCH; ++i) {
+            if (!ok[i]) continue;
+            float y[3];
+#pragma unroll
+            for (int rr = 0; rr < 3; ++rr)
+                y[rr] = __builtin_fmaf(m[i][3 * rr + 2], v[i][2],
+                                       __builtin_fmaf(m[i][3 * rr + 1], v[i][1], m[i][3 * rr] * v[i][0]));
+            qp[i][0] = y[0];
+            qp[i][1] = y[1];
+            qp[i][2] = y[2];
+        }
     }
 }
 
