@@ -85,3 +85,47 @@ def test_tq_score(K, mode):
     qn = np.linalg.norm(q.astype(np.float64), axis=1)
     nh = np.stack([OC.half_value(hrec.norms[(h // group) * t:(h // group) * t + t]) for h in range(hq)])
     assert np.all(np.abs(s.cpu().numpy() - ref) <= PR.SCORE_TOL * qn[:, None] * nh)
+
+
+@pytest.mark.parametrize("mode", [OP.DENSE, OP.DENSE | OP.QJL])
+@pytest.mark.parametrize("n", [1100, 70001])
+def test_tq_strided_rows(K, mode, n):
+    """Padded row pitches on both sides, a ragged last tile and (at 70,001
+    keys) waves with two tiles: the records and outputs equal those of
+    packed rows bit for bit, and the output rows' padding is never written."""
+    c = K.Codec(bits=3, seed=0, mode=mode)
+    x = W.gaussian(n, seed=77, dtype=np.float16)
+    xt = torch.from_numpy(x).cuda()
+    rec_a, y_a = c.roundtrip(xt, dtype=torch.float16)
+    y32_a = c.dequantize(rec_a, dtype=torch.float32)
+    # fp16 input at a pitch of 136 halves, fp16 output at 144 with a sentinel pad
+    xb = torch.zeros((n, 136), dtype=torch.float16, device="cuda")
+    xb[:, :128] = xt
+    yb = torch.full((n, 144), 7.0, dtype=torch.float16, device="cuda")
+    rec_b = c.alloc_record(n, "cuda")
+    c.roundtrip(xb[:, :128], rec=rec_b, out=yb[:, :128])
+    # fp32 input at a pitch of 132 floats, fp32 output at 136, against packed
+    # fp32 rows (the fp32 path normalises before rotating, so its record is
+    # compared with its own packed run); the dequantiser into a padded pitch
+    x32 = xt.float().contiguous()
+    rec_p, y_p = c.roundtrip(x32, dtype=torch.float32)
+    xc = torch.zeros((n, 132), dtype=torch.float32, device="cuda")
+    xc[:, :128] = x32
+    yc = torch.full((n, 136), -3.0, dtype=torch.float32, device="cuda")
+    rec_c = c.alloc_record(n, "cuda")
+    c.roundtrip(xc[:, :128], rec=rec_c, out=yc[:, :128])
+    yd = torch.full((n, 136), -5.0, dtype=torch.float32, device="cuda")
+    c.dequantize(rec_b, out=yd[:, :128])
+    torch.cuda.synchronize()
+    for a, b in zip(rec_a.host(), rec_b.host()):
+        if a is not None:
+            assert np.array_equal(a, b)
+    for a, b in zip(rec_p.host(), rec_c.host()):
+        if a is not None:
+            assert np.array_equal(a, b)
+    assert torch.equal(y_a, yb[:, :128])
+    assert torch.all(yb[:, 128:] == 7.0)
+    assert torch.equal(y_p, yc[:, :128])
+    assert torch.all(yc[:, 128:] == -3.0)
+    assert torch.equal(y32_a, yd[:, :128])
+    assert torch.all(yd[:, 128:] == -5.0)
