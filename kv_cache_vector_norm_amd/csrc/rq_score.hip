@@ -652,7 +652,26 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
     if constexpr (NMT == 0) {
         // Lane (c, g) = (l % 16, l / 16) serves keys 16 j + c (j = 0..3) of the
         // 64-key tile and K slots 32 ks + 8 g .. + 7 of each 32-wide step; the
-        // A operand of step ks is chunk 4 ks + g of staged row c.
+        // A operand of step ks is chunk 4 ks + g of staged row c.  The block's
+        // query rows do not change, so the A operands are read from LDS once
+        // for all of the wave's tiles (Q1 = 2^11 Q2 is rebuilt by an exact
+        // packed multiply): LDS bandwidth bounds this loop.
+        u32x4 aq2[4], aq3[4], ap1[4], ap2[4];
+        {
+            const int l = lane_id(), c = l & 15, g = l >> 4;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int r = c * kRowStride + 4 * ks + g;
+                if constexpr (B > 0) {
+                    aq2[ks] = lds.qrows[r + kOffQ2];
+                    aq3[ks] = lds.qrows[r + kOffQ3];
+                }
+                if constexpr (QJL) {
+                    ap1[ks] = lds.qrows[r + kOffP1];
+                    ap2[ks] = lds.qrows[r + kOffP2];
+                }
+            }
+        }
         for (; tile < ntiles; tile += tstep) {
             const int z = opaque_zero();
             const int l = lane_id() + z;
@@ -708,11 +727,14 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
             }
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                const int r = c * kRowStride + 4 * ks + g;
                 if constexpr (B > 0) {
-                    const u32x4 q1 = lds.qrows[r + kOffQ1];
-                    const u32x4 q2 = lds.qrows[r + kOffQ2];
-                    const u32x4 q3 = lds.qrows[r + kOffQ3];
+                    const u32x4 q2 = aq2[ks], q3 = aq3[ks];
+                    u32x4 q1;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t v = q2[e];
+                        q1[e] = pk_scale2048(v);
+                    }
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         u32x4 ch, cl;
@@ -723,8 +745,7 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
                     }
                 }
                 if constexpr (QJL) {
-                    const u32x4 p1 = lds.qrows[r + kOffP1];
-                    const u32x4 p2 = lds.qrows[r + kOffP2];
+                    const u32x4 p1 = ap1[ks], p2 = ap2[ks];
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         u32x4 sv;
