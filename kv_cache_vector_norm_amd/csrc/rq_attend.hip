@@ -483,6 +483,350 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CODES ? 2 :
     }
 }
 
+// Groups of at most 16 query rows (GQA 4:1 and 8:1): both weighted sums in
+// one pass over the tiles, on 16x16x32 MFMAs whose M dimension is the
+// group's rows (a 32-row M tile would carry 4 or 8 live rows of 32).  Per
+// 64-key tile each wave stages the records key-minor in LDS and writes the
+// weights of the live rows (p n^, and with QJL p n^ gamma^) to its tables as
+// the two-pass kernel does; then two K steps of 32 keys: lane (c, g) =
+// (l % 16, l / 16) holds keys 32 ks + 8 g .. + 7 and, in N tile nt,
+// coordinate (sign index) 8 c + nt, so the lane's eight coordinates share
+// one field of 8 B code bits per key and one byte of its sign bits.  The
+// scores, norms and the staging are read once for both sums.
+template <int B, bool QJL, bool PAD>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attend_values16_kernel(AttendArgs a) {
+    constexpr int L = 1 << B;
+    constexpr int W = (((PAD ? kRotCoords : kD) * B) + 31) / 32;
+    constexpr int WTS = 36;               // weight-table row pitch (dwords)
+    constexpr int NK = QJL ? 2 : 1;       // weight kinds: p n^, p n^ gamma^
+    constexpr bool STR = 32 % (8 * B) != 0;   // 3-bit fields straddle code words
+    struct alignas(16) Wave {
+        uint32_t code[W + 1][68];         // [word][key], as in the two-pass kernel
+        uint32_t sign[QJL ? 4 : 1][68];
+        alignas(16) uint16_t nrm[64];
+        alignas(16) uint16_t gam[64];
+    };
+    struct WaveW {
+        uint32_t hi[NK][16][WTS];         // [kind][row][key pair]: fp16 hi of the weights
+        uint32_t lo[NK][16][WTS];         // lo11 = half((w - hi) 2^11)
+    };
+    struct Lds {
+        uint32_t ptab[2 * 257];           // code pairs -> C_lo at [p], C_hi at [257 + p]
+        float centf[PAD ? L : 1];
+        u32x4 sig[QJL ? 256 : 1];         // two keys' sign nibbles -> +-1 half pairs, per bit
+        Wave w[4];
+        union {
+            WaveW wt[4];
+            float sum[16][kPartStride];
+        };
+    };
+    __shared__ Lds lds;
+
+    const int kvh = blockIdx.y;            // one row block per KV head
+    const int row0 = kvh * a.group;
+    const int nrows = a.group;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t rbase = static_cast<int64_t>(kvh) * a.kv_stride;
+    const int64_t ntiles = (a.t + 63) / 64;
+
+    const float cmax = fmaxf(fabsf(a.cent[L - 1]), fabsf(a.cent[0]));
+    int ce;
+    frexpf(cmax, &ce);
+    const float sc = cmax > 0.0f ? ldexpf(1.0f, 1 - ce) : 1.0f;   // |sc c| in [1, 2) at most
+    for (int p = threadIdx.x; p < L * L; p += kBlock) {
+        uint32_t h0, l0, h1, l1;
+        split_h11(a.cent[p & (L - 1)] * sc, &h0, &l0);
+        split_h11(a.cent[p >> B] * sc, &h1, &l1);
+        lds.ptab[p] = l0 | (l1 << 16);
+        lds.ptab[257 + p] = h0 | (h1 << 16);
+    }
+    for (int i = threadIdx.x; i < 4 * 64; i += kBlock) lds.w[i >> 6].code[W][i & 63] = 0u;
+    if constexpr (PAD) {
+        if (threadIdx.x < L) lds.centf[threadIdx.x] = a.cent[threadIdx.x];
+    }
+    if constexpr (QJL) {
+        for (int p = threadIdx.x; p < 256; p += kBlock) {
+            u32x4 e;
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                const uint32_t ba = (p >> nt) & 1u, bb = (p >> (4 + nt)) & 1u;
+                e[nt] = 0x3C003C00u | ((ba ^ 1u) << 15) | ((bb ^ 1u) << 31);
+            }
+            lds.sig[p] = e;
+        }
+    }
+    __syncthreads();
+
+    Wave& wv = lds.w[wave];
+    WaveW& wt = lds.wt[wave];
+    const int l = lane_id();
+    const int n = l & 31, hh = l >> 5;    // weights: key pair n of rows hh + 2 i
+    const int c = l & 15, g = l >> 4;     // MFMA operands
+    const bool live = c < nrows;
+    const rsrc_t rsc = make_rsrc(a.scores + static_cast<int64_t>(row0) * a.ld,
+                                 static_cast<uint32_t>(nrows * a.ld * 4));
+    const int ri = (nrows - hh + 1) >> 1;
+    float mrow[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mrow[i] = i < ri ? a.stats[row0 + hh + 2 * i].x : 0.0f;
+
+    f32x4 acc_c[8], acc_s[QJL ? 8 : 1];
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) acc_c[nt] = f32x4{};
+#pragma unroll
+    for (int nt = 0; nt < (QJL ? 8 : 1); ++nt) acc_s[nt] = f32x4{};
+    float padacc[PAD ? 8 : 1];
+#pragma unroll
+    for (int i = 0; i < (PAD ? 8 : 1); ++i) padacc[i] = 0.0f;
+
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    struct TileIn {
+        u32x2 sp[8];
+        uint32_t cw[W];
+        uint32_t sw[4];
+        uint32_t nb, gb;
+    };
+    auto fetch = [&](int64_t tile, TileIn& r) {
+        const int64_t kbase = tile * 64;
+        const uint32_t soff = static_cast<uint32_t>((hh * a.ld + kbase + 2 * n) * 4);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (i < ri) r.sp[i] = __builtin_amdgcn_raw_buffer_load_b64(rsc, soff, static_cast<int>(2 * i * a.ld * 4),
+                                                                      kNonTemporal);
+        const int64_t left = a.t - kbase;
+        int64_t row = rbase + kbase;
+        if (a.pt.pages != nullptr) {
+            const int64_t pg = a.pt.pages[kvh * a.pt.stride + (kbase >> a.pt.shift)];
+            row = (pg << a.pt.shift) + (kbase & ((int64_t(1) << a.pt.shift) - 1));
+        }
+        const rsrc_t rc = make_rsrc(a.codes + row * W, tile_range(left, 4 * W));
+#pragma unroll
+        for (int it = 0; it < W; ++it)
+            r.cw[it] = __builtin_amdgcn_raw_buffer_load_b32(rc, static_cast<uint32_t>(4 * l), 256 * it, kNonTemporal);
+        if constexpr (QJL) {
+            const rsrc_t rs = make_rsrc(a.signs + row * 4, tile_range(left, 16));
+#pragma unroll
+            for (int it = 0; it < 4; ++it)
+                r.sw[it] = __builtin_amdgcn_raw_buffer_load_b32(rs, static_cast<uint32_t>(4 * l), 256 * it, kNonTemporal);
+        }
+        const rsrc_t rn = make_rsrc(a.norms + row, tile_range(left, 2));
+        r.nb = __builtin_amdgcn_raw_buffer_load_b16(rn, static_cast<uint32_t>(2 * l), 0, kNonTemporal);
+        r.gb = 0u;
+        if constexpr (QJL) {
+            const rsrc_t rg = make_rsrc(a.rnorms + row, tile_range(left, 2));
+            r.gb = __builtin_amdgcn_raw_buffer_load_b16(rg, static_cast<uint32_t>(2 * l), 0, kNonTemporal);
+        }
+    };
+
+    const int64_t tstep = gridDim.x * 4LL;
+    TileIn nx;
+    if (blockIdx.x * 4LL + wave < ntiles) fetch(blockIdx.x * 4LL + wave, nx);
+    for (int64_t tile = blockIdx.x * 4LL + wave; tile < ntiles; tile += tstep) {
+        const int64_t kbase = tile * 64;
+        const int kleft = static_cast<int>(a.t - kbase < 64 ? a.t - kbase : 64);
+        u32x2 sp[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sp[i] = nx.sp[i];
+        wave_lds_sync();
+#pragma unroll
+        for (int it = 0; it < W; ++it) {
+            const int d = it * 64 + l;
+            wv.code[d % W][d / W] = nx.cw[it];
+        }
+        if constexpr (QJL) {
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                const int d = it * 64 + l;
+                wv.sign[d & 3][d >> 2] = nx.sw[it];
+            }
+            wv.gam[l] = static_cast<uint16_t>(nx.gb);
+        }
+        wv.nrm[l] = static_cast<uint16_t>(nx.nb);
+        wave_lds_sync();
+        {
+            const uint32_t nn = *reinterpret_cast<const uint32_t*>(&wv.nrm[2 * n]);
+            uint32_t gg = 0u;
+            if constexpr (QJL) gg = *reinterpret_cast<const uint32_t*>(&wv.gam[2 * n]);
+            const float n0 = h2f(nn & 0xFFFFu), n1 = h2f(nn >> 16);
+            const float ga = h2f(gg & 0xFFFFu), gb = h2f(gg >> 16);
+            const bool in0 = 2 * n < kleft, in1 = 2 * n + 1 < kleft;
+            float cp0 = 0.0f, cp1 = 0.0f;   // centroids of the pad slot of keys 2 n, 2 n + 1
+            if constexpr (PAD) {
+                cp0 = lds.centf[wv.code[4 * B][2 * n] & (L - 1)];
+                cp1 = lds.centf[wv.code[4 * B][2 * n + 1] & (L - 1)];
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if (i < ri) {
+                    const uint32_t b0 = sp[i][0];
+                    const uint32_t b1 = sp[i][1];
+                    const float s0 = __builtin_bit_cast(float, b0), s1 = __builtin_bit_cast(float, b1);
+                    const float e0 = in0 ? exp2_hw((s0 * a.scale - mrow[i]) * kLog2e) : 0.0f;
+                    const float e1 = in1 ? exp2_hw((s1 * a.scale - mrow[i]) * kLog2e) : 0.0f;
+                    const float w0 = e0 * n0, w1 = e1 * n1;
+                    if constexpr (PAD) padacc[i] = __builtin_fmaf(w1, cp1, __builtin_fmaf(w0, cp0, padacc[i]));
+                    uint32_t h, lo;
+                    split_pair11(w0, w1, &h, &lo);
+                    wt.hi[0][hh + 2 * i][n] = h;
+                    wt.lo[0][hh + 2 * i][n] = lo;
+                    if constexpr (QJL) {
+                        split_pair11(w0 * ga, w1 * gb, &h, &lo);
+                        wt.hi[NK - 1][hh + 2 * i][n] = h;
+                        wt.lo[NK - 1][hh + 2 * i][n] = lo;
+                    }
+                }
+            }
+        }
+        wave_lds_sync();
+        if (tile + tstep < ntiles) fetch(tile + tstep, nx);
+
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int k0 = 32 * ks + 8 * g;   // the lane's first key of this K step
+            // A operands: row c's weights of keys k0 .. k0 + 7 (zero past the live rows)
+            u32x4 wh{}, wl{};
+            if (live) {
+                wh = *reinterpret_cast<const u32x4*>(&wt.hi[0][c][16 * ks + 4 * g]);
+                wl = *reinterpret_cast<const u32x4*>(&wt.lo[0][c][16 * ks + 4 * g]);
+            }
+            {
+                const int bit = 8 * B * c, wi = bit >> 5, off = bit & 31;
+                const u32x4 w0a = *reinterpret_cast<const u32x4*>(&wv.code[wi][k0]);
+                const u32x4 w0b = *reinterpret_cast<const u32x4*>(&wv.code[wi][k0 + 4]);
+                u32x4 w1a{}, w1b{};
+                if constexpr (STR) {
+                    w1a = *reinterpret_cast<const u32x4*>(&wv.code[wi + 1][k0]);
+                    w1b = *reinterpret_cast<const u32x4*>(&wv.code[wi + 1][k0 + 4]);
+                }
+                uint32_t fld[8];   // keys k0 .. k0 + 7: codes of coordinates 8 c .. 8 c + 7 from bit 0
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const uint32_t x0 = k < 4 ? w0a[k] : w0b[k - 4];
+                    if constexpr (STR) {
+                        const uint32_t x1 = k < 4 ? w1a[k] : w1b[k - 4];
+                        fld[k] = __builtin_amdgcn_alignbit(x1, x0, off);
+                    } else {
+                        fld[k] = x0 >> off;
+                    }
+                }
+#pragma unroll
+                for (int nt = 0; nt < 8; ++nt) {
+                    u32x4 b11, blo, bhi;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const uint32_t f0 = (fld[2 * q] >> (B * nt)) & (L - 1);
+                        const uint32_t f1 = (fld[2 * q + 1] >> (B * nt)) & (L - 1);
+                        const uint32_t ix = f0 | (f1 << B);
+                        const uint32_t hp = lds.ptab[257 + ix];
+                        blo[q] = lds.ptab[ix];
+                        bhi[q] = hp;
+                        b11[q] = pk_scale2048(hp);
+                    }
+                    acc_c[nt] = mfma16(wh, b11, acc_c[nt]);
+                    acc_c[nt] = mfma16(wh, blo, acc_c[nt]);
+                    acc_c[nt] = mfma16(wl, bhi, acc_c[nt]);
+                }
+            }
+            if constexpr (QJL) {
+                u32x4 swh{}, swl{};
+                if (live) {
+                    swh = *reinterpret_cast<const u32x4*>(&wt.hi[NK - 1][c][16 * ks + 4 * g]);
+                    swl = *reinterpret_cast<const u32x4*>(&wt.lo[NK - 1][c][16 * ks + 4 * g]);
+                }
+                // sign index 8 c + nt is bit nt of byte c % 4 of sign word c / 4;
+                // the low nibbles of two keys give N tiles 0..3, the high ones 4..7
+                const u32x4 sa = *reinterpret_cast<const u32x4*>(&wv.sign[c >> 2][k0]);
+                const u32x4 sb = *reinterpret_cast<const u32x4*>(&wv.sign[c >> 2][k0 + 4]);
+                const int sh = 8 * (c & 3);
+                uint32_t by[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const uint32_t x = k < 4 ? sa[k] : sb[k - 4];
+                    by[k] = (x >> sh) & 0xFFu;
+                }
+#pragma unroll
+                for (int hn = 0; hn < 2; ++hn) {
+                    u32x4 s1[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const uint32_t pb = ((by[2 * q] >> (4 * hn)) & 0xFu) | (((by[2 * q + 1] >> (4 * hn)) & 0xFu) << 4);
+                        const u32x4 e = lds.sig[pb];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const uint32_t ej = e[j];
+                            s1[j][q] = ej;
+                        }
+                    }
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        u32x4 s11;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const uint32_t v = s1[j][q];
+                            s11[q] = pk_scale2048(v);
+                        }
+                        acc_s[4 * hn + j] = mfma16(swh, s11, acc_s[4 * hn + j]);
+                        acc_s[4 * hn + j] = mfma16(swl, s1[j], acc_s[4 * hn + j]);
+                    }
+                }
+            }
+        }
+    }
+
+    // the block's partial rows: the four waves' sums added in wave order
+    // through LDS (over the weight tables, once every wave has left its
+    // tiles), then written as producer blockIdx.x
+    __syncthreads();
+    if constexpr (PAD) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int off = 16; off >= 1; off >>= 1) padacc[i] += __shfl_xor(padacc[i], off);
+    }
+    const float uc = 1.0f / (2048.0f * sc), us = 1.0f / 2048.0f;
+    for (int w = 0; w < 4; ++w) {
+        if (wave == w) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = 4 * g + i;
+                if (m < nrows) {
+                    float* dst = lds.sum[m];
+#pragma unroll
+                    for (int nt = 0; nt < 8; ++nt) {
+                        const int col = 8 * c + nt;
+                        const float cv = acc_c[nt][i] * uc;
+                        dst[col] = w == 0 ? cv : dst[col] + cv;
+                        if constexpr (QJL) {
+                            const float sv = acc_s[nt][i] * us;
+                            dst[kPartSigma + col] = w == 0 ? sv : dst[kPartSigma + col] + sv;
+                        }
+                    }
+                }
+            }
+            if (n == 0) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    if (i < ri) {
+                        float* dst = lds.sum[hh + 2 * i];
+                        float pc = 0.0f;
+                        if constexpr (PAD) pc = padacc[i];
+                        dst[kPartPad] = w == 0 ? pc : dst[kPartPad] + pc;
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+    float* out = a.part + (static_cast<int64_t>(blockIdx.x) * a.rows + row0) * kPartStride;
+    for (int i = threadIdx.x; i < nrows * kPartStride; i += kBlock) {
+        const int m = i / kPartStride, col = i % kPartStride;
+        const bool sig = col >= kPartSigma && col < kPartSigma + kD;
+        if (!sig || QJL)
+            out[static_cast<int64_t>(m) * kPartStride + col] =
+                (sig || col < kPartSigma || col == kPartPad) ? lds.sum[m][col] : 0.0f;
+    }
+}
+
 // ----------------------------------------------------- pass 4: combine --
 struct CombineArgs {
     const float* part;
@@ -569,9 +913,14 @@ AttendPlan attend_plan(int hq, int group, int64_t t, int plan_rows) {
     return p;
 }
 
-// Centroid sums, then (QJL) sign sums: two passes over the tiles.
+// Groups of at most 16 rows: both sums in one pass.  Larger groups:
+// centroid sums, then (QJL) sign sums, two passes over the tiles.
 template <int B, bool QJL, bool PAD>
 static void launch_values(const AttendArgs& a, const AttendPlan& p, int kv_heads, hipStream_t s) {
+    if (a.group <= 16) {
+        hipLaunchKernelGGL((attend_values16_kernel<B, QJL, PAD>), dim3(p.gx, kv_heads), dim3(kBlock), 0, s, a);
+        return;
+    }
     const int qblocks = (a.group + 31) / 32;
     const dim3 grid(p.gx, kv_heads * qblocks);
     hipLaunchKernelGGL((attend_values_kernel<B, false, PAD, true>), grid, dim3(kBlock), 0, s, a);

@@ -323,6 +323,13 @@ __device__ __forceinline__ f32x16 mfma(const u32x4& a, const u32x4& b, const f32
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
                                                  0, 0);
 }
+// 16x16x32: lane l holds row (A) or column (B) l % 16, K elements
+// 8 (l / 16) .. + 7; the result holds column l % 16, rows 4 (l / 16) .. + 3.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                 0, 0);
+}
 
 // Lane l holds X = its own vector's K-chunk 0 and Y = chunk 1 (8 halves each).
 // Returns the B (or A) operands for the tile's two 32-vector halves:

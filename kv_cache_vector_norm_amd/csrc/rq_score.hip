@@ -99,12 +99,6 @@ __device__ __forceinline__ u32x4 sigma8(uint32_t byte) {
     return d;
 }
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f32x4& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
-                                                 0, 0);
-}
-
 // One 16-bit record entry of key `idx` (relative to the tile base), 0 past n.
 __device__ __forceinline__ uint32_t half_at(const uint16_t* __restrict__ src, int64_t base, int64_t n, int idx) {
     const rsrc_t rs = make_rsrc(src + base, tile_range(n - base, 2));
