@@ -483,6 +483,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CODES ? 2 :
     }
 }
 
+// Exact split of a pair into bf16 hi = bf16(x) and lo = bf16(x - hi) (both
+// round to nearest even; x - hi is exact in fp32): x = hi + lo to 2^-18.
+__device__ __forceinline__ void split_pair_bf16(float a, float b, uint32_t* hi, uint32_t* lo) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
+    const float ha = __builtin_bit_cast(float, h << 16), hb = __builtin_bit_cast(float, h & 0xFFFF0000u);
+    *hi = h;
+    *lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a - ha, b - hb}), bf16x2));
+}
+__device__ __forceinline__ f32x4 mfma16_bf(const u32x4& a, const u32x4& b, const f32x4& c) {
+    typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                  0, 0);
+}
+
+// 8x8 bit matrix held in (lo, hi), row k = byte k (bytes 0..3 in lo, 4..7 in
+// hi), column j = bit j: transposed in place by three rounds of masked swaps
+// (1x1, 2x2 and 4x4 blocks), so that afterwards byte j holds column j.
+__device__ __forceinline__ void transpose8x8(uint32_t& lo, uint32_t& hi) {
+    uint32_t t;
+    t = (lo ^ (lo >> 7)) & 0x00AA00AAu;
+    lo ^= t ^ (t << 7);
+    t = (hi ^ (hi >> 7)) & 0x00AA00AAu;
+    hi ^= t ^ (t << 7);
+    t = (lo ^ (lo >> 14)) & 0x0000CCCCu;
+    lo ^= t ^ (t << 14);
+    t = (hi ^ (hi >> 14)) & 0x0000CCCCu;
+    hi ^= t ^ (t << 14);
+    t = (lo ^ (hi << 4)) & 0xF0F0F0F0u;
+    lo ^= t;
+    hi ^= t >> 4;
+}
+
 // Groups of at most 16 query rows (GQA 4:1 and 8:1): both weighted sums in
 // one pass over the tiles, on 16x16x32 MFMAs whose M dimension is the
 // group's rows (a 32-row M tile would carry 4 or 8 live rows of 32).  Per
@@ -492,7 +525,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CODES ? 2 :
 // (l % 16, l / 16) holds keys 32 ks + 8 g .. + 7 and, in N tile nt,
 // coordinate (sign index) 8 c + nt, so the lane's eight coordinates share
 // one field of 8 B code bits per key and one byte of its sign bits.  The
-// scores, norms and the staging are read once for both sums.
+// eight keys' sign bytes are gathered into an 8x8 bit matrix and transposed,
+// so that byte nt (their bits of sign index 8 c + nt) indexes the +-1
+// operand of N tile nt in one table read.  The sign sums run on bf16 MFMAs:
+// +-1 is exact in bf16, so the exact split of the weight into bf16 hi + lo
+// (2^-18 relative) multiplies one shared B operand.  The scores, norms and
+// the staging are read once for both sums.
 template <int B, bool QJL, bool PAD>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attend_values16_kernel(AttendArgs a) {
     constexpr int L = 1 << B;
@@ -507,13 +545,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
         alignas(16) uint16_t gam[64];
     };
     struct WaveW {
-        uint32_t hi[NK][16][WTS];         // [kind][row][key pair]: fp16 hi of the weights
-        uint32_t lo[NK][16][WTS];         // lo11 = half((w - hi) 2^11)
+        // [kind][row][key pair]: the weights of keys 2 q, 2 q + 1 split as fp16
+        // hi and lo11 = half((w - hi) 2^11) (kind 0), bf16 hi and lo (kind 1)
+        uint32_t hi[NK][16][WTS];
+        uint32_t lo[NK][16][WTS];
     };
     struct Lds {
-        uint32_t ptab[2 * 257];           // code pairs -> C_lo at [p], C_hi at [257 + p]
+        // code pairs -> C_lo at [p], C_hi at [257 + p] (1,028 bytes apart: no
+        // two-address read pairs them)
+        uint32_t ptab[2 * 257];
         float centf[PAD ? L : 1];
-        u32x4 sig[QJL ? 256 : 1];         // two keys' sign nibbles -> +-1 half pairs, per bit
+        // eight keys' bits of one sign index -> their +-1 as bf16 pairs
+        u32x4 sig[QJL ? 256 : 1];
         Wave w[4];
         union {
             WaveW wt[4];
@@ -545,12 +588,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
         if (threadIdx.x < L) lds.centf[threadIdx.x] = a.cent[threadIdx.x];
     }
     if constexpr (QJL) {
+        // sigma = 2 bit - 1 (the sign bit set where the stored bit is 0); dword
+        // q holds keys 2 q and 2 q + 1
         for (int p = threadIdx.x; p < 256; p += kBlock) {
             u32x4 e;
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                const uint32_t ba = (p >> nt) & 1u, bb = (p >> (4 + nt)) & 1u;
-                e[nt] = 0x3C003C00u | ((ba ^ 1u) << 15) | ((bb ^ 1u) << 31);
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t neg = ((((p >> (2 * q)) & 1u) ^ 1u) << 15) | ((((p >> (2 * q + 1)) & 1u) ^ 1u) << 31);
+                e[q] = 0x3F803F80u | neg;
             }
             lds.sig[p] = e;
         }
@@ -562,6 +607,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     const int l = lane_id();
     const int n = l & 31, hh = l >> 5;    // weights: key pair n of rows hh + 2 i
     const int c = l & 15, g = l >> 4;     // MFMA operands
+    // byte c % 4 of two sign words into bytes 0, 1 (selA) or 2, 3 (selB) of a dword
+    const uint32_t sb4 = static_cast<uint32_t>(c & 3);
+    const uint32_t selA = sb4 | ((4u + sb4) << 8) | 0x0C0C0000u;
+    const uint32_t selB = 0x00000C0Cu | (sb4 << 16) | ((4u + sb4) << 24);
     const bool live = c < nrows;
     const rsrc_t rsc = make_rsrc(a.scores + static_cast<int64_t>(row0) * a.ld,
                                  static_cast<uint32_t>(nrows * a.ld * 4));
@@ -670,7 +719,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
                     wt.hi[0][hh + 2 * i][n] = h;
                     wt.lo[0][hh + 2 * i][n] = lo;
                     if constexpr (QJL) {
-                        split_pair11(w0 * ga, w1 * gb, &h, &lo);
+                        split_pair_bf16(w0 * ga, w1 * gb, &h, &lo);
                         wt.hi[NK - 1][hh + 2 * i][n] = h;
                         wt.lo[NK - 1][hh + 2 * i][n] = lo;
                     }
@@ -733,41 +782,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
                     swh = *reinterpret_cast<const u32x4*>(&wt.hi[NK - 1][c][16 * ks + 4 * g]);
                     swl = *reinterpret_cast<const u32x4*>(&wt.lo[NK - 1][c][16 * ks + 4 * g]);
                 }
-                // sign index 8 c + nt is bit nt of byte c % 4 of sign word c / 4;
-                // the low nibbles of two keys give N tiles 0..3, the high ones 4..7
+                // sign index 8 c + nt is bit nt of byte c % 4 of sign word c / 4:
+                // the eight keys' bytes, transposed, give one table index per N tile
                 const u32x4 sa = *reinterpret_cast<const u32x4*>(&wv.sign[c >> 2][k0]);
                 const u32x4 sb = *reinterpret_cast<const u32x4*>(&wv.sign[c >> 2][k0 + 4]);
-                const int sh = 8 * (c & 3);
-                uint32_t by[8];
+                uint32_t x[8];
 #pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    const uint32_t x = k < 4 ? sa[k] : sb[k - 4];
-                    by[k] = (x >> sh) & 0xFFu;
+                for (int k = 0; k < 4; ++k) {
+                    const uint32_t xa = sa[k], xb = sb[k];
+                    x[k] = xa;
+                    x[4 + k] = xb;
                 }
+                uint32_t blo = __builtin_amdgcn_perm(x[1], x[0], selA) | __builtin_amdgcn_perm(x[3], x[2], selB);
+                uint32_t bhi = __builtin_amdgcn_perm(x[5], x[4], selA) | __builtin_amdgcn_perm(x[7], x[6], selB);
+                transpose8x8(blo, bhi);
 #pragma unroll
-                for (int hn = 0; hn < 2; ++hn) {
-                    u32x4 s1[4];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const uint32_t pb = ((by[2 * q] >> (4 * hn)) & 0xFu) | (((by[2 * q + 1] >> (4 * hn)) & 0xFu) << 4);
-                        const u32x4 e = lds.sig[pb];
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const uint32_t ej = e[j];
-                            s1[j][q] = ej;
-                        }
-                    }
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        u32x4 s11;
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const uint32_t v = s1[j][q];
-                            s11[q] = pk_scale2048(v);
-                        }
-                        acc_s[4 * hn + j] = mfma16(swh, s11, acc_s[4 * hn + j]);
-                        acc_s[4 * hn + j] = mfma16(swl, s1[j], acc_s[4 * hn + j]);
-                    }
+                for (int nt = 0; nt < 8; ++nt) {
+                    const uint32_t p = ((nt < 4 ? blo : bhi) >> (8 * (nt & 3))) & 0xFFu;
+                    const u32x4 s1 = lds.sig[p];
+                    acc_s[nt] = mfma16_bf(swh, s1, acc_s[nt]);
+                    acc_s[nt] = mfma16_bf(swl, s1, acc_s[nt]);
                 }
             }
         }
@@ -783,7 +817,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 #pragma unroll
             for (int off = 16; off >= 1; off >>= 1) padacc[i] += __shfl_xor(padacc[i], off);
     }
-    const float uc = 1.0f / (2048.0f * sc), us = 1.0f / 2048.0f;
+    const float uc = 1.0f / (2048.0f * sc);
     for (int w = 0; w < 4; ++w) {
         if (wave == w) {
 #pragma unroll
@@ -797,7 +831,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
                         const float cv = acc_c[nt][i] * uc;
                         dst[col] = w == 0 ? cv : dst[col] + cv;
                         if constexpr (QJL) {
-                            const float sv = acc_s[nt][i] * us;
+                            const float sv = acc_s[nt][i];
                             dst[kPartSigma + col] = w == 0 ? sv : dst[kPartSigma + col] + sv;
                         }
                     }
