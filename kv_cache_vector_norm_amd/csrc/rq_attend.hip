@@ -516,6 +516,29 @@ __device__ __forceinline__ void transpose8x8(uint32_t& lo, uint32_t& hi) {
     hi ^= t >> 4;
 }
 
+// 8x8 matrix of 2-bit elements in d[0..3], row r in bits 16 (r % 2) .. + 15
+// of d[r / 2], element c of a row at bits 2 c, 2 c + 1: transposed in place
+// (masked swaps of 1x1, 2x2 and 4x4 blocks).
+__device__ __forceinline__ void transpose8x8_2b(uint32_t (&d)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t t = ((d[i] >> 14) ^ d[i]) & 0x0000CCCCu;
+        d[i] ^= t ^ (t << 14);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i += 2) {
+        const uint32_t t = ((d[i] >> 4) ^ d[i + 1]) & 0x0F0F0F0Fu;
+        d[i + 1] ^= t;
+        d[i] ^= t << 4;
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const uint32_t t = ((d[i] >> 8) ^ d[i + 2]) & 0x00FF00FFu;
+        d[i + 2] ^= t;
+        d[i] ^= t << 8;
+    }
+}
+
 // Groups of at most 16 query rows (GQA 4:1 and 8:1): both weighted sums in
 // one pass over the tiles, on 16x16x32 MFMAs whose M dimension is the
 // group's rows (a 32-row M tile would carry 4 or 8 live rows of 32).  Per
@@ -538,6 +561,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     constexpr int WTS = 36;               // weight-table row pitch (dwords)
     constexpr int NK = QJL ? 2 : 1;       // weight kinds: p n^, p n^ gamma^
     constexpr bool STR = 32 % (8 * B) != 0;   // 3-bit fields straddle code words
+    // 1- and 2-bit codes: the lane's 8 x 8 block of codes (keys x coordinates)
+    // is transposed, so that four keys' codes of one coordinate form the index
+    // of a table entry holding their four C_lo (or C_hi) halves
+    constexpr bool QV = B <= 2;
+    constexpr int NQV = QV ? 1 << (4 * B) : 1;
     struct alignas(16) Wave {
         uint32_t code[W + 1][68];         // [word][key], as in the two-pass kernel
         uint32_t sign[QJL ? 4 : 1][68];
@@ -552,8 +580,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     };
     struct Lds {
         // code pairs -> C_lo at [p], C_hi at [257 + p] (1,028 bytes apart: no
-        // two-address read pairs them)
-        uint32_t ptab[2 * 257];
+        // two-address read pairs them); 1- and 2-bit codes: four codes -> C_lo
+        // halves at qtab[p], C_hi at qtab[257 + p] (2,056 bytes apart)
+        uint32_t ptab[QV ? 1 : 2 * 257];
+        uint2 qtab[QV ? 257 + NQV : 1];
         float centf[PAD ? L : 1];
         // eight keys' bits of one sign index -> their +-1 as bf16 pairs
         u32x4 sig[QJL ? 256 : 1];
@@ -576,12 +606,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     int ce;
     frexpf(cmax, &ce);
     const float sc = cmax > 0.0f ? ldexpf(1.0f, 1 - ce) : 1.0f;   // |sc c| in [1, 2) at most
-    for (int p = threadIdx.x; p < L * L; p += kBlock) {
-        uint32_t h0, l0, h1, l1;
-        split_h11(a.cent[p & (L - 1)] * sc, &h0, &l0);
-        split_h11(a.cent[p >> B] * sc, &h1, &l1);
-        lds.ptab[p] = l0 | (l1 << 16);
-        lds.ptab[257 + p] = h0 | (h1 << 16);
+    if constexpr (QV) {
+        for (int p = threadIdx.x; p < NQV; p += kBlock) {
+            uint32_t h[4], o[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) split_h11(a.cent[(p >> (B * k)) & (L - 1)] * sc, &h[k], &o[k]);
+            lds.qtab[p] = make_uint2(o[0] | (o[1] << 16), o[2] | (o[3] << 16));
+            lds.qtab[257 + p] = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+        }
+    } else {
+        for (int p = threadIdx.x; p < L * L; p += kBlock) {
+            uint32_t h0, l0, h1, l1;
+            split_h11(a.cent[p & (L - 1)] * sc, &h0, &l0);
+            split_h11(a.cent[p >> B] * sc, &h1, &l1);
+            lds.ptab[p] = l0 | (l1 << 16);
+            lds.ptab[257 + p] = h0 | (h1 << 16);
+        }
     }
     for (int i = threadIdx.x; i < 4 * 64; i += kBlock) lds.w[i >> 6].code[W][i & 63] = 0u;
     if constexpr (PAD) {
@@ -758,6 +798,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
                         fld[k] = x0 >> off;
                     }
                 }
+                if constexpr (QV) {
+                    // rows of the transposed block: the 8 keys' codes of
+                    // coordinate 8 c + nt, key k at bit B k
+                    uint32_t tr[4];
+                    if constexpr (B == 2) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) tr[i] = __builtin_amdgcn_perm(fld[2 * i + 1], fld[2 * i], 0x05040100u);
+                        transpose8x8_2b(tr);
+                    } else {
+                        tr[0] = __builtin_amdgcn_perm(fld[1], fld[0], 0x0C0C0400u) |
+                                __builtin_amdgcn_perm(fld[3], fld[2], 0x04000C0Cu);
+                        tr[1] = __builtin_amdgcn_perm(fld[5], fld[4], 0x0C0C0400u) |
+                                __builtin_amdgcn_perm(fld[7], fld[6], 0x04000C0Cu);
+                        transpose8x8(tr[0], tr[1]);
+                    }
+#pragma unroll
+                    for (int nt = 0; nt < 8; ++nt) {
+                        const uint32_t v = B == 2 ? tr[nt >> 1] >> (16 * (nt & 1)) : tr[nt >> 2] >> (8 * (nt & 3));
+                        const uint32_t i0 = v & (NQV - 1), i1 = (v >> (4 * B)) & (NQV - 1);
+                        const uint2 l0 = lds.qtab[i0], l1 = lds.qtab[i1];
+                        const uint2 h0 = lds.qtab[257 + i0], h1 = lds.qtab[257 + i1];
+                        const u32x4 blo = u32x4{l0.x, l0.y, l1.x, l1.y};
+                        const u32x4 bhi = u32x4{h0.x, h0.y, h1.x, h1.y};
+                        u32x4 b11;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const uint32_t hq = bhi[q];
+                            b11[q] = pk_scale2048(hq);
+                        }
+                        acc_c[nt] = mfma16(wh, b11, acc_c[nt]);
+                        acc_c[nt] = mfma16(wh, blo, acc_c[nt]);
+                        acc_c[nt] = mfma16(wl, bhi, acc_c[nt]);
+                    }
+                } else {
 #pragma unroll
                 for (int nt = 0; nt < 8; ++nt) {
                     u32x4 b11, blo, bhi;
@@ -774,6 +848,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
                     acc_c[nt] = mfma16(wh, b11, acc_c[nt]);
                     acc_c[nt] = mfma16(wh, blo, acc_c[nt]);
                     acc_c[nt] = mfma16(wl, bhi, acc_c[nt]);
+                }
                 }
             }
             if constexpr (QJL) {
