@@ -813,24 +813,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
                                 __builtin_amdgcn_perm(fld[7], fld[6], 0x04000C0Cu);
                         transpose8x8(tr[0], tr[1]);
                     }
-#pragma unroll
-                    for (int nt = 0; nt < 8; ++nt) {
+                    // table reads run one N tile ahead of their MFMAs
+                    u32x4 blo[2], bhi[2];
+                    auto qread = [&](int nt, u32x4& lo4, u32x4& hi4) __attribute__((always_inline)) {
                         const uint32_t v = B == 2 ? tr[nt >> 1] >> (16 * (nt & 1)) : tr[nt >> 2] >> (8 * (nt & 3));
                         const uint32_t i0 = v & (NQV - 1), i1 = (v >> (4 * B)) & (NQV - 1);
                         const uint2 l0 = lds.qtab[i0], l1 = lds.qtab[i1];
                         const uint2 h0 = lds.qtab[257 + i0], h1 = lds.qtab[257 + i1];
-                        const u32x4 blo = u32x4{l0.x, l0.y, l1.x, l1.y};
-                        const u32x4 bhi = u32x4{h0.x, h0.y, h1.x, h1.y};
+                        lo4 = u32x4{l0.x, l0.y, l1.x, l1.y};
+                        hi4 = u32x4{h0.x, h0.y, h1.x, h1.y};
+                    };
+                    qread(0, blo[0], bhi[0]);
+#pragma unroll
+                    for (int nt = 0; nt < 8; ++nt) {
+                        __builtin_amdgcn_sched_barrier(0);
+                        if (nt < 7) qread(nt + 1, blo[(nt + 1) & 1], bhi[(nt + 1) & 1]);
+                        const u32x4 lo4 = blo[nt & 1], hi4 = bhi[nt & 1];
                         u32x4 b11;
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
-                            const uint32_t hq = bhi[q];
+                            const uint32_t hq = hi4[q];
                             b11[q] = pk_scale2048(hq);
                         }
                         acc_c[nt] = mfma16(wh, b11, acc_c[nt]);
-                        acc_c[nt] = mfma16(wh, blo, acc_c[nt]);
-                        acc_c[nt] = mfma16(wl, bhi, acc_c[nt]);
+                        acc_c[nt] = mfma16(wh, lo4, acc_c[nt]);
+                        acc_c[nt] = mfma16(wl, hi4, acc_c[nt]);
                     }
+                    __builtin_amdgcn_sched_barrier(0);
                 } else {
 #pragma unroll
                 for (int nt = 0; nt < 8; ++nt) {
@@ -871,12 +880,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
                 uint32_t blo = __builtin_amdgcn_perm(x[1], x[0], selA) | __builtin_amdgcn_perm(x[3], x[2], selB);
                 uint32_t bhi = __builtin_amdgcn_perm(x[5], x[4], selA) | __builtin_amdgcn_perm(x[7], x[6], selB);
                 transpose8x8(blo, bhi);
+                // all eight table reads before the MFMAs
+                u32x4 s1[8];
+#pragma unroll
+                for (int nt = 0; nt < 8; ++nt) s1[nt] = lds.sig[((nt < 4 ? blo : bhi) >> (8 * (nt & 3))) & 0xFFu];
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int nt = 0; nt < 8; ++nt) {
-                    const uint32_t p = ((nt < 4 ? blo : bhi) >> (8 * (nt & 3))) & 0xFFu;
-                    const u32x4 s1 = lds.sig[p];
-                    acc_s[nt] = mfma16_bf(swh, s1, acc_s[nt]);
-                    acc_s[nt] = mfma16_bf(swl, s1, acc_s[nt]);
+                    acc_s[nt] = mfma16_bf(swh, s1[nt], acc_s[nt]);
+                    acc_s[nt] = mfma16_bf(swl, s1[nt], acc_s[nt]);
                 }
             }
         }
