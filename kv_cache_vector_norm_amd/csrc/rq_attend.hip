@@ -548,12 +548,11 @@ __device__ __forceinline__ void transpose8x8_2b(uint32_t (&d)[4]) {
 // (l % 16, l / 16) holds keys 32 ks + 8 g .. + 7 and, in N tile nt,
 // coordinate (sign index) 8 c + nt, so the lane's eight coordinates share
 // one field of 8 B code bits per key and one byte of its sign bits.  The
-// eight keys' sign bytes are gathered into an 8x8 bit matrix and transposed,
-// so that byte nt (their bits of sign index 8 c + nt) indexes the +-1
-// operand of N tile nt in one table read.  The sign sums run on bf16 MFMAs:
-// +-1 is exact in bf16, so the exact split of the weight into bf16 hi + lo
-// (2^-18 relative) multiplies one shared B operand.  The scores, norms and
-// the staging are read once for both sums.
+// sign sums run on bf16 MFMAs: +-1 is exact in bf16, so the exact split of
+// the weight into bf16 hi + lo (2^-18 relative) multiplies one shared B
+// operand, which is built on the VALU from the eight keys' sign bytes (a
+// shift, a mask and byte permutes: LDS bandwidth bounds this loop, so no
+// table).  The scores, norms and the staging are read once for both sums.
 template <int B, bool QJL, bool PAD>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attend_values16_kernel(AttendArgs a) {
     constexpr int L = 1 << B;
@@ -585,8 +584,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
         uint32_t ptab[QV ? 1 : 2 * 257];
         uint2 qtab[QV ? 257 + NQV : 1];
         float centf[PAD ? L : 1];
-        // eight keys' bits of one sign index -> their +-1 as bf16 pairs
-        u32x4 sig[QJL ? 256 : 1];
         Wave w[4];
         union {
             WaveW wt[4];
@@ -626,19 +623,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     for (int i = threadIdx.x; i < 4 * 64; i += kBlock) lds.w[i >> 6].code[W][i & 63] = 0u;
     if constexpr (PAD) {
         if (threadIdx.x < L) lds.centf[threadIdx.x] = a.cent[threadIdx.x];
-    }
-    if constexpr (QJL) {
-        // sigma = 2 bit - 1 (the sign bit set where the stored bit is 0); dword
-        // q holds keys 2 q and 2 q + 1
-        for (int p = threadIdx.x; p < 256; p += kBlock) {
-            u32x4 e;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint32_t neg = ((((p >> (2 * q)) & 1u) ^ 1u) << 15) | ((((p >> (2 * q + 1)) & 1u) ^ 1u) << 31);
-                e[q] = 0x3F803F80u | neg;
-            }
-            lds.sig[p] = e;
-        }
     }
     __syncthreads();
 
@@ -877,13 +861,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
                     x[k] = xa;
                     x[4 + k] = xb;
                 }
-                uint32_t blo = __builtin_amdgcn_perm(x[1], x[0], selA) | __builtin_amdgcn_perm(x[3], x[2], selB);
-                uint32_t bhi = __builtin_amdgcn_perm(x[5], x[4], selA) | __builtin_amdgcn_perm(x[7], x[6], selB);
-                transpose8x8(blo, bhi);
-                // all eight table reads before the MFMAs
+                const uint32_t glo = __builtin_amdgcn_perm(x[1], x[0], selA) | __builtin_amdgcn_perm(x[3], x[2], selB);
+                const uint32_t ghi = __builtin_amdgcn_perm(x[5], x[4], selA) | __builtin_amdgcn_perm(x[7], x[6], selB);
+                // byte k of glo / ghi: key k's (k + 4's) byte.  Operand of N tile
+                // nt: the high byte of key k's bf16 +-1 is 0x3F or 0xBF by bit nt
+                // of that byte, the low byte 0x80; one byte permute per dword
                 u32x4 s1[8];
 #pragma unroll
-                for (int nt = 0; nt < 8; ++nt) s1[nt] = lds.sig[((nt < 4 ? blo : bhi) >> (8 * (nt & 3))) & 0xFFu];
+                for (int nt = 0; nt < 8; ++nt) {
+                    const uint32_t ylo = ((glo << (7 - nt)) & 0x80808080u) ^ 0xBFBFBFBFu;
+                    const uint32_t yhi = ((ghi << (7 - nt)) & 0x80808080u) ^ 0xBFBFBFBFu;
+                    s1[nt] = u32x4{__builtin_amdgcn_perm(ylo, 0x80808080u, 0x05000400u),
+                                   __builtin_amdgcn_perm(ylo, 0x80808080u, 0x07000600u),
+                                   __builtin_amdgcn_perm(yhi, 0x80808080u, 0x05000400u),
+                                   __builtin_amdgcn_perm(yhi, 0x80808080u, 0x07000600u)};
+                }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int nt = 0; nt < 8; ++nt) {
