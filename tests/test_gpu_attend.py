@@ -72,6 +72,13 @@ CODECS = [
     ((4, OP.DENSE | OP.QJL), (3, OP.DENSE)),
     ((3, OP.MSE), (3, OP.DENSE | OP.QJL)),
     ((5, OP.QJL), (1, OP.MSE)),
+    # value codes of every width with and without signs (1- and 2-bit codes
+    # go through the transposed four-key tables, 3- and 4-bit ones by pairs)
+    ((3, OP.QJL), (2, OP.QJL)),
+    ((3, OP.QJL), (4, OP.QJL)),
+    ((2, OP.QJL), (3, OP.MSE)),
+    ((3, OP.MSE), (5, OP.DENSE | OP.QJL)),
+    ((3, OP.QJL), (2, OP.DENSE | OP.QJL)),
 ]
 
 
@@ -88,7 +95,9 @@ def test_attend_codecs(K, kspec, vspec, t):
 
 
 @pytest.mark.parametrize("t,hq,group,stride", [(63, 4, 4, None), (130, 6, 1, 140), (257, 16, 8, 300),
-                                                (700, 40, 40, None), (64, 64, 32, 64), (2049, 8, 2, None)])
+                                                (700, 40, 40, None), (64, 64, 32, 64), (2049, 8, 2, None),
+                                                (300, 16, 16, None), (129, 48, 16, 140), (200, 9, 3, None),
+                                                (150, 17, 17, None)])
 def test_attend_shapes(K, t, hq, group, stride):
     stride = t if stride is None else stride
     kc, vc = K.Codec(bits=3, seed=0, mode=OP.QJL), K.Codec(bits=3, seed=0, mode=OP.MSE)
