@@ -639,22 +639,43 @@ __global__ __launch_bounds__(kPqWaves * 64) void pq_attend_values_kernel(PolarDe
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x16{};
 
-    for (int64_t tile = blockIdx.x * (int64_t)kPqWaves + wave; tile < ntiles; tile += gridDim.x * (int64_t)kPqWaves) {
-        const int64_t kbase = tile * 64;
-        const int kleft = static_cast<int>(a.t - kbase < 64 ? a.t - kbase : 64);   // live keys of the tile
-        const int z = opaque_zero();
-        const int lz = l + z;
-        // estimates of row n for keys 16 kb + 8 hh .. + 7
+    // One tile's inputs, fetched a tile ahead of their use: the estimates of
+    // row n for keys 16 kb + 8 hh .. + 7, and dword it * 64 + l of the tile's
+    // record run.
+    struct PvIn {
         u32x4 sv[4][2];
+        uint32_t rw[kPolarWords];
+    };
+    auto fetch = [&](int64_t tile, PvIn& r) {
+        const int64_t kbase = tile * 64;
         const uint32_t soff = static_cast<uint32_t>((n * a.ld + kbase + 8 * hh) * 4);
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
             for (int q = 0; q < 2; ++q)
-                sv[kb][q] = __builtin_amdgcn_raw_buffer_load_b128(rsc, soff, 64 * kb + 16 * q, kNonTemporal);
-        // key lz's record (zero past the end) and its radii norm
+                r.sv[kb][q] = __builtin_amdgcn_raw_buffer_load_b128(rsc, soff, 64 * kb + 16 * q, kNonTemporal);
+        const rsrc_t rs = make_rsrc(a.words + (rbase + kbase) * kPolarWords, tile_range(a.t - kbase, 4 * kPolarWords));
+#pragma unroll
+        for (int it = 0; it < kPolarWords; ++it)
+            r.rw[it] = __builtin_amdgcn_raw_buffer_load_b32(rs, static_cast<uint32_t>(4 * l), 256 * it, kNonTemporal);
+    };
+    const int64_t tstep = gridDim.x * (int64_t)kPqWaves;
+    PvIn nx;
+    if (blockIdx.x * (int64_t)kPqWaves + wave < ntiles) fetch(blockIdx.x * (int64_t)kPqWaves + wave, nx);
+    for (int64_t tile = blockIdx.x * (int64_t)kPqWaves + wave; tile < ntiles; tile += tstep) {
+        const int64_t kbase = tile * 64;
+        const int kleft = static_cast<int>(a.t - kbase < 64 ? a.t - kbase : 64);   // live keys of the tile
+        const int z = opaque_zero();
+        const int lz = l + z;
+        // key lz's record (zero past the end) through the stage, and its radii norm
         uint32_t w[kPolarWords];
-        words_load<kPolarWords>(a.words + rbase * kPolarWords, kbase, a.t, w, stage, lz);
+        wave_lds_sync();
+#pragma unroll
+        for (int it = 0; it < kPolarWords; ++it) stage[it * 64 + lz] = nx.rw[it];
+        wave_lds_sync();
+#pragma unroll
+        for (int k = 0; k < kPolarWords; ++k) w[k] = stage[lz * kPolarWords + k];
+        wave_lds_sync();
         float R[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) R[i] = h2f((w[12 + (i >> 1)] >> (16 * (i & 1))) & 0xFFFFu);
@@ -676,7 +697,7 @@ __global__ __launch_bounds__(kPqWaves * 64) void pq_attend_values_kernel(PolarDe
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
                     const int k = 2 * q + e;
-                    const uint32_t sbits = sv[kb][k >> 2][k & 3];
+                    const uint32_t sbits = nx.sv[kb][k >> 2][k & 3];
                     const float sc = __builtin_bit_cast(float, sbits);
                     const bool in = live && k0 + k < kleft;
                     const float ex = in ? __builtin_amdgcn_exp2f((sc * a.scale - mrow) * 1.44269504088896341f) : 0.0f;
@@ -687,6 +708,7 @@ __global__ __launch_bounds__(kPqWaves * 64) void pq_attend_values_kernel(PolarDe
                 wl[kb][q] = cvt_pk((w2[0] - h2f(h & 0xFFFFu)) * 2048.0f, (w2[1] - h2f(h >> 16)) * 2048.0f);
             }
         }
+        if (tile + tstep < ntiles) fetch(tile + tstep, nx);
         // y~ / ||r||, 32 coordinates (M tile MT of the dequantiser) at a time
 #pragma unroll
         for (int MT = 0; MT < 4; ++MT) {
