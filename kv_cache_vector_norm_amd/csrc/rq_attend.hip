@@ -12,8 +12,9 @@
 // (X^T = the inverse rotor sandwich, or Pi^T; kappa = sqrt(pi/2)/m), so
 //   sum_t p_t v~_t = X^T (sum_t p_t n^_t c_t) + kappa S^T (sum_t p_t n^_t gamma^_t sigma_t).
 // The two sums are products of a weight matrix [rows x keys] with the
-// centroid / sign matrices [keys x coordinates] and run on 32x32x16 fp16
-// MFMAs; X^T and S^T are applied once per query row at the end.  PolarQuant
+// centroid / sign matrices [keys x coordinates] and run on MFMAs (32x32x16
+// fp16 for groups of more than 16 query rows; 16x16x32, the signs in bf16,
+// for smaller groups); X^T and S^T are applied once per query row at the end.  PolarQuant
 // values are the one kind decoded (to y~ = Pi x~, in rq_polar.hip's value
 // pass): sum_t p_t v~_t = Pi^T (sum_t p_t y~_t), Pi^T once per row.  PolarQuant
 // keys are scored by pq_score in pass 1.
@@ -23,7 +24,8 @@
 //   2. per row M = max scale*s and L = sum exp(scale*s - M) (one pass, the
 //      running-maximum form);
 //   3. per (KV head, <= 32 rows, key slice) wave: the two weighted sums over
-//      its tiles in the rotated domain, written as partial rows;
+//      its tiles in the rotated domain, written as partial rows (one launch
+//      for groups of at most 16 rows, else one per sum);
 //   4. per row: sum the partials in a fixed order, apply X^T and kappa S^T,
 //      divide by L.
 #include "rq_common_dev.h"
