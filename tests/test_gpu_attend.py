@@ -109,6 +109,20 @@ def test_attend_shapes(K, t, hq, group, stride):
     _check(K, kc, vc, OP.QJL, 3, OP.MSE, 3, keys, vals, q, group, t, stride, 1 / np.sqrt(D))
 
 
+@pytest.mark.parametrize("vspec", [(2, OP.QJL), (4, OP.QJL), (5, OP.DENSE | OP.QJL), (3, OP.QJL)])
+def test_attend_several_tiles_per_wave(K, vspec):
+    """20,000 keys per KV head (two heads, GQA 4:1): some waves of the value
+    pass walk two 64-key tiles, carrying their sums and the staged tables
+    from one tile to the next (value codes 1 to 4 bits with signs)."""
+    vb, vm = vspec
+    kc, vc = K.Codec(bits=3, seed=0, mode=OP.QJL), K.Codec(bits=vb, seed=0, mode=vm)
+    t, hq, group = 20000, 8, 4
+    keys = W.gaussian(2 * t, seed=84, dtype=np.float16)
+    vals = W.gaussian(2 * t, seed=85, dtype=np.float16)
+    q = W.queries(hq, seed=86)
+    _check(K, kc, vc, OP.QJL, 3, vm, vb, keys, vals, q, group, t, t, 1 / np.sqrt(D))
+
+
 @pytest.mark.parametrize("scale", [0.0, 1.0, -0.3])
 def test_attend_scales(K, scale):
     """scale 0 is the plain mean; scale 1 makes the softmax sharp."""
