@@ -562,12 +562,30 @@ __global__ __launch_bounds__(kPqWaves * 64) void pq_score_kernel(PolarDev P, con
     float* out = scores + row0 * ld;
     uint32_t* stage = sm.stage[wave];
     const int64_t ntiles = (t + 63) / 64;
-    for (int64_t tt = blockIdx.x * (int64_t)kPqWaves + wave; tt < ntiles; tt += gridDim.x * (int64_t)kPqWaves) {
+    // dword it * 64 + l of a tile's record run, fetched a tile ahead of its use
+    uint32_t nx[kPolarWords];
+    auto fetch = [&](int64_t tt) {
+        const rsrc_t rs = make_rsrc(kw + tt * 64 * kPolarWords, tile_range(t - tt * 64, 4 * kPolarWords));
+#pragma unroll
+        for (int it = 0; it < kPolarWords; ++it)
+            nx[it] = __builtin_amdgcn_raw_buffer_load_b32(rs, static_cast<uint32_t>(4 * l), 256 * it, kNonTemporal);
+    };
+    const int64_t tstep = gridDim.x * (int64_t)kPqWaves;
+    if (blockIdx.x * (int64_t)kPqWaves + wave < ntiles) fetch(blockIdx.x * (int64_t)kPqWaves + wave);
+    for (int64_t tt = blockIdx.x * (int64_t)kPqWaves + wave; tt < ntiles; tt += tstep) {
         const int64_t base = tt * 64;
         const int z = opaque_zero();
         const int lz = lane_id() + z;
+        // key lz's record through the stage (zero past the end)
         uint32_t w[kPolarWords];
-        words_load<kPolarWords>(kw, base, t, w, stage, lz);
+        wave_lds_sync();
+#pragma unroll
+        for (int it = 0; it < kPolarWords; ++it) stage[it * 64 + lz] = nx[it];
+        wave_lds_sync();
+#pragma unroll
+        for (int k = 0; k < kPolarWords; ++k) w[k] = stage[lz * kPolarWords + k];
+        wave_lds_sync();
+        if (tt + tstep < ntiles) fetch(tt + tstep);
         float s0[16], s1[16];
         const float rn = pq_decode_rot(
                              sm.tab, w, [&](int row, int chunk) { return mat_frag(sm.ah, row, chunk); },
