@@ -108,6 +108,12 @@ struct AttendArgs {
     const float* cent;        // value centroids
     float* part;              // [producers][rows][kPartStride]
     PageTable pt;             // value record rows (pages == nullptr: kvh * kv_stride + key)
+    // groups of at most 16 rows, row statistics taken here: the scoring
+    // launch's per-workgroup maxima ([rm_n][rm_ld]) instead of stats; the
+    // partial rows then carry their sums of weights and the row maximum
+    const float* rowmax = nullptr;
+    int64_t rm_ld = 0;
+    int rm_n = 0;
 };
 
 // Exact split of a pair into fp16 hi and lo11 = half((x - hi) 2^11).
@@ -641,9 +647,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     const rsrc_t rsc = make_rsrc(a.scores + static_cast<int64_t>(row0) * a.ld,
                                  static_cast<uint32_t>(nrows * a.ld * 4));
     const int ri = (nrows - hh + 1) >> 1;
+    // row maxima: from the row statistics, or (rowmax) over the scoring
+    // launch's workgroups, reduced through LDS before the tile loop
+    const bool fused = a.rowmax != nullptr;
+    if (fused) {
+        const int r = threadIdx.x & 15, b0 = threadIdx.x >> 4;
+        float m = -INFINITY;
+        if (r < nrows)
+            for (int b = b0; b < a.rm_n; b += kBlock / 16) m = fmaxf(m, a.rowmax[b * a.rm_ld + row0 + r]);
+        lds.sum[r][b0] = m;
+        __syncthreads();
+        if (threadIdx.x < 16) {
+            float mm = lds.sum[threadIdx.x][0];
+            for (int b = 1; b < kBlock / 16; ++b) mm = fmaxf(mm, lds.sum[threadIdx.x][b]);
+            lds.sum[threadIdx.x][kPartStride - 1] = mm;
+        }
+        __syncthreads();
+    }
     float mrow[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) mrow[i] = i < ri ? a.stats[row0 + hh + 2 * i].x : 0.0f;
+    for (int i = 0; i < 8; ++i)
+        mrow[i] = i < ri ? (fused ? lds.sum[hh + 2 * i][kPartStride - 1] : a.stats[row0 + hh + 2 * i].x) : 0.0f;
+    // (fused) this lane's sum of exp(scale s - M) of rows hh + 2 i over its keys
+    float lsum[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) lsum[i] = 0.0f;
+    __syncthreads();   // the maxima are read before the weight tables take their place
 
     f32x4 acc_c[8], acc_s[QJL ? 8 : 1];
 #pragma unroll
@@ -739,6 +768,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
                     const float e0 = in0 ? exp2_hw((s0 * a.scale - mrow[i]) * kLog2e) : 0.0f;
                     const float e1 = in1 ? exp2_hw((s1 * a.scale - mrow[i]) * kLog2e) : 0.0f;
                     const float w0 = e0 * n0, w1 = e1 * n1;
+                    lsum[i] += e0 + e1;
                     if constexpr (PAD) padacc[i] = __builtin_fmaf(w1, cp1, __builtin_fmaf(w0, cp0, padacc[i]));
                     uint32_t h, lo;
                     split_pair11(w0, w1, &h, &lo);
@@ -898,6 +928,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 #pragma unroll
             for (int off = 16; off >= 1; off >>= 1) padacc[i] += __shfl_xor(padacc[i], off);
     }
+    if (fused) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int off = 16; off >= 1; off >>= 1) lsum[i] += __shfl_xor(lsum[i], off);
+    }
     const float uc = 1.0f / (2048.0f * sc);
     for (int w = 0; w < 4; ++w) {
         if (wave == w) {
@@ -926,6 +962,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
                         float pc = 0.0f;
                         if constexpr (PAD) pc = padacc[i];
                         dst[kPartPad] = w == 0 ? pc : dst[kPartPad] + pc;
+                        dst[kPartPad + 1] = w == 0 ? lsum[i] : dst[kPartPad + 1] + lsum[i];
+                        dst[kPartPad + 2] = mrow[i];
                     }
                 }
             }
@@ -933,12 +971,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
         __syncthreads();
     }
     float* out = a.part + (static_cast<int64_t>(blockIdx.x) * a.rows + row0) * kPartStride;
+    // columns: centroid sums, (QJL) sign sums, the pad slot, and (fused) the
+    // sum of weights and the row maximum
     for (int i = threadIdx.x; i < nrows * kPartStride; i += kBlock) {
         const int m = i / kPartStride, col = i % kPartStride;
         const bool sig = col >= kPartSigma && col < kPartSigma + kD;
-        if (!sig || QJL)
-            out[static_cast<int64_t>(m) * kPartStride + col] =
-                (sig || col < kPartSigma || col == kPartPad) ? lds.sum[m][col] : 0.0f;
+        const bool keep = sig || col < kPartSigma || col == kPartPad || (fused && col <= kPartPad + 2);
+        if (!sig || QJL) out[static_cast<int64_t>(m) * kPartStride + col] = keep ? lds.sum[m][col] : 0.0f;
     }
 }
 
@@ -956,17 +995,33 @@ struct CombineArgs {
     float kappa;
     float* out;
     int64_t ld_out;
+    // the partial rows carry the sums of weights (column kPartPad + 1) and the
+    // row maximum (kPartPad + 2): their sum and that maximum are written to
+    // stats_out, which takes the place of the row statistics pass
+    float2* stats_out = nullptr;
 };
 
 __global__ __launch_bounds__(320) void attend_combine_kernel(CombineArgs a) {
     const int row = blockIdx.x;
     __shared__ float oc[kRotCoords + 3];
     __shared__ float os[kD];
+    __shared__ float lsum;
     const int j = threadIdx.x;
+    const bool fused = a.stats_out != nullptr;
     // producers in a fixed order: eight interleaved running sums (loads in
     // flight together), added pairwise at the end
-    const int col = j < kD ? j : (j < 2 * kD ? kPartSigma + (j - kD) : kPartPad);
-    if (j < 2 * kD + 1 && (j < kD || j == 2 * kD || a.qjl)) {
+    const int col = j < kD ? j : (j < 2 * kD ? kPartSigma + (j - kD) : kPartPad + (j - 2 * kD));
+    if (fused && j == 2 * kD + 1) {
+        float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+        const int64_t pstride = static_cast<int64_t>(a.rows) * kPartStride;
+        const float* src = a.part + static_cast<int64_t>(row) * kPartStride + col;
+        int64_t p = 0;
+        for (; p + 8 <= a.producers; p += 8)
+#pragma unroll
+            for (int u = 0; u < 8; ++u) acc[u] += src[(p + u) * pstride];
+        for (int u = 0; p < a.producers; ++p, ++u) acc[u] += src[p * pstride];
+        lsum = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+    } else if (j < 2 * kD + 1 && (j < kD || j == 2 * kD || a.qjl)) {
         float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
         const int64_t pstride = static_cast<int64_t>(a.rows) * kPartStride;
         const float* src = a.part + static_cast<int64_t>(row) * kPartStride + col;
@@ -1001,7 +1056,9 @@ __global__ __launch_bounds__(320) void attend_combine_kernel(CombineArgs a) {
             for (int k = 0; k < kD; ++k) y = __builtin_fmaf(h2f(a.s_rows[k * kD + j]), os[k], y);
             x = __builtin_fmaf(a.kappa, y, x);
         }
-        a.out[row * a.ld_out + j] = x / a.stats[row].y;
+        a.out[row * a.ld_out + j] = x / (fused ? lsum : a.stats[row].y);
+        if (fused && j == 0)
+            a.stats_out[row] = make_float2(a.part[static_cast<int64_t>(row) * kPartStride + kPartPad + 2], lsum);
     }
 }
 
@@ -1024,7 +1081,16 @@ AttendPlan attend_plan(int hq, int group, int64_t t, int plan_rows) {
     p.off_scores = 0;
     p.off_stats = up(static_cast<int64_t>(hq) * p.ld * 4);
     p.off_part = p.off_stats + up(static_cast<int64_t>(hq) * 8);
-    p.bytes = p.off_part + up(p.producers * hq * kPartStride * 4);
+    p.off_rowmax = p.off_part + up(p.producers * hq * kPartStride * 4);
+    // groups of at most 16 rows: the scoring launches' per-workgroup row maxima
+    int64_t rm = 0;
+    if (group <= 16) {
+        const int all = hq / group, chunk = kScoreChunkRows / group;
+        const int first = all < chunk ? all : chunk, last = all - (all - 1) / chunk * chunk;
+        const int a = score_slices16(t, first), b = score_slices16(t, last);
+        rm = static_cast<int64_t>(a > b ? a : b) * hq * 4;
+    }
+    p.bytes = p.off_rowmax + up(rm);
     return p;
 }
 
@@ -1065,21 +1131,41 @@ hipError_t attend(const ScoreTables& kt, const ScoreTables& vt, const float* q, 
     float2* stats = reinterpret_cast<float2*>(ws + p.off_stats);
     float* part = reinterpret_cast<float*>(ws + p.off_part);
     const int kv_heads = hq / group;
+    const int heads_per_chunk = group >= kScoreChunkRows ? 1 : kScoreChunkRows / group;
+    // Groups of at most 16 rows over rotor or dense keys and values: no row
+    // statistics pass.  The scoring launches leave per-workgroup row maxima,
+    // the value pass reduces them and sums its weights, and the combine adds
+    // those sums (and writes the statistics for later use) -- when every
+    // scoring chunk has the same number of workgroups.
+    int rm_n = 0;
+    bool fused = false;
+    if (group <= 16 && !kt.polar && !vt.polar) {
+        const int first = kv_heads < heads_per_chunk ? kv_heads : heads_per_chunk;
+        const int last = kv_heads - (kv_heads - 1) / heads_per_chunk * heads_per_chunk;
+        rm_n = score_slices16(t, first);
+        fused = score_slices16(t, last) == rm_n;
+    }
+    float* rowmax = fused ? reinterpret_cast<float*>(ws + p.off_rowmax) : nullptr;
     // 1. estimates, in chunks of whole KV heads (PolarQuant keys: one launch)
     if (kt.polar) {
         const hipError_t e = polar_score(kt.pol, q, hq, group, kcodes, t, kv_heads > 1 ? kv_stride : 0, scores, p.ld, s);
         if (e != hipSuccess) return e;
     }
-    const int heads_per_chunk = group >= kScoreChunkRows ? 1 : kScoreChunkRows / group;
     for (int h0 = 0; h0 < (kt.polar ? 0 : kv_heads); h0 += heads_per_chunk) {
         const int nh = kv_heads - h0 < heads_per_chunk ? kv_heads - h0 : heads_per_chunk;
+        RowMax rm;
+        if (fused) {
+            rm.ptr = rowmax + static_cast<int64_t>(h0) * group;
+            rm.ld = hq;
+            rm.scale = scale;
+        }
         const hipError_t e = score(kt, q + static_cast<int64_t>(h0) * group * kD, nh * group, group, kcodes, knorms,
                                    ksigns, krnorms, t, kv_stride, h0, scores + static_cast<int64_t>(h0) * group * p.ld,
-                                   p.ld, s, kpt);
+                                   p.ld, s, kpt, ScoreOutliers{}, rm);
         if (e != hipSuccess) return e;
     }
     // 2. row statistics
-    hipLaunchKernelGGL(attend_stats_kernel, dim3(hq), dim3(kBlock), 0, s, scores, p.ld, t, scale, stats);
+    if (!fused) hipLaunchKernelGGL(attend_stats_kernel, dim3(hq), dim3(kBlock), 0, s, scores, p.ld, t, scale, stats);
     // 3. weighted sums in the rotated domain (PolarQuant values: of y~)
     if (vt.polar) {
         PolarValueArgs pa;
@@ -1112,6 +1198,9 @@ hipError_t attend(const ScoreTables& kt, const ScoreTables& vt, const float* q, 
     a.cent = vt.dense ? vt.den.cent : vt.rot.cent;
     a.part = part;
     a.pt = vpt;
+    a.rowmax = rowmax;
+    a.rm_ld = hq;
+    a.rm_n = rm_n;
     hipError_t e = hipSuccess;
     if (vt.polar) {
         // (done above)
@@ -1137,6 +1226,7 @@ hipError_t attend(const ScoreTables& kt, const ScoreTables& vt, const float* q, 
     c.kappa = vt.qjl_scale;
     c.out = out;
     c.ld_out = ld_out;
+    c.stats_out = fused ? stats : nullptr;
     hipLaunchKernelGGL(attend_combine_kernel, dim3(hq), dim3(320), 0, s, c);
     return hipGetLastError();
 }

@@ -131,13 +131,28 @@ struct PageTable {
     int64_t stride = 0;     // table entries per KV head
 };
 
+// Optional output of the scoring kernel for groups of at most 16 rows (the
+// attention path): for each workgroup x of the launch and query row r of the
+// call, the largest scale * estimate over the workgroup's keys, at
+// ptr[x * ld + r] (-inf where it has none).
+struct RowMax {
+    float* ptr = nullptr;
+    int64_t ld = 0;
+    float scale = 0.0f;
+};
+
+// Workgroups along the keys of one scoring launch for groups of at most 16
+// rows over kv_heads KV heads of t keys (the launch's grid.x).
+int score_slices16(int64_t t, int kv_heads);
+
 // Scores hq query rows (group rows per KV head) against t keys per KV head;
 // KV head j (0-based within this call) reads record rows
 // (kv_head0 + j) * kv_stride + [0, t).
 hipError_t score(const ScoreTables& t, const float* q, int hq, int group, const uint32_t* codes,
                  const uint16_t* norms, const uint32_t* signs, const uint16_t* rnorms, int64_t tkeys,
                  int64_t kv_stride, int kv_head0, float* scores, int64_t ld_scores, hipStream_t s,
-                 const PageTable& pt = PageTable{}, const ScoreOutliers& so = ScoreOutliers{});
+                 const PageTable& pt = PageTable{}, const ScoreOutliers& so = ScoreOutliers{},
+                 const RowMax& rm = RowMax{});
 
 
 // A partial row of the attention value pass: centroid sums for coordinates
@@ -169,7 +184,7 @@ struct AttendPlan {
     int64_t ld;                      // row pitch of the estimates (floats)
     int gx;                          // key slices per (KV head, 32-row block)
     int64_t producers;               // partial rows per query row (one per key-slice block)
-    int64_t off_scores, off_stats, off_part, bytes;
+    int64_t off_scores, off_stats, off_part, off_rowmax, bytes;
 };
 // plan_rows: the query rows whose KV heads size the key slices (default
 // hq).  A call over several layers of a paged cache passes one layer's rows,

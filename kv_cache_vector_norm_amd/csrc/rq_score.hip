@@ -79,6 +79,7 @@ struct MainArgs {
     const uint8_t* ochans = nullptr;   // OUTL: outlier channels, [KV heads][ok]
     const uint16_t* outl = nullptr;    // OUTL: outlier halves of the keys, [record rows][ok]
     int ok = 0;                        // outlier channels per head (<= 16)
+    RowMax rm;                         // groups of at most 16 rows: per-workgroup row maxima
 };
 
 // Record row of the first key of the 64-key tile at key kbase of KV head
@@ -666,6 +667,8 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
                 }
             }
         }
+        // largest scale * estimate of rows 4 g .. 4 g + 3 over this lane's keys
+        float rmax[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
         for (; tile < ntiles; tile += tstep) {
             const int z = opaque_zero();
             const int l = lane_id() + z;
@@ -790,12 +793,32 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
                         }
                         v *= kn[j];
                         if constexpr (OUTL) v += ot[i][j];
-                        const uint32_t voff =
-                            kbase + key < nk ? static_cast<uint32_t>((row * a.ld + key) * 4) : 0x80000000u;
+                        const bool in = kbase + key < nk;
+                        const uint32_t voff = in ? static_cast<uint32_t>((row * a.ld + key) * 4) : 0x80000000u;
                         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rs, voff, 0,
                                                               kNonTemporal);
+                        if (a.rm.ptr != nullptr && in) rmax[i] = fmaxf(rmax[i], v * a.rm.scale);
                     }
                 }
+            }
+        }
+        if (a.rm.ptr != nullptr) {
+            // the 16 lanes of each row quad, then the four waves, through LDS
+            const int l = lane_id(), c = l & 15, g = l >> 4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int o = 1; o < 16; o <<= 1) rmax[i] = fmaxf(rmax[i], __shfl_xor(rmax[i], o));
+            __syncthreads();
+            if (c == 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) lds.part[0][wave][4 * g + i] = rmax[i];
+            }
+            __syncthreads();
+            if (t < nrows) {
+                const float m = fmaxf(fmaxf(lds.part[0][0][t], lds.part[0][1][t]),
+                                      fmaxf(lds.part[0][2][t], lds.part[0][3][t]));
+                a.rm.ptr[static_cast<int64_t>(blockIdx.x) * a.rm.ld + row0 + t] = m;
             }
         }
     } else {
@@ -995,15 +1018,20 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
 // as many as fill the workgroup slots of the chip in one round (two per CU
 // for the 32-row variant, one for the 64-row variant, whose LDS is larger);
 // each wave then walks many 64-key tiles.  At least one tile per wave.
-template <int B, bool QJL, bool PAD, int NMT, bool OUTL = false>
-static void launch_main(const MainArgs& a, int kv_heads, int qblocks, hipStream_t s) {
-    const int64_t ntiles = (a.t + 63) / 64;
+static int64_t score_slices(int64_t t, int64_t units, int nmt) {
+    const int64_t ntiles = (t + 63) / 64;
     const int64_t want = (ntiles + 3) / 4;
-    const int64_t slots = 256LL * (NMT < 2 ? 2 : 1);
-    const int64_t units = static_cast<int64_t>(kv_heads) * qblocks;
+    const int64_t slots = 256LL * (nmt < 2 ? 2 : 1);
     int64_t gx = slots / units;
     if (gx > want) gx = want;
     if (gx < 1) gx = 1;
+    return gx;
+}
+int score_slices16(int64_t t, int kv_heads) { return static_cast<int>(score_slices(t, kv_heads, 0)); }
+
+template <int B, bool QJL, bool PAD, int NMT, bool OUTL = false>
+static void launch_main(const MainArgs& a, int kv_heads, int qblocks, hipStream_t s) {
+    const int64_t gx = score_slices(a.t, static_cast<int64_t>(kv_heads) * qblocks, NMT);
     hipLaunchKernelGGL((score_kernel<B, QJL, PAD, NMT, OUTL>), dim3(static_cast<unsigned>(gx), kv_heads * qblocks),
                        dim3(kBlock), 0, s, a);
 }
@@ -1024,8 +1052,9 @@ static void launch_main_b(bool dense, int nmt, const MainArgs& a, int kv_heads, 
 hipError_t score(const ScoreTables& t, const float* q, int hq, int group, const uint32_t* codes,
                  const uint16_t* norms, const uint32_t* signs, const uint16_t* rnorms, int64_t tkeys,
                  int64_t kv_stride, int kv_head0, float* scores, int64_t ld_scores, hipStream_t s,
-                 const PageTable& pt, const ScoreOutliers& so) {
+                 const PageTable& pt, const ScoreOutliers& so, const RowMax& rm) {
     MainArgs a;
+    a.rm = rm;
     a.pt = pt;
     a.q = q;
     a.rotmat = t.rot.rotmat;
@@ -1048,6 +1077,7 @@ hipError_t score(const ScoreTables& t, const float* q, int hq, int group, const 
     const int kv_heads = hq / group;
     const int qblocks = (group + 63) / 64;
     const int nmt = a.rows_per_block > 32 ? 2 : a.rows_per_block > 16 ? 1 : 0;
+    if (rm.ptr != nullptr && nmt != 0) return hipErrorInvalidValue;
     if (so.chans) {
         if (t.mse_bits != 0 || !t.qjl) return hipErrorInvalidValue;
         a.ochans = so.chans;
