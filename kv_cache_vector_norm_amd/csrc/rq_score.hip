@@ -646,17 +646,20 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
 
     if constexpr (NMT == 0) {
         // Lane (c, g) = (l % 16, l / 16) serves keys 16 j + c (j = 0..3) of the
-        // 64-key tile and K slots 32 ks + 8 g .. + 7 of each 32-wide step; the
-        // A operand of step ks is chunk 4 ks + g of staged row c.  The block's
-        // query rows do not change, so the A operands are read from LDS once
-        // for all of the wave's tiles (Q1 = 2^11 Q2 is rebuilt by an exact
-        // packed multiply): LDS bandwidth bounds this loop.
+        // 64-key tile and, in the 32-wide K step ks, slots 32 g + 8 ks .. + 7
+        // (the order of the K slots is free; this one gives each lane 32
+        // consecutive slots, so their code bits are B consecutive words of
+        // the key's record and their sign bits one sign word, read once per
+        // key); the A operand of step ks is chunk 4 g + ks of staged row c.
+        // The block's query rows do not change, so the A operands are read from
+        // LDS once for all of the wave's tiles (Q1 = 2^11 Q2 is rebuilt by an
+        // exact packed multiply): LDS bandwidth bounds this loop.
         u32x4 aq2[4], aq3[4], ap1[4], ap2[4];
         {
             const int l = lane_id(), c = l & 15, g = l >> 4;
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                const int r = c * kRowStride + 4 * ks + g;
+                const int r = c * kRowStride + 4 * g + ks;
                 if constexpr (B > 0) {
                     aq2[ks] = lds.qrows[r + kOffQ2];
                     aq3[ks] = lds.qrows[r + kOffQ3];
@@ -674,7 +677,6 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
             const int l = lane_id() + z;
             const int c = l & 15, g = l >> 4;
             const int64_t kbase = tile * 64;
-            const int gb = 8 * B * g;   // this lane's first code bit within a K step
             uint32_t cs[4][4];          // [j][ks]: the lane's 8 B code bits, from bit 0
             float cpad[4] = {0.0f, 0.0f, 0.0f, 0.0f};
             if constexpr (B > 0) {
@@ -685,12 +687,18 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const uint32_t* kw = st + (16 * j + c) * W;
+                    // slots 32 g .. 32 g + 31: words B g .. B g + B - 1 of the key's
+                    // stream; step ks starts at bit 8 B ks of them (only 3-bit
+                    // codes straddle words)
+                    uint32_t lw[B];
+#pragma unroll
+                    for (int k = 0; k < B; ++k) lw[k] = kw[B * g + k];
 #pragma unroll
                     for (int ks = 0; ks < 4; ++ks) {
-                        // bit B (32 ks + 8 g) of the key's stream; only 3-bit codes straddle words
-                        const uint32_t* wp = kw + B * ks + (gb >> 5);
-                        if constexpr (B == 3) cs[j][ks] = __builtin_amdgcn_alignbit(wp[1], wp[0], gb & 31);
-                        else cs[j][ks] = wp[0] >> (gb & 31);
+                        const int bit = 8 * B * ks, wi = bit >> 5, off = bit & 31;
+                        if (off + 8 * B > 32)
+                            cs[j][ks] = __builtin_amdgcn_alignbit(lw[wi + 1 < B ? wi + 1 : wi], lw[wi], off);
+                        else cs[j][ks] = lw[wi] >> off;
                     }
                     if constexpr (PAD) cpad[j] = lds.cent[kw[4 * B] & (L - 1)];
                 }
@@ -702,9 +710,12 @@ __global__ __launch_bounds__(256) void score_kernel(MainArgs a) {
                 for (int it = 0; it < 4; ++it) st[it * 64 + l] = rec.s[it];
                 wave_lds_sync();
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < 4; ++j) {
+                    // sign indices 32 g .. 32 g + 31: sign word g, byte ks for step ks
+                    const uint32_t sw = st[(16 * j + c) * 4 + g];
 #pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) sb[j][ks] = (st[(16 * j + c) * 4 + ks] >> (8 * g)) & 0xFFu;
+                    for (int ks = 0; ks < 4; ++ks) sb[j][ks] = (sw >> (8 * ks)) & 0xFFu;
+                }
             }
             wave_lds_sync();
             float kn[4], kg[4];
