@@ -157,6 +157,11 @@ ROUNDTRIP_SYMBOL = "_ZN3rqk15rq_quant_kernelILi2ELb1ELb1ELb1ELb1ELi8EEEvNS_8Roto
 def profile_cases():
     n1, nm, nd = N_VEC, 1 << 20, 262144
     fl = 2 * 128 * 128      # flops of one 128 x 128 matrix-vector product
+    # Qwen2.5-3B-shaped decode step: keys (or values) of every layer and the
+    # estimates of every query row
+    from kv_cache_vector_norm_amd import workloads as W
+    qs = W.QWEN25_3B
+    qk, qr, qt = qs["layers"] * qs["kv_heads"] * qs["tokens"], qs["layers"] * qs["q_heads"], qs["tokens"]
     return [
         ("copy_65536_same_bytes", "rqk::copy_kernel", "11copy_kernel", 4, n1 * 568, 0,
          "reference copy of 65,536 x 568 B (read 284 B, write 284 B per vector)"),
@@ -179,12 +184,12 @@ def profile_cases():
         ("tq_roundtrip_dense_qjl3_262144", "rqk::tq_quant_kernel<2, true, true, true, true,",
          "15tq_quant_kernelILi2ELb1ELb1ELb1ELb1ELi", 4, nd * (256 + 52 + 256), nd * fl * (3 + 3 + 2 + 2 + 1),
          "TurboQuant roundtrip, 2-bit + QJL, fp16 in/out, 262,144 keys"),
-        ("rq_attend_values_qwen", "rqk::attend_values_kernel<2, false, true, true>",
-         "20attend_values_kernelILi2ELb0ELb1ELb1EE", 4, 0, 0,
-         "decode attention value pass (centroid sums), Qwen2.5-3B-shaped cache, all layers"),
-        ("rq_attend_signs_qwen", "rqk::attend_values_kernel<1, true, false, false>",
-         "20attend_values_kernelILi1ELb1ELb0ELb0EE", 4, 0, 0,
-         "decode attention value pass (sign sums), Qwen2.5-3B-shaped cache, all layers"),
+        ("rq_attend_scores_qwen", "rqk::score_kernel<2, true, true, 0, false>",
+         "12score_kernelILi2ELb1ELb1ELi0ELb0EE", 4, qk * 56 + 4 * qr * qt, 0,
+         "decode attention pass 1 (estimates and per-workgroup row maxima), Qwen2.5-3B-shaped cache, all layers"),
+        ("rq_attend_values_qwen", "rqk::attend_values16_kernel<2, true, true>",
+         "22attend_values16_kernelILi2ELb1ELb1EE", 4, qk * 56 + 4 * qr * qt, 0,
+         "decode attention value pass (centroid and sign sums), Qwen2.5-3B-shaped cache, all layers"),
         ("copy_calibration_256mib", "rqk::copy_kernel", "11copy_kernel", 1, 2 * (256 << 20), 0,
          "counter calibration: reference copy of 256 MiB"),
     ]
@@ -269,7 +274,7 @@ def profile_set(K, W, dev):
     g = HQ // H
     ws = torch.empty(K.rq_attend_workspace(L * HQ, g, T) + 256, dtype=torch.uint8, device=dev)
     att = torch.empty((L * HQ, 128), dtype=torch.float32, device=dev)
-    note("rq_attend_qwen (rq_attend_values_qwen, rq_attend_signs_qwen)")
+    note("rq_attend_qwen (rq_attend_scores_qwen, rq_attend_values_qwen)")
     for _ in range(4):
         K.attend(c, c, qq.view(L * HQ, 128), krec, vrec, g, T, T, out=att, workspace=ws)
     del kv, crec, ws
