@@ -173,6 +173,9 @@ def profile_cases():
         ("rq_roundtrip_mse3_65536", "rqk::rq_quant_kernel<3, false, true, true, true, 4>",
          "15rq_quant_kernelILi3ELb0ELb1ELb1ELb1ELi4EE", 4, n1 * 566, 0,
          "rotor roundtrip, 3-bit MSE only, fp16 in/out, 65,536 keys"),
+        ("pq_roundtrip_65536", "rqk::pq_quant_kernel<true, true, true, 8>",
+         "15pq_quant_kernelILb1ELb1ELb1ELi8EE", 4, n1 * (256 + 64 + 256), n1 * 2 * fl * 3,
+         "PolarQuant roundtrip, fp16 in/out, 65,536 keys (flops: Pi x, Pi^T y~, 3 fp16 MFMAs each)"),
         ("rq_roundtrip_mse3_1048576", "rqk::rq_quant_kernel<3, false, true, true, true, 4>",
          "15rq_quant_kernelILi3ELb0ELb1ELb1ELb1ELi4EE", 4, nm * 566, 0,
          "rotor roundtrip, 3-bit MSE only, fp16 in/out, 1,048,576 keys"),
@@ -244,7 +247,12 @@ def profile_set(K, W, dev):
     note("rq_roundtrip_mse3_65536")
     for i in order:
         m.roundtrip(xs[i], rec=mrecs[i], out=ys[i])
-    del xs, ys, recs, scs, mrecs
+    pc = K.PolarCodec(seed=0)
+    pws = [pc.alloc_words(N_VEC, dev) for _ in range(sets)]
+    note("pq_roundtrip_65536")
+    for i in order:
+        pc.roundtrip(xs[i], words=pws[i], out=ys[i])
+    del xs, ys, recs, scs, mrecs, pws, pc
     mrec = m.alloc_record(1 << 20, dev)
     note("rq_roundtrip_mse3_1048576")
     for _ in range(4):

@@ -387,8 +387,8 @@ int rq_init(int d, int bits, uint64_t seed, int mode, rq_ctx** out) {
                 pit_lo[c * n + r] = lo;
             }
     }
-    if (mode & RQ_DENSE) {
-        // The dense codec kernels' MFMA layouts (two lanes per vector, slot j
+    if (mode & (RQ_DENSE | RQ_POLAR)) {
+        // The dense and PolarQuant codec kernels' MFMA layouts (two lanes per vector, slot j
         // of half h = coordinate 64 h + j): accumulator row r of M tile mt
         // (lane half h = bit 2 of r % 32, element 4 (r % 32 / 8) + r % 4) is
         // coordinate 64 h + 16 mt + element; K column c is slot 8 (c / 16) +
@@ -437,11 +437,13 @@ int rq_init(int d, int bits, uint64_t seed, int mode, rq_ctx** out) {
             if ((e = upload(reinterpret_cast<void**>(&ctx->pit_hi), pit_hi.data(), pit_hi.size() * 2)) != hipSuccess) break;
             if ((e = upload(reinterpret_cast<void**>(&ctx->pit_lo), pit_lo.data(), pit_lo.size() * 2)) != hipSuccess) break;
         }
-        if (mode & RQ_DENSE) {
+        if (mode & (RQ_DENSE | RQ_POLAR)) {
             if ((e = upload(reinterpret_cast<void**>(&ctx->pi2_hi), pi2_hi.data(), pi2_hi.size() * 2)) != hipSuccess) break;
             if ((e = upload(reinterpret_cast<void**>(&ctx->pi2_lo), pi2_lo.data(), pi2_lo.size() * 2)) != hipSuccess) break;
             if ((e = upload(reinterpret_cast<void**>(&ctx->pit2_hi), pit2_hi.data(), pit2_hi.size() * 2)) != hipSuccess) break;
             if ((e = upload(reinterpret_cast<void**>(&ctx->pit2_lo), pit2_lo.data(), pit2_lo.size() * 2)) != hipSuccess) break;
+        }
+        if (mode & RQ_DENSE) {
             if ((e = upload(reinterpret_cast<void**>(&ctx->t2_hi), t2_hi.data(), t2_hi.size() * 2)) != hipSuccess) break;
             if ((e = upload(reinterpret_cast<void**>(&ctx->t2_lo), t2_lo.data(), t2_lo.size() * 2)) != hipSuccess) break;
         }
@@ -582,6 +584,10 @@ static rqk::PolarDev polar_tables(const rq_ctx* c) {
     p.pit_lo = c->pit_lo;
     p.pi32 = c->pi32;
     p.tab = c->pq_tab;
+    p.pi2_hi = c->pi2_hi;
+    p.pi2_lo = c->pi2_lo;
+    p.pit2_hi = c->pit2_hi;
+    p.pit2_lo = c->pit2_lo;
     return p;
 }
 

@@ -71,6 +71,12 @@ struct PolarDev {
     const uint16_t* pit_lo;
     const float* pi32;        // Pi in fp32, row-major
     const float* tab;         // kPolarTab floats: (cos, sin) of boundaries, then of centroids
+    // codec kernels (two lanes per vector): the pair permuted as for the dense
+    // codec, Pi row by row (staged in LDS), Pi^T in MFMA fragment order
+    const uint16_t* pi2_hi;
+    const uint16_t* pi2_lo;
+    const uint16_t* pit2_hi;
+    const uint16_t* pit2_lo;
 };
 struct ScoreTables {
     bool dense;

@@ -5,12 +5,14 @@
 // Lloyd codebook (4 bits on [0, 2 pi), then 2 bits on [0, pi/2]), the 8 final
 // radii stored as halves: 16 words per vector.
 //
-// One vector per lane, 64 per wave, as in the other codec kernels.  The
-// rotation reuses the TurboQuant kernels' exact-enough MFMA scheme (Pi and the
-// unit vector both as half pairs, three 32x32x16 products per K step).  The
-// pairs of each level sit in one lane and, for every level, inside the same
-// 32-coordinate M tile, so each tile's codes and radii are finished straight
-// from its accumulators.
+// The quantiser and dequantiser run two lanes per vector, 32 vectors per
+// wave, on the TurboQuant codec's MFMA scheme (Pi permuted on the host so
+// that lane half h holds coordinates 64 h .. 64 h + 63 and accumulator
+// element r of M tile mt is coordinate 64 h + 16 mt + r; exact half pairs,
+// three 32x32x16 products per K block): every level's pairs sit in one lane
+// and inside one 16-coordinate M tile, so each tile's codes and final radius
+// are finished straight from its accumulators.  Scoring and the attention
+// value pass decode one key per lane.
 //
 // Angle codes are taken without any arctangent: for a boundary t, the angle
 // of (a, b) exceeds t exactly when b cos t - a sin t > 0 (the angle and t
@@ -19,7 +21,7 @@
 // a turn by pi (negation), a turn by -pi/2 (swap and negate), a reflection
 // in the diagonal (swap) — each adding its share of the code, and one cross
 // product against t_1 finishes it.
-#include "rq_dense_dev.h"
+#include "rq_dense_codec_dev.h"
 
 namespace rqk {
 
@@ -82,104 +84,88 @@ struct PqBounds {
     }
 };
 
-// Codes and radii of M tile MT (unit-domain coordinates 32 MT .. 32 MT + 31,
-// y0 / y1 as from_accumulators leaves them, still scaled by 2^19) into the
-// record words w; its two final radii go to rad[2 MT], rad[2 MT + 1].
-// Tile-local pair m covers coordinates 2m, 2m + 1 = rows 8 b + 4 h + 2 p and
-// the next, b = m / 4, h = (m / 2) % 2, p = m % 2: registers 4 b + 2 p and
-// 4 b + 2 p + 1 of own half h.
-template <int MT>
-__device__ __forceinline__ void pq_encode_tile(const float (&y0)[16], const float (&y1)[16], const PqBounds& B,
-                                               uint32_t (&w)[kPolarWords], float (&rad)[8]) {
-    float r1[16], r2[8], r3[4];
+// The record fields of one lane half's 64 coordinates (two lanes per
+// vector, half h = coordinates 64 h .. 64 h + 63): the 32 level-1 pairs are
+// record words 4 h .. 4 h + 3, the 16 level-2 pairs word 8 + h, the 8
+// level-3 pairs the half's 16 bits of word 10 (l3), the 4 level-4 pairs its
+// 8 bits of word 11 (l4); final radius I = 4 h + mt closes the 16
+// coordinates of M tile mt.
+struct PqHalf {
+    uint32_t w1[4];
+    uint32_t w2, l3, l4;
+};
+
+// Codes of the lane half from the unit-domain coordinates yv(mt, r) of
+// local slot 16 mt + r (coordinate 64 h + 16 mt + r), and the four final
+// radii of the half in the unit domain.
+template <class YV>
+__device__ __forceinline__ void pq_encode_half(YV yv, const PqBounds& B, PqHalf& c, float (&rad)[4]) {
+    c.w2 = 0u;
+    c.l3 = 0u;
+    c.l4 = 0u;
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-        const int b = m >> 2, h = (m >> 1) & 1, p = m & 1;
-        const float a = (h ? y1[4 * b + 2 * p] : y0[4 * b + 2 * p]) * kRotScale;
-        const float bb = (h ? y1[4 * b + 2 * p + 1] : y0[4 * b + 2 * p + 1]) * kRotScale;
-        const int M = 16 * MT + m;                                   // level-1 pair, bits 4 M
-        w[M >> 3] |= pq_code_first(a, bb, B.c0, B.s0) << (4 * (M & 7));
-        r1[m] = pq_radius(a, bb);
-    }
+    for (int mt = 0; mt < 4; ++mt) {
+        float r1[8], r2[4], r3[2];
+        uint32_t w = 0u;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const int K = 8 * MT + k;                                    // level 2, bits 256 + 2 K
-        w[8 + (K >> 4)] |= pq_code_later(r1[2 * k], r1[2 * k + 1], B.c[0], B.s[0]) << (2 * (K & 15));
-        r2[k] = pq_radius(r1[2 * k], r1[2 * k + 1]);
-    }
+        for (int m = 0; m < 8; ++m) {
+            const float a = yv(mt, 2 * m), b = yv(mt, 2 * m + 1);
+            w |= pq_code_first(a, b, B.c0, B.s0) << (4 * m);
+            r1[m] = pq_radius(a, b);
+        }
+        c.w1[mt] = w;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int J = 4 * MT + j;                                    // level 3, bits 320 + 2 J
-        w[10] |= pq_code_later(r2[2 * j], r2[2 * j + 1], B.c[1], B.s[1]) << (2 * J);
-        r3[j] = pq_radius(r2[2 * j], r2[2 * j + 1]);
-    }
+        for (int k = 0; k < 4; ++k) {
+            c.w2 |= pq_code_later(r1[2 * k], r1[2 * k + 1], B.c[0], B.s[0]) << (2 * (4 * mt + k));
+            r2[k] = pq_radius(r1[2 * k], r1[2 * k + 1]);
+        }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int I = 2 * MT + i;                                    // level 4, bits 352 + 2 I
-        w[11] |= pq_code_later(r3[2 * i], r3[2 * i + 1], B.c[2], B.s[2]) << (2 * I);
-        rad[I] = pq_radius(r3[2 * i], r3[2 * i + 1]);
+        for (int j = 0; j < 2; ++j) {
+            c.l3 |= pq_code_later(r2[2 * j], r2[2 * j + 1], B.c[1], B.s[1]) << (2 * (2 * mt + j));
+            r3[j] = pq_radius(r2[2 * j], r2[2 * j + 1]);
+        }
+        c.l4 |= pq_code_later(r3[0], r3[1], B.c[2], B.s[2]) << (2 * mt);
+        rad[mt] = pq_radius(r3[0], r3[1]);
     }
 }
 
-// y~ of one record, divided by the norm of its radii and split into the
-// half pairs of the rotation (h11 = 2^11 hi, hi, lo of 16 y~_u); returns that
-// norm.  The levels are walked back from the radii: r -> (r cos c, r sin c).
-__device__ __forceinline__ float pq_decode_split(const float2* __restrict__ tab, const uint32_t (&w)[kPolarWords],
-                                                 uint32_t (&yh11)[64], uint32_t (&yh)[64], uint32_t (&yl)[64]) {
-    float R[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) R[i] = h2f((w[12 + (i >> 1)] >> (16 * (i & 1))) & 0xFFFFu);
-    float ss = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) ss = __builtin_fmaf(R[i], R[i], ss);
-    const float rn = __builtin_sqrtf(ss);
-    const float inv16 = rn > 0.0f ? 16.0f / rn : 0.0f;
-#pragma unroll
-    for (int MT = 0; MT < 4; ++MT) {
-        float r3[4], r2[8], r1[16];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int I = 2 * MT + i;
-            const float2 cs = tab[kPqCen + 8 + ((w[11] >> (2 * I)) & 3u)];
-            const float r = R[I] * inv16;
-            r3[2 * i] = r * cs.x;
-            r3[2 * i + 1] = r * cs.y;
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int J = 4 * MT + j;
-            const float2 cs = tab[kPqCen + 4 + ((w[10] >> (2 * J)) & 3u)];
-            r2[2 * j] = r3[j] * cs.x;
-            r2[2 * j + 1] = r3[j] * cs.y;
-        }
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int K = 8 * MT + k;
-            const float2 cs = tab[kPqCen + ((w[8 + (K >> 4)] >> (2 * (K & 15))) & 3u)];
-            r1[2 * k] = r2[k] * cs.x;
-            r1[2 * k + 1] = r2[k] * cs.y;
-        }
-#pragma unroll
-        for (int m = 0; m < 16; ++m) {
-            const int M = 16 * MT + m;
-            const float2 cs = tab[kPqCen0 + ((w[M >> 3] >> (4 * (M & 7))) & 15u)];
-            // 16 y~_u of coordinates 2M, 2M + 1 -> hi = half(v), lo = half((v - hi) 2^11)
-            const float va = r1[m] * cs.x, vb = r1[m] * cs.y;
-            const uint32_t hi = cvt_pk(va, vb);
-            const float da = va - h2f(hi & 0xFFFFu), db = vb - h2f(hi >> 16);
-            yh[M] = hi;
-            yl[M] = cvt_pk(da * 2048.0f, db * 2048.0f);
-            yh11[M] = pk_scale2048(hi);
-        }
+// 16 y~ / ||r^|| of M tile mt of a lane half (local slots 16 mt .. 16 mt +
+// 15), from its final radius r = R_I * 16 / ||r^||: the levels are walked
+// back, r -> (r cos c, r sin c).  Values come out times 16, as the split of
+// the rotation operands takes them.
+__device__ __forceinline__ void pq_decode_tile(const float2* __restrict__ tab, const PqHalf& c, int mt, float r,
+                                               float (&v)[16]) {
+    float r3[2], r2[4], r1[8];
+    {
+        const float2 cs = tab[kPqCen + 8 + ((c.l4 >> (2 * mt)) & 3u)];
+        r3[0] = r * cs.x;
+        r3[1] = r * cs.y;
     }
-    return rn;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const float2 cs = tab[kPqCen + 4 + ((c.l3 >> (2 * (2 * mt + j))) & 3u)];
+        r2[2 * j] = r3[j] * cs.x;
+        r2[2 * j + 1] = r3[j] * cs.y;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float2 cs = tab[kPqCen + ((c.w2 >> (2 * (4 * mt + k))) & 3u)];
+        r1[2 * k] = r2[k] * cs.x;
+        r1[2 * k + 1] = r2[k] * cs.y;
+    }
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const float2 cs = tab[kPqCen0 + ((c.w1[mt] >> (4 * m)) & 15u)];
+        v[2 * m] = r1[m] * cs.x;
+        v[2 * m + 1] = r1[m] * cs.y;
+    }
 }
 
-// x~ = Pi^T y~ of one record into `out` (coordinates in increasing order);
-// The scoring form of pq_decode_split followed by rot_mfma<0>: each 32
+// y~ of one record (one vector per lane), divided by the norm of its radii,
+// split into half pairs and rotated by the A fragments fa_hi / fa_lo: each 32
 // coordinates are split and enter the rotation's two K blocks as soon as
-// they are decoded, so only one chunk's half pairs are live (the same
-// values and the same MFMA order as the two steps one after the other).
+// they are decoded, so only one chunk's half pairs are live.  The levels are
+// walked back from the radii: r -> (r cos c, r sin c).
 template <class FragHi, class FragLo>
 __device__ __forceinline__ float pq_decode_rot(const float2* __restrict__ tab, const uint32_t (&w)[kPolarWords],
                                                FragHi fa_hi, FragLo fa_lo, int l, float (&own0)[16],
@@ -255,193 +241,248 @@ __device__ __forceinline__ float pq_decode_rot(const float2* __restrict__ tab, c
     return rn;
 }
 
-// done(mt) runs once coordinates 32 mt .. 32 mt + 31 are set.
-template <class Out, class Done>
-__device__ __forceinline__ void pq_dequant_vec(const PolarDev& P, const float2* __restrict__ tab,
-                                               const uint32_t (&w)[kPolarWords], Out& out, int l, Done done) {
-    uint32_t yh11[64], yh[64], yl[64];
-    const float rn = pq_decode_split(tab, w, yh11, yh, yl) * kRotScale;
-    auto tile = [&](auto mt_c) {
-        constexpr int MT = decltype(mt_c)::value;
-        float x0[16], x1[16];
-        rot_mfma<MT>(
-            yh11, yh, yl, [&](int row, int chunk) { return gmat_frag(P.pit_hi, row, chunk); },
-            [&](int row, int chunk) { return gmat_frag(P.pit_lo, row, chunk); }, l, x0, x1);
-#pragma unroll
-        for (int il = 0; il < 32; ++il) {
-            const int b8 = il >> 3, k = il & 7;
-            const float xv = k < 4 ? x0[4 * b8 + k] : x1[4 * b8 + k - 4];
-            out.set(32 * MT + il, rn * xv);
-        }
-        done(MT);
-    };
-    tile(std::integral_constant<int, 0>{});
-    tile(std::integral_constant<int, 1>{});
-    tile(std::integral_constant<int, 2>{});
-    tile(std::integral_constant<int, 3>{});
-}
-
 // ------------------------------------------------------------ kernels --
 constexpr int kPqWaves = 4;
 
-struct PqQuantLds {
-    u32x4 tiles[kPqWaves][kTileBytes / 16];
-    u32x4 pih[128 * 16];
-    u32x4 pil[128 * 16];
-    float2 tab[kPqTab2];
-};
+// Norm of the eight stored radii (R_0 .. R_7 from record words 12 .. 15, in
+// that order, as every decoder sums them) and the lane half's own four.
+__device__ __forceinline__ float pq_radii(const uint32_t (&rw)[4], int h, float (&own)[4]) {
+    float R[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) R[i] = h2f((rw[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+    float ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss = __builtin_fmaf(R[i], R[i], ss);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) own[mt] = h ? R[4 + mt] : R[mt];
+    return __builtin_sqrtf(ss);
+}
 
-template <bool IN_F16, bool OUT_F16, bool ROUNDTRIP>
-__global__ __launch_bounds__(kPqWaves * 64) void pq_quant_kernel(PolarDev P, const char* __restrict__ x,
-                                                                 int64_t ldx_bytes, int64_t n,
-                                                                 uint32_t* __restrict__ words, char* __restrict__ y,
-                                                                 int64_t ldy_bytes) {
-    __shared__ PqQuantLds sm;
+// x~ = Pi^T y~ of the lane half's 64 slots (accumulator scale 2^19 / ||r^||):
+// each M tile's 16 values are decoded and split as the K blocks 2 mt and
+// 2 mt + 1 that take them come up; the same sequence in the roundtrip and
+// in the dequantiser.
+__device__ __forceinline__ void pq_pit2(const GPair& g, const Frag8& first, const float2* __restrict__ tab,
+                                        const PqHalf& c, const float (&own)[4], float inv16, f32x16 (&ax)[4]) {
+    float v[16];
+    gprod3(ax, g, first, [&](int kb) {
+        const int mt = kb >> 1;
+        if ((kb & 1) == 0) pq_decode_tile(tab, c, mt, own[mt] * inv16, v);
+        return split8([&](int e) { return v[8 * (kb & 1) + e]; });
+    });
+}
+
+// Quantiser (and fused roundtrip): a wave owns a tile of 32 vectors, lanes
+// v and v + 32 sharing vector v as in the dense codec (Pi permuted on the
+// host so that accumulator element r of M tile mt in half h is coordinate
+// 64 h + 16 mt + r).  Every level's pairs then lie in one lane: each half
+// codes its 64 coordinates down to four final radii, and the two halves
+// join only for record words 10 and 11 and for the norm of the radii.
+template <bool IN_F16, bool OUT_F16, bool ROUNDTRIP, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void pq_quant_kernel(PolarDev P, const char* __restrict__ x,
+                                                              int64_t ldx_bytes, int64_t n,
+                                                              uint32_t* __restrict__ words, char* __restrict__ y,
+                                                              int64_t ldy_bytes) {
+    constexpr int NT = 64 * WAVES;
+    constexpr int TB = 32 * (IN_F16 ? 256 : 512);   // input tile (LDS DMA)
+    static_assert(WAVES * TB <= 65536, "input tiles must lie in the first 64 KB of LDS");
+    struct Lds {
+        u32x4 tiles[WAVES][TB / 16];
+        u32x4 pih[128 * 16];   // P_hi, or 2^11 P_hi for fp16 input
+        u32x4 pil[128 * 16];
+        float2 tab[kPqTab2];
+        uint32_t stage[WAVES][32 * kPolarWords];
+    };
+    __shared__ Lds lds;
+
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t ntiles = (n + 63) / 64;
-    const bool single = ntiles <= kSimds;   // at most one tile per SIMD: output leaves in quarters
-    const int64_t tstep = gridDim.x * (int64_t)kPqWaves;
-    // fp16 input is fetched one tile ahead (the first one before the block's
-    // staging), so each tile's load latency hides behind the previous tile
-    TileRegs nxt;
-    const int64_t t0 = blockIdx.x * (int64_t)kPqWaves + wave;
-    if constexpr (IN_F16) {
-        if (t0 < ntiles) tile_fetch(x, ldx_bytes, t0 * 64, n, 0, nxt, lane_id());
-    }
-    pq_tab_to_lds(P.tab, sm.tab);
-    mat_to_lds<kPqWaves * 64>(P.pi_hi, sm.pih);
-    mat_to_lds<kPqWaves * 64>(P.pi_lo, sm.pil);
+    const int64_t ntiles = (n + 31) / 32;
+    const int64_t tstep = static_cast<int64_t>(gridDim.x) * WAVES;
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * WAVES + wave;
+    char* tile = reinterpret_cast<char*>(lds.tiles[wave]);
+    if (t0 < ntiles) tile2_dma<IN_F16>(x, ldx_bytes, t0 * 32, n, tile, lane_id());
+    pq_tab_to_lds(P.tab, lds.tab);
+    if constexpr (IN_F16) mat_to_lds_x2048<NT>(P.pi2_hi, lds.pih);
+    else mat_to_lds<NT>(P.pi2_hi, lds.pih);
+    mat_to_lds<NT>(P.pi2_lo, lds.pil);
     __syncthreads();
+    uint32_t* stw = lds.stage[wave];
 
-    u32x4* tile = sm.tiles[wave];
-    uint32_t* stage = reinterpret_cast<uint32_t*>(tile);
+    // a roundtrip stores each tile's output after the next tile's input has
+    // arrived
+    OutWords<OUT_F16> pend;
+    int64_t pend_base = -1;
+
     for (int64_t t = t0; t < ntiles; t += tstep) {
-        const int64_t base = t * 64;
+        const int64_t base = t * 32;
         const int z = opaque_zero();
         const int l = lane_id() + z;
+        const int h = l >> 5, vi = l & 31;
         PqBounds B;
-        B.load(sm.tab, z);
-
-        // load, norm (same arithmetic as the other codec kernels)
-        uint32_t xin[IN_F16 ? 64 : 1];
-        float xf32[IN_F16 ? 1 : 128];
+        B.load(lds.tab, z);
+        DSlots<IN_F16> in;
+        tile2_dma_wait();
+        in.read(tile, vi, h);
+        lds_reads_done();
+        if (t + tstep < ntiles) tile2_dma<IN_F16>(x, ldx_bytes, (t + tstep) * 32, n, tile, l);
+        if constexpr (ROUNDTRIP) {
+            if (pend_base >= 0) dense_out_put<OUT_F16>(pend, y, ldy_bytes, pend_base, n, vi, h);
+        }
+        float ss = 0.0f;
         if constexpr (IN_F16) {
-            tile_put(nxt, tile, l);
-            if (t + tstep < ntiles) tile_fetch(x, ldx_bytes, (t + tstep) * 64, n, 0, nxt, l);
-            wave_lds_sync();
 #pragma unroll
-            for (int c = 0; c < 16; ++c) {
-                const u32x4 q = tile[swz(l, c)];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) xin[4 * c + e] = q[e];
+            for (int k = 0; k < kDenseSlots / 2; ++k) {
+                const f16x2 v = __builtin_bit_cast(f16x2, in.w[k]);
+                ss = __builtin_amdgcn_fdot2(v, v, ss, false);
             }
         } else {
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                tile_load(x, ldx_bytes, base, n, 256 * h, tile, l);
-                wave_lds_sync();
-#pragma unroll
-                for (int c = 0; c < 16; ++c) {
-                    const u32x4 q = tile[swz(l, c)];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const uint32_t qe = q[e];
-                        xf32[64 * h + 4 * c + e] = __builtin_bit_cast(float, qe);
-                    }
-                }
+            for (int j = 0; j < kDenseSlots; ++j) {
+                const float v = in.get(j);
+                ss = __builtin_fmaf(v, v, ss);
             }
         }
-        auto xget = [&](int i) -> float {
-            if constexpr (IN_F16) {
-                const uint32_t v = xin[i >> 1];
-                return h2f((i & 1) ? (v >> 16) : (v & 0xFFFFu));
-            } else {
-                return xf32[i];
-            }
-        };
-        float ss = 0.0f;
-#pragma unroll
-        for (int i = 0; i < kD; ++i) {
-            const float v = xget(i);
-            ss = __builtin_fmaf(v, v, ss);
-        }
+        ss = ss + other_half(ss, h);
         const float nrm = __builtin_sqrtf(ss);
         const float inv = nrm > 0.0f ? 1.0f / nrm : 0.0f;
+        const float inv16 = 16.0f * inv;
 
-        // y_u = Pi x_u tile by tile, each tile's codes and radii at once
-        uint32_t w[kPolarWords];
+        // y = Pi x as in the dense codec: fp16 input enters the MFMAs as it
+        // is ((2^11 P_hi) x + P_lo x = 2^15 Pi x), fp32 input is normalised
+        // and split (accumulator 2^19 Pi x_u)
+        f32x16 ay[4];
+        u32x4 fh[2][4], fl[2][4];
+        auto pi_frags = [&](int kb, u32x4 (&dh)[4], u32x4 (&dl)[4]) {
 #pragma unroll
-        for (int k = 0; k < kPolarWords; ++k) w[k] = 0u;
-        float rad[8];
-        {
-            uint32_t vh11[64], vh[64], vl[64];
-#pragma unroll
-            for (int i = 0; i < kD; ++i) {
-                uint32_t a, b, c;
-                split16(xget(i) * inv, &a, &b, &c);
-                put_pair(vh11, i, a);
-                put_pair(vh, i, b);
-                put_pair(vl, i, c);
+            for (int mt = 0; mt < 4; ++mt) {
+                const int row = 32 * mt + (l & 31), chunk = 2 * kb + h;
+                dh[mt] = mat_frag(lds.pih, row, chunk);
+                dl[mt] = mat_frag(lds.pil, row, chunk);
             }
-            auto tile_q = [&](auto mt_c) {
-                constexpr int MT = decltype(mt_c)::value;
-                float y0[16], y1[16];
-                rot_mfma<MT>(
-                    vh11, vh, vl, [&](int row, int chunk) { return mat_frag(sm.pih, row, chunk); },
-                    [&](int row, int chunk) { return mat_frag(sm.pil, row, chunk); }, l, y0, y1);
-                pq_encode_tile<MT>(y0, y1, B, w, rad);
-            };
-            tile_q(std::integral_constant<int, 0>{});
-            tile_q(std::integral_constant<int, 1>{});
-            tile_q(std::integral_constant<int, 2>{});
-            tile_q(std::integral_constant<int, 3>{});
-        }
+        };
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w[12 + i] = f2h(rad[2 * i] * nrm) | (f2h(rad[2 * i + 1] * nrm) << 16);
+        for (int mt = 0; mt < 4; ++mt) ay[mt] = f32x16{};
+        pi_frags(0, fh[0], fl[0]);
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) {
+            const int cur = kb & 1;
+            if (kb < 7) pi_frags(kb + 1, fh[cur ^ 1], fl[cur ^ 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (IN_F16) {
+                const u32x4 xb = {in.w[4 * kb], in.w[4 * kb + 1], in.w[4 * kb + 2], in.w[4 * kb + 3]};
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) ay[mt] = mfma(fh[cur][mt], xb, ay[mt]);
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) ay[mt] = mfma(fl[cur][mt], xb, ay[mt]);
+            } else {
+                kblock3(ay, split8([&](int e) { return in.get(8 * kb + e) * inv16; }), fh[cur], fl[cur]);
+            }
+        }
+        // accumulator -> unit-domain y_u (a power-of-two rescaling of inv)
+        const float ysc = IN_F16 ? inv16 * kRotScale : kRotScale;
+        __builtin_amdgcn_sched_barrier(0);
 
-        words_store<kPolarWords>(words, base, n, w, stage, l);
+        PqHalf c;
+        float rad[4];
+        pq_encode_half([&](int mt, int r) { return ay[mt][r] * ysc; }, B, c, rad);
+        // stored radii (halves of the radii times the norm), then the other
+        // half's l3 / l4 fields for words 10 and 11
+        const uint32_t rw0 = f2h(rad[0] * nrm) | (f2h(rad[1] * nrm) << 16);
+        const uint32_t rw1 = f2h(rad[2] * nrm) | (f2h(rad[3] * nrm) << 16);
+        const uint32_t mine = c.l3 | (c.l4 << 16);
+        const uint32_t other = other_half(mine, h);
+
+        // the reconstruction's first Pi^T fragments requested before the
+        // record is written
+        const GPair pg(P.pit2_hi, P.pit2_lo, l);
+        Frag8 pf0;
+        if constexpr (ROUNDTRIP) pf0 = pg.load(0);
+
+        wave_lds_sync();
+        {
+            uint32_t* row = stw + vi * kPolarWords;
+            *reinterpret_cast<u32x4*>(row + 4 * h) = u32x4{c.w1[0], c.w1[1], c.w1[2], c.w1[3]};
+            row[8 + h] = c.w2;
+            // half 0: word 10 = l3 of both halves; half 1: word 11 = l4 of both
+            row[10 + h] = h ? ((other >> 16) | ((mine >> 16) << 8)) : ((mine & 0xFFFFu) | (other << 16));
+            *reinterpret_cast<uint2*>(row + 12 + 2 * h) = make_uint2(rw0, rw1);
+        }
+        words2_store<kPolarWords>(words, base, n, stw, l);
+
+        // The reconstruction is exactly what pq_dequant_kernel forms from the
+        // record just written (the stored radii, the norm of all eight).
         if constexpr (ROUNDTRIP) {
-            VecOutT<OUT_F16> out;
-            if constexpr (!OUT_F16) out.bind(y, ldy_bytes, base, n);
-            out.begin(tile, l);
-            pq_dequant_vec(P, sm.tab, w, out, l, [&](int mt) {
-                if constexpr (OUT_F16) {
-                    if (single) out.store_cols(y, ldy_bytes, base, n, 4 * mt);
-                }
-            });
-            if (!OUT_F16 || !single) out.store(y, ldy_bytes, base, n);
+            const uint32_t ow0 = other_half(rw0, h), ow1 = other_half(rw1, h);
+            const uint32_t rw[4] = {h ? ow0 : rw0, h ? ow1 : rw1, h ? rw0 : ow0, h ? rw1 : ow1};
+            float own[4];
+            const float rn = pq_radii(rw, h, own);
+            const float inv16r = rn > 0.0f ? 16.0f / rn : 0.0f;
+            f32x16 ax[4];
+            pq_pit2(pg, pf0, lds.tab, c, own, inv16r, ax);
+            dense_out_words<false, OUT_F16>(ax, ax, 0.0f, rn, pend);
+            pend_base = base;
+        }
+    }
+    if constexpr (ROUNDTRIP) {
+        if (pend_base >= 0) {
+            const int l = lane_id();
+            dense_out_put<OUT_F16>(pend, y, ldy_bytes, pend_base, n, l & 31, l >> 5);
         }
     }
 }
 
 template <bool OUT_F16>
-__global__ __launch_bounds__(kPqWaves * 64) void pq_dequant_kernel(PolarDev P, const uint32_t* __restrict__ words,
-                                                                   int64_t n, char* __restrict__ y,
-                                                                   int64_t ldy_bytes) {
-    __shared__ u32x4 tiles[kPqWaves][kTileBytes / 16];
-    __shared__ float2 tab[kPqTab2];
-    pq_tab_to_lds(P.tab, tab);
+__global__ __launch_bounds__(256, 2) void pq_dequant_kernel(PolarDev P, const uint32_t* __restrict__ words, int64_t n,
+                                                         char* __restrict__ y, int64_t ldy_bytes) {
+    struct Lds {
+        float2 tab[kPqTab2];
+        uint32_t stage[4][32 * kPolarWords];
+    };
+    __shared__ Lds lds;
+    pq_tab_to_lds(P.tab, lds.tab);
     __syncthreads();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    u32x4* tile = tiles[wave];
-    uint32_t* stage = reinterpret_cast<uint32_t*>(tile);
-    const int64_t ntiles = (n + 63) / 64;
-    const bool single = ntiles <= kSimds;
-    for (int64_t t = blockIdx.x * (int64_t)kPqWaves + wave; t < ntiles; t += gridDim.x * (int64_t)kPqWaves) {
-        const int64_t base = t * 64;
+    uint32_t* stw = lds.stage[wave];
+    const int64_t ntiles = (n + 31) / 32;
+    // each tile's output is stored after the next tile's record has arrived
+    OutWords<OUT_F16> pend;
+    int64_t pend_base = -1;
+    for (int64_t t = blockIdx.x * 4LL + wave; t < ntiles; t += gridDim.x * 4LL) {
+        const int64_t base = t * 32;
         const int z = opaque_zero();
         const int l = lane_id() + z;
-        uint32_t w[kPolarWords];
-        words_load<kPolarWords>(words, base, n, w, stage, l);
-        VecOutT<OUT_F16> out;
-        if constexpr (!OUT_F16) out.bind(y, ldy_bytes, base, n);
-        out.begin(tile, l);
-        pq_dequant_vec(P, tab, w, out, l, [&](int mt) {
-            if constexpr (OUT_F16) {
-                if (single) out.store_cols(y, ldy_bytes, base, n, 4 * mt);
+        const int h = l >> 5, vi = l & 31;
+        words2_load<kPolarWords>(words, base, n, stw, l);
+        PqHalf c;
+        uint32_t rw[4];
+        {
+            const uint32_t* row = stw + vi * kPolarWords;
+            const u32x4 a = *reinterpret_cast<const u32x4*>(row + 4 * h);
+            const u32x4 b = *reinterpret_cast<const u32x4*>(row + 8);
+            const u32x4 r = *reinterpret_cast<const u32x4*>(row + 12);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                c.w1[k] = a[k];
+                rw[k] = r[k];
             }
-        });
-        if (!OUT_F16 || !single) out.store(y, ldy_bytes, base, n);
+            const uint32_t b0 = b[0], b1 = b[1], b2 = b[2], b3 = b[3];
+            c.w2 = h ? b1 : b0;
+            c.l3 = (b2 >> (16 * h)) & 0xFFFFu;
+            c.l4 = (b3 >> (8 * h)) & 0xFFu;
+        }
+        if (pend_base >= 0) dense_out_put<OUT_F16>(pend, y, ldy_bytes, pend_base, n, vi, h);
+        float own[4];
+        const float rn = pq_radii(rw, h, own);
+        const float inv16r = rn > 0.0f ? 16.0f / rn : 0.0f;
+        f32x16 ax[4];
+        const GPair pg(P.pit2_hi, P.pit2_lo, l);
+        pq_pit2(pg, pg.load(0), lds.tab, c, own, inv16r, ax);
+        dense_out_words<false, OUT_F16>(ax, ax, 0.0f, rn, pend);
+        pend_base = base;
+    }
+    if (pend_base >= 0) {
+        const int l = lane_id();
+        dense_out_put<OUT_F16>(pend, y, ldy_bytes, pend_base, n, l & 31, l >> 5);
     }
 }
 
@@ -819,18 +860,27 @@ static int pq_grid(int64_t n, int64_t cap) {
 
 hipError_t polar_quantize(const PolarDev& P, const void* x, bool in_f16, int64_t ldx_bytes, int64_t n,
                           uint32_t* words, void* y, bool out_f16, int64_t ldy_bytes, bool roundtrip, hipStream_t s) {
-    const int grid = pq_grid(n, 256 * 4);
     const char* xc = static_cast<const char*>(x);
     char* yc = static_cast<char*>(y);
-#define PQ_LAUNCH(IF, OF, RT)                                                                                     \
-    hipLaunchKernelGGL((pq_quant_kernel<IF, OF, RT>), dim3(grid), dim3(kPqWaves * 64), 0, s, P, xc, ldx_bytes, n, \
+    // fp16 input: eight-wave workgroups sharing one LDS copy of Pi (two waves
+    // per SIMD); fp32 input tiles need four waves' LDS
+    auto grid = [n](int waves) {
+        const int64_t ntiles = (n + 31) / 32;
+        const int64_t blocks = (ntiles + waves - 1) / waves;
+        return static_cast<int>(blocks < 256 ? (blocks > 0 ? blocks : 1) : 256);
+    };
+#define PQ_LAUNCH(IF, OF, RT, WV)                                                                                  \
+    hipLaunchKernelGGL((pq_quant_kernel<IF, OF, RT, WV>), dim3(grid(WV)), dim3(64 * WV), 0, s, P, xc, ldx_bytes, n, \
                        words, yc, ldy_bytes)
     if (!roundtrip) {
-        if (in_f16) PQ_LAUNCH(true, true, false); else PQ_LAUNCH(false, true, false);
+        if (in_f16) PQ_LAUNCH(true, true, false, 8);
+        else PQ_LAUNCH(false, true, false, 4);
     } else if (in_f16) {
-        if (out_f16) PQ_LAUNCH(true, true, true); else PQ_LAUNCH(true, false, true);
+        if (out_f16) PQ_LAUNCH(true, true, true, 8);
+        else PQ_LAUNCH(true, false, true, 8);
     } else {
-        if (out_f16) PQ_LAUNCH(false, true, true); else PQ_LAUNCH(false, false, true);
+        if (out_f16) PQ_LAUNCH(false, true, true, 4);
+        else PQ_LAUNCH(false, false, true, 4);
     }
 #undef PQ_LAUNCH
     return hipGetLastError();
@@ -838,12 +888,14 @@ hipError_t polar_quantize(const PolarDev& P, const void* x, bool in_f16, int64_t
 
 hipError_t polar_dequantize(const PolarDev& P, const uint32_t* words, int64_t n, void* y, bool out_f16,
                             int64_t ldy_bytes, hipStream_t s) {
-    const int grid = pq_grid(n, 256 * 8);
+    const int64_t ntiles = (n + 31) / 32;
+    const int64_t blocks = (ntiles + 3) / 4;
+    const int grid = static_cast<int>(blocks < 256 * 2 ? (blocks > 0 ? blocks : 1) : 256 * 2);
     char* yc = static_cast<char*>(y);
     if (out_f16)
-        hipLaunchKernelGGL((pq_dequant_kernel<true>), dim3(grid), dim3(kPqWaves * 64), 0, s, P, words, n, yc, ldy_bytes);
+        hipLaunchKernelGGL((pq_dequant_kernel<true>), dim3(grid), dim3(256), 0, s, P, words, n, yc, ldy_bytes);
     else
-        hipLaunchKernelGGL((pq_dequant_kernel<false>), dim3(grid), dim3(kPqWaves * 64), 0, s, P, words, n, yc, ldy_bytes);
+        hipLaunchKernelGGL((pq_dequant_kernel<false>), dim3(grid), dim3(256), 0, s, P, words, n, yc, ldy_bytes);
     return hipGetLastError();
 }
 
