@@ -82,6 +82,36 @@ def test_polar_keys_65536(K, P):
     assert rep["band_count"] <= 1e-4 * rep["angles"] + 3 * np.sqrt(1e-4 * rep["angles"])
 
 
+@pytest.mark.parametrize("in_dtype,out_dtype", [(torch.float16, torch.float16), (torch.float16, torch.float32),
+                                                (torch.float32, torch.float32)])
+def test_polar_several_tiles_per_wave(K, P, in_dtype, out_dtype):
+    """300,000 keys: every wave of the quantiser, the fused roundtrip and the
+    dequantiser walks several 32-vector tiles (the next tile's input is
+    fetched during the current one, each tile's output is stored after the
+    next tile's input or record has arrived).  The roundtrip's records equal
+    pq_quantize's and its output equals pq_dequantize of them, bit for bit;
+    rows sampled from the first and the last 65,536 match the oracle."""
+    n = 300_000
+    c = K.PolarCodec(seed=0)
+    g = torch.Generator(device="cuda").manual_seed(7)
+    x = torch.randn((n, D), generator=g, device="cuda").to(in_dtype)
+    words, y = c.roundtrip(x, dtype=out_dtype)
+    w2 = c.quantize(x)
+    d = c.dequantize(words, dtype=out_dtype)
+    torch.cuda.synchronize()
+    assert torch.equal(words, w2)
+    assert torch.equal(y, d)
+    rows = np.concatenate([W.sample_rows(65536, 1 / 32, seed=120),
+                           n - 65536 + W.sample_rows(65536, 1 / 32, seed=121)])
+    idx = torch.from_numpy(rows).cuda()
+    xs = x[idx].float().cpu().numpy()
+    gw = _words(words[idx])
+    PR.check_polar_words(P, xs, gw)
+    tol = PR.RECON_TOL + (2.0 ** -11 if out_dtype == torch.float16 else 0.0)
+    PR.compare_recon(y[idx].float().cpu().numpy(), PQ.dequantize(P, gw), PR.polar_radius_norm(gw),
+                     "polar roundtrip sample", tol=tol)
+
+
 @pytest.mark.parametrize("t,hq,group", [(1, 1, 1), (300, 8, 4), (2049, 32, 8), (640, 40, 40), (777, 66, 33),
                                         (4096, 32, 4)])
 def test_polar_score(K, P, t, hq, group):
