@@ -63,6 +63,9 @@ def parse():
                     help="run each profiled kernel a few times (for rocprofv3) and exit")
     ap.add_argument("--summarize", metavar="DIR",
                     help="turn rocprofv3 runs of --profile-set under DIR into profiles/ summaries, then exit")
+    ap.add_argument("--trace-command", default=None,
+                    help="with --trace-summary: the command that made the trace, written as the summary's header")
+    ap.add_argument("--trace-title", default=None, help="with --trace-summary: the header's title")
     ap.add_argument("--trace-summary", nargs=2, metavar=("TRACE_CSV", "OUT_MD"),
                     help="group a rocprofv3 kernel trace by kernel and grid size into a markdown table, then exit")
     return ap.parse_args()
@@ -867,6 +870,9 @@ def main():
         return
     if a.trace_summary:
         with open(a.trace_summary[1], "w") as f:
+            if a.trace_command:
+                f.write(f"# {a.trace_title or 'rocprofv3 kernel trace'}, by kernel and grid size\n\n"
+                        f"Command (MI355X):\n\n{a.trace_command}\n\n")
             f.write(trace_summary(a.trace_summary[0]))
         return
     if a.gpus != 1:
