@@ -394,3 +394,44 @@ def test_qwen_polar_scores_full(K, qwen, qwen_polar):
         ratio = (st["scores"][j * g:(j + 1) * g].to(torch.float64) - ref).abs() / lim
         worst = max(worst, float(ratio.max()))
     assert worst <= 1.0, f"polar score vs dequantised key: worst {worst:.3g} x tolerance"
+
+
+# ------------------------------------ PolarQuant keys at the Llama shape ----
+def test_llama_polar_sample(K, llama):
+    """The Llama-shaped cache's keys (all 32 layers, 33,554,432 vectors: 8.6
+    GB of fp16 input and 2.1 GB of records, so row offsets pass 2^32 bytes)
+    as PolarQuant records in one call, and one decode step of all layers'
+    scores in one pq_score call.  A seeded 0.1% of the key rows against the
+    oracle: angle codes, radii, dequantisation and the 4 query heads' scores
+    of every sampled key."""
+    from oracle import polar as PQ
+    spec = llama["spec"]
+    L, H, T, HQ, g = spec["layers"], spec["kv_heads"], spec["tokens"], spec["q_heads"], llama["group"]
+    n_k = L * H * T
+    c = K.PolarCodec(seed=0)
+    p = PQ.PolarParams(D, 0)
+    words = c.quantize(llama["flat"][:n_k])
+    scores = torch.empty((L * HQ, T), dtype=torch.float32, device=DEV)
+    c.score(llama["q"].view(L * HQ, D), words, g, T, T, out=scores)
+    _sync()
+    rows = W.sample_rows(n_k, 0.001, seed=9)
+    it = torch.from_numpy(rows).to(DEV)
+    gw = words.index_select(0, it).cpu().numpy().view(np.uint32)
+    x = llama["flat"].index_select(0, it).cpu().numpy()
+    rep = PR.check_polar_words(p, x, gw)
+    print(f"llama polar sample: {rows.size} keys, {rep}", flush=True)
+    y = c.dequantize(words.index_select(0, it), dtype=torch.float32).cpu().numpy()
+    rn = PR.polar_radius_norm(gw)
+    PR.compare_recon(y, PQ.dequantize(p, gw), rn, "polar dequantize")
+    layer, head, tok = rows // (H * T), (rows // T) % H, rows % T
+    qrows = (layer * HQ + head * g)[:, None] + np.arange(g)[None, :]
+    got = scores[torch.from_numpy(qrows).to(DEV), torch.from_numpy(tok).to(DEV)[:, None]]
+    got = got.cpu().numpy().astype(np.float64)
+    qh = llama["q_host"].reshape(-1, D).astype(np.float64)
+    for key in np.unique(layer * H + head):
+        sel = (layer * H + head) == key
+        qk = qh[qrows[sel][0]]
+        ref = PQ.score(p, qk, gw[sel])
+        PR.compare_scores(got[sel].T, ref, np.linalg.norm(qk, axis=1)[:, None], rn[sel][None, :],
+                          f"polar kv head {key}")
+    del words, scores
