@@ -661,8 +661,9 @@ def quality_row(K, W, dev, stream):
 
 
 def sweeps(K, dev, stream, codecs):
-    """Roundtrip rate over N (65,536 * 4^k up to 16,777,216) for each codec,
-    beside the reference copy of the same bytes at each N.  Below 1 M
+    """Roundtrip rate over N (65,536 * 4^k up to 16,777,216) for each codec
+    (rotor sessions and PolarQuant), beside the reference copy of the same
+    bytes at each N.  Below 1 M
     vectors the launches rotate over enough buffer sets to read cold data."""
     import torch
     out = {}
@@ -670,12 +671,13 @@ def sweeps(K, dev, stream, codecs):
     xb = torch.empty((nmax, 128), dtype=torch.float16, device=dev)
     xb.normal_()
     yb = torch.empty_like(xb)
-    ccap = nmax * 284
+    ccap = nmax * 288      # half of the largest record + fp16 in/out (PolarQuant: 576 B per vector)
     csrc = torch.empty(ccap, dtype=torch.uint8, device=dev)
     cdst = torch.empty_like(csrc)
     for key, cdc in codecs.items():
         nb = algorithmic_bytes(cdc.layout)
-        rb = cdc.alloc_record(nmax, dev)
+        polar = hasattr(cdc, "alloc_words")
+        rb = cdc.alloc_words(nmax, dev) if polar else cdc.alloc_record(nmax, dev)
         sweep = {}
         for n in (65536, 262144, 1048576, 4194304, 16777216):
             sets = max(1, min(nmax // n, (1 << 30) // (n * nb)))
@@ -685,6 +687,9 @@ def sweeps(K, dev, stream, codecs):
 
             def rt(i, n=n, sets=sets):
                 k = i % sets
+                if polar:
+                    cdc.roundtrip(xb[k * n:(k + 1) * n], words=rb[k * n:(k + 1) * n], out=yb[k * n:(k + 1) * n])
+                    return
                 r = K.Record(rb.codes[k * n:(k + 1) * n], rb.norms[k * n:(k + 1) * n],
                              None if rb.signs is None else rb.signs[k * n:(k + 1) * n],
                              None if rb.rnorms is None else rb.rnorms[k * n:(k + 1) * n])
@@ -1003,7 +1008,7 @@ def main():
     torch.cuda.empty_cache()
 
     if not a.no_sweep:
-        extras["sweeps"] = sweeps(K, dev, stream, {"mse3": mse, "qjl3": codec})
+        extras["sweeps"] = sweeps(K, dev, stream, {"mse3": mse, "qjl3": codec, "polar": K.PolarCodec(seed=0)})
 
     # the runtime's own device copy of 1 GiB, for comparison with rq_bench_copy
     src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
